@@ -1,0 +1,187 @@
+"""CPU oracle for the sparse Mixture-of-Experts feed-forward layer.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  The product path (the
+HIP library and its Python binding) never imports, links or calls it, and it
+never imports the product: the two share only the seeded inputs.
+
+This module is a thin ctypes wrapper over ``moe_oracle.c`` (plain C, binary64
+after the binary32 router logit).  Arrays are numpy: bfloat16 data is passed as
+``uint16`` bit patterns, binary32 data as ``float32``.
+
+What each function follows (pages cited by title and section):
+  * ``route`` -- router logits, softmax, top-k, selected-weight normalisation:
+    the Feed-forward panel of the "Decoder microscope" on the
+    Qwen3.8-Flash-Next anatomy page (frontier-model-atlas).
+  * ``experts`` / ``forward`` -- gated-MLP experts with SiLU
+    (llm-architectures-explained "Qwen3.8-Flash-Next", "Every architecture
+    field", ffns.moe.gated; llm-atlas "Qwen3.8-Flash-Next", "Raw config
+    fields", hidden_act) plus one shared expert scaled by its own sigmoid gate
+    (anatomy page, Feed-forward panel and "Evidence for layer 1").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+F32 = 0
+BF16 = 1
+
+
+def build(force: bool = True) -> str:
+    """Compile moe_oracle.c into oracle/liboracle.so with gcc (no fast-math,
+    no FMA contraction, OpenMP)."""
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+           "-fopenmp", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.oracle_router_logits.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp]
+    lib.oracle_route.argtypes = [i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+    lib.oracle_experts.argtypes = [i64, i32, i32, i32, i32, i32, i32,
+                                   vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.oracle_forward.argtypes = [i64, i32, i32, i32, i32, i32, i32,
+                                   vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    for f in (lib.oracle_router_logits, lib.oracle_route, lib.oracle_experts,
+              lib.oracle_forward, lib.oracle_threads):
+        f.restype = ctypes.c_int
+    lib.oracle_threads.argtypes = []
+    _lib = lib
+    return lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().oracle_threads())
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.uint16:
+        return BF16
+    if a.dtype == np.float32:
+        return F32
+    raise TypeError(f"oracle arrays are float32 or uint16 (bf16 bits), got {a.dtype}")
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    if not a.flags["C_CONTIGUOUS"]:
+        raise ValueError("oracle arrays must be C-contiguous")
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _same(dt, *arrays):
+    for a in arrays:
+        if a is not None and _dtype_code(a) != dt:
+            raise TypeError("all weight/activation arrays must share one dtype")
+
+
+def _bias(bias, E):
+    if bias is None:
+        return None
+    b = np.ascontiguousarray(bias, dtype=np.float32)
+    if b.shape != (E,):
+        raise ValueError("router bias must have shape [E]")
+    return b
+
+
+def router_logits(x, w_router, bias=None) -> np.ndarray:
+    """binary32 router logits [T, E] in the canonical accumulation order."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    dt = _dtype_code(x)
+    _same(dt, w_router)
+    b = _bias(bias, E)
+    out = np.empty((T, E), np.float32)
+    rc = _load().oracle_router_logits(T, d, E, dt, _ptr(x), _ptr(w_router),
+                                      _ptr(b), _ptr(out))
+    if rc:
+        raise RuntimeError(f"oracle_router_logits failed ({rc})")
+    return out
+
+
+def route(x, w_router, k, bias=None, return_logits=False):
+    """Top-k routing: (topk_idx int32 [T,k], topk_w float64 [T,k][, logits])."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    dt = _dtype_code(x)
+    _same(dt, w_router)
+    b = _bias(bias, E)
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    logits = np.empty((T, E), np.float32) if return_logits else None
+    rc = _load().oracle_route(T, d, E, k, dt, _ptr(x), _ptr(w_router), _ptr(b),
+                              _ptr(idx), _ptr(w), _ptr(logits))
+    if rc:
+        raise RuntimeError(f"oracle_route failed ({rc})")
+    return (idx, w, logits) if return_logits else (idx, w)
+
+
+def experts(x, w_gate_up, w_down, topk_idx, topk_w, w_sh_gate_up=None,
+            w_sh_down=None, sh_gate=None, return_gate=False):
+    """Expert stage with the routing given: float64 out [T, d] (and the
+    shared gate s [T] if asked)."""
+    T, d = x.shape
+    E, twoF, d2 = w_gate_up.shape
+    F = twoF // 2
+    assert d2 == d and w_down.shape == (E, d, F)
+    Fs = 0 if w_sh_gate_up is None else w_sh_gate_up.shape[0] // 2
+    k = topk_idx.shape[1]
+    dt = _dtype_code(x)
+    _same(dt, w_gate_up, w_down, w_sh_gate_up, w_sh_down, sh_gate)
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    w = np.ascontiguousarray(topk_w, dtype=np.float64)
+    out = np.empty((T, d), np.float64)
+    s = np.full((T,), np.nan, np.float64)
+    rc = _load().oracle_experts(T, d, E, k, F, Fs, dt, _ptr(x), _ptr(w_gate_up),
+                                _ptr(w_down), _ptr(w_sh_gate_up), _ptr(w_sh_down),
+                                _ptr(sh_gate), _ptr(idx), _ptr(w), _ptr(out), _ptr(s))
+    if rc:
+        raise RuntimeError(f"oracle_experts failed ({rc})")
+    return (out, s) if return_gate else out
+
+
+def forward(x, w_router, w_gate_up, w_down, k, w_sh_gate_up=None, w_sh_down=None,
+            sh_gate=None, bias=None):
+    """The whole layer: (out float64 [T,d], topk_idx [T,k], topk_w float64
+    [T,k], s float64 [T] (NaN without a shared expert))."""
+    T, d = x.shape
+    E, twoF, _ = w_gate_up.shape
+    F = twoF // 2
+    Fs = 0 if w_sh_gate_up is None else w_sh_gate_up.shape[0] // 2
+    dt = _dtype_code(x)
+    _same(dt, w_router, w_gate_up, w_down, w_sh_gate_up, w_sh_down, sh_gate)
+    b = _bias(bias, E)
+    out = np.empty((T, d), np.float64)
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    s = np.full((T,), np.nan, np.float64)
+    rc = _load().oracle_forward(T, d, E, k, F, Fs, dt, _ptr(x), _ptr(w_router), _ptr(b),
+                                _ptr(w_gate_up), _ptr(w_down), _ptr(w_sh_gate_up),
+                                _ptr(w_sh_down), _ptr(sh_gate), _ptr(out), _ptr(idx),
+                                _ptr(w), _ptr(s))
+    if rc:
+        raise RuntimeError(f"oracle_forward failed ({rc})")
+    return out, idx, w, s

@@ -1,0 +1,210 @@
+"""Seeded synthetic inputs for the sparse MoE feed-forward layer.
+
+This module generates data only: it holds none of the layer's arithmetic and
+is the one piece of code that both the CPU oracle's tests and the HIP path's
+tests/benchmark consume.
+
+Shapes follow the pages: d_model 2,560, 512 routed experts, top-10, expert
+width 640, one shared expert of width 640 (llm-architectures-explained
+"Qwen3.8-Flash-Next", table "Every architecture field", rows d_model and
+ffns.moe.*; anatomy page, "Decoder microscope", Feed-forward panel).  Weights
+are drawn N(0, 0.02^2): 0.02 is the checkpoint's initializer range (llm-atlas
+"Qwen3.8-Flash-Next", "Raw config fields", initializer_range), read as a
+standard deviation.  Data type bfloat16 ("Key facts", Dtype).  No trained
+weights exist here; these random weights stand in for them.
+
+Arrays are numpy.  bfloat16 tensors are ``uint16`` arrays of bit patterns
+(round-to-nearest-even from float32 draws); the fp32 configuration uses
+``float32``.
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+from statistics import NormalDist
+from typing import Optional
+
+import numpy as np
+
+WEIGHT_STD = 0.02
+
+# Independent counter streams per tensor: SeedSequence([seed, TENSOR_ID, i]).
+_X, _WR, _WGU, _WDN, _WSGU, _WSDN, _G, _BIAS = range(8)
+
+
+@dataclass(frozen=True)
+class MoEConfig:
+    name: str
+    T: int
+    d: int
+    E: int
+    k: int
+    F: int
+    Fs: int
+    dtype: str                      # "f32" | "bf16"
+    bias: Optional[str] = None      # None | "zipf" | "hot10"
+    seed_w: int = 1
+    seed_x: int = 100
+    seed_b: int = 1000
+    note: str = field(default="", compare=False)
+
+
+CONFIGS = {
+    1: MoEConfig("tiny_fp32_T32", 32, 128, 16, 4, 32, 32, "f32", None, 0, 0, 0,
+                 "T=32, d=128, 16 experts top-4, width 32, shared 32, fp32, seed 0"),
+    2: MoEConfig("decode_T32", 32, 2560, 512, 10, 640, 640, "bf16", None, 1, 102, 1002,
+                 "decode-shaped: T=32, near-uniform routing"),
+    3: MoEConfig("prefill_T4096", 4096, 2560, 512, 10, 640, 640, "bf16", None, 1, 103, 1003,
+                 "prefill-shaped: T=4096"),
+    4: MoEConfig("zipf_T16384", 16384, 2560, 512, 10, 640, 640, "bf16", "zipf", 1, 104, 1004,
+                 "router bias with a Zipf(1.2) prior over a seeded expert permutation"),
+    5: MoEConfig("hot10_T32768", 32768, 2560, 512, 10, 640, 640, "bf16", "hot10", 1, 105, 1005,
+                 "router bias making 10 seeded experts take about half of all assignments"),
+}
+
+
+def _rng(seed: int, *key: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, *key])))
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (nearest, ties to even); returns uint16 bits."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + r) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _normal(rng: np.random.Generator, shape, std: float, dtype: str) -> np.ndarray:
+    a = rng.standard_normal(shape, dtype=np.float32)
+    if std != 1.0:
+        a *= np.float32(std)
+    return f32_to_bf16_bits(a) if dtype == "bf16" else a
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def make_layer(d: int, E: int, F: int, Fs: int, dtype: str, seed: int) -> dict:
+    """Layer weights: router [E,d], packed gate/up [E,2F,d] (gate rows first),
+    down [E,d,F], shared gate/up [2Fs,d], shared down [d,Fs], shared gate
+    vector [d].  Each expert's blocks come from their own seeded stream, so
+    they can be drawn in parallel and do not depend on E."""
+    npdt = np.uint16 if dtype == "bf16" else np.float32
+    w_gu = np.empty((E, 2 * F, d), npdt)
+    w_dn = np.empty((E, d, F), npdt)
+
+    def expert(e):
+        w_gu[e] = _normal(_rng(seed, _WGU, e), (2 * F, d), WEIGHT_STD, dtype)
+        w_dn[e] = _normal(_rng(seed, _WDN, e), (d, F), WEIGHT_STD, dtype)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(expert, range(E)))
+    layer = dict(
+        w_router=_normal(_rng(seed, _WR), (E, d), WEIGHT_STD, dtype),
+        w_gate_up=w_gu,
+        w_down=w_dn,
+        w_sh_gate_up=None, w_sh_down=None, sh_gate=None,
+    )
+    if Fs > 0:
+        layer["w_sh_gate_up"] = _normal(_rng(seed, _WSGU), (2 * Fs, d), WEIGHT_STD, dtype)
+        layer["w_sh_down"] = _normal(_rng(seed, _WSDN), (d, Fs), WEIGHT_STD, dtype)
+        layer["sh_gate"] = _normal(_rng(seed, _G), (d,), WEIGHT_STD, dtype)
+    return layer
+
+
+def make_x(T: int, d: int, dtype: str, seed: int, row0: int = 0) -> np.ndarray:
+    """Tokens x ~ N(0,1), [T, d].  Rows are drawn in blocks of 256 tokens from
+    per-block streams, so a row's value does not depend on T (a prefix of a
+    longer batch equals the shorter batch) and ``row0`` selects a window."""
+    npdt = np.uint16 if dtype == "bf16" else np.float32
+    out = np.empty((T, d), npdt)
+    B = 256
+    b0, b1 = row0 // B, (row0 + T + B - 1) // B
+
+    def block(b):
+        rows = _normal(_rng(seed, _X, b), (B, d), 1.0, dtype)
+        lo, hi = max(b * B, row0), min((b + 1) * B, row0 + T)
+        out[lo - row0:hi - row0] = rows[lo - b * B:hi - b * B]
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(block, range(b0, b1)))
+    return out
+
+
+def zipf_bias(E: int, s: float, seed: int) -> np.ndarray:
+    """Router bias whose softmax prior is exactly Zipf(s) over a seeded
+    permutation pi of the experts: b[pi(r)] = -s ln r for ranks r = 1..E."""
+    perm = _rng(seed, _BIAS).permutation(E)
+    b = np.empty(E, np.float32)
+    b[perm] = (-s * np.log(np.arange(1, E + 1, dtype=np.float64))).astype(np.float32)
+    return b
+
+
+def hot_bias(E: int, k: int, d: int, n_hot: int, share: float, seed: int):
+    """Router bias +beta on n_hot seeded experts, 0 elsewhere.  beta is the
+    mean-field value at which the hot experts take ``share`` of all
+    assignments when logits are N(0, sigma^2) with sigma = 0.02*sqrt(d) (the
+    spread of x.w for x ~ N(0,1), w ~ N(0, 0.02^2)): each hot expert must be
+    selected with probability k*share/n_hot, so beta sits at the cold
+    experts' selection threshold.  Returns (bias, hot expert ids)."""
+    sigma = WEIGHT_STD * math.sqrt(d)
+    p_hot = k * share / n_hot                     # selection prob. of a hot expert
+    cold_slots = k * (1.0 - share)                # expected cold picks per token
+    p_cold = cold_slots / (E - n_hot)
+    tau = sigma * NormalDist().inv_cdf(1.0 - p_cold)
+    beta = tau - sigma * NormalDist().inv_cdf(1.0 - p_hot)
+    hot = np.sort(_rng(seed, _BIAS).choice(E, n_hot, replace=False))
+    b = np.zeros(E, np.float32)
+    b[hot] = np.float32(beta)
+    return b, hot
+
+
+def make_bias(cfg: MoEConfig) -> Optional[np.ndarray]:
+    if cfg.bias is None:
+        return None
+    if cfg.bias == "zipf":
+        return zipf_bias(cfg.E, 1.2, cfg.seed_b)
+    if cfg.bias == "hot10":
+        return hot_bias(cfg.E, cfg.k, cfg.d, 10, 0.5, cfg.seed_b)[0]
+    raise ValueError(cfg.bias)
+
+
+_layer_cache: dict = {}
+
+
+def layer_for(cfg: MoEConfig) -> dict:
+    key = (cfg.d, cfg.E, cfg.F, cfg.Fs, cfg.dtype, cfg.seed_w)
+    if key not in _layer_cache:
+        _layer_cache.clear()      # keep at most one full-size layer resident
+        _layer_cache[key] = make_layer(cfg.d, cfg.E, cfg.F, cfg.Fs, cfg.dtype, cfg.seed_w)
+    return _layer_cache[key]
+
+
+def make_inputs(cfg: MoEConfig, T: Optional[int] = None) -> dict:
+    """All inputs of one configuration: the layer (shared across configs with
+    the same shapes and weight seed), x and the router bias."""
+    T = cfg.T if T is None else T
+    inp = dict(layer_for(cfg))
+    inp["x"] = make_x(T, cfg.d, cfg.dtype, cfg.seed_x)
+    inp["bias"] = make_bias(cfg)
+    return inp
+
+
+def small_case(T, d, E, k, F, Fs, dtype="bf16", seed=7, bias=None) -> dict:
+    """Inputs at an arbitrary small shape (weights seed ``seed``, x seed+1)."""
+    inp = make_layer(d, E, F, Fs, dtype, seed)
+    inp["x"] = make_x(T, d, dtype, seed + 1)
+    inp["bias"] = bias
+    return inp
