@@ -1,0 +1,147 @@
+/*
+ * moe.h -- C ABI of libmoe: the sparse Mixture-of-Experts feed-forward layer
+ * on one AMD MI355X (gfx950) GPU.
+ *
+ * The layer (Qwen3.8-Flash-Next anatomy page on frontier-model-atlas,
+ * "Decoder microscope", Feed-forward panel; "Expert fan-out"):
+ *   router logits -> softmax -> top-k routed experts -> normalisation of the
+ *   selected weights; one shared expert computed alongside the routed path
+ *   and scaled by its own sigmoid gate.  Every expert, routed or shared, is a
+ *   gated MLP with SiLU (llm-architectures-explained "Qwen3.8-Flash-Next",
+ *   "Every architecture field", ffns.moe.gated; llm-atlas
+ *   "Qwen3.8-Flash-Next", "Raw config fields", hidden_act).
+ *
+ * For token x_t (length d):
+ *   l[t,e]   = x_t . W_r[e] + b[e]                  (binary32, fixed order*)
+ *   idx[t,:] = the k largest l[t,.], descending; equal logits -> lower e
+ *   w[t,j]   = softmax(l[t,.])[idx_j] / sum_j' softmax(l[t,.])[idx_j']
+ *   s[t]     = sigmoid(g . x_t)
+ *   E_e(x)   = W_dn[e] (silu(W_g[e] x) * (W_u[e] x))
+ *   out[t]   = sum_j w[t,j] E_{idx_j}(x_t) + s[t] E_shared(x_t)
+ * (*) the router logit is accumulated in binary32 in one fixed order: 64
+ * partial sums; element kk feeds partial (kk mod 512) div 8; each partial
+ * takes its elements in ascending kk with a fused multiply-add starting at
+ * +0; the partials are then combined by acc[j] += acc[j+s] for
+ * s = 32,16,8,4,2,1; the bias is added last.  This makes topk_idx
+ * reproducible bit for bit.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers owned by the caller (e.g. allocated by
+ *     PyTorch).  The library allocates no device memory and keeps no state
+ *     between calls; work is enqueued on `stream` (a hipStream_t, NULL = the
+ *     default stream) and returns before it completes.
+ *   - Arrays are dense, row-major and 16-byte aligned.  Weights and x are in
+ *     desc->dtype (MOE_BF16: bfloat16; MOE_F32: binary32).  out, topk_w,
+ *     router bias and the shared-gate output are binary32; topk_idx is int32.
+ *   - Layouts: x [T,d]; w_router [E,d]; router_bias [E] (NULL = zeros);
+ *     w_gate_up [E,2F,d], rows 0..F-1 the gate projection (SiLU side), rows
+ *     F..2F-1 the up projection; w_down [E,d,F]; w_sh_gate_up [2Fs,d];
+ *     w_sh_down [d,Fs]; sh_gate [d]; out [T,d]; topk_idx/topk_w [T,k].
+ *   - Argument errors are reported before any GPU work is enqueued.  T == 0
+ *     is a no-op that returns MOE_OK once desc is valid (pointers unread).  A failed launch returns MOE_ERR_HIP;
+ *     a fault inside a kernel surfaces at the caller's next synchronisation.
+ *   - Calls on one stream are ordered.  Calls that may run concurrently must
+ *     use distinct workspaces and outputs.
+ */
+#ifndef SPARSE_MOE_FEED_AMD_MOE_H
+#define SPARSE_MOE_FEED_AMD_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,  /* NULL / negative / out-of-range argument, misalignment */
+    MOE_ERR_UNSUPPORTED = 2,  /* valid layer the kernels do not handle (see moe_desc) */
+    MOE_ERR_WORKSPACE = 3,    /* ws NULL or ws_bytes < moe_workspace_size() */
+    MOE_ERR_HIP = 4           /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Layer shape.  d_model = d, n_experts = E, top_k = k, d_expert = F,
+ * d_shared = Fs (0: no shared expert).
+ * Valid: d, E, F >= 1; 1 <= k <= E; Fs >= 0; dtype MOE_F32 or MOE_BF16.
+ * Supported: k <= 32; E <= 1024; d <= 16384; for MOE_BF16 additionally
+ * d, F and Fs multiples of 64.  Anything valid but outside this returns
+ * MOE_ERR_UNSUPPORTED. */
+typedef struct {
+    int32_t d_model;
+    int32_t n_experts;
+    int32_t top_k;
+    int32_t d_expert;
+    int32_t d_shared;
+    int32_t dtype; /* moe_dtype */
+} moe_desc;
+
+/* Bytes of device workspace a call with T tokens needs (0 on an invalid or
+ * unsupported desc).  The workspace holds the router logits, the routing
+ * histogram and permutation, and the gated-MLP activations h (bf16 for
+ * MOE_BF16); it is scratch, its contents are undefined between calls. */
+size_t moe_workspace_size(const moe_desc *desc, int64_t T);
+
+/* Byte offsets of the workspace regions, for inspection by tests.  Valid
+ * after a call on the same stream has completed.
+ *   logits   float [T, E+1]   router logits, column E = g . x_t
+ *   gate     float [T]        s_t = sigmoid(g . x_t)
+ *   counts   int32 [E+1]      tokens per expert; counts[E] = T (shared)
+ *   offsets  int32 [E+1]      exclusive prefix of counts[0..E-1]
+ *   perm     int32 [T*k]      row r of expert e (offsets[e] <= r < offsets[e+1])
+ *                             holds the pair id t*k+j; rows of one expert are in
+ *                             ascending pair id
+ *   h        [T*k, F]         gated activations of the routed rows (bf16 / f32)
+ *   h_shared [T, Fs]          gated activations of the shared expert */
+typedef struct {
+    size_t logits, gate, counts, offsets, perm, h, h_shared, total;
+} moe_workspace_layout;
+
+moe_status moe_workspace_query(const moe_desc *desc, int64_t T,
+                               moe_workspace_layout *layout);
+
+/* Routing only: router logits, softmax, top-k, normalised weights.
+ * Writes topk_idx, topk_w and, when sh_gate and sh_gate_out are both
+ * non-NULL, sh_gate_out[t] = sigmoid(sh_gate . x_t).  Reads x, w_router,
+ * router_bias, sh_gate. */
+moe_status moe_route(const moe_desc *desc, int64_t T, const void *x,
+                     const void *w_router, const float *router_bias,
+                     const void *sh_gate, int32_t *topk_idx, float *topk_w,
+                     float *sh_gate_out, void *ws, size_t ws_bytes,
+                     void *stream);
+
+/* The whole layer: routing as moe_route, then the routed experts and the
+ * shared expert, combined into out (overwritten, binary32).  With
+ * d_shared == 0 the shared pointers may be NULL and the shared term is
+ * absent.  topk_idx and topk_w are outputs. */
+moe_status moe_forward(const moe_desc *desc, int64_t T, const void *x,
+                       const void *w_router, const float *router_bias,
+                       const void *w_gate_up, const void *w_down,
+                       const void *w_sh_gate_up, const void *w_sh_down,
+                       const void *sh_gate, float *out, int32_t *topk_idx,
+                       float *topk_w, void *ws, size_t ws_bytes, void *stream);
+
+/* The expert stage alone, with the routing given: topk_idx (each entry in
+ * [0,E), entries of one row distinct) and topk_w are INPUTS.  out is
+ * overwritten.  Indices out of range make the result undefined; the kernels
+ * clamp them and never access memory outside the weights. */
+moe_status moe_experts(const moe_desc *desc, int64_t T, const void *x,
+                       const void *w_gate_up, const void *w_down,
+                       const void *w_sh_gate_up, const void *w_sh_down,
+                       const void *sh_gate, const int32_t *topk_idx,
+                       const float *topk_w, float *out, void *ws,
+                       size_t ws_bytes, void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *moe_status_string(moe_status status);
+
+/* Text of the last HIP error seen by this thread ("" if none). */
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_MOE_FEED_AMD_MOE_H */

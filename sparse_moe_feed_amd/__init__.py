@@ -1,0 +1,231 @@
+"""Sparse Mixture-of-Experts feed-forward layer on AMD MI355X (gfx950).
+
+Thin ctypes binding over ``libmoe.so`` (C ABI in ``include/moe.h``).  This
+module only checks and marshals arguments: every step of the layer runs in the
+library's HIP kernels.  PyTorch supplies device memory and the stream.  There
+is no CPU fallback: if the library is missing, every call raises.
+
+The layer (anatomy page on frontier-model-atlas, "Decoder microscope",
+Feed-forward panel): router logits -> softmax -> top-k -> normalised selected
+weights; SwiGLU experts; one shared expert scaled by its own sigmoid gate.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+
+EXPORTED = ("moe_workspace_size", "moe_workspace_query", "moe_route", "moe_forward",
+            "moe_experts", "moe_status_string", "moe_last_error")
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str = ""):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}" + (f" ({detail})" if detail else ""))
+
+
+class moe_desc(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("d_expert", ctypes.c_int32),
+                ("d_shared", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class moe_workspace_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("logits", "gate", "counts", "offsets", "perm", "h", "h_shared", "total")]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libmoe.so.  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m sparse_moe_feed_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    dp = ctypes.POINTER(moe_desc)
+    L.moe_workspace_size.argtypes = [dp, i64]
+    L.moe_workspace_size.restype = sz
+    L.moe_workspace_query.argtypes = [dp, i64, ctypes.POINTER(moe_workspace_layout)]
+    L.moe_route.argtypes = [dp, i64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_forward.argtypes = [dp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_experts.argtypes = [dp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    for f in (L.moe_workspace_query, L.moe_route, L.moe_forward, L.moe_experts):
+        f.restype = ctypes.c_int
+    L.moe_status_string.argtypes = [ctypes.c_int]
+    L.moe_status_string.restype = ctypes.c_char_p
+    L.moe_last_error.argtypes = []
+    L.moe_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(status).decode()
+
+
+@dataclass(frozen=True)
+class Shape:
+    d_model: int
+    n_experts: int
+    top_k: int
+    d_expert: int
+    d_shared: int
+    dtype: torch.dtype
+
+    def desc(self) -> moe_desc:
+        code = {torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}.get(self.dtype)
+        if code is None:
+            raise TypeError(f"unsupported dtype {self.dtype}")
+        return moe_desc(self.d_model, self.n_experts, self.top_k, self.d_expert,
+                        self.d_shared, code)
+
+
+def workspace_size(shape: Shape, T: int) -> int:
+    return int(lib().moe_workspace_size(ctypes.byref(shape.desc()), T))
+
+
+def workspace_layout(shape: Shape, T: int) -> moe_workspace_layout:
+    lay = moe_workspace_layout()
+    st = lib().moe_workspace_query(ctypes.byref(shape.desc()), T, ctypes.byref(lay))
+    if st != MOE_OK:
+        raise MoEError(st, "moe_workspace_query")
+    return lay
+
+
+def alloc_workspace(shape: Shape, T: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(workspace_size(shape, T), 1), dtype=torch.uint8, device=device)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None, shape=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(st: int, where: str):
+    if st != MOE_OK:
+        raise MoEError(st, where, lib().moe_last_error().decode() if st == MOE_ERR_HIP else "")
+
+
+def shape_of(x, w_gate_up, k, w_sh_gate_up=None) -> Shape:
+    E, twoF, d = w_gate_up.shape
+    Fs = 0 if w_sh_gate_up is None else w_sh_gate_up.shape[0] // 2
+    return Shape(d, E, k, twoF // 2, Fs, x.dtype)
+
+
+def route(x, w_router, k, bias=None, sh_gate=None, ws=None):
+    """(topk_idx int32 [T,k], topk_w float32 [T,k], s float32 [T] or None)."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    shape = Shape(d, E, k, 64, 0, x.dtype)
+    _dev(x, "x"), _dev(w_router, "w_router", x.dtype, (E, d))
+    _dev(bias, "router_bias", torch.float32, (E,)), _dev(sh_gate, "sh_gate", x.dtype, (d,))
+    idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    s = torch.empty((T,), dtype=torch.float32, device=x.device) if sh_gate is not None else None
+    ws = alloc_workspace(shape, T, x.device) if ws is None else ws
+    st = lib().moe_route(ctypes.byref(shape.desc()), T, _ptr(x), _ptr(w_router), _ptr(bias),
+                         _ptr(sh_gate), _ptr(idx), _ptr(w), _ptr(s), _ptr(ws), ws.numel(),
+                         _stream())
+    _check(st, "moe_route")
+    return idx, w, s
+
+
+def forward(x, w_router, w_gate_up, w_down, k, w_sh_gate_up=None, w_sh_down=None,
+            sh_gate=None, bias=None, out=None, topk_idx=None, topk_w=None, ws=None):
+    """The whole layer.  Returns (out float32 [T,d], topk_idx, topk_w)."""
+    T, d = x.shape
+    shape = shape_of(x, w_gate_up, k, w_sh_gate_up)
+    E, F, Fs = shape.n_experts, shape.d_expert, shape.d_shared
+    _dev(x, "x"), _dev(w_router, "w_router", x.dtype, (E, d))
+    _dev(w_gate_up, "w_gate_up", x.dtype), _dev(w_down, "w_down", x.dtype, (E, d, F))
+    if Fs:
+        _dev(w_sh_gate_up, "w_sh_gate_up", x.dtype, (2 * Fs, d))
+        _dev(w_sh_down, "w_sh_down", x.dtype, (d, Fs)), _dev(sh_gate, "sh_gate", x.dtype, (d,))
+    _dev(bias, "router_bias", torch.float32, (E,))
+    out = torch.empty((T, d), dtype=torch.float32, device=x.device) if out is None else out
+    topk_idx = torch.empty((T, k), dtype=torch.int32, device=x.device) if topk_idx is None else topk_idx
+    topk_w = torch.empty((T, k), dtype=torch.float32, device=x.device) if topk_w is None else topk_w
+    _dev(out, "out", torch.float32, (T, d)), _dev(topk_idx, "topk_idx", torch.int32, (T, k))
+    _dev(topk_w, "topk_w", torch.float32, (T, k))
+    ws = alloc_workspace(shape, T, x.device) if ws is None else ws
+    st = lib().moe_forward(ctypes.byref(shape.desc()), T, _ptr(x), _ptr(w_router), _ptr(bias),
+                           _ptr(w_gate_up), _ptr(w_down), _ptr(w_sh_gate_up), _ptr(w_sh_down),
+                           _ptr(sh_gate), _ptr(out), _ptr(topk_idx), _ptr(topk_w), _ptr(ws),
+                           ws.numel(), _stream())
+    _check(st, "moe_forward")
+    return out, topk_idx, topk_w
+
+
+def experts(x, w_gate_up, w_down, topk_idx, topk_w, w_sh_gate_up=None, w_sh_down=None,
+            sh_gate=None, out=None, ws=None):
+    """Expert stage with the routing given (topk_idx/topk_w are inputs)."""
+    T, d = x.shape
+    k = topk_idx.shape[1]
+    shape = shape_of(x, w_gate_up, k, w_sh_gate_up)
+    E, F, Fs = shape.n_experts, shape.d_expert, shape.d_shared
+    _dev(x, "x"), _dev(w_gate_up, "w_gate_up", x.dtype), _dev(w_down, "w_down", x.dtype, (E, d, F))
+    _dev(topk_idx, "topk_idx", torch.int32, (T, k)), _dev(topk_w, "topk_w", torch.float32, (T, k))
+    if Fs:
+        _dev(w_sh_gate_up, "w_sh_gate_up", x.dtype, (2 * Fs, d))
+        _dev(w_sh_down, "w_sh_down", x.dtype, (d, Fs)), _dev(sh_gate, "sh_gate", x.dtype, (d,))
+    out = torch.empty((T, d), dtype=torch.float32, device=x.device) if out is None else out
+    _dev(out, "out", torch.float32, (T, d))
+    ws = alloc_workspace(shape, T, x.device) if ws is None else ws
+    st = lib().moe_experts(ctypes.byref(shape.desc()), T, _ptr(x), _ptr(w_gate_up), _ptr(w_down),
+                           _ptr(w_sh_gate_up), _ptr(w_sh_down), _ptr(sh_gate), _ptr(topk_idx),
+                           _ptr(topk_w), _ptr(out), _ptr(ws), ws.numel(), _stream())
+    _check(st, "moe_experts")
+    return out
+
+
+class MoELayer:
+    """Device-resident weights plus a workspace sized for up to ``max_tokens``
+    tokens, so repeated calls allocate nothing but their outputs."""
+
+    def __init__(self, w_router, w_gate_up, w_down, k, w_sh_gate_up=None, w_sh_down=None,
+                 sh_gate=None, bias=None, max_tokens=1):
+        self.w = dict(w_router=w_router, w_gate_up=w_gate_up, w_down=w_down,
+                      w_sh_gate_up=w_sh_gate_up, w_sh_down=w_sh_down, sh_gate=sh_gate, bias=bias)
+        self.k = k
+        self.shape = shape_of(w_router, w_gate_up, k, w_sh_gate_up)
+        self.max_tokens = max_tokens
+        self.ws = alloc_workspace(self.shape, max_tokens, w_router.device)
+
+    def __call__(self, x, out=None, topk_idx=None, topk_w=None):
+        if x.shape[0] > self.max_tokens:
+            raise ValueError("more tokens than the workspace was sized for")
+        w = self.w
+        return forward(x, w["w_router"], w["w_gate_up"], w["w_down"], self.k, w["w_sh_gate_up"],
+                       w["w_sh_down"], w["sh_gate"], w["bias"], out, topk_idx, topk_w, self.ws)

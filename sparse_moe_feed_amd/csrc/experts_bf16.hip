@@ -1,0 +1,234 @@
+// experts_bf16.hip -- grouped SwiGLU experts on MFMA (bfloat16 in, binary32
+// accumulate) with the weighted scatter-combine.
+//
+// Experts are gated MLPs with SiLU (llm-architectures-explained
+// "Qwen3.8-Flash-Next", "Every architecture field", ffns.moe.gated;
+// llm-atlas "Qwen3.8-Flash-Next", "Raw config fields", hidden_act); each token
+// sums its k routed experts weighted by the normalised router weights, plus
+// the shared expert scaled by its sigmoid gate (anatomy page on
+// frontier-model-atlas, "Decoder microscope", Feed-forward panel).
+//
+// Two launches over a tile list built by the permutation step.  A tile is
+// up to BM consecutive permuted rows of one group; group E is the shared
+// expert, whose rows are all tokens in order.
+//   gate/up:  h[r, n] = bf16( silu(x_t . Wg[n]) * (x_t . Wu[n]) )   (t = token of row r)
+//             A rows are gathered from x through the permutation; the block's
+//             B tile stacks 64 gate rows on the matching 64 up rows, so the
+//             SiLU*up product is formed in registers.
+//   down:     out[t, n] += w_r * (h[r] . Wdn[n])   with binary32 atomics; w_r is
+//             the pair's routing weight, or s_t for the shared expert.
+// h is rounded to bfloat16 once; everything else stays binary32.
+#include "moe_device.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+struct GemmArgs {
+    const uint16_t *x;
+    const uint16_t *w;     // gate/up: [E, 2F, d]   down: [E, d, F]
+    const uint16_t *w_sh;  // gate/up: [2Fs, d]     down: [d, Fs]
+    uint16_t *h;           // [T*k, F]
+    uint16_t *h_sh;        // [T, Fs]
+    float *out;            // [T, d]
+    const int32_t *perm, *counts, *offsets, *tile_start, *tile_group;
+    const float *topk_w, *gate;
+    int64_t T;
+    int d, E, k, F, Fs;
+};
+
+constexpr int BM = kGemmBM, BN = 128, BK = 64, LDK = BK + 8;  // LDS row: 144 B, 9 x 16 B
+
+// MODE 0: gate/up (K = d).  MODE 1: down (K = F).
+// 256 threads = 4 waves in a 2 x 2 grid; wave (wm, wn) owns rows
+// [64 wm, 64 wm + 64) and two 32-wide column blocks of B.  Each 32 x 32
+// output block comes from v_mfma_f32_32x32x16_bf16.
+template <int MODE>
+__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
+    __shared__ __align__(16) uint16_t As[2][BM * LDK];
+    __shared__ __align__(16) uint16_t Bs[2][BN * LDK];
+    __shared__ int32_t row_tok[BM];
+    __shared__ float row_w[BM];
+
+    const int tile = blockIdx.x;
+    if (tile >= a.tile_start[a.E + 1]) return;
+    const int g = a.tile_group[tile];
+    const bool shared = g == a.E;
+    const int m_local = (tile - a.tile_start[g]) * BM;
+    int row0, nrows;
+    if (!shared) {
+        row0 = a.offsets[g] + m_local;
+        nrows = min(BM, a.counts[g] - m_local);
+    } else {
+        row0 = m_local;
+        nrows = (int)min<int64_t>(BM, a.T - m_local);
+    }
+    const int Fg = shared ? a.Fs : a.F;            // width of this group's expert
+    const int N = MODE == 0 ? Fg : a.d;            // output columns (gate half for MODE 0)
+    const int K = MODE == 0 ? a.d : Fg;
+    const int n0 = blockIdx.y * (MODE == 0 ? 64 : BN);
+    if (n0 >= N) return;
+
+    const int tid = threadIdx.x;
+    for (int i = tid; i < BM; i += 256) {
+        const int r = min(i, nrows - 1);  // padding rows repeat the last row; never stored
+        int tok;
+        float wgt = 0.f;
+        if (!shared) {
+            const int pair = a.perm[row0 + r];
+            tok = pair / a.k;
+            if (MODE == 1) wgt = a.topk_w[pair];
+        } else {
+            tok = row0 + r;
+            if (MODE == 1) wgt = a.gate[tok];
+        }
+        row_tok[i] = tok;
+        row_w[i] = wgt;
+    }
+    __syncthreads();
+
+    // Global -> register staging: thread owns 16-byte chunk (tid % 8) of rows
+    // tid / 8 + 32 p, p = 0..3, for both A and B.
+    const int lrow = tid >> 3, lchunk = tid & 7;
+    const uint16_t *asrc[4];
+    const uint16_t *bsrc[4];
+    const uint16_t *wbase = shared ? a.w_sh
+                                   : a.w + (int64_t)g * (MODE == 0 ? (int64_t)2 * a.F * a.d
+                                                                   : (int64_t)a.d * a.F);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int r = lrow + 32 * p;
+        if (MODE == 0) {
+            asrc[p] = a.x + (int64_t)row_tok[r] * a.d;
+            const int wrow = r < 64 ? n0 + r : Fg + n0 + (r - 64);
+            bsrc[p] = wbase + (int64_t)wrow * a.d;
+        } else {
+            const int rr = min(r, nrows - 1);
+            asrc[p] = shared ? a.h_sh + (int64_t)(row0 + rr) * a.Fs : a.h + (int64_t)(row0 + rr) * a.F;
+            const int wrow = min(n0 + r, a.d - 1);
+            bsrc[p] = wbase + (int64_t)wrow * Fg;
+        }
+        asrc[p] += lchunk * 8;
+        bsrc[p] += lchunk * 8;
+    }
+
+    uint4 ra[4], rb[4];
+    auto load_tile = [&](int k0) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            ra[p] = *reinterpret_cast<const uint4 *>(asrc[p] + k0);
+            rb[p] = *reinterpret_cast<const uint4 *>(bsrc[p] + k0);
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int off = (lrow + 32 * p) * LDK + lchunk * 8;
+            *reinterpret_cast<uint4 *>(&As[buf][off]) = ra[p];
+            *reinterpret_cast<uint4 *>(&Bs[buf][off]) = rb[p];
+        }
+    };
+
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int brow0 = MODE == 0 ? 32 * wn : 64 * wn;
+    const int brow1 = MODE == 0 ? 64 + 32 * wn : 64 * wn + 32;
+    const int fr = lane & 31, fk = 8 * (lane >> 5);
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    const int nk = K / BK;
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk) load_tile((kt + 1) * BK);
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            bf16x8 af[2], bf[2];
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+                af[mi] = *reinterpret_cast<const bf16x8 *>(
+                    &As[cur][(64 * wm + 32 * mi + fr) * LDK + 16 * ks + fk]);
+            bf[0] = *reinterpret_cast<const bf16x8 *>(&Bs[cur][(brow0 + fr) * LDK + 16 * ks + fk]);
+            bf[1] = *reinterpret_cast<const bf16x8 *>(&Bs[cur][(brow1 + fr) * LDK + 16 * ks + fk]);
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni],
+                                                                          acc[mi][ni], 0, 0, 0);
+        }
+        if (kt + 1 < nk) store_tile(cur ^ 1);
+        __syncthreads();
+    }
+
+    // 32x32 accumulator layout: lane holds column (lane % 32) and rows
+    // 8 (v / 4) + 4 (lane / 32) + (v % 4), v = 0..15.
+    if (MODE == 0) {
+        uint16_t *H = shared ? a.h_sh : a.h;
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = 64 * wm + 32 * mi + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (row < nrows) {
+                    const int col = n0 + 32 * wn + fr;
+                    H[(int64_t)(row0 + row) * Fg + col] =
+                        f32_to_bf16_rne(silu_mul(acc[mi][0][v], acc[mi][1][v]));
+                }
+            }
+    } else {
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int row = 64 * wm + 32 * mi + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    const int col = n0 + (ni ? brow1 : brow0) + fr;
+                    if (row < nrows && col < a.d)
+                        unsafeAtomicAdd(&a.out[(int64_t)row_tok[row] * a.d + col],
+                                        row_w[row] * acc[mi][ni][v]);
+                }
+    }
+}
+
+hipError_t launch_experts_bf16(const Problem &p, hipStream_t s) {
+    GemmArgs a;
+    a.x = static_cast<const uint16_t *>(p.x);
+    a.h = static_cast<uint16_t *>(p.h);
+    a.h_sh = static_cast<uint16_t *>(p.h_shared);
+    a.out = p.out;
+    a.perm = p.perm;
+    a.counts = p.counts;
+    a.offsets = p.offsets;
+    a.tile_start = p.tile_start;
+    a.tile_group = p.tile_group;
+    a.topk_w = p.topk_w;
+    a.gate = p.gate;
+    a.T = p.T;
+    a.d = p.d;
+    a.E = p.E;
+    a.k = p.k;
+    a.F = p.F;
+    a.Fs = p.Fs;
+
+    const int fmax = p.F > p.Fs ? p.F : p.Fs;
+    a.w = static_cast<const uint16_t *>(p.w_gate_up);
+    a.w_sh = static_cast<const uint16_t *>(p.w_sh_gate_up);
+    hipLaunchKernelGGL(grouped_gemm_kernel<0>, dim3(p.max_tiles, fmax / 64), dim3(256), 0, s, a);
+    a.w = static_cast<const uint16_t *>(p.w_down);
+    a.w_sh = static_cast<const uint16_t *>(p.w_sh_down);
+    hipLaunchKernelGGL(grouped_gemm_kernel<1>, dim3(p.max_tiles, (p.d + BN - 1) / BN), dim3(256),
+                       0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

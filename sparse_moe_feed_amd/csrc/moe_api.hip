@@ -1,0 +1,261 @@
+// moe_api.hip -- the C ABI of libmoe: argument checks, workspace plan and
+// the launch sequence of the sparse MoE feed-forward layer.
+//
+// Order of the layer (anatomy page on frontier-model-atlas, "Decoder
+// microscope", Feed-forward panel): router logits, softmax, top-k routed
+// experts, selected-weight normalisation; the shared expert runs alongside
+// and is scaled by its own sigmoid gate.  moe_forward enqueues:
+//   1. router logits + shared-gate column     (router.hip)
+//   2. top-k, weights, gate                   (router.hip)
+//   3. histogram / scan / permutation / tiles (permute.hip)
+//   4. out := 0
+//   5. gate/up grouped GEMM -> h              (experts_*.hip)
+//   6. down grouped GEMM, weighted combine    (experts_*.hip)
+#include "moe.h"
+#include "moe_kernels.h"
+
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+moe_status check_desc(const moe_desc *desc) {
+    if (!desc) return MOE_ERR_INVALID_ARG;
+    const moe_desc &d = *desc;
+    if (d.d_model < 1 || d.n_experts < 1 || d.d_expert < 1 || d.d_shared < 0 || d.top_k < 1 ||
+        d.top_k > d.n_experts)
+        return MOE_ERR_INVALID_ARG;
+    if (d.dtype != MOE_F32 && d.dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+    if (d.top_k > 32 || d.n_experts > 1024 || d.d_model > 16384) return MOE_ERR_UNSUPPORTED;
+    if (d.dtype == MOE_BF16 &&
+        (d.d_model % 64 != 0 || d.d_expert % 64 != 0 || d.d_shared % 64 != 0))
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+// T*(k+1) rows and T*(E+1) logits must stay within int32 indexing of rows.
+moe_status check_T(const moe_desc *desc, int64_t T) {
+    if (T < 0) return MOE_ERR_INVALID_ARG;
+    const int64_t rows = T * (int64_t)(desc->top_k + 1);
+    if (rows > (int64_t)0x7FFFFFFF / 2) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+struct Plan {
+    size_t logits, gate, counts, offsets, tile_start, tile_group, blk, rank, perm, h, h_shared,
+        total;
+    int nblk;
+    int max_tiles;
+};
+
+Plan make_plan(const moe_desc &d, int64_t T) {
+    Plan p;
+    const size_t esize = d.dtype == MOE_BF16 ? 2 : 4;
+    const int64_t pairs = T * d.top_k;
+    p.nblk = (int)((T + moe::kCountBlock - 1) / moe::kCountBlock);
+    p.max_tiles = (int)moe::max_gemm_tiles(T, d.top_k, d.n_experts, moe::kGemmBM, d.d_shared > 0);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align_up(off + bytes);
+        return at;
+    };
+    p.logits = take((size_t)T * (d.n_experts + 1) * sizeof(float));
+    p.gate = take((size_t)T * sizeof(float));
+    p.counts = take((size_t)(d.n_experts + 1) * sizeof(int32_t));
+    p.offsets = take((size_t)(d.n_experts + 1) * sizeof(int32_t));
+    p.tile_start = take((size_t)(d.n_experts + 2) * sizeof(int32_t));
+    p.tile_group = take((size_t)(p.max_tiles + 1) * sizeof(int32_t));
+    p.blk = take((size_t)d.n_experts * p.nblk * sizeof(int32_t));
+    p.rank = take((size_t)pairs * sizeof(int32_t));
+    p.perm = take((size_t)pairs * sizeof(int32_t));
+    p.h = take((size_t)pairs * d.d_expert * esize);
+    p.h_shared = take((size_t)T * d.d_shared * esize);
+    p.total = off;
+    return p;
+}
+
+moe::Problem make_problem(const moe_desc &d, int64_t T, const Plan &pl, void *ws) {
+    moe::Problem p;
+    memset(&p, 0, sizeof p);
+    p.T = T;
+    p.d = d.d_model;
+    p.E = d.n_experts;
+    p.k = d.top_k;
+    p.F = d.d_expert;
+    p.Fs = d.d_shared;
+    p.bf16 = d.dtype == MOE_BF16;
+    char *base = static_cast<char *>(ws);
+    p.logits = reinterpret_cast<float *>(base + pl.logits);
+    p.gate = reinterpret_cast<float *>(base + pl.gate);
+    p.counts = reinterpret_cast<int32_t *>(base + pl.counts);
+    p.offsets = reinterpret_cast<int32_t *>(base + pl.offsets);
+    p.tile_start = reinterpret_cast<int32_t *>(base + pl.tile_start);
+    p.tile_group = reinterpret_cast<int32_t *>(base + pl.tile_group);
+    p.blk = reinterpret_cast<int32_t *>(base + pl.blk);
+    p.rank = reinterpret_cast<int32_t *>(base + pl.rank);
+    p.perm = reinterpret_cast<int32_t *>(base + pl.perm);
+    p.h = base + pl.h;
+    p.h_shared = base + pl.h_shared;
+    p.nblk = pl.nblk;
+    p.max_tiles = pl.max_tiles;
+    return p;
+}
+
+moe_status hip_status(hipError_t err) {
+    if (err == hipSuccess) return MOE_OK;
+    g_last_error = hipGetErrorString(err);
+    return MOE_ERR_HIP;
+}
+
+bool all_aligned(std::initializer_list<const void *> ptrs) {
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return false;
+    return true;
+}
+
+// Checks shared by the entry points.  Required pointers are listed in `req`.
+moe_status check_common(const moe_desc *desc, int64_t T, std::initializer_list<const void *> req,
+                        std::initializer_list<const void *> opt, void *ws, size_t ws_bytes) {
+    moe_status st = check_desc(desc);
+    if (st != MOE_OK) return st;
+    st = check_T(desc, T);
+    if (st != MOE_OK || T == 0) return st;
+    for (const void *p : req)
+        if (!p) return MOE_ERR_INVALID_ARG;
+    if (!all_aligned(req) || !all_aligned(opt)) return MOE_ERR_INVALID_ARG;
+    if (!ws || !aligned16(ws)) return MOE_ERR_WORKSPACE;
+    if (ws_bytes < make_plan(*desc, T).total) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+moe_status run_experts(const moe::Problem &p, hipStream_t s) {
+    hipError_t err = moe::launch_permute(p, moe::kGemmBM, s);
+    if (err == hipSuccess) err = moe::launch_zero(p.out, p.T * p.d, s);
+    if (err == hipSuccess) err = p.bf16 ? moe::launch_experts_bf16(p, s) : moe::launch_experts_f32(p, s);
+    return hip_status(err);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_desc *desc, int64_t T) {
+    if (check_desc(desc) != MOE_OK || check_T(desc, T) != MOE_OK) return 0;
+    return make_plan(*desc, T).total;
+}
+
+moe_status moe_workspace_query(const moe_desc *desc, int64_t T, moe_workspace_layout *layout) {
+    moe_status st = check_desc(desc);
+    if (st != MOE_OK) return st;
+    st = check_T(desc, T);
+    if (st != MOE_OK) return st;
+    if (!layout) return MOE_ERR_INVALID_ARG;
+    const Plan p = make_plan(*desc, T);
+    layout->logits = p.logits;
+    layout->gate = p.gate;
+    layout->counts = p.counts;
+    layout->offsets = p.offsets;
+    layout->perm = p.perm;
+    layout->h = p.h;
+    layout->h_shared = p.h_shared;
+    layout->total = p.total;
+    return MOE_OK;
+}
+
+moe_status moe_route(const moe_desc *desc, int64_t T, const void *x, const void *w_router,
+                     const float *router_bias, const void *sh_gate, int32_t *topk_idx,
+                     float *topk_w, float *sh_gate_out, void *ws, size_t ws_bytes, void *stream) {
+    moe_status st = check_common(desc, T, {x, w_router, topk_idx, topk_w},
+                                 {router_bias, sh_gate, sh_gate_out}, ws, ws_bytes);
+    if (st != MOE_OK || T == 0) return st;
+    const Plan pl = make_plan(*desc, T);
+    moe::Problem p = make_problem(*desc, T, pl, ws);
+    p.x = x;
+    p.w_router = w_router;
+    p.router_bias = router_bias;
+    // The gate column is computed only when both the vector and an output exist.
+    p.sh_gate = (sh_gate && sh_gate_out) ? sh_gate : nullptr;
+    p.topk_idx = topk_idx;
+    p.topk_w = topk_w;
+    return hip_status(moe::launch_router(p, sh_gate_out, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_forward(const moe_desc *desc, int64_t T, const void *x, const void *w_router,
+                       const float *router_bias, const void *w_gate_up, const void *w_down,
+                       const void *w_sh_gate_up, const void *w_sh_down, const void *sh_gate,
+                       float *out, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+                       void *stream) {
+    moe_status st = check_common(desc, T, {x, w_router, w_gate_up, w_down, out, topk_idx, topk_w},
+                                 {router_bias, w_sh_gate_up, w_sh_down, sh_gate}, ws, ws_bytes);
+    if (st != MOE_OK || T == 0) return st;
+    if (desc->d_shared > 0 && (!w_sh_gate_up || !w_sh_down || !sh_gate)) return MOE_ERR_INVALID_ARG;
+    const Plan pl = make_plan(*desc, T);
+    moe::Problem p = make_problem(*desc, T, pl, ws);
+    p.x = x;
+    p.w_router = w_router;
+    p.router_bias = router_bias;
+    p.w_gate_up = w_gate_up;
+    p.w_down = w_down;
+    p.w_sh_gate_up = w_sh_gate_up;
+    p.w_sh_down = w_sh_down;
+    p.sh_gate = desc->d_shared > 0 ? sh_gate : nullptr;
+    p.out = out;
+    p.topk_idx = topk_idx;
+    p.topk_w = topk_w;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = hip_status(moe::launch_router(p, nullptr, s));
+    if (st != MOE_OK) return st;
+    return run_experts(p, s);
+}
+
+moe_status moe_experts(const moe_desc *desc, int64_t T, const void *x, const void *w_gate_up,
+                       const void *w_down, const void *w_sh_gate_up, const void *w_sh_down,
+                       const void *sh_gate, const int32_t *topk_idx, const float *topk_w,
+                       float *out, void *ws, size_t ws_bytes, void *stream) {
+    moe_status st = check_common(desc, T, {x, w_gate_up, w_down, topk_idx, topk_w, out},
+                                 {w_sh_gate_up, w_sh_down, sh_gate}, ws, ws_bytes);
+    if (st != MOE_OK || T == 0) return st;
+    if (desc->d_shared > 0 && (!w_sh_gate_up || !w_sh_down || !sh_gate)) return MOE_ERR_INVALID_ARG;
+    const Plan pl = make_plan(*desc, T);
+    moe::Problem p = make_problem(*desc, T, pl, ws);
+    p.x = x;
+    p.w_gate_up = w_gate_up;
+    p.w_down = w_down;
+    p.w_sh_gate_up = w_sh_gate_up;
+    p.w_sh_down = w_sh_down;
+    p.sh_gate = sh_gate;
+    p.out = out;
+    p.topk_idx = const_cast<int32_t *>(topk_idx);
+    p.topk_w = const_cast<float *>(topk_w);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p.Fs > 0) {
+        st = hip_status(moe::launch_shared_gate(p, s));
+        if (st != MOE_OK) return st;
+    }
+    return run_experts(p, s);
+}
+
+const char *moe_status_string(moe_status status) {
+    switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: layer shape not supported";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP runtime error";
+    }
+    return "unknown moe_status";
+}
+
+const char *moe_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// moe_kernels.h -- host-side launchers of the libmoe kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Everything a launch needs to know about one call.  Pointers are device
+// pointers; `esize` is the byte size of a weight/activation element.
+struct Problem {
+    int64_t T;
+    int d, E, k, F, Fs;
+    bool bf16;
+    // inputs
+    const void *x, *w_router, *w_gate_up, *w_down, *w_sh_gate_up, *w_sh_down, *sh_gate;
+    const float *router_bias;
+    // outputs / routing
+    float *out;
+    int32_t *topk_idx;
+    float *topk_w;
+    // workspace regions
+    float *logits;      // [T, E+1]
+    float *gate;        // [T]
+    int32_t *counts;    // [E+1]
+    int32_t *offsets;   // [E+1]
+    int32_t *tile_start;// [E+2]
+    int32_t *tile_group;// [max_tiles] group (expert, or E = shared) of each GEMM tile
+    int max_tiles;      // upper bound on GEMM tiles for the tile height in use
+    int32_t *blk;       // [E, nblk]
+    int32_t *rank;      // [T*k]
+    int32_t *perm;      // [T*k]
+    void *h;            // [T*k, F]
+    void *h_shared;     // [T, Fs]
+    int nblk;           // ceil(T / kCountBlock)
+};
+
+constexpr int kCountBlock = 256;     // tokens per histogram block
+constexpr int kGemmBM = 128;         // rows per grouped-GEMM tile (MFMA path)
+
+// Upper bound on sum_e ceil(c_e / bm) + ceil(T / bm) over any routing with
+// sum_e c_e = T*k: each non-empty expert adds at most one partial tile.
+inline int64_t max_gemm_tiles(int64_t T, int k, int E, int bm, bool shared) {
+    const int64_t pairs = T * k;
+    const int64_t routed = (pairs < E ? pairs : E) + pairs / bm;
+    return routed + (shared ? (T + bm - 1) / bm : 0);
+}
+
+// Router: logits (canonical binary32 order) then top-k / weights / gate.
+hipError_t launch_router(const Problem &p, float *sh_gate_user, hipStream_t s);
+// Shared gate alone (used when the routing is given).
+hipError_t launch_shared_gate(const Problem &p, hipStream_t s);
+// Histogram, scan, stable permutation and GEMM tile map for tile height bm.
+hipError_t launch_permute(const Problem &p, int bm, hipStream_t s);
+// out := 0
+hipError_t launch_zero(float *out, int64_t n, hipStream_t s);
+// Expert stage for bfloat16 (MFMA) and binary32 (plain FMA) layers.
+hipError_t launch_experts_bf16(const Problem &p, hipStream_t s);
+hipError_t launch_experts_f32(const Problem &p, hipStream_t s);
+
+}  // namespace moe

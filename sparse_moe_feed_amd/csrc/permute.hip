@@ -1,0 +1,174 @@
+// permute.hip -- per-expert histogram, prefix scan and stable token
+// permutation, plus the tile map of the grouped GEMMs.
+//
+// After routing every token t holds k (token, slot) pairs, pair id t*k+j,
+// each naming one expert.  The expert GEMMs want the pairs of one expert in
+// consecutive rows.  Row r of expert e lies in [offsets[e], offsets[e]+counts[e])
+// and rows of one expert are in ascending pair id, so the permutation is
+// deterministic (no atomics decide an order):
+//   count:   blocks of 256 tokens set one bit per (expert, token) in LDS;
+//            a pair's rank inside its block is a popcount of the lower bits;
+//   scan:    per expert, exclusive prefix of the block counts; across experts,
+//            exclusive prefix of the totals (offsets) and of the tile counts;
+//   scatter: perm[offsets[e] + block_base[e] + rank] = pair id.
+// Every row a block reserves is written by some pair, so perm never holds
+// stale entries, even when a routing given from outside repeats an expert
+// within one token (that pair's copies then share one row).
+#include "moe_device.h"
+#include "moe_kernels.h"
+
+#include <algorithm>
+
+namespace moe {
+
+__device__ __forceinline__ int clamp_expert(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
+
+constexpr int kWords = kCountBlock / 32;
+
+__global__ __launch_bounds__(kCountBlock) void route_count_kernel(
+    const int32_t *__restrict__ topk_idx, int64_t ntok, int k, int E, int nblk,
+    int32_t *__restrict__ rank, int32_t *__restrict__ blk) {
+    extern __shared__ uint32_t bits[];  // [E][kWords]
+    for (int i = threadIdx.x; i < E * kWords; i += kCountBlock) bits[i] = 0;
+    __syncthreads();
+    const int64_t t = (int64_t)blockIdx.x * kCountBlock + threadIdx.x;
+    const bool valid = t < ntok;
+    const int word = threadIdx.x >> 5;
+    const uint32_t bit = 1u << (threadIdx.x & 31);
+    if (valid)
+        for (int j = 0; j < k; ++j)
+            atomicOr(&bits[clamp_expert(topk_idx[t * k + j], E) * kWords + word], bit);
+    __syncthreads();
+    if (valid)
+        for (int j = 0; j < k; ++j) {
+            const uint32_t *b = bits + clamp_expert(topk_idx[t * k + j], E) * kWords;
+            int r = __popc(b[word] & (bit - 1u));
+            for (int w = 0; w < word; ++w) r += __popc(b[w]);
+            rank[t * k + j] = r;
+        }
+    for (int e = threadIdx.x; e < E; e += kCountBlock) {
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < kWords; ++w) c += __popc(bits[e * kWords + w]);
+        blk[(int64_t)e * nblk + blockIdx.x] = c;
+    }
+}
+
+// Block-wide exclusive scan of one int per thread (1024 threads).
+__device__ int block_exclusive_scan(int v, int *total) {
+    __shared__ int warp_sums[16];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+    for (int o = 1; o < 64; o <<= 1) {
+        int n = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += n;
+    }
+    if (lane == 63) warp_sums[wave] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+    for (int w = 0; w < 16; ++w) {
+        if (w < wave) before += warp_sums[w];
+        all += warp_sums[w];
+    }
+    __syncthreads();
+    *total = all;
+    return before + incl - v;
+}
+
+// One block of 1024 threads; thread e owns expert e (E <= 1024).
+__global__ __launch_bounds__(1024) void route_scan_kernel(int32_t *__restrict__ blk, int nblk,
+                                                          int E, int64_t ntok, int bm,
+                                                          int has_shared,
+                                                          int32_t *__restrict__ counts,
+                                                          int32_t *__restrict__ offsets,
+                                                          int32_t *__restrict__ tile_start,
+                                                          int32_t *__restrict__ tile_group) {
+    const int e = threadIdx.x;
+    int total = 0;
+    if (e < E) {
+        int32_t *col = blk + (int64_t)e * nblk;
+        int b = 0;
+        for (; b + 8 <= nblk; b += 8) {
+            int c[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) c[i] = col[b + i];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                col[b + i] = total;
+                total += c[i];
+            }
+        }
+        for (; b < nblk; ++b) {
+            int c = col[b];
+            col[b] = total;
+            total += c;
+        }
+        counts[e] = total;
+    }
+    const int tiles = e < E ? (total + bm - 1) / bm : 0;
+    int all_rows, all_tiles;
+    const int off = block_exclusive_scan(e < E ? total : 0, &all_rows);
+    const int ts = block_exclusive_scan(tiles, &all_tiles);
+    if (e < E) {
+        offsets[e] = off;
+        tile_start[e] = ts;
+        for (int i = 0; i < tiles; ++i) tile_group[ts + i] = e;
+    }
+    if (e == 0) {
+        offsets[E] = all_rows;
+        counts[E] = (int)ntok;
+        tile_start[E] = all_tiles;
+        tile_start[E + 1] = all_tiles + (has_shared ? (int)((ntok + bm - 1) / bm) : 0);
+    }
+    if (has_shared) {
+        const int shared_tiles = (int)((ntok + bm - 1) / bm);
+        for (int i = threadIdx.x; i < shared_tiles; i += 1024) tile_group[all_tiles + i] = E;
+    }
+}
+
+__global__ __launch_bounds__(kCountBlock) void route_scatter_kernel(
+    const int32_t *__restrict__ topk_idx, int64_t ntok, int k, int E, int nblk,
+    const int32_t *__restrict__ rank, const int32_t *__restrict__ blk,
+    const int32_t *__restrict__ offsets, int32_t *__restrict__ perm) {
+    const int64_t t = (int64_t)blockIdx.x * kCountBlock + threadIdx.x;
+    if (t >= ntok) return;
+    for (int j = 0; j < k; ++j) {
+        const int e = clamp_expert(topk_idx[t * k + j], E);
+        const int pos = offsets[e] + blk[(int64_t)e * nblk + blockIdx.x] + rank[t * k + j];
+        perm[pos] = (int32_t)(t * k + j);
+    }
+}
+
+hipError_t launch_permute(const Problem &p, int bm, hipStream_t s) {
+    const size_t lds = (size_t)p.E * kWords * sizeof(uint32_t);
+    hipLaunchKernelGGL(route_count_kernel, dim3(p.nblk), dim3(kCountBlock), lds, s, p.topk_idx,
+                       p.T, p.k, p.E, p.nblk, p.rank, p.blk);
+    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, s, p.blk, p.nblk, p.E, p.T, bm,
+                       p.Fs > 0 ? 1 : 0, p.counts, p.offsets, p.tile_start, p.tile_group);
+    hipLaunchKernelGGL(route_scatter_kernel, dim3(p.nblk), dim3(kCountBlock), 0, s, p.topk_idx,
+                       p.T, p.k, p.E, p.nblk, p.rank, p.blk, p.offsets, p.perm);
+    return hipGetLastError();
+}
+
+__global__ void zero_kernel(float4 *__restrict__ out, int64_t n4) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+         i += (int64_t)gridDim.x * blockDim.x)
+        out[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+__global__ void zero_tail_kernel(float *__restrict__ out, int64_t from, int64_t n) {
+    int64_t i = from + threadIdx.x;
+    if (i < n) out[i] = 0.f;
+}
+
+hipError_t launch_zero(float *out, int64_t n, hipStream_t s) {
+    const int64_t n4 = n / 4;
+    if (n4 > 0) {
+        const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 8192);
+        hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                           reinterpret_cast<float4 *>(out), n4);
+    }
+    if (n % 4) hipLaunchKernelGGL(zero_tail_kernel, dim3(1), dim3(4), 0, s, out, n4 * 4, n);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,241 @@
+// router.hip -- router logits, top-k selection, normalised weights and the
+// shared-expert gate.
+//
+// The layer's first four steps (Qwen3.8-Flash-Next anatomy page on
+// frontier-model-atlas, "Decoder microscope", Feed-forward panel): router
+// logits, softmax, top-k routed experts, normalisation of the selected
+// weights; plus the shared expert's own sigmoid gate.
+//
+// Logits are accumulated in binary32 in a fixed order so that the integer
+// top-k decision is reproducible bit for bit: 64 partial sums, element kk
+// feeds partial (kk mod 512) div 8, each partial folds its elements in
+// ascending kk with one fused multiply-add, partials are combined by
+// acc[j] += acc[j+s] for s = 32..1, the bias is added last.  On a wave64 this
+// is lane j holding partial j and reading 8 consecutive elements per 512-wide
+// chunk: one coalesced 16-byte load per lane.
+//
+// The selected weights use the identity softmax(l)_i / sum_sel softmax(l) =
+// exp(l_i - l_max) / sum_sel exp(l_j - l_max): the full softmax denominator
+// cancels, so only the k selected logits are needed.
+#include "moe_device.h"
+#include "moe_kernels.h"
+
+#include <math.h>
+
+#pragma clang fp contract(off)
+
+namespace moe {
+
+// Rows 0..E-1 of the extended router matrix are W_r, row E is the shared gate
+// vector g (absent when g == nullptr).  Block (x, y) owns tokens
+// [TT x, TT x + TT) and rows [16 y, 16 y + 16); each wave owns 4 rows.  The
+// block's token rows are staged in LDS.
+template <typename T, int TT>
+__global__ __launch_bounds__(256) void router_logits_kernel(
+    const T *__restrict__ x, const T *__restrict__ w_router, const T *__restrict__ g,
+    const float *__restrict__ bias, float *__restrict__ logits, int64_t ntok, int d, int E) {
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    T *xs = reinterpret_cast<T *>(smem_raw);  // [TT][d]
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t t0 = (int64_t)blockIdx.x * TT;
+    const int ntt = (int)min<int64_t>(TT, ntok - t0);
+
+    if ((d * (int)sizeof(T)) % 16 == 0) {
+        // whole rows are 16-byte multiples: copy the contiguous [ntt, d] slab
+        const int per_row = d * (int)sizeof(T) / 16;
+        const uint4 *src = reinterpret_cast<const uint4 *>(x + t0 * d);
+        uint4 *dst = reinterpret_cast<uint4 *>(xs);
+        for (int i = threadIdx.x; i < TT * per_row; i += 256)
+            dst[i] = i < ntt * per_row ? src[i] : make_uint4(0, 0, 0, 0);
+    } else {
+        for (int i = threadIdx.x; i < TT * d; i += 256) {
+            int tt = i / d;
+            xs[i] = tt < ntt ? x[(t0 + tt) * d + (i - tt * d)] : T(0);
+        }
+    }
+    __syncthreads();
+
+    const bool vec = (d % 8) == 0;
+    for (int rr = 0; rr < 4; ++rr) {
+        const int row = blockIdx.y * 16 + wave * 4 + rr;
+        if (row > E || (row == E && g == nullptr)) break;
+        const T *wrow = row < E ? w_router + (int64_t)row * d : g;
+        float acc[TT];
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) acc[tt] = 0.0f;
+        for (int chunk = 0; chunk < d; chunk += 512) {
+            const int kk0 = chunk + 8 * lane;
+            if (kk0 >= d) continue;
+            float wv[8];
+            if (vec) {
+                load8(wrow + kk0, wv);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) wv[q] = kk0 + q < d ? to_f32(wrow[kk0 + q]) : 0.0f;
+            }
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt) {
+                float xv[8];
+                if (vec) {
+                    load8(xs + tt * d + kk0, xv);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+                        xv[q] = kk0 + q < d ? to_f32(xs[tt * d + kk0 + q]) : 0.0f;
+                }
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    if (kk0 + q < d) acc[tt] = __builtin_fmaf(xv[q], wv[q], acc[tt]);
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+            float a = acc[tt];
+            for (int s = 32; s >= 1; s >>= 1) {
+                float o = __shfl_down(a, s, kWave);
+                a = a + o;
+            }
+            acc[tt] = a;
+        }
+        if (lane == 0) {
+            const float b = (row < E && bias) ? bias[row] : 0.0f;
+            for (int tt = 0; tt < ntt; ++tt)
+                logits[(t0 + tt) * (E + 1) + row] = acc[tt] + b;
+        }
+    }
+}
+
+// One wave per token: top-k by (logit desc, expert asc), weights, gate.
+// Lane L holds the logits of experts L, L+64, ..., so a lane's candidates
+// are already in ascending expert order.
+template <int NV>
+__global__ __launch_bounds__(256) void router_select_kernel(
+    const float *__restrict__ logits, int64_t ntok, int E, int k, int has_gate,
+    int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, float *__restrict__ gate,
+    float *__restrict__ gate_user) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= ntok) return;
+    const float *l = logits + t * (E + 1);
+
+    float v[NV];
+    uint32_t removed = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = lane + 64 * i;
+        float val = e < E ? l[e] : -INFINITY;
+        v[i] = (val == val) ? val : -INFINITY;  // NaN orders as -inf
+        if (e >= E) removed |= 1u << i;
+    }
+
+    float my_l = 0.0f;
+    int my_e = 0;
+    for (int j = 0; j < k; ++j) {
+        float bv = -INFINITY;
+        int be = 0x7FFFFFFF;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int e = lane + 64 * i;
+            if (!((removed >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < be))) {
+                bv = v[i];
+                be = e;
+            }
+        }
+        for (int o = 32; o >= 1; o >>= 1) {
+            const float ov = __shfl_xor(bv, o, kWave);
+            const int oe = __shfl_xor(be, o, kWave);
+            if (ov > bv || (ov == bv && oe < be)) {
+                bv = ov;
+                be = oe;
+            }
+        }
+        if ((be & 63) == lane) removed |= 1u << (be >> 6);
+        if (lane == j) {
+            my_l = bv;
+            my_e = be;
+        }
+    }
+    const float lmax = __shfl(my_l, 0, kWave);
+    const float ex = lane < k ? expf(my_l - lmax) : 0.0f;
+    const float z = wave_sum(ex);
+    if (lane < k) {
+        topk_idx[t * k + lane] = my_e;
+        topk_w[t * k + lane] = ex / z;
+    }
+    if (has_gate && lane == 0) {
+        const float s = 1.0f / (1.0f + expf(-l[E]));
+        gate[t] = s;
+        if (gate_user) gate_user[t] = s;
+    }
+}
+
+// s_t = sigmoid(g . x_t): one wave per token (routing-given entry point).
+template <typename T>
+__global__ __launch_bounds__(256) void shared_gate_kernel(const T *__restrict__ x,
+                                                          const T *__restrict__ g,
+                                                          float *__restrict__ gate,
+                                                          int64_t ntok, int d) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= ntok) return;
+    float a = 0.0f;
+    for (int kk = lane; kk < d; kk += 64) a += to_f32(x[t * d + kk]) * to_f32(g[kk]);
+    a = wave_sum(a);
+    if (lane == 0) gate[t] = 1.0f / (1.0f + expf(-a));
+}
+
+template <typename T>
+static hipError_t launch_logits(const Problem &p, hipStream_t s) {
+    const size_t row_bytes = (size_t)p.d * sizeof(T);
+    const dim3 block(256);
+    const unsigned row_groups = (unsigned)((p.E + 1 + 15) / 16);
+    const T *x = static_cast<const T *>(p.x);
+    const T *wr = static_cast<const T *>(p.w_router);
+    const T *g = static_cast<const T *>(p.sh_gate);
+#define MOE_LOGITS(TT)                                                                       \
+    do {                                                                                     \
+        dim3 gr((unsigned)((p.T + TT - 1) / TT), row_groups);                                \
+        hipLaunchKernelGGL((router_logits_kernel<T, TT>), gr, block, TT * row_bytes, s, x,   \
+                           wr, g, p.router_bias, p.logits, p.T, p.d, p.E);                   \
+    } while (0)
+    if (8 * row_bytes <= 65536) MOE_LOGITS(8);
+    else if (4 * row_bytes <= 65536) MOE_LOGITS(4);
+    else if (2 * row_bytes <= 65536) MOE_LOGITS(2);
+    else MOE_LOGITS(1);
+#undef MOE_LOGITS
+    return hipGetLastError();
+}
+
+hipError_t launch_router(const Problem &p, float *sh_gate_user, hipStream_t s) {
+    hipError_t err = p.bf16 ? launch_logits<uint16_t>(p, s) : launch_logits<float>(p, s);
+    if (err != hipSuccess) return err;
+    const int nv = (p.E + 63) / 64;
+    const dim3 grid((unsigned)((p.T + 3) / 4)), block(256);
+    const int has_gate = p.sh_gate != nullptr;
+#define MOE_SELECT(NV)                                                                        \
+    hipLaunchKernelGGL((router_select_kernel<NV>), grid, block, 0, s, p.logits, p.T, p.E, p.k, \
+                       has_gate, p.topk_idx, p.topk_w, p.gate, sh_gate_user)
+    if (nv <= 1) MOE_SELECT(1);
+    else if (nv <= 2) MOE_SELECT(2);
+    else if (nv <= 4) MOE_SELECT(4);
+    else if (nv <= 8) MOE_SELECT(8);
+    else MOE_SELECT(16);
+#undef MOE_SELECT
+    return hipGetLastError();
+}
+
+hipError_t launch_shared_gate(const Problem &p, hipStream_t s) {
+    const dim3 grid((unsigned)((p.T + 3) / 4)), block(256);
+    if (p.bf16)
+        hipLaunchKernelGGL((shared_gate_kernel<uint16_t>), grid, block, 0, s,
+                           static_cast<const uint16_t *>(p.x),
+                           static_cast<const uint16_t *>(p.sh_gate), p.gate, p.T, p.d);
+    else
+        hipLaunchKernelGGL((shared_gate_kernel<float>), grid, block, 0, s,
+                           static_cast<const float *>(p.x), static_cast<const float *>(p.sh_gate),
+                           p.gate, p.T, p.d);
+    return hipGetLastError();
+}
+
+}  // namespace moe

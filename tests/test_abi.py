@@ -1,0 +1,140 @@
+"""The C ABI without a GPU: the library loads, exports what include/moe.h
+declares, and rejects bad arguments before any GPU work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_moe_feed_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(moe.LIB_PATH):
+        from sparse_moe_feed_amd import build
+        build.build()
+    return moe.lib()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert names == set(moe.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def desc(d=256, E=16, k=4, F=128, Fs=64, dtype=moe.MOE_BF16):
+    return moe.moe_desc(d, E, k, F, Fs, dtype)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(d=0), dict(E=0), dict(k=0), dict(k=17), dict(F=0), dict(Fs=-1), dict(dtype=7)])
+def test_invalid_desc(L, bad):
+    D = desc(**bad)
+    assert L.moe_workspace_size(ctypes.byref(D), 10) == 0
+    lay = moe.moe_workspace_layout()
+    assert L.moe_workspace_query(ctypes.byref(D), 10, ctypes.byref(lay)) == moe.MOE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad", [
+    dict(k=33, E=64), dict(E=2048, k=4), dict(d=100), dict(F=96), dict(Fs=32), dict(d=32768)])
+def test_unsupported_desc(L, bad):
+    D = desc(**bad)
+    lay = moe.moe_workspace_layout()
+    assert L.moe_workspace_query(ctypes.byref(D), 10, ctypes.byref(lay)) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_fp32_accepts_any_width(L):
+    D = desc(d=100, F=33, Fs=7, dtype=moe.MOE_F32)
+    assert L.moe_workspace_size(ctypes.byref(D), 10) > 0
+
+
+def test_workspace_grows_with_T_and_layout_is_consistent(L):
+    D = desc()
+    sizes = [L.moe_workspace_size(ctypes.byref(D), T) for T in (1, 10, 1000)]
+    assert sizes[0] < sizes[1] < sizes[2]
+    lay = moe.moe_workspace_layout()
+    assert L.moe_workspace_query(ctypes.byref(D), 1000, ctypes.byref(lay)) == moe.MOE_OK
+    assert lay.total == sizes[2]
+    offs = [lay.logits, lay.gate, lay.counts, lay.offsets, lay.perm, lay.h, lay.h_shared]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert lay.h_shared + 1000 * 64 * 2 <= lay.total
+    assert lay.perm + 1000 * 4 * 4 <= lay.h
+
+
+FAKE = 0x10000  # never dereferenced: every case fails validation first
+
+
+def call_forward(L, D, T, ptrs=None, ws=FAKE, ws_bytes=1 << 40):
+    p = dict(x=FAKE, wr=FAKE, b=None, gu=FAKE, dn=FAKE, sgu=FAKE, sdn=FAKE, g=FAKE, out=FAKE,
+             idx=FAKE, w=FAKE)
+    p.update(ptrs or {})
+    v = lambda a: None if a is None else ctypes.c_void_p(a)
+    return L.moe_forward(ctypes.byref(D), T, v(p["x"]), v(p["wr"]), v(p["b"]), v(p["gu"]),
+                         v(p["dn"]), v(p["sgu"]), v(p["sdn"]), v(p["g"]), v(p["out"]),
+                         v(p["idx"]), v(p["w"]), v(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("missing", ["x", "wr", "gu", "dn", "out", "idx", "w", "sgu", "sdn", "g"])
+def test_null_required_pointer(L, missing):
+    assert call_forward(L, desc(), 8, {missing: None}) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_shared_pointers_optional_without_shared_expert(L):
+    D = desc(Fs=0)
+    # all pointers fine, workspace too small -> reaches the workspace check
+    assert call_forward(L, D, 8, {"sgu": None, "sdn": None, "g": None}, ws_bytes=16) == \
+        moe.MOE_ERR_WORKSPACE
+
+
+def test_misaligned_pointer(L):
+    assert call_forward(L, desc(), 8, {"x": FAKE + 2}) == moe.MOE_ERR_INVALID_ARG
+    assert call_forward(L, desc(), 8, {"b": FAKE + 4}) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_negative_T_and_workspace(L):
+    D = desc()
+    assert call_forward(L, D, -1) == moe.MOE_ERR_INVALID_ARG
+    assert call_forward(L, D, 8, ws=None) == moe.MOE_ERR_WORKSPACE
+    need = L.moe_workspace_size(ctypes.byref(D), 8)
+    assert call_forward(L, D, 8, ws_bytes=need - 1) == moe.MOE_ERR_WORKSPACE
+
+
+def test_zero_tokens_is_noop(L):
+    assert call_forward(L, desc(), 0, ws=None, ws_bytes=0) == moe.MOE_OK
+    assert call_forward(L, desc(), 0, {"x": None, "out": None}, ws=None, ws_bytes=0) == moe.MOE_OK
+
+
+def test_route_and_experts_validate(L):
+    D = desc()
+    v = ctypes.c_void_p
+    assert L.moe_route(ctypes.byref(D), 8, None, v(FAKE), None, None, v(FAKE), v(FAKE), None,
+                       v(FAKE), 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_route(ctypes.byref(D), 0, v(FAKE), v(FAKE), None, None, v(FAKE), v(FAKE), None,
+                       None, 0, None) == moe.MOE_OK
+    assert L.moe_experts(ctypes.byref(D), 8, v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE),
+                         None, v(FAKE), v(FAKE), v(FAKE), 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_experts(ctypes.byref(D), 8, v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE),
+                         v(FAKE), v(FAKE), v(FAKE), v(FAKE), 16, None) == moe.MOE_ERR_WORKSPACE
+
+
+def test_status_strings(L):
+    for st in range(5):
+        assert moe.status_string(st).startswith("MOE_")
+    assert "unknown" in moe.status_string(99)
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        moe.route(x, torch.zeros(8, 64, dtype=torch.bfloat16), 2)

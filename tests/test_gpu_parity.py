@@ -1,0 +1,218 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+topk_idx must match bit for bit; topk_w and the shared gate within 1e-5;
+out within 2e-2 x RMS(oracle out) (bfloat16 weights and activations, binary32
+accumulation, h rounded to bfloat16 once).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_moe_feed_amd as moe
+import workloads as W
+from gpu_util import GATE_TOL, W_TOL, announce, assert_out, rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+SH = ("w_sh_gate_up", "w_sh_down", "sh_gate")
+
+
+def gpu_forward(inp, k):
+    args = [to_dev(inp[n]) for n in ("x", "w_router", "w_gate_up", "w_down")]
+    sh = [to_dev(inp[n]) for n in SH]
+    bias = to_dev(inp.get("bias"))
+    out, idx, w = moe.forward(*args, k, *sh, bias=bias)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+
+
+def oracle_forward(inp, k):
+    return oracle.forward(inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], k,
+                          *[inp[n] for n in SH], bias=inp.get("bias"))
+
+
+def check_case(inp, k, name):
+    announce(name)
+    out, idx, w = gpu_forward(inp, k)
+    ref_out, ref_idx, ref_w, _ = oracle_forward(inp, k)
+    assert np.array_equal(idx, ref_idx), f"{name}: topk_idx differs in {(idx != ref_idx).sum()} entries"
+    assert np.abs(w - ref_w).max() <= W_TOL
+    return assert_out(out, ref_out)
+
+
+# ------------------------------------------------------------------ small cases
+
+def test_tiny_fp32_layer():
+    """T=32, d=128, 16 experts top-4, width 32, shared 32, binary32, seed 0."""
+    cfg = W.CONFIGS[1]
+    inp = W.make_inputs(cfg)
+    r = check_case(inp, cfg.k, cfg.name)
+    assert r < 1e-4     # binary32 end to end: far inside the bound
+
+
+@pytest.mark.parametrize("T,d,E,k,F,Fs", [
+    (300, 256, 16, 4, 128, 64),     # ~75 rows per expert, 3 ragged shared tiles
+    (1000, 320, 64, 8, 64, 128),    # some experts > 128 rows (2 tiles); d % 128 = 64
+    (1, 512, 32, 3, 64, 0),         # one token, no shared expert
+    (77, 128, 8, 8, 64, 64),        # k = E
+    (130, 192, 40, 1, 192, 64),     # k = 1
+    (513, 64, 1024, 32, 64, 64),    # largest E and k supported
+])
+def test_small_bf16_layers(T, d, E, k, F, Fs):
+    inp = W.small_case(T, d, E, k, F, Fs, "bf16", seed=T + E)
+    check_case(inp, k, f"bf16 T={T} d={d} E={E} k={k} F={F} Fs={Fs}")
+
+
+def test_fp32_ragged_width():
+    inp = W.small_case(45, 100, 12, 3, 33, 7, "f32", seed=5)
+    check_case(inp, 3, "fp32 d=100 F=33 Fs=7")
+
+
+def test_route_entry_matches_oracle():
+    inp = W.small_case(200, 256, 64, 10, 64, 64, "bf16", seed=9)
+    announce("moe_route T=200 E=64 k=10")
+    idx, w, s = moe.route(to_dev(inp["x"]), to_dev(inp["w_router"]), 10,
+                          sh_gate=to_dev(inp["sh_gate"]))
+    torch.cuda.synchronize()
+    ref_idx, ref_w = oracle.route(inp["x"], inp["w_router"], 10)
+    _, ref_s = oracle.experts(inp["x"], inp["w_gate_up"], inp["w_down"], ref_idx, ref_w,
+                              *[inp[n] for n in SH], return_gate=True)
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+    assert np.abs(w.cpu().numpy() - ref_w).max() <= W_TOL
+    assert np.abs(s.cpu().numpy() - ref_s).max() <= GATE_TOL
+
+
+def test_experts_entry_with_given_routing():
+    """Routing supplied from outside (random distinct experts, random
+    weights): exercises the expert stage alone."""
+    T, d, E, k, F, Fs = 257, 256, 32, 5, 128, 64
+    inp = W.small_case(T, d, E, k, F, Fs, "bf16", seed=12)
+    rng = np.random.default_rng(4)
+    idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    announce("moe_experts given routing")
+    out = moe.experts(to_dev(inp["x"]), to_dev(inp["w_gate_up"]), to_dev(inp["w_down"]),
+                      to_dev(idx), to_dev(w), *[to_dev(inp[n]) for n in SH])
+    torch.cuda.synchronize()
+    ref = oracle.experts(inp["x"], inp["w_gate_up"], inp["w_down"], idx, w.astype(np.float64),
+                         *[inp[n] for n in SH])
+    assert_out(out.cpu().numpy(), ref)
+
+
+def test_zero_router_ties_to_lower_index():
+    T, d, E, k = 70, 128, 32, 6
+    inp = W.small_case(T, d, E, k, 64, 64, "bf16", seed=1)
+    inp["w_router"] = np.zeros_like(inp["w_router"])
+    announce("zero router")
+    out, idx, w = gpu_forward(inp, k)
+    assert (idx == np.arange(k)).all()
+    assert np.abs(w - 1.0 / k).max() <= W_TOL
+
+
+def test_duplicate_router_rows():
+    inp = W.small_case(300, 256, 16, 5, 64, 64, "bf16", seed=21)
+    inp["w_router"] = inp["w_router"].copy()
+    inp["w_router"][9] = inp["w_router"][3]
+    check_case(inp, 5, "duplicate router rows 3 and 9")
+
+
+def test_bias_sends_every_token_to_one_expert():
+    """All T tokens pick expert 5 first: one group spanning several tiles."""
+    T, d, E, k = 600, 128, 16, 2
+    inp = W.small_case(T, d, E, k, 64, 64, "bf16", seed=8)
+    inp["bias"] = np.zeros(E, np.float32)
+    inp["bias"][5] = 100.0
+    check_case(inp, k, "bias -> expert 5")
+
+
+def test_workspace_grouping_matches_routing():
+    """counts / offsets / perm in the workspace are exactly the grouping the
+    routing implies, rows of one expert in ascending pair id."""
+    T, d, E, k, F, Fs = 700, 128, 24, 4, 64, 64
+    inp = W.small_case(T, d, E, k, F, Fs, "bf16", seed=33)
+    shape = moe.Shape(d, E, k, F, Fs, torch.bfloat16)
+    ws = moe.alloc_workspace(shape, T)
+    announce("workspace grouping")
+    args = [to_dev(inp[n]) for n in ("x", "w_router", "w_gate_up", "w_down")]
+    _, idx, _ = moe.forward(*args, k, *[to_dev(inp[n]) for n in SH], ws=ws)
+    torch.cuda.synchronize()
+    lay = moe.workspace_layout(shape, T)
+    wsb = ws.cpu().numpy()
+    counts = wsb[lay.counts:lay.counts + 4 * (E + 1)].view(np.int32)
+    offsets = wsb[lay.offsets:lay.offsets + 4 * (E + 1)].view(np.int32)
+    perm = wsb[lay.perm:lay.perm + 4 * T * k].view(np.int32)
+    ref_idx, _ = oracle.route(inp["x"], inp["w_router"], k)
+    flat = ref_idx.ravel()
+    assert counts[E] == T
+    for e in range(E):
+        pairs = np.nonzero(flat == e)[0]
+        assert counts[e] == len(pairs)
+        assert np.array_equal(perm[offsets[e]:offsets[e] + counts[e]], pairs)
+    assert offsets[E] == T * k
+
+
+def test_deterministic_and_batch_split():
+    T, d, E, k = 400, 256, 32, 6
+    inp = W.small_case(T, d, E, k, 128, 64, "bf16", seed=55)
+    announce("determinism / batch split")
+    out1, idx1, _ = gpu_forward(inp, k)
+    out2, idx2, _ = gpu_forward(inp, k)
+    assert np.array_equal(idx1, idx2)
+    for a, b in [(0, 1), (1, 150), (150, 400)]:
+        part = dict(inp)
+        part["x"] = np.ascontiguousarray(inp["x"][a:b])
+        o, i, _ = gpu_forward(part, k)
+        assert np.array_equal(i, idx1[a:b])
+        assert rel_err(o, out1[a:b].astype(np.float64)) < 1e-2
+
+
+def test_zero_tokens():
+    inp = W.small_case(0, 128, 8, 2, 64, 64, "bf16", seed=2)
+    announce("T=0")
+    out, idx, w = gpu_forward(inp, 2)
+    assert out.shape == (0, 128) and idx.shape == (0, 2)
+
+
+# ------------------------------------------------------------------ full-size configs
+
+@pytest.fixture(scope="module")
+def full_layer():
+    cfg = W.CONFIGS[2]
+    lay = W.layer_for(cfg)
+    dev = {n: to_dev(lay[n]) for n in ("w_router", "w_gate_up", "w_down") + SH}
+    return lay, dev
+
+
+def sample_tokens(T, n, seed):
+    rng = np.random.default_rng(seed)
+    pick = rng.choice(T, min(n, T), replace=False)
+    return np.unique(np.concatenate([[0, T - 1], pick]))
+
+
+@pytest.mark.parametrize("c", [2, 3, 4, 5])
+def test_full_config(full_layer, c):
+    """Pages' shapes (d 2560, 512 experts top-10, width 640, shared 640):
+    topk_idx of every token bit-exact; out on sampled tokens."""
+    cfg = W.CONFIGS[c]
+    lay, dev = full_layer
+    x = W.make_x(cfg.T, cfg.d, cfg.dtype, cfg.seed_x)
+    bias = W.make_bias(cfg)
+    announce(f"{cfg.name}: GPU forward")
+    out, idx, w = moe.forward(to_dev(x), dev["w_router"], dev["w_gate_up"], dev["w_down"], cfg.k,
+                              *[dev[n] for n in SH], bias=to_dev(bias))
+    torch.cuda.synchronize()
+    out, idx, w = out.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+    announce(f"{cfg.name}: oracle routing of all {cfg.T} tokens")
+    ref_idx, ref_w = oracle.route(x, lay["w_router"], cfg.k, bias=bias)
+    bad = (idx != ref_idx).any(1).sum()
+    assert bad == 0, f"{bad} tokens with a different topk_idx"
+    assert np.abs(w - ref_w).max() <= W_TOL
+    n = 32 if cfg.T == 32 else 48
+    toks = sample_tokens(cfg.T, n, c)
+    announce(f"{cfg.name}: oracle forward of {len(toks)} sampled tokens")
+    ref_out, _, _, _ = oracle.forward(np.ascontiguousarray(x[toks]), lay["w_router"],
+                                      lay["w_gate_up"], lay["w_down"], cfg.k,
+                                      *[lay[n] for n in SH], bias=bias)
+    r = assert_out(out[toks], ref_out)
+    announce(f"{cfg.name}: max|err|/rms = {r:.3e}")
