@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse MoE feed-forward layer on one MI355X.
+
+One step = one moe_forward of the whole layer (router logits, softmax, top-k,
+normalised weights, grouped SwiGLU experts, sigmoid-gated shared expert,
+combine) over one batch of seeded synthetic tokens already resident in HBM.
+
+Prints ONE JSON line.  `value` is tokens/s on the decode-shaped layer
+(T=32, d_model 2560, 512 experts top-10, width 640, shared 640, bf16); the
+prefill-shaped layer (T=4096) is reported inside the same line under "also".
+`roofline` is for the dominant kernel of the step, timed with HIP events
+recorded on the library's stream at its stage boundaries during the timed
+loop.  `cpu_baseline` times the CPU oracle on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import glob
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def sources_digest() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "sparse_moe_feed_amd", "csrc", "*"))):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload: str, stage: str):
+    """HBM bytes per launch of a kernel from a committed rocprofv3 counter
+    summary, if one exists for the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"counters_{stage}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"sources_sha256:\s*([0-9a-f]+)", text)
+    b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not b or m.group(1) != sources_digest():
+        return None
+    return float(b.group(1))
+
+
+def algorithmic(cfg, U: int):
+    """Algorithmic HBM bytes and FLOPs of one call and of its gate/up and down
+    stages: distinct routed experts touched (U), the shared expert, router,
+    gate vector, x, out (fp32), topk_idx and topk_w."""
+    T, d, E, k, F, Fs = cfg.T, cfg.d, cfg.E, cfg.k, cfg.F, cfg.Fs
+    b = 2
+    gu_w = U * 2 * F * d * b + 2 * Fs * d * b
+    dn_w = U * d * F * b + d * Fs * b
+    call_bytes = gu_w + dn_w + E * d * b + d * b + T * d * b + T * d * 4 + T * k * 8
+    flops_gu = 2 * T * k * 2 * F * d + 2 * T * 2 * Fs * d
+    flops_dn = 2 * T * k * F * d + 2 * T * Fs * d
+    call_flops = 2 * T * d * (E + 1) + flops_gu + flops_dn
+    return dict(call_bytes=call_bytes, call_flops=call_flops,
+                gate_up_bytes=gu_w + T * d * b + (T * k * F + T * Fs) * b,
+                gate_up_flops=flops_gu,
+                down_bytes=dn_w + (T * k * F + T * Fs) * b + T * k * d * 4 + T * d * 4,
+                down_flops=flops_dn)
+
+
+def measure(cfg, dev_layer, steps, warmup):
+    import numpy as np
+    import torch
+
+    import sparse_moe_feed_amd as moe
+    import workloads as W
+
+    x_np = W.make_x(cfg.T, cfg.d, cfg.dtype, cfg.seed_x)
+    bias_np = W.make_bias(cfg)
+    to = lambda a: None if a is None else torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    x = to(x_np)
+    bias = None if bias_np is None else torch.from_numpy(bias_np).cuda()
+    L = moe.MoELayer(dev_layer["w_router"], dev_layer["w_gate_up"], dev_layer["w_down"], cfg.k,
+                     dev_layer["w_sh_gate_up"], dev_layer["w_sh_down"], dev_layer["sh_gate"], bias,
+                     max_tokens=cfg.T)
+    out = torch.empty(cfg.T, cfg.d, device="cuda")
+    idx = torch.empty(cfg.T, cfg.k, dtype=torch.int32, device="cuda")
+    w = torch.empty(cfg.T, cfg.k, device="cuda")
+    for _ in range(warmup):
+        L(x, out, idx, w)
+    n_ev = 1 + len(moe.STAGES)
+    evs = [[moe.HipEvent() for _ in range(n_ev)] for _ in range(steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        moe.stage_events(evs[i])
+        L(x, out, idx, w)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t0.elapsed_time(t1) / steps
+    stage_ms = {name: sum(e[j].elapsed_ms(e[j + 1]) for e in evs) / steps
+                for j, name in enumerate(moe.STAGES)}
+    U = int(np.unique(idx.cpu().numpy()).size)
+    return dict(ms=ms, wall_ms=wall * 1e3 / steps, stage_ms=stage_ms, U=U)
+
+
+def roofline_of(cfg, r, workload):
+    a = algorithmic(cfg, r["U"])
+    stage = max(("gate_up", "down"), key=lambda s: r["stage_ms"][s])
+    t = r["stage_ms"][stage] * 1e-3
+    by, fl = a[f"{stage}_bytes"], a[f"{stage}_flops"]
+    hbm_frac = by / t / (HBM_PEAK_GBS * 1e9)
+    mfma_frac = fl / t / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    bound = "hbm" if by / (HBM_PEAK_GBS * 1e9) >= fl / (MFMA_BF16_PEAK_TFLOPS * 1e12) else "mfma"
+    traffic = committed_traffic(workload, stage)
+    if bound == "hbm":
+        roof = dict(bound="hbm", achieved=round(by / t / 1e9, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(hbm_frac, 4))
+    else:
+        roof = dict(bound="mfma", achieved=round(fl / t / 1e12, 1), peak=MFMA_BF16_PEAK_TFLOPS,
+                    unit="TFLOP/s", frac=round(mfma_frac, 4))
+    roof.update(traffic=traffic, kernel=stage, kernel_ms=round(r["stage_ms"][stage], 4),
+                alg_bytes=by, alg_flops=fl)
+    call_t = r["ms"] * 1e-3
+    layer = dict(hbm_frac=round(a["call_bytes"] / call_t / (HBM_PEAK_GBS * 1e9), 4),
+                 mfma_frac=round(a["call_flops"] / call_t / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
+                 alg_bytes=a["call_bytes"], alg_flops=a["call_flops"], unique_experts=r["U"])
+    return roof, layer
+
+
+def cpu_baseline(cfg, layer_np, seconds):
+    import oracle
+    import workloads as W
+
+    x = W.make_x(cfg.T, cfg.d, cfg.dtype, cfg.seed_x)
+    bias = W.make_bias(cfg)
+    args = (x, layer_np["w_router"], layer_np["w_gate_up"], layer_np["w_down"], cfg.k,
+            layer_np["w_sh_gate_up"], layer_np["w_sh_down"], layer_np["sh_gate"])
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(*args, bias=bias)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return dict(value=round(reps * cfg.T / el, 2), unit="tokens/s", cores=oracle.threads(),
+                kind="oracle",
+                sample=f"all {cfg.T} tokens of {cfg.name}, {reps} full passes in {el:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, help="workload of `value` (2 = decode T=32)")
+    ap.add_argument("--also", default="3", help="extra workloads reported in the line")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: measures one GPU only (the layer is not sharded across GPUs in this "
+              f"build); got --gpus {args.gpus}, WORLD_SIZE {world}", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+
+    cfg = W.CONFIGS[args.config]
+    layer_np = W.layer_for(cfg)
+    to = lambda a: None if a is None else torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    dev_layer = {n: to(layer_np[n]) for n in ("w_router", "w_gate_up", "w_down", "w_sh_gate_up",
+                                              "w_sh_down", "sh_gate")}
+    r = measure(cfg, dev_layer, args.steps, args.warmup)
+    roof, layer = roofline_of(cfg, r, cfg.name)
+    also = {}
+    for c in [int(v) for v in args.also.split(",") if v]:
+        c_cfg = W.CONFIGS[c]
+        rc = measure(c_cfg, dev_layer, max(3, args.steps // 2), args.warmup)
+        rroof, rlayer = roofline_of(c_cfg, rc, c_cfg.name)
+        also[c_cfg.name] = dict(value=round(c_cfg.T / (rc["ms"] * 1e-3), 1), unit="tokens/s",
+                                ms_per_step=round(rc["ms"], 4), roofline=rroof, layer=rlayer,
+                                stage_ms={k: round(v, 4) for k, v in rc["stage_ms"].items()})
+    del dev_layer
+    torch.cuda.empty_cache()
+    base = None if args.no_cpu_baseline else cpu_baseline(cfg, layer_np, args.cpu_seconds)
+    line = {
+        "metric": "MoE-layer tokens/s at T=32 decode and T=4096 prefill; % HBM / MFMA peak",
+        "value": round(cfg.T / (r["ms"] * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) tokens, N(0,0.02^2) weights (random init, no checkpoint)",
+        "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d, "experts": cfg.E,
+                   "top_k": cfg.k, "d_expert": cfg.F, "d_shared": cfg.Fs, "router_bias": cfg.bias},
+        "roofline": roof,
+        "layer": layer,
+        "stage_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},
+        "also": also,
+        "cpu_baseline": base,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

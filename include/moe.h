@@ -38,8 +38,11 @@
  *     F..2F-1 the up projection; w_down [E,d,F]; w_sh_gate_up [2Fs,d];
  *     w_sh_down [d,Fs]; sh_gate [d]; out [T,d]; topk_idx/topk_w [T,k].
  *   - Argument errors are reported before any GPU work is enqueued.  T == 0
- *     is a no-op that returns MOE_OK once desc is valid (pointers unread).  A failed launch returns MOE_ERR_HIP;
- *     a fault inside a kernel surfaces at the caller's next synchronisation.
+ *     is a no-op that returns MOE_OK once desc is valid (pointers unread).
+ *     A failed launch returns MOE_ERR_HIP; a fault inside a kernel surfaces
+ *     at the caller's next synchronisation.
+ *   - out is combined without atomics in a fixed order, so results are
+ *     deterministic run to run.
  *   - Calls on one stream are ordered.  Calls that may run concurrently must
  *     use distinct workspaces and outputs.
  */
@@ -85,7 +88,7 @@ typedef struct {
 size_t moe_workspace_size(const moe_desc *desc, int64_t T);
 
 /* Byte offsets of the workspace regions, for inspection by tests.  Valid
- * after a call on the same stream has completed.
+ * after a call on the same stream has completed (y: moe_forward/moe_experts).
  *   logits   float [T, E+1]   router logits, column E = g . x_t
  *   gate     float [T]        s_t = sigmoid(g . x_t)
  *   counts   int32 [E+1]      tokens per expert; counts[E] = T (shared)
@@ -94,9 +97,11 @@ size_t moe_workspace_size(const moe_desc *desc, int64_t T);
  *                             holds the pair id t*k+j; rows of one expert are in
  *                             ascending pair id
  *   h        [T*k, F]         gated activations of the routed rows (bf16 / f32)
- *   h_shared [T, Fs]          gated activations of the shared expert */
+ *   h_shared [T, Fs]          gated activations of the shared expert
+ *   y        float [T*k, d]   w[t,j] * expert output of each routed row; the
+ *                             combine adds a token's k rows to the shared term */
 typedef struct {
-    size_t logits, gate, counts, offsets, perm, h, h_shared, total;
+    size_t logits, gate, counts, offsets, perm, h, h_shared, y, total;
 } moe_workspace_layout;
 
 moe_status moe_workspace_query(const moe_desc *desc, int64_t T,
@@ -139,6 +144,16 @@ const char *moe_status_string(moe_status status);
 
 /* Text of the last HIP error seen by this thread ("" if none). */
 const char *moe_last_error(void);
+
+/* Stage timing for benchmarks and profilers.  The NEXT moe_forward or
+ * moe_experts call on this thread records events[i] (hipEvent_t, created by
+ * the caller) on its stream at stage boundaries, then forgets the array:
+ *   0 start; 1 after routing (moe_experts: after the shared gate);
+ *   2 after the histogram/permutation; 3 after the gate/up GEMM;
+ *   4 after the down GEMM; 5 after the combine.
+ * n (<= 8) is the number of entries; entries may be NULL.  The events only
+ * observe the stream, they change nothing the call computes. */
+moe_status moe_stage_events(void *const *events, int n);
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16 = 0, 1
 
 EXPORTED = ("moe_workspace_size", "moe_workspace_query", "moe_route", "moe_forward",
-            "moe_experts", "moe_status_string", "moe_last_error")
+            "moe_experts", "moe_status_string", "moe_last_error", "moe_stage_events")
 
 
 class MoEError(RuntimeError):
@@ -42,7 +42,7 @@ class moe_desc(ctypes.Structure):
 
 class moe_workspace_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("logits", "gate", "counts", "offsets", "perm", "h", "h_shared", "total")]
+                ("logits", "gate", "counts", "offsets", "perm", "h", "h_shared", "y", "total")]
 
 
 _lib = None
@@ -71,6 +71,8 @@ def lib():
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_last_error.argtypes = []
     L.moe_last_error.restype = ctypes.c_char_p
+    L.moe_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+    L.moe_stage_events.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -110,6 +112,57 @@ def workspace_layout(shape: Shape, T: int) -> moe_workspace_layout:
 
 def alloc_workspace(shape: Shape, T: int, device="cuda") -> torch.Tensor:
     return torch.empty(max(workspace_size(shape, T), 1), dtype=torch.uint8, device=device)
+
+
+STAGES = ("route", "permute", "gate_up", "down", "combine")
+
+_hip = None
+
+
+def _hip_rt():
+    global _hip
+    if _hip is None:
+        h = ctypes.CDLL("libamdhip64.so")
+        h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                          ctypes.c_void_p]
+        h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        for f in (h.hipEventCreateWithFlags, h.hipEventElapsedTime, h.hipEventSynchronize,
+                  h.hipEventDestroy):
+            f.restype = ctypes.c_int
+        _hip = h
+    return _hip
+
+
+class HipEvent:
+    """A raw hipEvent_t with timing, for the library's stage marks."""
+
+    def __init__(self):
+        self.handle = ctypes.c_void_p()
+        if _hip_rt().hipEventCreateWithFlags(ctypes.byref(self.handle), 0) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def elapsed_ms(self, end: "HipEvent") -> float:
+        ms = ctypes.c_float()
+        _hip_rt().hipEventSynchronize(end.handle)
+        if _hip_rt().hipEventElapsedTime(ctypes.byref(ms), self.handle, end.handle) != 0:
+            raise RuntimeError("hipEventElapsedTime failed (event not recorded?)")
+        return float(ms.value)
+
+    def __del__(self):
+        if self.handle and _hip is not None:
+            _hip.hipEventDestroy(self.handle)
+
+
+def stage_events(events):
+    """Have the next forward/experts call on this thread record the given
+    HipEvent objects (len <= 8) at its stage boundaries: index 0 at the start,
+    then after routing, permutation, gate/up, down and combine."""
+    arr = (ctypes.c_void_p * max(1, len(events)))(*[e.handle for e in events])
+    st = lib().moe_stage_events(arr, len(events))
+    if st != MOE_OK:
+        raise MoEError(st, "moe_stage_events")
 
 
 def _ptr(t: Optional[torch.Tensor]):

@@ -15,8 +15,10 @@
 //             A rows are gathered from x through the permutation; the block's
 //             B tile stacks 64 gate rows on the matching 64 up rows, so the
 //             SiLU*up product is formed in registers.
-//   down:     out[t, n] += w_r * (h[r] . Wdn[n])   with binary32 atomics; w_r is
-//             the pair's routing weight, or s_t for the shared expert.
+//   down:     y[r, n] = w_r * (h[r] . Wdn[n]) for routed rows (w_r the pair's
+//             routing weight) and out[t, n] = s_t * (h_sh[t] . Wsdn[n]) for the
+//             shared expert; a combine kernel then adds each token's k rows.
+//             Plain stores only: no atomics, deterministic result.
 // h is rounded to bfloat16 once; everything else stays binary32.
 #include "moe_device.h"
 #include "moe_kernels.h"
@@ -29,7 +31,8 @@ struct GemmArgs {
     const uint16_t *w_sh;  // gate/up: [2Fs, d]     down: [d, Fs]
     uint16_t *h;           // [T*k, F]
     uint16_t *h_sh;        // [T, Fs]
-    float *out;            // [T, d]
+    float *out;            // [T, d]   shared expert's term (plain stores)
+    float *y;              // [T*k, d] routed rows, weighted (plain stores)
     const int32_t *perm, *counts, *offsets, *tile_start, *tile_group;
     const float *topk_w, *gate;
     int64_t T;
@@ -111,22 +114,30 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
         bsrc[p] += lchunk * 8;
     }
 
-    uint4 ra[4], rb[4];
-    auto load_tile = [&](int k0) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            ra[p] = *reinterpret_cast<const uint4 *>(asrc[p] + k0);
-            rb[p] = *reinterpret_cast<const uint4 *>(bsrc[p] + k0);
-        }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int off = (lrow + 32 * p) * LDK + lchunk * 8;
-            *reinterpret_cast<uint4 *>(&As[buf][off]) = ra[p];
-            *reinterpret_cast<uint4 *>(&Bs[buf][off]) = rb[p];
-        }
-    };
+    uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
+#define MOE_LOAD_TILE(k0)                                                           \
+    do {                                                                            \
+        ra0 = *reinterpret_cast<const uint4 *>(asrc[0] + (k0));                     \
+        ra1 = *reinterpret_cast<const uint4 *>(asrc[1] + (k0));                     \
+        ra2 = *reinterpret_cast<const uint4 *>(asrc[2] + (k0));                     \
+        ra3 = *reinterpret_cast<const uint4 *>(asrc[3] + (k0));                     \
+        rb0 = *reinterpret_cast<const uint4 *>(bsrc[0] + (k0));                     \
+        rb1 = *reinterpret_cast<const uint4 *>(bsrc[1] + (k0));                     \
+        rb2 = *reinterpret_cast<const uint4 *>(bsrc[2] + (k0));                     \
+        rb3 = *reinterpret_cast<const uint4 *>(bsrc[3] + (k0));                     \
+    } while (0)
+#define MOE_STORE_TILE(buf)                                                         \
+    do {                                                                            \
+        const int off = lrow * LDK + lchunk * 8;                                    \
+        *reinterpret_cast<uint4 *>(&As[buf][off]) = ra0;                            \
+        *reinterpret_cast<uint4 *>(&As[buf][off + 32 * LDK]) = ra1;                 \
+        *reinterpret_cast<uint4 *>(&As[buf][off + 64 * LDK]) = ra2;                 \
+        *reinterpret_cast<uint4 *>(&As[buf][off + 96 * LDK]) = ra3;                 \
+        *reinterpret_cast<uint4 *>(&Bs[buf][off]) = rb0;                            \
+        *reinterpret_cast<uint4 *>(&Bs[buf][off + 32 * LDK]) = rb1;                 \
+        *reinterpret_cast<uint4 *>(&Bs[buf][off + 64 * LDK]) = rb2;                 \
+        *reinterpret_cast<uint4 *>(&Bs[buf][off + 96 * LDK]) = rb3;                 \
+    } while (0)
 
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -143,12 +154,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
     const int nk = K / BK;
-    load_tile(0);
-    store_tile(0);
+    MOE_LOAD_TILE(0);
+    MOE_STORE_TILE(0);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
-        if (kt + 1 < nk) load_tile((kt + 1) * BK);
+        if (kt + 1 < nk) MOE_LOAD_TILE((kt + 1) * BK);
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
             bf16x8 af[2], bf[2];
@@ -165,9 +176,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
                     acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni],
                                                                           acc[mi][ni], 0, 0, 0);
         }
-        if (kt + 1 < nk) store_tile(cur ^ 1);
+        if (kt + 1 < nk) MOE_STORE_TILE(cur ^ 1);
         __syncthreads();
     }
+#undef MOE_LOAD_TILE
+#undef MOE_STORE_TILE
 
     // 32x32 accumulator layout: lane holds column (lane % 32) and rows
     // 8 (v / 4) + 4 (lane / 32) + (v % 4), v = 0..15.
@@ -193,19 +206,23 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
                 for (int v = 0; v < 16; ++v) {
                     const int row = 64 * wm + 32 * mi + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
                     const int col = n0 + (ni ? brow1 : brow0) + fr;
-                    if (row < nrows && col < a.d)
-                        unsafeAtomicAdd(&a.out[(int64_t)row_tok[row] * a.d + col],
-                                        row_w[row] * acc[mi][ni][v]);
+                    if (row < nrows && col < a.d) {
+                        float *dst = shared ? a.out + (int64_t)row_tok[row] * a.d
+                                            : a.y + (int64_t)(row0 + row) * a.d;
+                        dst[col] = row_w[row] * acc[mi][ni][v];
+                    }
                 }
     }
 }
 
-hipError_t launch_experts_bf16(const Problem &p, hipStream_t s) {
+hipError_t launch_experts_bf16(const Problem &p, hipStream_t s,
+                               const std::function<void(int)> &mark) {
     GemmArgs a;
     a.x = static_cast<const uint16_t *>(p.x);
     a.h = static_cast<uint16_t *>(p.h);
     a.h_sh = static_cast<uint16_t *>(p.h_shared);
     a.out = p.out;
+    a.y = p.y;
     a.perm = p.perm;
     a.counts = p.counts;
     a.offsets = p.offsets;
@@ -224,10 +241,12 @@ hipError_t launch_experts_bf16(const Problem &p, hipStream_t s) {
     a.w = static_cast<const uint16_t *>(p.w_gate_up);
     a.w_sh = static_cast<const uint16_t *>(p.w_sh_gate_up);
     hipLaunchKernelGGL(grouped_gemm_kernel<0>, dim3(p.max_tiles, fmax / 64), dim3(256), 0, s, a);
+    mark(3);
     a.w = static_cast<const uint16_t *>(p.w_down);
     a.w_sh = static_cast<const uint16_t *>(p.w_sh_down);
     hipLaunchKernelGGL(grouped_gemm_kernel<1>, dim3(p.max_tiles, (p.d + BN - 1) / BN), dim3(256),
                        0, s, a);
+    mark(4);
     return hipGetLastError();
 }
 

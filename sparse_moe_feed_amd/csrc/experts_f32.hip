@@ -4,7 +4,8 @@
 // combine plus the sigmoid-gated shared expert; anatomy page on
 // frontier-model-atlas, "Decoder microscope", Feed-forward panel) for small
 // binary32 layers: one block per permuted row, threads across the outputs.
-// h stays binary32.
+// h stays binary32.  Routed rows land in y (weighted), the shared expert's
+// term in out; the combine kernel adds them.
 #include "moe_device.h"
 #include "moe_kernels.h"
 
@@ -12,7 +13,7 @@ namespace moe {
 
 struct F32Args {
     const float *x, *w_gu, *w_dn, *w_sgu, *w_sdn;
-    float *h, *h_sh, *out;
+    float *h, *h_sh, *out, *y;
     const int32_t *perm, *offsets;
     const float *topk_w, *gate;
     int64_t T;
@@ -33,7 +34,7 @@ __device__ int group_of_row(const int32_t *offsets, int E, int r) {
 // Resolve block row -> (token, expert weights, h row, width); false if the
 // row is unused.  Routed rows come first ([0, T*k)), then the T shared rows.
 __device__ bool resolve_row(const F32Args &a, int64_t r, int64_t &tok, int &grp, int &width,
-                            float *&hrow, float &wgt) {
+                            float *&hrow, float &wgt, float *&dst) {
     const int64_t routed = a.T * a.k;
     if (r < routed) {
         if (r >= a.offsets[a.E]) return false;
@@ -43,6 +44,7 @@ __device__ bool resolve_row(const F32Args &a, int64_t r, int64_t &tok, int &grp,
         wgt = a.topk_w[pair];
         width = a.F;
         hrow = a.h + r * a.F;
+        dst = a.y + r * a.d;
     } else {
         if (a.Fs == 0) return false;
         tok = r - routed;
@@ -50,6 +52,7 @@ __device__ bool resolve_row(const F32Args &a, int64_t r, int64_t &tok, int &grp,
         wgt = a.gate[tok];
         width = a.Fs;
         hrow = a.h_sh + tok * a.Fs;
+        dst = a.out + tok * a.d;
     }
     return true;
 }
@@ -57,9 +60,9 @@ __device__ bool resolve_row(const F32Args &a, int64_t r, int64_t &tok, int &grp,
 __global__ __launch_bounds__(256) void f32_gateup_kernel(F32Args a) {
     int64_t tok;
     int grp, width;
-    float *hrow;
+    float *hrow, *dst;
     float wgt;
-    if (!resolve_row(a, blockIdx.x, tok, grp, width, hrow, wgt)) return;
+    if (!resolve_row(a, blockIdx.x, tok, grp, width, hrow, wgt, dst)) return;
     const float *W = grp < a.E ? a.w_gu + (int64_t)grp * 2 * a.F * a.d : a.w_sgu;
     const float *xr = a.x + tok * a.d;
     for (int n = threadIdx.x; n < width; n += blockDim.x) {
@@ -77,19 +80,20 @@ __global__ __launch_bounds__(256) void f32_gateup_kernel(F32Args a) {
 __global__ __launch_bounds__(256) void f32_down_kernel(F32Args a) {
     int64_t tok;
     int grp, width;
-    float *hrow;
+    float *hrow, *dst;
     float wgt;
-    if (!resolve_row(a, blockIdx.x, tok, grp, width, hrow, wgt)) return;
+    if (!resolve_row(a, blockIdx.x, tok, grp, width, hrow, wgt, dst)) return;
     const float *W = grp < a.E ? a.w_dn + (int64_t)grp * a.d * a.F : a.w_sdn;
     for (int m = threadIdx.x; m < a.d; m += blockDim.x) {
         const float *wr = W + (int64_t)m * width;
         float y = 0.f;
         for (int n = 0; n < width; ++n) y = fmaf(wr[n], hrow[n], y);
-        unsafeAtomicAdd(&a.out[tok * a.d + m], wgt * y);
+        dst[m] = wgt * y;
     }
 }
 
-hipError_t launch_experts_f32(const Problem &p, hipStream_t s) {
+hipError_t launch_experts_f32(const Problem &p, hipStream_t s,
+                               const std::function<void(int)> &mark) {
     F32Args a;
     a.x = static_cast<const float *>(p.x);
     a.w_gu = static_cast<const float *>(p.w_gate_up);
@@ -99,6 +103,7 @@ hipError_t launch_experts_f32(const Problem &p, hipStream_t s) {
     a.h = static_cast<float *>(p.h);
     a.h_sh = static_cast<float *>(p.h_shared);
     a.out = p.out;
+    a.y = p.y;
     a.perm = p.perm;
     a.offsets = p.offsets;
     a.topk_w = p.topk_w;
@@ -111,7 +116,9 @@ hipError_t launch_experts_f32(const Problem &p, hipStream_t s) {
     a.Fs = p.Fs;
     const int64_t rows = p.T * p.k + p.T;
     hipLaunchKernelGGL(f32_gateup_kernel, dim3((unsigned)rows), dim3(64), 0, s, a);
+    mark(3);
     hipLaunchKernelGGL(f32_down_kernel, dim3((unsigned)rows), dim3(256), 0, s, a);
+    mark(4);
     return hipGetLastError();
 }
 

@@ -8,9 +8,9 @@
 //   1. router logits + shared-gate column     (router.hip)
 //   2. top-k, weights, gate                   (router.hip)
 //   3. histogram / scan / permutation / tiles (permute.hip)
-//   4. out := 0
-//   5. gate/up grouped GEMM -> h              (experts_*.hip)
-//   6. down grouped GEMM, weighted combine    (experts_*.hip)
+//   4. gate/up grouped GEMM -> h              (experts_*.hip)
+//   5. down grouped GEMM -> weighted rows y, shared term -> out
+//   6. combine: out[t] += sum_j y[row(t,j)]   (permute.hip)
 #include "moe.h"
 #include "moe_kernels.h"
 
@@ -22,6 +22,14 @@
 namespace {
 
 thread_local std::string g_last_error;
+
+// Events the next call on this thread records at its stage boundaries.
+thread_local hipEvent_t g_stage_events[8];
+thread_local int g_n_stage_events = 0;
+
+void mark_stage(int i, hipStream_t s) {
+    if (i < g_n_stage_events && g_stage_events[i]) (void)hipEventRecord(g_stage_events[i], s);
+}
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -51,7 +59,7 @@ moe_status check_T(const moe_desc *desc, int64_t T) {
 }
 
 struct Plan {
-    size_t logits, gate, counts, offsets, tile_start, tile_group, blk, rank, perm, h, h_shared,
+    size_t logits, gate, counts, offsets, tile_start, tile_group, blk, rank, perm, h, h_shared, y,
         total;
     int nblk;
     int max_tiles;
@@ -80,6 +88,7 @@ Plan make_plan(const moe_desc &d, int64_t T) {
     p.perm = take((size_t)pairs * sizeof(int32_t));
     p.h = take((size_t)pairs * d.d_expert * esize);
     p.h_shared = take((size_t)T * d.d_shared * esize);
+    p.y = take((size_t)pairs * d.d_model * sizeof(float));
     p.total = off;
     return p;
 }
@@ -106,6 +115,7 @@ moe::Problem make_problem(const moe_desc &d, int64_t T, const Plan &pl, void *ws
     p.perm = reinterpret_cast<int32_t *>(base + pl.perm);
     p.h = base + pl.h;
     p.h_shared = base + pl.h_shared;
+    p.y = reinterpret_cast<float *>(base + pl.y);
     p.nblk = pl.nblk;
     p.max_tiles = pl.max_tiles;
     return p;
@@ -138,10 +148,15 @@ moe_status check_common(const moe_desc *desc, int64_t T, std::initializer_list<c
     return MOE_OK;
 }
 
+// Stages 2..5 of a call: permutation, gate/up, down, combine.
 moe_status run_experts(const moe::Problem &p, hipStream_t s) {
     hipError_t err = moe::launch_permute(p, moe::kGemmBM, s);
-    if (err == hipSuccess) err = moe::launch_zero(p.out, p.T * p.d, s);
-    if (err == hipSuccess) err = p.bf16 ? moe::launch_experts_bf16(p, s) : moe::launch_experts_f32(p, s);
+    mark_stage(2, s);
+    if (err == hipSuccess) err = p.bf16 ? moe::launch_experts_bf16(p, s, [&](int i) { mark_stage(i, s); })
+                                        : moe::launch_experts_f32(p, s, [&](int i) { mark_stage(i, s); });
+    if (err == hipSuccess) err = moe::launch_combine(p, s);
+    mark_stage(5, s);
+    g_n_stage_events = 0;
     return hip_status(err);
 }
 
@@ -168,6 +183,7 @@ moe_status moe_workspace_query(const moe_desc *desc, int64_t T, moe_workspace_la
     layout->perm = p.perm;
     layout->h = p.h;
     layout->h_shared = p.h_shared;
+    layout->y = p.y;
     layout->total = p.total;
     return MOE_OK;
 }
@@ -213,8 +229,13 @@ moe_status moe_forward(const moe_desc *desc, int64_t T, const void *x, const voi
     p.topk_idx = topk_idx;
     p.topk_w = topk_w;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    mark_stage(0, s);
     st = hip_status(moe::launch_router(p, nullptr, s));
-    if (st != MOE_OK) return st;
+    mark_stage(1, s);
+    if (st != MOE_OK) {
+        g_n_stage_events = 0;
+        return st;
+    }
     return run_experts(p, s);
 }
 
@@ -238,10 +259,15 @@ moe_status moe_experts(const moe_desc *desc, int64_t T, const void *x, const voi
     p.topk_idx = const_cast<int32_t *>(topk_idx);
     p.topk_w = const_cast<float *>(topk_w);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    mark_stage(0, s);
     if (p.Fs > 0) {
         st = hip_status(moe::launch_shared_gate(p, s));
-        if (st != MOE_OK) return st;
+        if (st != MOE_OK) {
+            g_n_stage_events = 0;
+            return st;
+        }
     }
+    mark_stage(1, s);
     return run_experts(p, s);
 }
 
@@ -257,5 +283,12 @@ const char *moe_status_string(moe_status status) {
 }
 
 const char *moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status moe_stage_events(void *const *events, int n) {
+    if (n < 0 || n > 8 || (n > 0 && !events)) return MOE_ERR_INVALID_ARG;
+    for (int i = 0; i < n; ++i) g_stage_events[i] = static_cast<hipEvent_t>(events[i]);
+    g_n_stage_events = n;
+    return MOE_OK;
+}
 
 }  // extern "C"

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <functional>
+
 namespace moe {
 
 // Everything a launch needs to know about one call.  Pointers are device
@@ -29,8 +31,9 @@ struct Problem {
     int32_t *tile_group;// [max_tiles] group (expert, or E = shared) of each GEMM tile
     int max_tiles;      // upper bound on GEMM tiles for the tile height in use
     int32_t *blk;       // [E, nblk]
-    int32_t *rank;      // [T*k]
+    int32_t *rank;      // [T*k] rank inside the histogram block, then the pair's row
     int32_t *perm;      // [T*k]
+    float *y;           // [T*k, d] weighted down-projection of each routed row
     void *h;            // [T*k, F]
     void *h_shared;     // [T, Fs]
     int nblk;           // ceil(T / kCountBlock)
@@ -53,10 +56,11 @@ hipError_t launch_router(const Problem &p, float *sh_gate_user, hipStream_t s);
 hipError_t launch_shared_gate(const Problem &p, hipStream_t s);
 // Histogram, scan, stable permutation and GEMM tile map for tile height bm.
 hipError_t launch_permute(const Problem &p, int bm, hipStream_t s);
-// out := 0
-hipError_t launch_zero(float *out, int64_t n, hipStream_t s);
-// Expert stage for bfloat16 (MFMA) and binary32 (plain FMA) layers.
-hipError_t launch_experts_bf16(const Problem &p, hipStream_t s);
-hipError_t launch_experts_f32(const Problem &p, hipStream_t s);
+// out[t] (= shared term, if any) += sum_j y[row(t, j)]
+hipError_t launch_combine(const Problem &p, hipStream_t s);
+// Expert stage for bfloat16 (MFMA) and binary32 (plain FMA) layers:
+// gate/up then down.  mark(3) is called after gate/up, mark(4) after down.
+hipError_t launch_experts_bf16(const Problem &p, hipStream_t s, const std::function<void(int)> &mark);
+hipError_t launch_experts_f32(const Problem &p, hipStream_t s, const std::function<void(int)> &mark);
 
 }  // namespace moe

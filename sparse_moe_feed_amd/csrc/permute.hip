@@ -10,14 +10,13 @@
 //            a pair's rank inside its block is a popcount of the lower bits;
 //   scan:    per expert, exclusive prefix of the block counts; across experts,
 //            exclusive prefix of the totals (offsets) and of the tile counts;
-//   scatter: perm[offsets[e] + block_base[e] + rank] = pair id.
+//   scatter: perm[offsets[e] + block_base[e] + rank] = pair id, and the
+//            pair's row is kept for the combine.
 // Every row a block reserves is written by some pair, so perm never holds
 // stale entries, even when a routing given from outside repeats an expert
 // within one token (that pair's copies then share one row).
 #include "moe_device.h"
 #include "moe_kernels.h"
-
-#include <algorithm>
 
 namespace moe {
 
@@ -126,9 +125,10 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t *__restrict__ 
     }
 }
 
+// Also turns rank[pair] into the pair's row, for the combine.
 __global__ __launch_bounds__(kCountBlock) void route_scatter_kernel(
     const int32_t *__restrict__ topk_idx, int64_t ntok, int k, int E, int nblk,
-    const int32_t *__restrict__ rank, const int32_t *__restrict__ blk,
+    int32_t *__restrict__ rank, const int32_t *__restrict__ blk,
     const int32_t *__restrict__ offsets, int32_t *__restrict__ perm) {
     const int64_t t = (int64_t)blockIdx.x * kCountBlock + threadIdx.x;
     if (t >= ntok) return;
@@ -136,6 +136,7 @@ __global__ __launch_bounds__(kCountBlock) void route_scatter_kernel(
         const int e = clamp_expert(topk_idx[t * k + j], E);
         const int pos = offsets[e] + blk[(int64_t)e * nblk + blockIdx.x] + rank[t * k + j];
         perm[pos] = (int32_t)(t * k + j);
+        rank[t * k + j] = pos;
     }
 }
 
@@ -150,24 +151,47 @@ hipError_t launch_permute(const Problem &p, int bm, hipStream_t s) {
     return hipGetLastError();
 }
 
-__global__ void zero_kernel(float4 *__restrict__ out, int64_t n4) {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
-         i += (int64_t)gridDim.x * blockDim.x)
-        out[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-}
-__global__ void zero_tail_kernel(float *__restrict__ out, int64_t from, int64_t n) {
-    int64_t i = from + threadIdx.x;
-    if (i < n) out[i] = 0.f;
+// Weighted combine, one block per token, binary32, fixed order: the shared
+// term already in out[t] (written by the down-projection's shared tiles), then
+// the routed rows in slot order j = 0..k-1.  Deterministic: no atomics.
+template <bool SHARED>
+__global__ __launch_bounds__(128) void combine_kernel(const float *__restrict__ y,
+                                                      const int32_t *__restrict__ row_of,
+                                                      float *__restrict__ out, int64_t ntok,
+                                                      int d, int k) {
+    const int64_t t = blockIdx.x;
+    __shared__ int32_t rows[32];
+    if (threadIdx.x < k) rows[threadIdx.x] = row_of[t * k + threadIdx.x];
+    __syncthreads();
+    float *o = out + t * d;
+    if ((d & 3) == 0) {
+        for (int c = threadIdx.x; c < d / 4; c += 128) {
+            float4 acc = SHARED ? reinterpret_cast<const float4 *>(o)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int j = 0; j < k; ++j) {
+                const float4 v = reinterpret_cast<const float4 *>(y + (int64_t)rows[j] * d)[c];
+                acc.x += v.x;
+                acc.y += v.y;
+                acc.z += v.z;
+                acc.w += v.w;
+            }
+            reinterpret_cast<float4 *>(o)[c] = acc;
+        }
+    } else {
+        for (int c = threadIdx.x; c < d; c += 128) {
+            float acc = SHARED ? o[c] : 0.f;
+            for (int j = 0; j < k; ++j) acc += y[(int64_t)rows[j] * d + c];
+            o[c] = acc;
+        }
+    }
 }
 
-hipError_t launch_zero(float *out, int64_t n, hipStream_t s) {
-    const int64_t n4 = n / 4;
-    if (n4 > 0) {
-        const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 8192);
-        hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                           reinterpret_cast<float4 *>(out), n4);
-    }
-    if (n % 4) hipLaunchKernelGGL(zero_tail_kernel, dim3(1), dim3(4), 0, s, out, n4 * 4, n);
+hipError_t launch_combine(const Problem &p, hipStream_t s) {
+    if (p.Fs > 0)
+        hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)p.T), dim3(128), 0, s, p.y, p.rank,
+                           p.out, p.T, p.d, p.k);
+    else
+        hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)p.T), dim3(128), 0, s, p.y, p.rank,
+                           p.out, p.T, p.d, p.k);
     return hipGetLastError();
 }
 

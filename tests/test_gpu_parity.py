@@ -159,12 +159,27 @@ def test_deterministic_and_batch_split():
     out1, idx1, _ = gpu_forward(inp, k)
     out2, idx2, _ = gpu_forward(inp, k)
     assert np.array_equal(idx1, idx2)
+    assert np.array_equal(out1, out2)       # fixed-order combine, no atomics
     for a, b in [(0, 1), (1, 150), (150, 400)]:
         part = dict(inp)
         part["x"] = np.ascontiguousarray(inp["x"][a:b])
         o, i, _ = gpu_forward(part, k)
         assert np.array_equal(i, idx1[a:b])
         assert rel_err(o, out1[a:b].astype(np.float64)) < 1e-2
+
+
+def test_stage_events_are_recorded():
+    T, d, E, k = 300, 256, 16, 4
+    inp = W.small_case(T, d, E, k, 128, 64, "bf16", seed=3)
+    args = [to_dev(inp[n]) for n in ("x", "w_router", "w_gate_up", "w_down")]
+    sh = [to_dev(inp[n]) for n in SH]
+    evs = [moe.HipEvent() for _ in range(1 + len(moe.STAGES))]
+    announce("stage events")
+    moe.stage_events(evs)
+    moe.forward(*args, k, *sh)
+    torch.cuda.synchronize()
+    times = [evs[i].elapsed_ms(evs[i + 1]) for i in range(len(moe.STAGES))]
+    assert all(t >= 0 for t in times) and sum(times) > 0
 
 
 def test_zero_tokens():
