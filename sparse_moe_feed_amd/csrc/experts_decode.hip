@@ -1,0 +1,281 @@
+// experts_decode.hip -- grouped SwiGLU experts when each expert sees only a
+// few tokens (decode): weight streaming from HBM.
+//
+// Same maths as experts_bf16.hip (gated MLP with SiLU per expert, weighted
+// rows y, shared expert scaled by its sigmoid gate; anatomy page on
+// frontier-model-atlas, "Decoder microscope", Feed-forward panel and "Expert
+// fan-out").  With about one token per touched expert, the work is reading
+// every touched expert's 3 x F x d weights once; the arithmetic is a few
+// MFMAs per 16-byte load.
+//
+// Tiles hold up to 32 permuted rows of one group (two 16-row halves of
+// v_mfma_f32_16x16x32_bf16).  Each wave owns NB blocks of 16 output columns
+// and walks K with weights loaded straight from HBM into registers: 4 MFMA
+// K-steps (128 elements, 256 contiguous bytes per weight row) per group, two
+// groups in flight (ping-pong).  A fragments (token rows) come from L2.  No
+// LDS staging: every weight byte is used by exactly one wave.
+#include "moe_device.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+constexpr int DBM = kDecodeBM;  // rows per decode tile
+constexpr int KG = 128;         // K elements per pipeline group (4 MFMA steps)
+
+struct DecodeArgs {
+    const uint16_t *x;
+    const uint16_t *w;     // gate/up: [E, 2F, d]   down: [E, d, F]
+    const uint16_t *w_sh;  // gate/up: [2Fs, d]     down: [d, Fs]
+    uint16_t *h;           // [T*k, F]
+    uint16_t *h_sh;        // [T, Fs]
+    float *out, *y;
+    const int32_t *perm, *counts, *offsets, *tile_start, *tile_group;
+    const float *topk_w, *gate;
+    int64_t T;
+    int d, E, k, F, Fs;
+};
+
+struct Frag {
+    uint4 v[4];  // one 16-byte slice for each of the 4 MFMA steps of a group
+};
+
+// No per-lane conditions on loads (padding rows read a valid row): divergent
+// branches around loads make the compiler's wait counts conservative and
+// drain the pipeline every group.
+template <int NB, int HALVES>
+__device__ __forceinline__ void load_group(Frag (&b)[NB], Frag (&a)[HALVES],
+                                           const uint16_t *const (&bp)[NB],
+                                           const uint16_t *const (&ap)[HALVES], int g) {
+    const int kb = g * KG;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int n = 0; n < NB; ++n) b[n].v[s] = *reinterpret_cast<const uint4 *>(bp[n] + kb + 32 * s);
+#pragma unroll
+        for (int h = 0; h < HALVES; ++h) a[h].v[s] = *reinterpret_cast<const uint4 *>(ap[h] + kb + 32 * s);
+    }
+}
+
+template <int NB, int HALVES>
+__device__ __forceinline__ void mfma_group(f32x4 (&acc)[HALVES][NB], const Frag (&b)[NB],
+                                           const Frag (&a)[HALVES]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int h = 0; h < HALVES; ++h)
+#pragma unroll
+            for (int n = 0; n < NB; ++n)
+                acc[h][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, a[h].v[s]), __builtin_bit_cast(bf16x8, b[n].v[s]),
+                    acc[h][n], 0, 0, 0);
+}
+
+// Streams K (a multiple of KG) for NB weight-row blocks and HALVES row halves.
+// bp[n]: this lane's weight row plus its 8-element k offset; ap[h]: this
+// lane's token row plus k offset (padding rows point at a valid row; their
+// results are never stored).  Two groups of loads are kept in flight
+// (ping-pong register buffers).
+template <int NB, int HALVES>
+__device__ __forceinline__ void stream_k(const uint16_t *const (&bp)[NB],
+                                         const uint16_t *const (&ap)[HALVES], int K,
+                                         f32x4 (&acc)[HALVES][NB]) {
+    Frag b0[NB], b1[NB], a0[HALVES], a1[HALVES];
+    const int ng = K / KG;
+    // The steady-state body has no branches around loads (any branch makes
+    // the compiler's wait counts fall back to zero), and sched_barrier keeps
+    // the phases in program order, so a group's loads are in flight while the
+    // previous group's MFMAs run.  The last one or two groups are peeled.
+    load_group<NB, HALVES>(b0, a0, bp, ap, 0);
+    int g = 0;
+    for (; g + 2 < ng; g += 2) {
+        load_group<NB, HALVES>(b1, a1, bp, ap, g + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_group<NB, HALVES>(acc, b0, a0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_group<NB, HALVES>(b0, a0, bp, ap, g + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_group<NB, HALVES>(acc, b1, a1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (g + 1 < ng) {
+        load_group<NB, HALVES>(b1, a1, bp, ap, g + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_group<NB, HALVES>(acc, b0, a0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_group<NB, HALVES>(acc, b1, a1);
+    } else {
+        mfma_group<NB, HALVES>(acc, b0, a0);
+    }
+}
+
+struct TileInfo {
+    int g, row0, nrows;
+    bool shared;
+};
+
+__device__ __forceinline__ bool decode_tile(const DecodeArgs &a, TileInfo &ti) {
+    const int tile = blockIdx.x;
+    if (tile >= a.tile_start[a.E + 1]) return false;
+    ti.g = a.tile_group[tile];
+    ti.shared = ti.g == a.E;
+    const int m_local = (tile - a.tile_start[ti.g]) * DBM;
+    if (!ti.shared) {
+        ti.row0 = a.offsets[ti.g] + m_local;
+        ti.nrows = min(DBM, a.counts[ti.g] - m_local);
+    } else {
+        ti.row0 = m_local;
+        ti.nrows = (int)min<int64_t>(DBM, a.T - m_local);
+    }
+    return true;
+}
+
+// gate/up: block = 4 waves, wave w owns gate columns n0 + 16 w .. + 16 and the
+// matching up columns; grid.y walks 64-column slabs of the expert width.
+template <int HALVES>
+__device__ void decode_gateup_body(const DecodeArgs &a, const TileInfo &ti, const int *row_tok) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int Fg = ti.shared ? a.Fs : a.F;
+    const int ncol = blockIdx.y * 64 + wave * 16;  // first gate column of this wave
+    const uint16_t *W = ti.shared ? a.w_sh : a.w + (int64_t)ti.g * 2 * a.F * a.d;
+    const int rl = lane & 15, kq = 8 * (lane >> 4);
+    const uint16_t *bp[2] = {W + (int64_t)(ncol + rl) * a.d + kq,
+                             W + (int64_t)(Fg + ncol + rl) * a.d + kq};
+    const uint16_t *ap[HALVES];
+#pragma unroll
+    for (int h = 0; h < HALVES; ++h) {
+        const int r = 16 * h + rl;
+        ap[h] = a.x + (int64_t)row_tok[r] * a.d + kq;  // row_tok is clamped to valid rows
+    }
+    f32x4 acc[HALVES][2];
+#pragma unroll
+    for (int h = 0; h < HALVES; ++h)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) acc[h][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    stream_k<2, HALVES>(bp, ap, a.d, acc);
+    uint16_t *H = ti.shared ? a.h_sh : a.h;
+    // 16x16 accumulator: lane holds column lane % 16, rows 4 (lane / 16) + i.
+#pragma unroll
+    for (int h = 0; h < HALVES; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * h + 4 * (lane >> 4) + i;
+            if (row < ti.nrows)
+                H[(int64_t)(ti.row0 + row) * Fg + ncol + rl] =
+                    f32_to_bf16_rne(silu_mul(acc[h][0][i], acc[h][1][i]));
+        }
+}
+
+__global__ __launch_bounds__(256) void decode_gateup_kernel(DecodeArgs a) {
+    __shared__ int row_tok[DBM];
+    TileInfo ti;
+    if (!decode_tile(a, ti)) return;
+    const int Fg = ti.shared ? a.Fs : a.F;
+    if (blockIdx.y * 64 >= Fg) return;
+    if (threadIdx.x < DBM) {
+        const int r = min((int)threadIdx.x, ti.nrows - 1);
+        row_tok[threadIdx.x] = ti.shared ? ti.row0 + r : a.perm[ti.row0 + r] / a.k;
+    }
+    __syncthreads();
+    if (ti.nrows > 16) decode_gateup_body<2>(a, ti, row_tok);
+    else decode_gateup_body<1>(a, ti, row_tok);
+}
+
+// down: block = 4 waves, wave w owns output columns n0 + 32 w .. + 32 (two
+// 16-column blocks); grid.y walks 128-column slabs of d.
+template <int HALVES>
+__device__ void decode_down_body(const DecodeArgs &a, const TileInfo &ti, const int *row_tok,
+                                 const float *row_w) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int Fg = ti.shared ? a.Fs : a.F;
+    const int ncol = blockIdx.y * 128 + wave * 32;
+    const uint16_t *W = ti.shared ? a.w_sh : a.w + (int64_t)ti.g * a.d * a.F;
+    const int rl = lane & 15, kq = 8 * (lane >> 4);
+    const uint16_t *bp[2] = {W + (int64_t)min(ncol + rl, a.d - 1) * Fg + kq,
+                             W + (int64_t)min(ncol + 16 + rl, a.d - 1) * Fg + kq};
+    const uint16_t *H = ti.shared ? a.h_sh : a.h;
+    const uint16_t *ap[HALVES];
+#pragma unroll
+    for (int h = 0; h < HALVES; ++h) {
+        const int r = 16 * h + rl;
+        ap[h] = H + (int64_t)(ti.row0 + min(r, ti.nrows - 1)) * Fg + kq;
+    }
+    f32x4 acc[HALVES][2];
+#pragma unroll
+    for (int h = 0; h < HALVES; ++h)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) acc[h][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    stream_k<2, HALVES>(bp, ap, Fg, acc);
+#pragma unroll
+    for (int h = 0; h < HALVES; ++h)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * h + 4 * (lane >> 4) + i;
+                const int col = ncol + 16 * n + rl;
+                if (row < ti.nrows && col < a.d) {
+                    float *dst = ti.shared ? a.out + (int64_t)row_tok[row] * a.d
+                                           : a.y + (int64_t)(ti.row0 + row) * a.d;
+                    dst[col] = row_w[row] * acc[h][n][i];
+                }
+            }
+}
+
+__global__ __launch_bounds__(256) void decode_down_kernel(DecodeArgs a) {
+    __shared__ int row_tok[DBM];
+    __shared__ float row_w[DBM];
+    TileInfo ti;
+    if (!decode_tile(a, ti)) return;
+    if (blockIdx.y * 128 >= a.d) return;
+    if (threadIdx.x < DBM) {
+        const int r = min((int)threadIdx.x, ti.nrows - 1);
+        if (ti.shared) {
+            row_tok[threadIdx.x] = ti.row0 + r;
+            row_w[threadIdx.x] = a.gate[ti.row0 + r];
+        } else {
+            const int pair = a.perm[ti.row0 + r];
+            row_tok[threadIdx.x] = pair / a.k;
+            row_w[threadIdx.x] = a.topk_w[pair];
+        }
+    }
+    __syncthreads();
+    if (ti.nrows > 16) decode_down_body<2>(a, ti, row_tok, row_w);
+    else decode_down_body<1>(a, ti, row_tok, row_w);
+}
+
+hipError_t launch_experts_decode(const Problem &p, hipStream_t s,
+                                 const std::function<void(int)> &mark) {
+    DecodeArgs a;
+    a.x = static_cast<const uint16_t *>(p.x);
+    a.h = static_cast<uint16_t *>(p.h);
+    a.h_sh = static_cast<uint16_t *>(p.h_shared);
+    a.out = p.out;
+    a.y = p.y;
+    a.perm = p.perm;
+    a.counts = p.counts;
+    a.offsets = p.offsets;
+    a.tile_start = p.tile_start;
+    a.tile_group = p.tile_group;
+    a.topk_w = p.topk_w;
+    a.gate = p.gate;
+    a.T = p.T;
+    a.d = p.d;
+    a.E = p.E;
+    a.k = p.k;
+    a.F = p.F;
+    a.Fs = p.Fs;
+    const int fmax = p.F > p.Fs ? p.F : p.Fs;
+    a.w = static_cast<const uint16_t *>(p.w_gate_up);
+    a.w_sh = static_cast<const uint16_t *>(p.w_sh_gate_up);
+    hipLaunchKernelGGL(decode_gateup_kernel, dim3(p.max_tiles, (fmax + 63) / 64), dim3(256), 0, s,
+                       a);
+    mark(3);
+    a.w = static_cast<const uint16_t *>(p.w_down);
+    a.w_sh = static_cast<const uint16_t *>(p.w_sh_down);
+    hipLaunchKernelGGL(decode_down_kernel, dim3(p.max_tiles, (p.d + 127) / 128), dim3(256), 0, s,
+                       a);
+    mark(4);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -70,7 +70,8 @@ Plan make_plan(const moe_desc &d, int64_t T) {
     const size_t esize = d.dtype == MOE_BF16 ? 2 : 4;
     const int64_t pairs = T * d.top_k;
     p.nblk = (int)((T + moe::kCountBlock - 1) / moe::kCountBlock);
-    p.max_tiles = (int)moe::max_gemm_tiles(T, d.top_k, d.n_experts, moe::kGemmBM, d.d_shared > 0);
+    // tile map sized for the smaller of the two tile heights (the larger bound)
+    p.max_tiles = (int)moe::max_gemm_tiles(T, d.top_k, d.n_experts, moe::kDecodeBM, d.d_shared > 0);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t at = off;
@@ -148,12 +149,24 @@ moe_status check_common(const moe_desc *desc, int64_t T, std::initializer_list<c
     return MOE_OK;
 }
 
+// Weight streaming (few rows per expert) or LDS-tiled MFMA GEMM (many).
+bool use_decode_path(const moe::Problem &p) {
+    if (!p.bf16 || p.d % 128 || p.F % 128 || p.Fs % 128) return false;
+    return p.T * p.k <= (int64_t)16 * p.E;
+}
+
 // Stages 2..5 of a call: permutation, gate/up, down, combine.
-moe_status run_experts(const moe::Problem &p, hipStream_t s) {
-    hipError_t err = moe::launch_permute(p, moe::kGemmBM, s);
+moe_status run_experts(moe::Problem p, hipStream_t s) {
+    const bool decode = use_decode_path(p);
+    const int bm = decode ? moe::kDecodeBM : moe::kGemmBM;
+    p.max_tiles = (int)moe::max_gemm_tiles(p.T, p.k, p.E, bm, p.Fs > 0);
+    hipError_t err = moe::launch_permute(p, bm, s);
     mark_stage(2, s);
-    if (err == hipSuccess) err = p.bf16 ? moe::launch_experts_bf16(p, s, [&](int i) { mark_stage(i, s); })
-                                        : moe::launch_experts_f32(p, s, [&](int i) { mark_stage(i, s); });
+    auto mark = [&](int i) { mark_stage(i, s); };
+    if (err == hipSuccess)
+        err = !p.bf16 ? moe::launch_experts_f32(p, s, mark)
+                      : decode ? moe::launch_experts_decode(p, s, mark)
+                               : moe::launch_experts_bf16(p, s, mark);
     if (err == hipSuccess) err = moe::launch_combine(p, s);
     mark_stage(5, s);
     g_n_stage_events = 0;

@@ -41,6 +41,7 @@ struct Problem {
 
 constexpr int kCountBlock = 256;     // tokens per histogram block
 constexpr int kGemmBM = 128;         // rows per grouped-GEMM tile (MFMA path)
+constexpr int kDecodeBM = 32;        // rows per tile of the weight-streaming (decode) path
 
 // Upper bound on sum_e ceil(c_e / bm) + ceil(T / bm) over any routing with
 // sum_e c_e = T*k: each non-empty expert adds at most one partial tile.
@@ -62,5 +63,8 @@ hipError_t launch_combine(const Problem &p, hipStream_t s);
 // gate/up then down.  mark(3) is called after gate/up, mark(4) after down.
 hipError_t launch_experts_bf16(const Problem &p, hipStream_t s, const std::function<void(int)> &mark);
 hipError_t launch_experts_f32(const Problem &p, hipStream_t s, const std::function<void(int)> &mark);
+// Weight-streaming expert stage for few tokens per expert (tiles of kDecodeBM).
+hipError_t launch_experts_decode(const Problem &p, hipStream_t s,
+                                 const std::function<void(int)> &mark);
 
 }  // namespace moe

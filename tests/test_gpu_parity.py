@@ -58,6 +58,9 @@ def test_tiny_fp32_layer():
     (77, 128, 8, 8, 64, 64),        # k = E
     (130, 192, 40, 1, 192, 64),     # k = 1
     (513, 64, 1024, 32, 64, 64),    # largest E and k supported
+    (40, 256, 64, 4, 128, 128),     # weight-streaming path (few rows per expert)
+    (7, 384, 128, 6, 256, 0),       # weight-streaming path, no shared expert
+    (100, 256, 16, 2, 128, 128),    # streaming path, experts with 17..32+ rows
 ])
 def test_small_bf16_layers(T, d, E, k, F, Fs):
     inp = W.small_case(T, d, E, k, F, Fs, "bf16", seed=T + E)
@@ -117,10 +120,11 @@ def test_duplicate_router_rows():
     check_case(inp, 5, "duplicate router rows 3 and 9")
 
 
-def test_bias_sends_every_token_to_one_expert():
-    """All T tokens pick expert 5 first: one group spanning several tiles."""
-    T, d, E, k = 600, 128, 16, 2
-    inp = W.small_case(T, d, E, k, 64, 64, "bf16", seed=8)
+@pytest.mark.parametrize("T,d,E,k,F", [(600, 128, 16, 2, 64), (100, 256, 32, 2, 128)])
+def test_bias_sends_every_token_to_one_expert(T, d, E, k, F):
+    """All T tokens pick expert 5 first: one group spanning several tiles
+    (LDS-tiled GEMM path, then the weight-streaming path)."""
+    inp = W.small_case(T, d, E, k, F, F, "bf16", seed=8)
     inp["bias"] = np.zeros(E, np.float32)
     inp["bias"][5] = 100.0
     check_case(inp, k, "bias -> expert 5")
