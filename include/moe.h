@@ -66,12 +66,22 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
+/* Router algorithm (moe_desc.flags).  Both give the same topk_idx bit for
+ * bit (the canonical binary32 logits decide); they differ in cost.
+ *   0                        automatic: shortlist for MOE_BF16 with T >= 128
+ *   MOE_FLAG_ROUTER_EXACT    canonical logits of every expert (vector ALUs)
+ *   MOE_FLAG_ROUTER_SHORTLIST MFMA logits bound the canonical ones; only the
+ *                            experts that can still reach the top k are
+ *                            recomputed exactly (MOE_BF16 only) */
+enum { MOE_FLAG_ROUTER_EXACT = 1, MOE_FLAG_ROUTER_SHORTLIST = 2 };
+
 /* Layer shape.  d_model = d, n_experts = E, top_k = k, d_expert = F,
  * d_shared = Fs (0: no shared expert).
  * Valid: d, E, F >= 1; 1 <= k <= E; Fs >= 0; dtype MOE_F32 or MOE_BF16.
  * Supported: k <= 32; E <= 1024; d <= 16384; for MOE_BF16 additionally
  * d, F and Fs multiples of 64.  Anything valid but outside this returns
- * MOE_ERR_UNSUPPORTED. */
+ * MOE_ERR_UNSUPPORTED.  flags: 0 or one MOE_FLAG_ROUTER_* value
+ * (MOE_FLAG_ROUTER_SHORTLIST with MOE_F32 is unsupported). */
 typedef struct {
     int32_t d_model;
     int32_t n_experts;
@@ -79,6 +89,7 @@ typedef struct {
     int32_t d_expert;
     int32_t d_shared;
     int32_t dtype; /* moe_dtype */
+    int32_t flags; /* MOE_FLAG_ROUTER_* or 0 */
 } moe_desc;
 
 /* Bytes of device workspace a call with T tokens needs (0 on an invalid or
@@ -89,7 +100,9 @@ size_t moe_workspace_size(const moe_desc *desc, int64_t T);
 
 /* Byte offsets of the workspace regions, for inspection by tests.  Valid
  * after a call on the same stream has completed (y: moe_forward/moe_experts).
- *   logits   float [T, E+1]   router logits, column E = g . x_t
+ *   logits   float [T, E+1]   router logits: exact router: canonical logits,
+ *                             column E = g . x_t; shortlist router: the
+ *                             MFMA logits f (no bias, column E unused)
  *   gate     float [T]        s_t = sigmoid(g . x_t)
  *   counts   int32 [E+1]      tokens per expert; counts[E] = T (shared)
  *   offsets  int32 [E+1]      exclusive prefix of counts[0..E-1]

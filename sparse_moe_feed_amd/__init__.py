@@ -23,6 +23,9 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
+MOE_FLAG_ROUTER_EXACT, MOE_FLAG_ROUTER_SHORTLIST = 1, 2
+ROUTERS = {None: 0, "auto": 0, "exact": MOE_FLAG_ROUTER_EXACT,
+           "shortlist": MOE_FLAG_ROUTER_SHORTLIST}
 
 EXPORTED = ("moe_workspace_size", "moe_workspace_query", "moe_route", "moe_forward",
             "moe_experts", "moe_status_string", "moe_last_error", "moe_stage_events")
@@ -37,7 +40,8 @@ class MoEError(RuntimeError):
 class moe_desc(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("d_expert", ctypes.c_int32),
-                ("d_shared", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("d_shared", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("flags", ctypes.c_int32)]
 
 
 class moe_workspace_layout(ctypes.Structure):
@@ -89,13 +93,14 @@ class Shape:
     d_expert: int
     d_shared: int
     dtype: torch.dtype
+    router: Optional[str] = None   # None/"auto", "exact" or "shortlist"
 
     def desc(self) -> moe_desc:
         code = {torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}.get(self.dtype)
         if code is None:
             raise TypeError(f"unsupported dtype {self.dtype}")
         return moe_desc(self.d_model, self.n_experts, self.top_k, self.d_expert,
-                        self.d_shared, code)
+                        self.d_shared, code, ROUTERS[self.router])
 
 
 def workspace_size(shape: Shape, T: int) -> int:
@@ -191,17 +196,17 @@ def _check(st: int, where: str):
         raise MoEError(st, where, lib().moe_last_error().decode() if st == MOE_ERR_HIP else "")
 
 
-def shape_of(x, w_gate_up, k, w_sh_gate_up=None) -> Shape:
+def shape_of(x, w_gate_up, k, w_sh_gate_up=None, router=None) -> Shape:
     E, twoF, d = w_gate_up.shape
     Fs = 0 if w_sh_gate_up is None else w_sh_gate_up.shape[0] // 2
-    return Shape(d, E, k, twoF // 2, Fs, x.dtype)
+    return Shape(d, E, k, twoF // 2, Fs, x.dtype, router)
 
 
-def route(x, w_router, k, bias=None, sh_gate=None, ws=None):
+def route(x, w_router, k, bias=None, sh_gate=None, ws=None, router=None):
     """(topk_idx int32 [T,k], topk_w float32 [T,k], s float32 [T] or None)."""
     T, d = x.shape
     E = w_router.shape[0]
-    shape = Shape(d, E, k, 64, 0, x.dtype)
+    shape = Shape(d, E, k, 64, 0, x.dtype, router)
     _dev(x, "x"), _dev(w_router, "w_router", x.dtype, (E, d))
     _dev(bias, "router_bias", torch.float32, (E,)), _dev(sh_gate, "sh_gate", x.dtype, (d,))
     idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
@@ -216,10 +221,10 @@ def route(x, w_router, k, bias=None, sh_gate=None, ws=None):
 
 
 def forward(x, w_router, w_gate_up, w_down, k, w_sh_gate_up=None, w_sh_down=None,
-            sh_gate=None, bias=None, out=None, topk_idx=None, topk_w=None, ws=None):
+            sh_gate=None, bias=None, out=None, topk_idx=None, topk_w=None, ws=None, router=None):
     """The whole layer.  Returns (out float32 [T,d], topk_idx, topk_w)."""
     T, d = x.shape
-    shape = shape_of(x, w_gate_up, k, w_sh_gate_up)
+    shape = shape_of(x, w_gate_up, k, w_sh_gate_up, router)
     E, F, Fs = shape.n_experts, shape.d_expert, shape.d_shared
     _dev(x, "x"), _dev(w_router, "w_router", x.dtype, (E, d))
     _dev(w_gate_up, "w_gate_up", x.dtype), _dev(w_down, "w_down", x.dtype, (E, d, F))
@@ -268,11 +273,12 @@ class MoELayer:
     tokens, so repeated calls allocate nothing but their outputs."""
 
     def __init__(self, w_router, w_gate_up, w_down, k, w_sh_gate_up=None, w_sh_down=None,
-                 sh_gate=None, bias=None, max_tokens=1):
+                 sh_gate=None, bias=None, max_tokens=1, router=None):
         self.w = dict(w_router=w_router, w_gate_up=w_gate_up, w_down=w_down,
                       w_sh_gate_up=w_sh_gate_up, w_sh_down=w_sh_down, sh_gate=sh_gate, bias=bias)
         self.k = k
-        self.shape = shape_of(w_router, w_gate_up, k, w_sh_gate_up)
+        self.router = router
+        self.shape = shape_of(w_router, w_gate_up, k, w_sh_gate_up, router)
         self.max_tokens = max_tokens
         self.ws = alloc_workspace(self.shape, max_tokens, w_router.device)
 
@@ -281,4 +287,5 @@ class MoELayer:
             raise ValueError("more tokens than the workspace was sized for")
         w = self.w
         return forward(x, w["w_router"], w["w_gate_up"], w["w_down"], self.k, w["w_sh_gate_up"],
-                       w["w_sh_down"], w["sh_gate"], w["bias"], out, topk_idx, topk_w, self.ws)
+                       w["w_sh_down"], w["sh_gate"], w["bias"], out, topk_idx, topk_w, self.ws,
+                       self.router)

@@ -23,6 +23,8 @@
 #include "moe_device.h"
 #include "moe_kernels.h"
 
+#include <string.h>
+
 namespace moe {
 
 struct GemmArgs {
@@ -33,6 +35,8 @@ struct GemmArgs {
     uint16_t *h_sh;        // [T, Fs]
     float *out;            // [T, d]   shared expert's term (plain stores)
     float *y;              // [T*k, d] routed rows, weighted (plain stores)
+    float *f;              // router logits [T, ldf] (MODE 2)
+    int ldf;
     const int32_t *perm, *counts, *offsets, *tile_start, *tile_group;
     const float *topk_w, *gate;
     int64_t T;
@@ -41,7 +45,9 @@ struct GemmArgs {
 
 constexpr int BM = kGemmBM, BN = 128, BK = 64, LDK = BK + 8;  // LDS row: 144 B, 9 x 16 B
 
-// MODE 0: gate/up (K = d).  MODE 1: down (K = F).
+// MODE 0: gate/up (K = d).  MODE 1: down (K = F).  MODE 2: dense router
+// logits f = x W_r^T (K = d, N = E, rows = tokens, no tile map), binary32
+// accumulate in the MFMA's own order (used only to shortlist experts).
 // 256 threads = 4 waves in a 2 x 2 grid; wave (wm, wn) owns rows
 // [64 wm, 64 wm + 64) and two 32-wide column blocks of B.  Each 32 x 32
 // output block comes from v_mfma_f32_32x32x16_bf16.
@@ -52,22 +58,30 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
     __shared__ int32_t row_tok[BM];
     __shared__ float row_w[BM];
 
-    const int tile = blockIdx.x;
-    if (tile >= a.tile_start[a.E + 1]) return;
-    const int g = a.tile_group[tile];
-    const bool shared = g == a.E;
-    const int m_local = (tile - a.tile_start[g]) * BM;
-    int row0, nrows;
-    if (!shared) {
-        row0 = a.offsets[g] + m_local;
-        nrows = min(BM, a.counts[g] - m_local);
+    int g = 0, row0, nrows;
+    bool shared = false;
+    if (MODE == 2) {
+        row0 = blockIdx.x * BM;
+        if (row0 >= a.T) return;
+        nrows = (int)min<int64_t>(BM, a.T - row0);
     } else {
-        row0 = m_local;
-        nrows = (int)min<int64_t>(BM, a.T - m_local);
+        const int tile = blockIdx.x;
+        if (tile >= a.tile_start[a.E + 1]) return;
+        g = a.tile_group[tile];
+        shared = g == a.E;
+        const int m_local = (tile - a.tile_start[g]) * BM;
+        if (!shared) {
+            row0 = a.offsets[g] + m_local;
+            nrows = min(BM, a.counts[g] - m_local);
+        } else {
+            row0 = m_local;
+            nrows = (int)min<int64_t>(BM, a.T - m_local);
+        }
     }
     const int Fg = shared ? a.Fs : a.F;            // width of this group's expert
-    const int N = MODE == 0 ? Fg : a.d;            // output columns (gate half for MODE 0)
-    const int K = MODE == 0 ? a.d : Fg;
+    // output columns (gate half for MODE 0) and contraction length
+    const int N = MODE == 0 ? Fg : MODE == 1 ? a.d : a.E;
+    const int K = MODE == 1 ? Fg : a.d;
     const int n0 = blockIdx.y * (MODE == 0 ? 64 : BN);
     if (n0 >= N) return;
 
@@ -76,7 +90,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
         const int r = min(i, nrows - 1);  // padding rows repeat the last row; never stored
         int tok;
         float wgt = 0.f;
-        if (!shared) {
+        if (MODE == 2) {
+            tok = row0 + r;
+        } else if (!shared) {
             const int pair = a.perm[row0 + r];
             tok = pair / a.k;
             if (MODE == 1) wgt = a.topk_w[pair];
@@ -94,9 +110,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
     const int lrow = tid >> 3, lchunk = tid & 7;
     const uint16_t *asrc[4];
     const uint16_t *bsrc[4];
-    const uint16_t *wbase = shared ? a.w_sh
-                                   : a.w + (int64_t)g * (MODE == 0 ? (int64_t)2 * a.F * a.d
-                                                                   : (int64_t)a.d * a.F);
+    const uint16_t *wbase = MODE == 2 ? a.w
+                            : shared  ? a.w_sh
+                                      : a.w + (int64_t)g * (MODE == 0 ? (int64_t)2 * a.F * a.d
+                                                                      : (int64_t)a.d * a.F);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const int r = lrow + 32 * p;
@@ -104,6 +121,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
             asrc[p] = a.x + (int64_t)row_tok[r] * a.d;
             const int wrow = r < 64 ? n0 + r : Fg + n0 + (r - 64);
             bsrc[p] = wbase + (int64_t)wrow * a.d;
+        } else if (MODE == 2) {
+            asrc[p] = a.x + (int64_t)row_tok[r] * a.d;
+            bsrc[p] = wbase + (int64_t)min(n0 + r, a.E - 1) * a.d;
         } else {
             const int rr = min(r, nrows - 1);
             asrc[p] = shared ? a.h_sh + (int64_t)(row0 + rr) * a.Fs : a.h + (int64_t)(row0 + rr) * a.F;
@@ -197,6 +217,18 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
                         f32_to_bf16_rne(silu_mul(acc[mi][0][v], acc[mi][1][v]));
                 }
             }
+    } else if (MODE == 2) {
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int row = 64 * wm + 32 * mi + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    const int col = n0 + (ni ? brow1 : brow0) + fr;
+                    if (row < nrows && col < a.E)
+                        a.f[(int64_t)(row0 + row) * a.ldf + col] = acc[mi][ni][v];
+                }
     } else {
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi)
@@ -247,6 +279,21 @@ hipError_t launch_experts_bf16(const Problem &p, hipStream_t s,
     hipLaunchKernelGGL(grouped_gemm_kernel<1>, dim3(p.max_tiles, (p.d + BN - 1) / BN), dim3(256),
                        0, s, a);
     mark(4);
+    return hipGetLastError();
+}
+
+hipError_t launch_router_gemm(const Problem &p, hipStream_t s) {
+    GemmArgs a;
+    memset(&a, 0, sizeof a);
+    a.x = static_cast<const uint16_t *>(p.x);
+    a.w = static_cast<const uint16_t *>(p.w_router);
+    a.f = p.logits;
+    a.ldf = p.E + 1;
+    a.T = p.T;
+    a.d = p.d;
+    a.E = p.E;
+    hipLaunchKernelGGL(grouped_gemm_kernel<2>, dim3((unsigned)((p.T + BM - 1) / BM), (p.E + BN - 1) / BN),
+                       dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -43,6 +43,9 @@ moe_status check_desc(const moe_desc *desc) {
         d.top_k > d.n_experts)
         return MOE_ERR_INVALID_ARG;
     if (d.dtype != MOE_F32 && d.dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+    if (d.flags != 0 && d.flags != MOE_FLAG_ROUTER_EXACT && d.flags != MOE_FLAG_ROUTER_SHORTLIST)
+        return MOE_ERR_INVALID_ARG;
+    if (d.flags == MOE_FLAG_ROUTER_SHORTLIST && d.dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
     if (d.top_k > 32 || d.n_experts > 1024 || d.d_model > 16384) return MOE_ERR_UNSUPPORTED;
     if (d.dtype == MOE_BF16 &&
         (d.d_model % 64 != 0 || d.d_expert % 64 != 0 || d.d_shared % 64 != 0))
@@ -59,7 +62,7 @@ moe_status check_T(const moe_desc *desc, int64_t T) {
 }
 
 struct Plan {
-    size_t logits, gate, counts, offsets, tile_start, tile_group, blk, rank, perm, h, h_shared, y,
+    size_t logits, wnorm, gate, counts, offsets, tile_start, tile_group, blk, rank, perm, h, h_shared, y,
         total;
     int nblk;
     int max_tiles;
@@ -79,6 +82,7 @@ Plan make_plan(const moe_desc &d, int64_t T) {
         return at;
     };
     p.logits = take((size_t)T * (d.n_experts + 1) * sizeof(float));
+    p.wnorm = take((size_t)d.n_experts * sizeof(float));
     p.gate = take((size_t)T * sizeof(float));
     p.counts = take((size_t)(d.n_experts + 1) * sizeof(int32_t));
     p.offsets = take((size_t)(d.n_experts + 1) * sizeof(int32_t));
@@ -106,6 +110,9 @@ moe::Problem make_problem(const moe_desc &d, int64_t T, const Plan &pl, void *ws
     p.bf16 = d.dtype == MOE_BF16;
     char *base = static_cast<char *>(ws);
     p.logits = reinterpret_cast<float *>(base + pl.logits);
+    p.wnorm = reinterpret_cast<float *>(base + pl.wnorm);
+    p.router = d.flags == MOE_FLAG_ROUTER_SHORTLIST ||
+               (d.flags == 0 && d.dtype == MOE_BF16 && T >= 128);
     p.gate = reinterpret_cast<float *>(base + pl.gate);
     p.counts = reinterpret_cast<int32_t *>(base + pl.counts);
     p.offsets = reinterpret_cast<int32_t *>(base + pl.offsets);

@@ -24,6 +24,8 @@ struct Problem {
     float *topk_w;
     // workspace regions
     float *logits;      // [T, E+1]
+    float *wnorm;       // [E] Euclidean norms of the router rows
+    int router;         // 0: exact canonical logits for all experts; 1: MFMA shortlist
     float *gate;        // [T]
     int32_t *counts;    // [E+1]
     int32_t *offsets;   // [E+1]
@@ -51,6 +53,8 @@ inline int64_t max_gemm_tiles(int64_t T, int k, int E, int bm, bool shared) {
     return routed + (shared ? (T + bm - 1) / bm : 0);
 }
 
+// Router logits f = x W_r^T on MFMA (binary32 accumulate, any order).
+hipError_t launch_router_gemm(const Problem &p, hipStream_t s);
 // Router: logits (canonical binary32 order) then top-k / weights / gate.
 hipError_t launch_router(const Problem &p, float *sh_gate_user, hipStream_t s);
 // Shared gate alone (used when the routing is given).

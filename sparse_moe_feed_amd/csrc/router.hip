@@ -14,6 +14,23 @@
 // is lane j holding partial j and reading 8 consecutive elements per 512-wide
 // chunk: one coalesced 16-byte load per lane.
 //
+// For many tokens the exact logits of all experts cost E dot products per
+// token on the vector ALUs.  The shortlist router instead computes
+// f = x W_r^T on MFMA (binary32 accumulate, the hardware's own order), which
+// is within Delta_e of the exact canonical logit l_e, and recomputes l_e
+// exactly only for experts that can still reach the top k:
+//   tau = k-th largest f_e, Delta_A = max Delta over those k experts,
+//   S = { e : f_e + Delta_e >= tau - Delta_A }.
+// The k experts with the largest f have l >= tau - Delta_A, so the k-th
+// largest l is at least that; any expert of the exact top k then has
+// f_e >= l_e - Delta_e >= tau - Delta_A - Delta_e, i.e. it is in S.  The
+// top k of S under the exact order (l desc, e asc) is therefore the exact
+// top k.  Delta_e = coef ||x_t|| ||W_r[e]|| + 2^-22 |f_e| bounds the two
+// summation errors (each at most n u sum|x_k w_k| <= n u ||x|| ||w||, with
+// u = 2^-23 allowing truncating adds in the MFMA) plus the bias roundings,
+// with a factor 2 to spare.  When S has more than 32 experts the exact
+// logits of all experts are computed instead.
+//
 // The selected weights use the identity softmax(l)_i / sum_sel softmax(l) =
 // exp(l_i - l_max) / sum_sel exp(l_j - l_max): the full softmax denominator
 // cancels, so only the k selected logits are needed.
@@ -170,6 +187,234 @@ __global__ __launch_bounds__(256) void router_select_kernel(
     }
 }
 
+// Euclidean norm of each router row: one wave per row.
+__global__ __launch_bounds__(256) void router_row_norm_kernel(const uint16_t *__restrict__ w,
+                                                              float *__restrict__ wnorm, int E,
+                                                              int d) {
+    const int lane = threadIdx.x & 63;
+    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (e >= E) return;
+    float s2 = 0.f;
+    for (int kk = 8 * lane; kk < d; kk += 512) {
+        float v[8];
+        load8(w + (int64_t)e * d + kk, v);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) s2 += v[q] * v[q];
+    }
+    s2 = wave_sum(s2);
+    if (lane == 0) wnorm[e] = sqrtf(s2);
+}
+
+// Exact canonical logit of expert e for the token whose 512-chunk slices
+// this wave holds (lane j: elements 512 c + 8 j .. + 8 of chunk c); the same
+// order as router_logits_kernel, so the bits agree.
+template <int NC>
+__device__ __forceinline__ float canonical_logit(const uint4 (&xs)[NC], const uint16_t *wrow,
+                                                 int d, int lane, float b) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int kk0 = 512 * c + 8 * lane;
+        if (kk0 < d) {
+            float wv[8];
+            load8(wrow + kk0, wv);
+            const uint32_t q4[4] = {xs[c].x, xs[c].y, xs[c].z, xs[c].w};
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const float xv = (q & 1) ? bf16_hi(q4[q >> 1]) : bf16_lo(q4[q >> 1]);
+                acc = __builtin_fmaf(xv, wv[q], acc);
+            }
+        }
+    }
+    for (int s = 32; s >= 1; s >>= 1) {
+        float o = __shfl_down(acc, s, kWave);
+        acc = acc + o;
+    }
+    return __shfl(acc, 0, kWave) + b;
+}
+
+// Wave-wide argmax under (value desc, expert asc); every lane gets the result.
+__device__ __forceinline__ void wave_best(float &bv, int &be) {
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, kWave);
+        const int oe = __shfl_xor(be, o, kWave);
+        if (ov > bv || (ov == bv && oe < be)) {
+            bv = ov;
+            be = oe;
+        }
+    }
+}
+
+// One wave per token; NV = ceil(E / 64) logits per lane, NC >= ceil(d / 512).
+template <int NV, int NC>
+__global__ __launch_bounds__(256) void router_select_shortlist_kernel(
+    const float *__restrict__ f, const float *__restrict__ wnorm, const uint16_t *__restrict__ x,
+    const uint16_t *__restrict__ w_router, const uint16_t *__restrict__ g,
+    const float *__restrict__ bias, int64_t ntok, int d, int E, int k, float coef,
+    int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, float *__restrict__ gate,
+    float *__restrict__ gate_user) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= ntok) return;
+
+    // this lane's slices of x_t, ||x_t||^2 and g . x_t
+    uint4 xs[NC];
+    float xx = 0.f, zg = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int kk0 = 512 * c + 8 * lane;
+        xs[c] = make_uint4(0, 0, 0, 0);
+        if (kk0 < d) {
+            xs[c] = *reinterpret_cast<const uint4 *>(x + t * d + kk0);
+            float xv[8];
+            load8(x + t * d + kk0, xv);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) xx += xv[q] * xv[q];
+            if (g) {
+                float gv[8];
+                load8(g + kk0, gv);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) zg += xv[q] * gv[q];
+            }
+        }
+    }
+    const float xnorm = sqrtf(wave_sum(xx));
+    if (g) zg = wave_sum(zg);
+
+    const float *ft = f + t * (E + 1);
+    float fb[NV], dl[NV];
+    uint32_t removed = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E) {
+            const float v = ft[e] + (bias ? bias[e] : 0.0f);
+            fb[i] = (v == v) ? v : -INFINITY;
+            dl[i] = coef * xnorm * wnorm[e] + 0x1p-22f * fabsf(fb[i]);
+        } else {
+            fb[i] = -INFINITY;
+            dl[i] = 0.f;
+            removed |= 1u << i;
+        }
+    }
+
+    // tau and Delta_A from the k largest approximate logits
+    float tau = 0.f, dA = 0.f;
+    {
+        uint32_t rem = removed;
+        for (int j = 0; j < k; ++j) {
+            float bv = -INFINITY;
+            int be = 0x7FFFFFFF;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int e = lane + 64 * i;
+                if (!((rem >> i) & 1u) && (fb[i] > bv || (fb[i] == bv && e < be))) {
+                    bv = fb[i];
+                    be = e;
+                }
+            }
+            wave_best(bv, be);
+            float mine = 0.f;
+            if ((be & 63) == lane) {
+                rem |= 1u << (be >> 6);
+#pragma unroll
+                for (int i = 0; i < NV; ++i)
+                    if (i == (be >> 6)) mine = dl[i];
+            }
+            dA = fmaxf(dA, __shfl(mine, be & 63, kWave));
+            tau = bv;
+        }
+    }
+    const float theta = tau - dA;
+    int count = 0;
+    uint64_t pass[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        pass[i] = __ballot(!((removed >> i) & 1u) && fb[i] + dl[i] >= theta);
+        count += __popcll(pass[i]);
+    }
+
+    float my_l = 0.f;
+    int my_e = 0;
+    if (count <= 32) {
+        // exact logits of the shortlist; candidate c lives in lane c
+        float lc = -INFINITY;
+        int ec = 0x7FFFFFFF;
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            uint64_t m = pass[i];
+            while (m) {
+                const int e = 64 * i + __builtin_ctzll(m);
+                m &= m - 1;
+                const float l = canonical_logit<NC>(xs, w_router + (int64_t)e * d, d, lane,
+                                                    bias ? bias[e] : 0.0f);
+                if (lane == c) {
+                    lc = (l == l) ? l : -INFINITY;
+                    ec = e;
+                }
+                ++c;
+            }
+        }
+        bool gone = lane >= count;
+        for (int j = 0; j < k; ++j) {
+            float bv = gone ? -INFINITY : lc;
+            int be = gone ? 0x7FFFFFFF : ec;
+            wave_best(bv, be);
+            if (be == ec) gone = true;
+            if (lane == j) {
+                my_l = bv;
+                my_e = be;
+            }
+        }
+    } else {
+        // exact logits of every expert, lane-strided as in the plain router
+        float lv[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) lv[i] = -INFINITY;
+        for (int e = 0; e < E; ++e) {
+            const float l = canonical_logit<NC>(xs, w_router + (int64_t)e * d, d, lane,
+                                                bias ? bias[e] : 0.0f);
+            if ((e & 63) == lane) {
+#pragma unroll
+                for (int i = 0; i < NV; ++i)
+                    if (i == (e >> 6)) lv[i] = (l == l) ? l : -INFINITY;
+            }
+        }
+        uint32_t rem = removed;
+        for (int j = 0; j < k; ++j) {
+            float bv = -INFINITY;
+            int be = 0x7FFFFFFF;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int e = lane + 64 * i;
+                if (!((rem >> i) & 1u) && (lv[i] > bv || (lv[i] == bv && e < be))) {
+                    bv = lv[i];
+                    be = e;
+                }
+            }
+            wave_best(bv, be);
+            if ((be & 63) == lane) rem |= 1u << (be >> 6);
+            if (lane == j) {
+                my_l = bv;
+                my_e = be;
+            }
+        }
+    }
+    const float lmax = __shfl(my_l, 0, kWave);
+    const float ex = lane < k ? expf(my_l - lmax) : 0.0f;
+    const float z = wave_sum(ex);
+    if (lane < k) {
+        topk_idx[t * k + lane] = my_e;
+        topk_w[t * k + lane] = ex / z;
+    }
+    if (g && lane == 0) {
+        const float s = 1.0f / (1.0f + expf(-zg));
+        gate[t] = s;
+        if (gate_user) gate_user[t] = s;
+    }
+}
+
 // s_t = sigmoid(g . x_t): one wave per token (routing-given entry point).
 template <typename T>
 __global__ __launch_bounds__(256) void shared_gate_kernel(const T *__restrict__ x,
@@ -207,7 +452,45 @@ static hipError_t launch_logits(const Problem &p, hipStream_t s) {
     return hipGetLastError();
 }
 
+static hipError_t launch_shortlist(const Problem &p, float *sh_gate_user, hipStream_t s) {
+    hipError_t err = launch_router_gemm(p, s);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(router_row_norm_kernel, dim3((p.E + 3) / 4), dim3(256), 0, s,
+                       static_cast<const uint16_t *>(p.w_router), p.wnorm, p.E, p.d);
+    const int nchunk = (p.d + 511) / 512;
+    const int nc = (p.d + 511) / 512;
+    const double u = 1.0 / 8388608.0;  // 2^-23
+    const float coef = (float)(2.0 * (p.d * u + (8.0 * nchunk + 7.0) * u));
+    const int nv = (p.E + 63) / 64;
+    const dim3 grid((unsigned)((p.T + 3) / 4)), block(256);
+    const uint16_t *x = static_cast<const uint16_t *>(p.x);
+    const uint16_t *wr = static_cast<const uint16_t *>(p.w_router);
+    const uint16_t *g = static_cast<const uint16_t *>(p.sh_gate);
+#define MOE_SL(NV, NC)                                                                          \
+    hipLaunchKernelGGL((router_select_shortlist_kernel<NV, NC>), grid, block, 0, s, p.logits,   \
+                       p.wnorm, x, wr, g, p.router_bias, p.T, p.d, p.E, p.k, coef, p.topk_idx,  \
+                       p.topk_w, p.gate, sh_gate_user)
+#define MOE_SL_NV(NC)                                                                           \
+    do {                                                                                        \
+        if (nv <= 1) MOE_SL(1, NC);                                                             \
+        else if (nv <= 2) MOE_SL(2, NC);                                                        \
+        else if (nv <= 4) MOE_SL(4, NC);                                                        \
+        else if (nv <= 8) MOE_SL(8, NC);                                                        \
+        else MOE_SL(16, NC);                                                                    \
+    } while (0)
+    if (nc <= 1) MOE_SL_NV(1);
+    else if (nc <= 2) MOE_SL_NV(2);
+    else if (nc <= 5) MOE_SL_NV(5);
+    else if (nc <= 8) MOE_SL_NV(8);
+    else if (nc <= 16) MOE_SL_NV(16);
+    else MOE_SL_NV(32);
+#undef MOE_SL_NV
+#undef MOE_SL
+    return hipGetLastError();
+}
+
 hipError_t launch_router(const Problem &p, float *sh_gate_user, hipStream_t s) {
+    if (p.router == 1) return launch_shortlist(p, sh_gate_user, s);
     hipError_t err = p.bf16 ? launch_logits<uint16_t>(p, s) : launch_logits<float>(p, s);
     if (err != hipSuccess) return err;
     const int nv = (p.E + 63) / 64;

@@ -32,12 +32,13 @@ def test_exports_every_declared_symbol(L):
         assert hasattr(L, n), n
 
 
-def desc(d=256, E=16, k=4, F=128, Fs=64, dtype=moe.MOE_BF16):
-    return moe.moe_desc(d, E, k, F, Fs, dtype)
+def desc(d=256, E=16, k=4, F=128, Fs=64, dtype=moe.MOE_BF16, flags=0):
+    return moe.moe_desc(d, E, k, F, Fs, dtype, flags)
 
 
 @pytest.mark.parametrize("bad", [
-    dict(d=0), dict(E=0), dict(k=0), dict(k=17), dict(F=0), dict(Fs=-1), dict(dtype=7)])
+    dict(d=0), dict(E=0), dict(k=0), dict(k=17), dict(F=0), dict(Fs=-1), dict(dtype=7),
+    dict(flags=3), dict(flags=-1)])
 def test_invalid_desc(L, bad):
     D = desc(**bad)
     assert L.moe_workspace_size(ctypes.byref(D), 10) == 0
@@ -46,7 +47,8 @@ def test_invalid_desc(L, bad):
 
 
 @pytest.mark.parametrize("bad", [
-    dict(k=33, E=64), dict(E=2048, k=4), dict(d=100), dict(F=96), dict(Fs=32), dict(d=32768)])
+    dict(k=33, E=64), dict(E=2048, k=4), dict(d=100), dict(F=96), dict(Fs=32), dict(d=32768),
+    dict(dtype=moe.MOE_F32, flags=moe.MOE_FLAG_ROUTER_SHORTLIST)])
 def test_unsupported_desc(L, bad):
     D = desc(**bad)
     lay = moe.moe_workspace_layout()

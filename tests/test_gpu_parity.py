@@ -235,3 +235,66 @@ def test_full_config(full_layer, c):
                                       *[lay[n] for n in SH], bias=bias)
     r = assert_out(out[toks], ref_out)
     announce(f"{cfg.name}: max|err|/rms = {r:.3e}")
+
+
+# ------------------------------------------------------------------ shortlist router
+
+def gpu_route(inp, k, router):
+    idx, w, _ = moe.route(to_dev(inp["x"]), to_dev(inp["w_router"]), k, bias=to_dev(inp.get("bias")),
+                          router=router)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), w.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,d,E,k,case", [
+    (300, 256, 64, 10, "plain"),
+    (260, 2560, 512, 10, "pages' shapes"),
+    (129, 640, 96, 7, "ragged chunk (d % 512 != 0)"),
+    (150, 128, 64, 6, "zero router: > 32 candidates, exact fallback"),
+    (200, 256, 16, 4, "duplicate rows"),
+    (180, 512, 128, 12, "large bias on a few experts"),
+])
+def test_shortlist_router_equals_exact(T, d, E, k, case):
+    """MFMA shortlist + exact recompute selects exactly what the canonical
+    router over all experts selects, and both match the oracle."""
+    inp = W.small_case(T, d, E, k, 64, 0, "bf16", seed=T + d)
+    if case.startswith("zero"):
+        inp["w_router"] = np.zeros_like(inp["w_router"])
+    if case == "duplicate rows":
+        inp["w_router"] = inp["w_router"].copy()
+        inp["w_router"][7] = inp["w_router"][2]
+        inp["w_router"][11] = inp["w_router"][2]
+    if case.startswith("large bias"):
+        b = np.zeros(E, np.float32)
+        b[[3, 40, 77]] = [4.0, 2.5, 6.0]
+        inp["bias"] = b
+    announce(f"shortlist vs exact router: {case}")
+    i_ex, w_ex = gpu_route(inp, k, "exact")
+    i_sl, w_sl = gpu_route(inp, k, "shortlist")
+    ref_idx, ref_w = oracle.route(inp["x"], inp["w_router"], k, bias=inp.get("bias"))
+    assert np.array_equal(i_ex, ref_idx)
+    assert np.array_equal(i_sl, ref_idx)
+    assert np.array_equal(w_ex, w_sl)
+    assert np.abs(w_sl - ref_w).max() <= W_TOL
+
+
+def test_shortlist_bound_is_far_from_tight():
+    """Observed |f - l| of the MFMA logits stays well inside the bound the
+    shortlist relies on (Delta = coef ||x|| ||w_e||, without the bias term)."""
+    T, d, E, k = 256, 2560, 512, 10
+    inp = W.small_case(T, d, E, k, 64, 0, "bf16", seed=77)
+    shape = moe.Shape(d, E, k, 64, 0, torch.bfloat16, "shortlist")
+    ws = moe.alloc_workspace(shape, T)
+    announce("shortlist bound")
+    moe.route(to_dev(inp["x"]), to_dev(inp["w_router"]), k, ws=ws, router="shortlist")
+    torch.cuda.synchronize()
+    lay = moe.workspace_layout(shape, T)
+    f = ws.cpu().numpy()[lay.logits:lay.logits + 4 * T * (E + 1)].view(np.float32).reshape(T, E + 1)[:, :E]
+    l = oracle.router_logits(inp["x"], inp["w_router"]).astype(np.float64)
+    xf = W.bf16_bits_to_f32(inp["x"]).astype(np.float64)
+    wf = W.bf16_bits_to_f32(inp["w_router"]).astype(np.float64)
+    u = 2.0 ** -23
+    coef = 2 * (d * u + (8 * ((d + 511) // 512) + 7) * u)
+    delta = coef * np.linalg.norm(xf, axis=1)[:, None] * np.linalg.norm(wf, axis=1)[None, :]
+    ratio = np.abs(f.astype(np.float64) - l) / delta
+    assert ratio.max() < 0.05, ratio.max()
