@@ -164,7 +164,19 @@ def main():
     ap.add_argument("--also", default="3", help="extra workloads reported in the line")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (HBM counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n * 4}))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: measures one GPU only (the layer is not sharded across GPUs in this "
