@@ -140,7 +140,71 @@ __global__ __launch_bounds__(kCountBlock) void route_scatter_kernel(
     }
 }
 
+// All of the above in one block of 1024 threads when every token fits one
+// histogram block (T <= 256): no block prefix is needed and one launch
+// replaces three.
+__global__ __launch_bounds__(1024) void route_permute_small_kernel(
+    const int32_t *__restrict__ topk_idx, int ntok, int k, int E, int bm, int has_shared,
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ tile_start,
+    int32_t *__restrict__ tile_group, int32_t *__restrict__ row_of, int32_t *__restrict__ perm) {
+    extern __shared__ uint32_t bits[];  // [E][kWords], then offsets [E]
+    int32_t *s_off = reinterpret_cast<int32_t *>(bits + E * kWords);
+    for (int i = threadIdx.x; i < E * kWords; i += 1024) bits[i] = 0;
+    __syncthreads();
+    const int t = threadIdx.x;
+    const bool valid = t < ntok;
+    const int word = t >> 5;
+    const uint32_t bit = 1u << (t & 31);
+    if (valid)
+        for (int j = 0; j < k; ++j)
+            atomicOr(&bits[clamp_expert(topk_idx[t * k + j], E) * kWords + word], bit);
+    __syncthreads();
+    const int e = threadIdx.x;
+    int total = 0;
+    if (e < E) {
+#pragma unroll
+        for (int w = 0; w < kWords; ++w) total += __popc(bits[e * kWords + w]);
+        counts[e] = total;
+    }
+    const int tiles = e < E ? (total + bm - 1) / bm : 0;
+    int all_rows, all_tiles;
+    const int off = block_exclusive_scan(e < E ? total : 0, &all_rows);
+    const int ts = block_exclusive_scan(tiles, &all_tiles);
+    if (e < E) {
+        offsets[e] = off;
+        s_off[e] = off;
+        tile_start[e] = ts;
+        for (int i = 0; i < tiles; ++i) tile_group[ts + i] = e;
+    }
+    if (e == 0) {
+        offsets[E] = all_rows;
+        counts[E] = ntok;
+        tile_start[E] = all_tiles;
+        tile_start[E + 1] = all_tiles + (has_shared ? (ntok + bm - 1) / bm : 0);
+    }
+    if (has_shared)
+        for (int i = threadIdx.x; i < (ntok + bm - 1) / bm; i += 1024) tile_group[all_tiles + i] = E;
+    __syncthreads();
+    if (valid)
+        for (int j = 0; j < k; ++j) {
+            const int ee = clamp_expert(topk_idx[t * k + j], E);
+            const uint32_t *b = bits + ee * kWords;
+            int r = __popc(b[word] & (bit - 1u));
+            for (int w = 0; w < word; ++w) r += __popc(b[w]);
+            const int pos = s_off[ee] + r;
+            perm[pos] = t * k + j;
+            row_of[t * k + j] = pos;
+        }
+}
+
 hipError_t launch_permute(const Problem &p, int bm, hipStream_t s) {
+    if (p.nblk == 1) {
+        const size_t lds = (size_t)p.E * (kWords + 1) * sizeof(uint32_t);
+        hipLaunchKernelGGL(route_permute_small_kernel, dim3(1), dim3(1024), lds, s, p.topk_idx,
+                           (int)p.T, p.k, p.E, bm, p.Fs > 0 ? 1 : 0, p.counts, p.offsets,
+                           p.tile_start, p.tile_group, p.rank, p.perm);
+        return hipGetLastError();
+    }
     const size_t lds = (size_t)p.E * kWords * sizeof(uint32_t);
     hipLaunchKernelGGL(route_count_kernel, dim3(p.nblk), dim3(kCountBlock), lds, s, p.topk_idx,
                        p.T, p.k, p.E, p.nblk, p.rank, p.blk);

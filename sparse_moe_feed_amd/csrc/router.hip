@@ -45,9 +45,13 @@ namespace moe {
 
 // Rows 0..E-1 of the extended router matrix are W_r, row E is the shared gate
 // vector g (absent when g == nullptr).  Block (x, y) owns tokens
-// [TT x, TT x + TT) and rows [16 y, 16 y + 16); each wave owns 4 rows.  The
-// block's token rows are staged in LDS.
-template <typename T, int TT>
+// [TT x, TT x + TT) and rows [4 RW y, 4 RW y + 4 RW); each wave owns RW rows.
+// The block's token rows are staged in LDS.  For bf16 rows of at most
+// kMaxChunks 512-element chunks, all of a row's chunk loads are issued before
+// any arithmetic, so a row costs one memory round trip.
+constexpr int kMaxChunks = 8;
+
+template <typename T, int TT, int RW>
 __global__ __launch_bounds__(256) void router_logits_kernel(
     const T *__restrict__ x, const T *__restrict__ w_router, const T *__restrict__ g,
     const float *__restrict__ bias, float *__restrict__ logits, int64_t ntok, int d, int E) {
@@ -74,36 +78,64 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
     __syncthreads();
 
     const bool vec = (d % 8) == 0;
-    for (int rr = 0; rr < 4; ++rr) {
-        const int row = blockIdx.y * 16 + wave * 4 + rr;
+    const bool preload = vec && sizeof(T) == 2 && d <= 512 * kMaxChunks;
+    for (int rr = 0; rr < RW; ++rr) {
+        const int row = blockIdx.y * 4 * RW + wave * RW + rr;
         if (row > E || (row == E && g == nullptr)) break;
         const T *wrow = row < E ? w_router + (int64_t)row * d : g;
         float acc[TT];
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) acc[tt] = 0.0f;
-        for (int chunk = 0; chunk < d; chunk += 512) {
-            const int kk0 = chunk + 8 * lane;
-            if (kk0 >= d) continue;
-            float wv[8];
-            if (vec) {
-                load8(wrow + kk0, wv);
-            } else {
+        if (preload) {
+            uint4 wq[kMaxChunks];
 #pragma unroll
-                for (int q = 0; q < 8; ++q) wv[q] = kk0 + q < d ? to_f32(wrow[kk0 + q]) : 0.0f;
+            for (int c = 0; c < kMaxChunks; ++c) {
+                const int kk0 = 512 * c + 8 * lane;
+                wq[c] = kk0 < d ? *reinterpret_cast<const uint4 *>(wrow + kk0) : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
-            for (int tt = 0; tt < TT; ++tt) {
-                float xv[8];
+            for (int c = 0; c < kMaxChunks; ++c) {
+                const int kk0 = 512 * c + 8 * lane;
+                if (512 * c >= d) break;
+                if (kk0 < d) {
+                    const uint32_t q4[4] = {wq[c].x, wq[c].y, wq[c].z, wq[c].w};
+#pragma unroll
+                    for (int tt = 0; tt < TT; ++tt) {
+                        float xv[8];
+                        load8(xs + tt * d + kk0, xv);
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) {
+                            const float wv = (q & 1) ? bf16_hi(q4[q >> 1]) : bf16_lo(q4[q >> 1]);
+                            acc[tt] = __builtin_fmaf(xv[q], wv, acc[tt]);
+                        }
+                    }
+                }
+            }
+        } else {
+            for (int chunk = 0; chunk < d; chunk += 512) {
+                const int kk0 = chunk + 8 * lane;
+                if (kk0 >= d) continue;
+                float wv[8];
                 if (vec) {
-                    load8(xs + tt * d + kk0, xv);
+                    load8(wrow + kk0, wv);
                 } else {
 #pragma unroll
-                    for (int q = 0; q < 8; ++q)
-                        xv[q] = kk0 + q < d ? to_f32(xs[tt * d + kk0 + q]) : 0.0f;
+                    for (int q = 0; q < 8; ++q) wv[q] = kk0 + q < d ? to_f32(wrow[kk0 + q]) : 0.0f;
                 }
 #pragma unroll
-                for (int q = 0; q < 8; ++q)
-                    if (kk0 + q < d) acc[tt] = __builtin_fmaf(xv[q], wv[q], acc[tt]);
+                for (int tt = 0; tt < TT; ++tt) {
+                    float xv[8];
+                    if (vec) {
+                        load8(xs + tt * d + kk0, xv);
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 8; ++q)
+                            xv[q] = kk0 + q < d ? to_f32(xs[tt * d + kk0 + q]) : 0.0f;
+                    }
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+                        if (kk0 + q < d) acc[tt] = __builtin_fmaf(xv[q], wv[q], acc[tt]);
+                }
             }
         }
 #pragma unroll
@@ -430,24 +462,31 @@ __global__ __launch_bounds__(256) void shared_gate_kernel(const T *__restrict__ 
     if (lane == 0) gate[t] = 1.0f / (1.0f + expf(-a));
 }
 
+// Few tokens: one row per wave (more blocks in flight); many: four.
 template <typename T>
 static hipError_t launch_logits(const Problem &p, hipStream_t s) {
     const size_t row_bytes = (size_t)p.d * sizeof(T);
     const dim3 block(256);
-    const unsigned row_groups = (unsigned)((p.E + 1 + 15) / 16);
     const T *x = static_cast<const T *>(p.x);
     const T *wr = static_cast<const T *>(p.w_router);
     const T *g = static_cast<const T *>(p.sh_gate);
-#define MOE_LOGITS(TT)                                                                       \
-    do {                                                                                     \
-        dim3 gr((unsigned)((p.T + TT - 1) / TT), row_groups);                                \
-        hipLaunchKernelGGL((router_logits_kernel<T, TT>), gr, block, TT * row_bytes, s, x,   \
-                           wr, g, p.router_bias, p.logits, p.T, p.d, p.E);                   \
+#define MOE_LOGITS(TT, RW)                                                                       \
+    do {                                                                                         \
+        dim3 gr((unsigned)((p.T + TT - 1) / TT), (unsigned)((p.E + 1 + 4 * RW - 1) / (4 * RW))); \
+        hipLaunchKernelGGL((router_logits_kernel<T, TT, RW>), gr, block, TT * row_bytes, s, x,   \
+                           wr, g, p.router_bias, p.logits, p.T, p.d, p.E);                       \
     } while (0)
-    if (8 * row_bytes <= 65536) MOE_LOGITS(8);
-    else if (4 * row_bytes <= 65536) MOE_LOGITS(4);
-    else if (2 * row_bytes <= 65536) MOE_LOGITS(2);
-    else MOE_LOGITS(1);
+    if (p.T <= 256) {
+        if (8 * row_bytes <= 65536) MOE_LOGITS(8, 1);
+        else if (4 * row_bytes <= 65536) MOE_LOGITS(4, 1);
+        else if (2 * row_bytes <= 65536) MOE_LOGITS(2, 1);
+        else MOE_LOGITS(1, 1);
+    } else {
+        if (8 * row_bytes <= 65536) MOE_LOGITS(8, 4);
+        else if (4 * row_bytes <= 65536) MOE_LOGITS(4, 4);
+        else if (2 * row_bytes <= 65536) MOE_LOGITS(2, 4);
+        else MOE_LOGITS(1, 4);
+    }
 #undef MOE_LOGITS
     return hipGetLastError();
 }

@@ -130,10 +130,12 @@ def test_bias_sends_every_token_to_one_expert(T, d, E, k, F):
     check_case(inp, k, "bias -> expert 5")
 
 
-def test_workspace_grouping_matches_routing():
+@pytest.mark.parametrize("T", [700, 200])
+def test_workspace_grouping_matches_routing(T):
     """counts / offsets / perm in the workspace are exactly the grouping the
-    routing implies, rows of one expert in ascending pair id."""
-    T, d, E, k, F, Fs = 700, 128, 24, 4, 64, 64
+    routing implies, rows of one expert in ascending pair id (multi-block
+    histogram at T=700, the single-block path at T=200)."""
+    d, E, k, F, Fs = 128, 24, 4, 64, 64
     inp = W.small_case(T, d, E, k, F, Fs, "bf16", seed=33)
     shape = moe.Shape(d, E, k, F, Fs, torch.bfloat16)
     ws = moe.alloc_workspace(shape, T)
