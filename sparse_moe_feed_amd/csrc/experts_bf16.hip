@@ -27,21 +27,6 @@
 
 namespace moe {
 
-struct GemmArgs {
-    const uint16_t *x;
-    const uint16_t *w;     // gate/up: [E, 2F, d]   down: [E, d, F]
-    const uint16_t *w_sh;  // gate/up: [2Fs, d]     down: [d, Fs]
-    uint16_t *h;           // [T*k, F]
-    uint16_t *h_sh;        // [T, Fs]
-    float *out;            // [T, d]   shared expert's term (plain stores)
-    float *y;              // [T*k, d] routed rows, weighted (plain stores)
-    float *f;              // router logits [T, ldf] (MODE 2)
-    int ldf;
-    const int32_t *perm, *counts, *offsets, *tile_start, *tile_group;
-    const float *topk_w, *gate;
-    int64_t T;
-    int d, E, k, F, Fs;
-};
 
 constexpr int BM = kGemmBM, BN = 128, BK = 64, LDK = BK + 8;  // LDS row: 144 B, 9 x 16 B
 
@@ -58,14 +43,16 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
     __shared__ int32_t row_tok[BM];
     __shared__ float row_w[BM];
 
+    int mt, nt;
+    if (!raster_tile(a.nm, a.nn, a.gm, mt, nt)) return;
     int g = 0, row0, nrows;
     bool shared = false;
     if (MODE == 2) {
-        row0 = blockIdx.x * BM;
+        row0 = mt * BM;
         if (row0 >= a.T) return;
         nrows = (int)min<int64_t>(BM, a.T - row0);
     } else {
-        const int tile = blockIdx.x;
+        const int tile = mt;
         if (tile >= a.tile_start[a.E + 1]) return;
         g = a.tile_group[tile];
         shared = g == a.E;
@@ -82,7 +69,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
     // output columns (gate half for MODE 0) and contraction length
     const int N = MODE == 0 ? Fg : MODE == 1 ? a.d : a.E;
     const int K = MODE == 1 ? Fg : a.d;
-    const int n0 = blockIdx.y * (MODE == 0 ? 64 : BN);
+    const int n0 = nt * (MODE == 0 ? 64 : BN);
     if (n0 >= N) return;
 
     const int tid = threadIdx.x;
@@ -159,7 +146,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
         *reinterpret_cast<uint4 *>(&Bs[buf][off + 96 * LDK]) = rb3;                 \
     } while (0)
 
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = wave_id();
     const int wm = wave >> 1, wn = wave & 1;
     const int brow0 = MODE == 0 ? 32 * wn : 64 * wn;
     const int brow1 = MODE == 0 ? 64 + 32 * wn : 64 * wn + 32;
@@ -270,14 +257,18 @@ hipError_t launch_experts_bf16(const Problem &p, hipStream_t s,
     a.Fs = p.Fs;
 
     const int fmax = p.F > p.Fs ? p.F : p.Fs;
+    auto grid = [](const GemmArgs &g) { return dim3((unsigned)(8 * ((g.nm * g.nn + 7) / 8))); };
     a.w = static_cast<const uint16_t *>(p.w_gate_up);
     a.w_sh = static_cast<const uint16_t *>(p.w_sh_gate_up);
-    hipLaunchKernelGGL(grouped_gemm_kernel<0>, dim3(p.max_tiles, fmax / 64), dim3(256), 0, s, a);
+    a.nm = p.max_tiles;
+    a.nn = fmax / 64;
+    a.gm = 0;  // N fastest: a tile's column blocks run back to back
+    hipLaunchKernelGGL(grouped_gemm_kernel<0>, grid(a), dim3(256), 0, s, a);
     mark(3);
     a.w = static_cast<const uint16_t *>(p.w_down);
     a.w_sh = static_cast<const uint16_t *>(p.w_sh_down);
-    hipLaunchKernelGGL(grouped_gemm_kernel<1>, dim3(p.max_tiles, (p.d + BN - 1) / BN), dim3(256),
-                       0, s, a);
+    a.nn = (p.d + BN - 1) / BN;
+    hipLaunchKernelGGL(grouped_gemm_kernel<1>, grid(a), dim3(256), 0, s, a);
     mark(4);
     return hipGetLastError();
 }
@@ -292,7 +283,10 @@ hipError_t launch_router_gemm(const Problem &p, hipStream_t s) {
     a.T = p.T;
     a.d = p.d;
     a.E = p.E;
-    hipLaunchKernelGGL(grouped_gemm_kernel<2>, dim3((unsigned)((p.T + BM - 1) / BM), (p.E + BN - 1) / BN),
+    a.nm = (int)((p.T + BM - 1) / BM);
+    a.nn = (p.E + BN - 1) / BN;
+    a.gm = 8;
+    hipLaunchKernelGGL(grouped_gemm_kernel<2>, dim3((unsigned)(8 * ((a.nm * a.nn + 7) / 8))),
                        dim3(256), 0, s, a);
     return hipGetLastError();
 }

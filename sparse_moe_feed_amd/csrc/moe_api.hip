@@ -162,18 +162,31 @@ bool use_decode_path(const moe::Problem &p) {
     return p.T * p.k <= (int64_t)16 * p.E;
 }
 
+// 256 x 256 tiles once experts average 192+ rows (their 32-bit row offsets
+// must fit: T*k*max(d, F) and T*d below 2^32).
+bool use_gemm256_path(const moe::Problem &p) {
+    if (!p.bf16 || p.F % 128 || p.Fs % 128) return false;
+    const int64_t pairs = p.T * p.k;
+    const int64_t widest = p.d > p.F ? p.d : p.F;
+    if (pairs * widest >= ((int64_t)1 << 32) || p.T * (int64_t)(p.E + 1) >= ((int64_t)1 << 32))
+        return false;
+    return pairs >= (int64_t)192 * p.E;
+}
+
 // Stages 2..5 of a call: permutation, gate/up, down, combine.
 moe_status run_experts(moe::Problem p, hipStream_t s) {
     const bool decode = use_decode_path(p);
-    const int bm = decode ? moe::kDecodeBM : moe::kGemmBM;
+    const bool big = !decode && use_gemm256_path(p);
+    const int bm = decode ? moe::kDecodeBM : big ? moe::kGemm256BM : moe::kGemmBM;
     p.max_tiles = (int)moe::max_gemm_tiles(p.T, p.k, p.E, bm, p.Fs > 0);
     hipError_t err = moe::launch_permute(p, bm, s);
     mark_stage(2, s);
     auto mark = [&](int i) { mark_stage(i, s); };
     if (err == hipSuccess)
-        err = !p.bf16 ? moe::launch_experts_f32(p, s, mark)
-                      : decode ? moe::launch_experts_decode(p, s, mark)
-                               : moe::launch_experts_bf16(p, s, mark);
+        err = !p.bf16  ? moe::launch_experts_f32(p, s, mark)
+              : decode ? moe::launch_experts_decode(p, s, mark)
+              : big    ? moe::launch_experts_gemm256(p, s, mark)
+                       : moe::launch_experts_bf16(p, s, mark);
     if (err == hipSuccess) err = moe::launch_combine(p, s);
     mark_stage(5, s);
     g_n_stage_events = 0;

@@ -11,6 +11,7 @@ constexpr int kWave = 64;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Storage types: bfloat16 travels as its 16-bit pattern.
 struct bf16_t {
@@ -55,6 +56,35 @@ __device__ __forceinline__ float wave_sum(float v) {
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
     return v;
 }
+
+// Block -> (m, n) tile for a GEMM grid of nm x nn tiles launched as a 1-D
+// grid of 8 * ceil(nm * nn / 8) blocks.  Workgroups are dispatched to the 8
+// XCDs round robin, so block b runs on XCD b % 8; logical tile ids are made
+// contiguous per XCD, and within an XCD consecutive ids sweep gm M-tiles
+// before advancing N, so the blocks that run together on one XCD share both
+// their A rows and their B columns through that XCD's L2.  gm == 0 instead
+// takes the plain order with N fastest.  Returns false for padding blocks.
+__device__ __forceinline__ bool raster_tile(int nm, int nn, int gm, int &m, int &n) {
+    const int nblocks = nm * nn;
+    const int b = blockIdx.x;
+    if (gm == 0) {
+        if (b >= nblocks) return false;
+        m = b / nn;
+        n = b - m * nn;
+        return true;
+    }
+    const int per = (nblocks + 7) / 8;
+    const int L = (b & 7) * per + (b >> 3);
+    if (L >= nblocks) return false;
+    const int span = gm * nn;
+    const int group = L / span, idx = L - group * span;
+    const int rows = min(gm, nm - group * gm);  // M-tiles in this (possibly short) group
+    m = group * gm + idx % rows;
+    n = idx / rows;
+    return true;
+}
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
     return g / (1.0f + __expf(-g)) * u;

@@ -44,6 +44,7 @@ struct Problem {
 constexpr int kCountBlock = 256;     // tokens per histogram block
 constexpr int kGemmBM = 128;         // rows per grouped-GEMM tile (MFMA path)
 constexpr int kDecodeBM = 32;        // rows per tile of the weight-streaming (decode) path
+constexpr int kGemm256BM = 256;      // rows per tile of the large-tile GEMM path
 
 // Upper bound on sum_e ceil(c_e / bm) + ceil(T / bm) over any routing with
 // sum_e c_e = T*k: each non-empty expert adds at most one partial tile.
@@ -53,8 +54,29 @@ inline int64_t max_gemm_tiles(int64_t T, int k, int E, int bm, bool shared) {
     return routed + (shared ? (T + bm - 1) / bm : 0);
 }
 
+// Arguments of the LDS-tiled grouped GEMM kernels (bf16 in, fp32 accumulate).
+struct GemmArgs {
+    const uint16_t *x;
+    const uint16_t *w;     // gate/up: [E, 2F, d]   down: [E, d, F]
+    const uint16_t *w_sh;  // gate/up: [2Fs, d]     down: [d, Fs]
+    uint16_t *h;           // [T*k, F]
+    uint16_t *h_sh;        // [T, Fs]
+    float *out;            // [T, d]   shared expert's term (plain stores)
+    float *y;              // [T*k, d] routed rows, weighted (plain stores)
+    float *f;              // router logits [T, ldf] (MODE 2)
+    int ldf;
+    const int32_t *perm, *counts, *offsets, *tile_start, *tile_group;
+    const float *topk_w, *gate;
+    int64_t T;
+    int d, E, k, F, Fs;
+    int nm, nn, gm;        // M-tiles, N-tiles and raster group height (raster_tile)
+};
+
 // Router logits f = x W_r^T on MFMA (binary32 accumulate, any order).
 hipError_t launch_router_gemm(const Problem &p, hipStream_t s);
+// Large-tile (256 x 256) grouped GEMM expert stage for many tokens per expert.
+hipError_t launch_experts_gemm256(const Problem &p, hipStream_t s,
+                                  const std::function<void(int)> &mark);
 // Router: logits (canonical binary32 order) then top-k / weights / gate.
 hipError_t launch_router(const Problem &p, float *sh_gate_user, hipStream_t s);
 // Shared gate alone (used when the routing is given).

@@ -61,6 +61,8 @@ def test_tiny_fp32_layer():
     (40, 256, 64, 4, 128, 128),     # weight-streaming path (few rows per expert)
     (7, 384, 128, 6, 256, 0),       # weight-streaming path, no shared expert
     (100, 256, 16, 2, 128, 128),    # streaming path, experts with 17..32+ rows
+    (1000, 256, 16, 4, 128, 128),   # 256-row tiles (partial tiles)
+    (1200, 384, 8, 2, 256, 128),    # 256-row tiles, 2 per expert; d % 256 = 128
 ])
 def test_small_bf16_layers(T, d, E, k, F, Fs):
     inp = W.small_case(T, d, E, k, F, Fs, "bf16", seed=T + E)
