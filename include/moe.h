@@ -111,8 +111,9 @@ size_t moe_workspace_size(const moe_desc *desc, int64_t T);
  *                             ascending pair id
  *   h        [T*k, F]         gated activations of the routed rows (bf16 / f32)
  *   h_shared [T, Fs]          gated activations of the shared expert
- *   y        float [T*k, d]   w[t,j] * expert output of each routed row; the
- *                             combine adds a token's k rows to the shared term */
+ *   y        [T*k, d]         w[t,j] * expert output of each routed row (bf16 /
+ *                             f32, as h); the combine adds a token's k rows to
+ *                             the shared term in binary32 */
 typedef struct {
     size_t logits, gate, counts, offsets, perm, h, h_shared, y, total;
 } moe_workspace_layout;

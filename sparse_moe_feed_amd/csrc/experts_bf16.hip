@@ -226,9 +226,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
                     const int row = 64 * wm + 32 * mi + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
                     const int col = n0 + (ni ? brow1 : brow0) + fr;
                     if (row < nrows && col < a.d) {
-                        float *dst = shared ? a.out + (int64_t)row_tok[row] * a.d
-                                            : a.y + (int64_t)(row0 + row) * a.d;
-                        dst[col] = row_w[row] * acc[mi][ni][v];
+                        const float val = row_w[row] * acc[mi][ni][v];
+                        if (shared) a.out[(int64_t)row_tok[row] * a.d + col] = val;
+                        else a.y[(int64_t)(row0 + row) * a.d + col] = f32_to_bf16_rne(val);
                     }
                 }
     }
@@ -241,7 +241,7 @@ hipError_t launch_experts_bf16(const Problem &p, hipStream_t s,
     a.h = static_cast<uint16_t *>(p.h);
     a.h_sh = static_cast<uint16_t *>(p.h_shared);
     a.out = p.out;
-    a.y = p.y;
+    a.y = static_cast<uint16_t *>(p.y);
     a.perm = p.perm;
     a.counts = p.counts;
     a.offsets = p.offsets;

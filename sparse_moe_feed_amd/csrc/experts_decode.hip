@@ -28,7 +28,8 @@ struct DecodeArgs {
     const uint16_t *w_sh;  // gate/up: [2Fs, d]     down: [d, Fs]
     uint16_t *h;           // [T*k, F]
     uint16_t *h_sh;        // [T, Fs]
-    float *out, *y;
+    float *out;
+    uint16_t *y;           // [T*k, d] weighted routed rows (bf16)
     const int32_t *perm, *counts, *offsets, *tile_start, *tile_group;
     const float *topk_w, *gate;
     int64_t T;
@@ -214,9 +215,9 @@ __device__ void decode_down_body(const DecodeArgs &a, const TileInfo &ti, const 
                 const int row = 16 * h + 4 * (lane >> 4) + i;
                 const int col = ncol + 16 * n + rl;
                 if (row < ti.nrows && col < a.d) {
-                    float *dst = ti.shared ? a.out + (int64_t)row_tok[row] * a.d
-                                           : a.y + (int64_t)(ti.row0 + row) * a.d;
-                    dst[col] = row_w[row] * acc[h][n][i];
+                    const float v = row_w[row] * acc[h][n][i];
+                    if (ti.shared) a.out[(int64_t)row_tok[row] * a.d + col] = v;
+                    else a.y[(int64_t)(ti.row0 + row) * a.d + col] = f32_to_bf16_rne(v);
                 }
             }
 }
@@ -250,7 +251,7 @@ hipError_t launch_experts_decode(const Problem &p, hipStream_t s,
     a.h = static_cast<uint16_t *>(p.h);
     a.h_sh = static_cast<uint16_t *>(p.h_shared);
     a.out = p.out;
-    a.y = p.y;
+    a.y = static_cast<uint16_t *>(p.y);
     a.perm = p.perm;
     a.counts = p.counts;
     a.offsets = p.offsets;

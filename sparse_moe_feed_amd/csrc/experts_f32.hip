@@ -103,7 +103,7 @@ hipError_t launch_experts_f32(const Problem &p, hipStream_t s,
     a.h = static_cast<float *>(p.h);
     a.h_sh = static_cast<float *>(p.h_shared);
     a.out = p.out;
-    a.y = p.y;
+    a.y = static_cast<float *>(p.y);
     a.perm = p.perm;
     a.offsets = p.offsets;
     a.topk_w = p.topk_w;

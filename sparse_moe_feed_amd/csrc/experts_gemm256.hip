@@ -6,14 +6,23 @@
 // frontier-model-atlas, "Decoder microscope", Feed-forward panel).  A tile is
 // up to 256 consecutive permuted rows of one group (group E = the shared
 // expert) against 256 output columns; gate/up tiles stack 128 gate rows on the
-// matching 128 up rows.  8 waves (2 x 4), each owning 128 x 64 of the tile as
-// 4 x 2 v_mfma_f32_32x32x16_bf16 blocks (128 accumulators per lane), so each
-// staged byte feeds 128 FLOP (a 128 x 128 tile gives 64).  K advances in steps of 64 through double-buffered LDS rows of
-// 72 elements (144 B: 16 lanes reading 16 consecutive rows hit 16 disjoint
-// 4-bank groups).  Global loads for the next step are issued before the
-// current step's MFMAs and are unconditional (the last step re-reads itself)
-// so no branch sits around them.  32-row sub-tiles past the group's last row
-// skip their MFMAs.
+// matching 128 up rows.  4 waves (2 x 2, one per SIMD) each own 128 x 128 of
+// the tile as 4 x 4 v_mfma_f32_32x32x16_bf16 blocks (256 accumulators per
+// lane), so each staged byte feeds 128 FLOP.
+//
+// Tiles go straight from global memory into LDS (global_load_lds_dwordx4:
+// lane i of one load writes 16 bytes at the load's LDS base + 16 i), so no
+// registers hold tiles in flight and the K loop runs three steps ahead
+// through four 32 KB stages of BK = 32.  One load fills 16 tile rows of 64
+// bytes; chunk c of row R sits at chunk c ^ ((R >> 2) & 3).  A 16-byte read
+// by 64 lanes is served 16 lanes (256 bytes) per clock, so the 16 rows read
+// together at one chunk must cover all 64 banks: rows R .. R+3 fill four
+// 16-byte bank groups each and the XOR moves every group of four rows to a
+// different quarter (measured conflict-free; without it each read takes 4x
+// as long).  A step waits for its
+// own stage with an explicit vmcnt and a bare s_barrier (a __syncthreads
+// fence would drain every load in flight); the block drains all its loads
+// before it ends.
 #include "moe_device.h"
 #include "moe_kernels.h"
 
@@ -22,117 +31,203 @@
 namespace moe {
 
 namespace {
-constexpr int BM = kGemm256BM, BN = 256, BK = 64, LDK = BK + 8;
+constexpr int BM = kGemm256BM, BN = 256, BK = 32, STAGES = 4;
+constexpr int ROWB = BK * 2;    // bytes per staged tile row
+constexpr int OPB = BM * ROWB;  // bytes per operand per stage (16 KB)
+constexpr int STB = 2 * OPB;    // bytes per stage (A, then B)
+constexpr int NB = 4;           // 32-column blocks per wave
+constexpr int LOADS = 8;        // loads per wave per stage
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(1))) void global_void_t;
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are
+// outstanding, leaving the other counters free (vmcnt is split over bits
+// [3:0] and [15:14]).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+__device__ __forceinline__ int swz(int R) { return (R >> 2) & 3; }
+__device__ __forceinline__ int tile_off(int R, int c) { return R * ROWB + ((c ^ swz(R)) << 4); }
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+}  // namespace
+
+// Issue one stage's loads: this wave fills rows 16 (4 wave + j) .. + 15 of
+// both operands, j = 0..3.  aoff/boff are this lane's element offsets (its
+// row and swizzled chunk); k0 selects the K step.
+__device__ __forceinline__ void dma_stage(unsigned char *stage, const uint16_t *abase,
+                                          const uint16_t *wbase, const uint32_t (&aoff)[4],
+                                          const uint32_t (&boff)[4], int k0, int wave) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        unsigned char *dst = stage + (4 * wave + j) * 16 * ROWB;
+        __builtin_amdgcn_global_load_lds((const global_void_t *)(abase + aoff[j] + k0),
+                                         (lds_void_t *)dst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const global_void_t *)(wbase + boff[j] + k0),
+                                         (lds_void_t *)(dst + OPB), 16, 0, 0);
+    }
 }
 
-// The K loop of one wave: MACT of its four 32-row sub-tiles do MFMAs; every
-// wave loads, stores and synchronises alike.
+// Operand fragments of one k16 step: MACT A blocks and the wave's NB B blocks.
+struct Frags {
+    bf16x8 a[4], b[NB];
+};
+
 template <int MACT>
-__device__ __forceinline__ void k_loop(uint16_t (*As)[BM * LDK], uint16_t (*Bs)[BN * LDK],
-                                       const uint16_t *abase, const uint16_t *wbase,
-                                       const uint32_t (&aoff)[4], const uint32_t (&boff)[4],
-                                       int sofs, int nk, int wm, const int (&brow)[2], int fr,
-                                       int fk, f32x16 (&acc)[4][2]) {
-    u32x4 ra[4], rb[4];
+__device__ __forceinline__ void read_frags(const unsigned char *stage, int ks, int wm,
+                                           const int (&brow)[NB], int fr, int lane, Frags &f) {
+    if (MACT == 0) return;
+    const int c = 2 * ks + (lane >> 5);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        ra[p] = *reinterpret_cast<const u32x4 *>(abase + aoff[p]);
-        rb[p] = *reinterpret_cast<const u32x4 *>(wbase + boff[p]);
-    }
+    for (int mi = 0; mi < MACT; ++mi)
+        f.a[mi] = *reinterpret_cast<const bf16x8 *>(stage + tile_off(128 * wm + 32 * mi + fr, c));
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        *reinterpret_cast<u32x4 *>(&As[0][sofs + 64 * p * LDK]) = ra[p];
-        *reinterpret_cast<u32x4 *>(&Bs[0][sofs + 64 * p * LDK]) = rb[p];
-    }
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const int knext = min(kt + 1, nk - 1) * BK;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            ra[p] = *reinterpret_cast<const u32x4 *>(abase + aoff[p] + knext);
-            rb[p] = *reinterpret_cast<const u32x4 *>(wbase + boff[p] + knext);
-        }
-        // keep the next step's loads above this step's MFMAs (the scheduler
-        // otherwise sinks them to their LDS stores and nothing overlaps)
-        __builtin_amdgcn_sched_barrier(0);
-        if (MACT > 0) {
-            const uint16_t *A = As[cur];
-            const uint16_t *B = Bs[cur];
-#pragma unroll
-            for (int ks = 0; ks < BK / 16; ++ks) {
-                bf16x8 af[4], bf[2];
-#pragma unroll
-                for (int mi = 0; mi < MACT; ++mi)
-                    af[mi] = *reinterpret_cast<const bf16x8 *>(
-                        &A[(128 * wm + 32 * mi + fr) * LDK + 16 * ks + fk]);
-#pragma unroll
-                for (int ni = 0; ni < 2; ++ni)
-                    bf[ni] = *reinterpret_cast<const bf16x8 *>(&B[(brow[ni] + fr) * LDK + 16 * ks + fk]);
-#pragma unroll
-                for (int mi = 0; mi < MACT; ++mi)
-#pragma unroll
-                    for (int ni = 0; ni < 2; ++ni)
-                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni],
-                                                                              acc[mi][ni], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        if (kt + 1 < nk) {
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                *reinterpret_cast<u32x4 *>(&As[cur ^ 1][sofs + 64 * p * LDK]) = ra[p];
-                *reinterpret_cast<u32x4 *>(&Bs[cur ^ 1][sofs + 64 * p * LDK]) = rb[p];
-            }
-        }
-        __syncthreads();
-    }
+    for (int ni = 0; ni < NB; ++ni)
+        f.b[ni] = *reinterpret_cast<const bf16x8 *>(stage + OPB + tile_off(brow[ni] + fr, c));
 }
 
-// MODE 0: gate/up (K = d).  MODE 1: down (K = F).  MODE 2: router logits.
+// acc[mi][ni] accumulates B_ni A_mi^T (output features by tokens), so each
+// lane ends with one token row and runs of four consecutive output columns.
+template <int MACT>
+__device__ __forceinline__ void mfma_frags(const Frags &f, f32x16 (&acc)[4][NB]) {
+#pragma unroll
+    for (int mi = 0; mi < MACT; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NB; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 0);
+}
+
+struct Stages {
+    unsigned char *s[STAGES];
+};
+
+// Scheduling groups: one MFMA, then the fragment reads each followed by one
+// MFMA, then the remaining MFMAs.  The first MFMA waits for the fragments it
+// uses (read one half step earlier, so that wait is free); the reads for the
+// next half step then overlap the MFMAs.
+template <int MACT>
+__device__ __forceinline__ void interleave_reads() {
+    constexpr int reads = MACT + NB;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+    for (int i = 0; i < reads; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, MACT * NB - 1 - reads, 0);
+}
+
+// One K step kt on stage S = kt % 4, entered with stage kt visible to all
+// waves and its first k16 fragments in f0.  Stages kt+1 and kt+2 are in
+// flight (16 loads per wave, oldest first).
+//   1. MFMAs on f0 while the second k16 fragments of stage kt go to f1;
+//   2. wait until this wave's part of stage kt+1 has landed (vmcnt <= 8),
+//      then barrier: stage kt+1 is visible, and every wave has consumed
+//      stage kt-1, whose buffer ((kt+3) % 4) the next loads refill;
+//   3. issue stage kt+3's loads (past the last step they re-read it into a
+//      buffer that is never computed);
+//   4. MFMAs on f1 while the first k16 fragments of stage kt+1 go to f0.
+// Every stage buffer is its own LDS array named by a constant index, so the
+// compiler ties each LDS read to the loads of that buffer alone instead of
+// waiting for every load in flight.
+template <int MACT, int S>
+__device__ __forceinline__ void k_step(const Stages &st, int kt, int last, const uint16_t *abase,
+                                       const uint16_t *wbase, const uint32_t (&aoff)[4],
+                                       const uint32_t (&boff)[4], int wave, int wm,
+                                       const int (&brow)[NB], int fr, int lane, Frags &f0,
+                                       Frags &f1, f32x16 (&acc)[4][NB]) {
+    if (MACT > 0) {
+        mfma_frags<MACT>(f0, acc);
+        read_frags<MACT>(st.s[S], 1, wm, brow, fr, lane, f1);
+        interleave_reads<MACT>();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    dma_stage(st.s[(S + 3) & 3], abase, wbase, aoff, boff, min((kt + 3) * BK, last), wave);
+    __builtin_amdgcn_sched_barrier(0);
+    if (MACT > 0) {
+        mfma_frags<MACT>(f1, acc);
+        read_frags<MACT>(st.s[(S + 1) & 3], 0, wm, brow, fr, lane, f0);
+        interleave_reads<MACT>();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int MACT>
+__device__ __forceinline__ void k_loop(const Stages &st, const uint16_t *abase,
+                                       const uint16_t *wbase, const uint32_t (&aoff)[4],
+                                       const uint32_t (&boff)[4], int nk, int wave, int wm,
+                                       const int (&brow)[NB], int fr, int lane,
+                                       f32x16 (&acc)[4][NB]) {
+    const int last = (nk - 1) * BK;
+    dma_stage(st.s[0], abase, wbase, aoff, boff, 0, wave);
+    dma_stage(st.s[1], abase, wbase, aoff, boff, min(BK, last), wave);
+    dma_stage(st.s[2], abase, wbase, aoff, boff, min(2 * BK, last), wave);
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LOADS));
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    Frags f0, f1;
+    read_frags<MACT>(st.s[0], 0, wm, brow, fr, lane, f0);
+#define MOE_STEP(S, KT) \
+    k_step<MACT, S>(st, KT, last, abase, wbase, aoff, boff, wave, wm, brow, fr, lane, f0, f1, acc)
+    int kt = 0;
+    for (; kt + 4 <= nk; kt += 4) {
+        MOE_STEP(0, kt);
+        MOE_STEP(1, kt + 1);
+        MOE_STEP(2, kt + 2);
+        MOE_STEP(3, kt + 3);
+    }
+    const int rem = nk - kt;
+    if (rem > 0) MOE_STEP(0, kt);
+    if (rem > 1) MOE_STEP(1, kt + 1);
+    if (rem > 2) MOE_STEP(2, kt + 2);
+#undef MOE_STEP
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land after the block ends
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+}
+
+// MODE 0: gate/up (K = d).  MODE 1: down (K = F).
 template <int MODE>
-__global__ __launch_bounds__(512, 1) void gemm256_kernel(GemmArgs a) {
-    __shared__ __align__(16) uint16_t As[2][BM * LDK];
-    __shared__ __align__(16) uint16_t Bs[2][BN * LDK];
+__global__ __launch_bounds__(256, 1) void gemm256_kernel(GemmArgs a) {
+    __shared__ __align__(1024) unsigned char st0[STB];
+    __shared__ __align__(1024) unsigned char st1[STB];
+    __shared__ __align__(1024) unsigned char st2[STB];
+    __shared__ __align__(1024) unsigned char st3[STB];
     __shared__ int32_t row_tok[BM];
     __shared__ float row_w[BM];
 
     int mt, nt;
     if (!raster_tile(a.nm, a.nn, a.gm, mt, nt)) return;
-    int g = 0, row0, nrows;
-    bool shared = false;
-    if (MODE == 2) {
-        row0 = mt * BM;
-        if (row0 >= a.T) return;
-        nrows = (int)min<int64_t>(BM, a.T - row0);
+    const int tile = mt;
+    if (tile >= a.tile_start[a.E + 1]) return;
+    const int g = a.tile_group[tile];
+    const bool shared = g == a.E;
+    const int m_local = (tile - a.tile_start[g]) * BM;
+    int row0, nrows;
+    if (!shared) {
+        row0 = a.offsets[g] + m_local;
+        nrows = min(BM, a.counts[g] - m_local);
     } else {
-        const int tile = mt;
-        if (tile >= a.tile_start[a.E + 1]) return;
-        g = a.tile_group[tile];
-        shared = g == a.E;
-        const int m_local = (tile - a.tile_start[g]) * BM;
-        if (!shared) {
-            row0 = a.offsets[g] + m_local;
-            nrows = min(BM, a.counts[g] - m_local);
-        } else {
-            row0 = m_local;
-            nrows = (int)min<int64_t>(BM, a.T - m_local);
-        }
+        row0 = m_local;
+        nrows = (int)min<int64_t>(BM, a.T - m_local);
     }
     const int Fg = shared ? a.Fs : a.F;
-    const int N = MODE == 0 ? Fg : MODE == 1 ? a.d : a.E;
+    const int N = MODE == 0 ? Fg : a.d;
     const int K = MODE == 1 ? Fg : a.d;
     const int n0 = nt * (MODE == 0 ? BN / 2 : BN);
     if (n0 >= N) return;
 
     const int tid = threadIdx.x;
-    if (tid < BM) {
+    {
         const int r = min(tid, nrows - 1);  // padding rows repeat the last row; never stored
         int tok;
         float wgt = 0.f;
-        if (MODE == 2) {
-            tok = row0 + r;
-        } else if (!shared) {
+        if (!shared) {
             const int pair = a.perm[row0 + r];
             tok = pair / a.k;
             if (MODE == 1) wgt = a.topk_w[pair];
@@ -145,103 +240,118 @@ __global__ __launch_bounds__(512, 1) void gemm256_kernel(GemmArgs a) {
     }
     __syncthreads();
 
-    // Thread owns 16-byte chunk (tid % 8) of rows tid / 8 + 64 p, p = 0..3,
-    // of both the A and the B tile.
-    const int lrow = tid >> 3, lchunk = tid & 7;
-    const uint16_t *wbase = MODE == 2 ? a.w
-                            : shared  ? a.w_sh
-                                      : a.w + (int64_t)g * (MODE == 0 ? (int64_t)2 * a.F * a.d
-                                                                      : (int64_t)a.d * a.F);
-    // per-row element offsets from block-uniform bases (32-bit: the host
-    // checks that every offset fits)
+    const int lane = tid & 63, wave = wave_id();
+    const uint16_t *wbase = shared ? a.w_sh
+                                   : a.w + (int64_t)g * (MODE == 0 ? (int64_t)2 * a.F * a.d
+                                                                   : (int64_t)a.d * a.F);
     const uint16_t *abase = MODE == 1 ? (shared ? a.h_sh : a.h) : a.x;
+    // element offsets (32-bit: the host checks that every offset fits) of this
+    // lane's row and swizzled chunk in each of its four loads per operand
     uint32_t aoff[4], boff[4];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int r = lrow + 64 * p;
+    for (int j = 0; j < 4; ++j) {
+        const int R = (4 * wave + j) * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ swz(R);
         if (MODE == 1) {
-            aoff[p] = (uint32_t)(row0 + min(r, nrows - 1)) * (uint32_t)Fg;
-            boff[p] = (uint32_t)min(n0 + r, a.d - 1) * (uint32_t)Fg;
+            aoff[j] = (uint32_t)(row0 + min(R, nrows - 1)) * (uint32_t)Fg;
+            boff[j] = (uint32_t)min(n0 + R, a.d - 1) * (uint32_t)Fg;
         } else {
-            aoff[p] = (uint32_t)row_tok[r] * (uint32_t)a.d;
-            if (MODE == 0)
-                boff[p] = (uint32_t)(r < BN / 2 ? n0 + r : Fg + n0 + (r - BN / 2)) * (uint32_t)a.d;
-            else
-                boff[p] = (uint32_t)min(n0 + r, a.E - 1) * (uint32_t)a.d;
+            aoff[j] = (uint32_t)row_tok[R] * (uint32_t)a.d;
+            boff[j] = (uint32_t)(R < BN / 2 ? n0 + R : Fg + n0 + (R - BN / 2)) * (uint32_t)a.d;
         }
-        aoff[p] += lchunk * 8;
-        boff[p] += lchunk * 8;
+        aoff[j] += 8 * c;
+        boff[j] += 8 * c;
     }
 
-    const int sofs = lrow * LDK + lchunk * 8;
-
-    const int lane = tid & 63, wave = wave_id();
-    const int wm = wave >> 2, wn = wave & 3;
-    const int fr = lane & 31, fk = 8 * (lane >> 5);
-    // B rows of this wave's two 32-column blocks: gate/up pairs gate column
-    // block 32 wn with the matching up block; down takes 64 wn .. 64 wn + 63.
-    int brow[2];
+    const int wm = wave >> 1, wn = wave & 1;
+    const int fr = lane & 31;
+    // B rows of this wave's four 32-column blocks.  Gate/up: gate blocks
+    // 64 wn and 64 wn + 32, then the matching up blocks, so block pr pairs
+    // with pr + 2.  Down: 128 wn + 32 ni.
+    int brow[NB];
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) brow[ni] = MODE == 0 ? ni * (BN / 2) + 32 * wn : 64 * wn + 32 * ni;
-    // active 32-row sub-tiles of this wave's 128 rows
+    for (int ni = 0; ni < NB; ++ni)
+        brow[ni] = MODE == 0 ? (ni >> 1) * (BN / 2) + 64 * wn + 32 * (ni & 1) : 128 * wn + 32 * ni;
+    // active 32-row sub-tiles of this wave's 128 rows (wave-uniform)
     const int mact = min(4, max(0, (nrows - 128 * wm + 31) / 32));
 
-    f32x16 acc[4][2];
+    f32x16 acc[4][NB];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NB; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
     const int nk = K / BK;
-    // mact is wave-uniform (scalar): the sub-tile skip is decided once, outside
-    // the K loop, so the loop body is one straight block of loads and MFMAs.
+    const Stages st = {{st0, st1, st2, st3}};
+    // mact is decided once, outside the K loop, so the loop body is one
+    // straight block of loads and MFMAs.
     switch (mact) {
-    case 4: k_loop<4>(As, Bs, abase, wbase, aoff, boff, sofs, nk, wm, brow, fr, fk, acc); break;
-    case 3: k_loop<3>(As, Bs, abase, wbase, aoff, boff, sofs, nk, wm, brow, fr, fk, acc); break;
-    case 2: k_loop<2>(As, Bs, abase, wbase, aoff, boff, sofs, nk, wm, brow, fr, fk, acc); break;
-    case 1: k_loop<1>(As, Bs, abase, wbase, aoff, boff, sofs, nk, wm, brow, fr, fk, acc); break;
-    default: k_loop<0>(As, Bs, abase, wbase, aoff, boff, sofs, nk, wm, brow, fr, fk, acc); break;
+    case 4: k_loop<4>(st, abase, wbase, aoff, boff, nk, wave, wm, brow, fr, lane, acc); break;
+    case 3: k_loop<3>(st, abase, wbase, aoff, boff, nk, wave, wm, brow, fr, lane, acc); break;
+    case 2: k_loop<2>(st, abase, wbase, aoff, boff, nk, wave, wm, brow, fr, lane, acc); break;
+    case 1: k_loop<1>(st, abase, wbase, aoff, boff, nk, wave, wm, brow, fr, lane, acc); break;
+    default: k_loop<0>(st, abase, wbase, aoff, boff, nk, wave, wm, brow, fr, lane, acc); break;
     }
 
-    // 32x32 accumulator layout: lane holds column (lane % 32) and rows
-    // 8 (v / 4) + 4 (lane / 32) + (v % 4), v = 0..15.
+    // Accumulator layout (B A^T): lane holds token row 128 wm + 32 mi + lane % 32
+    // and, in acc[mi][ni][4 g + q], output column brow[ni] + 8 g + 4 (lane / 32) + q.
+    const int cq = 4 * (lane >> 5);
     if (MODE == 0) {
         uint16_t *H = shared ? a.h_sh : a.h;
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
-            if (mi >= mact) continue;
+            const int row = 128 * wm + 32 * mi + fr;
+            if (mi >= mact || row >= nrows) continue;
+            uint16_t *hrow = H + (int64_t)(row0 + row) * Fg + n0 + 64 * wn + cq;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = 128 * wm + 32 * mi + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (row < nrows) {
-                    const int col = n0 + 32 * wn + fr;
-                    H[(int64_t)(row0 + row) * Fg + col] =
-                        f32_to_bf16_rne(silu_mul(acc[mi][0][v], acc[mi][1][v]));
+            for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x16 &gt = acc[mi][pr], &up = acc[mi][pr + 2];
+                    uint2 q;
+                    q.x = pack_bf16x2(silu_mul(gt[4 * g], up[4 * g]), silu_mul(gt[4 * g + 1], up[4 * g + 1]));
+                    q.y = pack_bf16x2(silu_mul(gt[4 * g + 2], up[4 * g + 2]),
+                                      silu_mul(gt[4 * g + 3], up[4 * g + 3]));
+                    *reinterpret_cast<uint2 *>(hrow + 32 * pr + 8 * g) = q;
                 }
-            }
         }
     } else {
-        // one block-uniform base, 32-bit element offsets
-        float *obase = MODE == 2 ? a.f : (shared ? a.out : a.y);
-        const int ncol = MODE == 2 ? a.E : a.d;
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
-            if (mi >= mact) continue;
+            const int row = 128 * wm + 32 * mi + fr;
+            if (mi >= mact || row >= nrows) continue;
+            const float wgt = row_w[row];
+            if (!shared) {
+                // routed rows: weighted, bf16, into y
+                uint16_t *yrow = a.y + (int64_t)(row0 + row) * a.d + n0 + cq;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = 128 * wm + 32 * mi + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (row >= nrows) continue;
-                const uint32_t ro = MODE == 2 ? (uint32_t)(row0 + row) * (uint32_t)a.ldf
-                                    : shared  ? (uint32_t)row_tok[row] * (uint32_t)a.d
-                                              : (uint32_t)(row0 + row) * (uint32_t)a.d;
-                const float wgt = MODE == 2 ? 1.0f : row_w[row];
+                for (int ni = 0; ni < NB; ++ni)
 #pragma unroll
-                for (int ni = 0; ni < 2; ++ni) {
-                    const int col = n0 + brow[ni] + fr;
-                    if (col < ncol) obase[ro + col] = wgt * acc[mi][ni][v];
-                }
+                    for (int g = 0; g < 4; ++g) {
+                        const int col = n0 + brow[ni] + 8 * g + cq;
+                        if (col >= a.d) continue;
+                        const f32x16 &c = acc[mi][ni];
+                        uint2 q;
+                        q.x = pack_bf16x2(wgt * c[4 * g], wgt * c[4 * g + 1]);
+                        q.y = pack_bf16x2(wgt * c[4 * g + 2], wgt * c[4 * g + 3]);
+                        *reinterpret_cast<uint2 *>(yrow + brow[ni] + 8 * g) = q;
+                    }
+            } else {
+                // shared expert: gated term, binary32, straight into out
+                float *orow = a.out + (int64_t)row_tok[row] * a.d + n0 + cq;
+#pragma unroll
+                for (int ni = 0; ni < NB; ++ni)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int col = n0 + brow[ni] + 8 * g + cq;
+                        if (col >= a.d) continue;
+                        const f32x16 &c = acc[mi][ni];
+                        *reinterpret_cast<float4 *>(orow + brow[ni] + 8 * g) =
+                            make_float4(wgt * c[4 * g], wgt * c[4 * g + 1], wgt * c[4 * g + 2],
+                                        wgt * c[4 * g + 3]);
+                    }
             }
         }
     }
@@ -255,7 +365,7 @@ hipError_t launch_experts_gemm256(const Problem &p, hipStream_t s,
     a.h = static_cast<uint16_t *>(p.h);
     a.h_sh = static_cast<uint16_t *>(p.h_shared);
     a.out = p.out;
-    a.y = p.y;
+    a.y = static_cast<uint16_t *>(p.y);
     a.perm = p.perm;
     a.counts = p.counts;
     a.offsets = p.offsets;
@@ -275,13 +385,13 @@ hipError_t launch_experts_gemm256(const Problem &p, hipStream_t s,
     a.w_sh = static_cast<const uint16_t *>(p.w_sh_gate_up);
     a.nm = p.max_tiles;
     a.nn = (fmax + BN / 2 - 1) / (BN / 2);
-    a.gm = 0;  // N fastest (measured best; the XCD-grouped order is not faster here)
-    hipLaunchKernelGGL(gemm256_kernel<0>, grid(a), dim3(512), 0, s, a);
+    a.gm = 0;  // N fastest
+    hipLaunchKernelGGL(gemm256_kernel<0>, grid(a), dim3(256), 0, s, a);
     mark(3);
     a.w = static_cast<const uint16_t *>(p.w_down);
     a.w_sh = static_cast<const uint16_t *>(p.w_sh_down);
     a.nn = (p.d + BN - 1) / BN;
-    hipLaunchKernelGGL(gemm256_kernel<1>, grid(a), dim3(512), 0, s, a);
+    hipLaunchKernelGGL(gemm256_kernel<1>, grid(a), dim3(256), 0, s, a);
     mark(4);
     return hipGetLastError();
 }

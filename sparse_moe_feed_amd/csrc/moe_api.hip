@@ -93,7 +93,7 @@ Plan make_plan(const moe_desc &d, int64_t T) {
     p.perm = take((size_t)pairs * sizeof(int32_t));
     p.h = take((size_t)pairs * d.d_expert * esize);
     p.h_shared = take((size_t)T * d.d_shared * esize);
-    p.y = take((size_t)pairs * d.d_model * sizeof(float));
+    p.y = take((size_t)pairs * d.d_model * esize);
     p.total = off;
     return p;
 }
@@ -123,7 +123,7 @@ moe::Problem make_problem(const moe_desc &d, int64_t T, const Plan &pl, void *ws
     p.perm = reinterpret_cast<int32_t *>(base + pl.perm);
     p.h = base + pl.h;
     p.h_shared = base + pl.h_shared;
-    p.y = reinterpret_cast<float *>(base + pl.y);
+    p.y = base + pl.y;
     p.nblk = pl.nblk;
     p.max_tiles = pl.max_tiles;
     return p;

@@ -35,7 +35,8 @@ struct Problem {
     int32_t *blk;       // [E, nblk]
     int32_t *rank;      // [T*k] rank inside the histogram block, then the pair's row
     int32_t *perm;      // [T*k]
-    float *y;           // [T*k, d] weighted down-projection of each routed row
+    void *y;            // [T*k, d] weighted down-projection of each routed row
+                        // (bf16 for bfloat16 layers, binary32 otherwise)
     void *h;            // [T*k, F]
     void *h_shared;     // [T, Fs]
     int nblk;           // ceil(T / kCountBlock)
@@ -62,7 +63,7 @@ struct GemmArgs {
     uint16_t *h;           // [T*k, F]
     uint16_t *h_sh;        // [T, Fs]
     float *out;            // [T, d]   shared expert's term (plain stores)
-    float *y;              // [T*k, d] routed rows, weighted (plain stores)
+    uint16_t *y;           // [T*k, d] routed rows, weighted, bf16 (plain stores)
     float *f;              // router logits [T, ldf] (MODE 2)
     int ldf;
     const int32_t *perm, *counts, *offsets, *tile_start, *tile_group;

@@ -215,47 +215,77 @@ hipError_t launch_permute(const Problem &p, int bm, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Weighted combine, one block per token, binary32, fixed order: the shared
-// term already in out[t] (written by the down-projection's shared tiles), then
-// the routed rows in slot order j = 0..k-1.  Deterministic: no atomics.
+// Weighted combine in a fixed order: the shared term already in out[t]
+// (written by the down-projection's shared tiles), then the routed rows in
+// slot order j = 0..k-1, all in binary32.  Deterministic: no atomics.
+//
+// bfloat16 layers keep the routed rows in bf16: block (t, c) handles token t
+// and columns 512 c .. 512 c + 511, eight per thread.
 template <bool SHARED>
-__global__ __launch_bounds__(128) void combine_kernel(const float *__restrict__ y,
-                                                      const int32_t *__restrict__ row_of,
-                                                      float *__restrict__ out, int64_t ntok,
-                                                      int d, int k) {
+__global__ __launch_bounds__(64) void combine_bf16_kernel(const uint16_t *__restrict__ y,
+                                                          const int32_t *__restrict__ row_of,
+                                                          float *__restrict__ out, int d, int k) {
+    const int64_t t = blockIdx.x;
+    const int c = (blockIdx.y * 64 + threadIdx.x) * 8;
+    if (c >= d) return;
+    float acc[8];
+    float *o = out + t * d + c;
+    if (SHARED) {
+        const float4 lo = reinterpret_cast<const float4 *>(o)[0];
+        const float4 hi = reinterpret_cast<const float4 *>(o)[1];
+        acc[0] = lo.x; acc[1] = lo.y; acc[2] = lo.z; acc[3] = lo.w;
+        acc[4] = hi.x; acc[5] = hi.y; acc[6] = hi.z; acc[7] = hi.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    }
+    const int32_t *rows = row_of + t * k;
+    for (int j = 0; j < k; ++j) {
+        float v[8];
+        load8(y + (int64_t)rows[j] * d + c, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    reinterpret_cast<float4 *>(o)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    reinterpret_cast<float4 *>(o)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+}
+
+// binary32 layers: one block per token.
+template <bool SHARED>
+__global__ __launch_bounds__(128) void combine_f32_kernel(const float *__restrict__ y,
+                                                          const int32_t *__restrict__ row_of,
+                                                          float *__restrict__ out, int d, int k) {
     const int64_t t = blockIdx.x;
     __shared__ int32_t rows[32];
     if (threadIdx.x < k) rows[threadIdx.x] = row_of[t * k + threadIdx.x];
     __syncthreads();
     float *o = out + t * d;
-    if ((d & 3) == 0) {
-        for (int c = threadIdx.x; c < d / 4; c += 128) {
-            float4 acc = SHARED ? reinterpret_cast<const float4 *>(o)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-            for (int j = 0; j < k; ++j) {
-                const float4 v = reinterpret_cast<const float4 *>(y + (int64_t)rows[j] * d)[c];
-                acc.x += v.x;
-                acc.y += v.y;
-                acc.z += v.z;
-                acc.w += v.w;
-            }
-            reinterpret_cast<float4 *>(o)[c] = acc;
-        }
-    } else {
-        for (int c = threadIdx.x; c < d; c += 128) {
-            float acc = SHARED ? o[c] : 0.f;
-            for (int j = 0; j < k; ++j) acc += y[(int64_t)rows[j] * d + c];
-            o[c] = acc;
-        }
+    for (int c = threadIdx.x; c < d; c += 128) {
+        float acc = SHARED ? o[c] : 0.f;
+        for (int j = 0; j < k; ++j) acc += y[(int64_t)rows[j] * d + c];
+        o[c] = acc;
     }
 }
 
 hipError_t launch_combine(const Problem &p, hipStream_t s) {
-    if (p.Fs > 0)
-        hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)p.T), dim3(128), 0, s, p.y, p.rank,
-                           p.out, p.T, p.d, p.k);
-    else
-        hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)p.T), dim3(128), 0, s, p.y, p.rank,
-                           p.out, p.T, p.d, p.k);
+    if (p.bf16) {
+        const dim3 grid((unsigned)p.T, (unsigned)((p.d / 8 + 63) / 64));
+        const uint16_t *y = static_cast<const uint16_t *>(p.y);
+        if (p.Fs > 0)
+            hipLaunchKernelGGL(combine_bf16_kernel<true>, grid, dim3(64), 0, s, y, p.rank, p.out,
+                               p.d, p.k);
+        else
+            hipLaunchKernelGGL(combine_bf16_kernel<false>, grid, dim3(64), 0, s, y, p.rank, p.out,
+                               p.d, p.k);
+    } else {
+        const float *y = static_cast<const float *>(p.y);
+        if (p.Fs > 0)
+            hipLaunchKernelGGL(combine_f32_kernel<true>, dim3((unsigned)p.T), dim3(128), 0, s, y,
+                               p.rank, p.out, p.d, p.k);
+        else
+            hipLaunchKernelGGL(combine_f32_kernel<false>, dim3((unsigned)p.T), dim3(128), 0, s, y,
+                               p.rank, p.out, p.d, p.k);
+    }
     return hipGetLastError();
 }
 
