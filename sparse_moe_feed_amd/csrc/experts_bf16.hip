@@ -257,12 +257,12 @@ hipError_t launch_experts_bf16(const Problem &p, hipStream_t s,
     a.Fs = p.Fs;
 
     const int fmax = p.F > p.Fs ? p.F : p.Fs;
-    auto grid = [](const GemmArgs &g) { return dim3((unsigned)(8 * ((g.nm * g.nn + 7) / 8))); };
+    auto grid = [](const GemmArgs &g) { return dim3(raster_blocks(g.nm, g.nn, g.gm)); };
     a.w = static_cast<const uint16_t *>(p.w_gate_up);
     a.w_sh = static_cast<const uint16_t *>(p.w_sh_gate_up);
     a.nm = p.max_tiles;
     a.nn = fmax / 64;
-    a.gm = 0;  // N fastest: a tile's column blocks run back to back
+    a.gm = -1;  // M-tile m on XCD m % 8: its N-tiles share A through one L2
     hipLaunchKernelGGL(grouped_gemm_kernel<0>, grid(a), dim3(256), 0, s, a);
     mark(3);
     a.w = static_cast<const uint16_t *>(p.w_down);

@@ -1,28 +1,29 @@
-// experts_gemm256.hip -- grouped SwiGLU expert GEMMs with 256 x 256 tiles for
-// many tokens per expert (long prefill chunks, skewed routing).
+// experts_dma.hip -- grouped SwiGLU expert GEMMs with tiles of BM = 256 or
+// 128 rows by 256 output columns, staged by direct global -> LDS loads.
 //
 // Same maths and epilogues as experts_bf16.hip (gated MLP with SiLU, weighted
 // rows y, the shared expert scaled by its sigmoid gate; anatomy page on
 // frontier-model-atlas, "Decoder microscope", Feed-forward panel).  A tile is
-// up to 256 consecutive permuted rows of one group (group E = the shared
+// up to BM consecutive permuted rows of one group (group E = the shared
 // expert) against 256 output columns; gate/up tiles stack 128 gate rows on the
-// matching 128 up rows.  4 waves (2 x 2, one per SIMD) each own 128 x 128 of
-// the tile as 4 x 4 v_mfma_f32_32x32x16_bf16 blocks (256 accumulators per
-// lane), so each staged byte feeds 128 FLOP.
+// matching 128 up rows.  4 waves (2 x 2, one per SIMD) each own BM/2 x 128 of
+// the tile as (BM/64) x 4 v_mfma_f32_32x32x16_bf16 blocks.  BM = 256 serves
+// many tokens per expert (each staged byte feeds 128 FLOP); BM = 128 serves
+// the middle ground, where streaming the expert weights sets the time.
 //
 // Tiles go straight from global memory into LDS (global_load_lds_dwordx4:
 // lane i of one load writes 16 bytes at the load's LDS base + 16 i), so no
-// registers hold tiles in flight and the K loop runs three steps ahead
-// through four 32 KB stages of BK = 32.  One load fills 16 tile rows of 64
-// bytes; chunk c of row R sits at chunk c ^ ((R >> 2) & 3).  A 16-byte read
-// by 64 lanes is served 16 lanes (256 bytes) per clock, so the 16 rows read
+// registers hold tiles in flight and the K loop runs up to three steps
+// ahead through three stage buffers of BK = 32 (a buffer is refilled as soon
+// as every wave has read it).  One load fills 16 tile rows of 64 bytes;
+// chunk c of row R sits at chunk c ^ ((R >> 2) & 3).  A 16-byte read by 64
+// lanes is served 16 lanes (256 bytes) per clock, so the 16 rows read
 // together at one chunk must cover all 64 banks: rows R .. R+3 fill four
 // 16-byte bank groups each and the XOR moves every group of four rows to a
 // different quarter (measured conflict-free; without it each read takes 4x
-// as long).  A step waits for its
-// own stage with an explicit vmcnt and a bare s_barrier (a __syncthreads
-// fence would drain every load in flight); the block drains all its loads
-// before it ends.
+// as long).  A step waits for its own stage with an explicit vmcnt and a
+// bare s_barrier (a __syncthreads fence would drain every load in flight);
+// the block drains all its loads before it ends.
 #include "moe_device.h"
 #include "moe_kernels.h"
 
@@ -30,41 +31,59 @@
 
 namespace moe {
 
+#ifndef MOE_NS128
+#define MOE_NS128 3
+#endif
+
 namespace {
-constexpr int BM = kGemm256BM, BN = 256, BK = 32, STAGES = 4;
+constexpr int BN = 256, BK = 32;
 constexpr int ROWB = BK * 2;    // bytes per staged tile row
-constexpr int OPB = BM * ROWB;  // bytes per operand per stage (16 KB)
-constexpr int STB = 2 * OPB;    // bytes per stage (A, then B)
+constexpr int OPB = BN * ROWB;  // B bytes per stage (16 KB)
 constexpr int NB = 4;           // 32-column blocks per wave
-constexpr int LOADS = 8;        // loads per wave per stage
+
+// Per tile height: A bytes per stage, stage bytes (A then B), A loads per
+// wave per stage, loads per wave per stage, 32-row sub-tiles per wave.
+template <int BM> struct Geo {
+    static constexpr int OPA = BM * ROWB;
+    static constexpr int STB = OPA + OPB;
+    static constexpr int AL = BM / 64;
+    static constexpr int LOADS = AL + 4;
+    static constexpr int MI = BM / 64;
+};
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void global_void_t;
 
 // s_waitcnt immediate that waits until at most n vector-memory operations are
 // outstanding, leaving the other counters free (vmcnt is split over bits
-// [3:0] and [15:14]).
+// [3:0] and [15:14]); the second form also waits for every LDS access.
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+constexpr int vmcnt_lgkm0_imm(int n) { return vmcnt_imm(n) & ~(0xF << 8); }
 
 __device__ __forceinline__ int swz(int R) { return (R >> 2) & 3; }
 __device__ __forceinline__ int tile_off(int R, int c) { return R * ROWB + ((c ^ swz(R)) << 4); }
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 }  // namespace
 
-// Issue one stage's loads: this wave fills rows 16 (4 wave + j) .. + 15 of
-// both operands, j = 0..3.  aoff/boff are this lane's element offsets (its
-// row and swizzled chunk); k0 selects the K step.
+// Issue one stage's loads: this wave fills A rows 16 (AL wave + j) .. + 15,
+// j < AL, and B rows 16 (4 wave + j) .. + 15, j < 4.  aoff/boff are this
+// lane's element offsets (its row and swizzled chunk); k0 selects the K step.
+template <int BM>
 __device__ __forceinline__ void dma_stage(unsigned char *stage, const uint16_t *abase,
-                                          const uint16_t *wbase, const uint32_t (&aoff)[4],
+                                          const uint16_t *wbase,
+                                          const uint32_t (&aoff)[Geo<BM>::AL],
                                           const uint32_t (&boff)[4], int k0, int wave) {
+    constexpr int AL = Geo<BM>::AL;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        unsigned char *dst = stage + (4 * wave + j) * 16 * ROWB;
+    for (int j = 0; j < AL; ++j)
         __builtin_amdgcn_global_load_lds((const global_void_t *)(abase + aoff[j] + k0),
-                                         (lds_void_t *)dst, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const global_void_t *)(wbase + boff[j] + k0),
-                                         (lds_void_t *)(dst + OPB), 16, 0, 0);
-    }
+                                         (lds_void_t *)(stage + (AL * wave + j) * 16 * ROWB), 16,
+                                         0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        __builtin_amdgcn_global_load_lds(
+            (const global_void_t *)(wbase + boff[j] + k0),
+            (lds_void_t *)(stage + Geo<BM>::OPA + (4 * wave + j) * 16 * ROWB), 16, 0, 0);
 }
 
 // Operand fragments of one k16 step: MACT A blocks and the wave's NB B blocks.
@@ -72,23 +91,23 @@ struct Frags {
     bf16x8 a[4], b[NB];
 };
 
-template <int MACT>
+template <int BM, int MACT>
 __device__ __forceinline__ void read_frags(const unsigned char *stage, int ks, int wm,
                                            const int (&brow)[NB], int fr, int lane, Frags &f) {
     if (MACT == 0) return;
     const int c = 2 * ks + (lane >> 5);
 #pragma unroll
     for (int mi = 0; mi < MACT; ++mi)
-        f.a[mi] = *reinterpret_cast<const bf16x8 *>(stage + tile_off(128 * wm + 32 * mi + fr, c));
+        f.a[mi] = *reinterpret_cast<const bf16x8 *>(stage + tile_off(BM / 2 * wm + 32 * mi + fr, c));
 #pragma unroll
     for (int ni = 0; ni < NB; ++ni)
-        f.b[ni] = *reinterpret_cast<const bf16x8 *>(stage + OPB + tile_off(brow[ni] + fr, c));
+        f.b[ni] = *reinterpret_cast<const bf16x8 *>(stage + Geo<BM>::OPA + tile_off(brow[ni] + fr, c));
 }
 
 // acc[mi][ni] accumulates B_ni A_mi^T (output features by tokens), so each
 // lane ends with one token row and runs of four consecutive output columns.
-template <int MACT>
-__device__ __forceinline__ void mfma_frags(const Frags &f, f32x16 (&acc)[4][NB]) {
+template <int MACT, int MI>
+__device__ __forceinline__ void mfma_frags(const Frags &f, f32x16 (&acc)[MI][NB]) {
 #pragma unroll
     for (int mi = 0; mi < MACT; ++mi)
 #pragma unroll
@@ -96,8 +115,8 @@ __device__ __forceinline__ void mfma_frags(const Frags &f, f32x16 (&acc)[4][NB])
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 0);
 }
 
-struct Stages {
-    unsigned char *s[STAGES];
+template <int NS> struct Stages {
+    unsigned char *s[NS];
 };
 
 // Scheduling groups: one MFMA, then the fragment reads each followed by one
@@ -116,88 +135,116 @@ __device__ __forceinline__ void interleave_reads() {
     __builtin_amdgcn_sched_group_barrier(0x008, MACT * NB - 1 - reads, 0);
 }
 
-// One K step kt on stage S = kt % 4, entered with stage kt visible to all
-// waves and its first k16 fragments in f0.  Stages kt+1 and kt+2 are in
-// flight (16 loads per wave, oldest first).
+// One K step kt on stage buffer S = kt % NS, entered with stage kt visible to
+// all waves and its first k16 fragments in f0.  Stages kt+1 .. kt+NS-1 are in
+// flight ((NS-1) LOADS loads per wave, oldest first).
 //   1. MFMAs on f0 while the second k16 fragments of stage kt go to f1;
-//   2. wait until this wave's part of stage kt+1 has landed (vmcnt <= 8),
-//      then barrier: stage kt+1 is visible, and every wave has consumed
-//      stage kt-1, whose buffer ((kt+3) % 4) the next loads refill;
-//   3. issue stage kt+3's loads (past the last step they re-read it into a
-//      buffer that is never computed);
+//   2. wait until this wave's reads of stage kt are done and its part of
+//      stage kt+1 has landed (lgkmcnt 0, vmcnt <= (NS-2) LOADS), then
+//      barrier: stage kt+1 is visible and no wave reads buffer S any more;
+//   3. refill buffer S with stage kt+NS (past the last step the loads re-read
+//      it into a buffer that is never computed);
 //   4. MFMAs on f1 while the first k16 fragments of stage kt+1 go to f0.
 // Every stage buffer is its own LDS array named by a constant index, so the
 // compiler ties each LDS read to the loads of that buffer alone instead of
 // waiting for every load in flight.
-template <int MACT, int S>
-__device__ __forceinline__ void k_step(const Stages &st, int kt, int last, const uint16_t *abase,
-                                       const uint16_t *wbase, const uint32_t (&aoff)[4],
+template <int BM, int NS, int MACT, int S>
+__device__ __forceinline__ void k_step(const Stages<NS> &st, int kt, int last,
+                                       const uint16_t *abase, const uint16_t *wbase,
+                                       const uint32_t (&aoff)[Geo<BM>::AL],
                                        const uint32_t (&boff)[4], int wave, int wm,
                                        const int (&brow)[NB], int fr, int lane, Frags &f0,
-                                       Frags &f1, f32x16 (&acc)[4][NB]) {
+                                       Frags &f1, f32x16 (&acc)[Geo<BM>::MI][NB]) {
     if (MACT > 0) {
         mfma_frags<MACT>(f0, acc);
-        read_frags<MACT>(st.s[S], 1, wm, brow, fr, lane, f1);
+        read_frags<BM, MACT>(st.s[S], 1, wm, brow, fr, lane, f1);
         interleave_reads<MACT>();
     }
     __builtin_amdgcn_sched_barrier(0);
     compiler_fence();
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
+    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm((NS - 2) * Geo<BM>::LOADS));
     __builtin_amdgcn_s_barrier();
     compiler_fence();
-    dma_stage(st.s[(S + 3) & 3], abase, wbase, aoff, boff, min((kt + 3) * BK, last), wave);
+    dma_stage<BM>(st.s[S], abase, wbase, aoff, boff, min((kt + NS) * BK, last), wave);
     __builtin_amdgcn_sched_barrier(0);
     if (MACT > 0) {
         mfma_frags<MACT>(f1, acc);
-        read_frags<MACT>(st.s[(S + 1) & 3], 0, wm, brow, fr, lane, f0);
+        read_frags<BM, MACT>(st.s[(S + 1) % NS], 0, wm, brow, fr, lane, f0);
         interleave_reads<MACT>();
     }
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int MACT>
-__device__ __forceinline__ void k_loop(const Stages &st, const uint16_t *abase,
-                                       const uint16_t *wbase, const uint32_t (&aoff)[4],
+// Steps kt + S .. kt + cnt - 1 (cnt <= NS), each on its constant buffer.
+template <int BM, int NS, int MACT, int S>
+__device__ __forceinline__ void k_steps(const Stages<NS> &st, int kt, int cnt, int last,
+                                        const uint16_t *abase, const uint16_t *wbase,
+                                        const uint32_t (&aoff)[Geo<BM>::AL],
+                                        const uint32_t (&boff)[4], int wave, int wm,
+                                        const int (&brow)[NB], int fr, int lane, Frags &f0,
+                                        Frags &f1, f32x16 (&acc)[Geo<BM>::MI][NB]) {
+    if constexpr (S < NS) {
+        if (S < cnt) {
+            k_step<BM, NS, MACT, S>(st, kt + S, last, abase, wbase, aoff, boff, wave, wm, brow, fr,
+                                    lane, f0, f1, acc);
+            k_steps<BM, NS, MACT, S + 1>(st, kt, cnt, last, abase, wbase, aoff, boff, wave, wm,
+                                         brow, fr, lane, f0, f1, acc);
+        }
+    }
+}
+
+// Issue stages S .. NS-1 of the prologue into their buffers.
+template <int BM, int NS, int S>
+__device__ __forceinline__ void prologue(const Stages<NS> &st, int last, const uint16_t *abase,
+                                         const uint16_t *wbase,
+                                         const uint32_t (&aoff)[Geo<BM>::AL],
+                                         const uint32_t (&boff)[4], int wave) {
+    if constexpr (S < NS) {
+        dma_stage<BM>(st.s[S], abase, wbase, aoff, boff, min(S * BK, last), wave);
+        prologue<BM, NS, S + 1>(st, last, abase, wbase, aoff, boff, wave);
+    }
+}
+
+template <int BM, int NS, int MACT>
+__device__ __forceinline__ void k_loop(const Stages<NS> &st, const uint16_t *abase,
+                                       const uint16_t *wbase,
+                                       const uint32_t (&aoff)[Geo<BM>::AL],
                                        const uint32_t (&boff)[4], int nk, int wave, int wm,
                                        const int (&brow)[NB], int fr, int lane,
-                                       f32x16 (&acc)[4][NB]) {
+                                       f32x16 (&acc)[Geo<BM>::MI][NB]) {
     const int last = (nk - 1) * BK;
-    dma_stage(st.s[0], abase, wbase, aoff, boff, 0, wave);
-    dma_stage(st.s[1], abase, wbase, aoff, boff, min(BK, last), wave);
-    dma_stage(st.s[2], abase, wbase, aoff, boff, min(2 * BK, last), wave);
+    prologue<BM, NS, 0>(st, last, abase, wbase, aoff, boff, wave);
     compiler_fence();
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LOADS));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 1) * Geo<BM>::LOADS));
     __builtin_amdgcn_s_barrier();
     compiler_fence();
     Frags f0, f1;
-    read_frags<MACT>(st.s[0], 0, wm, brow, fr, lane, f0);
-#define MOE_STEP(S, KT) \
-    k_step<MACT, S>(st, KT, last, abase, wbase, aoff, boff, wave, wm, brow, fr, lane, f0, f1, acc)
+    read_frags<BM, MACT>(st.s[0], 0, wm, brow, fr, lane, f0);
     int kt = 0;
-    for (; kt + 4 <= nk; kt += 4) {
-        MOE_STEP(0, kt);
-        MOE_STEP(1, kt + 1);
-        MOE_STEP(2, kt + 2);
-        MOE_STEP(3, kt + 3);
-    }
-    const int rem = nk - kt;
-    if (rem > 0) MOE_STEP(0, kt);
-    if (rem > 1) MOE_STEP(1, kt + 1);
-    if (rem > 2) MOE_STEP(2, kt + 2);
-#undef MOE_STEP
+    for (; kt + NS <= nk; kt += NS)
+        k_steps<BM, NS, MACT, 0>(st, kt, NS, last, abase, wbase, aoff, boff, wave, wm, brow, fr,
+                                 lane, f0, f1, acc);
+    k_steps<BM, NS, MACT, 0>(st, kt, nk - kt, last, abase, wbase, aoff, boff, wave, wm, brow, fr,
+                             lane, f0, f1, acc);
     compiler_fence();
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land after the block ends
     __builtin_amdgcn_s_barrier();
     compiler_fence();
 }
 
-// MODE 0: gate/up (K = d).  MODE 1: down (K = F).
-template <int MODE>
-__global__ __launch_bounds__(256, 1) void gemm256_kernel(GemmArgs a) {
-    __shared__ __align__(1024) unsigned char st0[STB];
-    __shared__ __align__(1024) unsigned char st1[STB];
-    __shared__ __align__(1024) unsigned char st2[STB];
-    __shared__ __align__(1024) unsigned char st3[STB];
+// NS stage buffers; up to 80 KB of them leaves room for two blocks per CU, so
+// one block's start-up and epilogue overlap the other's streaming.
+template <int MODE, int BM, int NS>
+__global__ __launch_bounds__(256, NS * Geo<BM>::STB <= 80 * 1024 ? 2 : 1) void gemm_dma_kernel(
+    GemmArgs a) {
+    using G = Geo<BM>;
+    static_assert(NS >= 3 && NS <= 6, "three to six stage buffers");
+    __shared__ __align__(1024) unsigned char st0[G::STB];
+    __shared__ __align__(1024) unsigned char st1[G::STB];
+    __shared__ __align__(1024) unsigned char st2[G::STB];
+    __shared__ __align__(1024) unsigned char st3[NS > 3 ? G::STB : 16];
+    __shared__ __align__(1024) unsigned char st4[NS > 4 ? G::STB : 16];
+    __shared__ __align__(1024) unsigned char st5[NS > 5 ? G::STB : 16];
     __shared__ int32_t row_tok[BM];
     __shared__ float row_w[BM];
 
@@ -223,7 +270,7 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(GemmArgs a) {
     if (n0 >= N) return;
 
     const int tid = threadIdx.x;
-    {
+    if (tid < BM) {
         const int r = min(tid, nrows - 1);  // padding rows repeat the last row; never stored
         int tok;
         float wgt = 0.f;
@@ -246,21 +293,22 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(GemmArgs a) {
                                                                    : (int64_t)a.d * a.F);
     const uint16_t *abase = MODE == 1 ? (shared ? a.h_sh : a.h) : a.x;
     // element offsets (32-bit: the host checks that every offset fits) of this
-    // lane's row and swizzled chunk in each of its four loads per operand
-    uint32_t aoff[4], boff[4];
+    // lane's row and swizzled chunk in each of its loads
+    uint32_t aoff[G::AL], boff[4];
+#pragma unroll
+    for (int j = 0; j < G::AL; ++j) {
+        const int R = (G::AL * wave + j) * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ swz(R);
+        aoff[j] = (MODE == 1 ? (uint32_t)(row0 + min(R, nrows - 1)) * (uint32_t)Fg
+                             : (uint32_t)row_tok[R] * (uint32_t)a.d) + 8 * c;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int R = (4 * wave + j) * 16 + (lane >> 2);
         const int c = (lane & 3) ^ swz(R);
-        if (MODE == 1) {
-            aoff[j] = (uint32_t)(row0 + min(R, nrows - 1)) * (uint32_t)Fg;
-            boff[j] = (uint32_t)min(n0 + R, a.d - 1) * (uint32_t)Fg;
-        } else {
-            aoff[j] = (uint32_t)row_tok[R] * (uint32_t)a.d;
-            boff[j] = (uint32_t)(R < BN / 2 ? n0 + R : Fg + n0 + (R - BN / 2)) * (uint32_t)a.d;
-        }
-        aoff[j] += 8 * c;
-        boff[j] += 8 * c;
+        boff[j] = (MODE == 1 ? (uint32_t)min(n0 + R, a.d - 1) * (uint32_t)Fg
+                             : (uint32_t)(R < BN / 2 ? n0 + R : Fg + n0 + (R - BN / 2)) *
+                                   (uint32_t)a.d) + 8 * c;
     }
 
     const int wm = wave >> 1, wn = wave & 1;
@@ -272,37 +320,52 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(GemmArgs a) {
 #pragma unroll
     for (int ni = 0; ni < NB; ++ni)
         brow[ni] = MODE == 0 ? (ni >> 1) * (BN / 2) + 64 * wn + 32 * (ni & 1) : 128 * wn + 32 * ni;
-    // active 32-row sub-tiles of this wave's 128 rows (wave-uniform)
-    const int mact = min(4, max(0, (nrows - 128 * wm + 31) / 32));
+    // active 32-row sub-tiles of this wave's BM/2 rows (wave-uniform)
+    const int mact = min(G::MI, max(0, (nrows - BM / 2 * wm + 31) / 32));
 
-    f32x16 acc[4][NB];
+    f32x16 acc[G::MI][NB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < G::MI; ++i)
 #pragma unroll
         for (int j = 0; j < NB; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
     const int nk = K / BK;
-    const Stages st = {{st0, st1, st2, st3}};
+    Stages<NS> st;
+    {
+        unsigned char *all[6] = {st0, st1, st2, st3, st4, st5};
+#pragma unroll
+        for (int i = 0; i < NS; ++i) st.s[i] = all[i];
+    }
     // mact is decided once, outside the K loop, so the loop body is one
     // straight block of loads and MFMAs.
-    switch (mact) {
-    case 4: k_loop<4>(st, abase, wbase, aoff, boff, nk, wave, wm, brow, fr, lane, acc); break;
-    case 3: k_loop<3>(st, abase, wbase, aoff, boff, nk, wave, wm, brow, fr, lane, acc); break;
-    case 2: k_loop<2>(st, abase, wbase, aoff, boff, nk, wave, wm, brow, fr, lane, acc); break;
-    case 1: k_loop<1>(st, abase, wbase, aoff, boff, nk, wave, wm, brow, fr, lane, acc); break;
-    default: k_loop<0>(st, abase, wbase, aoff, boff, nk, wave, wm, brow, fr, lane, acc); break;
+#define MOE_LOOP(M) k_loop<BM, NS, M>(st, abase, wbase, aoff, boff, nk, wave, wm, brow, fr, lane, acc)
+    if constexpr (G::MI == 4) {
+        switch (mact) {
+        case 4: MOE_LOOP(4); break;
+        case 3: MOE_LOOP(3); break;
+        case 2: MOE_LOOP(2); break;
+        case 1: MOE_LOOP(1); break;
+        default: MOE_LOOP(0); break;
+        }
+    } else {
+        switch (mact) {
+        case 2: MOE_LOOP(2); break;
+        case 1: MOE_LOOP(1); break;
+        default: MOE_LOOP(0); break;
+        }
     }
+#undef MOE_LOOP
 
-    // Accumulator layout (B A^T): lane holds token row 128 wm + 32 mi + lane % 32
+    // Accumulator layout (B A^T): lane holds token row BM/2 wm + 32 mi + lane % 32
     // and, in acc[mi][ni][4 g + q], output column brow[ni] + 8 g + 4 (lane / 32) + q.
     const int cq = 4 * (lane >> 5);
     if (MODE == 0) {
         uint16_t *H = shared ? a.h_sh : a.h;
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            const int row = 128 * wm + 32 * mi + fr;
+        for (int mi = 0; mi < G::MI; ++mi) {
+            const int row = BM / 2 * wm + 32 * mi + fr;
             if (mi >= mact || row >= nrows) continue;
             uint16_t *hrow = H + (int64_t)(row0 + row) * Fg + n0 + 64 * wn + cq;
 #pragma unroll
@@ -319,8 +382,8 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(GemmArgs a) {
         }
     } else {
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            const int row = 128 * wm + 32 * mi + fr;
+        for (int mi = 0; mi < G::MI; ++mi) {
+            const int row = BM / 2 * wm + 32 * mi + fr;
             if (mi >= mact || row >= nrows) continue;
             const float wgt = row_w[row];
             if (!shared) {
@@ -357,8 +420,8 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(GemmArgs a) {
     }
 }
 
-hipError_t launch_experts_gemm256(const Problem &p, hipStream_t s,
-                                  const std::function<void(int)> &mark) {
+hipError_t launch_experts_dma(const Problem &p, int bm, hipStream_t s,
+                              const std::function<void(int)> &mark) {
     GemmArgs a;
     memset(&a, 0, sizeof a);
     a.x = static_cast<const uint16_t *>(p.x);
@@ -380,18 +443,20 @@ hipError_t launch_experts_gemm256(const Problem &p, hipStream_t s,
     a.F = p.F;
     a.Fs = p.Fs;
     const int fmax = p.F > p.Fs ? p.F : p.Fs;
-    auto grid = [](const GemmArgs &g) { return dim3((unsigned)(8 * ((g.nm * g.nn + 7) / 8))); };
+    auto grid = [](const GemmArgs &g) { return dim3(raster_blocks(g.nm, g.nn, g.gm)); };
     a.w = static_cast<const uint16_t *>(p.w_gate_up);
     a.w_sh = static_cast<const uint16_t *>(p.w_sh_gate_up);
     a.nm = p.max_tiles;
     a.nn = (fmax + BN / 2 - 1) / (BN / 2);
-    a.gm = 0;  // N fastest
-    hipLaunchKernelGGL(gemm256_kernel<0>, grid(a), dim3(256), 0, s, a);
+    a.gm = -1;  // M-tile m on XCD m % 8: its N-tiles share A through one L2
+    if (bm == 256) hipLaunchKernelGGL((gemm_dma_kernel<0, 256, 3>), grid(a), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((gemm_dma_kernel<0, 128, MOE_NS128>), grid(a), dim3(256), 0, s, a);
     mark(3);
     a.w = static_cast<const uint16_t *>(p.w_down);
     a.w_sh = static_cast<const uint16_t *>(p.w_sh_down);
     a.nn = (p.d + BN - 1) / BN;
-    hipLaunchKernelGGL(gemm256_kernel<1>, grid(a), dim3(256), 0, s, a);
+    if (bm == 256) hipLaunchKernelGGL((gemm_dma_kernel<1, 256, 3>), grid(a), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((gemm_dma_kernel<1, 128, MOE_NS128>), grid(a), dim3(256), 0, s, a);
     mark(4);
     return hipGetLastError();
 }

@@ -162,21 +162,21 @@ bool use_decode_path(const moe::Problem &p) {
     return p.T * p.k <= (int64_t)16 * p.E;
 }
 
-// 256 x 256 tiles once experts average 192+ rows (their 32-bit row offsets
-// must fit: T*k*max(d, F) and T*d below 2^32).
-bool use_gemm256_path(const moe::Problem &p) {
+// Tiles staged by direct global -> LDS loads need 128-column multiples and
+// 32-bit row offsets (T*k*max(d, F) and T*(E+1) below 2^32).
+bool use_dma_path(const moe::Problem &p) {
     if (!p.bf16 || p.F % 128 || p.Fs % 128) return false;
     const int64_t pairs = p.T * p.k;
     const int64_t widest = p.d > p.F ? p.d : p.F;
-    if (pairs * widest >= ((int64_t)1 << 32) || p.T * (int64_t)(p.E + 1) >= ((int64_t)1 << 32))
-        return false;
-    return pairs >= (int64_t)192 * p.E;
+    return pairs * widest < ((int64_t)1 << 32) && p.T * (int64_t)(p.E + 1) < ((int64_t)1 << 32);
 }
 
 // Stages 2..5 of a call: permutation, gate/up, down, combine.
 moe_status run_experts(moe::Problem p, hipStream_t s) {
     const bool decode = use_decode_path(p);
-    const bool big = !decode && use_gemm256_path(p);
+    const bool dma = !decode && use_dma_path(p);
+    // 256-row tiles once experts average 192+ rows
+    const bool big = dma && p.T * p.k >= (int64_t)192 * p.E;
     const int bm = decode ? moe::kDecodeBM : big ? moe::kGemm256BM : moe::kGemmBM;
     p.max_tiles = (int)moe::max_gemm_tiles(p.T, p.k, p.E, bm, p.Fs > 0);
     hipError_t err = moe::launch_permute(p, bm, s);
@@ -185,7 +185,7 @@ moe_status run_experts(moe::Problem p, hipStream_t s) {
     if (err == hipSuccess)
         err = !p.bf16  ? moe::launch_experts_f32(p, s, mark)
               : decode ? moe::launch_experts_decode(p, s, mark)
-              : big    ? moe::launch_experts_gemm256(p, s, mark)
+              : dma    ? moe::launch_experts_dma(p, bm, s, mark)
                        : moe::launch_experts_bf16(p, s, mark);
     if (err == hipSuccess) err = moe::launch_combine(p, s);
     mark_stage(5, s);

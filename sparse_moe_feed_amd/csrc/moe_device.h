@@ -58,7 +58,8 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // Block -> (m, n) tile for a GEMM grid of nm x nn tiles launched as a 1-D
-// grid of 8 * ceil(nm * nn / 8) blocks.  Workgroups are dispatched to the 8
+// grid of 8 * ceil(nm * nn / 8) blocks (gm >= 0) or 8 * ceil(nm / 8) * nn
+// blocks (gm < 0).  Workgroups are dispatched to the 8
 // XCDs round robin, so block b runs on XCD b % 8; logical tile ids are made
 // contiguous per XCD, and within an XCD consecutive ids sweep gm M-tiles
 // before advancing N, so the blocks that run together on one XCD share both
@@ -67,6 +68,15 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ bool raster_tile(int nm, int nn, int gm, int &m, int &n) {
     const int nblocks = nm * nn;
     const int b = blockIdx.x;
+    if (gm < 0) {
+        // M-tile m runs on XCD m % 8 and its N-tiles are 8 block ids apart:
+        // they share the tile's A rows through one L2, while consecutive
+        // M-tiles still alternate over the XCDs (grid of 8 * ceil(nm / 8) * nn)
+        const int x = b & 7, q = b >> 3;
+        n = q % nn;
+        m = 8 * (q / nn) + x;
+        return m < nm;
+    }
     if (gm == 0) {
         if (b >= nblocks) return false;
         m = b / nn;

@@ -43,9 +43,9 @@ struct Problem {
 };
 
 constexpr int kCountBlock = 256;     // tokens per histogram block
-constexpr int kGemmBM = 128;         // rows per grouped-GEMM tile (MFMA path)
+constexpr int kGemmBM = 128;         // rows per grouped-GEMM tile (MFMA paths)
 constexpr int kDecodeBM = 32;        // rows per tile of the weight-streaming (decode) path
-constexpr int kGemm256BM = 256;      // rows per tile of the large-tile GEMM path
+constexpr int kGemm256BM = 256;      // rows per tile for many tokens per expert
 
 // Upper bound on sum_e ceil(c_e / bm) + ceil(T / bm) over any routing with
 // sum_e c_e = T*k: each non-empty expert adds at most one partial tile.
@@ -73,11 +73,17 @@ struct GemmArgs {
     int nm, nn, gm;        // M-tiles, N-tiles and raster group height (raster_tile)
 };
 
+// Blocks of the 1-D grid that raster_tile maps onto nm x nn tiles.
+inline unsigned raster_blocks(int nm, int nn, int gm) {
+    return gm < 0 ? (unsigned)(8 * ((nm + 7) / 8) * nn) : (unsigned)(8 * ((nm * nn + 7) / 8));
+}
+
 // Router logits f = x W_r^T on MFMA (binary32 accumulate, any order).
 hipError_t launch_router_gemm(const Problem &p, hipStream_t s);
-// Large-tile (256 x 256) grouped GEMM expert stage for many tokens per expert.
-hipError_t launch_experts_gemm256(const Problem &p, hipStream_t s,
-                                  const std::function<void(int)> &mark);
+// Grouped GEMM expert stage with bm x 256 tiles (bm = 256 or 128) staged by
+// direct global -> LDS loads; needs F, Fs % 128 == 0 and 32-bit offsets.
+hipError_t launch_experts_dma(const Problem &p, int bm, hipStream_t s,
+                              const std::function<void(int)> &mark);
 // Router: logits (canonical binary32 order) then top-k / weights / gate.
 hipError_t launch_router(const Problem &p, float *sh_gate_user, hipStream_t s);
 // Shared gate alone (used when the routing is given).

@@ -63,6 +63,8 @@ def test_tiny_fp32_layer():
     (100, 256, 16, 2, 128, 128),    # streaming path, experts with 17..32+ rows
     (1000, 256, 16, 4, 128, 128),   # 256-row tiles (partial tiles)
     (1200, 384, 8, 2, 256, 128),    # 256-row tiles, 2 per expert; d % 256 = 128
+    (600, 256, 16, 4, 128, 128),    # 128-row LDS-DMA tiles, some experts > 128 rows
+    (500, 320, 16, 3, 256, 128),    # 128-row LDS-DMA tiles; d % 256 = 64
 ])
 def test_small_bf16_layers(T, d, E, k, F, Fs):
     inp = W.small_case(T, d, E, k, F, Fs, "bf16", seed=T + E)
