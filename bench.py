@@ -92,19 +92,25 @@ def measure(cfg, dev_layer, steps, warmup):
     w = torch.empty(cfg.T, cfg.k, device="cuda")
     for _ in range(warmup):
         L(x, out, idx, w)
-    n_ev = 1 + len(moe.STAGES)
-    evs = [[moe.HipEvent() for _ in range(n_ev)] for _ in range(steps)]
+    # the timed steps: nothing but the layer calls between the two events
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record()
     for i in range(steps):
-        moe.stage_events(evs[i])
         L(x, out, idx, w)
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = t0.elapsed_time(t1) / steps
+    # a second pass of the same steps with HIP events recorded by the library
+    # at its stage boundaries (on its own stream) for the per-stage split
+    n_ev = 1 + len(moe.STAGES)
+    evs = [[moe.HipEvent() for _ in range(n_ev)] for _ in range(steps)]
+    for i in range(steps):
+        moe.stage_events(evs[i])
+        L(x, out, idx, w)
+    torch.cuda.synchronize()
     stage_ms = {name: sum(e[j].elapsed_ms(e[j + 1]) for e in evs) / steps
                 for j, name in enumerate(moe.STAGES)}
     U = int(np.unique(idx.cpu().numpy()).size)

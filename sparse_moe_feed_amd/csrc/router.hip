@@ -62,13 +62,41 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
     const int64_t t0 = (int64_t)blockIdx.x * TT;
     const int ntt = (int)min<int64_t>(TT, ntok - t0);
 
+    const bool vec = (d % 8) == 0;
+    const bool preload = vec && sizeof(T) == 2 && d <= 512 * kMaxChunks;
+    // The first row's weight chunks do not depend on x: their loads go out
+    // before the token rows are staged.
+    uint4 wq[kMaxChunks];
+    if (preload) {
+        const int row = blockIdx.y * 4 * RW + wave * RW;
+        const T *wrow = row < E ? w_router + (int64_t)row * d : (row == E ? g : nullptr);
+#pragma unroll
+        for (int c = 0; c < kMaxChunks; ++c) {
+            const int kk0 = 512 * c + 8 * lane;
+            wq[c] = wrow && kk0 < d ? *reinterpret_cast<const uint4 *>(wrow + kk0)
+                                    : make_uint4(0, 0, 0, 0);
+        }
+    }
+
     if ((d * (int)sizeof(T)) % 16 == 0) {
-        // whole rows are 16-byte multiples: copy the contiguous [ntt, d] slab
+        // whole rows are 16-byte multiples: copy the contiguous [ntt, d] slab,
+        // eight loads in flight per thread before their stores
         const int per_row = d * (int)sizeof(T) / 16;
         const uint4 *src = reinterpret_cast<const uint4 *>(x + t0 * d);
         uint4 *dst = reinterpret_cast<uint4 *>(xs);
-        for (int i = threadIdx.x; i < TT * per_row; i += 256)
-            dst[i] = i < ntt * per_row ? src[i] : make_uint4(0, 0, 0, 0);
+        for (int i0 = threadIdx.x; i0 < TT * per_row; i0 += 256 * 8) {
+            uint4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + 256 * u;
+                v[u] = i < ntt * per_row ? src[i] : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + 256 * u;
+                if (i < TT * per_row) dst[i] = v[u];
+            }
+        }
     } else {
         for (int i = threadIdx.x; i < TT * d; i += 256) {
             int tt = i / d;
@@ -77,8 +105,6 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
     }
     __syncthreads();
 
-    const bool vec = (d % 8) == 0;
-    const bool preload = vec && sizeof(T) == 2 && d <= 512 * kMaxChunks;
     for (int rr = 0; rr < RW; ++rr) {
         const int row = blockIdx.y * 4 * RW + wave * RW + rr;
         if (row > E || (row == E && g == nullptr)) break;
@@ -87,11 +113,13 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) acc[tt] = 0.0f;
         if (preload) {
-            uint4 wq[kMaxChunks];
+            if (rr > 0) {
 #pragma unroll
-            for (int c = 0; c < kMaxChunks; ++c) {
-                const int kk0 = 512 * c + 8 * lane;
-                wq[c] = kk0 < d ? *reinterpret_cast<const uint4 *>(wrow + kk0) : make_uint4(0, 0, 0, 0);
+                for (int c = 0; c < kMaxChunks; ++c) {
+                    const int kk0 = 512 * c + 8 * lane;
+                    wq[c] = kk0 < d ? *reinterpret_cast<const uint4 *>(wrow + kk0)
+                                    : make_uint4(0, 0, 0, 0);
+                }
             }
 #pragma unroll
             for (int c = 0; c < kMaxChunks; ++c) {
@@ -155,6 +183,25 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
     }
 }
 
+// Maximum of v over the wave, in every lane: quad permutes, row rotates and
+// row broadcasts (DPP) leave the full maximum in lane 63.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_max_step(float x) {
+    const int o = __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, ROW_MASK,
+                                              0xF, false);
+    return fmaxf(x, __int_as_float(o));
+}
+
+__device__ __forceinline__ float wave_max_dpp(float v) {
+    v = dpp_max_step<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+    v = dpp_max_step<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+    v = dpp_max_step<0x124, 0xF>(v);  // row_ror:4
+    v = dpp_max_step<0x128, 0xF>(v);  // row_ror:8
+    v = dpp_max_step<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v = dpp_max_step<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 // One wave per token: top-k by (logit desc, expert asc), weights, gate.
 // Lane L holds the logits of experts L, L+64, ..., so a lane's candidates
 // are already in ascending expert order.
@@ -181,28 +228,27 @@ __global__ __launch_bounds__(256) void router_select_kernel(
     float my_l = 0.0f;
     int my_e = 0;
     for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int be = 0x7FFFFFFF;
+        // largest remaining logit (a DPP max over the wave) ...
+        float lm = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            if (!((removed >> i) & 1u)) lm = fmaxf(lm, v[i]);
+        const float m = wave_max_dpp(lm);
+        // ... and the lowest expert holding it: expert lane + 64 i grows with
+        // i first, then with the lane
+        int e = 0;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int e = lane + 64 * i;
-            if (!((removed >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < be))) {
-                bv = v[i];
-                be = e;
+            const uint64_t hit = __ballot(!((removed >> i) & 1u) && v[i] == m);
+            if (hit) {
+                e = 64 * i + (int)__builtin_ctzll(hit);
+                break;
             }
         }
-        for (int o = 32; o >= 1; o >>= 1) {
-            const float ov = __shfl_xor(bv, o, kWave);
-            const int oe = __shfl_xor(be, o, kWave);
-            if (ov > bv || (ov == bv && oe < be)) {
-                bv = ov;
-                be = oe;
-            }
-        }
-        if ((be & 63) == lane) removed |= 1u << (be >> 6);
+        if ((e & 63) == lane) removed |= 1u << (e >> 6);
         if (lane == j) {
-            my_l = bv;
-            my_e = be;
+            my_l = m;
+            my_e = e;
         }
     }
     const float lmax = __shfl(my_l, 0, kWave);
