@@ -21,6 +21,7 @@ namespace moe {
 
 constexpr int DBM = kDecodeBM;  // rows per decode tile
 constexpr int KG = 128;         // K elements per pipeline group (4 MFMA steps)
+constexpr int DW = 2;           // waves per block (finer blocks: a shorter tail)
 
 struct DecodeArgs {
     const uint16_t *x;
@@ -130,13 +131,13 @@ __device__ __forceinline__ bool decode_tile(const DecodeArgs &a, TileInfo &ti) {
     return true;
 }
 
-// gate/up: block = 4 waves, wave w owns gate columns n0 + 16 w .. + 16 and the
-// matching up columns; grid.y walks 64-column slabs of the expert width.
+// gate/up: block = DW waves, wave w owns gate columns n0 + 16 w .. + 16 and
+// the matching up columns; grid.y walks 16 DW-column slabs of the expert width.
 template <int HALVES>
 __device__ void decode_gateup_body(const DecodeArgs &a, const TileInfo &ti, const int *row_tok) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int Fg = ti.shared ? a.Fs : a.F;
-    const int ncol = blockIdx.y * 64 + wave * 16;  // first gate column of this wave
+    const int ncol = blockIdx.y * 16 * DW + wave * 16;  // first gate column of this wave
     const uint16_t *W = ti.shared ? a.w_sh : a.w + (int64_t)ti.g * 2 * a.F * a.d;
     const int rl = lane & 15, kq = 8 * (lane >> 4);
     const uint16_t *bp[2] = {W + (int64_t)(ncol + rl) * a.d + kq,
@@ -166,12 +167,12 @@ __device__ void decode_gateup_body(const DecodeArgs &a, const TileInfo &ti, cons
         }
 }
 
-__global__ __launch_bounds__(256) void decode_gateup_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(DecodeArgs a) {
     __shared__ int row_tok[DBM];
     TileInfo ti;
     if (!decode_tile(a, ti)) return;
     const int Fg = ti.shared ? a.Fs : a.F;
-    if (blockIdx.y * 64 >= Fg) return;
+    if (blockIdx.y * 16 * DW >= Fg) return;
     if (threadIdx.x < DBM) {
         const int r = min((int)threadIdx.x, ti.nrows - 1);
         row_tok[threadIdx.x] = ti.shared ? ti.row0 + r : a.perm[ti.row0 + r] / a.k;
@@ -181,14 +182,14 @@ __global__ __launch_bounds__(256) void decode_gateup_kernel(DecodeArgs a) {
     else decode_gateup_body<1>(a, ti, row_tok);
 }
 
-// down: block = 4 waves, wave w owns output columns n0 + 32 w .. + 32 (two
-// 16-column blocks); grid.y walks 128-column slabs of d.
+// down: block = DW waves, wave w owns output columns n0 + 32 w .. + 32 (two
+// 16-column blocks); grid.y walks 32 DW-column slabs of d.
 template <int HALVES>
 __device__ void decode_down_body(const DecodeArgs &a, const TileInfo &ti, const int *row_tok,
                                  const float *row_w) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int Fg = ti.shared ? a.Fs : a.F;
-    const int ncol = blockIdx.y * 128 + wave * 32;
+    const int ncol = blockIdx.y * 32 * DW + wave * 32;
     const uint16_t *W = ti.shared ? a.w_sh : a.w + (int64_t)ti.g * a.d * a.F;
     const int rl = lane & 15, kq = 8 * (lane >> 4);
     const uint16_t *bp[2] = {W + (int64_t)min(ncol + rl, a.d - 1) * Fg + kq,
@@ -222,12 +223,12 @@ __device__ void decode_down_body(const DecodeArgs &a, const TileInfo &ti, const 
             }
 }
 
-__global__ __launch_bounds__(256) void decode_down_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * DW) void decode_down_kernel(DecodeArgs a) {
     __shared__ int row_tok[DBM];
     __shared__ float row_w[DBM];
     TileInfo ti;
     if (!decode_tile(a, ti)) return;
-    if (blockIdx.y * 128 >= a.d) return;
+    if (blockIdx.y * 32 * DW >= a.d) return;
     if (threadIdx.x < DBM) {
         const int r = min((int)threadIdx.x, ti.nrows - 1);
         if (ti.shared) {
@@ -268,12 +269,12 @@ hipError_t launch_experts_decode(const Problem &p, hipStream_t s,
     const int fmax = p.F > p.Fs ? p.F : p.Fs;
     a.w = static_cast<const uint16_t *>(p.w_gate_up);
     a.w_sh = static_cast<const uint16_t *>(p.w_sh_gate_up);
-    hipLaunchKernelGGL(decode_gateup_kernel, dim3(p.max_tiles, (fmax + 63) / 64), dim3(256), 0, s,
+    hipLaunchKernelGGL(decode_gateup_kernel, dim3(p.max_tiles, (fmax + 16 * DW - 1) / (16 * DW)), dim3(64 * DW), 0, s,
                        a);
     mark(3);
     a.w = static_cast<const uint16_t *>(p.w_down);
     a.w_sh = static_cast<const uint16_t *>(p.w_sh_down);
-    hipLaunchKernelGGL(decode_down_kernel, dim3(p.max_tiles, (p.d + 127) / 128), dim3(256), 0, s,
+    hipLaunchKernelGGL(decode_down_kernel, dim3(p.max_tiles, (p.d + 32 * DW - 1) / (32 * DW)), dim3(64 * DW), 0, s,
                        a);
     mark(4);
     return hipGetLastError();
