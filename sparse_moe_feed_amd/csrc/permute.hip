@@ -142,22 +142,23 @@ __global__ __launch_bounds__(kCountBlock) void route_scatter_kernel(
 
 // All of the above in one block of 1024 threads when every token fits one
 // histogram block (T <= 256): no block prefix is needed and one launch
-// replaces three.
-__global__ __launch_bounds__(1024) void route_permute_small_kernel(
-    const int32_t *__restrict__ topk_idx, int ntok, int k, int E, int bm, int has_shared,
-    int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ tile_start,
-    int32_t *__restrict__ tile_group, int32_t *__restrict__ row_of, int32_t *__restrict__ perm) {
-    extern __shared__ uint32_t bits[];  // [E][kWords], then offsets [E]
-    int32_t *s_off = reinterpret_cast<int32_t *>(bits + E * kWords);
-    for (int i = threadIdx.x; i < E * kWords; i += 1024) bits[i] = 0;
-    __syncthreads();
+// replaces three.  topk points at the routing (global memory or LDS); bits
+// is [E][kWords] and s_off [E], both in LDS.
+__device__ __forceinline__ void permute_small(const int32_t *topk, int ntok, int k, int E, int bm,
+                                              int has_shared, uint32_t *bits, int32_t *s_off,
+                                              int32_t *__restrict__ counts,
+                                              int32_t *__restrict__ offsets,
+                                              int32_t *__restrict__ tile_start,
+                                              int32_t *__restrict__ tile_group,
+                                              int32_t *__restrict__ row_of,
+                                              int32_t *__restrict__ perm) {
     const int t = threadIdx.x;
     const bool valid = t < ntok;
     const int word = t >> 5;
     const uint32_t bit = 1u << (t & 31);
     if (valid)
         for (int j = 0; j < k; ++j)
-            atomicOr(&bits[clamp_expert(topk_idx[t * k + j], E) * kWords + word], bit);
+            atomicOr(&bits[clamp_expert(topk[t * k + j], E) * kWords + word], bit);
     __syncthreads();
     const int e = threadIdx.x;
     int total = 0;
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(1024) void route_permute_small_kernel(
     __syncthreads();
     if (valid)
         for (int j = 0; j < k; ++j) {
-            const int ee = clamp_expert(topk_idx[t * k + j], E);
+            const int ee = clamp_expert(topk[t * k + j], E);
             const uint32_t *b = bits + ee * kWords;
             int r = __popc(b[word] & (bit - 1u));
             for (int w = 0; w < word; ++w) r += __popc(b[w]);
@@ -195,6 +196,18 @@ __global__ __launch_bounds__(1024) void route_permute_small_kernel(
             perm[pos] = t * k + j;
             row_of[t * k + j] = pos;
         }
+}
+
+__global__ __launch_bounds__(1024) void route_permute_small_kernel(
+    const int32_t *__restrict__ topk_idx, int ntok, int k, int E, int bm, int has_shared,
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ tile_start,
+    int32_t *__restrict__ tile_group, int32_t *__restrict__ row_of, int32_t *__restrict__ perm) {
+    extern __shared__ uint32_t bits[];  // [E][kWords], then offsets [E]
+    int32_t *s_off = reinterpret_cast<int32_t *>(bits + E * kWords);
+    for (int i = threadIdx.x; i < E * kWords; i += 1024) bits[i] = 0;
+    __syncthreads();
+    permute_small(topk_idx, ntok, k, E, bm, has_shared, bits, s_off, counts, offsets, tile_start,
+                  tile_group, row_of, perm);
 }
 
 hipError_t launch_permute(const Problem &p, int bm, hipStream_t s) {

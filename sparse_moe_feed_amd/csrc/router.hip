@@ -36,6 +36,7 @@
 // cancels, so only the k selected logits are needed.
 #include "moe_device.h"
 #include "moe_kernels.h"
+#include "router_select.h"
 
 #include <math.h>
 
@@ -183,28 +184,8 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
     }
 }
 
-// Maximum of v over the wave, in every lane: quad permutes, row rotates and
-// row broadcasts (DPP) leave the full maximum in lane 63.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_max_step(float x) {
-    const int o = __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, ROW_MASK,
-                                              0xF, false);
-    return fmaxf(x, __int_as_float(o));
-}
-
-__device__ __forceinline__ float wave_max_dpp(float v) {
-    v = dpp_max_step<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
-    v = dpp_max_step<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
-    v = dpp_max_step<0x124, 0xF>(v);  // row_ror:4
-    v = dpp_max_step<0x128, 0xF>(v);  // row_ror:8
-    v = dpp_max_step<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
-    v = dpp_max_step<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-
-// One wave per token: top-k by (logit desc, expert asc), weights, gate.
-// Lane L holds the logits of experts L, L+64, ..., so a lane's candidates
-// are already in ascending expert order.
+// One wave per token: top-k by (logit desc, expert asc), weights, gate
+// (select_topk in router_select.h).
 template <int NV>
 __global__ __launch_bounds__(256) void router_select_kernel(
     const float *__restrict__ logits, int64_t ntok, int E, int k, int has_gate,
@@ -213,56 +194,9 @@ __global__ __launch_bounds__(256) void router_select_kernel(
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= ntok) return;
-    const float *l = logits + t * (E + 1);
-
-    float v[NV];
-    uint32_t removed = 0;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int e = lane + 64 * i;
-        float val = e < E ? l[e] : -INFINITY;
-        v[i] = (val == val) ? val : -INFINITY;  // NaN orders as -inf
-        if (e >= E) removed |= 1u << i;
-    }
-
-    float my_l = 0.0f;
-    int my_e = 0;
-    for (int j = 0; j < k; ++j) {
-        // largest remaining logit (a DPP max over the wave) ...
-        float lm = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < NV; ++i)
-            if (!((removed >> i) & 1u)) lm = fmaxf(lm, v[i]);
-        const float m = wave_max_dpp(lm);
-        // ... and the lowest expert holding it: expert lane + 64 i grows with
-        // i first, then with the lane
-        int e = 0;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const uint64_t hit = __ballot(!((removed >> i) & 1u) && v[i] == m);
-            if (hit) {
-                e = 64 * i + (int)__builtin_ctzll(hit);
-                break;
-            }
-        }
-        if ((e & 63) == lane) removed |= 1u << (e >> 6);
-        if (lane == j) {
-            my_l = m;
-            my_e = e;
-        }
-    }
-    const float lmax = __shfl(my_l, 0, kWave);
-    const float ex = lane < k ? expf(my_l - lmax) : 0.0f;
-    const float z = wave_sum(ex);
-    if (lane < k) {
-        topk_idx[t * k + lane] = my_e;
-        topk_w[t * k + lane] = ex / z;
-    }
-    if (has_gate && lane == 0) {
-        const float s = 1.0f / (1.0f + expf(-l[E]));
-        gate[t] = s;
-        if (gate_user) gate_user[t] = s;
-    }
+    select_topk<NV>(logits + t * (E + 1), E, k, lane, topk_idx + t * k, topk_w + t * k,
+                    has_gate ? gate + t : nullptr, has_gate && gate_user ? gate_user + t : nullptr,
+                    nullptr);
 }
 
 // Euclidean norm of each router row: one wave per row.

@@ -76,6 +76,13 @@ def test_fp32_ragged_width():
     check_case(inp, 3, "fp32 d=100 F=33 Fs=7")
 
 
+def test_one_block_permutation_largest():
+    # T <= 256: the permutation runs in one block; E = 1024 and k = 32 give
+    # it the largest histogram
+    inp = W.small_case(256, 64, 1024, 32, 32, 32, "f32", seed=6)
+    check_case(inp, 32, "fp32 T=256 E=1024 k=32")
+
+
 def test_route_entry_matches_oracle():
     inp = W.small_case(200, 256, 64, 10, 64, 64, "bf16", seed=9)
     announce("moe_route T=200 E=64 k=10")
