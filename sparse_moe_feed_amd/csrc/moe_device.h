@@ -23,11 +23,12 @@ __device__ __forceinline__ float bf16_hi(uint32_t two) { return __uint_as_float(
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // binary32 -> bfloat16, round to nearest, ties to even (NaN -> quiet NaN).
+// A select, not a branch: the streaming loops call it and must stay branch-free.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t quiet = (u >> 16) | 0x40u;
+    return (uint16_t)((u & 0x7FFFFFFFu) > 0x7F800000u ? quiet : rounded);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {

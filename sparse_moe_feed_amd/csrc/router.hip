@@ -456,7 +456,12 @@ static hipError_t launch_logits(const Problem &p, hipStream_t s) {
         hipLaunchKernelGGL((router_logits_kernel<T, TT, RW>), gr, block, TT * row_bytes, s, x,   \
                            wr, g, p.router_bias, p.logits, p.T, p.d, p.E);                       \
     } while (0)
-    if (p.T <= 256) {
+    if (p.T <= 64) {
+        // fewer tokens per block: more blocks in flight for a small batch
+        if (4 * row_bytes <= 65536) MOE_LOGITS(4, 1);
+        else if (2 * row_bytes <= 65536) MOE_LOGITS(2, 1);
+        else MOE_LOGITS(1, 1);
+    } else if (p.T <= 256) {
         if (8 * row_bytes <= 65536) MOE_LOGITS(8, 1);
         else if (4 * row_bytes <= 65536) MOE_LOGITS(4, 1);
         else if (2 * row_bytes <= 65536) MOE_LOGITS(2, 1);
