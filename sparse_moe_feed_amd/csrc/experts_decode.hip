@@ -58,6 +58,24 @@ __device__ __forceinline__ void load_group(Frag (&b)[NB], Frag (&a)[HALVES],
     }
 }
 
+template <int NB>
+__device__ __forceinline__ void load_b(Frag (&b)[NB], const uint16_t *const (&bp)[NB], int g) {
+    const int kb = g * KG;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int n = 0; n < NB; ++n) b[n].v[s] = *reinterpret_cast<const uint4 *>(bp[n] + kb + 32 * s);
+}
+
+template <int HALVES>
+__device__ __forceinline__ void load_a(Frag (&a)[HALVES], const uint16_t *const (&ap)[HALVES], int g) {
+    const int kb = g * KG;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int h = 0; h < HALVES; ++h) a[h].v[s] = *reinterpret_cast<const uint4 *>(ap[h] + kb + 32 * s);
+}
+
 template <int NB, int HALVES>
 __device__ __forceinline__ void mfma_group(f32x4 (&acc)[HALVES][NB], const Frag (&b)[NB],
                                            const Frag (&a)[HALVES]) {
@@ -77,17 +95,19 @@ __device__ __forceinline__ void mfma_group(f32x4 (&acc)[HALVES][NB], const Frag 
 // lane's token row plus k offset (padding rows point at a valid row; their
 // results are never stored).  Two groups of loads are kept in flight
 // (ping-pong register buffers).
+// stream_k_from: the same with group 0 already loaded into b0 / a0 by the
+// caller (which can then issue its B loads before the A addresses are known).
 template <int NB, int HALVES>
-__device__ __forceinline__ void stream_k(const uint16_t *const (&bp)[NB],
-                                         const uint16_t *const (&ap)[HALVES], int K,
-                                         f32x4 (&acc)[HALVES][NB]) {
-    Frag b0[NB], b1[NB], a0[HALVES], a1[HALVES];
+__device__ __forceinline__ void stream_k_from(Frag (&b0)[NB], Frag (&a0)[HALVES],
+                                              const uint16_t *const (&bp)[NB],
+                                              const uint16_t *const (&ap)[HALVES], int K,
+                                              f32x4 (&acc)[HALVES][NB]) {
+    Frag b1[NB], a1[HALVES];
     const int ng = K / KG;
     // The steady-state body has no branches around loads (any branch makes
     // the compiler's wait counts fall back to zero), and sched_barrier keeps
     // the phases in program order, so a group's loads are in flight while the
     // previous group's MFMAs run.  The last one or two groups are peeled.
-    load_group<NB, HALVES>(b0, a0, bp, ap, 0);
     int g = 0;
     for (; g + 2 < ng; g += 2) {
         load_group<NB, HALVES>(b1, a1, bp, ap, g + 1);
@@ -108,6 +128,15 @@ __device__ __forceinline__ void stream_k(const uint16_t *const (&bp)[NB],
     } else {
         mfma_group<NB, HALVES>(acc, b0, a0);
     }
+}
+
+template <int NB, int HALVES>
+__device__ __forceinline__ void stream_k(const uint16_t *const (&bp)[NB],
+                                         const uint16_t *const (&ap)[HALVES], int K,
+                                         f32x4 (&acc)[HALVES][NB]) {
+    Frag b0[NB], a0[HALVES];
+    load_group<NB, HALVES>(b0, a0, bp, ap, 0);
+    stream_k_from<NB, HALVES>(b0, a0, bp, ap, K, acc);
 }
 
 struct TileInfo {
@@ -133,27 +162,36 @@ __device__ __forceinline__ bool decode_tile(const DecodeArgs &a, TileInfo &ti) {
 
 // gate/up: block = DW waves, wave w owns gate columns n0 + 16 w .. + 16 and
 // the matching up columns; grid.y walks 16 DW-column slabs of the expert width.
+// Each lane looks up the token of its own A rows; the first group's weight
+// loads are issued before those lookups are waited for.
 template <int HALVES>
-__device__ void decode_gateup_body(const DecodeArgs &a, const TileInfo &ti, const int *row_tok) {
+__device__ void decode_gateup_body(const DecodeArgs &a, const TileInfo &ti) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int Fg = ti.shared ? a.Fs : a.F;
     const int ncol = blockIdx.y * 16 * DW + wave * 16;  // first gate column of this wave
     const uint16_t *W = ti.shared ? a.w_sh : a.w + (int64_t)ti.g * 2 * a.F * a.d;
     const int rl = lane & 15, kq = 8 * (lane >> 4);
-    const uint16_t *bp[2] = {W + (int64_t)(ncol + rl) * a.d + kq,
-                             W + (int64_t)(Fg + ncol + rl) * a.d + kq};
-    const uint16_t *ap[HALVES];
+    int tok[HALVES];
 #pragma unroll
     for (int h = 0; h < HALVES; ++h) {
-        const int r = 16 * h + rl;
-        ap[h] = a.x + (int64_t)row_tok[r] * a.d + kq;  // row_tok is clamped to valid rows
+        const int r = min(16 * h + rl, ti.nrows - 1);  // padding rows repeat the last row
+        tok[h] = ti.shared ? ti.row0 + r : a.perm[ti.row0 + r];
     }
+    const uint16_t *bp[2] = {W + (int64_t)(ncol + rl) * a.d + kq,
+                             W + (int64_t)(Fg + ncol + rl) * a.d + kq};
+    Frag b0[2], a0[HALVES];
+    load_b<2>(b0, bp, 0);
+    const uint16_t *ap[HALVES];
+#pragma unroll
+    for (int h = 0; h < HALVES; ++h)
+        ap[h] = a.x + (int64_t)(ti.shared ? tok[h] : tok[h] / a.k) * a.d + kq;
+    load_a<HALVES>(a0, ap, 0);
     f32x4 acc[HALVES][2];
 #pragma unroll
     for (int h = 0; h < HALVES; ++h)
 #pragma unroll
         for (int n = 0; n < 2; ++n) acc[h][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    stream_k<2, HALVES>(bp, ap, a.d, acc);
+    stream_k_from<2, HALVES>(b0, a0, bp, ap, a.d, acc);
     uint16_t *H = ti.shared ? a.h_sh : a.h;
     // 16x16 accumulator: lane holds column lane % 16, rows 4 (lane / 16) + i.
 #pragma unroll
@@ -168,30 +206,36 @@ __device__ void decode_gateup_body(const DecodeArgs &a, const TileInfo &ti, cons
 }
 
 __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(DecodeArgs a) {
-    __shared__ int row_tok[DBM];
     TileInfo ti;
     if (!decode_tile(a, ti)) return;
     const int Fg = ti.shared ? a.Fs : a.F;
     if (blockIdx.y * 16 * DW >= Fg) return;
-    if (threadIdx.x < DBM) {
-        const int r = min((int)threadIdx.x, ti.nrows - 1);
-        row_tok[threadIdx.x] = ti.shared ? ti.row0 + r : a.perm[ti.row0 + r] / a.k;
-    }
-    __syncthreads();
-    if (ti.nrows > 16) decode_gateup_body<2>(a, ti, row_tok);
-    else decode_gateup_body<1>(a, ti, row_tok);
+    if (ti.nrows > 16) decode_gateup_body<2>(a, ti);
+    else decode_gateup_body<1>(a, ti);
 }
 
 // down: block = DW waves, wave w owns output columns n0 + 32 w .. + 32 (two
-// 16-column blocks); grid.y walks 32 DW-column slabs of d.
+// 16-column blocks); grid.y walks 32 DW-column slabs of d.  Nothing in the
+// stream depends on the routing (h rows are the tile's own rows), so the
+// lookups that the epilogue needs (pair ids, then weights) are issued first
+// and resolved after the stream.
 template <int HALVES>
-__device__ void decode_down_body(const DecodeArgs &a, const TileInfo &ti, const int *row_tok,
-                                 const float *row_w) {
+__device__ void decode_down_body(const DecodeArgs &a, const TileInfo &ti) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int Fg = ti.shared ? a.Fs : a.F;
     const int ncol = blockIdx.y * 32 * DW + wave * 32;
-    const uint16_t *W = ti.shared ? a.w_sh : a.w + (int64_t)ti.g * a.d * a.F;
     const int rl = lane & 15, kq = 8 * (lane >> 4);
+    // this lane's output rows 16 h + 4 (lane / 16) + i: routed rows need their
+    // pair id (for the weight), shared rows are tokens row0 + row
+    int src[HALVES][4];
+#pragma unroll
+    for (int h = 0; h < HALVES; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = min(16 * h + 4 * (lane >> 4) + i, ti.nrows - 1);
+            src[h][i] = ti.shared ? ti.row0 + r : a.perm[ti.row0 + r];
+        }
+    const uint16_t *W = ti.shared ? a.w_sh : a.w + (int64_t)ti.g * a.d * a.F;
     const uint16_t *bp[2] = {W + (int64_t)min(ncol + rl, a.d - 1) * Fg + kq,
                              W + (int64_t)min(ncol + 16 + rl, a.d - 1) * Fg + kq};
     const uint16_t *H = ti.shared ? a.h_sh : a.h;
@@ -207,6 +251,11 @@ __device__ void decode_down_body(const DecodeArgs &a, const TileInfo &ti, const 
 #pragma unroll
         for (int n = 0; n < 2; ++n) acc[h][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     stream_k<2, HALVES>(bp, ap, Fg, acc);
+    float wr[HALVES][4];
+#pragma unroll
+    for (int h = 0; h < HALVES; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wr[h][i] = ti.shared ? a.gate[src[h][i]] : a.topk_w[src[h][i]];
 #pragma unroll
     for (int h = 0; h < HALVES; ++h)
 #pragma unroll
@@ -216,33 +265,19 @@ __device__ void decode_down_body(const DecodeArgs &a, const TileInfo &ti, const 
                 const int row = 16 * h + 4 * (lane >> 4) + i;
                 const int col = ncol + 16 * n + rl;
                 if (row < ti.nrows && col < a.d) {
-                    const float v = row_w[row] * acc[h][n][i];
-                    if (ti.shared) a.out[(int64_t)row_tok[row] * a.d + col] = v;
+                    const float v = wr[h][i] * acc[h][n][i];
+                    if (ti.shared) a.out[(int64_t)(ti.row0 + row) * a.d + col] = v;
                     else a.y[(int64_t)(ti.row0 + row) * a.d + col] = f32_to_bf16_rne(v);
                 }
             }
 }
 
 __global__ __launch_bounds__(64 * DW) void decode_down_kernel(DecodeArgs a) {
-    __shared__ int row_tok[DBM];
-    __shared__ float row_w[DBM];
     TileInfo ti;
     if (!decode_tile(a, ti)) return;
     if (blockIdx.y * 32 * DW >= a.d) return;
-    if (threadIdx.x < DBM) {
-        const int r = min((int)threadIdx.x, ti.nrows - 1);
-        if (ti.shared) {
-            row_tok[threadIdx.x] = ti.row0 + r;
-            row_w[threadIdx.x] = a.gate[ti.row0 + r];
-        } else {
-            const int pair = a.perm[ti.row0 + r];
-            row_tok[threadIdx.x] = pair / a.k;
-            row_w[threadIdx.x] = a.topk_w[pair];
-        }
-    }
-    __syncthreads();
-    if (ti.nrows > 16) decode_down_body<2>(a, ti, row_tok, row_w);
-    else decode_down_body<1>(a, ti, row_tok, row_w);
+    if (ti.nrows > 16) decode_down_body<2>(a, ti);
+    else decode_down_body<1>(a, ti);
 }
 
 hipError_t launch_experts_decode(const Problem &p, hipStream_t s,

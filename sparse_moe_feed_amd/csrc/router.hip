@@ -310,31 +310,36 @@ __global__ __launch_bounds__(256) void router_select_shortlist_kernel(
         }
     }
 
-    // tau and Delta_A from the k largest approximate logits
+    // tau and Delta_A from the k largest approximate logits: per round a DPP
+    // wave maximum, the lowest expert holding it by ballot, and that expert's
+    // Delta read from its lane (taken candidates become NaN)
     float tau = 0.f, dA = 0.f;
     {
-        uint32_t rem = removed;
+        float fr[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) fr[i] = ((removed >> i) & 1u) ? __builtin_nanf("") : fb[i];
         for (int j = 0; j < k; ++j) {
-            float bv = -INFINITY;
-            int be = 0x7FFFFFFF;
+            float lm = fr[0];
+#pragma unroll
+            for (int i = 1; i < NV; ++i) lm = fmaxf(lm, fr[i]);
+            const float m = wave_max_dpp(lm);
+            int e = 0;
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
-                const int e = lane + 64 * i;
-                if (!((rem >> i) & 1u) && (fb[i] > bv || (fb[i] == bv && e < be))) {
-                    bv = fb[i];
-                    be = e;
+                const uint64_t hit = __ballot(fr[i] == m);
+                if (hit) {
+                    e = 64 * i + (int)__builtin_ctzll(hit);
+                    break;
                 }
             }
-            wave_best(bv, be);
             float mine = 0.f;
-            if ((be & 63) == lane) {
-                rem |= 1u << (be >> 6);
 #pragma unroll
-                for (int i = 0; i < NV; ++i)
-                    if (i == (be >> 6)) mine = dl[i];
+            for (int i = 0; i < NV; ++i) {
+                if (i == (e >> 6)) mine = dl[i];
+                if (e == lane + 64 * i) fr[i] = __builtin_nanf("");
             }
-            dA = fmaxf(dA, __shfl(mine, be & 63, kWave));
-            tau = bv;
+            dA = fmaxf(dA, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), e & 63)));
+            tau = m;
         }
     }
     const float theta = tau - dA;
@@ -368,14 +373,16 @@ __global__ __launch_bounds__(256) void router_select_shortlist_kernel(
                 ++c;
             }
         }
-        bool gone = lane >= count;
+        // top k of the shortlist: DPP maximum, lowest lane (= lowest expert,
+        // candidates being in ascending order) holding it, which drops out
+        if (lane >= count) lc = __builtin_nanf("");
         for (int j = 0; j < k; ++j) {
-            float bv = gone ? -INFINITY : lc;
-            int be = gone ? 0x7FFFFFFF : ec;
-            wave_best(bv, be);
-            if (be == ec) gone = true;
+            const float mx = wave_max_dpp(lc);
+            const int wl = (int)__builtin_ctzll(__ballot(lc == mx));
+            const int be = __builtin_amdgcn_readlane(ec, wl);
+            if (lane == wl) lc = __builtin_nanf("");
             if (lane == j) {
-                my_l = bv;
+                my_l = mx;
                 my_e = be;
             }
         }
