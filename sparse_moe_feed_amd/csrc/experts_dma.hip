@@ -14,16 +14,20 @@
 // Tiles go straight from global memory into LDS (global_load_lds_dwordx4:
 // lane i of one load writes 16 bytes at the load's LDS base + 16 i), so no
 // registers hold tiles in flight and the K loop runs up to three steps
-// ahead through three stage buffers of BK = 32 (a buffer is refilled as soon
-// as every wave has read it).  One load fills 16 tile rows of 64 bytes;
-// chunk c of row R sits at chunk c ^ ((R >> 2) & 3).  A 16-byte read by 64
-// lanes is served 16 lanes (256 bytes) per clock, so the 16 rows read
-// together at one chunk must cover all 64 banks: rows R .. R+3 fill four
-// 16-byte bank groups each and the XOR moves every group of four rows to a
-// different quarter (measured conflict-free; without it each read takes 4x
-// as long).  A step waits for its own stage with an explicit vmcnt and a
-// bare s_barrier (a __syncthreads fence would drain every load in flight);
-// the block drains all its loads before it ends.
+// ahead through three stage buffers of BK = 32 or 64 (a buffer is refilled as
+// soon as every wave has read it).  BK = 64 reads 128 contiguous bytes of
+// each weight row per step, which HBM streams about 10% faster than 64-byte
+// pieces; its 48 KB stages leave room for one block per CU, so it serves the
+// long-K gate/up tiles of 128 rows, and BK = 32 (two blocks per CU) the
+// short-K down tiles and the 256-row tiles.  One load fills one KB of LDS:
+// 16 rows of 64 bytes (BK = 32) or 8 rows of 128 bytes (BK = 64).  A 16-byte
+// read by 64 lanes is served 16 lanes (256 bytes) per clock, so the 16 rows
+// read together at one chunk must cover all 64 banks: chunk c of row R sits
+// at chunk c ^ ((R >> 2) & 3) for 64-byte rows and c ^ ((R >> 1) & 7) for
+// 128-byte rows (measured conflict-free for 64-byte rows; without the XOR
+// each read takes 4x as long).  A step waits for its own stage with an
+// explicit vmcnt and a bare s_barrier (a __syncthreads fence would drain
+// every load in flight); the block drains all its loads before it ends.
 #include "moe_device.h"
 #include "moe_kernels.h"
 
@@ -31,23 +35,24 @@
 
 namespace moe {
 
-#ifndef MOE_NS128
-#define MOE_NS128 3
-#endif
-
 namespace {
-constexpr int BN = 256, BK = 32;
-constexpr int ROWB = BK * 2;    // bytes per staged tile row
-constexpr int OPB = BN * ROWB;  // B bytes per stage (16 KB)
-constexpr int NB = 4;           // 32-column blocks per wave
+constexpr int BN = 256;
+constexpr int NB = 4;  // 32-column blocks per wave
 
-// Per tile height: A bytes per stage, stage bytes (A then B), A loads per
-// wave per stage, loads per wave per stage, 32-row sub-tiles per wave.
-template <int BM> struct Geo {
+// Per tile height BM and K step BK (32 or 64): bytes per staged row, 16-byte
+// chunks per row, rows per 1 KB load, A and stage bytes (A then B), A and B
+// loads per wave per stage, k16 sub-steps per stage, 32-row sub-tiles per wave.
+template <int BM, int BK> struct Geo {
+    static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
+    static constexpr int ROWB = BK * 2;
+    static constexpr int CH = ROWB / 16;
+    static constexpr int RPL = 64 / CH;
     static constexpr int OPA = BM * ROWB;
-    static constexpr int STB = OPA + OPB;
-    static constexpr int AL = BM / 64;
-    static constexpr int LOADS = AL + 4;
+    static constexpr int STB = OPA + BN * ROWB;
+    static constexpr int AL = BM / RPL / 4;
+    static constexpr int BL = BN / RPL / 4;
+    static constexpr int LOADS = AL + BL;
+    static constexpr int Q = BK / 16;
     static constexpr int MI = BM / 64;
 };
 
@@ -60,30 +65,38 @@ typedef const __attribute__((address_space(1))) void global_void_t;
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 constexpr int vmcnt_lgkm0_imm(int n) { return vmcnt_imm(n) & ~(0xF << 8); }
 
-__device__ __forceinline__ int swz(int R) { return (R >> 2) & 3; }
-__device__ __forceinline__ int tile_off(int R, int c) { return R * ROWB + ((c ^ swz(R)) << 4); }
+// Chunk swizzle: the 16 rows that one 16-lane read phase touches at one
+// logical chunk land on 16 distinct 16-byte bank groups.
+template <int BK> __device__ __forceinline__ int swz(int R) {
+    return BK == 32 ? (R >> 2) & 3 : (R >> 1) & 7;
+}
+template <int BK> __device__ __forceinline__ int tile_off(int R, int c) {
+    return R * (2 * BK) + ((c ^ swz<BK>(R)) << 4);
+}
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 }  // namespace
 
-// Issue one stage's loads: this wave fills A rows 16 (AL wave + j) .. + 15,
-// j < AL, and B rows 16 (4 wave + j) .. + 15, j < 4.  aoff/boff are this
-// lane's element offsets (its row and swizzled chunk); k0 selects the K step.
-template <int BM>
+// Issue one stage's loads: each load fills one contiguous KB of LDS, RPL
+// tile rows.  This wave fills A rows RPL (AL wave + j) .., j < AL, and B rows
+// RPL (BL wave + j) .., j < BL.  aoff/boff are this lane's element offsets
+// (its row and swizzled chunk); k0 selects the K step.
+template <int BM, int BK>
 __device__ __forceinline__ void dma_stage(unsigned char *stage, const uint16_t *abase,
                                           const uint16_t *wbase,
-                                          const uint32_t (&aoff)[Geo<BM>::AL],
-                                          const uint32_t (&boff)[4], int k0, int wave) {
-    constexpr int AL = Geo<BM>::AL;
+                                          const uint32_t (&aoff)[Geo<BM, BK>::AL],
+                                          const uint32_t (&boff)[Geo<BM, BK>::BL], int k0,
+                                          int wave) {
+    using G = Geo<BM, BK>;
 #pragma unroll
-    for (int j = 0; j < AL; ++j)
+    for (int j = 0; j < G::AL; ++j)
         __builtin_amdgcn_global_load_lds((const global_void_t *)(abase + aoff[j] + k0),
-                                         (lds_void_t *)(stage + (AL * wave + j) * 16 * ROWB), 16,
+                                         (lds_void_t *)(stage + (G::AL * wave + j) * 1024), 16,
                                          0, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < G::BL; ++j)
         __builtin_amdgcn_global_load_lds(
             (const global_void_t *)(wbase + boff[j] + k0),
-            (lds_void_t *)(stage + Geo<BM>::OPA + (4 * wave + j) * 16 * ROWB), 16, 0, 0);
+            (lds_void_t *)(stage + G::OPA + (G::BL * wave + j) * 1024), 16, 0, 0);
 }
 
 // Operand fragments of one k16 step: MACT A blocks and the wave's NB B blocks.
@@ -91,17 +104,19 @@ struct Frags {
     bf16x8 a[4], b[NB];
 };
 
-template <int BM, int MACT>
+template <int BM, int BK, int MACT>
 __device__ __forceinline__ void read_frags(const unsigned char *stage, int ks, int wm,
                                            const int (&brow)[NB], int fr, int lane, Frags &f) {
     if (MACT == 0) return;
     const int c = 2 * ks + (lane >> 5);
 #pragma unroll
     for (int mi = 0; mi < MACT; ++mi)
-        f.a[mi] = *reinterpret_cast<const bf16x8 *>(stage + tile_off(BM / 2 * wm + 32 * mi + fr, c));
+        f.a[mi] = *reinterpret_cast<const bf16x8 *>(stage +
+                                                    tile_off<BK>(BM / 2 * wm + 32 * mi + fr, c));
 #pragma unroll
     for (int ni = 0; ni < NB; ++ni)
-        f.b[ni] = *reinterpret_cast<const bf16x8 *>(stage + Geo<BM>::OPA + tile_off(brow[ni] + fr, c));
+        f.b[ni] = *reinterpret_cast<const bf16x8 *>(stage + Geo<BM, BK>::OPA +
+                                                    tile_off<BK>(brow[ni] + fr, c));
 }
 
 // acc[mi][ni] accumulates B_ni A_mi^T (output features by tokens), so each
@@ -135,10 +150,25 @@ __device__ __forceinline__ void interleave_reads() {
     __builtin_amdgcn_sched_group_barrier(0x008, MACT * NB - 1 - reads, 0);
 }
 
+// MFMAs on the k16 fragments in cur while sub-step ks of stage goes to nxt.
+template <int BM, int BK, int MACT>
+__device__ __forceinline__ void sub_step(const unsigned char *stage, int ks, int wm,
+                                         const int (&brow)[NB], int fr, int lane, const Frags &cur,
+                                         Frags &nxt, f32x16 (&acc)[Geo<BM, BK>::MI][NB]) {
+    if (MACT > 0) {
+        mfma_frags<MACT>(cur, acc);
+        read_frags<BM, BK, MACT>(stage, ks, wm, brow, fr, lane, nxt);
+        interleave_reads<MACT>();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // One K step kt on stage buffer S = kt % NS, entered with stage kt visible to
 // all waves and its first k16 fragments in f0.  Stages kt+1 .. kt+NS-1 are in
 // flight ((NS-1) LOADS loads per wave, oldest first).
-//   1. MFMAs on f0 while the second k16 fragments of stage kt go to f1;
+//   1. MFMAs on each k16 sub-step but the last while the next one's
+//      fragments are read (f0 and f1 alternate; Q is even, so the last
+//      sub-step's fragments end in f1);
 //   2. wait until this wave's reads of stage kt are done and its part of
 //      stage kt+1 has landed (lgkmcnt 0, vmcnt <= (NS-2) LOADS), then
 //      barrier: stage kt+1 is visible and no wave reads buffer S any more;
@@ -148,84 +178,79 @@ __device__ __forceinline__ void interleave_reads() {
 // Every stage buffer is its own LDS array named by a constant index, so the
 // compiler ties each LDS read to the loads of that buffer alone instead of
 // waiting for every load in flight.
-template <int BM, int NS, int MACT, int S>
+template <int BM, int BK, int NS, int MACT, int S>
 __device__ __forceinline__ void k_step(const Stages<NS> &st, int kt, int last,
                                        const uint16_t *abase, const uint16_t *wbase,
-                                       const uint32_t (&aoff)[Geo<BM>::AL],
-                                       const uint32_t (&boff)[4], int wave, int wm,
+                                       const uint32_t (&aoff)[Geo<BM, BK>::AL],
+                                       const uint32_t (&boff)[Geo<BM, BK>::BL], int wave, int wm,
                                        const int (&brow)[NB], int fr, int lane, Frags &f0,
-                                       Frags &f1, f32x16 (&acc)[Geo<BM>::MI][NB]) {
-    if (MACT > 0) {
-        mfma_frags<MACT>(f0, acc);
-        read_frags<BM, MACT>(st.s[S], 1, wm, brow, fr, lane, f1);
-        interleave_reads<MACT>();
+                                       Frags &f1, f32x16 (&acc)[Geo<BM, BK>::MI][NB]) {
+    using G = Geo<BM, BK>;
+    sub_step<BM, BK, MACT>(st.s[S], 1, wm, brow, fr, lane, f0, f1, acc);
+    if constexpr (G::Q == 4) {
+        sub_step<BM, BK, MACT>(st.s[S], 2, wm, brow, fr, lane, f1, f0, acc);
+        sub_step<BM, BK, MACT>(st.s[S], 3, wm, brow, fr, lane, f0, f1, acc);
     }
-    __builtin_amdgcn_sched_barrier(0);
     compiler_fence();
-    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm((NS - 2) * Geo<BM>::LOADS));
+    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm((NS - 2) * G::LOADS));
     __builtin_amdgcn_s_barrier();
     compiler_fence();
-    dma_stage<BM>(st.s[S], abase, wbase, aoff, boff, min((kt + NS) * BK, last), wave);
+    dma_stage<BM, BK>(st.s[S], abase, wbase, aoff, boff, min((kt + NS) * BK, last), wave);
     __builtin_amdgcn_sched_barrier(0);
-    if (MACT > 0) {
-        mfma_frags<MACT>(f1, acc);
-        read_frags<BM, MACT>(st.s[(S + 1) % NS], 0, wm, brow, fr, lane, f0);
-        interleave_reads<MACT>();
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    sub_step<BM, BK, MACT>(st.s[(S + 1) % NS], 0, wm, brow, fr, lane, f1, f0, acc);
 }
 
 // Steps kt + S .. kt + cnt - 1 (cnt <= NS), each on its constant buffer.
-template <int BM, int NS, int MACT, int S>
+template <int BM, int BK, int NS, int MACT, int S>
 __device__ __forceinline__ void k_steps(const Stages<NS> &st, int kt, int cnt, int last,
                                         const uint16_t *abase, const uint16_t *wbase,
-                                        const uint32_t (&aoff)[Geo<BM>::AL],
-                                        const uint32_t (&boff)[4], int wave, int wm,
+                                        const uint32_t (&aoff)[Geo<BM, BK>::AL],
+                                        const uint32_t (&boff)[Geo<BM, BK>::BL], int wave, int wm,
                                         const int (&brow)[NB], int fr, int lane, Frags &f0,
-                                        Frags &f1, f32x16 (&acc)[Geo<BM>::MI][NB]) {
+                                        Frags &f1, f32x16 (&acc)[Geo<BM, BK>::MI][NB]) {
     if constexpr (S < NS) {
         if (S < cnt) {
-            k_step<BM, NS, MACT, S>(st, kt + S, last, abase, wbase, aoff, boff, wave, wm, brow, fr,
-                                    lane, f0, f1, acc);
-            k_steps<BM, NS, MACT, S + 1>(st, kt, cnt, last, abase, wbase, aoff, boff, wave, wm,
-                                         brow, fr, lane, f0, f1, acc);
+            k_step<BM, BK, NS, MACT, S>(st, kt + S, last, abase, wbase, aoff, boff, wave, wm,
+                                        brow, fr, lane, f0, f1, acc);
+            k_steps<BM, BK, NS, MACT, S + 1>(st, kt, cnt, last, abase, wbase, aoff, boff, wave,
+                                             wm, brow, fr, lane, f0, f1, acc);
         }
     }
 }
 
 // Issue stages S .. NS-1 of the prologue into their buffers.
-template <int BM, int NS, int S>
+template <int BM, int BK, int NS, int S>
 __device__ __forceinline__ void prologue(const Stages<NS> &st, int last, const uint16_t *abase,
                                          const uint16_t *wbase,
-                                         const uint32_t (&aoff)[Geo<BM>::AL],
-                                         const uint32_t (&boff)[4], int wave) {
+                                         const uint32_t (&aoff)[Geo<BM, BK>::AL],
+                                         const uint32_t (&boff)[Geo<BM, BK>::BL], int wave) {
     if constexpr (S < NS) {
-        dma_stage<BM>(st.s[S], abase, wbase, aoff, boff, min(S * BK, last), wave);
-        prologue<BM, NS, S + 1>(st, last, abase, wbase, aoff, boff, wave);
+        dma_stage<BM, BK>(st.s[S], abase, wbase, aoff, boff, min(S * BK, last), wave);
+        prologue<BM, BK, NS, S + 1>(st, last, abase, wbase, aoff, boff, wave);
     }
 }
 
-template <int BM, int NS, int MACT>
+template <int BM, int BK, int NS, int MACT>
 __device__ __forceinline__ void k_loop(const Stages<NS> &st, const uint16_t *abase,
                                        const uint16_t *wbase,
-                                       const uint32_t (&aoff)[Geo<BM>::AL],
-                                       const uint32_t (&boff)[4], int nk, int wave, int wm,
-                                       const int (&brow)[NB], int fr, int lane,
-                                       f32x16 (&acc)[Geo<BM>::MI][NB]) {
+                                       const uint32_t (&aoff)[Geo<BM, BK>::AL],
+                                       const uint32_t (&boff)[Geo<BM, BK>::BL], int nk, int wave,
+                                       int wm, const int (&brow)[NB], int fr, int lane,
+                                       f32x16 (&acc)[Geo<BM, BK>::MI][NB]) {
     const int last = (nk - 1) * BK;
-    prologue<BM, NS, 0>(st, last, abase, wbase, aoff, boff, wave);
+    prologue<BM, BK, NS, 0>(st, last, abase, wbase, aoff, boff, wave);
     compiler_fence();
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 1) * Geo<BM>::LOADS));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 1) * Geo<BM, BK>::LOADS));
     __builtin_amdgcn_s_barrier();
     compiler_fence();
     Frags f0, f1;
-    read_frags<BM, MACT>(st.s[0], 0, wm, brow, fr, lane, f0);
+    read_frags<BM, BK, MACT>(st.s[0], 0, wm, brow, fr, lane, f0);
     int kt = 0;
     for (; kt + NS <= nk; kt += NS)
-        k_steps<BM, NS, MACT, 0>(st, kt, NS, last, abase, wbase, aoff, boff, wave, wm, brow, fr,
-                                 lane, f0, f1, acc);
-    k_steps<BM, NS, MACT, 0>(st, kt, nk - kt, last, abase, wbase, aoff, boff, wave, wm, brow, fr,
-                             lane, f0, f1, acc);
+        k_steps<BM, BK, NS, MACT, 0>(st, kt, NS, last, abase, wbase, aoff, boff, wave, wm, brow,
+                                     fr, lane, f0, f1, acc);
+    k_steps<BM, BK, NS, MACT, 0>(st, kt, nk - kt, last, abase, wbase, aoff, boff, wave, wm, brow,
+                                 fr, lane, f0, f1, acc);
     compiler_fence();
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land after the block ends
     __builtin_amdgcn_s_barrier();
@@ -234,10 +259,10 @@ __device__ __forceinline__ void k_loop(const Stages<NS> &st, const uint16_t *aba
 
 // NS stage buffers; up to 80 KB of them leaves room for two blocks per CU, so
 // one block's start-up and epilogue overlap the other's streaming.
-template <int MODE, int BM, int NS>
-__global__ __launch_bounds__(256, NS * Geo<BM>::STB <= 80 * 1024 ? 2 : 1) void gemm_dma_kernel(
+template <int MODE, int BM, int BK, int NS>
+__global__ __launch_bounds__(256, (NS * Geo<BM, BK>::STB <= 80 * 1024 ? 2 : 1)) void gemm_dma_kernel(
     GemmArgs a) {
-    using G = Geo<BM>;
+    using G = Geo<BM, BK>;
     static_assert(NS >= 3 && NS <= 6, "three to six stage buffers");
     __shared__ __align__(1024) unsigned char st0[G::STB];
     __shared__ __align__(1024) unsigned char st1[G::STB];
@@ -294,18 +319,18 @@ __global__ __launch_bounds__(256, NS * Geo<BM>::STB <= 80 * 1024 ? 2 : 1) void g
     const uint16_t *abase = MODE == 1 ? (shared ? a.h_sh : a.h) : a.x;
     // element offsets (32-bit: the host checks that every offset fits) of this
     // lane's row and swizzled chunk in each of its loads
-    uint32_t aoff[G::AL], boff[4];
+    uint32_t aoff[G::AL], boff[G::BL];
 #pragma unroll
     for (int j = 0; j < G::AL; ++j) {
-        const int R = (G::AL * wave + j) * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ swz(R);
+        const int R = (G::AL * wave + j) * G::RPL + lane / G::CH;
+        const int c = (lane % G::CH) ^ swz<BK>(R);
         aoff[j] = (MODE == 1 ? (uint32_t)(row0 + min(R, nrows - 1)) * (uint32_t)Fg
                              : (uint32_t)row_tok[R] * (uint32_t)a.d) + 8 * c;
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int R = (4 * wave + j) * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ swz(R);
+    for (int j = 0; j < G::BL; ++j) {
+        const int R = (G::BL * wave + j) * G::RPL + lane / G::CH;
+        const int c = (lane % G::CH) ^ swz<BK>(R);
         boff[j] = (MODE == 1 ? (uint32_t)min(n0 + R, a.d - 1) * (uint32_t)Fg
                              : (uint32_t)(R < BN / 2 ? n0 + R : Fg + n0 + (R - BN / 2)) *
                                    (uint32_t)a.d) + 8 * c;
@@ -340,7 +365,7 @@ __global__ __launch_bounds__(256, NS * Geo<BM>::STB <= 80 * 1024 ? 2 : 1) void g
     }
     // mact is decided once, outside the K loop, so the loop body is one
     // straight block of loads and MFMAs.
-#define MOE_LOOP(M) k_loop<BM, NS, M>(st, abase, wbase, aoff, boff, nk, wave, wm, brow, fr, lane, acc)
+#define MOE_LOOP(M) k_loop<BM, BK, NS, M>(st, abase, wbase, aoff, boff, nk, wave, wm, brow, fr, lane, acc)
     if constexpr (G::MI == 4) {
         switch (mact) {
         case 4: MOE_LOOP(4); break;
@@ -449,14 +474,14 @@ hipError_t launch_experts_dma(const Problem &p, int bm, hipStream_t s,
     a.nm = p.max_tiles;
     a.nn = (fmax + BN / 2 - 1) / (BN / 2);
     a.gm = -1;  // M-tile m on XCD m % 8: its N-tiles share A through one L2
-    if (bm == 256) hipLaunchKernelGGL((gemm_dma_kernel<0, 256, 3>), grid(a), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((gemm_dma_kernel<0, 128, MOE_NS128>), grid(a), dim3(256), 0, s, a);
+    if (bm == 256) hipLaunchKernelGGL((gemm_dma_kernel<0, 256, 32, 3>), grid(a), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((gemm_dma_kernel<0, 128, 64, 3>), grid(a), dim3(256), 0, s, a);
     mark(3);
     a.w = static_cast<const uint16_t *>(p.w_down);
     a.w_sh = static_cast<const uint16_t *>(p.w_sh_down);
     a.nn = (p.d + BN - 1) / BN;
-    if (bm == 256) hipLaunchKernelGGL((gemm_dma_kernel<1, 256, 3>), grid(a), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((gemm_dma_kernel<1, 128, MOE_NS128>), grid(a), dim3(256), 0, s, a);
+    if (bm == 256) hipLaunchKernelGGL((gemm_dma_kernel<1, 256, 32, 3>), grid(a), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((gemm_dma_kernel<1, 128, 32, 3>), grid(a), dim3(256), 0, s, a);
     mark(4);
     return hipGetLastError();
 }
