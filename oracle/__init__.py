@@ -18,6 +18,14 @@ What each function follows (pages cited by title and section):
     field", ffns.moe.gated; llm-atlas "Qwen3.8-Flash-Next", "Raw config
     fields", hidden_act) plus one shared expert scaled by its own sigmoid gate
     (anatomy page, Feed-forward panel and "Evidence for layer 1").
+  * ``experts_mx4`` / ``forward_mx4`` / ``mx4_decode`` -- the same layer with
+    low-bit expert weights.  The published weights are packed low-bit tensors
+    (llm-atlas "Qwen3.8-Flash-Next", "Modelled costs"); the encoding is not
+    named there, and the reading taken is MXFP4 of the OCP Microscaling (MX)
+    specification v1.0 (E2M1 elements, one E8M0 scale per 32 elements of a
+    row, two codes per byte with the even element in the low nibble).  An MX
+    tensor is passed as a pair ``(codes uint8 [..., K/2], scales uint8
+    [..., K/32])``.
 """
 from __future__ import annotations
 
@@ -63,8 +71,12 @@ def _load():
                                    vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.oracle_forward.argtypes = [i64, i32, i32, i32, i32, i32, i32,
                                    vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.oracle_experts_mx4.argtypes = [i64, i32, i32, i32, i32, i32] + [vp] * 14
+    lib.oracle_forward_mx4.argtypes = [i64, i32, i32, i32, i32, i32] + [vp] * 16
+    lib.oracle_mx4_decode.argtypes = [i64, i64, vp, vp, vp]
     for f in (lib.oracle_router_logits, lib.oracle_route, lib.oracle_experts,
-              lib.oracle_forward, lib.oracle_threads):
+              lib.oracle_forward, lib.oracle_threads, lib.oracle_experts_mx4,
+              lib.oracle_forward_mx4, lib.oracle_mx4_decode):
         f.restype = ctypes.c_int
     lib.oracle_threads.argtypes = []
     _lib = lib
@@ -184,4 +196,88 @@ def forward(x, w_router, w_gate_up, w_down, k, w_sh_gate_up=None, w_sh_down=None
                                 _ptr(w), _ptr(s))
     if rc:
         raise RuntimeError(f"oracle_forward failed ({rc})")
+    return out, idx, w, s
+
+
+def _mx(t, rows_shape, K):
+    """Validate one MXFP4 tensor (codes, scales) of logical shape rows_shape + (K,)."""
+    if t is None:
+        return None, None
+    codes, scales = t
+    if codes.dtype != np.uint8 or scales.dtype != np.uint8:
+        raise TypeError("MXFP4 codes and scales are uint8 arrays")
+    if K % 32:
+        raise ValueError("MXFP4 rows must hold a multiple of 32 elements")
+    if codes.shape != tuple(rows_shape) + (K // 2,) or scales.shape != tuple(rows_shape) + (K // 32,):
+        raise ValueError(f"MXFP4 tensor shapes {codes.shape}/{scales.shape} do not match "
+                         f"{tuple(rows_shape)} x {K}")
+    return _ptr(codes), _ptr(scales)
+
+
+def mx4_decode(codes, scales) -> np.ndarray:
+    """Every element of an MXFP4 tensor [rows, K] decoded exactly (float64)."""
+    rows = int(np.prod(codes.shape[:-1]))
+    K = codes.shape[-1] * 2
+    c, sc = _mx((codes, scales), codes.shape[:-1], K)
+    out = np.empty(codes.shape[:-1] + (K,), np.float64)
+    rc = _load().oracle_mx4_decode(rows, K, c, sc, _ptr(out))
+    if rc:
+        raise RuntimeError(f"oracle_mx4_decode failed ({rc})")
+    return out
+
+
+def _mx4_layer_ptrs(gu, dn, sgu, sdn, E, F, Fs, d):
+    ptrs = []
+    ptrs += _mx(gu, (E, 2 * F), d)
+    ptrs += _mx(dn, (E, d), F)
+    ptrs += _mx(sgu, (2 * Fs,), d) if Fs else (None, None)
+    ptrs += _mx(sdn, (d,), Fs) if Fs else (None, None)
+    return ptrs
+
+
+def experts_mx4(x, gu, dn, topk_idx, topk_w, sgu=None, sdn=None, sh_gate=None,
+                return_gate=False):
+    """Expert stage with MXFP4 expert weights and the routing given.  x and
+    sh_gate are bfloat16 bits; gu, dn, sgu, sdn are (codes, scales) pairs of
+    logical shapes [E,2F,d], [E,d,F], [2Fs,d], [d,Fs]."""
+    T, d = x.shape
+    if _dtype_code(x) != BF16:
+        raise TypeError("MXFP4 layers take bfloat16 activations")
+    E, twoF = gu[0].shape[:2]
+    F = twoF // 2
+    Fs = 0 if sgu is None else sgu[0].shape[0] // 2
+    k = topk_idx.shape[1]
+    ptrs = _mx4_layer_ptrs(gu, dn, sgu, sdn, E, F, Fs, d)
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    w = np.ascontiguousarray(topk_w, dtype=np.float64)
+    out = np.empty((T, d), np.float64)
+    s = np.full((T,), np.nan, np.float64)
+    rc = _load().oracle_experts_mx4(T, d, E, k, F, Fs, _ptr(x), *ptrs, _ptr(sh_gate),
+                                    _ptr(idx), _ptr(w), _ptr(out), _ptr(s))
+    if rc:
+        raise RuntimeError(f"oracle_experts_mx4 failed ({rc})")
+    return (out, s) if return_gate else out
+
+
+def forward_mx4(x, w_router, gu, dn, k, sgu=None, sdn=None, sh_gate=None, bias=None):
+    """The whole layer with MXFP4 expert weights: (out float64 [T,d], topk_idx
+    [T,k], topk_w float64 [T,k], s float64 [T])."""
+    T, d = x.shape
+    if _dtype_code(x) != BF16:
+        raise TypeError("MXFP4 layers take bfloat16 activations")
+    _same(BF16, w_router, sh_gate)
+    E, twoF = gu[0].shape[:2]
+    F = twoF // 2
+    Fs = 0 if sgu is None else sgu[0].shape[0] // 2
+    ptrs = _mx4_layer_ptrs(gu, dn, sgu, sdn, E, F, Fs, d)
+    b = _bias(bias, E)
+    out = np.empty((T, d), np.float64)
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    s = np.full((T,), np.nan, np.float64)
+    rc = _load().oracle_forward_mx4(T, d, E, k, F, Fs, _ptr(x), _ptr(w_router), _ptr(b),
+                                    *ptrs, _ptr(sh_gate), _ptr(out), _ptr(idx), _ptr(w),
+                                    _ptr(s))
+    if rc:
+        raise RuntimeError(f"oracle_forward_mx4 failed ({rc})")
     return out, idx, w, s

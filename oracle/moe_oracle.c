@@ -35,6 +35,17 @@
  *   - An optional fp32 router bias b[E] is added to the finished dot product.
  *   - Everything after the router logit is computed in binary64 with no
  *     intermediate rounding.
+ *   - Low-bit expert weights: the model's published weights are packed
+ *     low-bit tensors (llm-atlas "Qwen3.8-Flash-Next", "Modelled costs",
+ *     published-weights row); the pages do not name the encoding.  The
+ *     reading taken here is MXFP4 from the OCP Microscaling (MX)
+ *     specification v1.0: each run of 32 consecutive elements of a weight row
+ *     (along the reduction axis) shares one E8M0 scale byte X, worth
+ *     2^(X - 127), and every element is an FP4 E2M1 code (sign bit 3,
+ *     exponent bits 2..1 with bias 1, mantissa bit 0; exponent 0 encodes
+ *     0 or 0.5).  Codes are stored two per byte, element 2i in bits 3..0 and
+ *     element 2i+1 in bits 7..4.  The oracle decodes every element exactly
+ *     and then runs the same binary64 gated MLPs.
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fopenmp -shared -fPIC
  * (no fast-math: the binary32 router logit must round exactly as written).
@@ -46,6 +57,7 @@
 
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
+#define ORACLE_MXFP4 2
 
 /* Read element i of an array that holds either binary32 values or bfloat16
  * bit patterns.  Widening bfloat16 to binary32 is exact (append 16 zero
@@ -58,6 +70,44 @@ static float load_elem(const void *base, int dtype, int64_t i)
     float f;
     memcpy(&f, &bits, sizeof f);
     return f;
+}
+
+/* FP4 E2M1 element (OCP MX v1.0): sign bit 3, 2-bit exponent field e with
+ * bias 1, 1-bit mantissa m.  e = 0 is the subnormal range, m * 2^(1-1) / 2;
+ * otherwise 2^(e-1) * (1 + m/2).  The format has no infinity or NaN. */
+static double e2m1_value(unsigned code)
+{
+    unsigned sign = (code >> 3) & 1u, e = (code >> 1) & 3u, m = code & 1u;
+    double v = e == 0 ? 0.5 * (double)m : ldexp(1.0 + 0.5 * (double)m, (int)e - 1);
+    return sign ? -v : v;
+}
+
+/* E8M0 scale (OCP MX v1.0): 2^(X - 127); X = 255 is NaN. */
+static double e8m0_value(unsigned x)
+{
+    return x == 255u ? NAN : ldexp(1.0, (int)x - 127);
+}
+
+/* An expert weight matrix of `cols` elements per row (the reduction axis):
+ * binary32 or bfloat16 elements, or MXFP4 codes with one scale byte per 32
+ * elements of a row (scales [rows, cols/32]). */
+typedef struct {
+    int fmt;
+    const void *data;
+    const uint8_t *scales;
+    int64_t cols;
+} wsrc;
+
+/* Element (row, kk) of w, exactly, in binary64. */
+static double load_w(const wsrc *w, int64_t row, int64_t kk)
+{
+    if (w->fmt != ORACLE_MXFP4)
+        return (double)load_elem(w->data, w->fmt, row * w->cols + kk);
+    int64_t i = row * w->cols + kk;
+    unsigned byte = ((const uint8_t *)w->data)[i / 2];
+    unsigned code = (i % 2) ? (byte >> 4) : (byte & 15u);
+    unsigned x = w->scales[row * (w->cols / 32) + kk / 32];
+    return e2m1_value(code) * e8m0_value(x);
 }
 
 /* Router logit l = sum_k x[k] * w[k] + bias in binary32, canonical order:
@@ -199,43 +249,40 @@ static double shared_gate(const void *x, int64_t xoff, const void *g, int d,
 /* One gated-MLP expert on one token, binary64:
  *   a = W_gate x, u = W_up x, h = silu(a) * u with silu(a) = a / (1 + e^-a),
  *   y = W_down h.
- * w_gu points at the packed [2F, d] gate/up block (gate rows first), w_dn at
- * the [d, F] down block. */
-static void gated_mlp(const void *x, int64_t xoff, const void *w_gu,
-                      int64_t gu_off, const void *w_dn, int64_t dn_off, int d,
-                      int F, int dtype, double *h, double *y)
+ * The expert's gate/up block is rows gu_row .. gu_row + 2F - 1 of w_gu
+ * (gate rows first, d elements each); its down block is rows
+ * dn_row .. dn_row + d - 1 of w_dn (F elements each). */
+static void gated_mlp(const void *x, int64_t xoff, int dtype, const wsrc *w_gu,
+                      int64_t gu_row, const wsrc *w_dn, int64_t dn_row, int d,
+                      int F, double *h, double *y)
 {
     for (int n = 0; n < F; n++) {
         double a = 0.0, u = 0.0;
         for (int kk = 0; kk < d; kk++) {
             double xv = (double)load_elem(x, dtype, xoff + kk);
-            a += (double)load_elem(w_gu, dtype, gu_off + (int64_t)n * d + kk) * xv;
-            u += (double)load_elem(w_gu, dtype, gu_off + (int64_t)(F + n) * d + kk) * xv;
+            a += load_w(w_gu, gu_row + n, kk) * xv;
+            u += load_w(w_gu, gu_row + F + n, kk) * xv;
         }
         h[n] = a / (1.0 + exp(-a)) * u;
     }
     for (int m = 0; m < d; m++) {
         double acc = 0.0;
         for (int n = 0; n < F; n++)
-            acc += (double)load_elem(w_dn, dtype, dn_off + (int64_t)m * F + n) * h[n];
+            acc += load_w(w_dn, dn_row + m, n) * h[n];
         y[m] = acc;
     }
 }
 
 /* Expert stage with routing given: out[t] = sum_j w[t,j] * y_{idx[t,j]}(x_t)
  * + s_t * y_shared(x_t).  With Fs == 0 the shared term is absent.  s_out
- * (nullable) receives the shared gate values. */
-int oracle_experts(int64_t T, int d, int E, int k, int F, int Fs, int dtype,
-                   const void *x, const void *w_gate_up, const void *w_down,
-                   const void *w_sh_gate_up, const void *w_sh_down,
-                   const void *sh_gate, const int32_t *topk_idx,
-                   const double *topk_w, double *out, double *s_out)
+ * (nullable) receives the shared gate values.  x and sh_gate are in dtype;
+ * the four expert weight tensors are described by their wsrc. */
+static int experts_impl(int64_t T, int d, int E, int k, int F, int Fs,
+                        int dtype, const void *x, const wsrc *w_gu,
+                        const wsrc *w_dn, const wsrc *w_sgu, const wsrc *w_sdn,
+                        const void *sh_gate, const int32_t *topk_idx,
+                        const double *topk_w, double *out, double *s_out)
 {
-    if (T < 0 || d < 1 || E < 1 || k < 1 || F < 1 || Fs < 0 || !x ||
-        !w_gate_up || !w_down || !topk_idx || !topk_w || !out)
-        return 1;
-    if (Fs > 0 && (!w_sh_gate_up || !w_sh_down || !sh_gate))
-        return 1;
     for (int64_t i = 0; i < T * k; i++)
         if (topk_idx[i] < 0 || topk_idx[i] >= E)
             return 1;
@@ -257,8 +304,8 @@ int oracle_experts(int64_t T, int d, int E, int k, int F, int Fs, int dtype,
                 o[m] = 0.0;
             for (int j = 0; j < k; j++) {
                 int e = topk_idx[t * k + j];
-                gated_mlp(x, t * d, w_gate_up, (int64_t)e * 2 * F * d, w_down,
-                          (int64_t)e * d * F, d, F, dtype, h, y);
+                gated_mlp(x, t * d, dtype, w_gu, (int64_t)e * 2 * F, w_dn,
+                          (int64_t)e * d, d, F, h, y);
                 for (int m = 0; m < d; m++)
                     o[m] += topk_w[t * k + j] * y[m];
             }
@@ -266,8 +313,7 @@ int oracle_experts(int64_t T, int d, int E, int k, int F, int Fs, int dtype,
                 double s = shared_gate(x, t * d, sh_gate, d, dtype);
                 if (s_out)
                     s_out[t] = s;
-                gated_mlp(x, t * d, w_sh_gate_up, 0, w_sh_down, 0, d, Fs, dtype,
-                          h, y);
+                gated_mlp(x, t * d, dtype, w_sgu, 0, w_sdn, 0, d, Fs, h, y);
                 for (int m = 0; m < d; m++)
                     o[m] += s * y[m];
             }
@@ -276,6 +322,65 @@ int oracle_experts(int64_t T, int d, int E, int k, int F, int Fs, int dtype,
         free(y);
     }
     return fail ? 2 : 0;
+}
+
+int oracle_experts(int64_t T, int d, int E, int k, int F, int Fs, int dtype,
+                   const void *x, const void *w_gate_up, const void *w_down,
+                   const void *w_sh_gate_up, const void *w_sh_down,
+                   const void *sh_gate, const int32_t *topk_idx,
+                   const double *topk_w, double *out, double *s_out)
+{
+    if (T < 0 || d < 1 || E < 1 || k < 1 || F < 1 || Fs < 0 || !x ||
+        !w_gate_up || !w_down || !topk_idx || !topk_w || !out)
+        return 1;
+    if (Fs > 0 && (!w_sh_gate_up || !w_sh_down || !sh_gate))
+        return 1;
+    wsrc gu = {dtype, w_gate_up, NULL, d}, dn = {dtype, w_down, NULL, F};
+    wsrc sgu = {dtype, w_sh_gate_up, NULL, d}, sdn = {dtype, w_sh_down, NULL, Fs};
+    return experts_impl(T, d, E, k, F, Fs, dtype, x, &gu, &dn, &sgu, &sdn,
+                        sh_gate, topk_idx, topk_w, out, s_out);
+}
+
+/* The expert stage with MXFP4 expert weights (routed and shared): codes
+ * [E,2F,d/2], [E,d,F/2], [2Fs,d/2], [d,Fs/2]; scales [E,2F,d/32],
+ * [E,d,F/32], [2Fs,d/32], [d,Fs/32].  x and sh_gate are bfloat16.  d, F and
+ * Fs must be multiples of 32. */
+int oracle_experts_mx4(int64_t T, int d, int E, int k, int F, int Fs,
+                       const void *x, const uint8_t *gu_codes,
+                       const uint8_t *gu_scales, const uint8_t *dn_codes,
+                       const uint8_t *dn_scales, const uint8_t *sgu_codes,
+                       const uint8_t *sgu_scales, const uint8_t *sdn_codes,
+                       const uint8_t *sdn_scales, const void *sh_gate,
+                       const int32_t *topk_idx, const double *topk_w,
+                       double *out, double *s_out)
+{
+    if (T < 0 || d < 1 || E < 1 || k < 1 || F < 1 || Fs < 0 || !x ||
+        !gu_codes || !gu_scales || !dn_codes || !dn_scales || !topk_idx ||
+        !topk_w || !out || d % 32 || F % 32 || Fs % 32)
+        return 1;
+    if (Fs > 0 && (!sgu_codes || !sgu_scales || !sdn_codes || !sdn_scales ||
+                   !sh_gate))
+        return 1;
+    wsrc gu = {ORACLE_MXFP4, gu_codes, gu_scales, d};
+    wsrc dn = {ORACLE_MXFP4, dn_codes, dn_scales, F};
+    wsrc sgu = {ORACLE_MXFP4, sgu_codes, sgu_scales, d};
+    wsrc sdn = {ORACLE_MXFP4, sdn_codes, sdn_scales, Fs};
+    return experts_impl(T, d, E, k, F, Fs, ORACLE_BF16, x, &gu, &dn, &sgu,
+                        &sdn, sh_gate, topk_idx, topk_w, out, s_out);
+}
+
+/* Decoded value of every MXFP4 element of a [rows, cols] tensor, binary64
+ * (for tests of the decoder itself). */
+int oracle_mx4_decode(int64_t rows, int64_t cols, const uint8_t *codes,
+                      const uint8_t *scales, double *out)
+{
+    if (rows < 0 || cols < 1 || cols % 32 || !codes || !scales || !out)
+        return 1;
+    wsrc w = {ORACLE_MXFP4, codes, scales, cols};
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t c = 0; c < cols; c++)
+            out[r * cols + c] = load_w(&w, r, c);
+    return 0;
 }
 
 /* The whole layer: routing (oracle_route) then the expert stage. */
@@ -293,6 +398,27 @@ int oracle_forward(int64_t T, int d, int E, int k, int F, int Fs, int dtype,
     return oracle_experts(T, d, E, k, F, Fs, dtype, x, w_gate_up, w_down,
                           w_sh_gate_up, w_sh_down, sh_gate, topk_idx, topk_w,
                           out, s_out);
+}
+
+/* The whole layer with MXFP4 expert weights: routing on the bfloat16 router
+ * (oracle_route), then oracle_experts_mx4. */
+int oracle_forward_mx4(int64_t T, int d, int E, int k, int F, int Fs,
+                       const void *x, const void *w_router, const float *bias,
+                       const uint8_t *gu_codes, const uint8_t *gu_scales,
+                       const uint8_t *dn_codes, const uint8_t *dn_scales,
+                       const uint8_t *sgu_codes, const uint8_t *sgu_scales,
+                       const uint8_t *sdn_codes, const uint8_t *sdn_scales,
+                       const void *sh_gate, double *out, int32_t *topk_idx,
+                       double *topk_w, double *s_out)
+{
+    int rc = oracle_route(T, d, E, k, ORACLE_BF16, x, w_router, bias, topk_idx,
+                          topk_w, NULL);
+    if (rc)
+        return rc;
+    return oracle_experts_mx4(T, d, E, k, F, Fs, x, gu_codes, gu_scales,
+                              dn_codes, dn_scales, sgu_codes, sgu_scales,
+                              sdn_codes, sdn_scales, sh_gate, topk_idx, topk_w,
+                              out, s_out);
 }
 
 /* Number of threads the parallel loops above use. */

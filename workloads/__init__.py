@@ -16,6 +16,16 @@ weights exist here; these random weights stand in for them.
 Arrays are numpy.  bfloat16 tensors are ``uint16`` arrays of bit patterns
 (round-to-nearest-even from float32 draws); the fp32 configuration uses
 ``float32``.
+
+Low-bit expert weights (configurations of dtype "mxfp4"): the published
+checkpoint stores packed low-bit tensors (llm-atlas "Qwen3.8-Flash-Next",
+"Modelled costs"), encoding unnamed; these inputs use MXFP4 of the OCP
+Microscaling (MX) specification v1.0.  ``mx4_quantize`` plays the part of the
+checkpoint writer: it turns the same float32 draws into E2M1 codes with one
+E8M0 scale per 32 elements along each weight row, by the specification's
+conversion rule (shared exponent floor(log2 max|v|) - 2, elements rounded to
+nearest with ties to even and saturated at 6).  Router, shared gate vector and
+tokens stay bfloat16.
 """
 from __future__ import annotations
 
@@ -43,7 +53,7 @@ class MoEConfig:
     k: int
     F: int
     Fs: int
-    dtype: str                      # "f32" | "bf16"
+    dtype: str                      # "f32" | "bf16" | "mxfp4" (bf16, MXFP4 expert weights)
     bias: Optional[str] = None      # None | "zipf" | "hot10"
     seed_w: int = 1
     seed_x: int = 100
@@ -62,6 +72,8 @@ CONFIGS = {
                  "router bias with a Zipf(1.2) prior over a seeded expert permutation"),
     5: MoEConfig("hot10_T32768", 32768, 2560, 512, 10, 640, 640, "bf16", "hot10", 1, 105, 1005,
                  "router bias making 10 seeded experts take about half of all assignments"),
+    6: MoEConfig("decode_T32_mxfp4", 32, 2560, 512, 10, 640, 640, "mxfp4", None, 1, 102, 1002,
+                 "decode_T32 with MXFP4 expert weights quantized from the same draws"),
 }
 
 
@@ -86,6 +98,47 @@ def _normal(rng: np.random.Generator, shape, std: float, dtype: str) -> np.ndarr
     if std != 1.0:
         a *= np.float32(std)
     return f32_to_bf16_bits(a) if dtype == "bf16" else a
+
+
+# FP4 E2M1 magnitudes by code 0..7 (code = 2 * exponent field + mantissa bit)
+# and the midpoints between neighbours.
+_E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], np.float32)
+_E2M1_MID = (_E2M1_GRID[1:] + _E2M1_GRID[:-1]) / np.float32(2)
+
+
+def mx4_quantize(a: np.ndarray, with_values: bool = False):
+    """MXFP4-encode float32 ``a`` [..., K] along its last axis (K % 32 == 0):
+    returns (codes uint8 [..., K/2], scales uint8 [..., K/32]) and, if asked,
+    the encoded values as float32 [..., K].
+
+    Per block of 32: X = floor(log2(max |v|)) - 2 + 127 (127 for an all-zero
+    block), clamped to 0..254; each v / 2^(X-127) goes to the nearest E2M1
+    value, ties to the even code, magnitudes past 6 saturate to 6.  Element 2i
+    sits in the low nibble of byte i."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    K = a.shape[-1]
+    if K % 32:
+        raise ValueError("MXFP4 rows need a multiple of 32 elements")
+    blk = a.reshape(a.shape[:-1] + (K // 32, 32))
+    amax = np.abs(blk).max(axis=-1)
+    _, ex = np.frexp(amax)                       # amax = m 2^ex, m in [0.5, 1)
+    X = np.where(amax > 0, ex.astype(np.int32) - 1 - 2 + 127, 127)
+    X = np.clip(X, 0, 254)
+    scaled = np.ldexp(blk, (127 - X)[..., None].astype(np.int32)).astype(np.float32)
+    mag = np.abs(scaled)
+    idx = np.searchsorted(_E2M1_MID, mag, side="left")
+    at = np.minimum(idx, len(_E2M1_MID) - 1)
+    tie = (idx < len(_E2M1_MID)) & (_E2M1_MID[at] == mag) & (idx % 2 == 1)
+    idx = (idx + tie).astype(np.uint8)
+    code = idx | (np.signbit(scaled).astype(np.uint8) << 3)
+    code = code.reshape(a.shape)
+    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
+    scales = X.astype(np.uint8)
+    if not with_values:
+        return packed, scales
+    vals = np.where(np.signbit(scaled), -1.0, 1.0).astype(np.float32) * _E2M1_GRID[idx]
+    vals = np.ldexp(vals, (X - 127)[..., None].astype(np.int32)).astype(np.float32)
+    return packed, scales, vals.reshape(a.shape)
 
 
 def _threads() -> int:
@@ -124,10 +177,55 @@ def make_layer(d: int, E: int, F: int, Fs: int, dtype: str, seed: int) -> dict:
     return layer
 
 
+def make_layer_mx4(d: int, E: int, F: int, Fs: int, seed: int, with_values: bool = False) -> dict:
+    """The layer of ``make_layer(d, E, F, Fs, "bf16", seed)`` with its expert
+    weights (routed and shared) MXFP4-encoded from the same float32 draws:
+    keys w_router, sh_gate (bfloat16, identical to the bf16 layer) and gu, dn,
+    sgu, sdn, each a (codes, scales) pair of logical shapes [E,2F,d],
+    [E,d,F], [2Fs,d], [d,Fs].  with_values adds the encoded values as float32
+    arrays gu_values, dn_values, sgu_values, sdn_values."""
+    gu_c = np.empty((E, 2 * F, d // 2), np.uint8)
+    gu_s = np.empty((E, 2 * F, d // 32), np.uint8)
+    dn_c = np.empty((E, d, F // 2), np.uint8)
+    dn_s = np.empty((E, d, F // 32), np.uint8)
+    vals = {}
+    if with_values:
+        vals["gu_values"] = np.empty((E, 2 * F, d), np.float32)
+        vals["dn_values"] = np.empty((E, d, F), np.float32)
+
+    def expert(e):
+        r = mx4_quantize(_normal(_rng(seed, _WGU, e), (2 * F, d), WEIGHT_STD, "f32"), with_values)
+        gu_c[e], gu_s[e] = r[0], r[1]
+        if with_values:
+            vals["gu_values"][e] = r[2]
+        r = mx4_quantize(_normal(_rng(seed, _WDN, e), (d, F), WEIGHT_STD, "f32"), with_values)
+        dn_c[e], dn_s[e] = r[0], r[1]
+        if with_values:
+            vals["dn_values"][e] = r[2]
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(expert, range(E)))
+    layer = dict(w_router=_normal(_rng(seed, _WR), (E, d), WEIGHT_STD, "bf16"),
+                 gu=(gu_c, gu_s), dn=(dn_c, dn_s), sgu=None, sdn=None, sh_gate=None, **vals)
+    if Fs > 0:
+        r = mx4_quantize(_normal(_rng(seed, _WSGU), (2 * Fs, d), WEIGHT_STD, "f32"), with_values)
+        layer["sgu"] = (r[0], r[1])
+        if with_values:
+            layer["sgu_values"] = r[2]
+        r = mx4_quantize(_normal(_rng(seed, _WSDN), (d, Fs), WEIGHT_STD, "f32"), with_values)
+        layer["sdn"] = (r[0], r[1])
+        if with_values:
+            layer["sdn_values"] = r[2]
+        layer["sh_gate"] = _normal(_rng(seed, _G), (d,), WEIGHT_STD, "bf16")
+    return layer
+
+
 def make_x(T: int, d: int, dtype: str, seed: int, row0: int = 0) -> np.ndarray:
     """Tokens x ~ N(0,1), [T, d].  Rows are drawn in blocks of 256 tokens from
     per-block streams, so a row's value does not depend on T (a prefix of a
     longer batch equals the shorter batch) and ``row0`` selects a window."""
+    if dtype == "mxfp4":
+        dtype = "bf16"
     npdt = np.uint16 if dtype == "bf16" else np.float32
     out = np.empty((T, d), npdt)
     B = 256
@@ -188,7 +286,10 @@ def layer_for(cfg: MoEConfig) -> dict:
     key = (cfg.d, cfg.E, cfg.F, cfg.Fs, cfg.dtype, cfg.seed_w)
     if key not in _layer_cache:
         _layer_cache.clear()      # keep at most one full-size layer resident
-        _layer_cache[key] = make_layer(cfg.d, cfg.E, cfg.F, cfg.Fs, cfg.dtype, cfg.seed_w)
+        if cfg.dtype == "mxfp4":
+            _layer_cache[key] = make_layer_mx4(cfg.d, cfg.E, cfg.F, cfg.Fs, cfg.seed_w)
+        else:
+            _layer_cache[key] = make_layer(cfg.d, cfg.E, cfg.F, cfg.Fs, cfg.dtype, cfg.seed_w)
     return _layer_cache[key]
 
 
