@@ -153,6 +153,55 @@ moe_status moe_experts(const moe_desc *desc, int64_t T, const void *x,
                        const float *topk_w, float *out, void *ws,
                        size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Low-bit expert weights (MXFP4).
+ *
+ * The model's published weights are packed low-bit tensors (llm-atlas
+ * "Qwen3.8-Flash-Next", "Modelled costs"; the encoding is not named there).
+ * These entry points take the expert weights, routed and shared, in MXFP4 as
+ * defined by the OCP Microscaling (MX) specification v1.0: every run of 32
+ * consecutive elements of a weight row (along the reduction axis: d for the
+ * gate/up matrices, F or Fs for the down matrices) shares one E8M0 scale
+ * byte X, worth 2^(X-127); each element is an FP4 E2M1 code (sign bit 3,
+ * exponent bits 2..1 with bias 1, mantissa bit 0: magnitudes 0, 0.5, 1, 1.5,
+ * 2, 3, 4, 6).  A tensor of logical shape [rows, K] is two arrays:
+ *   codes   uint8 [rows, K/2]   element 2i in bits 3..0 of byte i, element
+ *                                2i+1 in bits 7..4 (16-byte aligned)
+ *   scales  uint8 [rows, K/32]  the scale of elements 32b .. 32b+31 of a row
+ * so w_gate_up is codes [E,2F,d/2] + scales [E,2F,d/32], w_down codes
+ * [E,d,F/2] + scales [E,d,F/32], w_sh_gate_up [2Fs,d/2] + [2Fs,d/32] and
+ * w_sh_down [d,Fs/2] + [d,Fs/32].  Scale byte 255 (NaN) gives unspecified
+ * results.  Every element is decoded exactly (to bfloat16) and the layer is
+ * then the MOE_BF16 layer on the decoded weights: x, w_router and sh_gate
+ * are bfloat16, desc->dtype must be MOE_BF16, and the workspace is
+ * moe_workspace_size(desc, T).
+ *
+ * Supported: d, F and Fs multiples of 128 and T*k <= 16*E (the
+ * weight-streaming regime of few tokens per expert, e.g. decode); otherwise
+ * MOE_ERR_UNSUPPORTED, before any GPU work.  Errors as for moe_forward.
+ * --------------------------------------------------------------------------- */
+
+/* The whole layer with MXFP4 expert weights; as moe_forward otherwise. */
+moe_status moe_forward_mx4(const moe_desc *desc, int64_t T, const void *x,
+                           const void *w_router, const float *router_bias,
+                           const uint8_t *gate_up_codes, const uint8_t *gate_up_scales,
+                           const uint8_t *down_codes, const uint8_t *down_scales,
+                           const uint8_t *sh_gate_up_codes, const uint8_t *sh_gate_up_scales,
+                           const uint8_t *sh_down_codes, const uint8_t *sh_down_scales,
+                           const void *sh_gate, float *out, int32_t *topk_idx,
+                           float *topk_w, void *ws, size_t ws_bytes, void *stream);
+
+/* The expert stage alone with MXFP4 expert weights and the routing given
+ * (topk_idx, topk_w are INPUTS); as moe_experts otherwise. */
+moe_status moe_experts_mx4(const moe_desc *desc, int64_t T, const void *x,
+                           const uint8_t *gate_up_codes, const uint8_t *gate_up_scales,
+                           const uint8_t *down_codes, const uint8_t *down_scales,
+                           const uint8_t *sh_gate_up_codes, const uint8_t *sh_gate_up_scales,
+                           const uint8_t *sh_down_codes, const uint8_t *sh_down_scales,
+                           const void *sh_gate, const int32_t *topk_idx,
+                           const float *topk_w, float *out, void *ws, size_t ws_bytes,
+                           void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *moe_status_string(moe_status status);
 

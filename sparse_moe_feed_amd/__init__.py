@@ -8,6 +8,8 @@ is no CPU fallback: if the library is missing, every call raises.
 The layer (anatomy page on frontier-model-atlas, "Decoder microscope",
 Feed-forward panel): router logits -> softmax -> top-k -> normalised selected
 weights; SwiGLU experts; one shared expert scaled by its own sigmoid gate.
+Expert weights are bfloat16/binary32 tensors, or MXFP4 pairs ``(codes, scales)``
+of uint8 tensors (``forward_mx4``/``experts_mx4``; layout in ``include/moe.h``).
 """
 from __future__ import annotations
 
@@ -28,7 +30,8 @@ ROUTERS = {None: 0, "auto": 0, "exact": MOE_FLAG_ROUTER_EXACT,
            "shortlist": MOE_FLAG_ROUTER_SHORTLIST}
 
 EXPORTED = ("moe_workspace_size", "moe_workspace_query", "moe_route", "moe_forward",
-            "moe_experts", "moe_status_string", "moe_last_error", "moe_stage_events")
+            "moe_experts", "moe_forward_mx4", "moe_experts_mx4", "moe_status_string",
+            "moe_last_error", "moe_stage_events")
 
 
 class MoEError(RuntimeError):
@@ -69,7 +72,10 @@ def lib():
     L.moe_route.argtypes = [dp, i64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_forward.argtypes = [dp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_experts.argtypes = [dp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    for f in (L.moe_workspace_query, L.moe_route, L.moe_forward, L.moe_experts):
+    L.moe_forward_mx4.argtypes = [dp, i64] + [vp] * 3 + [vp] * 8 + [vp] * 4 + [vp, sz, vp]
+    L.moe_experts_mx4.argtypes = [dp, i64, vp] + [vp] * 8 + [vp] * 4 + [vp, sz, vp]
+    for f in (L.moe_workspace_query, L.moe_route, L.moe_forward, L.moe_experts,
+              L.moe_forward_mx4, L.moe_experts_mx4):
         f.restype = ctypes.c_int
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
@@ -268,6 +274,81 @@ def experts(x, w_gate_up, w_down, topk_idx, topk_w, w_sh_gate_up=None, w_sh_down
     return out
 
 
+def _mx4_dims(gu, sgu):
+    """(E, F, Fs) of an MXFP4 layer from its gate/up code arrays."""
+    E, twoF = gu[0].shape[:2]
+    return E, twoF // 2, 0 if sgu is None else sgu[0].shape[0] // 2
+
+
+def _dev_mx4(t, name, rows, K):
+    if not (isinstance(t, tuple) and len(t) == 2):
+        raise TypeError(f"{name} must be a (codes, scales) pair of uint8 tensors")
+    _dev(t[0], name + " codes", torch.uint8, tuple(rows) + (K // 2,))
+    _dev(t[1], name + " scales", torch.uint8, tuple(rows) + (K // 32,))
+
+
+def _mx4_ptrs(gu, dn, sgu, sdn):
+    ptrs = [_ptr(gu[0]), _ptr(gu[1]), _ptr(dn[0]), _ptr(dn[1])]
+    for t in (sgu, sdn):
+        ptrs += [None, None] if t is None else [_ptr(t[0]), _ptr(t[1])]
+    return ptrs
+
+
+def _check_mx4_weights(d, E, F, Fs, gu, dn, sgu, sdn):
+    _dev_mx4(gu, "w_gate_up", (E, 2 * F), d)
+    _dev_mx4(dn, "w_down", (E, d), F)
+    if Fs:
+        _dev_mx4(sgu, "w_sh_gate_up", (2 * Fs,), d)
+        _dev_mx4(sdn, "w_sh_down", (d,), Fs)
+
+
+def forward_mx4(x, w_router, gu, dn, k, sgu=None, sdn=None, sh_gate=None, bias=None, out=None,
+                topk_idx=None, topk_w=None, ws=None, router=None):
+    """The whole layer with MXFP4 expert weights (gu, dn, sgu, sdn are
+    (codes, scales) pairs).  Returns (out float32 [T,d], topk_idx, topk_w)."""
+    T, d = x.shape
+    E, F, Fs = _mx4_dims(gu, sgu)
+    shape = Shape(d, E, k, F, Fs, x.dtype, router)
+    _dev(x, "x", torch.bfloat16), _dev(w_router, "w_router", x.dtype, (E, d))
+    _check_mx4_weights(d, E, F, Fs, gu, dn, sgu, sdn)
+    if Fs:
+        _dev(sh_gate, "sh_gate", x.dtype, (d,))
+    _dev(bias, "router_bias", torch.float32, (E,))
+    out = torch.empty((T, d), dtype=torch.float32, device=x.device) if out is None else out
+    topk_idx = torch.empty((T, k), dtype=torch.int32, device=x.device) if topk_idx is None else topk_idx
+    topk_w = torch.empty((T, k), dtype=torch.float32, device=x.device) if topk_w is None else topk_w
+    _dev(out, "out", torch.float32, (T, d)), _dev(topk_idx, "topk_idx", torch.int32, (T, k))
+    _dev(topk_w, "topk_w", torch.float32, (T, k))
+    ws = alloc_workspace(shape, T, x.device) if ws is None else ws
+    st = lib().moe_forward_mx4(ctypes.byref(shape.desc()), T, _ptr(x), _ptr(w_router), _ptr(bias),
+                               *_mx4_ptrs(gu, dn, sgu, sdn), _ptr(sh_gate), _ptr(out),
+                               _ptr(topk_idx), _ptr(topk_w), _ptr(ws), ws.numel(), _stream())
+    _check(st, "moe_forward_mx4")
+    return out, topk_idx, topk_w
+
+
+def experts_mx4(x, gu, dn, topk_idx, topk_w, sgu=None, sdn=None, sh_gate=None, out=None,
+                ws=None):
+    """Expert stage with MXFP4 expert weights and the routing given."""
+    T, d = x.shape
+    k = topk_idx.shape[1]
+    E, F, Fs = _mx4_dims(gu, sgu)
+    shape = Shape(d, E, k, F, Fs, x.dtype)
+    _dev(x, "x", torch.bfloat16)
+    _check_mx4_weights(d, E, F, Fs, gu, dn, sgu, sdn)
+    _dev(topk_idx, "topk_idx", torch.int32, (T, k)), _dev(topk_w, "topk_w", torch.float32, (T, k))
+    if Fs:
+        _dev(sh_gate, "sh_gate", x.dtype, (d,))
+    out = torch.empty((T, d), dtype=torch.float32, device=x.device) if out is None else out
+    _dev(out, "out", torch.float32, (T, d))
+    ws = alloc_workspace(shape, T, x.device) if ws is None else ws
+    st = lib().moe_experts_mx4(ctypes.byref(shape.desc()), T, _ptr(x),
+                               *_mx4_ptrs(gu, dn, sgu, sdn), _ptr(sh_gate), _ptr(topk_idx),
+                               _ptr(topk_w), _ptr(out), _ptr(ws), ws.numel(), _stream())
+    _check(st, "moe_experts_mx4")
+    return out
+
+
 class MoELayer:
     """Device-resident weights plus a workspace sized for up to ``max_tokens``
     tokens, so repeated calls allocate nothing but their outputs."""
@@ -278,7 +359,13 @@ class MoELayer:
                       w_sh_gate_up=w_sh_gate_up, w_sh_down=w_sh_down, sh_gate=sh_gate, bias=bias)
         self.k = k
         self.router = router
-        self.shape = shape_of(w_router, w_gate_up, k, w_sh_gate_up, router)
+        # MXFP4 expert weights come as (codes, scales) pairs
+        self.mx4 = isinstance(w_gate_up, tuple)
+        if self.mx4:
+            E, F, Fs = _mx4_dims(w_gate_up, w_sh_gate_up)
+            self.shape = Shape(w_router.shape[1], E, k, F, Fs, w_router.dtype, router)
+        else:
+            self.shape = shape_of(w_router, w_gate_up, k, w_sh_gate_up, router)
         self.max_tokens = max_tokens
         self.ws = alloc_workspace(self.shape, max_tokens, w_router.device)
 
@@ -286,6 +373,7 @@ class MoELayer:
         if x.shape[0] > self.max_tokens:
             raise ValueError("more tokens than the workspace was sized for")
         w = self.w
-        return forward(x, w["w_router"], w["w_gate_up"], w["w_down"], self.k, w["w_sh_gate_up"],
-                       w["w_sh_down"], w["sh_gate"], w["bias"], out, topk_idx, topk_w, self.ws,
-                       self.router)
+        fwd = forward_mx4 if self.mx4 else forward
+        return fwd(x, w["w_router"], w["w_gate_up"], w["w_down"], self.k, w["w_sh_gate_up"],
+                   w["w_sh_down"], w["sh_gate"], w["bias"], out, topk_idx, topk_w, self.ws,
+                   self.router)

@@ -144,7 +144,8 @@ struct TileInfo {
     bool shared;
 };
 
-__device__ __forceinline__ bool decode_tile(const DecodeArgs &a, TileInfo &ti) {
+template <class Args>
+__device__ __forceinline__ bool decode_tile(const Args &a, TileInfo &ti) {
     const int tile = blockIdx.x;
     if (tile >= a.tile_start[a.E + 1]) return false;
     ti.g = a.tile_group[tile];
@@ -278,6 +279,302 @@ __global__ __launch_bounds__(64 * DW) void decode_down_kernel(DecodeArgs a) {
     if (blockIdx.y * 32 * DW >= a.d) return;
     if (ti.nrows > 16) decode_down_body<2>(a, ti);
     else decode_down_body<1>(a, ti);
+}
+
+// ---------------------------------------------------------------------------
+// MXFP4 expert weights.  Same tiles, blocks and ping-pong pipeline; the
+// weights arrive as E2M1 codes (two per byte, even element in the low nibble)
+// with one E8M0 scale per 32 elements of a row, and are decoded exactly to
+// bf16 in registers by v_cvt_scalef32_pk_bf16_fp4.  That instruction uses
+// only the exponent field of its binary32 scale operand, so scale byte X is
+// passed as the bits X << 23 (2^(X-127) for every X < 255, 2^-127 included).
+//
+// A lane's 16-byte load is one whole 32-element block: in K group g (128
+// elements) lane (r, q) loads elements 128 g + 32 q .. + 31 of its weight
+// row, and MFMA step s of the group takes, in lane q, elements
+// 128 g + 32 q + 8 s .. + 7 of the weights and of the token row alike.  The
+// four q lanes of a step still cover 32 distinct k and the four steps cover
+// the group, so every dot product is the same sum; only the binary32
+// summation order inside the MFMAs differs from the bf16 kernels'.  A wave
+// owns NB4 blocks of 16 weight rows, so one group streams 4 KB of codes per
+// wave (the bf16 kernels stream 8 KB of weights per group over 2 blocks).
+
+constexpr int NB4 = 4;
+
+struct Mx4Args {
+    const uint16_t *x;
+    const uint8_t *wc, *ws;        // routed codes / scales: gate/up [E,2F,d/2] / [E,2F,d/32],
+                                   // down [E,d,F/2] / [E,d,F/32]
+    const uint8_t *wc_sh, *ws_sh;  // shared: [2Fs,d/2] / [2Fs,d/32], [d,Fs/2] / [d,Fs/32]
+    uint16_t *h, *h_sh;
+    float *out;
+    uint16_t *y;
+    const int32_t *perm, *counts, *offsets, *tile_start, *tile_group;
+    const float *topk_w, *gate;
+    int64_t T;
+    int d, E, k, F, Fs;
+};
+
+struct Mx4Group {
+    uint4 c[NB4];      // one 32-element block of codes per weight-row block
+    uint32_t s[NB4];   // its scale byte
+};
+
+__device__ __forceinline__ void mx4_load_b(Mx4Group &b, const uint8_t *const (&cp)[NB4],
+                                           const uint8_t *const (&sp)[NB4], int g) {
+#pragma unroll
+    for (int n = 0; n < NB4; ++n) {
+        b.c[n] = *reinterpret_cast<const uint4 *>(cp[n] + 64 * g);
+        b.s[n] = sp[n][4 * g];
+    }
+}
+
+template <int HALVES>
+__device__ __forceinline__ void mx4_load_a(Frag (&a)[HALVES], const uint16_t *const (&ap)[HALVES],
+                                           int g) {
+#pragma unroll
+    for (int h = 0; h < HALVES; ++h)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            a[h].v[s] = *reinterpret_cast<const uint4 *>(ap[h] + 128 * g + 8 * s);
+}
+
+// Eight E2M1 codes (one dword, element 2j in the low nibble of byte j) times
+// 2^(X-127), exactly, as bf16 in element order.
+__device__ __forceinline__ bf16x8 mx4_decode8(uint32_t w, float scale) {
+    uint4 r;
+    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+    r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+    r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+    return __builtin_bit_cast(bf16x8, r);
+}
+
+template <int HALVES>
+__device__ __forceinline__ void mx4_mfma_group(f32x4 (&acc)[HALVES][NB4], const Mx4Group &b,
+                                               const Frag (&a)[HALVES]) {
+    float sc[NB4];
+#pragma unroll
+    for (int n = 0; n < NB4; ++n) sc[n] = __uint_as_float(b.s[n] << 23);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int n = 0; n < NB4; ++n) {
+            const uint32_t w = s == 0 ? b.c[n].x : s == 1 ? b.c[n].y : s == 2 ? b.c[n].z : b.c[n].w;
+            const bf16x8 wb = mx4_decode8(w, sc[n]);
+#pragma unroll
+            for (int h = 0; h < HALVES; ++h)
+                acc[h][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, a[h].v[s]), wb, acc[h][n], 0, 0, 0);
+        }
+}
+
+// K (a multiple of 128) streamed with group 0 already loaded into b0 / a0;
+// two groups in flight, branch-free steady state, tail peeled (as stream_k_from).
+template <int HALVES>
+__device__ __forceinline__ void mx4_stream(Mx4Group &b0, Frag (&a0)[HALVES],
+                                           const uint8_t *const (&cp)[NB4],
+                                           const uint8_t *const (&sp)[NB4],
+                                           const uint16_t *const (&ap)[HALVES], int K,
+                                           f32x4 (&acc)[HALVES][NB4]) {
+    Mx4Group b1;
+    Frag a1[HALVES];
+    const int ng = K / KG;
+    int g = 0;
+    for (; g + 2 < ng; g += 2) {
+        mx4_load_b(b1, cp, sp, g + 1);
+        mx4_load_a<HALVES>(a1, ap, g + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mx4_mfma_group<HALVES>(acc, b0, a0);
+        __builtin_amdgcn_sched_barrier(0);
+        mx4_load_b(b0, cp, sp, g + 2);
+        mx4_load_a<HALVES>(a0, ap, g + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        mx4_mfma_group<HALVES>(acc, b1, a1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (g + 1 < ng) {
+        mx4_load_b(b1, cp, sp, g + 1);
+        mx4_load_a<HALVES>(a1, ap, g + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mx4_mfma_group<HALVES>(acc, b0, a0);
+        __builtin_amdgcn_sched_barrier(0);
+        mx4_mfma_group<HALVES>(acc, b1, a1);
+    } else {
+        mx4_mfma_group<HALVES>(acc, b0, a0);
+    }
+}
+
+// gate/up: wave w owns gate columns c0 .. c0 + 31 (two 16-row blocks) and the
+// matching up columns; grid.y walks 32 DW-column slabs of the expert width.
+template <int HALVES>
+__device__ void mx4_gateup_body(const Mx4Args &a, const TileInfo &ti) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int Fg = ti.shared ? a.Fs : a.F;
+    const int c0 = blockIdx.y * 32 * DW + wave * 32;
+    const int rl = lane & 15, q = lane >> 4;
+    int tok[HALVES];
+#pragma unroll
+    for (int h = 0; h < HALVES; ++h) {
+        const int r = min(16 * h + rl, ti.nrows - 1);  // padding rows repeat the last row
+        tok[h] = ti.shared ? ti.row0 + r : a.perm[ti.row0 + r];
+    }
+    const int64_t row_base = ti.shared ? 0 : (int64_t)ti.g * 2 * a.F;
+    const uint8_t *C = ti.shared ? a.wc_sh : a.wc;
+    const uint8_t *S = ti.shared ? a.ws_sh : a.ws;
+    const uint8_t *cp[NB4], *sp[NB4];
+#pragma unroll
+    for (int n = 0; n < NB4; ++n) {
+        const int64_t r = row_base + (n < 2 ? c0 + 16 * n : Fg + c0 + 16 * (n - 2)) + rl;
+        cp[n] = C + r * (a.d / 2) + 16 * q;
+        sp[n] = S + r * (a.d / 32) + q;
+    }
+    Mx4Group b0;
+    mx4_load_b(b0, cp, sp, 0);
+    const uint16_t *ap[HALVES];
+#pragma unroll
+    for (int h = 0; h < HALVES; ++h)
+        ap[h] = a.x + (int64_t)(ti.shared ? tok[h] : tok[h] / a.k) * a.d + 32 * q;
+    Frag a0[HALVES];
+    mx4_load_a<HALVES>(a0, ap, 0);
+    f32x4 acc[HALVES][NB4];
+#pragma unroll
+    for (int h = 0; h < HALVES; ++h)
+#pragma unroll
+        for (int n = 0; n < NB4; ++n) acc[h][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mx4_stream<HALVES>(b0, a0, cp, sp, ap, a.d, acc);
+    uint16_t *H = ti.shared ? a.h_sh : a.h;
+    // 16x16 accumulator: lane holds column lane % 16, rows 4 (lane / 16) + i.
+#pragma unroll
+    for (int h = 0; h < HALVES; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * h + 4 * q + i;
+            if (row < ti.nrows)
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+                    H[(int64_t)(ti.row0 + row) * Fg + c0 + 16 * n + rl] =
+                        f32_to_bf16_rne(silu_mul(acc[h][n][i], acc[h][n + 2][i]));
+        }
+}
+
+__global__ __launch_bounds__(64 * DW) void decode_gateup_mx4_kernel(Mx4Args a) {
+    TileInfo ti;
+    if (!decode_tile(a, ti)) return;
+    const int Fg = ti.shared ? a.Fs : a.F;
+    if (blockIdx.y * 32 * DW >= Fg) return;
+    if (ti.nrows > 16) mx4_gateup_body<2>(a, ti);
+    else mx4_gateup_body<1>(a, ti);
+}
+
+// down: wave w owns output columns c0 .. c0 + 63 (four 16-row blocks of
+// W_dn); grid.y walks 64 DW-column slabs of d.  The epilogue's lookups (pair
+// ids, then weights) are issued before the stream, as in decode_down_body.
+template <int HALVES>
+__device__ void mx4_down_body(const Mx4Args &a, const TileInfo &ti) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int Fg = ti.shared ? a.Fs : a.F;
+    const int c0 = blockIdx.y * 64 * DW + wave * 64;
+    const int rl = lane & 15, q = lane >> 4;
+    int src[HALVES][4];
+#pragma unroll
+    for (int h = 0; h < HALVES; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = min(16 * h + 4 * q + i, ti.nrows - 1);
+            src[h][i] = ti.shared ? ti.row0 + r : a.perm[ti.row0 + r];
+        }
+    const int64_t row_base = ti.shared ? 0 : (int64_t)ti.g * a.d;
+    const uint8_t *C = ti.shared ? a.wc_sh : a.wc;
+    const uint8_t *S = ti.shared ? a.ws_sh : a.ws;
+    const uint8_t *cp[NB4], *sp[NB4];
+#pragma unroll
+    for (int n = 0; n < NB4; ++n) {
+        const int64_t r = row_base + min(c0 + 16 * n + rl, a.d - 1);
+        cp[n] = C + r * (Fg / 2) + 16 * q;
+        sp[n] = S + r * (Fg / 32) + q;
+    }
+    Mx4Group b0;
+    mx4_load_b(b0, cp, sp, 0);
+    const uint16_t *H = ti.shared ? a.h_sh : a.h;
+    const uint16_t *ap[HALVES];
+#pragma unroll
+    for (int h = 0; h < HALVES; ++h)
+        ap[h] = H + (int64_t)(ti.row0 + min(16 * h + rl, ti.nrows - 1)) * Fg + 32 * q;
+    Frag a0[HALVES];
+    mx4_load_a<HALVES>(a0, ap, 0);
+    f32x4 acc[HALVES][NB4];
+#pragma unroll
+    for (int h = 0; h < HALVES; ++h)
+#pragma unroll
+        for (int n = 0; n < NB4; ++n) acc[h][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mx4_stream<HALVES>(b0, a0, cp, sp, ap, Fg, acc);
+    float wr[HALVES][4];
+#pragma unroll
+    for (int h = 0; h < HALVES; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wr[h][i] = ti.shared ? a.gate[src[h][i]] : a.topk_w[src[h][i]];
+#pragma unroll
+    for (int h = 0; h < HALVES; ++h)
+#pragma unroll
+        for (int n = 0; n < NB4; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * h + 4 * q + i;
+                const int col = c0 + 16 * n + rl;
+                if (row < ti.nrows && col < a.d) {
+                    const float v = wr[h][i] * acc[h][n][i];
+                    if (ti.shared) a.out[(int64_t)(ti.row0 + row) * a.d + col] = v;
+                    else a.y[(int64_t)(ti.row0 + row) * a.d + col] = f32_to_bf16_rne(v);
+                }
+            }
+}
+
+__global__ __launch_bounds__(64 * DW) void decode_down_mx4_kernel(Mx4Args a) {
+    TileInfo ti;
+    if (!decode_tile(a, ti)) return;
+    if (blockIdx.y * 64 * DW >= a.d) return;
+    if (ti.nrows > 16) mx4_down_body<2>(a, ti);
+    else mx4_down_body<1>(a, ti);
+}
+
+hipError_t launch_experts_decode_mx4(const Problem &p, hipStream_t s,
+                                     const std::function<void(int)> &mark) {
+    Mx4Args a;
+    a.x = static_cast<const uint16_t *>(p.x);
+    a.h = static_cast<uint16_t *>(p.h);
+    a.h_sh = static_cast<uint16_t *>(p.h_shared);
+    a.out = p.out;
+    a.y = static_cast<uint16_t *>(p.y);
+    a.perm = p.perm;
+    a.counts = p.counts;
+    a.offsets = p.offsets;
+    a.tile_start = p.tile_start;
+    a.tile_group = p.tile_group;
+    a.topk_w = p.topk_w;
+    a.gate = p.gate;
+    a.T = p.T;
+    a.d = p.d;
+    a.E = p.E;
+    a.k = p.k;
+    a.F = p.F;
+    a.Fs = p.Fs;
+    const int fmax = p.F > p.Fs ? p.F : p.Fs;
+    a.wc = static_cast<const uint8_t *>(p.w_gate_up);
+    a.ws = p.sc_gate_up;
+    a.wc_sh = static_cast<const uint8_t *>(p.w_sh_gate_up);
+    a.ws_sh = p.sc_sh_gate_up;
+    hipLaunchKernelGGL(decode_gateup_mx4_kernel, dim3(p.max_tiles, (fmax + 32 * DW - 1) / (32 * DW)),
+                       dim3(64 * DW), 0, s, a);
+    mark(3);
+    a.wc = static_cast<const uint8_t *>(p.w_down);
+    a.ws = p.sc_down;
+    a.wc_sh = static_cast<const uint8_t *>(p.w_sh_down);
+    a.ws_sh = p.sc_sh_down;
+    hipLaunchKernelGGL(decode_down_mx4_kernel, dim3(p.max_tiles, (p.d + 64 * DW - 1) / (64 * DW)),
+                       dim3(64 * DW), 0, s, a);
+    mark(4);
+    return hipGetLastError();
 }
 
 hipError_t launch_experts_decode(const Problem &p, hipStream_t s,

@@ -173,7 +173,7 @@ bool use_dma_path(const moe::Problem &p) {
 
 // Stages 2..5 of a call: permutation, gate/up, down, combine.
 moe_status run_experts(moe::Problem p, hipStream_t s) {
-    const bool decode = use_decode_path(p);
+    const bool decode = p.mx4 || use_decode_path(p);
     const bool dma = !decode && use_dma_path(p);
     // 256-row tiles once experts average 192+ rows
     const bool big = dma && p.T * p.k >= (int64_t)192 * p.E;
@@ -184,6 +184,7 @@ moe_status run_experts(moe::Problem p, hipStream_t s) {
     auto mark = [&](int i) { mark_stage(i, s); };
     if (err == hipSuccess)
         err = !p.bf16  ? moe::launch_experts_f32(p, s, mark)
+              : p.mx4  ? moe::launch_experts_decode_mx4(p, s, mark)
               : decode ? moe::launch_experts_decode(p, s, mark)
               : dma    ? moe::launch_experts_dma(p, bm, s, mark)
                        : moe::launch_experts_bf16(p, s, mark);
@@ -191,6 +192,16 @@ moe_status run_experts(moe::Problem p, hipStream_t s) {
     mark_stage(5, s);
     g_n_stage_events = 0;
     return hip_status(err);
+}
+
+// MXFP4 expert weights: bf16 activations, 128-multiples (the decode
+// kernels' tiling) and the weight-streaming regime (T*k <= 16 E).
+moe_status check_mx4(const moe_desc *desc, int64_t T) {
+    if (desc->dtype != MOE_BF16 || desc->d_model % 128 || desc->d_expert % 128 ||
+        desc->d_shared % 128)
+        return MOE_ERR_UNSUPPORTED;
+    if (T * desc->top_k > (int64_t)16 * desc->n_experts) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
 }
 
 }  // namespace
@@ -287,6 +298,103 @@ moe_status moe_experts(const moe_desc *desc, int64_t T, const void *x, const voi
     p.w_down = w_down;
     p.w_sh_gate_up = w_sh_gate_up;
     p.w_sh_down = w_sh_down;
+    p.sh_gate = sh_gate;
+    p.out = out;
+    p.topk_idx = const_cast<int32_t *>(topk_idx);
+    p.topk_w = const_cast<float *>(topk_w);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    mark_stage(0, s);
+    if (p.Fs > 0) {
+        st = hip_status(moe::launch_shared_gate(p, s));
+        if (st != MOE_OK) {
+            g_n_stage_events = 0;
+            return st;
+        }
+    }
+    mark_stage(1, s);
+    return run_experts(p, s);
+}
+
+moe_status moe_forward_mx4(const moe_desc *desc, int64_t T, const void *x, const void *w_router,
+                           const float *router_bias, const uint8_t *gate_up_codes,
+                           const uint8_t *gate_up_scales, const uint8_t *down_codes,
+                           const uint8_t *down_scales, const uint8_t *sh_gate_up_codes,
+                           const uint8_t *sh_gate_up_scales, const uint8_t *sh_down_codes,
+                           const uint8_t *sh_down_scales, const void *sh_gate, float *out,
+                           int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+                           void *stream) {
+    moe_status st = check_common(desc, T,
+                                 {x, w_router, gate_up_codes, gate_up_scales, down_codes,
+                                  down_scales, out, topk_idx, topk_w},
+                                 {router_bias, sh_gate_up_codes, sh_gate_up_scales, sh_down_codes,
+                                  sh_down_scales, sh_gate},
+                                 ws, ws_bytes);
+    if (st != MOE_OK) return st;
+    st = check_mx4(desc, T);
+    if (st != MOE_OK || T == 0) return st;
+    if (desc->d_shared > 0 && (!sh_gate_up_codes || !sh_gate_up_scales || !sh_down_codes ||
+                               !sh_down_scales || !sh_gate))
+        return MOE_ERR_INVALID_ARG;
+    const Plan pl = make_plan(*desc, T);
+    moe::Problem p = make_problem(*desc, T, pl, ws);
+    p.x = x;
+    p.w_router = w_router;
+    p.router_bias = router_bias;
+    p.mx4 = true;
+    p.w_gate_up = gate_up_codes;
+    p.sc_gate_up = gate_up_scales;
+    p.w_down = down_codes;
+    p.sc_down = down_scales;
+    p.w_sh_gate_up = sh_gate_up_codes;
+    p.sc_sh_gate_up = sh_gate_up_scales;
+    p.w_sh_down = sh_down_codes;
+    p.sc_sh_down = sh_down_scales;
+    p.sh_gate = desc->d_shared > 0 ? sh_gate : nullptr;
+    p.out = out;
+    p.topk_idx = topk_idx;
+    p.topk_w = topk_w;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    mark_stage(0, s);
+    st = hip_status(moe::launch_router(p, nullptr, s));
+    mark_stage(1, s);
+    if (st != MOE_OK) {
+        g_n_stage_events = 0;
+        return st;
+    }
+    return run_experts(p, s);
+}
+
+moe_status moe_experts_mx4(const moe_desc *desc, int64_t T, const void *x,
+                           const uint8_t *gate_up_codes, const uint8_t *gate_up_scales,
+                           const uint8_t *down_codes, const uint8_t *down_scales,
+                           const uint8_t *sh_gate_up_codes, const uint8_t *sh_gate_up_scales,
+                           const uint8_t *sh_down_codes, const uint8_t *sh_down_scales,
+                           const void *sh_gate, const int32_t *topk_idx, const float *topk_w,
+                           float *out, void *ws, size_t ws_bytes, void *stream) {
+    moe_status st = check_common(desc, T,
+                                 {x, gate_up_codes, gate_up_scales, down_codes, down_scales,
+                                  topk_idx, topk_w, out},
+                                 {sh_gate_up_codes, sh_gate_up_scales, sh_down_codes,
+                                  sh_down_scales, sh_gate},
+                                 ws, ws_bytes);
+    if (st != MOE_OK) return st;
+    st = check_mx4(desc, T);
+    if (st != MOE_OK || T == 0) return st;
+    if (desc->d_shared > 0 && (!sh_gate_up_codes || !sh_gate_up_scales || !sh_down_codes ||
+                               !sh_down_scales || !sh_gate))
+        return MOE_ERR_INVALID_ARG;
+    const Plan pl = make_plan(*desc, T);
+    moe::Problem p = make_problem(*desc, T, pl, ws);
+    p.x = x;
+    p.mx4 = true;
+    p.w_gate_up = gate_up_codes;
+    p.sc_gate_up = gate_up_scales;
+    p.w_down = down_codes;
+    p.sc_down = down_scales;
+    p.w_sh_gate_up = sh_gate_up_codes;
+    p.sc_sh_gate_up = sh_gate_up_scales;
+    p.w_sh_down = sh_down_codes;
+    p.sc_sh_down = sh_down_scales;
     p.sh_gate = sh_gate;
     p.out = out;
     p.topk_idx = const_cast<int32_t *>(topk_idx);

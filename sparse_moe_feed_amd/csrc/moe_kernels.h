@@ -40,6 +40,11 @@ struct Problem {
     void *h;            // [T*k, F]
     void *h_shared;     // [T, Fs]
     int nblk;           // ceil(T / kCountBlock)
+    // MXFP4 expert weights: w_gate_up, w_down, w_sh_gate_up, w_sh_down then
+    // hold the packed E2M1 codes and these the E8M0 scales (one per 32
+    // elements of a row)
+    bool mx4;
+    const uint8_t *sc_gate_up, *sc_down, *sc_sh_gate_up, *sc_sh_down;
 };
 
 constexpr int kCountBlock = 256;     // tokens per histogram block
@@ -99,5 +104,8 @@ hipError_t launch_experts_f32(const Problem &p, hipStream_t s, const std::functi
 // Weight-streaming expert stage for few tokens per expert (tiles of kDecodeBM).
 hipError_t launch_experts_decode(const Problem &p, hipStream_t s,
                                  const std::function<void(int)> &mark);
+// The same with MXFP4 expert weights (p.mx4), decoded to bf16 in registers.
+hipError_t launch_experts_decode_mx4(const Problem &p, hipStream_t s,
+                                     const std::function<void(int)> &mark);
 
 }  // namespace moe

@@ -22,7 +22,7 @@ def L():
 def declared_functions():
     text = open(os.path.join(ROOT, "include", "moe.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text))
+    return set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text))
 
 
 def test_exports_every_declared_symbol(L):
@@ -127,6 +127,62 @@ def test_route_and_experts_validate(L):
                          None, v(FAKE), v(FAKE), v(FAKE), 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_experts(ctypes.byref(D), 8, v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE),
                          v(FAKE), v(FAKE), v(FAKE), v(FAKE), 16, None) == moe.MOE_ERR_WORKSPACE
+
+
+def call_forward_mx4(L, D, T, ptrs=None, ws=FAKE, ws_bytes=1 << 40):
+    p = dict(x=FAKE, wr=FAKE, b=None, guc=FAKE, gus=FAKE, dnc=FAKE, dns=FAKE, sguc=FAKE,
+             sgus=FAKE, sdnc=FAKE, sdns=FAKE, g=FAKE, out=FAKE, idx=FAKE, w=FAKE)
+    p.update(ptrs or {})
+    v = lambda a: None if a is None else ctypes.c_void_p(a)
+    return L.moe_forward_mx4(ctypes.byref(D), T, v(p["x"]), v(p["wr"]), v(p["b"]), v(p["guc"]),
+                             v(p["gus"]), v(p["dnc"]), v(p["dns"]), v(p["sguc"]), v(p["sgus"]),
+                             v(p["sdnc"]), v(p["sdns"]), v(p["g"]), v(p["out"]), v(p["idx"]),
+                             v(p["w"]), v(ws), ws_bytes, None)
+
+
+def mx4_desc(**kw):
+    base = dict(d=256, E=16, k=4, F=128, Fs=128)
+    base.update(kw)
+    return desc(**base)
+
+
+@pytest.mark.parametrize("missing", ["guc", "gus", "dnc", "dns", "sguc", "sgus", "sdnc", "sdns",
+                                     "g", "x", "out"])
+def test_mx4_null_required_pointer(L, missing):
+    assert call_forward_mx4(L, mx4_desc(), 8, {missing: None}) == moe.MOE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad", [dict(dtype=moe.MOE_F32), dict(Fs=64), dict(F=192),
+                                 dict(d=320)])
+def test_mx4_unsupported_shapes(L, bad):
+    """MXFP4 layers need bf16 activations and 128-multiples, at any T."""
+    assert call_forward_mx4(L, mx4_desc(**bad), 8) == moe.MOE_ERR_UNSUPPORTED
+    assert call_forward_mx4(L, mx4_desc(**bad), 0, ws=None, ws_bytes=0) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_mx4_only_in_weight_streaming_regime(L):
+    """T*k above 16 E (many tokens per expert) is not supported for MXFP4."""
+    D = mx4_desc()                                   # 16 E = 256 -> T <= 64 at k = 4
+    assert call_forward_mx4(L, D, 65) == moe.MOE_ERR_UNSUPPORTED
+    assert call_forward_mx4(L, D, 64, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
+
+
+def test_mx4_misaligned_codes_and_noop(L):
+    assert call_forward_mx4(L, mx4_desc(), 8, {"guc": FAKE + 8}) == moe.MOE_ERR_INVALID_ARG
+    assert call_forward_mx4(L, mx4_desc(), 0, ws=None, ws_bytes=0) == moe.MOE_OK
+    D = mx4_desc(Fs=0)
+    assert call_forward_mx4(L, D, 8, {"sguc": None, "sgus": None, "sdnc": None, "sdns": None,
+                                      "g": None}, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
+
+
+def test_mx4_experts_validate(L):
+    v = ctypes.c_void_p
+    D = mx4_desc()
+    args = [v(FAKE)] * 8
+    assert L.moe_experts_mx4(ctypes.byref(D), 8, v(FAKE), *args, v(FAKE), None, v(FAKE), v(FAKE),
+                             v(FAKE), 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_experts_mx4(ctypes.byref(D), 100, v(FAKE), *args, v(FAKE), v(FAKE), v(FAKE),
+                             v(FAKE), v(FAKE), 1 << 40, None) == moe.MOE_ERR_UNSUPPORTED
 
 
 def test_status_strings(L):

@@ -1,0 +1,122 @@
+"""Parity of the HIP path with MXFP4 expert weights (moe_forward_mx4 /
+moe_experts_mx4, through the C ABI) against the CPU oracle's MXFP4 layer.
+
+Bars as for the bf16 layer: topk_idx bit for bit, topk_w within 1e-5, out
+within 2e-2 x RMS(oracle out).  The decoded weights are exact in bf16, so the
+only rounding the GPU adds over the oracle is the bf16 h and y and the
+binary32 accumulation.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_moe_feed_amd as moe
+import workloads as W
+from gpu_util import W_TOL, announce, assert_out, to_dev
+
+pytestmark = pytest.mark.gpu
+
+MX = ("gu", "dn", "sgu", "sdn")
+
+
+def mx_dev(t):
+    return None if t is None else (to_dev(t[0]), to_dev(t[1]))
+
+
+def small_mx4(T, d, E, k, F, Fs, seed):
+    inp = W.make_layer_mx4(d, E, F, Fs, seed)
+    inp["x"] = W.make_x(T, d, "bf16", seed + 1)
+    inp["bias"] = None
+    return inp
+
+
+def gpu_forward_mx4(inp, k):
+    out, idx, w = moe.forward_mx4(to_dev(inp["x"]), to_dev(inp["w_router"]),
+                                  *[mx_dev(inp[n]) for n in MX[:2]], k,
+                                  *[mx_dev(inp[n]) for n in MX[2:]], to_dev(inp["sh_gate"]),
+                                  bias=to_dev(inp.get("bias")))
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+
+
+def oracle_forward_mx4(inp, k):
+    return oracle.forward_mx4(inp["x"], inp["w_router"], inp["gu"], inp["dn"], k, inp["sgu"],
+                              inp["sdn"], inp["sh_gate"], bias=inp.get("bias"))
+
+
+def check_mx4(inp, k, name):
+    announce(name)
+    out, idx, w = gpu_forward_mx4(inp, k)
+    ref_out, ref_idx, ref_w, _ = oracle_forward_mx4(inp, k)
+    assert np.array_equal(idx, ref_idx), f"{name}: topk_idx differs"
+    assert np.abs(w - ref_w).max() <= W_TOL
+    return assert_out(out, ref_out)
+
+
+@pytest.mark.parametrize("T,d,E,k,F,Fs", [
+    (8, 256, 16, 4, 128, 128),      # a few rows per expert
+    (40, 384, 32, 6, 256, 128),     # d % 256 = 128: odd number of K groups
+    (7, 512, 64, 3, 128, 0),        # no shared expert
+    (1, 256, 8, 2, 128, 128),       # one token
+    (64, 256, 16, 4, 384, 256),     # T k = 16 E (edge of the streaming regime)
+])
+def test_small_mx4_layers(T, d, E, k, F, Fs):
+    inp = small_mx4(T, d, E, k, F, Fs, seed=T + E + 40)
+    check_mx4(inp, k, f"mxfp4 T={T} d={d} E={E} k={k} F={F} Fs={Fs}")
+
+
+def test_mx4_bias_sends_every_token_to_one_expert():
+    """60 tokens all pick expert 5 first: a group of two 32-row tiles (the
+    two-half MFMA path) beside experts with one row."""
+    T, d, E, k, F = 60, 256, 16, 2, 128
+    inp = small_mx4(T, d, E, k, F, F, seed=81)
+    inp["bias"] = np.zeros(E, np.float32)
+    inp["bias"][5] = 100.0
+    check_mx4(inp, k, "mxfp4 bias -> expert 5")
+
+
+def test_mx4_experts_entry_with_given_routing():
+    T, d, E, k, F, Fs = 30, 256, 32, 5, 128, 128
+    inp = small_mx4(T, d, E, k, F, Fs, seed=12)
+    rng = np.random.default_rng(4)
+    idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    announce("moe_experts_mx4 given routing")
+    out = moe.experts_mx4(to_dev(inp["x"]), mx_dev(inp["gu"]), mx_dev(inp["dn"]), to_dev(idx),
+                          to_dev(w), mx_dev(inp["sgu"]), mx_dev(inp["sdn"]), to_dev(inp["sh_gate"]))
+    torch.cuda.synchronize()
+    ref = oracle.experts_mx4(inp["x"], inp["gu"], inp["dn"], idx, w.astype(np.float64),
+                             inp["sgu"], inp["sdn"], inp["sh_gate"])
+    assert_out(out.cpu().numpy(), ref)
+
+
+def test_mx4_deterministic_and_unsupported_regime():
+    T, d, E, k = 24, 256, 16, 4
+    inp = small_mx4(T, d, E, k, 128, 128, seed=55)
+    announce("mxfp4 determinism")
+    out1, idx1, _ = gpu_forward_mx4(inp, k)
+    out2, idx2, _ = gpu_forward_mx4(inp, k)
+    assert np.array_equal(idx1, idx2) and np.array_equal(out1, out2)
+    big = small_mx4(65, d, E, k, 128, 128, seed=56)     # T k > 16 E
+    with pytest.raises(moe.MoEError) as e:
+        gpu_forward_mx4(big, k)
+    assert e.value.status == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_mx4_zero_tokens():
+    inp = small_mx4(0, 256, 8, 2, 128, 128, seed=2)
+    announce("mxfp4 T=0")
+    out, idx, _ = gpu_forward_mx4(inp, 2)
+    assert out.shape == (0, 256) and idx.shape == (0, 2)
+
+
+def test_full_config_mx4():
+    """Pages' shapes with MXFP4 expert weights (decode, T=32): every token's
+    topk_idx bit-exact and out of every token against the oracle."""
+    cfg = W.CONFIGS[6]
+    lay = W.layer_for(cfg)
+    x = W.make_x(cfg.T, cfg.d, cfg.dtype, cfg.seed_x)
+    inp = dict(lay, x=x, bias=None)
+    r = check_mx4(inp, cfg.k, f"{cfg.name}: all {cfg.T} tokens")
+    announce(f"{cfg.name}: max|err|/rms = {r:.3e}")
