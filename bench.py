@@ -12,7 +12,11 @@ prefill-shaped layer (T=4096) is reported inside the same line under "also".
 recorded on the library's stream at its stage boundaries during the timed
 loop.  `cpu_baseline` times the CPU oracle on the host cores.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+`--config 6` measures the same decode layer with MXFP4 expert weights
+(moe_forward_mx4); its algorithmic weight bytes are 17/32 byte per element
+(a 4-bit code plus one scale byte per 32 elements).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C]
 """
 from __future__ import annotations
 
@@ -58,9 +62,10 @@ def algorithmic(cfg, U: int):
     stages: distinct routed experts touched (U), the shared expert, router,
     gate vector, x, out (fp32), topk_idx and topk_w."""
     T, d, E, k, F, Fs = cfg.T, cfg.d, cfg.E, cfg.k, cfg.F, cfg.Fs
-    b = 2
-    gu_w = U * 2 * F * d * b + 2 * Fs * d * b
-    dn_w = U * d * F * b + d * Fs * b
+    b = 2                                              # bf16 activations, router
+    bw = 17 / 32 if cfg.dtype == "mxfp4" else b        # bytes per expert weight
+    gu_w = int(U * 2 * F * d * bw + 2 * Fs * d * bw)
+    dn_w = int(U * d * F * bw + d * Fs * bw)
     call_bytes = gu_w + dn_w + E * d * b + d * b + T * d * b + T * d * 4 + T * k * 8
     flops_gu = 2 * T * k * 2 * F * d + 2 * T * 2 * Fs * d
     flops_dn = 2 * T * k * F * d + 2 * T * Fs * d
@@ -68,7 +73,7 @@ def algorithmic(cfg, U: int):
     return dict(call_bytes=call_bytes, call_flops=call_flops,
                 gate_up_bytes=gu_w + T * d * b + (T * k * F + T * Fs) * b,
                 gate_up_flops=flops_gu,
-                down_bytes=dn_w + (T * k * F + T * Fs) * b + T * k * d * 4 + T * d * 4,
+                down_bytes=dn_w + (T * k * F + T * Fs) * b + T * k * d * b + T * d * 4,
                 down_flops=flops_dn)
 
 
@@ -147,11 +152,17 @@ def cpu_baseline(cfg, layer_np, seconds):
 
     x = W.make_x(cfg.T, cfg.d, cfg.dtype, cfg.seed_x)
     bias = W.make_bias(cfg)
-    args = (x, layer_np["w_router"], layer_np["w_gate_up"], layer_np["w_down"], cfg.k,
-            layer_np["w_sh_gate_up"], layer_np["w_sh_down"], layer_np["sh_gate"])
+    if cfg.dtype == "mxfp4":
+        fwd = oracle.forward_mx4
+        args = (x, layer_np["w_router"], layer_np["gu"], layer_np["dn"], cfg.k, layer_np["sgu"],
+                layer_np["sdn"], layer_np["sh_gate"])
+    else:
+        fwd = oracle.forward
+        args = (x, layer_np["w_router"], layer_np["w_gate_up"], layer_np["w_down"], cfg.k,
+                layer_np["w_sh_gate_up"], layer_np["w_sh_down"], layer_np["sh_gate"])
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.forward(*args, bias=bias)
+        fwd(*args, bias=bias)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -159,6 +170,27 @@ def cpu_baseline(cfg, layer_np, seconds):
     return dict(value=round(reps * cfg.T / el, 2), unit="tokens/s", cores=oracle.threads(),
                 kind="oracle",
                 sample=f"all {cfg.T} tokens of {cfg.name}, {reps} full passes in {el:.1f} s")
+
+
+def device_layer(cfg, layer_np):
+    """The layer's weights on the GPU: bf16 tensors, or (codes, scales) uint8
+    pairs for MXFP4 expert weights."""
+    import numpy as np
+    import torch
+
+    bf = lambda a: None if a is None else torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    if cfg.dtype == "mxfp4":
+        u8 = lambda t: None if t is None else (torch.from_numpy(t[0]).cuda(),
+                                               torch.from_numpy(t[1]).cuda())
+        return dict(w_router=bf(layer_np["w_router"]), sh_gate=bf(layer_np["sh_gate"]),
+                    w_gate_up=u8(layer_np["gu"]), w_down=u8(layer_np["dn"]),
+                    w_sh_gate_up=u8(layer_np["sgu"]), w_sh_down=u8(layer_np["sdn"]))
+    return {n: bf(layer_np[n]) for n in ("w_router", "w_gate_up", "w_down", "w_sh_gate_up",
+                                         "w_sh_down", "sh_gate")}
+
+
+def layer_key(cfg):
+    return (cfg.d, cfg.E, cfg.F, cfg.Fs, cfg.dtype, cfg.seed_w)
 
 
 def main():
@@ -196,14 +228,16 @@ def main():
 
     cfg = W.CONFIGS[args.config]
     layer_np = W.layer_for(cfg)
-    to = lambda a: None if a is None else torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
-    dev_layer = {n: to(layer_np[n]) for n in ("w_router", "w_gate_up", "w_down", "w_sh_gate_up",
-                                              "w_sh_down", "sh_gate")}
+    dev_layer = device_layer(cfg, layer_np)
     r = measure(cfg, dev_layer, args.steps, args.warmup)
     roof, layer = roofline_of(cfg, r, cfg.name)
     also = {}
     for c in [int(v) for v in args.also.split(",") if v]:
         c_cfg = W.CONFIGS[c]
+        if layer_key(c_cfg) != layer_key(cfg):
+            print(f"bench.py: --also {c} skipped ({c_cfg.name} uses another layer)",
+                  file=sys.stderr)
+            continue
         rc = measure(c_cfg, dev_layer, max(3, args.steps // 2), args.warmup)
         rroof, rlayer = roofline_of(c_cfg, rc, c_cfg.name)
         also[c_cfg.name] = dict(value=round(c_cfg.T / (rc["ms"] * 1e-3), 1), unit="tokens/s",
@@ -226,7 +260,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic: seeded N(0,1) tokens, N(0,0.02^2) weights (random init, no checkpoint)",
         "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d, "experts": cfg.E,
-                   "top_k": cfg.k, "d_expert": cfg.F, "d_shared": cfg.Fs, "router_bias": cfg.bias},
+                   "top_k": cfg.k, "d_expert": cfg.F, "d_shared": cfg.Fs, "router_bias": cfg.bias,
+                   "expert_weights": "mxfp4" if cfg.dtype == "mxfp4" else "bf16"},
         "roofline": roof,
         "layer": layer,
         "stage_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},
