@@ -164,43 +164,65 @@ moe_status moe_experts(const moe_desc *desc, int64_t T, const void *x,
  * gate/up matrices, F or Fs for the down matrices) shares one E8M0 scale
  * byte X, worth 2^(X-127); each element is an FP4 E2M1 code (sign bit 3,
  * exponent bits 2..1 with bias 1, mantissa bit 0: magnitudes 0, 0.5, 1, 1.5,
- * 2, 3, 4, 6).  A tensor of logical shape [rows, K] is two arrays:
- *   codes   uint8 [rows, K/2]   element 2i in bits 3..0 of byte i, element
- *                                2i+1 in bits 7..4 (16-byte aligned)
- *   scales  uint8 [rows, K/32]  the scale of elements 32b .. 32b+31 of a row
- * so w_gate_up is codes [E,2F,d/2] + scales [E,2F,d/32], w_down codes
- * [E,d,F/2] + scales [E,d,F/32], w_sh_gate_up [2Fs,d/2] + [2Fs,d/32] and
- * w_sh_down [d,Fs/2] + [d,Fs/32].  Scale byte 255 (NaN) gives unspecified
- * results.  Every element is decoded exactly (to bfloat16) and the layer is
- * then the MOE_BF16 layer on the decoded weights: x, w_router and sh_gate
+ * 2, 3, 4, 6).  Every element is decoded exactly (to bfloat16) and the layer
+ * is then the MOE_BF16 layer on the decoded weights: x, w_router and sh_gate
  * are bfloat16, desc->dtype must be MOE_BF16, and the workspace is
  * moe_workspace_size(desc, T).
  *
+ * Row-major MX form of a tensor of logical shape [R, K] (what moe_mx4_pack
+ * reads):
+ *   codes   uint8 [R, K/2]   element 2i of a row in bits 3..0 of byte i,
+ *                            element 2i+1 in bits 7..4
+ *   scales  uint8 [R, K/32]  the scale of elements 32b .. 32b+31 of a row
+ * Packed form (what the layer reads; R % 16 == 0, K % 128 == 0): tiles of 16
+ * rows x 128 elements, 1088 bytes each, tile (b, t) (rows 16b .. 16b+15,
+ * elements 128t .. 128t+127) at byte offset (b * K/128 + t) * 1088:
+ *   byte 16 (r + 16 c) + j, r < 16, c < 4, j < 16:  codes byte 64 t + 16 c + j
+ *                            of row 16 b + r (elements 128 t + 32 c + 2 j and
+ *                            + 1)
+ *   byte 1024 + r + 16 c:    scales byte 4 t + c of row 16 b + r
+ * so R K 17/32 bytes in all.  A tile is exactly what one 64-lane wave reads
+ * with one 16-byte load per lane (plus one byte each for the scales), and
+ * the tiles of a 16-row block follow each other along K.  The layer's
+ * tensors, in this form: w_gate_up [E*2F, d], w_down [E*d, F], w_sh_gate_up
+ * [2Fs, d], w_sh_down [d, Fs] (experts stacked along the rows).
+ *
  * Supported: d, F and Fs multiples of 128 and T*k <= 16*E (the
  * weight-streaming regime of few tokens per expert, e.g. decode); otherwise
- * MOE_ERR_UNSUPPORTED, before any GPU work.  Errors as for moe_forward.
+ * MOE_ERR_UNSUPPORTED, before any GPU work.  Scale byte 255 (NaN) gives
+ * unspecified results.  Errors as for moe_forward.
  * --------------------------------------------------------------------------- */
 
-/* The whole layer with MXFP4 expert weights; as moe_forward otherwise. */
+/* Bytes of the packed form of an [R, K] MXFP4 tensor (0 unless R > 0,
+ * K > 0, R % 16 == 0 and K % 128 == 0). */
+size_t moe_mx4_packed_bytes(int64_t rows, int64_t K);
+
+/* Packs a row-major MXFP4 tensor [rows, K] (codes 16-byte aligned, scales
+ * any alignment) into `packed` (16-byte aligned, moe_mx4_packed_bytes(rows,
+ * K) bytes), enqueued on `stream`.  A pure byte permutation, done once per
+ * weight tensor.  MOE_ERR_INVALID_ARG for NULL or misaligned pointers, rows
+ * or K not positive or not multiples of 16 and 128. */
+moe_status moe_mx4_pack(const uint8_t *codes, const uint8_t *scales, int64_t rows,
+                        int64_t K, void *packed, void *stream);
+
+/* The whole layer with packed MXFP4 expert weights; as moe_forward
+ * otherwise (same arguments, the four expert weight pointers being packed
+ * tensors). */
 moe_status moe_forward_mx4(const moe_desc *desc, int64_t T, const void *x,
                            const void *w_router, const float *router_bias,
-                           const uint8_t *gate_up_codes, const uint8_t *gate_up_scales,
-                           const uint8_t *down_codes, const uint8_t *down_scales,
-                           const uint8_t *sh_gate_up_codes, const uint8_t *sh_gate_up_scales,
-                           const uint8_t *sh_down_codes, const uint8_t *sh_down_scales,
+                           const void *w_gate_up, const void *w_down,
+                           const void *w_sh_gate_up, const void *w_sh_down,
                            const void *sh_gate, float *out, int32_t *topk_idx,
                            float *topk_w, void *ws, size_t ws_bytes, void *stream);
 
-/* The expert stage alone with MXFP4 expert weights and the routing given
- * (topk_idx, topk_w are INPUTS); as moe_experts otherwise. */
+/* The expert stage alone with packed MXFP4 expert weights and the routing
+ * given (topk_idx, topk_w are INPUTS); as moe_experts otherwise. */
 moe_status moe_experts_mx4(const moe_desc *desc, int64_t T, const void *x,
-                           const uint8_t *gate_up_codes, const uint8_t *gate_up_scales,
-                           const uint8_t *down_codes, const uint8_t *down_scales,
-                           const uint8_t *sh_gate_up_codes, const uint8_t *sh_gate_up_scales,
-                           const uint8_t *sh_down_codes, const uint8_t *sh_down_scales,
+                           const void *w_gate_up, const void *w_down,
+                           const void *w_sh_gate_up, const void *w_sh_down,
                            const void *sh_gate, const int32_t *topk_idx,
-                           const float *topk_w, float *out, void *ws, size_t ws_bytes,
-                           void *stream);
+                           const float *topk_w, float *out, void *ws,
+                           size_t ws_bytes, void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *moe_status_string(moe_status status);

@@ -8,8 +8,9 @@ is no CPU fallback: if the library is missing, every call raises.
 The layer (anatomy page on frontier-model-atlas, "Decoder microscope",
 Feed-forward panel): router logits -> softmax -> top-k -> normalised selected
 weights; SwiGLU experts; one shared expert scaled by its own sigmoid gate.
-Expert weights are bfloat16/binary32 tensors, or MXFP4 pairs ``(codes, scales)``
-of uint8 tensors (``forward_mx4``/``experts_mx4``; layout in ``include/moe.h``).
+Expert weights are bfloat16/binary32 tensors, or MXFP4 tensors packed once by
+``mx4_pack`` from row-major ``(codes, scales)`` uint8 pairs (``forward_mx4`` /
+``experts_mx4``; both forms are defined in ``include/moe.h``).
 """
 from __future__ import annotations
 
@@ -30,8 +31,8 @@ ROUTERS = {None: 0, "auto": 0, "exact": MOE_FLAG_ROUTER_EXACT,
            "shortlist": MOE_FLAG_ROUTER_SHORTLIST}
 
 EXPORTED = ("moe_workspace_size", "moe_workspace_query", "moe_route", "moe_forward",
-            "moe_experts", "moe_forward_mx4", "moe_experts_mx4", "moe_status_string",
-            "moe_last_error", "moe_stage_events")
+            "moe_experts", "moe_mx4_packed_bytes", "moe_mx4_pack", "moe_forward_mx4",
+            "moe_experts_mx4", "moe_status_string", "moe_last_error", "moe_stage_events")
 
 
 class MoEError(RuntimeError):
@@ -72,10 +73,13 @@ def lib():
     L.moe_route.argtypes = [dp, i64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_forward.argtypes = [dp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_experts.argtypes = [dp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    L.moe_forward_mx4.argtypes = [dp, i64] + [vp] * 3 + [vp] * 8 + [vp] * 4 + [vp, sz, vp]
-    L.moe_experts_mx4.argtypes = [dp, i64, vp] + [vp] * 8 + [vp] * 4 + [vp, sz, vp]
+    L.moe_forward_mx4.argtypes = L.moe_forward.argtypes
+    L.moe_experts_mx4.argtypes = L.moe_experts.argtypes
+    L.moe_mx4_packed_bytes.argtypes = [i64, i64]
+    L.moe_mx4_packed_bytes.restype = sz
+    L.moe_mx4_pack.argtypes = [vp, vp, i64, i64, vp, vp]
     for f in (L.moe_workspace_query, L.moe_route, L.moe_forward, L.moe_experts,
-              L.moe_forward_mx4, L.moe_experts_mx4):
+              L.moe_forward_mx4, L.moe_experts_mx4, L.moe_mx4_pack):
         f.restype = ctypes.c_int
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
@@ -274,43 +278,58 @@ def experts(x, w_gate_up, w_down, topk_idx, topk_w, w_sh_gate_up=None, w_sh_down
     return out
 
 
-def _mx4_dims(gu, sgu):
-    """(E, F, Fs) of an MXFP4 layer from its gate/up code arrays."""
-    E, twoF = gu[0].shape[:2]
-    return E, twoF // 2, 0 if sgu is None else sgu[0].shape[0] // 2
+@dataclass(frozen=True)
+class MX4Tensor:
+    """A packed MXFP4 tensor of logical shape [rows, K] in device memory."""
+    data: torch.Tensor
+    rows: int
+    K: int
 
 
-def _dev_mx4(t, name, rows, K):
-    if not (isinstance(t, tuple) and len(t) == 2):
-        raise TypeError(f"{name} must be a (codes, scales) pair of uint8 tensors")
-    _dev(t[0], name + " codes", torch.uint8, tuple(rows) + (K // 2,))
-    _dev(t[1], name + " scales", torch.uint8, tuple(rows) + (K // 32,))
+def mx4_pack(codes: torch.Tensor, scales: torch.Tensor) -> MX4Tensor:
+    """Pack a row-major MXFP4 tensor (codes uint8 [..., K/2], scales uint8
+    [..., K/32]; leading dimensions are rows) into the layer's tiled form."""
+    K = codes.shape[-1] * 2
+    rows = codes.numel() // max(1, codes.shape[-1])
+    _dev(codes, "codes", torch.uint8), _dev(scales, "scales", torch.uint8,
+                                          tuple(codes.shape[:-1]) + (K // 32,))
+    nbytes = int(lib().moe_mx4_packed_bytes(rows, K))
+    if nbytes == 0:
+        raise ValueError(f"MXFP4 packing needs rows % 16 == 0 and K % 128 == 0 (got {rows} x {K})")
+    out = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+    _check(lib().moe_mx4_pack(_ptr(codes), _ptr(scales), rows, K, _ptr(out), _stream()),
+           "moe_mx4_pack")
+    return MX4Tensor(out, rows, K)
 
 
-def _mx4_ptrs(gu, dn, sgu, sdn):
-    ptrs = [_ptr(gu[0]), _ptr(gu[1]), _ptr(dn[0]), _ptr(dn[1])]
-    for t in (sgu, sdn):
-        ptrs += [None, None] if t is None else [_ptr(t[0]), _ptr(t[1])]
-    return ptrs
-
-
-def _check_mx4_weights(d, E, F, Fs, gu, dn, sgu, sdn):
-    _dev_mx4(gu, "w_gate_up", (E, 2 * F), d)
-    _dev_mx4(dn, "w_down", (E, d), F)
+def _mx4_dims(d, gu, dn, sgu, sdn):
+    """(E, F, Fs) of a layer from its packed tensors, shapes checked."""
+    for t, n in ((gu, "w_gate_up"), (dn, "w_down"), (sgu, "w_sh_gate_up"), (sdn, "w_sh_down")):
+        if t is not None and not isinstance(t, MX4Tensor):
+            raise TypeError(f"{n} must be an MX4Tensor (see mx4_pack)")
+    F = dn.K
+    E = dn.rows // d
+    Fs = 0 if sdn is None else sdn.K
+    ok = dn.rows == E * d and gu.rows == E * 2 * F and gu.K == d
     if Fs:
-        _dev_mx4(sgu, "w_sh_gate_up", (2 * Fs,), d)
-        _dev_mx4(sdn, "w_sh_down", (d,), Fs)
+        ok = ok and sgu is not None and sgu.rows == 2 * Fs and sgu.K == d and sdn.rows == d
+    if not ok:
+        raise ValueError("MXFP4 tensor shapes do not form one layer")
+    return E, F, Fs
+
+
+def _mx4_ptrs(*ts):
+    return [None if t is None else _ptr(t.data) for t in ts]
 
 
 def forward_mx4(x, w_router, gu, dn, k, sgu=None, sdn=None, sh_gate=None, bias=None, out=None,
                 topk_idx=None, topk_w=None, ws=None, router=None):
-    """The whole layer with MXFP4 expert weights (gu, dn, sgu, sdn are
-    (codes, scales) pairs).  Returns (out float32 [T,d], topk_idx, topk_w)."""
+    """The whole layer with packed MXFP4 expert weights (MX4Tensor each).
+    Returns (out float32 [T,d], topk_idx, topk_w)."""
     T, d = x.shape
-    E, F, Fs = _mx4_dims(gu, sgu)
+    E, F, Fs = _mx4_dims(d, gu, dn, sgu, sdn)
     shape = Shape(d, E, k, F, Fs, x.dtype, router)
     _dev(x, "x", torch.bfloat16), _dev(w_router, "w_router", x.dtype, (E, d))
-    _check_mx4_weights(d, E, F, Fs, gu, dn, sgu, sdn)
     if Fs:
         _dev(sh_gate, "sh_gate", x.dtype, (d,))
     _dev(bias, "router_bias", torch.float32, (E,))
@@ -329,13 +348,12 @@ def forward_mx4(x, w_router, gu, dn, k, sgu=None, sdn=None, sh_gate=None, bias=N
 
 def experts_mx4(x, gu, dn, topk_idx, topk_w, sgu=None, sdn=None, sh_gate=None, out=None,
                 ws=None):
-    """Expert stage with MXFP4 expert weights and the routing given."""
+    """Expert stage with packed MXFP4 expert weights and the routing given."""
     T, d = x.shape
     k = topk_idx.shape[1]
-    E, F, Fs = _mx4_dims(gu, sgu)
+    E, F, Fs = _mx4_dims(d, gu, dn, sgu, sdn)
     shape = Shape(d, E, k, F, Fs, x.dtype)
     _dev(x, "x", torch.bfloat16)
-    _check_mx4_weights(d, E, F, Fs, gu, dn, sgu, sdn)
     _dev(topk_idx, "topk_idx", torch.int32, (T, k)), _dev(topk_w, "topk_w", torch.float32, (T, k))
     if Fs:
         _dev(sh_gate, "sh_gate", x.dtype, (d,))
@@ -359,10 +377,15 @@ class MoELayer:
                       w_sh_gate_up=w_sh_gate_up, w_sh_down=w_sh_down, sh_gate=sh_gate, bias=bias)
         self.k = k
         self.router = router
-        # MXFP4 expert weights come as (codes, scales) pairs
-        self.mx4 = isinstance(w_gate_up, tuple)
+        # MXFP4 expert weights: MX4Tensor, or row-major (codes, scales) pairs
+        # packed here once
+        self.mx4 = isinstance(w_gate_up, (tuple, MX4Tensor))
         if self.mx4:
-            E, F, Fs = _mx4_dims(w_gate_up, w_sh_gate_up)
+            for n in ("w_gate_up", "w_down", "w_sh_gate_up", "w_sh_down"):
+                if isinstance(self.w[n], tuple):
+                    self.w[n] = mx4_pack(*self.w[n])
+            E, F, Fs = _mx4_dims(w_router.shape[1], self.w["w_gate_up"], self.w["w_down"],
+                                 self.w["w_sh_gate_up"], self.w["w_sh_down"])
             self.shape = Shape(w_router.shape[1], E, k, F, Fs, w_router.dtype, router)
         else:
             self.shape = shape_of(w_router, w_gate_up, k, w_sh_gate_up, router)

@@ -315,40 +315,41 @@ moe_status moe_experts(const moe_desc *desc, int64_t T, const void *x, const voi
     return run_experts(p, s);
 }
 
+size_t moe_mx4_packed_bytes(int64_t rows, int64_t K) {
+    if (rows <= 0 || K <= 0 || rows % 16 || K % 128) return 0;
+    return (size_t)(rows / 16) * (size_t)(K / 128) * 1088;
+}
+
+moe_status moe_mx4_pack(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t K,
+                        void *packed, void *stream) {
+    if (!codes || !scales || !packed || !aligned16(codes) || !aligned16(packed))
+        return MOE_ERR_INVALID_ARG;
+    if (moe_mx4_packed_bytes(rows, K) == 0) return MOE_ERR_INVALID_ARG;
+    return hip_status(
+        moe::launch_mx4_pack(codes, scales, rows, K, packed, static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_forward_mx4(const moe_desc *desc, int64_t T, const void *x, const void *w_router,
-                           const float *router_bias, const uint8_t *gate_up_codes,
-                           const uint8_t *gate_up_scales, const uint8_t *down_codes,
-                           const uint8_t *down_scales, const uint8_t *sh_gate_up_codes,
-                           const uint8_t *sh_gate_up_scales, const uint8_t *sh_down_codes,
-                           const uint8_t *sh_down_scales, const void *sh_gate, float *out,
-                           int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
-                           void *stream) {
-    moe_status st = check_common(desc, T,
-                                 {x, w_router, gate_up_codes, gate_up_scales, down_codes,
-                                  down_scales, out, topk_idx, topk_w},
-                                 {router_bias, sh_gate_up_codes, sh_gate_up_scales, sh_down_codes,
-                                  sh_down_scales, sh_gate},
-                                 ws, ws_bytes);
+                           const float *router_bias, const void *w_gate_up, const void *w_down,
+                           const void *w_sh_gate_up, const void *w_sh_down, const void *sh_gate,
+                           float *out, int32_t *topk_idx, float *topk_w, void *ws,
+                           size_t ws_bytes, void *stream) {
+    moe_status st = check_common(desc, T, {x, w_router, w_gate_up, w_down, out, topk_idx, topk_w},
+                                 {router_bias, w_sh_gate_up, w_sh_down, sh_gate}, ws, ws_bytes);
     if (st != MOE_OK) return st;
     st = check_mx4(desc, T);
     if (st != MOE_OK || T == 0) return st;
-    if (desc->d_shared > 0 && (!sh_gate_up_codes || !sh_gate_up_scales || !sh_down_codes ||
-                               !sh_down_scales || !sh_gate))
-        return MOE_ERR_INVALID_ARG;
+    if (desc->d_shared > 0 && (!w_sh_gate_up || !w_sh_down || !sh_gate)) return MOE_ERR_INVALID_ARG;
     const Plan pl = make_plan(*desc, T);
     moe::Problem p = make_problem(*desc, T, pl, ws);
     p.x = x;
     p.w_router = w_router;
     p.router_bias = router_bias;
     p.mx4 = true;
-    p.w_gate_up = gate_up_codes;
-    p.sc_gate_up = gate_up_scales;
-    p.w_down = down_codes;
-    p.sc_down = down_scales;
-    p.w_sh_gate_up = sh_gate_up_codes;
-    p.sc_sh_gate_up = sh_gate_up_scales;
-    p.w_sh_down = sh_down_codes;
-    p.sc_sh_down = sh_down_scales;
+    p.w_gate_up = w_gate_up;
+    p.w_down = w_down;
+    p.w_sh_gate_up = w_sh_gate_up;
+    p.w_sh_down = w_sh_down;
     p.sh_gate = desc->d_shared > 0 ? sh_gate : nullptr;
     p.out = out;
     p.topk_idx = topk_idx;
@@ -364,37 +365,24 @@ moe_status moe_forward_mx4(const moe_desc *desc, int64_t T, const void *x, const
     return run_experts(p, s);
 }
 
-moe_status moe_experts_mx4(const moe_desc *desc, int64_t T, const void *x,
-                           const uint8_t *gate_up_codes, const uint8_t *gate_up_scales,
-                           const uint8_t *down_codes, const uint8_t *down_scales,
-                           const uint8_t *sh_gate_up_codes, const uint8_t *sh_gate_up_scales,
-                           const uint8_t *sh_down_codes, const uint8_t *sh_down_scales,
+moe_status moe_experts_mx4(const moe_desc *desc, int64_t T, const void *x, const void *w_gate_up,
+                           const void *w_down, const void *w_sh_gate_up, const void *w_sh_down,
                            const void *sh_gate, const int32_t *topk_idx, const float *topk_w,
                            float *out, void *ws, size_t ws_bytes, void *stream) {
-    moe_status st = check_common(desc, T,
-                                 {x, gate_up_codes, gate_up_scales, down_codes, down_scales,
-                                  topk_idx, topk_w, out},
-                                 {sh_gate_up_codes, sh_gate_up_scales, sh_down_codes,
-                                  sh_down_scales, sh_gate},
-                                 ws, ws_bytes);
+    moe_status st = check_common(desc, T, {x, w_gate_up, w_down, topk_idx, topk_w, out},
+                                 {w_sh_gate_up, w_sh_down, sh_gate}, ws, ws_bytes);
     if (st != MOE_OK) return st;
     st = check_mx4(desc, T);
     if (st != MOE_OK || T == 0) return st;
-    if (desc->d_shared > 0 && (!sh_gate_up_codes || !sh_gate_up_scales || !sh_down_codes ||
-                               !sh_down_scales || !sh_gate))
-        return MOE_ERR_INVALID_ARG;
+    if (desc->d_shared > 0 && (!w_sh_gate_up || !w_sh_down || !sh_gate)) return MOE_ERR_INVALID_ARG;
     const Plan pl = make_plan(*desc, T);
     moe::Problem p = make_problem(*desc, T, pl, ws);
     p.x = x;
     p.mx4 = true;
-    p.w_gate_up = gate_up_codes;
-    p.sc_gate_up = gate_up_scales;
-    p.w_down = down_codes;
-    p.sc_down = down_scales;
-    p.w_sh_gate_up = sh_gate_up_codes;
-    p.sc_sh_gate_up = sh_gate_up_scales;
-    p.w_sh_down = sh_down_codes;
-    p.sc_sh_down = sh_down_scales;
+    p.w_gate_up = w_gate_up;
+    p.w_down = w_down;
+    p.w_sh_gate_up = w_sh_gate_up;
+    p.w_sh_down = w_sh_down;
     p.sh_gate = sh_gate;
     p.out = out;
     p.topk_idx = const_cast<int32_t *>(topk_idx);

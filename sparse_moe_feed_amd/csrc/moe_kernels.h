@@ -40,11 +40,9 @@ struct Problem {
     void *h;            // [T*k, F]
     void *h_shared;     // [T, Fs]
     int nblk;           // ceil(T / kCountBlock)
-    // MXFP4 expert weights: w_gate_up, w_down, w_sh_gate_up, w_sh_down then
-    // hold the packed E2M1 codes and these the E8M0 scales (one per 32
-    // elements of a row)
+    // MXFP4 expert weights: w_gate_up, w_down, w_sh_gate_up, w_sh_down are
+    // then packed MXFP4 tensors (16 x 128 tiles of codes and scales)
     bool mx4;
-    const uint8_t *sc_gate_up, *sc_down, *sc_sh_gate_up, *sc_sh_down;
 };
 
 constexpr int kCountBlock = 256;     // tokens per histogram block
@@ -104,8 +102,13 @@ hipError_t launch_experts_f32(const Problem &p, hipStream_t s, const std::functi
 // Weight-streaming expert stage for few tokens per expert (tiles of kDecodeBM).
 hipError_t launch_experts_decode(const Problem &p, hipStream_t s,
                                  const std::function<void(int)> &mark);
-// The same with MXFP4 expert weights (p.mx4), decoded to bf16 in registers.
+// The same with packed MXFP4 expert weights (p.mx4), decoded to bf16 in
+// registers.
 hipError_t launch_experts_decode_mx4(const Problem &p, hipStream_t s,
                                      const std::function<void(int)> &mark);
+// Row-major MXFP4 [rows, K] (codes, scales) -> packed tiles (rows % 16 == 0,
+// K % 128 == 0).
+hipError_t launch_mx4_pack(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t K,
+                           void *packed, hipStream_t s);
 
 }  // namespace moe

@@ -130,14 +130,13 @@ def test_route_and_experts_validate(L):
 
 
 def call_forward_mx4(L, D, T, ptrs=None, ws=FAKE, ws_bytes=1 << 40):
-    p = dict(x=FAKE, wr=FAKE, b=None, guc=FAKE, gus=FAKE, dnc=FAKE, dns=FAKE, sguc=FAKE,
-             sgus=FAKE, sdnc=FAKE, sdns=FAKE, g=FAKE, out=FAKE, idx=FAKE, w=FAKE)
+    p = dict(x=FAKE, wr=FAKE, b=None, gu=FAKE, dn=FAKE, sgu=FAKE, sdn=FAKE, g=FAKE, out=FAKE,
+             idx=FAKE, w=FAKE)
     p.update(ptrs or {})
     v = lambda a: None if a is None else ctypes.c_void_p(a)
-    return L.moe_forward_mx4(ctypes.byref(D), T, v(p["x"]), v(p["wr"]), v(p["b"]), v(p["guc"]),
-                             v(p["gus"]), v(p["dnc"]), v(p["dns"]), v(p["sguc"]), v(p["sgus"]),
-                             v(p["sdnc"]), v(p["sdns"]), v(p["g"]), v(p["out"]), v(p["idx"]),
-                             v(p["w"]), v(ws), ws_bytes, None)
+    return L.moe_forward_mx4(ctypes.byref(D), T, v(p["x"]), v(p["wr"]), v(p["b"]), v(p["gu"]),
+                             v(p["dn"]), v(p["sgu"]), v(p["sdn"]), v(p["g"]), v(p["out"]),
+                             v(p["idx"]), v(p["w"]), v(ws), ws_bytes, None)
 
 
 def mx4_desc(**kw):
@@ -146,8 +145,7 @@ def mx4_desc(**kw):
     return desc(**base)
 
 
-@pytest.mark.parametrize("missing", ["guc", "gus", "dnc", "dns", "sguc", "sgus", "sdnc", "sdns",
-                                     "g", "x", "out"])
+@pytest.mark.parametrize("missing", ["gu", "dn", "sgu", "sdn", "g", "x", "out"])
 def test_mx4_null_required_pointer(L, missing):
     assert call_forward_mx4(L, mx4_desc(), 8, {missing: None}) == moe.MOE_ERR_INVALID_ARG
 
@@ -167,22 +165,34 @@ def test_mx4_only_in_weight_streaming_regime(L):
     assert call_forward_mx4(L, D, 64, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
 
 
-def test_mx4_misaligned_codes_and_noop(L):
-    assert call_forward_mx4(L, mx4_desc(), 8, {"guc": FAKE + 8}) == moe.MOE_ERR_INVALID_ARG
+def test_mx4_misaligned_and_noop(L):
+    assert call_forward_mx4(L, mx4_desc(), 8, {"gu": FAKE + 8}) == moe.MOE_ERR_INVALID_ARG
     assert call_forward_mx4(L, mx4_desc(), 0, ws=None, ws_bytes=0) == moe.MOE_OK
     D = mx4_desc(Fs=0)
-    assert call_forward_mx4(L, D, 8, {"sguc": None, "sgus": None, "sdnc": None, "sdns": None,
-                                      "g": None}, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
+    assert call_forward_mx4(L, D, 8, {"sgu": None, "sdn": None, "g": None}, ws_bytes=16) == \
+        moe.MOE_ERR_WORKSPACE
 
 
 def test_mx4_experts_validate(L):
     v = ctypes.c_void_p
     D = mx4_desc()
-    args = [v(FAKE)] * 8
-    assert L.moe_experts_mx4(ctypes.byref(D), 8, v(FAKE), *args, v(FAKE), None, v(FAKE), v(FAKE),
-                             v(FAKE), 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
-    assert L.moe_experts_mx4(ctypes.byref(D), 100, v(FAKE), *args, v(FAKE), v(FAKE), v(FAKE),
-                             v(FAKE), v(FAKE), 1 << 40, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_experts_mx4(ctypes.byref(D), 8, v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE),
+                             v(FAKE), None, v(FAKE), v(FAKE), v(FAKE), 1 << 40,
+                             None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_experts_mx4(ctypes.byref(D), 100, v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE),
+                             v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE), 1 << 40,
+                             None) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_mx4_packed_bytes_and_pack_validation(L):
+    assert L.moe_mx4_packed_bytes(32, 256) == 2 * 2 * 1088
+    assert L.moe_mx4_packed_bytes(2 * 1280 * 512, 2560) == 2 * 1280 * 512 * 2560 * 17 // 32
+    for rows, K in [(0, 128), (16, 0), (24, 128), (16, 192), (-16, 128)]:
+        assert L.moe_mx4_packed_bytes(rows, K) == 0
+    v = ctypes.c_void_p
+    assert L.moe_mx4_pack(None, v(FAKE), 16, 128, v(FAKE), None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_mx4_pack(v(FAKE), v(FAKE), 16, 128, v(FAKE + 4), None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_mx4_pack(v(FAKE), v(FAKE), 24, 128, v(FAKE), None) == moe.MOE_ERR_INVALID_ARG
 
 
 def test_status_strings(L):

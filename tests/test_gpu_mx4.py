@@ -1,5 +1,6 @@
-"""Parity of the HIP path with MXFP4 expert weights (moe_forward_mx4 /
-moe_experts_mx4, through the C ABI) against the CPU oracle's MXFP4 layer.
+"""Parity of the HIP path with MXFP4 expert weights (moe_mx4_pack, then
+moe_forward_mx4 / moe_experts_mx4, through the C ABI) against the CPU oracle's
+MXFP4 layer, which reads the row-major MX form directly.
 
 Bars as for the bf16 layer: topk_idx bit for bit, topk_w within 1e-5, out
 within 2e-2 x RMS(oracle out).  The decoded weights are exact in bf16, so the
@@ -21,7 +22,40 @@ MX = ("gu", "dn", "sgu", "sdn")
 
 
 def mx_dev(t):
-    return None if t is None else (to_dev(t[0]), to_dev(t[1]))
+    """Row-major (codes, scales) -> packed MX4Tensor on the GPU."""
+    return None if t is None else moe.mx4_pack(to_dev(t[0]), to_dev(t[1]))
+
+
+def packed_reference(codes, scales):
+    """The packed form, written out from its definition in include/moe.h:
+    tile (b, t) of 16 rows x 128 elements at (b K/128 + t) 1088 bytes; byte
+    16 (r + 16 c) + j = codes byte 64 t + 16 c + j of row 16 b + r; byte
+    1024 + r + 16 c = scales byte 4 t + c of row 16 b + r."""
+    R, K = codes.shape[0], codes.shape[1] * 2
+    out = np.zeros(R // 16 * (K // 128) * 1088, np.uint8)
+    for b in range(R // 16):
+        for t in range(K // 128):
+            base = (b * (K // 128) + t) * 1088
+            for r in range(16):
+                for c in range(4):
+                    o = base + 16 * (r + 16 * c)
+                    out[o:o + 16] = codes[16 * b + r, 64 * t + 16 * c:64 * t + 16 * c + 16]
+                    out[base + 1024 + r + 16 * c] = scales[16 * b + r, 4 * t + c]
+    return out
+
+
+@pytest.mark.parametrize("R,K", [(16, 128), (48, 384), (32, 640)])
+def test_mx4_pack_matches_layout_definition(R, K):
+    """The pack kernel is a pure byte permutation: bit-exact against the
+    layout written out element by element."""
+    rng = np.random.default_rng(R + K)
+    codes = rng.integers(0, 256, (R, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, (R, K // 32), dtype=np.uint8)
+    announce(f"mx4_pack {R}x{K}")
+    p = moe.mx4_pack(to_dev(codes), to_dev(scales))
+    torch.cuda.synchronize()
+    assert (p.rows, p.K) == (R, K)
+    assert np.array_equal(p.data.cpu().numpy(), packed_reference(codes, scales))
 
 
 def small_mx4(T, d, E, k, F, Fs, seed):
