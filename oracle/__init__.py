@@ -18,6 +18,10 @@ What each function follows (pages cited by title and section):
     field", ffns.moe.gated; llm-atlas "Qwen3.8-Flash-Next", "Raw config
     fields", hidden_act) plus one shared expert scaled by its own sigmoid gate
     (anatomy page, Feed-forward panel and "Evidence for layer 1").
+  * ``rmsnorm`` -- the pre-FFN RMSNorm (eps 1e-6: llm-atlas "Qwen3.8-Flash-Next",
+    "Key facts" Norm, "Raw config fields" rms_norm_eps), read as a pre-norm
+    whose binary32 evaluation order is fixed so both sides route on the same
+    normalised bits.
   * ``experts_mx4`` / ``forward_mx4`` / ``mx4_decode`` -- the same layer with
     low-bit expert weights.  The published weights are packed low-bit tensors
     (llm-atlas "Qwen3.8-Flash-Next", "Modelled costs"); the encoding is not
@@ -74,9 +78,10 @@ def _load():
     lib.oracle_experts_mx4.argtypes = [i64, i32, i32, i32, i32, i32] + [vp] * 14
     lib.oracle_forward_mx4.argtypes = [i64, i32, i32, i32, i32, i32] + [vp] * 16
     lib.oracle_mx4_decode.argtypes = [i64, i64, vp, vp, vp]
+    lib.oracle_rmsnorm.argtypes = [i64, i32, i32, vp, vp, ctypes.c_float, vp]
     for f in (lib.oracle_router_logits, lib.oracle_route, lib.oracle_experts,
               lib.oracle_forward, lib.oracle_threads, lib.oracle_experts_mx4,
-              lib.oracle_forward_mx4, lib.oracle_mx4_decode):
+              lib.oracle_forward_mx4, lib.oracle_mx4_decode, lib.oracle_rmsnorm):
         f.restype = ctypes.c_int
     lib.oracle_threads.argtypes = []
     _lib = lib
@@ -281,3 +286,18 @@ def forward_mx4(x, w_router, gu, dn, k, sgu=None, sdn=None, sh_gate=None, bias=N
     if rc:
         raise RuntimeError(f"oracle_forward_mx4 failed ({rc})")
     return out, idx, w, s
+
+
+def rmsnorm(h, gamma, eps=1e-6):
+    """Pre-FFN RMSNorm of h [T, d] with weight gamma [d]: x in h's dtype
+    (bfloat16 bits rounded to nearest even, or float32)."""
+    T, d = h.shape
+    dt = _dtype_code(h)
+    _same(dt, gamma)
+    if gamma.shape != (d,):
+        raise ValueError("gamma must have shape [d]")
+    out = np.empty_like(h)
+    rc = _load().oracle_rmsnorm(T, d, dt, _ptr(h), _ptr(gamma), ctypes.c_float(eps), _ptr(out))
+    if rc:
+        raise RuntimeError(f"oracle_rmsnorm failed ({rc})")
+    return out

@@ -46,6 +46,13 @@
  *     0 or 0.5).  Codes are stored two per byte, element 2i in bits 3..0 and
  *     element 2i+1 in bits 7..4.  The oracle decodes every element exactly
  *     and then runs the same binary64 gated MLPs.
+ *   - Pre-FFN RMSNorm (oracle_rmsnorm): the norm is RMSNorm with eps 1e-6
+ *     (llm-atlas "Qwen3.8-Flash-Next", "Key facts" Norm and "Raw config
+ *     fields" rms_norm_eps); its placement is not disclosed and is read as
+ *     the usual pre-norm: the layer's input is x = h / sqrt(mean(h^2) + eps)
+ *     * gamma.  Because the normalised x feeds the integer top-k decision,
+ *     it is evaluated in one fixed binary32 order (below) and rounded to the
+ *     layer's dtype, so that both sides route on the same bits.
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fopenmp -shared -fPIC
  * (no fast-math: the binary32 router logit must round exactly as written).
@@ -138,6 +145,45 @@ static float router_logit(const void *x, int64_t xoff, const void *w,
         for (int j = 0; j < s; j++)
             acc[j] = acc[j] + acc[j + s];
     return acc[0] + bias;
+}
+
+/* binary32 -> bfloat16 bits, round to nearest, ties to even (finite input). */
+static uint16_t f32_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+/* Pre-FFN RMSNorm of each row of h [T, d] with weight gamma [d], in binary32:
+ *   ss   = sum_k h_k^2, in the canonical order of the router logit (the same
+ *          64 partials, fused multiply-adds and halving tree, no bias);
+ *   mean = ss / d;  v = mean + eps;  r = 1 / sqrtf(v)   (each rounded once);
+ *   x_k  = (h_k * r) * gamma_k                          (each product rounded),
+ * then rounded to bfloat16 (nearest even) for bfloat16 layers.  x_out has
+ * the layout and dtype of h. */
+int oracle_rmsnorm(int64_t T, int d, int dtype, const void *h, const void *gamma,
+                   float eps, void *x_out)
+{
+    if (T < 0 || d < 1 || !h || !gamma || !x_out || !(eps >= 0.0f))
+        return 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; t++) {
+        float ss = router_logit(h, t * d, h, t * d, d, dtype, 0.0f);
+        float mean = ss / (float)d;
+        float v = mean + eps;
+        float r = 1.0f / sqrtf(v);
+        for (int kk = 0; kk < d; kk++) {
+            float hr = load_elem(h, dtype, t * d + kk) * r;
+            float xv = hr * load_elem(gamma, dtype, kk);
+            if (dtype == ORACLE_BF16)
+                ((uint16_t *)x_out)[t * d + kk] = f32_to_bf16(xv);
+            else
+                ((float *)x_out)[t * d + kk] = xv;
+        }
+    }
+    return 0;
 }
 
 /* logits[t*E + e] for all tokens and experts. */
