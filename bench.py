@@ -12,7 +12,8 @@ prefill-shaped layer (T=4096) is reported inside the same line under "also".
 recorded on the library's stream at its stage boundaries during the timed
 loop.  `cpu_baseline` times the CPU oracle on the host cores.
 
-`--config 6` measures the same decode layer with MXFP4 expert weights
+`--config 7` measures the decode layer with its pre-FFN RMSNorm (one call:
+moe_forward_prenorm); `--config 6` measures the same decode layer with MXFP4 expert weights
 (moe_forward_mx4); its algorithmic weight bytes are 17/32 byte per element
 (a 4-bit code plus one scale byte per 32 elements).
 
@@ -89,9 +90,10 @@ def measure(cfg, dev_layer, steps, warmup):
     to = lambda a: None if a is None else torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
     x = to(x_np)
     bias = None if bias_np is None else torch.from_numpy(bias_np).cuda()
+    gamma = to(W.make_norm_weight(cfg.d, cfg.dtype, cfg.seed_w)) if cfg.prenorm else None
     L = moe.MoELayer(dev_layer["w_router"], dev_layer["w_gate_up"], dev_layer["w_down"], cfg.k,
                      dev_layer["w_sh_gate_up"], dev_layer["w_sh_down"], dev_layer["sh_gate"], bias,
-                     max_tokens=cfg.T)
+                     max_tokens=cfg.T, norm_weight=gamma)
     out = torch.empty(cfg.T, cfg.d, device="cuda")
     idx = torch.empty(cfg.T, cfg.k, dtype=torch.int32, device="cuda")
     w = torch.empty(cfg.T, cfg.k, device="cuda")
@@ -160,6 +162,9 @@ def cpu_baseline(cfg, layer_np, seconds):
         fwd = oracle.forward
         args = (x, layer_np["w_router"], layer_np["w_gate_up"], layer_np["w_down"], cfg.k,
                 layer_np["w_sh_gate_up"], layer_np["w_sh_down"], layer_np["sh_gate"])
+    if cfg.prenorm:
+        gamma, base = W.make_norm_weight(cfg.d, cfg.dtype, cfg.seed_w), fwd
+        fwd = lambda h, *a, bias=None: base(oracle.rmsnorm(h, gamma), *a, bias=bias)
     reps, t0 = 0, time.perf_counter()
     while True:
         fwd(*args, bias=bias)
@@ -261,7 +266,8 @@ def main():
         "data": "synthetic: seeded N(0,1) tokens, N(0,0.02^2) weights (random init, no checkpoint)",
         "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d, "experts": cfg.E,
                    "top_k": cfg.k, "d_expert": cfg.F, "d_shared": cfg.Fs, "router_bias": cfg.bias,
-                   "expert_weights": "mxfp4" if cfg.dtype == "mxfp4" else "bf16"},
+                   "expert_weights": "mxfp4" if cfg.dtype == "mxfp4" else "bf16",
+                   "pre_norm": "rmsnorm" if cfg.prenorm else None},
         "roofline": roof,
         "layer": layer,
         "stage_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},

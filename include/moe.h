@@ -113,9 +113,11 @@ size_t moe_workspace_size(const moe_desc *desc, int64_t T);
  *   h_shared [T, Fs]          gated activations of the shared expert
  *   y        [T*k, d]         w[t,j] * expert output of each routed row (bf16 /
  *                             f32, as h); the combine adds a token's k rows to
- *                             the shared term in binary32 */
+ *                             the shared term in binary32
+ *   xnorm    [T, d]           the normalised layer input of moe_forward_prenorm
+ *                             (desc->dtype) */
 typedef struct {
-    size_t logits, gate, counts, offsets, perm, h, h_shared, y, total;
+    size_t logits, gate, counts, offsets, perm, h, h_shared, y, xnorm, total;
 } moe_workspace_layout;
 
 moe_status moe_workspace_query(const moe_desc *desc, int64_t T,
@@ -223,6 +225,42 @@ moe_status moe_experts_mx4(const moe_desc *desc, int64_t T, const void *x,
                            const void *sh_gate, const int32_t *topk_idx,
                            const float *topk_w, float *out, void *ws,
                            size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Pre-FFN RMSNorm.
+ *
+ * The model's norm is RMSNorm with eps 1e-6 (llm-atlas "Qwen3.8-Flash-Next",
+ * "Key facts" Norm and "Raw config fields" rms_norm_eps); its placement is
+ * not disclosed and is read as the usual pre-norm in front of the layer:
+ *   x[t] = h[t] / sqrt(mean_k h[t,k]^2 + eps) * norm_weight
+ * The normalised rows decide the integer top-k, so they are computed in one
+ * fixed binary32 order: ss = sum_k h_k^2 in the router logit's canonical
+ * order (above, no bias); mean = ss / d; v = mean + eps; r = 1 / sqrt(v);
+ * x_k = (h_k * r) * norm_weight_k, every step rounded once to nearest; then
+ * rounded to desc->dtype (bfloat16: nearest even).  eps is binary32, finite
+ * and >= 0 (else MOE_ERR_INVALID_ARG); a zero row with eps = 0 gives NaN.
+ * h and norm_weight ([d]) are in desc->dtype.
+ * --------------------------------------------------------------------------- */
+
+/* x_out [T, d] = RMSNorm(h) as above (x_out may not alias h). */
+moe_status moe_rmsnorm(const moe_desc *desc, int64_t T, const void *h,
+                       const void *norm_weight, float eps, void *x_out, void *stream);
+
+/* Expert weight formats of moe_forward_prenorm. */
+enum { MOE_WEIGHTS_DTYPE = 0, MOE_WEIGHTS_MX4 = 1 };
+
+/* The layer on the normalised rows: RMSNorm(h) is written to the workspace
+ * (region xnorm) and the layer runs on it, with expert weights in
+ * desc->dtype (weight_format MOE_WEIGHTS_DTYPE, as moe_forward) or packed
+ * MXFP4 (MOE_WEIGHTS_MX4, as moe_forward_mx4, with its limits).  One call;
+ * out, topk_idx and topk_w as for moe_forward. */
+moe_status moe_forward_prenorm(const moe_desc *desc, int64_t T, const void *h,
+                               const void *norm_weight, float eps, int32_t weight_format,
+                               const void *w_router, const float *router_bias,
+                               const void *w_gate_up, const void *w_down,
+                               const void *w_sh_gate_up, const void *w_sh_down,
+                               const void *sh_gate, float *out, int32_t *topk_idx,
+                               float *topk_w, void *ws, size_t ws_bytes, void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *moe_status_string(moe_status status);

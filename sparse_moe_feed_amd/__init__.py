@@ -32,7 +32,9 @@ ROUTERS = {None: 0, "auto": 0, "exact": MOE_FLAG_ROUTER_EXACT,
 
 EXPORTED = ("moe_workspace_size", "moe_workspace_query", "moe_route", "moe_forward",
             "moe_experts", "moe_mx4_packed_bytes", "moe_mx4_pack", "moe_forward_mx4",
-            "moe_experts_mx4", "moe_status_string", "moe_last_error", "moe_stage_events")
+            "moe_experts_mx4", "moe_rmsnorm", "moe_forward_prenorm", "moe_status_string",
+            "moe_last_error", "moe_stage_events")
+MOE_WEIGHTS_DTYPE, MOE_WEIGHTS_MX4 = 0, 1
 
 
 class MoEError(RuntimeError):
@@ -50,7 +52,8 @@ class moe_desc(ctypes.Structure):
 
 class moe_workspace_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("logits", "gate", "counts", "offsets", "perm", "h", "h_shared", "y", "total")]
+                ("logits", "gate", "counts", "offsets", "perm", "h", "h_shared", "y", "xnorm",
+                 "total")]
 
 
 _lib = None
@@ -78,8 +81,12 @@ def lib():
     L.moe_mx4_packed_bytes.argtypes = [i64, i64]
     L.moe_mx4_packed_bytes.restype = sz
     L.moe_mx4_pack.argtypes = [vp, vp, i64, i64, vp, vp]
+    L.moe_rmsnorm.argtypes = [dp, i64, vp, vp, ctypes.c_float, vp, vp]
+    L.moe_forward_prenorm.argtypes = [dp, i64, vp, vp, ctypes.c_float, ctypes.c_int32] + \
+        L.moe_forward.argtypes[3:]
     for f in (L.moe_workspace_query, L.moe_route, L.moe_forward, L.moe_experts,
-              L.moe_forward_mx4, L.moe_experts_mx4, L.moe_mx4_pack):
+              L.moe_forward_mx4, L.moe_experts_mx4, L.moe_mx4_pack, L.moe_rmsnorm,
+              L.moe_forward_prenorm):
         f.restype = ctypes.c_int
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
@@ -367,16 +374,69 @@ def experts_mx4(x, gu, dn, topk_idx, topk_w, sgu=None, sdn=None, sh_gate=None, o
     return out
 
 
+def rmsnorm(h, norm_weight, eps=1e-6, out=None):
+    """Pre-FFN RMSNorm of h [T, d] (fixed binary32 order, rounded to h's
+    dtype; include/moe.h)."""
+    T, d = h.shape
+    shape = Shape(d, 1, 1, 64, 0, h.dtype)
+    _dev(h, "h"), _dev(norm_weight, "norm_weight", h.dtype, (d,))
+    out = torch.empty_like(h) if out is None else out
+    _dev(out, "out", h.dtype, (T, d))
+    _check(lib().moe_rmsnorm(ctypes.byref(shape.desc()), T, _ptr(h), _ptr(norm_weight),
+                             ctypes.c_float(eps), _ptr(out), _stream()), "moe_rmsnorm")
+    return out
+
+
+def forward_prenorm(h, norm_weight, w_router, w_gate_up, w_down, k, w_sh_gate_up=None,
+                    w_sh_down=None, sh_gate=None, bias=None, eps=1e-6, out=None, topk_idx=None,
+                    topk_w=None, ws=None, router=None):
+    """The layer on RMSNorm(h), one call.  Expert weights are tensors in h's
+    dtype, or MX4Tensor (packed MXFP4).  Returns (out, topk_idx, topk_w)."""
+    T, d = h.shape
+    mx4 = isinstance(w_gate_up, MX4Tensor)
+    if mx4:
+        E, F, Fs = _mx4_dims(d, w_gate_up, w_down, w_sh_gate_up, w_sh_down)
+        shape = Shape(d, E, k, F, Fs, h.dtype, router)
+        ptrs = _mx4_ptrs(w_gate_up, w_down, w_sh_gate_up, w_sh_down)
+    else:
+        shape = shape_of(h, w_gate_up, k, w_sh_gate_up, router)
+        E, F, Fs = shape.n_experts, shape.d_expert, shape.d_shared
+        _dev(w_gate_up, "w_gate_up", h.dtype), _dev(w_down, "w_down", h.dtype, (E, d, F))
+        if Fs:
+            _dev(w_sh_gate_up, "w_sh_gate_up", h.dtype, (2 * Fs, d))
+            _dev(w_sh_down, "w_sh_down", h.dtype, (d, Fs))
+        ptrs = [_ptr(w_gate_up), _ptr(w_down), _ptr(w_sh_gate_up), _ptr(w_sh_down)]
+    _dev(h, "h"), _dev(norm_weight, "norm_weight", h.dtype, (d,))
+    _dev(w_router, "w_router", h.dtype, (E, d)), _dev(bias, "router_bias", torch.float32, (E,))
+    if Fs:
+        _dev(sh_gate, "sh_gate", h.dtype, (d,))
+    out = torch.empty((T, d), dtype=torch.float32, device=h.device) if out is None else out
+    topk_idx = torch.empty((T, k), dtype=torch.int32, device=h.device) if topk_idx is None else topk_idx
+    topk_w = torch.empty((T, k), dtype=torch.float32, device=h.device) if topk_w is None else topk_w
+    _dev(out, "out", torch.float32, (T, d)), _dev(topk_idx, "topk_idx", torch.int32, (T, k))
+    _dev(topk_w, "topk_w", torch.float32, (T, k))
+    ws = alloc_workspace(shape, T, h.device) if ws is None else ws
+    st = lib().moe_forward_prenorm(ctypes.byref(shape.desc()), T, _ptr(h), _ptr(norm_weight),
+                                   ctypes.c_float(eps), MOE_WEIGHTS_MX4 if mx4 else MOE_WEIGHTS_DTYPE,
+                                   _ptr(w_router), _ptr(bias), *ptrs, _ptr(sh_gate), _ptr(out),
+                                   _ptr(topk_idx), _ptr(topk_w), _ptr(ws), ws.numel(), _stream())
+    _check(st, "moe_forward_prenorm")
+    return out, topk_idx, topk_w
+
+
 class MoELayer:
     """Device-resident weights plus a workspace sized for up to ``max_tokens``
     tokens, so repeated calls allocate nothing but their outputs."""
 
     def __init__(self, w_router, w_gate_up, w_down, k, w_sh_gate_up=None, w_sh_down=None,
-                 sh_gate=None, bias=None, max_tokens=1, router=None):
+                 sh_gate=None, bias=None, max_tokens=1, router=None, norm_weight=None,
+                 eps=1e-6):
         self.w = dict(w_router=w_router, w_gate_up=w_gate_up, w_down=w_down,
                       w_sh_gate_up=w_sh_gate_up, w_sh_down=w_sh_down, sh_gate=sh_gate, bias=bias)
         self.k = k
         self.router = router
+        # with norm_weight, calls take the un-normalised rows h (pre-FFN RMSNorm)
+        self.norm_weight, self.eps = norm_weight, eps
         # MXFP4 expert weights: MX4Tensor, or row-major (codes, scales) pairs
         # packed here once
         self.mx4 = isinstance(w_gate_up, (tuple, MX4Tensor))
@@ -396,6 +456,10 @@ class MoELayer:
         if x.shape[0] > self.max_tokens:
             raise ValueError("more tokens than the workspace was sized for")
         w = self.w
+        if self.norm_weight is not None:
+            return forward_prenorm(x, self.norm_weight, w["w_router"], w["w_gate_up"], w["w_down"],
+                                   self.k, w["w_sh_gate_up"], w["w_sh_down"], w["sh_gate"],
+                                   w["bias"], self.eps, out, topk_idx, topk_w, self.ws, self.router)
         fwd = forward_mx4 if self.mx4 else forward
         return fwd(x, w["w_router"], w["w_gate_up"], w["w_down"], self.k, w["w_sh_gate_up"],
                    w["w_sh_down"], w["sh_gate"], w["bias"], out, topk_idx, topk_w, self.ws,

@@ -15,6 +15,9 @@ HIPCC_FLAGS = [
     "-Wall", "-Wno-unused-function",
     # no packed binary32 instructions (v_pk_*_f32) in any generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # binary32 division and square root correctly rounded (the RMSNorm's
+    # fixed evaluation order relies on it; this is also hipcc's default)
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
 ]
 
 

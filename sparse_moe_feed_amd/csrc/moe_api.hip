@@ -63,7 +63,7 @@ moe_status check_T(const moe_desc *desc, int64_t T) {
 
 struct Plan {
     size_t logits, wnorm, gate, counts, offsets, tile_start, tile_group, blk, rank, perm, h, h_shared, y,
-        total;
+        xnorm, total;
     int nblk;
     int max_tiles;
 };
@@ -94,6 +94,7 @@ Plan make_plan(const moe_desc &d, int64_t T) {
     p.h = take((size_t)pairs * d.d_expert * esize);
     p.h_shared = take((size_t)T * d.d_shared * esize);
     p.y = take((size_t)pairs * d.d_model * esize);
+    p.xnorm = take((size_t)T * d.d_model * esize);
     p.total = off;
     return p;
 }
@@ -204,6 +205,56 @@ moe_status check_mx4(const moe_desc *desc, int64_t T) {
     return MOE_OK;
 }
 
+bool eps_ok(float eps) { return eps >= 0.0f && eps <= 3.4e38f; }
+
+// moe_forward / moe_forward_mx4 / moe_forward_prenorm: checks, then
+// [RMSNorm into the workspace,] router, permutation, experts, combine.
+// norm_weight != nullptr selects the pre-norm (x is then h).
+moe_status forward_impl(const moe_desc *desc, int64_t T, const void *x, const void *norm_weight,
+                        float eps, bool mx4, const void *w_router, const float *router_bias,
+                        const void *w_gate_up, const void *w_down, const void *w_sh_gate_up,
+                        const void *w_sh_down, const void *sh_gate, float *out,
+                        int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+                        void *stream) {
+    moe_status st = check_common(desc, T, {x, w_router, w_gate_up, w_down, out, topk_idx, topk_w},
+                                 {router_bias, w_sh_gate_up, w_sh_down, sh_gate}, ws, ws_bytes);
+    if (st != MOE_OK) return st;
+    if (mx4) {
+        st = check_mx4(desc, T);
+        if (st != MOE_OK) return st;
+    }
+    if (T == 0) return MOE_OK;
+    if (desc->d_shared > 0 && (!w_sh_gate_up || !w_sh_down || !sh_gate)) return MOE_ERR_INVALID_ARG;
+    const Plan pl = make_plan(*desc, T);
+    moe::Problem p = make_problem(*desc, T, pl, ws);
+    p.x = norm_weight ? static_cast<const void *>(static_cast<char *>(ws) + pl.xnorm) : x;
+    p.w_router = w_router;
+    p.router_bias = router_bias;
+    p.mx4 = mx4;
+    p.w_gate_up = w_gate_up;
+    p.w_down = w_down;
+    p.w_sh_gate_up = w_sh_gate_up;
+    p.w_sh_down = w_sh_down;
+    p.sh_gate = desc->d_shared > 0 ? sh_gate : nullptr;
+    p.out = out;
+    p.topk_idx = topk_idx;
+    p.topk_w = topk_w;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    mark_stage(0, s);
+    hipError_t err = hipSuccess;
+    if (norm_weight)
+        err = moe::launch_rmsnorm(x, norm_weight, eps, static_cast<char *>(ws) + pl.xnorm, T, p.d,
+                                  p.bf16, s);
+    if (err == hipSuccess) err = moe::launch_router(p, nullptr, s);
+    st = hip_status(err);
+    mark_stage(1, s);
+    if (st != MOE_OK) {
+        g_n_stage_events = 0;
+        return st;
+    }
+    return run_experts(p, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -228,6 +279,7 @@ moe_status moe_workspace_query(const moe_desc *desc, int64_t T, moe_workspace_la
     layout->h = p.h;
     layout->h_shared = p.h_shared;
     layout->y = p.y;
+    layout->xnorm = p.xnorm;
     layout->total = p.total;
     return MOE_OK;
 }
@@ -255,32 +307,9 @@ moe_status moe_forward(const moe_desc *desc, int64_t T, const void *x, const voi
                        const void *w_sh_gate_up, const void *w_sh_down, const void *sh_gate,
                        float *out, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
                        void *stream) {
-    moe_status st = check_common(desc, T, {x, w_router, w_gate_up, w_down, out, topk_idx, topk_w},
-                                 {router_bias, w_sh_gate_up, w_sh_down, sh_gate}, ws, ws_bytes);
-    if (st != MOE_OK || T == 0) return st;
-    if (desc->d_shared > 0 && (!w_sh_gate_up || !w_sh_down || !sh_gate)) return MOE_ERR_INVALID_ARG;
-    const Plan pl = make_plan(*desc, T);
-    moe::Problem p = make_problem(*desc, T, pl, ws);
-    p.x = x;
-    p.w_router = w_router;
-    p.router_bias = router_bias;
-    p.w_gate_up = w_gate_up;
-    p.w_down = w_down;
-    p.w_sh_gate_up = w_sh_gate_up;
-    p.w_sh_down = w_sh_down;
-    p.sh_gate = desc->d_shared > 0 ? sh_gate : nullptr;
-    p.out = out;
-    p.topk_idx = topk_idx;
-    p.topk_w = topk_w;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    mark_stage(0, s);
-    st = hip_status(moe::launch_router(p, nullptr, s));
-    mark_stage(1, s);
-    if (st != MOE_OK) {
-        g_n_stage_events = 0;
-        return st;
-    }
-    return run_experts(p, s);
+    return forward_impl(desc, T, x, nullptr, 0.0f, false, w_router, router_bias, w_gate_up, w_down,
+                        w_sh_gate_up, w_sh_down, sh_gate, out, topk_idx, topk_w, ws, ws_bytes,
+                        stream);
 }
 
 moe_status moe_experts(const moe_desc *desc, int64_t T, const void *x, const void *w_gate_up,
@@ -334,35 +363,41 @@ moe_status moe_forward_mx4(const moe_desc *desc, int64_t T, const void *x, const
                            const void *w_sh_gate_up, const void *w_sh_down, const void *sh_gate,
                            float *out, int32_t *topk_idx, float *topk_w, void *ws,
                            size_t ws_bytes, void *stream) {
-    moe_status st = check_common(desc, T, {x, w_router, w_gate_up, w_down, out, topk_idx, topk_w},
-                                 {router_bias, w_sh_gate_up, w_sh_down, sh_gate}, ws, ws_bytes);
+    return forward_impl(desc, T, x, nullptr, 0.0f, true, w_router, router_bias, w_gate_up, w_down,
+                        w_sh_gate_up, w_sh_down, sh_gate, out, topk_idx, topk_w, ws, ws_bytes,
+                        stream);
+}
+
+moe_status moe_rmsnorm(const moe_desc *desc, int64_t T, const void *h, const void *norm_weight,
+                       float eps, void *x_out, void *stream) {
+    moe_status st = check_desc(desc);
     if (st != MOE_OK) return st;
-    st = check_mx4(desc, T);
+    st = check_T(desc, T);
     if (st != MOE_OK || T == 0) return st;
-    if (desc->d_shared > 0 && (!w_sh_gate_up || !w_sh_down || !sh_gate)) return MOE_ERR_INVALID_ARG;
-    const Plan pl = make_plan(*desc, T);
-    moe::Problem p = make_problem(*desc, T, pl, ws);
-    p.x = x;
-    p.w_router = w_router;
-    p.router_bias = router_bias;
-    p.mx4 = true;
-    p.w_gate_up = w_gate_up;
-    p.w_down = w_down;
-    p.w_sh_gate_up = w_sh_gate_up;
-    p.w_sh_down = w_sh_down;
-    p.sh_gate = desc->d_shared > 0 ? sh_gate : nullptr;
-    p.out = out;
-    p.topk_idx = topk_idx;
-    p.topk_w = topk_w;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    mark_stage(0, s);
-    st = hip_status(moe::launch_router(p, nullptr, s));
-    mark_stage(1, s);
-    if (st != MOE_OK) {
-        g_n_stage_events = 0;
-        return st;
+    if (!h || !norm_weight || !x_out || !all_aligned({h, norm_weight, x_out}) || !eps_ok(eps))
+        return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_rmsnorm(h, norm_weight, eps, x_out, T, desc->d_model,
+                                          desc->dtype == MOE_BF16,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_forward_prenorm(const moe_desc *desc, int64_t T, const void *h,
+                               const void *norm_weight, float eps, int32_t weight_format,
+                               const void *w_router, const float *router_bias,
+                               const void *w_gate_up, const void *w_down,
+                               const void *w_sh_gate_up, const void *w_sh_down, const void *sh_gate,
+                               float *out, int32_t *topk_idx, float *topk_w, void *ws,
+                               size_t ws_bytes, void *stream) {
+    if (weight_format != MOE_WEIGHTS_DTYPE && weight_format != MOE_WEIGHTS_MX4)
+        return MOE_ERR_INVALID_ARG;
+    if (!norm_weight || !aligned16(norm_weight) || !eps_ok(eps)) {
+        // a bad desc is reported first, as everywhere else
+        moe_status st = check_desc(desc);
+        return st != MOE_OK ? st : MOE_ERR_INVALID_ARG;
     }
-    return run_experts(p, s);
+    return forward_impl(desc, T, h, norm_weight, eps, weight_format == MOE_WEIGHTS_MX4, w_router,
+                        router_bias, w_gate_up, w_down, w_sh_gate_up, w_sh_down, sh_gate, out,
+                        topk_idx, topk_w, ws, ws_bytes, stream);
 }
 
 moe_status moe_experts_mx4(const moe_desc *desc, int64_t T, const void *x, const void *w_gate_up,

@@ -89,6 +89,9 @@ hipError_t launch_experts_dma(const Problem &p, int bm, hipStream_t s,
                               const std::function<void(int)> &mark);
 // Router: logits (canonical binary32 order) then top-k / weights / gate.
 hipError_t launch_router(const Problem &p, float *sh_gate_user, hipStream_t s);
+// Pre-FFN RMSNorm of h [T, d] into x (bf16 or binary32), fixed binary32 order.
+hipError_t launch_rmsnorm(const void *h, const void *gamma, float eps, void *x, int64_t T, int d,
+                          bool bf16, hipStream_t s);
 // Shared gate alone (used when the routing is given).
 hipError_t launch_shared_gate(const Problem &p, hipStream_t s);
 // Histogram, scan, stable permutation and GEMM tile map for tile height bm.

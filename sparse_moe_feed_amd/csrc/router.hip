@@ -449,6 +449,67 @@ __global__ __launch_bounds__(256) void shared_gate_kernel(const T *__restrict__ 
     if (lane == 0) gate[t] = 1.0f / (1.0f + expf(-a));
 }
 
+// Pre-FFN RMSNorm, one wave per row (4 rows per block), evaluated in a fixed
+// binary32 order so that the routed bits match the definition's reading:
+// lane j holds partial j of sum h_k^2 exactly as in the router logit
+// (element kk feeds partial (kk mod 512) / 8, ascending kk, fused
+// multiply-adds from +0, then the halving tree); mean = ss / d,
+// v = mean + eps, r = 1 / sqrtf(v) with the division and square root
+// correctly rounded (HIP's default binary32 semantics, which the build keeps);
+// x_k = (h_k r) gamma_k, each product rounded, then rounded to the dtype.
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const T *__restrict__ h,
+                                                      const T *__restrict__ gamma, float eps,
+                                                      T *__restrict__ x, int64_t ntok, int d) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= ntok) return;
+    const T *hr = h + t * d;
+    T *xr = x + t * d;
+    const bool vec = (d % 8) == 0;
+    float acc = 0.0f;
+    for (int c = 0; c < d; c += 512) {
+        const int kk0 = c + 8 * lane;
+        if (kk0 >= d) continue;
+        float v[8];
+        if (vec) {
+            load8(hr + kk0, v);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = kk0 + q < d ? to_f32(hr[kk0 + q]) : 0.0f;
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (kk0 + q < d) acc = __builtin_fmaf(v[q], v[q], acc);
+    }
+    for (int s = 32; s >= 1; s >>= 1) {
+        float o = __shfl_down(acc, s, kWave);
+        acc = acc + o;
+    }
+    const float ss = __shfl(acc, 0, kWave);
+    const float mean = ss / (float)d;
+    const float r = 1.0f / sqrtf(mean + eps);
+    for (int kk = lane; kk < d; kk += 64) {
+        const float xv = (to_f32(hr[kk]) * r) * to_f32(gamma[kk]);
+        if constexpr (sizeof(T) == 2) xr[kk] = f32_to_bf16_rne(xv);
+        else xr[kk] = xv;
+    }
+}
+
+hipError_t launch_rmsnorm(const void *h, const void *gamma, float eps, void *x, int64_t T, int d,
+                          bool bf16, hipStream_t s) {
+    const dim3 grid((unsigned)((T + 3) / 4)), block(256);
+    if (bf16)
+        hipLaunchKernelGGL((rmsnorm_kernel<uint16_t>), grid, block, 0, s,
+                           static_cast<const uint16_t *>(h), static_cast<const uint16_t *>(gamma),
+                           eps, static_cast<uint16_t *>(x), T, d);
+    else
+        hipLaunchKernelGGL((rmsnorm_kernel<float>), grid, block, 0, s,
+                           static_cast<const float *>(h), static_cast<const float *>(gamma), eps,
+                           static_cast<float *>(x), T, d);
+    return hipGetLastError();
+}
+
 // Few tokens: one row per wave (more blocks in flight); many: four.
 template <typename T>
 static hipError_t launch_logits(const Problem &p, hipStream_t s) {

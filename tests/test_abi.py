@@ -195,6 +195,48 @@ def test_mx4_packed_bytes_and_pack_validation(L):
     assert L.moe_mx4_pack(v(FAKE), v(FAKE), 24, 128, v(FAKE), None) == moe.MOE_ERR_INVALID_ARG
 
 
+def test_rmsnorm_validation(L):
+    v = ctypes.c_void_p
+    D = desc()
+    assert L.moe_rmsnorm(ctypes.byref(D), 8, None, v(FAKE), ctypes.c_float(1e-6), v(FAKE),
+                         None) == moe.MOE_ERR_INVALID_ARG
+    for eps in (-1.0, float("nan"), float("inf")):
+        assert L.moe_rmsnorm(ctypes.byref(D), 8, v(FAKE), v(FAKE), ctypes.c_float(eps), v(FAKE),
+                             None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_rmsnorm(ctypes.byref(D), 8, v(FAKE + 2), v(FAKE), ctypes.c_float(1e-6),
+                         v(FAKE), None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_rmsnorm(ctypes.byref(D), 0, None, None, ctypes.c_float(1e-6), None,
+                         None) == moe.MOE_OK
+    assert L.moe_rmsnorm(ctypes.byref(desc(E=0)), 8, v(FAKE), v(FAKE), ctypes.c_float(1e-6),
+                         v(FAKE), None) == moe.MOE_ERR_INVALID_ARG
+
+
+def call_prenorm(L, D, T, fmt=0, eps=1e-6, g=FAKE, ws_bytes=1 << 40):
+    v = lambda a: None if a is None else ctypes.c_void_p(a)
+    return L.moe_forward_prenorm(ctypes.byref(D), T, v(FAKE), v(g), ctypes.c_float(eps), fmt,
+                                 v(FAKE), None, v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE),
+                                 v(FAKE), v(FAKE), v(FAKE), v(FAKE), ws_bytes, None)
+
+
+def test_forward_prenorm_validation(L):
+    D = desc()
+    assert call_prenorm(L, D, 8, fmt=2) == moe.MOE_ERR_INVALID_ARG
+    assert call_prenorm(L, D, 8, g=None) == moe.MOE_ERR_INVALID_ARG
+    assert call_prenorm(L, D, 8, eps=-1e-6) == moe.MOE_ERR_INVALID_ARG
+    assert call_prenorm(L, desc(k=0), 8, g=None) == moe.MOE_ERR_INVALID_ARG
+    assert call_prenorm(L, D, 8, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
+    # MXFP4 weights keep their limits
+    assert call_prenorm(L, mx4_desc(), 65, fmt=1) == moe.MOE_ERR_UNSUPPORTED
+    assert call_prenorm(L, mx4_desc(dtype=moe.MOE_F32), 8, fmt=1) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_workspace_has_xnorm_region(L):
+    D = desc()
+    lay = moe.moe_workspace_layout()
+    assert L.moe_workspace_query(ctypes.byref(D), 100, ctypes.byref(lay)) == moe.MOE_OK
+    assert lay.xnorm % 256 == 0 and lay.xnorm + 100 * 256 * 2 <= lay.total
+
+
 def test_status_strings(L):
     for st in range(5):
         assert moe.status_string(st).startswith("MOE_")

@@ -59,6 +59,7 @@ class MoEConfig:
     seed_x: int = 100
     seed_b: int = 1000
     note: str = field(default="", compare=False)
+    prenorm: bool = False           # the layer takes un-normalised rows h (pre-FFN RMSNorm)
 
 
 CONFIGS = {
@@ -74,6 +75,9 @@ CONFIGS = {
                  "router bias making 10 seeded experts take about half of all assignments"),
     6: MoEConfig("decode_T32_mxfp4", 32, 2560, 512, 10, 640, 640, "mxfp4", None, 1, 102, 1002,
                  "decode_T32 with MXFP4 expert weights quantized from the same draws"),
+    7: MoEConfig("decode_T32_prenorm", 32, 2560, 512, 10, 640, 640, "bf16", None, 1, 102, 1002,
+                 "decode_T32 on RMSNorm(h): h = the decode tokens, gamma = 1 + N(0, 0.1^2)",
+                 prenorm=True),
 }
 
 
@@ -218,6 +222,13 @@ def make_layer_mx4(d: int, E: int, F: int, Fs: int, seed: int, with_values: bool
             layer["sdn_values"] = r[2]
         layer["sh_gate"] = _normal(_rng(seed, _G), (d,), WEIGHT_STD, "bf16")
     return layer
+
+
+def make_norm_weight(d: int, dtype: str, seed: int) -> np.ndarray:
+    """RMSNorm weight gamma [d] = 1 + N(0, 0.1^2) (a trained-looking spread
+    around the usual initial value of ones)."""
+    g = (1.0 + 0.1 * _rng(seed, _G, 1).standard_normal(d)).astype(np.float32)
+    return f32_to_bf16_bits(g) if dtype in ("bf16", "mxfp4") else g
 
 
 def make_x(T: int, d: int, dtype: str, seed: int, row0: int = 0) -> np.ndarray:
