@@ -467,6 +467,46 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T *__restrict__ h,
     const T *hr = h + t * d;
     T *xr = x + t * d;
     const bool vec = (d % 8) == 0;
+    if (vec && d <= 512 * kMaxChunks) {
+        // the whole row and gamma in registers: one load round trip, vector stores
+        float v[kMaxChunks][8], gw[kMaxChunks][8];
+        float acc = 0.0f;
+#pragma unroll
+        for (int c = 0; c < kMaxChunks; ++c) {
+            const int kk0 = 512 * c + 8 * lane;
+            if (kk0 < d) {
+                load8(hr + kk0, v[c]);
+                load8(gamma + kk0, gw[c]);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kMaxChunks; ++c)
+            if (512 * c + 8 * lane < d)
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc = __builtin_fmaf(v[c][q], v[c][q], acc);
+        for (int s = 32; s >= 1; s >>= 1) {
+            float o = __shfl_down(acc, s, kWave);
+            acc = acc + o;
+        }
+        const float r = 1.0f / sqrtf(__shfl(acc, 0, kWave) / (float)d + eps);
+#pragma unroll
+        for (int c = 0; c < kMaxChunks; ++c) {
+            const int kk0 = 512 * c + 8 * lane;
+            if (kk0 >= d) continue;
+            float o[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) o[q] = (v[c][q] * r) * gw[c][q];
+            if constexpr (sizeof(T) == 2) {
+                *reinterpret_cast<uint4 *>(xr + kk0) =
+                    make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                               pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7]));
+            } else {
+                *reinterpret_cast<float4 *>(xr + kk0) = make_float4(o[0], o[1], o[2], o[3]);
+                *reinterpret_cast<float4 *>(xr + kk0 + 4) = make_float4(o[4], o[5], o[6], o[7]);
+            }
+        }
+        return;
+    }
     float acc = 0.0f;
     for (int c = 0; c < d; c += 512) {
         const int kk0 = c + 8 * lane;

@@ -104,3 +104,25 @@ def test_prenorm_full_decode_shape():
     g = W.make_norm_weight(cfg.d, "bf16", 11)
     r = check_prenorm(dict(lay, bias=None), h, g, cfg.k, "prenorm decode_T32")
     announce(f"prenorm decode_T32: max|err|/rms = {r:.3e}")
+
+
+@pytest.mark.parametrize("T", [24, 300])
+def test_prenorm_workspace_rows_bit_exact(T):
+    """The normalised rows the experts read (workspace region xnorm) equal
+    the oracle's bit for bit, in front of the exact router (T = 24) and of
+    the shortlist router (T = 300)."""
+    d, E, k, F, Fs = 256, 16, 4, 128, 64
+    inp = W.small_case(T, d, E, k, F, Fs, "bf16", seed=T)
+    h = rows(T, d, "bf16", T + 1)
+    g = W.make_norm_weight(d, "bf16", 12)
+    shape = moe.Shape(d, E, k, F, Fs, torch.bfloat16)
+    ws = moe.alloc_workspace(shape, T)
+    announce(f"prenorm workspace rows T={T}")
+    moe.forward_prenorm(to_dev(h), to_dev(g), to_dev(inp["w_router"]), to_dev(inp["w_gate_up"]),
+                        to_dev(inp["w_down"]), k, to_dev(inp["w_sh_gate_up"]),
+                        to_dev(inp["w_sh_down"]), to_dev(inp["sh_gate"]), ws=ws)
+    torch.cuda.synchronize()
+    lay = moe.workspace_layout(shape, T)
+    got = ws.cpu().numpy()[lay.xnorm:lay.xnorm + 2 * T * d].view(np.uint16).reshape(T, d)
+    ref = oracle.rmsnorm(h, g, 1e-6)
+    assert int((got != ref).sum()) == 0
