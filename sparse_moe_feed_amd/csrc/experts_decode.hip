@@ -346,17 +346,6 @@ __device__ __forceinline__ void mx4_load_a(Frag (&a)[HALVES], const uint16_t *co
             a[h].v[s] = *reinterpret_cast<const uint4 *>(ap[h] + 128 * g + 8 * s);
 }
 
-// Eight E2M1 codes (one dword, element 2j in the low nibble of byte j) times
-// 2^(X-127), exactly, as bf16 in element order.
-__device__ __forceinline__ bf16x8 mx4_decode8(uint32_t w, float scale) {
-    uint4 r;
-    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
-    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
-    r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
-    r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
-    return __builtin_bit_cast(bf16x8, r);
-}
-
 template <int HALVES>
 __device__ __forceinline__ void mx4_mfma_group(f32x4 (&acc)[HALVES][NB4], const Mx4Group &b,
                                                const Frag (&a)[HALVES]) {

@@ -174,10 +174,10 @@ bool use_dma_path(const moe::Problem &p) {
 
 // Stages 2..5 of a call: permutation, gate/up, down, combine.
 moe_status run_experts(moe::Problem p, hipStream_t s) {
-    const bool decode = p.mx4 || use_decode_path(p);
+    const bool decode = p.mx4 ? p.T * p.k <= (int64_t)16 * p.E : use_decode_path(p);
     const bool dma = !decode && use_dma_path(p);
     // 256-row tiles once experts average 192+ rows
-    const bool big = dma && p.T * p.k >= (int64_t)192 * p.E;
+    const bool big = dma && !p.mx4 && p.T * p.k >= (int64_t)192 * p.E;  // MXFP4 GEMM: 128 rows
     const int bm = decode ? moe::kDecodeBM : big ? moe::kGemm256BM : moe::kGemmBM;
     p.max_tiles = (int)moe::max_gemm_tiles(p.T, p.k, p.E, bm, p.Fs > 0);
     hipError_t err = moe::launch_permute(p, bm, s);
@@ -185,7 +185,8 @@ moe_status run_experts(moe::Problem p, hipStream_t s) {
     auto mark = [&](int i) { mark_stage(i, s); };
     if (err == hipSuccess)
         err = !p.bf16  ? moe::launch_experts_f32(p, s, mark)
-              : p.mx4  ? moe::launch_experts_decode_mx4(p, s, mark)
+              : p.mx4  ? (decode ? moe::launch_experts_decode_mx4(p, s, mark)
+                                 : moe::launch_experts_mx4_gemm(p, s, mark))
               : decode ? moe::launch_experts_decode(p, s, mark)
               : dma    ? moe::launch_experts_dma(p, bm, s, mark)
                        : moe::launch_experts_bf16(p, s, mark);
@@ -195,13 +196,16 @@ moe_status run_experts(moe::Problem p, hipStream_t s) {
     return hip_status(err);
 }
 
-// MXFP4 expert weights: bf16 activations, 128-multiples (the decode
-// kernels' tiling) and the weight-streaming regime (T*k <= 16 E).
+// MXFP4 expert weights: bf16 activations, 128-multiples (the packed tiles)
+// and, for the GEMM path, 32-bit row offsets as use_dma_path.
 moe_status check_mx4(const moe_desc *desc, int64_t T) {
     if (desc->dtype != MOE_BF16 || desc->d_model % 128 || desc->d_expert % 128 ||
         desc->d_shared % 128)
         return MOE_ERR_UNSUPPORTED;
-    if (T * desc->top_k > (int64_t)16 * desc->n_experts) return MOE_ERR_UNSUPPORTED;
+    const int64_t pairs = T * desc->top_k;
+    const int64_t widest = desc->d_model > desc->d_expert ? desc->d_model : desc->d_expert;
+    if (pairs * widest >= ((int64_t)1 << 32) || T * (int64_t)desc->d_model >= ((int64_t)1 << 32))
+        return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 

@@ -50,6 +50,20 @@ __device__ __forceinline__ void load8(const float *p, float v[8]) {
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+// Eight MXFP4 E2M1 codes (one dword, element 2j in the low nibble of byte j)
+// times 2^(X-127), exactly, as bf16 in element order.
+// v_cvt_scalef32_pk_bf16_fp4 reads only the exponent field of its binary32
+// scale operand, so scale byte X is passed as the bits X << 23.
+__device__ __forceinline__ bf16x8 mx4_decode8(uint32_t w, float scale) {
+    uint4 r;
+    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+    r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+    r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+    return __builtin_bit_cast(bf16x8, r);
+}
+__device__ __forceinline__ float mx4_scale(uint32_t x) { return __uint_as_float(x << 23); }
+
 __device__ __forceinline__ float to_f32(uint16_t b) { return bf16_to_f32(b); }
 __device__ __forceinline__ float to_f32(float f) { return f; }
 

@@ -109,6 +109,10 @@ hipError_t launch_experts_decode(const Problem &p, hipStream_t s,
 // registers.
 hipError_t launch_experts_decode_mx4(const Problem &p, hipStream_t s,
                                      const std::function<void(int)> &mark);
+// Grouped GEMM expert stage with packed MXFP4 weights for many rows per expert
+// (128 x 256 tiles, tile map for kGemmBM); d, F, Fs % 128 == 0, 32-bit offsets.
+hipError_t launch_experts_mx4_gemm(const Problem &p, hipStream_t s,
+                                   const std::function<void(int)> &mark);
 // Row-major MXFP4 [rows, K] (codes, scales) -> packed tiles (rows % 16 == 0,
 // K % 128 == 0).
 hipError_t launch_mx4_pack(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t K,

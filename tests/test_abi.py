@@ -158,11 +158,12 @@ def test_mx4_unsupported_shapes(L, bad):
     assert call_forward_mx4(L, mx4_desc(**bad), 0, ws=None, ws_bytes=0) == moe.MOE_ERR_UNSUPPORTED
 
 
-def test_mx4_only_in_weight_streaming_regime(L):
-    """T*k above 16 E (many tokens per expert) is not supported for MXFP4."""
-    D = mx4_desc()                                   # 16 E = 256 -> T <= 64 at k = 4
-    assert call_forward_mx4(L, D, 65) == moe.MOE_ERR_UNSUPPORTED
-    assert call_forward_mx4(L, D, 64, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
+def test_mx4_offset_limit(L):
+    """Batches whose row offsets would not fit 32 bits are refused before
+    any GPU work; smaller ones reach the workspace check."""
+    D = mx4_desc(d=2560, E=512, k=10, F=640, Fs=640)
+    assert call_forward_mx4(L, D, 200000) == moe.MOE_ERR_UNSUPPORTED   # T k d >= 2^32
+    assert call_forward_mx4(L, D, 4096, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
 
 
 def test_mx4_misaligned_and_noop(L):
@@ -179,9 +180,9 @@ def test_mx4_experts_validate(L):
     assert L.moe_experts_mx4(ctypes.byref(D), 8, v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE),
                              v(FAKE), None, v(FAKE), v(FAKE), v(FAKE), 1 << 40,
                              None) == moe.MOE_ERR_INVALID_ARG
-    assert L.moe_experts_mx4(ctypes.byref(D), 100, v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE),
-                             v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE), 1 << 40,
-                             None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_experts_mx4(ctypes.byref(mx4_desc(dtype=moe.MOE_F32)), 8, v(FAKE), v(FAKE),
+                             v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE),
+                             v(FAKE), 1 << 40, None) == moe.MOE_ERR_UNSUPPORTED
 
 
 def test_mx4_packed_bytes_and_pack_validation(L):
@@ -226,7 +227,8 @@ def test_forward_prenorm_validation(L):
     assert call_prenorm(L, desc(k=0), 8, g=None) == moe.MOE_ERR_INVALID_ARG
     assert call_prenorm(L, D, 8, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
     # MXFP4 weights keep their limits
-    assert call_prenorm(L, mx4_desc(), 65, fmt=1) == moe.MOE_ERR_UNSUPPORTED
+    assert call_prenorm(L, mx4_desc(d=2560, E=512, k=10, F=640, Fs=640), 200000,
+                        fmt=1) == moe.MOE_ERR_UNSUPPORTED
     assert call_prenorm(L, mx4_desc(dtype=moe.MOE_F32), 8, fmt=1) == moe.MOE_ERR_UNSUPPORTED
 
 

@@ -125,17 +125,37 @@ def test_mx4_experts_entry_with_given_routing():
     assert_out(out.cpu().numpy(), ref)
 
 
-def test_mx4_deterministic_and_unsupported_regime():
-    T, d, E, k = 24, 256, 16, 4
+@pytest.mark.parametrize("T", [24, 300])
+def test_mx4_deterministic(T):
+    """Both MXFP4 paths (weight streaming at T = 24, the GEMM at T = 300)
+    give the same bits twice."""
+    d, E, k = 256, 16, 4
     inp = small_mx4(T, d, E, k, 128, 128, seed=55)
-    announce("mxfp4 determinism")
+    announce(f"mxfp4 determinism T={T}")
     out1, idx1, _ = gpu_forward_mx4(inp, k)
     out2, idx2, _ = gpu_forward_mx4(inp, k)
     assert np.array_equal(idx1, idx2) and np.array_equal(out1, out2)
-    big = small_mx4(65, d, E, k, 128, 128, seed=56)     # T k > 16 E
-    with pytest.raises(moe.MoEError) as e:
-        gpu_forward_mx4(big, k)
-    assert e.value.status == moe.MOE_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("T,d,E,k,F,Fs", [
+    (65, 256, 16, 4, 128, 128),      # just past the streaming regime: GEMM path
+    (300, 256, 16, 4, 128, 128),     # ~75 rows per expert, 3 shared tiles (one ragged)
+    (500, 384, 16, 3, 256, 128),     # d % 256 = 128: the last down N-tile is half outside d
+    (700, 512, 8, 2, 384, 0),        # experts over 128 rows (two tiles), no shared expert
+    (260, 256, 64, 8, 128, 256),     # Fs > F
+])
+def test_mx4_gemm_layers(T, d, E, k, F, Fs):
+    inp = small_mx4(T, d, E, k, F, Fs, seed=T + d)
+    check_mx4(inp, k, f"mxfp4 GEMM T={T} d={d} E={E} k={k} F={F} Fs={Fs}")
+
+
+def test_mx4_gemm_bias_sends_every_token_to_one_expert():
+    """All 400 tokens pick expert 5 first: one group of four 128-row tiles."""
+    T, d, E, k, F = 400, 256, 16, 2, 128
+    inp = small_mx4(T, d, E, k, F, F, seed=82)
+    inp["bias"] = np.zeros(E, np.float32)
+    inp["bias"][5] = 100.0
+    check_mx4(inp, k, "mxfp4 GEMM bias -> expert 5")
 
 
 def test_mx4_zero_tokens():
@@ -143,6 +163,27 @@ def test_mx4_zero_tokens():
     announce("mxfp4 T=0")
     out, idx, _ = gpu_forward_mx4(inp, 2)
     assert out.shape == (0, 256) and idx.shape == (0, 2)
+
+
+def test_full_prefill_mx4_sampled():
+    """Pages' shapes with MXFP4 weights at T = 4096 (GEMM path): every
+    token's topk_idx bit-exact; out of 48 sampled tokens against the oracle."""
+    cfg = W.CONFIGS[8]
+    lay = W.layer_for(cfg)
+    x = W.make_x(cfg.T, cfg.d, cfg.dtype, cfg.seed_x)
+    announce(f"{cfg.name}: GPU forward")
+    out, idx, w = gpu_forward_mx4(dict(lay, x=x, bias=None), cfg.k)
+    announce(f"{cfg.name}: oracle routing of all {cfg.T} tokens")
+    ref_idx, ref_w = oracle.route(x, lay["w_router"], cfg.k)
+    assert np.array_equal(idx, ref_idx)
+    assert np.abs(w - ref_w).max() <= W_TOL
+    toks = np.unique(np.concatenate([[0, cfg.T - 1],
+                                     np.random.default_rng(8).choice(cfg.T, 46, replace=False)]))
+    announce(f"{cfg.name}: oracle forward of {len(toks)} sampled tokens")
+    ref, _, _, _ = oracle.forward_mx4(np.ascontiguousarray(x[toks]), lay["w_router"], lay["gu"],
+                                      lay["dn"], cfg.k, lay["sgu"], lay["sdn"], lay["sh_gate"])
+    r = assert_out(out[toks], ref)
+    announce(f"{cfg.name}: max|err|/rms = {r:.3e}")
 
 
 def test_full_config_mx4():

@@ -75,6 +75,8 @@ CONFIGS = {
                  "router bias making 10 seeded experts take about half of all assignments"),
     6: MoEConfig("decode_T32_mxfp4", 32, 2560, 512, 10, 640, 640, "mxfp4", None, 1, 102, 1002,
                  "decode_T32 with MXFP4 expert weights quantized from the same draws"),
+    8: MoEConfig("prefill_T4096_mxfp4", 4096, 2560, 512, 10, 640, 640, "mxfp4", None, 1, 103, 1003,
+                 "prefill_T4096 with MXFP4 expert weights quantized from the same draws"),
     7: MoEConfig("decode_T32_prenorm", 32, 2560, 512, 10, 640, 640, "bf16", None, 1, 102, 1002,
                  "decode_T32 on RMSNorm(h): h = the decode tokens, gamma = 1 + N(0, 0.1^2)",
                  prenorm=True),
