@@ -189,10 +189,12 @@ moe_status moe_experts(const moe_desc *desc, int64_t T, const void *x,
  * tensors, in this form: w_gate_up [E*2F, d], w_down [E*d, F], w_sh_gate_up
  * [2Fs, d], w_sh_down [d, Fs] (experts stacked along the rows).
  *
- * Supported: d, F and Fs multiples of 128 and T*k <= 16*E (the
- * weight-streaming regime of few tokens per expert, e.g. decode); otherwise
- * MOE_ERR_UNSUPPORTED, before any GPU work.  Scale byte 255 (NaN) gives
- * unspecified results.  Errors as for moe_forward.
+ * Supported: d, F and Fs multiples of 128, and T*k*max(d, F) and T*d below
+ * 2^32; otherwise MOE_ERR_UNSUPPORTED, before any GPU work.  Up to 16 rows
+ * per expert on average (T*k <= 16*E, e.g. decode) the weights are streamed
+ * straight into registers; above that a grouped GEMM stages the packed tiles
+ * in LDS and decodes them there.  Scale byte 255 (NaN) gives unspecified
+ * results.  Errors as for moe_forward.
  * --------------------------------------------------------------------------- */
 
 /* Bytes of the packed form of an [R, K] MXFP4 tensor (0 unless R > 0,
