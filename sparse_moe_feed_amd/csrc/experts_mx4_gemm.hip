@@ -88,29 +88,43 @@ struct XFrags {
     bf16x8 a[XMI], b[XNB];
 };
 
+// Codes and scale of the odd sub-step, kept from the even one: both read the
+// same 16-byte chunk and scale byte.
+struct XCarry {
+    uint32_t w[XNB], x[XNB];
+};
+
 // Fragments of k16 sub-step ks: lane half h takes k = 16 ks + 8 h .. + 7 of
 // its A row and of its B row (weight row n = brow + lane % 32: tile n / 16,
 // row n % 16; those 8 codes are bytes 8 (ks & 1) + 4 h .. + 3 of chunk ks / 2).
 template <int MACT>
 __device__ __forceinline__ void x_read_frags(const unsigned char *stage, int ks, int wm,
                                              const int (&brow)[XNB], int fr, int half,
-                                             XFrags &f) {
+                                             XFrags &f, XCarry &cr) {
     if (MACT == 0) return;
 #pragma unroll
     for (int mi = 0; mi < MACT; ++mi)
         f.a[mi] = *reinterpret_cast<const bf16x8 *>(stage + a_off(XBM / 2 * wm + 32 * mi + fr,
                                                                   2 * ks + half));
-    const int c = ks >> 1, j0 = 8 * (ks & 1) + 4 * half;
+    const int c = ks >> 1;
 #pragma unroll
     for (int ni = 0; ni < XNB; ++ni) {
-        const int n = brow[ni] + fr, tb = n >> 4, r = n & 15;
-        // the whole 16-byte chunk, then its dword: a 4-byte LDS read here makes
-        // the compiler wait for every direct-to-LDS load in flight
-        const uint4 q4 =
-            *reinterpret_cast<const uint4 *>(stage + X_CODES + tb * 1024 + 16 * (r + 16 * c));
-        const int wsel = j0 >> 2;
-        const uint32_t w = wsel == 0 ? q4.x : wsel == 1 ? q4.y : wsel == 2 ? q4.z : q4.w;
-        const uint32_t x = stage[X_SCALES + 64 * tb + r + 16 * c];
+        uint32_t w, x;
+        if ((ks & 1) == 0) {
+            const int n = brow[ni] + fr, tb = n >> 4, r = n & 15;
+            // the whole 16-byte chunk (a 4-byte LDS read here makes the compiler
+            // wait for every direct-to-LDS load in flight): dword half now,
+            // dword 2 + half for the odd sub-step
+            const uint4 q4 =
+                *reinterpret_cast<const uint4 *>(stage + X_CODES + tb * 1024 + 16 * (r + 16 * c));
+            x = stage[X_SCALES + 64 * tb + r + 16 * c];
+            w = half ? q4.y : q4.x;
+            cr.w[ni] = half ? q4.w : q4.z;
+            cr.x[ni] = x;
+        } else {
+            w = cr.w[ni];
+            x = cr.x[ni];
+        }
         f.b[ni] = mx4_decode8(w, mx4_scale(x));
     }
 }
@@ -128,10 +142,10 @@ __device__ __forceinline__ void x_mfma(const XFrags &f, f32x16 (&acc)[XMI][XNB])
 template <int MACT>
 __device__ __forceinline__ void x_sub(const unsigned char *stage, int ks, int wm,
                                       const int (&brow)[XNB], int fr, int half, const XFrags &cur,
-                                      XFrags &nxt, f32x16 (&acc)[XMI][XNB]) {
+                                      XFrags &nxt, XCarry &cr, f32x16 (&acc)[XMI][XNB]) {
     if (MACT > 0) {
         x_mfma<MACT>(cur, acc);
-        x_read_frags<MACT>(stage, ks, wm, brow, fr, half, nxt);
+        x_read_frags<MACT>(stage, ks, wm, brow, fr, half, nxt, cr);
     }
     __builtin_amdgcn_sched_barrier(0);
 }
@@ -139,11 +153,11 @@ __device__ __forceinline__ void x_sub(const unsigned char *stage, int ks, int wm
 // Sub-steps QQ .. XQ - 1 of one stage, fragments alternating between a and b.
 template <int MACT, int QQ>
 __device__ __forceinline__ void x_subs(const unsigned char *stage, int wm, const int (&brow)[XNB],
-                                       int fr, int half, XFrags &a, XFrags &b,
+                                       int fr, int half, XFrags &a, XFrags &b, XCarry &cr,
                                        f32x16 (&acc)[XMI][XNB]) {
     if constexpr (QQ < XQ) {
-        x_sub<MACT>(stage, QQ, wm, brow, fr, half, a, b, acc);
-        x_subs<MACT, QQ + 1>(stage, wm, brow, fr, half, b, a, acc);
+        x_sub<MACT>(stage, QQ, wm, brow, fr, half, a, b, cr, acc);
+        x_subs<MACT, QQ + 1>(stage, wm, brow, fr, half, b, a, cr, acc);
     }
 }
 
@@ -155,28 +169,29 @@ __device__ __forceinline__ void x_subs(const unsigned char *stage, int wm, const
 template <int MACT, int S>
 __device__ __forceinline__ void x_step(const XStages &st, int kt, int last, const uint16_t *abase,
                                        const XAddr &ad, int wave, int wm, const int (&brow)[XNB],
-                                       int fr, int half, XFrags &f0, XFrags &f1,
+                                       int fr, int half, XFrags &f0, XFrags &f1, XCarry &cr,
                                        f32x16 (&acc)[XMI][XNB]) {
-    x_subs<MACT, 1>(st.s[S], wm, brow, fr, half, f0, f1, acc);
+    x_subs<MACT, 1>(st.s[S], wm, brow, fr, half, f0, f1, cr, acc);
     xfence();
     __builtin_amdgcn_s_waitcnt(xvmcnt_lgkm0_imm((XNS - 2) * X_LOADS));
     __builtin_amdgcn_s_barrier();
     xfence();
     x_dma_stage(st.s[S], abase, ad, min(kt + XNS, last), wave);
     __builtin_amdgcn_sched_barrier(0);
-    x_sub<MACT>(st.s[(S + 1) % XNS], 0, wm, brow, fr, half, f1, f0, acc);
+    x_sub<MACT>(st.s[(S + 1) % XNS], 0, wm, brow, fr, half, f1, f0, cr, acc);
 }
 
 template <int MACT, int S>
 __device__ __forceinline__ void x_steps(const XStages &st, int kt, int cnt, int last,
                                         const uint16_t *abase, const XAddr &ad, int wave, int wm,
                                         const int (&brow)[XNB], int fr, int half, XFrags &f0,
-                                        XFrags &f1, f32x16 (&acc)[XMI][XNB]) {
+                                        XFrags &f1, XCarry &cr, f32x16 (&acc)[XMI][XNB]) {
     if constexpr (S < XNS) {
         if (S < cnt) {
-            x_step<MACT, S>(st, kt + S, last, abase, ad, wave, wm, brow, fr, half, f0, f1, acc);
+            x_step<MACT, S>(st, kt + S, last, abase, ad, wave, wm, brow, fr, half, f0, f1, cr,
+                            acc);
             x_steps<MACT, S + 1>(st, kt, cnt, last, abase, ad, wave, wm, brow, fr, half, f0, f1,
-                                 acc);
+                                 cr, acc);
         }
     }
 }
@@ -193,11 +208,12 @@ __device__ __forceinline__ void x_loop(const XStages &st, const uint16_t *abase,
     __builtin_amdgcn_s_barrier();
     xfence();
     XFrags f0, f1;
-    x_read_frags<MACT>(st.s[0], 0, wm, brow, fr, half, f0);
+    XCarry cr;
+    x_read_frags<MACT>(st.s[0], 0, wm, brow, fr, half, f0, cr);
     int kt = 0;
     for (; kt + XNS <= nk; kt += XNS)
-        x_steps<MACT, 0>(st, kt, XNS, last, abase, ad, wave, wm, brow, fr, half, f0, f1, acc);
-    x_steps<MACT, 0>(st, kt, nk - kt, last, abase, ad, wave, wm, brow, fr, half, f0, f1, acc);
+        x_steps<MACT, 0>(st, kt, XNS, last, abase, ad, wave, wm, brow, fr, half, f0, f1, cr, acc);
+    x_steps<MACT, 0>(st, kt, nk - kt, last, abase, ad, wave, wm, brow, fr, half, f0, f1, cr, acc);
     xfence();
     __builtin_amdgcn_s_waitcnt(xvmcnt_imm(0));  // no load may land after the block ends
     __builtin_amdgcn_s_barrier();
