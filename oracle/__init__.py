@@ -22,6 +22,11 @@ What each function follows (pages cited by title and section):
     "Key facts" Norm, "Raw config fields" rms_norm_eps), read as a pre-norm
     whose binary32 evaluation order is fixed so both sides route on the same
     normalised bits.
+  * ``backward`` -- the layer's gradients with the routing given, and the
+    router's auxiliary load-balancing loss, whose coefficient (0.001) is the
+    only thing the pages state about it (llm-atlas "Qwen3.8-Flash-Next",
+    "Raw config fields", router_aux_loss_coef); the formula is read as
+    coef * E * sum_e f_e P_e (share of assignments times mean probability).
   * ``experts_mx4`` / ``forward_mx4`` / ``mx4_decode`` -- the same layer with
     low-bit expert weights.  The published weights are packed low-bit tensors
     (llm-atlas "Qwen3.8-Flash-Next", "Modelled costs"); the encoding is not
@@ -79,9 +84,12 @@ def _load():
     lib.oracle_forward_mx4.argtypes = [i64, i32, i32, i32, i32, i32] + [vp] * 16
     lib.oracle_mx4_decode.argtypes = [i64, i64, vp, vp, vp]
     lib.oracle_rmsnorm.argtypes = [i64, i32, i32, vp, vp, ctypes.c_float, vp]
+    lib.oracle_backward.argtypes = ([i64, i32, i32, i32, i32, i32, i32] + [vp] * 11
+                                    + [ctypes.c_double, i32, vp, i64, vp] + [vp] * 8)
     for f in (lib.oracle_router_logits, lib.oracle_route, lib.oracle_experts,
               lib.oracle_forward, lib.oracle_threads, lib.oracle_experts_mx4,
-              lib.oracle_forward_mx4, lib.oracle_mx4_decode, lib.oracle_rmsnorm):
+              lib.oracle_forward_mx4, lib.oracle_mx4_decode, lib.oracle_rmsnorm,
+              lib.oracle_backward):
         f.restype = ctypes.c_int
     lib.oracle_threads.argtypes = []
     _lib = lib
@@ -301,3 +309,54 @@ def rmsnorm(h, gamma, eps=1e-6):
     if rc:
         raise RuntimeError(f"oracle_rmsnorm failed ({rc})")
     return out
+
+
+DX, DW_ROUTED, DW_SHARED, DW_ROUTER = 1, 2, 4, 8
+
+
+def backward(x, w_router, w_gate_up, w_down, topk_idx, topk_w, dout, w_sh_gate_up=None,
+             w_sh_down=None, sh_gate=None, bias=None, aux_coef=0.0,
+             parts=DX | DW_ROUTED | DW_SHARED | DW_ROUTER, tokens=None, experts=None):
+    """Gradients of sum(dout * out) + aux_coef * E * sum_e f_e P_e with the
+    routing (topk_idx, topk_w) given, in float64.  Returns a dict with dx
+    [T,d], dw_router [E,d], dw_gate_up [E,2F,d], dw_down [E,d,F],
+    dw_sh_gate_up [2Fs,d], dw_sh_down [d,Fs], dsh_gate [d] and aux_loss.
+    parts / tokens / experts restrict the work (dx of the listed tokens, the
+    routed weight gradients of the listed experts); what is not computed is
+    NaN."""
+    T, d = x.shape
+    E, twoF, _ = w_gate_up.shape
+    F = twoF // 2
+    Fs = 0 if w_sh_gate_up is None else w_sh_gate_up.shape[0] // 2
+    k = topk_idx.shape[1]
+    dt = _dtype_code(x)
+    _same(dt, w_router, w_gate_up, w_down, w_sh_gate_up, w_sh_down, sh_gate)
+    b = _bias(bias, E)
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    w = np.ascontiguousarray(topk_w, dtype=np.float64)
+    g = np.ascontiguousarray(dout, dtype=np.float64)
+    if g.shape != (T, d) or idx.shape != (T, k) or w.shape != (T, k):
+        raise ValueError("dout must be [T, d], topk_idx / topk_w [T, k]")
+    tok = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int32)
+    sel = None
+    if experts is not None:
+        sel = np.zeros(E, np.uint8)
+        sel[np.asarray(experts, dtype=np.int64)] = 1
+
+    def nan(*shape):
+        return np.full(shape, np.nan, np.float64)
+    r = dict(dx=nan(T, d), dw_router=nan(E, d), dw_gate_up=nan(E, 2 * F, d),
+             dw_down=nan(E, d, F), dw_sh_gate_up=nan(2 * Fs, d), dw_sh_down=nan(d, Fs),
+             dsh_gate=nan(d))
+    aux = ctypes.c_double(np.nan)
+    rc = _load().oracle_backward(
+        T, d, E, k, F, Fs, dt, _ptr(x), _ptr(w_router), _ptr(b), _ptr(w_gate_up),
+        _ptr(w_down), _ptr(w_sh_gate_up), _ptr(w_sh_down), _ptr(sh_gate), _ptr(idx), _ptr(w),
+        _ptr(g), ctypes.c_double(aux_coef), parts, _ptr(tok), 0 if tok is None else len(tok),
+        _ptr(sel), _ptr(r["dx"]), _ptr(r["dw_router"]), _ptr(r["dw_gate_up"]),
+        _ptr(r["dw_down"]), _ptr(r["dw_sh_gate_up"]), _ptr(r["dw_sh_down"]),
+        _ptr(r["dsh_gate"]), ctypes.byref(aux))
+    if rc:
+        raise RuntimeError(f"oracle_backward failed ({rc})")
+    r["aux_loss"] = aux.value
+    return r

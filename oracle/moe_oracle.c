@@ -53,6 +53,16 @@
  *     * gamma.  Because the normalised x feeds the integer top-k decision,
  *     it is evaluated in one fixed binary32 order (below) and rounded to the
  *     layer's dtype, so that both sides route on the same bits.
+ *   - Backward pass (oracle_backward): the training variant of the layer.
+ *     The pages give only the coefficient of the router's auxiliary loss,
+ *     0.001 (llm-atlas "Qwen3.8-Flash-Next", "Raw config fields",
+ *     router_aux_loss_coef), not its formula.  The reading taken is the
+ *     usual load-balancing loss: coef * E * sum_e f_e * P_e, where f_e is
+ *     the share of the T*k routed assignments that went to expert e (a count,
+ *     so it carries no gradient) and P_e the mean over tokens of the router's
+ *     softmax probability of e.  The selection itself is piecewise constant
+ *     and is taken as given; gradients reach the router through the
+ *     normalised weights of the selected experts and through P.
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fopenmp -shared -fPIC
  * (no fast-math: the binary32 router logit must round exactly as written).
@@ -465,6 +475,322 @@ int oracle_forward_mx4(int64_t T, int d, int E, int k, int F, int Fs,
                               dn_codes, dn_scales, sgu_codes, sgu_scales,
                               sdn_codes, sdn_scales, sh_gate, topk_idx, topk_w,
                               out, s_out);
+}
+
+/* ---------------------------------------------------------------------------
+ * Backward pass.
+ *
+ * The scalar being differentiated is
+ *     Lambda = sum_t dout_t . out_t  +  L_aux,
+ *     L_aux  = coef * E * sum_e f_e * P_e,   f_e = c_e / (T k),
+ *     P_e    = (1/T) sum_t p_te,             p_t = softmax over all E of l_t,
+ * with c_e the number of routed assignments (t, j) with idx[t,j] = e.  dout
+ * is the gradient arriving at the layer's output.  The routing idx is an
+ * input (the selection is piecewise constant); the selected weights are
+ * w_tj = softmax over the k selected logits (the normalised probabilities of
+ * the forward pass), given as topk_w.  Everything is binary64, including the
+ * router logits l_te = x_t . W_r[e] + b_e used for p (the selection being
+ * given, no bit-exact order is needed here).
+ *
+ * Per (token t, slot j) with expert e and weight w (chain rule through the
+ * gated MLP, silu(a) = a sigma(a), silu'(a) = sigma(a) (1 + a (1 - sigma(a)))):
+ *     a = W_g,e x_t,  u = W_u,e x_t,  h = silu(a) u,
+ *     G   = W_dn,e^T dout_t                 (F values)
+ *     dw  = G . h                           (dLambda / dw_tj)
+ *     dh  = w G
+ *     da  = dh u silu'(a),   du = dh silu(a)
+ *     dx_t     += W_g,e^T da + W_u,e^T du
+ *     dW_g,e   += da x_t^T,  dW_u,e += du x_t^T,  dW_dn,e += (w dout_t) h^T
+ * The shared expert is the same with w = s_t = sigma(z_t), z_t = g . x_t, and
+ * ds_t = G_sh . h_sh gives dz_t = ds_t s_t (1 - s_t), dg += dz_t x_t,
+ * dx_t += dz_t g.
+ * Router, per token (w = softmax of the selected logits, so its Jacobian is
+ * diag(w) - w w^T on the selected entries and zero elsewhere):
+ *     dl_te  = [e selected as slot j] w_j (dw_j - sum_j' w_j' dw_j')
+ *            + coef (E/T) p_te (f_e - sum_e' f_e' p_te')
+ *     dW_r[e] += dl_te x_t,   dx_t += sum_e dl_te W_r[e]
+ *
+ * parts selects what is computed (the rest of the outputs is left as is):
+ *     1 dx of the tokens in tok_sel (all tokens when tok_sel is NULL)
+ *     2 dW_gu, dW_dn of the experts e with exp_sel[e] != 0 (all when NULL)
+ *     4 dW_sgu, dW_sdn and dsh_gate (shared expert and its gate)
+ *     8 dW_router
+ * aux_loss (nullable) receives L_aux.  Returns 0, 1 on bad arguments, 2 when
+ * out of memory.
+ * ------------------------------------------------------------------------- */
+
+/* Per-pair backward quantities (see above); returns dw = G . h. */
+static double pair_backward(const void *x, int64_t xoff, int dtype,
+                            const wsrc *w_gu, int64_t gu_row, const wsrc *w_dn,
+                            int64_t dn_row, int d, int F, const double *dout_t,
+                            double w, double *h, double *da, double *du)
+{
+    double dw = 0.0;
+    for (int n = 0; n < F; n++) {
+        double a = 0.0, u = 0.0, g = 0.0;
+        for (int kk = 0; kk < d; kk++) {
+            double xv = (double)load_elem(x, dtype, xoff + kk);
+            a += load_w(w_gu, gu_row + n, kk) * xv;
+            u += load_w(w_gu, gu_row + F + n, kk) * xv;
+        }
+        for (int m = 0; m < d; m++)
+            g += load_w(w_dn, dn_row + m, n) * dout_t[m];
+        double sg = 1.0 / (1.0 + exp(-a));
+        double silu = a * sg;
+        double dsilu = sg * (1.0 + a * (1.0 - sg));
+        h[n] = silu * u;
+        dw += g * h[n];
+        double dh = w * g;
+        da[n] = dh * u * dsilu;
+        du[n] = dh * silu;
+    }
+    return dw;
+}
+
+int oracle_backward(int64_t T, int d, int E, int k, int F, int Fs, int dtype,
+                    const void *x, const void *w_router, const float *bias,
+                    const void *w_gate_up, const void *w_down,
+                    const void *w_sh_gate_up, const void *w_sh_down,
+                    const void *sh_gate, const int32_t *topk_idx,
+                    const double *topk_w, const double *dout, double coef,
+                    int parts, const int32_t *tok_sel, int64_t n_tok_sel,
+                    const uint8_t *exp_sel, double *dx, double *dw_router,
+                    double *dw_gu, double *dw_dn, double *dw_sgu,
+                    double *dw_sdn, double *dsh_gate, double *aux_loss)
+{
+    if (T < 1 || d < 1 || E < 1 || k < 1 || k > E || F < 1 || Fs < 0 || !x ||
+        !w_router || !w_gate_up || !w_down || !topk_idx || !topk_w || !dout)
+        return 1;
+    if (Fs > 0 && (!w_sh_gate_up || !w_sh_down || !sh_gate))
+        return 1;
+    if (((parts & 1) && !dx) || ((parts & 2) && (!dw_gu || !dw_dn)) ||
+        ((parts & 4) && Fs > 0 && (!dw_sgu || !dw_sdn || !dsh_gate)) ||
+        ((parts & 8) && !dw_router))
+        return 1;
+    for (int64_t i = 0; i < T * k; i++)
+        if (topk_idx[i] < 0 || topk_idx[i] >= E)
+            return 1;
+    if (tok_sel)
+        for (int64_t i = 0; i < n_tok_sel; i++)
+            if (tok_sel[i] < 0 || tok_sel[i] >= T)
+                return 1;
+    const int64_t P = T * k;
+    wsrc gu = {dtype, w_gate_up, NULL, d}, dn = {dtype, w_down, NULL, F};
+    wsrc sgu = {dtype, w_sh_gate_up, NULL, d}, sdn = {dtype, w_sh_down, NULL, Fs};
+
+    /* which tokens and pairs need their per-pair quantities */
+    uint8_t *tok_need = (uint8_t *)calloc((size_t)T, 1);
+    uint8_t *pair_need = (uint8_t *)calloc((size_t)P, 1);
+    double *f = (double *)calloc((size_t)E, sizeof(double));
+    double *h = (double *)malloc(sizeof(double) * (size_t)(P * F));
+    double *da = (double *)malloc(sizeof(double) * (size_t)(P * F));
+    double *du = (double *)malloc(sizeof(double) * (size_t)(P * F));
+    double *dwp = (double *)calloc((size_t)P, sizeof(double));
+    int sh = Fs > 0;
+    double *hs = sh ? (double *)malloc(sizeof(double) * (size_t)(T * Fs)) : NULL;
+    double *das = sh ? (double *)malloc(sizeof(double) * (size_t)(T * Fs)) : NULL;
+    double *dus = sh ? (double *)malloc(sizeof(double) * (size_t)(T * Fs)) : NULL;
+    double *sv = sh ? (double *)calloc((size_t)T, sizeof(double)) : NULL;
+    double *dl = (double *)calloc((size_t)(T * (E + 1)), sizeof(double));
+    double *pt = (double *)calloc((size_t)(T * E), sizeof(double));
+    int fail = !tok_need || !pair_need || !f || !h || !da || !du || !dwp || !dl ||
+               !pt || (sh && (!hs || !das || !dus || !sv));
+    if (fail)
+        goto done;
+
+    if (parts & 8)
+        memset(tok_need, 1, (size_t)T);
+    if (parts & 1) {
+        if (tok_sel)
+            for (int64_t i = 0; i < n_tok_sel; i++)
+                tok_need[tok_sel[i]] = 1;
+        else
+            memset(tok_need, 1, (size_t)T);
+    }
+    for (int64_t i = 0; i < P; i++) {
+        int e = topk_idx[i];
+        f[e] += 1.0; /* count first, divide once below */
+        if (tok_need[i / k] || ((parts & 2) && (!exp_sel || exp_sel[e])))
+            pair_need[i] = 1;
+    }
+    for (int e = 0; e < E; e++)
+        f[e] /= (double)P;
+
+    /* phase 1: per-pair, per-token quantities */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < P; i++) {
+        if (!pair_need[i])
+            continue;
+        int64_t t = i / k;
+        int e = topk_idx[i];
+        dwp[i] = pair_backward(x, t * d, dtype, &gu, (int64_t)e * 2 * F, &dn,
+                               (int64_t)e * d, d, F, dout + t * d, topk_w[i],
+                               h + i * F, da + i * F, du + i * F);
+    }
+    int shared_all = sh && (parts & 4);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; t++) {
+        int need_sh = sh && (tok_need[t] || shared_all);
+        double s = 0.0, dsv = 0.0;
+        if (need_sh) {
+            s = shared_gate(x, t * d, sh_gate, d, dtype);
+            sv[t] = s;
+            dsv = pair_backward(x, t * d, dtype, &sgu, 0, &sdn, 0, d, Fs, dout + t * d,
+                                s, hs + t * Fs, das + t * Fs, dus + t * Fs);
+            dl[t * (E + 1) + E] = dsv * s * (1.0 - s);
+        }
+        /* router: binary64 logits, softmax over all E */
+        double *p = pt + t * E;
+        double m = -INFINITY;
+        for (int e = 0; e < E; e++) {
+            double l = bias ? (double)bias[e] : 0.0;
+            for (int kk = 0; kk < d; kk++)
+                l += (double)load_elem(x, dtype, t * d + kk) *
+                     (double)load_elem(w_router, dtype, (int64_t)e * d + kk);
+            p[e] = l;
+            if (l > m)
+                m = l;
+        }
+        double z = 0.0;
+        for (int e = 0; e < E; e++) {
+            p[e] = exp(p[e] - m);
+            z += p[e];
+        }
+        double fp = 0.0;
+        for (int e = 0; e < E; e++) {
+            p[e] /= z;
+            fp += f[e] * p[e];
+        }
+        if (!tok_need[t])
+            continue;
+        double *dlt = dl + t * (E + 1);
+        double c = coef * (double)E / (double)T;
+        for (int e = 0; e < E; e++)
+            dlt[e] = c * p[e] * (f[e] - fp);
+        double wdw = 0.0;
+        for (int j = 0; j < k; j++)
+            wdw += topk_w[t * k + j] * dwp[t * k + j];
+        for (int j = 0; j < k; j++)
+            dlt[topk_idx[t * k + j]] += topk_w[t * k + j] * (dwp[t * k + j] - wdw);
+    }
+
+    /* phase 2: the outputs */
+    if (parts & 1) {
+        int64_t n = tok_sel ? n_tok_sel : T;
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t ii = 0; ii < n; ii++) {
+            int64_t t = tok_sel ? tok_sel[ii] : ii;
+            double *o = dx + t * d;
+            const double *dlt = dl + t * (E + 1);
+            for (int kk = 0; kk < d; kk++) {
+                double acc = 0.0;
+                for (int j = 0; j < k; j++) {
+                    int64_t i = t * k + j;
+                    int64_t row = (int64_t)topk_idx[i] * 2 * F;
+                    for (int nn = 0; nn < F; nn++)
+                        acc += load_w(&gu, row + nn, kk) * da[i * F + nn] +
+                               load_w(&gu, row + F + nn, kk) * du[i * F + nn];
+                }
+                if (sh) {
+                    for (int nn = 0; nn < Fs; nn++)
+                        acc += load_w(&sgu, nn, kk) * das[t * Fs + nn] +
+                               load_w(&sgu, Fs + nn, kk) * dus[t * Fs + nn];
+                    acc += dlt[E] * (double)load_elem(sh_gate, dtype, kk);
+                }
+                for (int e = 0; e < E; e++)
+                    acc += dlt[e] * (double)load_elem(w_router, dtype, (int64_t)e * d + kk);
+                o[kk] = acc;
+            }
+        }
+    }
+    if (parts & 2) {
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int e = 0; e < E; e++) {
+            if (exp_sel && !exp_sel[e])
+                continue;
+            double *g = dw_gu + (int64_t)e * 2 * F * d;
+            double *dd = dw_dn + (int64_t)e * d * F;
+            memset(g, 0, sizeof(double) * (size_t)(2 * F * d));
+            memset(dd, 0, sizeof(double) * (size_t)(d * F));
+            for (int64_t i = 0; i < P; i++) {
+                if (topk_idx[i] != e)
+                    continue;
+                int64_t t = i / k;
+                double w = topk_w[i];
+                for (int nn = 0; nn < F; nn++)
+                    for (int kk = 0; kk < d; kk++) {
+                        double xv = (double)load_elem(x, dtype, t * d + kk);
+                        g[(int64_t)nn * d + kk] += da[i * F + nn] * xv;
+                        g[(int64_t)(F + nn) * d + kk] += du[i * F + nn] * xv;
+                    }
+                for (int mm = 0; mm < d; mm++)
+                    for (int nn = 0; nn < F; nn++)
+                        dd[(int64_t)mm * F + nn] += w * dout[t * d + mm] * h[i * F + nn];
+            }
+        }
+    }
+    if ((parts & 4) && sh) {
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int nn = 0; nn < Fs; nn++)
+            for (int kk = 0; kk < d; kk++) {
+                double ag = 0.0, au = 0.0;
+                for (int64_t t = 0; t < T; t++) {
+                    double xv = (double)load_elem(x, dtype, t * d + kk);
+                    ag += das[t * Fs + nn] * xv;
+                    au += dus[t * Fs + nn] * xv;
+                }
+                dw_sgu[(int64_t)nn * d + kk] = ag;
+                dw_sgu[(int64_t)(Fs + nn) * d + kk] = au;
+            }
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int mm = 0; mm < d; mm++) {
+            for (int nn = 0; nn < Fs; nn++) {
+                double acc = 0.0;
+                for (int64_t t = 0; t < T; t++)
+                    acc += sv[t] * dout[t * d + mm] * hs[t * Fs + nn];
+                dw_sdn[(int64_t)mm * Fs + nn] = acc;
+            }
+            double ag = 0.0;
+            for (int64_t t = 0; t < T; t++)
+                ag += dl[t * (E + 1) + E] * (double)load_elem(x, dtype, t * d + mm);
+            dsh_gate[mm] = ag;
+        }
+    }
+    if (parts & 8) {
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int e = 0; e < E; e++)
+            for (int kk = 0; kk < d; kk++) {
+                double acc = 0.0;
+                for (int64_t t = 0; t < T; t++)
+                    acc += dl[t * (E + 1) + e] * (double)load_elem(x, dtype, t * d + kk);
+                dw_router[(int64_t)e * d + kk] = acc;
+            }
+    }
+    if (aux_loss) {
+        double acc = 0.0;
+        for (int e = 0; e < E; e++) {
+            double Pe = 0.0;
+            for (int64_t t = 0; t < T; t++)
+                Pe += pt[t * E + e];
+            acc += f[e] * (Pe / (double)T);
+        }
+        *aux_loss = coef * (double)E * acc;
+    }
+done:
+    free(tok_need);
+    free(pair_need);
+    free(f);
+    free(h);
+    free(da);
+    free(du);
+    free(dwp);
+    free(hs);
+    free(das);
+    free(dus);
+    free(sv);
+    free(dl);
+    free(pt);
+    return fail ? 2 : 0;
 }
 
 /* Number of threads the parallel loops above use. */
