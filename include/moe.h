@@ -264,18 +264,68 @@ moe_status moe_forward_prenorm(const moe_desc *desc, int64_t T, const void *h,
                                const void *sh_gate, float *out, int32_t *topk_idx,
                                float *topk_w, void *ws, size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Backward pass (training).
+ *
+ * Gradients of  Lambda = sum_t dout[t] . out[t] + L_aux  for the layer of
+ * moe_forward with the routing (topk_idx, topk_w) given, as moe_forward
+ * returned it.  The top-k selection is piecewise constant and carries no
+ * gradient; the router is reached through the normalised weights of the
+ * selected experts (w = softmax over the selected logits) and through the
+ * router's auxiliary load-balancing loss.  The pages give only that loss's
+ * coefficient, 0.001 (llm-atlas "Qwen3.8-Flash-Next", "Raw config fields",
+ * router_aux_loss_coef); the loss is read as the usual
+ *   L_aux = aux_coef * E * sum_e f_e * P_e,
+ *   f_e = (number of (t, j) with topk_idx[t,j] = e) / (T k),
+ *   P_e = (1/T) sum_t softmax(l_t)_e   (softmax over all E logits + bias).
+ * aux_coef = 0 gives the plain layer gradient.
+ *
+ * Inputs: the moe_forward operands, topk_idx / topk_w [T,k], dout [T,d]
+ * (binary32, the gradient arriving at out).  The entries of one topk_idx row
+ * must be distinct experts in [0,E) (else the result is undefined; every
+ * access stays in bounds).
+ * Outputs (all overwritten, none may alias an input):
+ *   dx [T,d] binary32;
+ *   dw_router [E,d], dw_gate_up [E,2F,d], dw_down [E,d,F], dw_sh_gate_up
+ *   [2Fs,d], dw_sh_down [d,Fs], dsh_gate [d] in desc->dtype (bfloat16 layers
+ *   round each gradient once to nearest even); the shared ones only with
+ *   d_shared > 0 (else they may be NULL); experts no token chose get zeros;
+ *   aux_loss (nullable, device pointer to one float, 4-byte aligned) = L_aux.
+ * The router bias gets no gradient (it is an input of the workload, not a
+ * weight).  Arithmetic: binary32 accumulation throughout; bfloat16 layers
+ * feed the MFMA with bfloat16 operands (dout and the intermediate gradients
+ * rounded to bfloat16 once).  T == 0 returns MOE_OK and writes nothing.
+ * The workspace (moe_backward_workspace_size bytes) is scratch.
+ * --------------------------------------------------------------------------- */
+size_t moe_backward_workspace_size(const moe_desc *desc, int64_t T);
+
+moe_status moe_backward(const moe_desc *desc, int64_t T, const void *x,
+                        const void *w_router, const float *router_bias,
+                        const void *w_gate_up, const void *w_down,
+                        const void *w_sh_gate_up, const void *w_sh_down,
+                        const void *sh_gate, const int32_t *topk_idx,
+                        const float *topk_w, const float *dout, float aux_coef,
+                        float *dx, void *dw_router, void *dw_gate_up, void *dw_down,
+                        void *dw_sh_gate_up, void *dw_sh_down, void *dsh_gate,
+                        float *aux_loss, void *ws, size_t ws_bytes, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *moe_status_string(moe_status status);
 
 /* Text of the last HIP error seen by this thread ("" if none). */
 const char *moe_last_error(void);
 
-/* Stage timing for benchmarks and profilers.  The NEXT moe_forward or
- * moe_experts call on this thread records events[i] (hipEvent_t, created by
- * the caller) on its stream at stage boundaries, then forgets the array:
+/* Stage timing for benchmarks and profilers.  The NEXT moe_forward,
+ * moe_experts or moe_backward call on this thread records events[i]
+ * (hipEvent_t, created by the caller) on its stream at stage boundaries,
+ * then forgets the array.  Forward:
  *   0 start; 1 after routing (moe_experts: after the shared gate);
  *   2 after the histogram/permutation; 3 after the gate/up GEMM;
  *   4 after the down GEMM; 5 after the combine.
+ * Backward: 0 start; 1 after the permutation and router logits; 2 after the
+ *   gate/up recompute and W_dn^T dout; 3 after the SwiGLU and router
+ *   backward; 4 after dx of the rows; 5 after dW_gate_up; 6 after dW_down;
+ *   7 after the router GEMMs, the dx combine and the loss.
  * n (<= 8) is the number of entries; entries may be NULL.  The events only
  * observe the stream, they change nothing the call computes. */
 moe_status moe_stage_events(void *const *events, int n);

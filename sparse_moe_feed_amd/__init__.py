@@ -32,7 +32,8 @@ ROUTERS = {None: 0, "auto": 0, "exact": MOE_FLAG_ROUTER_EXACT,
 
 EXPORTED = ("moe_workspace_size", "moe_workspace_query", "moe_route", "moe_forward",
             "moe_experts", "moe_mx4_packed_bytes", "moe_mx4_pack", "moe_forward_mx4",
-            "moe_experts_mx4", "moe_rmsnorm", "moe_forward_prenorm", "moe_status_string",
+            "moe_experts_mx4", "moe_rmsnorm", "moe_forward_prenorm",
+            "moe_backward_workspace_size", "moe_backward", "moe_status_string",
             "moe_last_error", "moe_stage_events")
 MOE_WEIGHTS_DTYPE, MOE_WEIGHTS_MX4 = 0, 1
 
@@ -84,9 +85,12 @@ def lib():
     L.moe_rmsnorm.argtypes = [dp, i64, vp, vp, ctypes.c_float, vp, vp]
     L.moe_forward_prenorm.argtypes = [dp, i64, vp, vp, ctypes.c_float, ctypes.c_int32] + \
         L.moe_forward.argtypes[3:]
+    L.moe_backward_workspace_size.argtypes = [dp, i64]
+    L.moe_backward_workspace_size.restype = sz
+    L.moe_backward.argtypes = [dp, i64] + [vp] * 11 + [ctypes.c_float] + [vp] * 8 + [vp, sz, vp]
     for f in (L.moe_workspace_query, L.moe_route, L.moe_forward, L.moe_experts,
               L.moe_forward_mx4, L.moe_experts_mx4, L.moe_mx4_pack, L.moe_rmsnorm,
-              L.moe_forward_prenorm):
+              L.moe_forward_prenorm, L.moe_backward):
         f.restype = ctypes.c_int
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
@@ -283,6 +287,61 @@ def experts(x, w_gate_up, w_down, topk_idx, topk_w, w_sh_gate_up=None, w_sh_down
                            _ptr(topk_w), _ptr(out), _ptr(ws), ws.numel(), _stream())
     _check(st, "moe_experts")
     return out
+
+
+BACKWARD_STAGES = ("logits", "gate_up_g", "swiglu_router", "dx_rows", "dw_gate_up", "dw_down",
+                   "router_combine")
+
+
+def backward_workspace_size(shape: Shape, T: int) -> int:
+    return int(lib().moe_backward_workspace_size(ctypes.byref(shape.desc()), T))
+
+
+def backward(x, w_router, w_gate_up, w_down, topk_idx, topk_w, dout, w_sh_gate_up=None,
+             w_sh_down=None, sh_gate=None, bias=None, aux_coef=0.0, ws=None, grads=None,
+             aux_loss=None):
+    """Gradients of sum(dout * out) + aux_coef * E * sum_e f_e P_e with the
+    routing given.  Returns a dict: dx (float32 [T,d]), dw_router,
+    dw_gate_up, dw_down, dw_sh_gate_up, dw_sh_down, dsh_gate (x.dtype; the
+    shared ones None without a shared expert) and aux_loss (float32 [1]).
+    grads may pass preallocated outputs under the same names."""
+    T, d = x.shape
+    k = topk_idx.shape[1]
+    shape = shape_of(x, w_gate_up, k, w_sh_gate_up)
+    E, F, Fs = shape.n_experts, shape.d_expert, shape.d_shared
+    dt = x.dtype
+    _dev(x, "x"), _dev(w_router, "w_router", dt, (E, d))
+    _dev(w_gate_up, "w_gate_up", dt, (E, 2 * F, d)), _dev(w_down, "w_down", dt, (E, d, F))
+    _dev(topk_idx, "topk_idx", torch.int32, (T, k)), _dev(topk_w, "topk_w", torch.float32, (T, k))
+    _dev(dout, "dout", torch.float32, (T, d)), _dev(bias, "router_bias", torch.float32, (E,))
+    if Fs:
+        _dev(w_sh_gate_up, "w_sh_gate_up", dt, (2 * Fs, d))
+        _dev(w_sh_down, "w_sh_down", dt, (d, Fs)), _dev(sh_gate, "sh_gate", dt, (d,))
+    shapes = dict(dx=((T, d), torch.float32), dw_router=((E, d), dt),
+                  dw_gate_up=((E, 2 * F, d), dt), dw_down=((E, d, F), dt),
+                  dw_sh_gate_up=((2 * Fs, d), dt), dw_sh_down=((d, Fs), dt), dsh_gate=((d,), dt))
+    g = {} if grads is None else dict(grads)
+    for n, (shp, ty) in shapes.items():
+        if Fs == 0 and n in ("dw_sh_gate_up", "dw_sh_down", "dsh_gate"):
+            g[n] = None
+            continue
+        if g.get(n) is None:
+            g[n] = torch.empty(shp, dtype=ty, device=x.device)
+        _dev(g[n], n, ty, shp)
+    aux = torch.empty(1, dtype=torch.float32, device=x.device) if aux_loss is None else aux_loss
+    _dev(aux, "aux_loss", torch.float32, (1,))
+    if ws is None:
+        ws = torch.empty(max(backward_workspace_size(shape, T), 1), dtype=torch.uint8,
+                         device=x.device)
+    st = lib().moe_backward(
+        ctypes.byref(shape.desc()), T, _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w_gate_up),
+        _ptr(w_down), _ptr(w_sh_gate_up), _ptr(w_sh_down), _ptr(sh_gate), _ptr(topk_idx),
+        _ptr(topk_w), _ptr(dout), ctypes.c_float(aux_coef), _ptr(g["dx"]), _ptr(g["dw_router"]),
+        _ptr(g["dw_gate_up"]), _ptr(g["dw_down"]), _ptr(g["dw_sh_gate_up"]),
+        _ptr(g["dw_sh_down"]), _ptr(g["dsh_gate"]), _ptr(aux), _ptr(ws), ws.numel(), _stream())
+    _check(st, "moe_backward")
+    g["aux_loss"] = aux
+    return g
 
 
 @dataclass(frozen=True)

@@ -1,0 +1,766 @@
+// backward.hip -- the layer's backward pass: gradients of every input and
+// weight for a given routing, plus the router's load-balancing loss.
+//
+// The pages give the router's auxiliary-loss coefficient only (llm-atlas
+// "Qwen3.8-Flash-Next", "Raw config fields", router_aux_loss_coef); the loss
+// is read as coef * E * sum_e f_e P_e, with f_e the share of the T*k routed
+// assignments that went to expert e and P_e the mean router probability of e.
+// The scalar differentiated is sum_t dout_t . out_t + L_aux, with the top-k
+// selection held fixed (it is piecewise constant).  Per (token t, slot j)
+// with expert e and routing weight w (experts are gated MLPs with SiLU:
+// llm-architectures-explained "Qwen3.8-Flash-Next", "Every architecture
+// field", ffns.moe.gated):
+//   a, u = W_g x, W_u x;  h = silu(a) u;  G = W_dn^T dout_t;  dw = G . h
+//   dh = w G;  da = dh u silu'(a);  du = dh silu(a)
+//   dx_t += W_gu^T [da; du];  dW_gu += [da; du] x_t^T;  dW_dn += (w dout_t) h^T
+// The shared expert is the same with w = s_t = sigmoid(g . x_t); its gate
+// logit gets ds s (1 - s), ds = G_sh . h_sh.  The router logits get
+//   dl_te = [e = idx_tj] w_j (dw_j - sum_j' w_j' dw_j') + coef (E/T) p_te (f_e - f . p_t)
+// and dW_r = dL^T X, dx += dL W_r (the shared-gate logit rides along as
+// column E, with g as router row E).
+//
+// Launch sequence (bfloat16 layers on MFMA; binary32 layers use the same jobs
+// with a plain FMA kernel):
+//   1. permutation and tile map of the given routing (permute.hip)
+//   2. logits   [T, E+1]  = X [W_r; g]^T                       (binary32)
+//   3. AU       [rows, 2F] = X_gathered W_gu^T  (pre-activations a | u)
+//   4. G        [rows, F]  = dOut_gathered W_dn                 (binary32)
+//   5. SwiGLU backward per row: dGU = [da | du], H = h, dw (pair) or ds (token)
+//   6. router backward per token: dL [T, E+1], q_t = f . p_t
+//   7. dXp      [rows, d]  = dGU W_gu
+//   8. dW_gu,e  = dGU_e^T X_e;   dW_dn,e = (w dOut)_e^T H_e     (K = rows of e)
+//   9. dW_r     = dL^T X;        dXr = dL [W_r; g]
+//  10. dx[t] = sum_j dXp[row(t,j)] + dXs[t] + dXr[t];  L_aux = coef E/T sum_t q_t
+//
+// One grouped-GEMM kernel serves every contraction.  An operand is either
+// contiguous along the reduction axis ("KC", e.g. a weight row of W_gu for
+// X W_gu^T) or along the output axis ("MC", e.g. W_dn read as W_dn^T, or the
+// token-major activations of a weight gradient, whose reduction runs over
+// tokens).  KC tiles go to LDS as they are; MC tiles are transposed on the
+// way through registers (two reduction indices packed per 32-bit LDS write),
+// so the MFMA fragments always read eight consecutive reduction elements.
+#include "moe_device.h"
+#include "moe_kernels.h"
+
+#include <limits.h>
+
+namespace moe {
+
+enum BwdKind { K_LOGITS, K_AU, K_G, K_DX, K_DWGU, K_DWDN, K_DWR, K_DXR };
+
+// Operand source.  The strided index s (the row for KC, the reduction index
+// for MC) runs from `base` to `lim` (absolute); beyond `lim` a KC operand
+// repeats its last row (its output is never stored) and an MC operand reads
+// zeros.  With `map`, source row = map[s] / div and the value is scaled by
+// scale[map[s]]; otherwise row = s and scale[s].  Rows at or past `alt` come
+// from p_alt (row - alt).  MC operands read the columns cb .. cb + 127 of a
+// row (tile-local i < ilim only).
+struct Opnd {
+    const char *p, *p_alt;
+    int64_t ld;          // bytes per row
+    const int32_t *map;
+    int div;
+    const float *scale;
+    int base, lim, alt;
+    int cb, ilim;
+};
+
+// One output tile: rows [0, mrows) x columns [0, ncols) of C at c (row
+// stride ldc; tile rows >= c_alt go to c_alt_p + (row - c_alt) * ldc), K
+// reduction steps of the job.
+struct Job {
+    Opnd a, b;
+    char *c, *c_alt_p;
+    int64_t ldc;
+    int c_alt;
+    int mrows, ncols, K;
+};
+
+constexpr int QB = 128;           // tile rows and columns
+constexpr int QK = 64;            // reduction elements per step
+constexpr int QLD = QK + 8;       // LDS row: 144 bytes
+
+template <int KIND> struct Traits;
+// A_KC / B_KC: operand contiguous along K; *_F32: binary32 source (rounded to
+// bf16 when staged for the MFMA); C_F32: binary32 output (else bf16).
+template <> struct Traits<K_LOGITS> { static constexpr bool A_KC = 1, B_KC = 1, A_F32 = 0, B_F32 = 0, C_F32 = 1; };
+template <> struct Traits<K_AU>     { static constexpr bool A_KC = 1, B_KC = 1, A_F32 = 0, B_F32 = 0, C_F32 = 0; };
+template <> struct Traits<K_G>      { static constexpr bool A_KC = 1, B_KC = 0, A_F32 = 1, B_F32 = 0, C_F32 = 1; };
+template <> struct Traits<K_DX>     { static constexpr bool A_KC = 1, B_KC = 0, A_F32 = 0, B_F32 = 0, C_F32 = 0; };
+template <> struct Traits<K_DWGU>   { static constexpr bool A_KC = 0, B_KC = 0, A_F32 = 0, B_F32 = 0, C_F32 = 0; };
+template <> struct Traits<K_DWDN>   { static constexpr bool A_KC = 0, B_KC = 0, A_F32 = 1, B_F32 = 0, C_F32 = 0; };
+template <> struct Traits<K_DWR>    { static constexpr bool A_KC = 0, B_KC = 0, A_F32 = 0, B_F32 = 0, C_F32 = 0; };
+template <> struct Traits<K_DXR>    { static constexpr bool A_KC = 1, B_KC = 0, A_F32 = 0, B_F32 = 0, C_F32 = 1; };
+
+__device__ __forceinline__ Opnd opnd(const void *p, int64_t ld, int base, int lim, int esize) {
+    Opnd o;
+    o.p = static_cast<const char *>(p);
+    o.p_alt = o.p;
+    o.ld = ld * esize;  // kept in bytes from here on
+    o.map = nullptr;
+    o.div = 1;
+    o.scale = nullptr;
+    o.base = base;
+    o.lim = lim;
+    o.alt = INT_MAX;
+    o.cb = 0;
+    o.ilim = QB;
+    return o;
+}
+
+// Source row of strided index s, and its scale.
+__device__ __forceinline__ const char *op_row(const Opnd &o, int s, float &sc) {
+    int row = s;
+    int si = s;
+    if (o.map) {
+        si = o.map[s];
+        row = si / o.div;
+    }
+    sc = o.scale ? o.scale[si] : 1.0f;
+    return row >= o.alt ? o.p_alt + (int64_t)(row - o.alt) * o.ld : o.p + (int64_t)row * o.ld;
+}
+
+// Tile decode shared by the grouped kinds that follow the permutation's tile
+// map (tiles of QB rows of one group; group E is the shared expert).
+struct MapTile {
+    int g, row0, nrows, Fg;
+    bool shared;
+};
+__device__ __forceinline__ bool map_tile(const BwdArgs &a, int tile, MapTile &t) {
+    if (tile >= a.tile_start[a.E + 1]) return false;
+    t.g = a.tile_group[tile];
+    t.shared = t.g == a.E;
+    const int m_local = (tile - a.tile_start[t.g]) * QB;
+    if (!t.shared) {
+        t.row0 = a.offsets[t.g] + m_local;
+        t.nrows = min(QB, a.counts[t.g] - m_local);
+    } else {
+        t.row0 = m_local;
+        t.nrows = (int)min<int64_t>(QB, a.T - m_local);
+    }
+    t.Fg = t.shared ? a.Fs : a.F;
+    return t.nrows > 0;
+}
+
+// The job of block (bx, by) for a contraction kind; false: nothing to do.
+// esize: bytes per element of the layer's dtype (2 bf16, 4 binary32).
+template <int KIND>
+__device__ bool make_job(const BwdArgs &a, int bx, int by, int es, Job &j) {
+    const int E = a.E, d = a.d;
+    const int sh_rows = a.Fs > 0 ? 1 : 0;  // router row E (the shared gate) exists
+    j.c_alt = INT_MAX;
+    j.c_alt_p = nullptr;
+    if (KIND == K_LOGITS || KIND == K_DXR || KIND == K_DWR) {
+        const int m0 = QB * bx, n0 = QB * by;
+        if (KIND == K_LOGITS) {
+            j.mrows = (int)min<int64_t>(QB, a.T - m0);
+            j.ncols = min(QB, E + sh_rows - n0);
+            j.K = d;
+            j.a = opnd(a.x, d, m0, (int)a.T, es);
+            j.b = opnd(a.w_router, d, n0, E + sh_rows, es);
+            j.b.alt = E;
+            j.b.p_alt = static_cast<const char *>(a.sh_gate ? a.sh_gate : a.w_router);
+            j.c = reinterpret_cast<char *>(a.logits + (int64_t)m0 * a.ldl + n0);
+            j.ldc = (int64_t)a.ldl * 4;
+        } else if (KIND == K_DXR) {
+            j.mrows = (int)min<int64_t>(QB, a.T - m0);
+            j.ncols = min(QB, d - n0);
+            j.K = a.ldd;
+            j.a = opnd(a.dl, a.ldd, m0, (int)a.T, es);
+            j.b = opnd(a.w_router, d, 0, E + sh_rows, es);
+            j.b.alt = E;
+            j.b.p_alt = static_cast<const char *>(a.sh_gate ? a.sh_gate : a.w_router);
+            j.b.cb = n0;
+            j.b.ilim = j.ncols;
+            j.c = reinterpret_cast<char *>(a.dxr + (int64_t)m0 * d + n0);
+            j.ldc = (int64_t)d * 4;
+        } else {  // K_DWR
+            j.mrows = min(QB, E + sh_rows - m0);
+            j.ncols = min(QB, d - n0);
+            j.K = (int)a.T;
+            j.a = opnd(a.dl, a.ldd, 0, (int)a.T, es);
+            j.a.cb = m0;
+            j.a.ilim = min(QB, E + 1 - m0);
+            j.b = opnd(a.x, d, 0, (int)a.T, es);
+            j.b.cb = n0;
+            j.b.ilim = j.ncols;
+            j.c = static_cast<char *>(a.dw_router) + ((int64_t)m0 * d + n0) * es;
+            j.ldc = (int64_t)d * es;
+            if (a.dsh_gate) {
+                j.c_alt = E - m0;
+                j.c_alt_p = static_cast<char *>(a.dsh_gate) + (int64_t)n0 * es;
+            }
+        }
+        return j.mrows > 0 && j.ncols > 0;
+    }
+    if (KIND == K_AU || KIND == K_G || KIND == K_DX) {
+        MapTile t;
+        if (!map_tile(a, bx, t)) return false;
+        const int N = KIND == K_AU ? 2 * t.Fg : KIND == K_G ? t.Fg : d;
+        const int n0 = QB * by;
+        if (n0 >= N) return false;
+        j.mrows = t.nrows;
+        j.ncols = min(QB, N - n0);
+        const int64_t g = t.g;
+        if (KIND == K_AU) {
+            j.K = d;
+            j.a = opnd(a.x, d, t.row0, t.row0 + t.nrows, es);
+            j.b = opnd(t.shared ? a.w_sgu : static_cast<const char *>(a.w_gu) + g * 2 * a.F * d * es,
+                       d, n0, N, es);
+            j.c = static_cast<char *>(t.shared ? a.au_sh : a.au) + ((int64_t)t.row0 * N + n0) * es;
+            j.ldc = (int64_t)N * es;
+        } else if (KIND == K_G) {
+            j.K = d;
+            j.a = opnd(a.dout, d, t.row0, t.row0 + t.nrows, 4);
+            j.b = opnd(t.shared ? a.w_sdn : static_cast<const char *>(a.w_dn) + g * d * a.F * es,
+                       t.Fg, 0, d, es);
+            j.b.cb = n0;
+            j.b.ilim = j.ncols;
+            j.c = reinterpret_cast<char *>((t.shared ? a.g_sh : a.g) + (int64_t)t.row0 * N + n0);
+            j.ldc = (int64_t)N * 4;
+        } else {  // K_DX
+            j.K = 2 * t.Fg;
+            j.a = opnd(t.shared ? a.dgu_sh : a.dgu, 2 * t.Fg, t.row0, t.row0 + t.nrows, es);
+            j.b = opnd(t.shared ? a.w_sgu : static_cast<const char *>(a.w_gu) + g * 2 * a.F * d * es,
+                       d, 0, 2 * t.Fg, es);
+            j.b.cb = n0;
+            j.b.ilim = j.ncols;
+            j.c = static_cast<char *>(t.shared ? a.dxs : a.dxp) + ((int64_t)t.row0 * d + n0) * es;
+            j.ldc = (int64_t)d * es;
+        }
+        if (!t.shared && (KIND == K_AU || KIND == K_G)) {
+            j.a.map = a.perm;
+            j.a.div = a.k;
+        }
+        return true;
+    }
+    // K_DWGU / K_DWDN: one group (expert, or E = shared) per run of M-tiles
+    const int Fmax = a.F > a.Fs ? a.F : a.Fs;
+    const int mtiles = KIND == K_DWGU ? (2 * Fmax + QB - 1) / QB : (d + QB - 1) / QB;
+    const int g = bx / mtiles, mt = bx - g * mtiles;
+    if (g > E || (g == E && a.Fs == 0)) return false;
+    const bool shared = g == E;
+    const int Fg = shared ? a.Fs : a.F;
+    const int M = KIND == K_DWGU ? 2 * Fg : d;
+    const int N = KIND == K_DWGU ? d : Fg;
+    const int m0 = QB * mt, n0 = QB * by;
+    if (m0 >= M || n0 >= N) return false;
+    j.mrows = min(QB, M - m0);
+    j.ncols = min(QB, N - n0);
+    const int rb = shared ? 0 : a.offsets[g];
+    const int cnt = shared ? (int)a.T : a.counts[g];
+    j.K = cnt;
+    if (KIND == K_DWGU) {
+        j.a = opnd(shared ? a.dgu_sh : a.dgu, 2 * Fg, rb, rb + cnt, es);
+        j.b = opnd(a.x, d, rb, rb + cnt, es);
+        j.c = (shared ? static_cast<char *>(a.dw_sgu)
+                      : static_cast<char *>(a.dw_gu) + (int64_t)g * 2 * a.F * d * es) +
+              ((int64_t)m0 * d + n0) * es;
+        j.ldc = (int64_t)d * es;
+    } else {
+        j.a = opnd(a.dout, d, rb, rb + cnt, 4);
+        j.a.scale = shared ? a.gate : a.topk_w;
+        j.b = opnd(shared ? a.hh_sh : a.hh, Fg, rb, rb + cnt, es);
+        j.c = (shared ? static_cast<char *>(a.dw_sdn)
+                      : static_cast<char *>(a.dw_dn) + (int64_t)g * d * a.F * es) +
+              ((int64_t)m0 * Fg + n0) * es;
+        j.ldc = (int64_t)Fg * es;
+    }
+    j.a.cb = m0;
+    j.a.ilim = j.mrows;
+    j.b.cb = n0;
+    j.b.ilim = j.ncols;
+    if (!shared) {
+        // token-indexed operands of routed rows follow the permutation
+        Opnd &tokop = KIND == K_DWGU ? j.b : j.a;
+        tokop.map = a.perm;
+        tokop.div = a.k;
+    }
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// Staging of one operand tile (QB x QK) into LDS, for 256 threads.
+
+// KC: chunk c = tid + 256 q (q < 4) is row c / 8, elements 8 (c % 8) .. +7.
+template <bool F32>
+struct StageKC {
+    const char *src[4];
+    uint4 r[4];
+    uint4 r2[4];  // binary32 sources: second half of the 8 values
+    __device__ void init(const Opnd &o, int tid) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = tid + 256 * q;
+            int s = o.base + (c >> 3);
+            if (s >= o.lim) s = o.lim - 1;
+            float sc;
+            src[q] = op_row(o, s, sc) + (int64_t)(8 * (c & 7)) * (F32 ? 4 : 2);
+        }
+    }
+    __device__ void load(int k0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (F32) {
+                const float4 *p = reinterpret_cast<const float4 *>(src[q] + (int64_t)k0 * 4);
+                r[q] = __builtin_bit_cast(uint4, p[0]);
+                r2[q] = __builtin_bit_cast(uint4, p[1]);
+            } else {
+                r[q] = *reinterpret_cast<const uint4 *>(src[q] + (int64_t)k0 * 2);
+            }
+        }
+    }
+    __device__ void store(uint16_t *lds, int tid) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = tid + 256 * q;
+            uint4 v = r[q];
+            if (F32) {
+                v.x = pack_bf16x2(__uint_as_float(r[q].x), __uint_as_float(r[q].y));
+                v.y = pack_bf16x2(__uint_as_float(r[q].z), __uint_as_float(r[q].w));
+                v.z = pack_bf16x2(__uint_as_float(r2[q].x), __uint_as_float(r2[q].y));
+                v.w = pack_bf16x2(__uint_as_float(r2[q].z), __uint_as_float(r2[q].w));
+            }
+            *reinterpret_cast<uint4 *>(lds + (c >> 3) * QLD + 8 * (c & 7)) = v;
+        }
+    }
+};
+
+// MC: thread owns reduction pair kp = tid % 32 (elements 2 kp, 2 kp + 1 of
+// the step) and column groups i8 = tid / 32 + 8 q (q < 2), eight columns each.
+// Each pair of 16-byte row pieces becomes eight 32-bit LDS writes of
+// (k, k+1) for one column.  The source rows of the next step are looked up
+// one step ahead (rows[], scl[]), so the data loads never wait on the map.
+template <bool F32>
+struct StageMC {
+    const char *rows[2];
+    float scl[2];   // scales of the looked-up step
+    float sld[2];   // scales of the step whose data is in r / r2
+    bool live[2];
+    uint4 r[2][2], r2[2][2];
+    int kp, i0;
+    __device__ void init(int tid) {
+        kp = tid & 31;
+        i0 = 8 * (tid >> 5);
+    }
+    __device__ void lookup(const Opnd &o, int k0) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int s = o.base + k0 + 2 * kp + h;
+            live[h] = s < o.lim;
+            rows[h] = live[h] ? op_row(o, s, scl[h]) : o.p;
+            if (!live[h]) scl[h] = 0.f;
+        }
+    }
+    __device__ void load(const Opnd &o) {
+        sld[0] = scl[0];
+        sld[1] = scl[1];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int i = i0 + 64 * q;
+                const bool ok = live[h] && i < o.ilim;
+                const char *p = rows[h] + (int64_t)(o.cb + i) * (F32 ? 4 : 2);
+                if (F32) {
+                    r[h][q] = ok ? __builtin_bit_cast(uint4, reinterpret_cast<const float4 *>(p)[0])
+                                 : uint4{0, 0, 0, 0};
+                    r2[h][q] = ok ? __builtin_bit_cast(uint4, reinterpret_cast<const float4 *>(p)[1])
+                                  : uint4{0, 0, 0, 0};
+                } else {
+                    r[h][q] = ok ? *reinterpret_cast<const uint4 *>(p) : uint4{0, 0, 0, 0};
+                }
+            }
+    }
+    __device__ void store(uint16_t *lds) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            uint32_t v[2][8];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if (F32) {
+                    const float s = sld[h];
+                    const uint4 &a = r[h][q], &b = r2[h][q];
+                    v[h][0] = f32_to_bf16_rne(s * __uint_as_float(a.x));
+                    v[h][1] = f32_to_bf16_rne(s * __uint_as_float(a.y));
+                    v[h][2] = f32_to_bf16_rne(s * __uint_as_float(a.z));
+                    v[h][3] = f32_to_bf16_rne(s * __uint_as_float(a.w));
+                    v[h][4] = f32_to_bf16_rne(s * __uint_as_float(b.x));
+                    v[h][5] = f32_to_bf16_rne(s * __uint_as_float(b.y));
+                    v[h][6] = f32_to_bf16_rne(s * __uint_as_float(b.z));
+                    v[h][7] = f32_to_bf16_rne(s * __uint_as_float(b.w));
+                } else {
+                    const uint4 &a = r[h][q];
+                    v[h][0] = a.x & 0xFFFFu; v[h][1] = a.x >> 16;
+                    v[h][2] = a.y & 0xFFFFu; v[h][3] = a.y >> 16;
+                    v[h][4] = a.z & 0xFFFFu; v[h][5] = a.z >> 16;
+                    v[h][6] = a.w & 0xFFFFu; v[h][7] = a.w >> 16;
+                }
+            }
+            const int i = i0 + 64 * q;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                *reinterpret_cast<uint32_t *>(lds + (i + e) * QLD + 2 * kp) = v[0][e] | (v[1][e] << 16);
+        }
+    }
+};
+
+// Only binary32 sources carry a scale (dOut scaled by the routing weight or
+// the shared gate); bfloat16 operands are staged as they are.
+
+template <bool KC, bool F32> struct Stager;
+template <bool F32> struct Stager<true, F32> {
+    StageKC<F32> s;
+    __device__ void init(const Opnd &o, int tid) { s.init(o, tid); }
+    __device__ void lookup(const Opnd &, int) {}
+    __device__ void load(const Opnd &, int k0) { s.load(k0); }
+    __device__ void store(uint16_t *lds, int tid) { s.store(lds, tid); }
+};
+template <bool F32> struct Stager<false, F32> {
+    StageMC<F32> s;
+    __device__ void init(const Opnd &, int tid) { s.init(tid); }
+    __device__ void lookup(const Opnd &o, int k0) { s.lookup(o, k0); }
+    __device__ void load(const Opnd &o, int) { s.load(o); }
+    __device__ void store(uint16_t *lds, int) { s.store(lds); }
+};
+
+// bfloat16 layers: 128 x 128 tiles, 4 waves in 2 x 2, each 64 x 64 from
+// v_mfma_f32_32x32x16_bf16; register-staged double buffer in LDS.
+template <int KIND>
+__global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(BwdArgs a) {
+    using Tr = Traits<KIND>;
+    __shared__ __align__(16) uint16_t As[2][QB * QLD];
+    __shared__ __align__(16) uint16_t Bs[2][QB * QLD];
+    Job j;
+    if (!make_job<KIND>(a, blockIdx.x, blockIdx.y, 2, j)) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const int wm = wave >> 1, wn = wave & 1;
+    const int fr = lane & 31, fk = 8 * (lane >> 5);
+    Stager<Tr::A_KC, Tr::A_F32> sa;
+    Stager<Tr::B_KC, Tr::B_F32> sb;
+    sa.init(j.a, tid);
+    sb.init(j.b, tid);
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
+
+    const int nk = (j.K + QK - 1) / QK;
+    if (nk > 0) {
+        sa.lookup(j.a, 0);
+        sb.lookup(j.b, 0);
+        sa.load(j.a, 0);
+        sb.load(j.b, 0);
+        if (nk > 1) {
+            sa.lookup(j.a, QK);
+            sb.lookup(j.b, QK);
+        }
+        sa.store(As[0], tid);
+        sb.store(Bs[0], tid);
+        __syncthreads();
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk) {
+            sa.load(j.a, (kt + 1) * QK);
+            sb.load(j.b, (kt + 1) * QK);
+            if (kt + 2 < nk) {
+                sa.lookup(j.a, (kt + 2) * QK);
+                sb.lookup(j.b, (kt + 2) * QK);
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < QK / 16; ++ks) {
+            bf16x8 af[2], bfr[2];
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+                af[mi] = *reinterpret_cast<const bf16x8 *>(
+                    &As[cur][(64 * wm + 32 * mi + fr) * QLD + 16 * ks + fk]);
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+                bfr[ni] = *reinterpret_cast<const bf16x8 *>(
+                    &Bs[cur][(64 * wn + 32 * ni + fr) * QLD + 16 * ks + fk]);
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni],
+                                                                          acc[mi][ni], 0, 0, 0);
+        }
+        if (kt + 1 < nk) {
+            sa.store(As[cur ^ 1], tid);
+            sb.store(Bs[cur ^ 1], tid);
+        }
+        __syncthreads();
+    }
+
+    // accumulator layout: lane holds column lane % 32 and rows
+    // 8 (v / 4) + 4 (lane / 32) + (v % 4)
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int row = 64 * wm + 32 * mi + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            if (row >= j.mrows) continue;
+            char *crow = row >= j.c_alt ? j.c_alt_p + (int64_t)(row - j.c_alt) * j.ldc
+                                        : j.c + (int64_t)row * j.ldc;
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni) {
+                const int col = 64 * wn + 32 * ni + fr;
+                if (col >= j.ncols) continue;
+                if (Tr::C_F32)
+                    reinterpret_cast<float *>(crow)[col] = acc[mi][ni][v];
+                else
+                    reinterpret_cast<uint16_t *>(crow)[col] = f32_to_bf16_rne(acc[mi][ni][v]);
+            }
+        }
+}
+
+// binary32 layers: the same jobs, one output element per thread and step,
+// plain binary32 fused multiply-adds over the reduction.
+__device__ __forceinline__ float op_elem_kc(const Opnd &o, int i, int k) {
+    int s = o.base + i;
+    if (s >= o.lim) s = o.lim - 1;
+    float sc;
+    return reinterpret_cast<const float *>(op_row(o, s, sc))[k] * sc;
+}
+__device__ __forceinline__ float op_elem_mc(const Opnd &o, int i, int k) {
+    const int s = o.base + k;
+    if (s >= o.lim || i >= o.ilim) return 0.f;
+    float sc;
+    return reinterpret_cast<const float *>(op_row(o, s, sc))[o.cb + i] * sc;
+}
+
+template <int KIND>
+__global__ __launch_bounds__(256) void bwd_gemm_f32_kernel(BwdArgs a) {
+    using Tr = Traits<KIND>;
+    Job j;
+    if (!make_job<KIND>(a, blockIdx.x, blockIdx.y, 4, j)) return;
+    for (int o = threadIdx.x; o < QB * QB; o += 256) {
+        const int i = o / QB, c = o % QB;
+        if (i >= j.mrows || c >= j.ncols) continue;
+        float acc = 0.f;
+        for (int k = 0; k < j.K; ++k) {
+            const float av = Tr::A_KC ? op_elem_kc(j.a, i, k) : op_elem_mc(j.a, i, k);
+            const float bv = Tr::B_KC ? op_elem_kc(j.b, c, k) : op_elem_mc(j.b, c, k);
+            acc = fmaf(av, bv, acc);
+        }
+        char *crow = i >= j.c_alt ? j.c_alt_p + (int64_t)(i - j.c_alt) * j.ldc
+                                  : j.c + (int64_t)i * j.ldc;
+        reinterpret_cast<float *>(crow)[c] = acc;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// SwiGLU backward, one wave per row: routed rows r < offsets[E] (pair
+// perm[r], weight topk_w), then the T shared rows (weight s_t = sigmoid of
+// logit column E, stored to gate[t]).  dw (routed, at the pair id) or ds
+// (shared, at the token) is G . h summed in a fixed order.
+template <typename Tv>
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(BwdArgs a) {
+    const int64_t routed = (int64_t)a.T * a.k;
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const bool shared = r >= routed;
+    int64_t row;
+    int Fg;
+    float w;
+    int pair = 0;
+    if (!shared) {
+        if (r >= a.offsets[a.E]) return;
+        row = r;
+        pair = a.perm[r];
+        w = a.topk_w[pair];
+        Fg = a.F;
+    } else {
+        if (a.Fs == 0 || r - routed >= a.T) return;
+        row = r - routed;
+        const float z = a.logits[row * a.ldl + a.E];
+        w = 1.0f / (1.0f + __expf(-z));
+        Fg = a.Fs;
+        if (lane == 0) a.gate[row] = w;
+    }
+    const Tv *au = static_cast<const Tv *>(shared ? a.au_sh : a.au) + row * 2 * Fg;
+    const float *G = (shared ? a.g_sh : a.g) + row * Fg;
+    Tv *dgu = static_cast<Tv *>(shared ? a.dgu_sh : a.dgu) + row * 2 * Fg;
+    Tv *hh = static_cast<Tv *>(shared ? a.hh_sh : a.hh) + row * Fg;
+    float acc = 0.f;
+    for (int f = lane; f < Fg; f += 64) {
+        const float av = to_f32(au[f]), uv = to_f32(au[Fg + f]), gv = G[f];
+        const float sg = 1.0f / (1.0f + __expf(-av));
+        const float silu = av * sg;
+        const float h = silu * uv;
+        acc = fmaf(gv, h, acc);
+        const float dh = w * gv;
+        const float da = dh * uv * (sg * (1.0f + av * (1.0f - sg)));
+        const float du = dh * silu;
+        if constexpr (sizeof(Tv) == 2) {
+            dgu[f] = f32_to_bf16_rne(da);
+            dgu[Fg + f] = f32_to_bf16_rne(du);
+            hh[f] = f32_to_bf16_rne(h);
+        } else {
+            dgu[f] = da;
+            dgu[Fg + f] = du;
+            hh[f] = h;
+        }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) {
+        if (!shared) a.dwp[pair] = acc;
+        else a.ds[row] = acc;
+    }
+}
+
+// Block-wide fixed-order reductions over 256 threads (4 waves).
+__device__ __forceinline__ float block_sum(float v, float *red) {
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    return (red[0] + red[1]) + (red[2] + red[3]);
+}
+__device__ __forceinline__ float block_max(float v, float *red) {
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// Router backward, one block of 256 threads per token: softmax p over the E
+// logits (+ bias), f . p, the load-balancing term, the selected experts'
+// term and the shared-gate logit's gradient, written as a dL row zero padded
+// to ldd columns (layer dtype).
+template <typename Tv>
+__global__ __launch_bounds__(256) void router_bwd_kernel(BwdArgs a) {
+    extern __shared__ float dls[];  // [ldd]
+    __shared__ float red[4];
+    const int64_t t = blockIdx.x;
+    const float *l = a.logits + t * a.ldl;
+    const float inv_pairs = 1.0f / (float)((int64_t)a.T * a.k);
+    float m = -INFINITY;
+    for (int e = threadIdx.x; e < a.E; e += 256)
+        m = fmaxf(m, l[e] + (a.bias ? a.bias[e] : 0.f));
+    m = block_max(m, red);
+    float z = 0.f;
+    for (int e = threadIdx.x; e < a.E; e += 256) z += __expf(l[e] + (a.bias ? a.bias[e] : 0.f) - m);
+    z = block_sum(z, red);
+    const float rz = 1.0f / z;
+    float fp = 0.f;
+    for (int e = threadIdx.x; e < a.E; e += 256) {
+        const float p = __expf(l[e] + (a.bias ? a.bias[e] : 0.f) - m) * rz;
+        dls[e] = p;
+        fp = fmaf((float)a.counts[e] * inv_pairs, p, fp);
+    }
+    fp = block_sum(fp, red);
+    const float c = a.coef * (float)a.E / (float)a.T;
+    for (int e = threadIdx.x; e < a.ldd; e += 256)
+        dls[e] = e < a.E ? c * dls[e] * ((float)a.counts[e] * inv_pairs - fp) : 0.f;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        a.q[t] = fp;
+        const float *w = a.topk_w + t * a.k;
+        const float *dw = a.dwp + t * a.k;
+        float wdw = 0.f;
+        for (int jj = 0; jj < a.k; ++jj) wdw = fmaf(w[jj], dw[jj], wdw);
+        for (int jj = 0; jj < a.k; ++jj) {
+            int e = a.topk_idx[t * a.k + jj];
+            e = e < 0 ? 0 : (e >= a.E ? a.E - 1 : e);
+            dls[e] += w[jj] * (dw[jj] - wdw);
+        }
+        if (a.Fs > 0) {
+            const float s = a.gate[t];
+            dls[a.E] = a.ds[t] * s * (1.0f - s);
+        }
+    }
+    __syncthreads();
+    Tv *out = static_cast<Tv *>(a.dl) + t * a.ldd;
+    for (int e = threadIdx.x; e < a.ldd; e += 256) {
+        if constexpr (sizeof(Tv) == 2) out[e] = f32_to_bf16_rne(dls[e]);
+        else out[e] = dls[e];
+    }
+}
+
+// dx[t] = sum_j dXp[row(t, j)] + dXs[t] + dXr[t], binary32, slot order.
+template <typename Tv>
+__global__ __launch_bounds__(256) void dx_combine_kernel(BwdArgs a) {
+    const int64_t t = blockIdx.x;
+    const int c = blockIdx.y * 256 + threadIdx.x;
+    if (c >= a.d) return;
+    float acc = 0.f;
+    const Tv *dxp = static_cast<const Tv *>(a.dxp);
+    for (int jj = 0; jj < a.k; ++jj)
+        acc += to_f32(dxp[(int64_t)a.rank[t * a.k + jj] * a.d + c]);
+    if (a.Fs > 0) acc += to_f32(static_cast<const Tv *>(a.dxs)[t * a.d + c]);
+    acc += a.dxr[t * a.d + c];
+    a.dx[t * a.d + c] = acc;
+}
+
+// L_aux = coef (E / T) sum_t q_t (q_t = f . p_t), one block, fixed order.
+__global__ __launch_bounds__(256) void aux_loss_kernel(BwdArgs a) {
+    __shared__ float red[4];
+    float s = 0.f;
+    for (int64_t t = threadIdx.x; t < a.T; t += 256) s += a.q[t];
+    s = block_sum(s, red);
+    if (threadIdx.x == 0) a.aux_loss[0] = a.coef * (float)a.E / (float)a.T * s;
+}
+
+// ---------------------------------------------------------------------------
+
+template <int KIND>
+static void launch_gemm(const BwdArgs &a, dim3 grid, hipStream_t s) {
+    if (grid.x == 0 || grid.y == 0) return;
+    if (a.bf16)
+        hipLaunchKernelGGL(bwd_gemm_kernel<KIND>, grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(bwd_gemm_f32_kernel<KIND>, grid, dim3(256), 0, s, a);
+}
+
+static unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
+
+hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
+                           const std::function<void(int)> &mark) {
+    hipError_t err = launch_permute(pp, QB, s);
+    if (err != hipSuccess) return err;
+    const int Fmax = a.F > a.Fs ? a.F : a.Fs;
+    const unsigned tiles = (unsigned)pp.max_tiles;
+    launch_gemm<K_LOGITS>(a, dim3(cdiv(a.T, QB), cdiv(a.E + 1, QB)), s);
+    mark(1);
+    launch_gemm<K_AU>(a, dim3(tiles, cdiv(2 * Fmax, QB)), s);
+    launch_gemm<K_G>(a, dim3(tiles, cdiv(Fmax, QB)), s);
+    mark(2);
+    const int64_t rows = (int64_t)a.T * a.k + (a.Fs > 0 ? a.T : 0);
+    const size_t lds = (size_t)a.ldd * sizeof(float);
+    if (a.bf16) {
+        hipLaunchKernelGGL(swiglu_bwd_kernel<uint16_t>, dim3(cdiv(rows, 4)), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(router_bwd_kernel<uint16_t>, dim3((unsigned)a.T), dim3(256), lds, s, a);
+    } else {
+        hipLaunchKernelGGL(swiglu_bwd_kernel<float>, dim3(cdiv(rows, 4)), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(router_bwd_kernel<float>, dim3((unsigned)a.T), dim3(256), lds, s, a);
+    }
+    mark(3);
+    launch_gemm<K_DX>(a, dim3(tiles, cdiv(a.d, QB)), s);
+    mark(4);
+    launch_gemm<K_DWGU>(a, dim3((unsigned)(a.E + 1) * cdiv(2 * Fmax, QB), cdiv(a.d, QB)), s);
+    mark(5);
+    launch_gemm<K_DWDN>(a, dim3((unsigned)(a.E + 1) * cdiv(a.d, QB), cdiv(Fmax, QB)), s);
+    mark(6);
+    launch_gemm<K_DWR>(a, dim3(cdiv(a.E + 1, QB), cdiv(a.d, QB)), s);
+    launch_gemm<K_DXR>(a, dim3(cdiv(a.T, QB), cdiv(a.d, QB)), s);
+    const dim3 cgrid((unsigned)a.T, cdiv(a.d, 256));
+    if (a.bf16)
+        hipLaunchKernelGGL(dx_combine_kernel<uint16_t>, cgrid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(dx_combine_kernel<float>, cgrid, dim3(256), 0, s, a);
+    if (a.aux_loss) hipLaunchKernelGGL(aux_loss_kernel, dim3(1), dim3(256), 0, s, a);
+    mark(7);
+    return hipGetLastError();
+}
+
+}  // namespace moe

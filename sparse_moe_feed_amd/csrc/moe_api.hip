@@ -130,6 +130,56 @@ moe::Problem make_problem(const moe_desc &d, int64_t T, const Plan &pl, void *ws
     return p;
 }
 
+// Workspace of moe_backward (regions as in moe::BwdArgs).
+struct BwdPlan {
+    size_t counts, offsets, tile_start, tile_group, blk, rank, perm, logits, au, au_sh, g, g_sh, dgu,
+        dgu_sh, hh, hh_sh, dwp, gate, ds, q, dl, dxp, dxs, dxr, total;
+    int nblk, max_tiles, ldl, ldd;
+};
+
+BwdPlan make_bwd_plan(const moe_desc &d, int64_t T) {
+    BwdPlan p;
+    const size_t es = d.dtype == MOE_BF16 ? 2 : 4;
+    const int64_t pairs = T * d.top_k;
+    const size_t F = (size_t)d.d_expert, Fs = (size_t)d.d_shared, dm = (size_t)d.d_model;
+    p.nblk = (int)((T + moe::kCountBlock - 1) / moe::kCountBlock);
+    p.max_tiles = (int)moe::max_gemm_tiles(T, d.top_k, d.n_experts, moe::kGemmBM, d.d_shared > 0);
+    p.ldl = d.n_experts + 1;
+    p.ldd = (d.n_experts + 1 + 127) / 128 * 128;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align_up(off + bytes);
+        return at;
+    };
+    p.counts = take((size_t)(d.n_experts + 1) * 4);
+    p.offsets = take((size_t)(d.n_experts + 1) * 4);
+    p.tile_start = take((size_t)(d.n_experts + 2) * 4);
+    p.tile_group = take((size_t)(p.max_tiles + 1) * 4);
+    p.blk = take((size_t)d.n_experts * p.nblk * 4);
+    p.rank = take((size_t)pairs * 4);
+    p.perm = take((size_t)pairs * 4);
+    p.logits = take((size_t)T * p.ldl * 4);
+    p.au = take((size_t)pairs * 2 * F * es);
+    p.au_sh = take((size_t)T * 2 * Fs * es);
+    p.g = take((size_t)pairs * F * 4);
+    p.g_sh = take((size_t)T * Fs * 4);
+    p.dgu = take((size_t)pairs * 2 * F * es);
+    p.dgu_sh = take((size_t)T * 2 * Fs * es);
+    p.hh = take((size_t)pairs * F * es);
+    p.hh_sh = take((size_t)T * Fs * es);
+    p.dwp = take((size_t)pairs * 4);
+    p.gate = take((size_t)T * 4);
+    p.ds = take((size_t)T * 4);
+    p.q = take((size_t)T * 4);
+    p.dl = take((size_t)T * p.ldd * es);
+    p.dxp = take((size_t)pairs * dm * es);
+    p.dxs = take((size_t)T * dm * es);
+    p.dxr = take((size_t)T * dm * 4);
+    p.total = off;
+    return p;
+}
+
 moe_status hip_status(hipError_t err) {
     if (err == hipSuccess) return MOE_OK;
     g_last_error = hipGetErrorString(err);
@@ -457,6 +507,127 @@ moe_status moe_stage_events(void *const *events, int n) {
     for (int i = 0; i < n; ++i) g_stage_events[i] = static_cast<hipEvent_t>(events[i]);
     g_n_stage_events = n;
     return MOE_OK;
+}
+
+}  // extern "C"
+
+extern "C" {
+
+size_t moe_backward_workspace_size(const moe_desc *desc, int64_t T) {
+    if (check_desc(desc) != MOE_OK || check_T(desc, T) != MOE_OK) return 0;
+    return make_bwd_plan(*desc, T).total;
+}
+
+moe_status moe_backward(const moe_desc *desc, int64_t T, const void *x, const void *w_router,
+                        const float *router_bias, const void *w_gate_up, const void *w_down,
+                        const void *w_sh_gate_up, const void *w_sh_down, const void *sh_gate,
+                        const int32_t *topk_idx, const float *topk_w, const float *dout,
+                        float aux_coef, float *dx, void *dw_router, void *dw_gate_up,
+                        void *dw_down, void *dw_sh_gate_up, void *dw_sh_down, void *dsh_gate,
+                        float *aux_loss, void *ws, size_t ws_bytes, void *stream) {
+    moe_status st = check_desc(desc);
+    if (st != MOE_OK) return st;
+    st = check_T(desc, T);
+    if (st != MOE_OK || T == 0) return st;
+    const bool sh = desc->d_shared > 0;
+    for (const void *q : std::initializer_list<const void *>{
+             x, w_router, w_gate_up, w_down, topk_idx, topk_w, dout, dx, dw_router, dw_gate_up,
+             dw_down})
+        if (!q) return MOE_ERR_INVALID_ARG;
+    if (sh && (!w_sh_gate_up || !w_sh_down || !sh_gate || !dw_sh_gate_up || !dw_sh_down ||
+               !dsh_gate))
+        return MOE_ERR_INVALID_ARG;
+    if (!all_aligned({x, w_router, router_bias, w_gate_up, w_down, w_sh_gate_up, w_sh_down,
+                      sh_gate, topk_idx, topk_w, dout, dx, dw_router, dw_gate_up, dw_down,
+                      dw_sh_gate_up, dw_sh_down, dsh_gate}))
+        return MOE_ERR_INVALID_ARG;
+    if (aux_loss && (reinterpret_cast<uintptr_t>(aux_loss) & 3u)) return MOE_ERR_INVALID_ARG;
+    if (!(aux_coef >= -3.4e38f && aux_coef <= 3.4e38f)) return MOE_ERR_INVALID_ARG;
+    const BwdPlan pl = make_bwd_plan(*desc, T);
+    if (!ws || !aligned16(ws)) return MOE_ERR_WORKSPACE;
+    if (ws_bytes < pl.total) return MOE_ERR_WORKSPACE;
+
+    char *base = static_cast<char *>(ws);
+    moe::Problem p;
+    memset(&p, 0, sizeof p);
+    p.T = T;
+    p.d = desc->d_model;
+    p.E = desc->n_experts;
+    p.k = desc->top_k;
+    p.F = desc->d_expert;
+    p.Fs = desc->d_shared;
+    p.bf16 = desc->dtype == MOE_BF16;
+    p.topk_idx = const_cast<int32_t *>(topk_idx);
+    p.counts = reinterpret_cast<int32_t *>(base + pl.counts);
+    p.offsets = reinterpret_cast<int32_t *>(base + pl.offsets);
+    p.tile_start = reinterpret_cast<int32_t *>(base + pl.tile_start);
+    p.tile_group = reinterpret_cast<int32_t *>(base + pl.tile_group);
+    p.blk = reinterpret_cast<int32_t *>(base + pl.blk);
+    p.rank = reinterpret_cast<int32_t *>(base + pl.rank);
+    p.perm = reinterpret_cast<int32_t *>(base + pl.perm);
+    p.nblk = pl.nblk;
+    p.max_tiles = pl.max_tiles;
+
+    moe::BwdArgs a;
+    memset(&a, 0, sizeof a);
+    a.T = T;
+    a.d = p.d;
+    a.E = p.E;
+    a.k = p.k;
+    a.F = p.F;
+    a.Fs = p.Fs;
+    a.bf16 = p.bf16;
+    a.x = x;
+    a.w_router = w_router;
+    a.w_gu = w_gate_up;
+    a.w_dn = w_down;
+    a.w_sgu = sh ? w_sh_gate_up : nullptr;
+    a.w_sdn = sh ? w_sh_down : nullptr;
+    a.sh_gate = sh ? sh_gate : nullptr;
+    a.bias = router_bias;
+    a.topk_idx = topk_idx;
+    a.topk_w = topk_w;
+    a.dout = dout;
+    a.coef = aux_coef;
+    a.dx = dx;
+    a.dw_router = dw_router;
+    a.dw_gu = dw_gate_up;
+    a.dw_dn = dw_down;
+    a.dw_sgu = sh ? dw_sh_gate_up : nullptr;
+    a.dw_sdn = sh ? dw_sh_down : nullptr;
+    a.dsh_gate = sh ? dsh_gate : nullptr;
+    a.aux_loss = aux_loss;
+    a.logits = reinterpret_cast<float *>(base + pl.logits);
+    a.ldl = pl.ldl;
+    a.counts = p.counts;
+    a.offsets = p.offsets;
+    a.tile_start = p.tile_start;
+    a.tile_group = p.tile_group;
+    a.perm = p.perm;
+    a.rank = p.rank;
+    a.au = base + pl.au;
+    a.au_sh = base + pl.au_sh;
+    a.g = reinterpret_cast<float *>(base + pl.g);
+    a.g_sh = reinterpret_cast<float *>(base + pl.g_sh);
+    a.dgu = base + pl.dgu;
+    a.dgu_sh = base + pl.dgu_sh;
+    a.hh = base + pl.hh;
+    a.hh_sh = base + pl.hh_sh;
+    a.dwp = reinterpret_cast<float *>(base + pl.dwp);
+    a.gate = reinterpret_cast<float *>(base + pl.gate);
+    a.ds = reinterpret_cast<float *>(base + pl.ds);
+    a.q = reinterpret_cast<float *>(base + pl.q);
+    a.dl = base + pl.dl;
+    a.ldd = pl.ldd;
+    a.dxp = base + pl.dxp;
+    a.dxs = base + pl.dxs;
+    a.dxr = reinterpret_cast<float *>(base + pl.dxr);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    mark_stage(0, s);
+    const hipError_t err = moe::launch_backward(p, a, s, [&](int i) { mark_stage(i, s); });
+    g_n_stage_events = 0;
+    return hip_status(err);
 }
 
 }  // extern "C"

@@ -113,6 +113,44 @@ hipError_t launch_experts_decode_mx4(const Problem &p, hipStream_t s,
 // (128 x 256 tiles, tile map for kGemmBM); d, F, Fs % 128 == 0, 32-bit offsets.
 hipError_t launch_experts_mx4_gemm(const Problem &p, hipStream_t s,
                                    const std::function<void(int)> &mark);
+// Backward pass of the layer for a given routing.  Weights, x and the
+// activation intermediates are in the layer's dtype; dout, dx, logits, G and
+// the per-row scalars are binary32.
+struct BwdArgs {
+    int64_t T;
+    int d, E, k, F, Fs;
+    bool bf16;
+    const void *x, *w_router, *w_gu, *w_dn, *w_sgu, *w_sdn, *sh_gate;
+    const float *bias;
+    const int32_t *topk_idx;
+    const float *topk_w;
+    const float *dout;  // [T, d]
+    float coef;         // load-balancing loss coefficient
+    // outputs
+    float *dx;          // [T, d]
+    void *dw_router, *dw_gu, *dw_dn, *dw_sgu, *dw_sdn, *dsh_gate;
+    float *aux_loss;    // [1] or null
+    // workspace
+    float *logits;      // [T, ldl]  x . [W_r; g] (no bias)
+    int ldl;
+    const int32_t *counts, *offsets, *tile_start, *tile_group, *perm, *rank;
+    void *au, *au_sh;   // [T*k, 2F], [T, 2Fs]  gate | up pre-activations
+    float *g, *g_sh;    // [T*k, F], [T, Fs]    W_dn^T dout of each row
+    void *dgu, *dgu_sh; // [T*k, 2F], [T, 2Fs]  da | du
+    void *hh, *hh_sh;   // [T*k, F], [T, Fs]    h = silu(a) u
+    float *dwp;         // [T*k] d/dw of each pair (pair order)
+    float *gate, *ds;   // [T] s_t and d/ds_t
+    float *q;           // [T] f . p_t
+    void *dl;           // [T, ldd] router-logit gradient, zero padded
+    int ldd;
+    void *dxp, *dxs;    // [T*k, d], [T, d]  dx of each routed row, of the shared expert
+    float *dxr;         // [T, d]            dx of the router
+};
+// p carries the routing and permutation buffers (tile map for kGemmBM rows).
+// mark(i) after stage i: 1 logits, 2 gate/up and G, 3 SwiGLU and router
+// backward, 4 dX, 5 dW_gu, 6 dW_dn, 7 router GEMMs, combine and loss.
+hipError_t launch_backward(const Problem &p, const BwdArgs &a, hipStream_t s,
+                           const std::function<void(int)> &mark);
 // Row-major MXFP4 [rows, K] (codes, scales) -> packed tiles (rows % 16 == 0,
 // K % 128 == 0).
 hipError_t launch_mx4_pack(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t K,

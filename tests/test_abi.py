@@ -250,3 +250,50 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         moe.route(x, torch.zeros(8, 64, dtype=torch.bfloat16), 2)
+
+
+BWD_PTRS = ("x", "wr", "b", "gu", "dn", "sgu", "sdn", "g", "idx", "w", "dout", "dx", "dwr",
+            "dgu", "ddn", "dsgu", "dsdn", "dg", "aux")
+
+
+def call_backward(L, D, T, ptrs=None, coef=0.001, ws=FAKE, ws_bytes=1 << 40):
+    p = {n: FAKE for n in BWD_PTRS}
+    p["b"] = p["aux"] = None
+    p.update(ptrs or {})
+    v = lambda a: None if a is None else ctypes.c_void_p(a)
+    args = [v(p[n]) for n in BWD_PTRS]
+    return L.moe_backward(ctypes.byref(D), T, *args[:11], ctypes.c_float(coef), *args[11:],
+                          v(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("missing", ["x", "wr", "gu", "dn", "idx", "w", "dout", "dx", "dwr",
+                                     "dgu", "ddn", "sgu", "sdn", "g", "dsgu", "dsdn", "dg"])
+def test_backward_null_required_pointer(L, missing):
+    assert call_backward(L, desc(), 8, {missing: None}) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_backward_validation(L):
+    D = desc()
+    assert call_backward(L, desc(d=0), 8) == moe.MOE_ERR_INVALID_ARG
+    assert call_backward(L, desc(F=96), 8) == moe.MOE_ERR_UNSUPPORTED
+    assert call_backward(L, D, -1) == moe.MOE_ERR_INVALID_ARG
+    assert call_backward(L, D, 8, {"dout": FAKE + 4}) == moe.MOE_ERR_INVALID_ARG
+    assert call_backward(L, D, 8, {"aux": FAKE + 2}) == moe.MOE_ERR_INVALID_ARG
+    assert call_backward(L, D, 8, coef=float("nan")) == moe.MOE_ERR_INVALID_ARG
+    assert call_backward(L, D, 8, ws=None) == moe.MOE_ERR_WORKSPACE
+    need = L.moe_backward_workspace_size(ctypes.byref(D), 8)
+    assert need > 0
+    assert call_backward(L, D, 8, ws_bytes=need - 1) == moe.MOE_ERR_WORKSPACE
+    # no shared expert: its pointers may be NULL (reaches the workspace check)
+    D0 = desc(Fs=0)
+    none = {n: None for n in ("sgu", "sdn", "g", "dsgu", "dsdn", "dg")}
+    assert call_backward(L, D0, 8, none, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
+    # T = 0: nothing is read or written
+    assert call_backward(L, D, 0, {n: None for n in BWD_PTRS}, ws=None, ws_bytes=0) == moe.MOE_OK
+
+
+def test_backward_workspace_grows_with_T(L):
+    D = desc()
+    sizes = [L.moe_backward_workspace_size(ctypes.byref(D), T) for T in (1, 10, 1000)]
+    assert 0 < sizes[0] < sizes[1] < sizes[2]
+    assert L.moe_backward_workspace_size(ctypes.byref(desc(E=0)), 10) == 0

@@ -1,0 +1,213 @@
+"""Parity of moe_backward (through the C ABI) with the oracle's backward pass.
+
+The routing (topk_idx, topk_w) and dout are inputs of both sides; the routing
+comes from the oracle's router.
+
+Bars, derived from the arithmetic of the bfloat16 path.  On the way to each
+gradient the kernels round about four operands to bfloat16 once each (dout,
+the pre-activations a and u, h or [da; du], dL; unit roundoff 2^-8, errors
+independent from element to element), accumulate in binary32, and bfloat16
+gradients are rounded once more when stored.  A rounding-faithful emulation
+of that scheme on the CPU gives an RMS error of 0.34% of RMS(oracle) and
+worst elements up to ~6% of RMS: an element dominated by one large product
+carries that product's rounding error.  The tests therefore bound
+  * RMS(g - oracle) <= 2^-7 RMS(oracle)                 (systematic errors);
+  * |g - oracle| <= 0.1 RMS(oracle) + 4 * 2^-8 |oracle|  element-wise (local
+    errors; the second term is four roundings of a single dominant product,
+    which is what an element of an expert with one or two tokens is);
+  * expert weight gradients are judged expert by expert (RMS of that expert's
+    gradient: its scale follows its own token count);
+  * binary32 layers (no bfloat16 rounding anywhere):
+    |g - oracle| <= 1e-4 RMS(oracle) element-wise;
+  * the auxiliary loss value: relative 1e-4 (binary32 softmax and sums).
+Index, sign or missing-term mistakes move elements by O(RMS) and fail the
+element-wise bar; a systematically wrong small term (e.g. the load-balancing
+gradient) is isolated by the test that drives the router with it alone.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_moe_feed_amd as moe
+import workloads as W
+from gpu_util import announce, to_dev
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("dw_router", "dw_gate_up", "dw_down", "dw_sh_gate_up", "dw_sh_down", "dsh_gate")
+WEIGHTS = ("x", "w_router", "w_gate_up", "w_down", "w_sh_gate_up", "w_sh_down", "sh_gate")
+
+
+def as_f64(t):
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return t.cpu().numpy().astype(np.float64)
+
+
+def check_grad(name, got, ref, bf16, sel=None, f32_layer=False):
+    """got: GPU tensor; ref: oracle float64 (NaN where not computed).  Expert
+    weight gradients ([E, ...]) are judged expert by expert: each one's
+    scale follows its own token count.  Returns the worst max|err| / RMS."""
+    g = as_f64(got)
+    if sel is not None:
+        g, ref = g[sel], ref[sel]
+    assert not np.isnan(ref).any(), name
+    groups = [(g, ref)] if ref.ndim < 3 else list(zip(g, ref))
+    worst = 0.0
+    for gi, ri in groups:
+        rms = np.sqrt((ri ** 2).mean())
+        err = np.abs(gi - ri)
+        if rms == 0:
+            assert err.max() == 0, name
+            continue
+        worst = max(worst, float(err.max() / rms))
+        if f32_layer:
+            assert np.all(err <= 1e-4 * rms), f"{name}: max|err|/rms = {err.max() / rms:.3e}"
+            continue
+        rms_err = np.sqrt((err ** 2).mean()) / rms
+        assert rms_err <= 2.0 ** -7, f"{name}: RMS err / RMS = {rms_err:.4f}"
+        bound = 0.1 * rms + 4 * 2.0 ** -8 * np.abs(ri)
+        assert np.all(err <= bound), f"{name}: max|err|/rms = {err.max() / rms:.4f}"
+    return worst
+
+
+def gpu_backward(inp, idx, w, dout, coef, bias=None):
+    ins = {n: to_dev(inp[n]) for n in WEIGHTS}
+    r = moe.backward(ins["x"], ins["w_router"], ins["w_gate_up"], ins["w_down"], to_dev(idx),
+                     to_dev(w.astype(np.float32)), to_dev(dout), ins["w_sh_gate_up"],
+                     ins["w_sh_down"], ins["sh_gate"], bias=to_dev(bias), aux_coef=coef)
+    torch.cuda.synchronize()
+    return r
+
+
+def oracle_backward(inp, idx, w, dout, coef, bias=None, **kw):
+    return oracle.backward(inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], idx, w,
+                           dout.astype(np.float64), inp["w_sh_gate_up"], inp["w_sh_down"],
+                           inp["sh_gate"], bias=bias, aux_coef=coef, **kw)
+
+
+def compare_all(inp, idx, w, dout, coef, bias, name, bf16=True):
+    announce(name)
+    got = gpu_backward(inp, idx, w, dout, coef, bias)
+    ref = oracle_backward(inp, idx, w, dout, coef, bias)
+    f32 = not bf16
+    worst = {"dx": check_grad("dx", got["dx"], ref["dx"], False, f32_layer=f32)}
+    Fs = 0 if inp["w_sh_gate_up"] is None else inp["w_sh_gate_up"].shape[0] // 2
+    for n in GRADS:
+        if Fs == 0 and n in ("dw_sh_gate_up", "dw_sh_down", "dsh_gate"):
+            assert got[n] is None
+            continue
+        worst[n] = check_grad(n, got[n], ref[n], bf16, f32_layer=f32)
+    aux = float(got["aux_loss"].cpu()[0])
+    assert aux == pytest.approx(ref["aux_loss"], rel=1e-4, abs=1e-12)
+    announce(f"{name}: max|err|/rms " + ", ".join(f"{k} {v:.4f}" for k, v in worst.items()))
+    return got, ref
+
+
+def routed_case(T, d, E, k, F, Fs, dtype, seed, bias):
+    inp = W.small_case(T, d, E, k, F, Fs, dtype, seed=seed)
+    b = (np.random.default_rng(seed + 3).standard_normal(E) * 0.5).astype(np.float32) \
+        if bias else None
+    idx, w = oracle.route(inp["x"], inp["w_router"], k, bias=b)
+    dout = W.make_dout(T, d, seed + 7)
+    return inp, idx, w, dout, b
+
+
+@pytest.mark.parametrize("T,d,E,k,F,Fs,coef,bias", [
+    (300, 256, 16, 4, 128, 128, 0.001, True),   # several tiles per expert
+    (200, 128, 24, 3, 64, 0, 0.01, False),      # no shared expert
+    (777, 320, 8, 2, 192, 64, 0.5, True),       # ragged tiles, d and F not multiples of 128
+    (20, 256, 64, 2, 128, 128, 0.001, False),   # most experts get no token: zero gradients
+    (1, 256, 16, 4, 128, 128, 0.001, False),    # one token
+])
+def test_backward_bf16_layers(T, d, E, k, F, Fs, coef, bias):
+    inp, idx, w, dout, b = routed_case(T, d, E, k, F, Fs, "bf16", T + E, bias)
+    got, _ = compare_all(inp, idx, w, dout, coef, b,
+                         f"backward bf16 T={T} d={d} E={E} k={k} F={F} Fs={Fs} coef={coef}")
+    unused = np.setdiff1d(np.arange(E), idx)
+    if len(unused):
+        assert not got["dw_gate_up"][unused].abs().max().item()
+        assert not got["dw_down"][unused].abs().max().item()
+
+
+def test_backward_pure_aux_loss():
+    """dout = 0: only the load-balancing loss drives the router, so the
+    expert weights get exact zeros and dW_router / dx are its gradient."""
+    inp, idx, w, _, b = routed_case(64, 256, 16, 4, 128, 128, "bf16", 5, True)
+    dout = np.zeros((64, 256), np.float32)
+    got, _ = compare_all(inp, idx, w, dout, 1.0, b, "backward: load-balancing loss only")
+    for n in ("dw_gate_up", "dw_down", "dw_sh_gate_up", "dw_sh_down", "dsh_gate"):
+        assert not got[n].abs().max().item(), n
+
+
+@pytest.mark.parametrize("T,d,E,k,F,Fs", [
+    (32, 128, 16, 4, 32, 32),    # the binary32 layer's shapes
+    (9, 100, 5, 2, 33, 7),       # widths that fill no tile
+])
+def test_backward_f32_layers(T, d, E, k, F, Fs):
+    inp, idx, w, dout, b = routed_case(T, d, E, k, F, Fs, "f32", 3, True)
+    compare_all(inp, idx, w, dout, 0.01, b, f"backward f32 T={T} d={d} F={F}", bf16=False)
+
+
+def test_backward_deterministic():
+    inp, idx, w, dout, b = routed_case(300, 256, 16, 4, 128, 128, "bf16", 9, True)
+    announce("backward determinism")
+    r1 = gpu_backward(inp, idx, w, dout, 0.01, b)
+    r2 = gpu_backward(inp, idx, w, dout, 0.01, b)
+    for n in ("dx",) + GRADS + ("aux_loss",):
+        assert torch.equal(r1[n], r2[n]), n
+
+
+def test_backward_full_shapes_small_batch():
+    """The pages' layer shapes (d 2560, 512 experts, top-10, widths 640) on 128
+    tokens: dx of every token, every router and shared gradient, and the
+    routed gradients of experts with and without tokens."""
+    cfg = W.CONFIGS[3]
+    lay = W.layer_for(cfg)
+    T = 128
+    x = W.make_x(T, cfg.d, "bf16", cfg.seed_x)
+    inp = dict(lay, x=x)
+    idx, w = oracle.route(x, lay["w_router"], cfg.k)
+    dout = W.make_dout(T, cfg.d, 17)
+    counts = np.bincount(idx.ravel(), minlength=cfg.E)
+    experts = list(np.argsort(-counts, kind="stable")[:4]) + list(np.nonzero(counts == 1)[0][:2]) \
+        + list(np.nonzero(counts == 0)[0][:2])
+    announce(f"backward full shapes T={T}: GPU")
+    got = gpu_backward(inp, idx, w, dout, 0.001)
+    announce(f"backward full shapes T={T}: oracle")
+    ref = oracle_backward(inp, idx, w, dout, 0.001, experts=experts)
+    check_grad("dx", got["dx"], ref["dx"], False)
+    for n in ("dw_router", "dw_sh_gate_up", "dw_sh_down", "dsh_gate"):
+        check_grad(n, got[n], ref[n], True)
+    for n in ("dw_gate_up", "dw_down"):
+        check_grad(n, got[n], ref[n], True, sel=np.array(experts))
+    assert float(got["aux_loss"].cpu()[0]) == pytest.approx(ref["aux_loss"], rel=1e-4)
+
+
+def test_backward_prefill_sampled():
+    """The timed training workload (T = 4096 at the pages' shapes): dx of
+    sampled tokens and the routed gradients of sampled experts against the
+    oracle, the loss value, and the softmax invariance sum_e dW_router[e] = 0
+    (within the bf16 rounding of the rows)."""
+    cfg = W.CONFIGS[3]
+    lay = W.layer_for(cfg)
+    x = W.make_x(cfg.T, cfg.d, "bf16", cfg.seed_x)
+    inp = dict(lay, x=x)
+    announce(f"{cfg.name} backward: oracle routing")
+    idx, w = oracle.route(x, lay["w_router"], cfg.k)
+    dout = W.make_dout(cfg.T, cfg.d, 23)
+    announce(f"{cfg.name} backward: GPU")
+    got = gpu_backward(inp, idx, w, dout, 0.001)
+    toks = np.unique(np.concatenate([[0, cfg.T - 1],
+                                     np.random.default_rng(4).choice(cfg.T, 14, replace=False)]))
+    experts = [int(e) for e in np.random.default_rng(5).choice(cfg.E, 3, replace=False)]
+    announce(f"{cfg.name} backward: oracle on {len(toks)} tokens, experts {experts}")
+    ref = oracle_backward(inp, idx, w, dout, 0.001, parts=oracle.DX | oracle.DW_ROUTED,
+                          tokens=toks, experts=experts)
+    check_grad("dx", got["dx"], ref["dx"], False, sel=toks)
+    for n in ("dw_gate_up", "dw_down"):
+        check_grad(n, got[n], ref[n], True, sel=np.array(experts))
+    assert float(got["aux_loss"].cpu()[0]) == pytest.approx(ref["aux_loss"], rel=1e-4)
+    dwr = as_f64(got["dw_router"])
+    assert np.abs(dwr.sum(axis=0)).max() <= 2.0 ** -8 * np.abs(dwr).sum(axis=0).max()

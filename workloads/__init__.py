@@ -41,7 +41,7 @@ import numpy as np
 WEIGHT_STD = 0.02
 
 # Independent counter streams per tensor: SeedSequence([seed, TENSOR_ID, i]).
-_X, _WR, _WGU, _WDN, _WSGU, _WSDN, _G, _BIAS = range(8)
+_X, _WR, _WGU, _WDN, _WSGU, _WSDN, _G, _BIAS, _DOUT = range(9)
 
 
 @dataclass(frozen=True)
@@ -252,6 +252,12 @@ def make_x(T: int, d: int, dtype: str, seed: int, row0: int = 0) -> np.ndarray:
     with ThreadPoolExecutor(_threads()) as ex:
         list(ex.map(block, range(b0, b1)))
     return out
+
+
+def make_dout(T: int, d: int, seed: int) -> np.ndarray:
+    """Gradient arriving at the layer's output for the backward pass:
+    dout ~ N(0,1), binary32 [T, d] (the layer's out is binary32)."""
+    return _rng(seed, _DOUT).standard_normal((T, d), dtype=np.float32)
 
 
 def zipf_bias(E: int, s: float, seed: int) -> np.ndarray:
