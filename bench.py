@@ -12,6 +12,10 @@ prefill-shaped layer (T=4096) is reported inside the same line under "also".
 recorded on the library's stream at its stage boundaries during the timed
 loop.  `cpu_baseline` times the CPU oracle on the host cores.
 
+`--config 9` (reported by default under "also") times the training backward
+pass of the prefill-shaped layer: one moe_backward call (dx and every weight
+gradient, plus the load-balancing loss) for the routing of its batch.
+
 `--config 7` measures the decode layer with its pre-FFN RMSNorm (one call:
 moe_forward_prenorm); `--config 6` measures the same decode layer with MXFP4 expert weights
 (moe_forward_mx4); its algorithmic weight bytes are 17/32 byte per element
@@ -76,6 +80,100 @@ def algorithmic(cfg, U: int):
                 gate_up_flops=flops_gu,
                 down_bytes=dn_w + (T * k * F + T * Fs) * b + T * k * d * b + T * d * 4,
                 down_flops=flops_dn)
+
+
+def algorithmic_backward(cfg, U: int):
+    """Algorithmic HBM bytes and FLOPs of one backward call (the contractions
+    of the gradient itself: 2x the forward's FLOPs; the recomputed gate/up
+    pre-activations and router logits are not counted) and of its three
+    single-kernel stages.  Bytes: each weight of a touched expert read once,
+    every weight gradient written (zeros for experts no token chose), x and
+    dout read, dx written."""
+    T, d, E, k, F, Fs = cfg.T, cfg.d, cfg.E, cfg.k, cfg.F, cfg.Fs
+    b = 2
+    rows, rows_sh = T * k, T
+    w_gu, w_dn = U * 2 * F * d * b + 2 * Fs * d * b, U * d * F * b + d * Fs * b
+    g_gu, g_dn = E * 2 * F * d * b + 2 * Fs * d * b, E * d * F * b + d * Fs * b
+    dgu_bytes = (rows * 2 * F + rows_sh * 2 * Fs) * b
+    call_bytes = (w_gu + w_dn + 2 * E * d * b + 2 * d * b + g_gu + g_dn
+                  + T * d * b + T * d * 4 + T * d * 4 + T * k * 8)
+    f_gu = 2 * (rows * 2 * F * d + rows_sh * 2 * Fs * d)
+    f_dn = 2 * (rows * d * F + rows_sh * d * Fs)
+    call_flops = 2 * (f_gu + f_dn) + 2 * 2 * T * d * (E + 1)
+    return dict(call_bytes=call_bytes, call_flops=call_flops,
+                dx_rows_bytes=w_gu + dgu_bytes + (rows + rows_sh) * d * b, dx_rows_flops=f_gu,
+                dw_gate_up_bytes=g_gu + dgu_bytes + (rows + rows_sh) * d * b,
+                dw_gate_up_flops=f_gu,
+                dw_down_bytes=g_dn + (rows + rows_sh) * d * 4 + (rows * F + rows_sh * Fs) * b,
+                dw_down_flops=f_dn)
+
+
+def measure_backward(cfg, dev_layer, steps, warmup):
+    import numpy as np
+    import torch
+
+    import sparse_moe_feed_amd as moe
+    import workloads as W
+
+    to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    x = to(W.make_x(cfg.T, cfg.d, cfg.dtype, cfg.seed_x))
+    dout = torch.from_numpy(W.dout_for(cfg)).cuda()
+    L = dev_layer
+    # the routing of this batch (an input of the backward pass)
+    _, idx, w = moe.forward(x, L["w_router"], L["w_gate_up"], L["w_down"], cfg.k,
+                            L["w_sh_gate_up"], L["w_sh_down"], L["sh_gate"])
+    shape = moe.shape_of(x, L["w_gate_up"], cfg.k, L["w_sh_gate_up"])
+    ws = torch.empty(moe.backward_workspace_size(shape, cfg.T), dtype=torch.uint8, device="cuda")
+    grads = moe.backward(x, L["w_router"], L["w_gate_up"], L["w_down"], idx, w, dout,
+                         L["w_sh_gate_up"], L["w_sh_down"], L["sh_gate"], aux_coef=cfg.aux_coef,
+                         ws=ws)
+    aux = grads.pop("aux_loss")
+
+    def step():
+        moe.backward(x, L["w_router"], L["w_gate_up"], L["w_down"], idx, w, dout,
+                     L["w_sh_gate_up"], L["w_sh_down"], L["sh_gate"], aux_coef=cfg.aux_coef,
+                     ws=ws, grads=grads, aux_loss=aux)
+    for _ in range(warmup):
+        step()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    n_ev = 1 + len(moe.BACKWARD_STAGES)
+    evs = [[moe.HipEvent() for _ in range(n_ev)] for _ in range(steps)]
+    for i in range(steps):
+        moe.stage_events(evs[i])
+        step()
+    torch.cuda.synchronize()
+    stage_ms = {name: sum(e[j].elapsed_ms(e[j + 1]) for e in evs) / steps
+                for j, name in enumerate(moe.BACKWARD_STAGES)}
+    U = int(np.unique(idx.cpu().numpy()).size)
+    return dict(ms=ms, stage_ms=stage_ms, U=U)
+
+
+def roofline_backward(cfg, r, workload):
+    a = algorithmic_backward(cfg, r["U"])
+    stage = max(("dx_rows", "dw_gate_up", "dw_down"), key=lambda s: r["stage_ms"][s])
+    t = r["stage_ms"][stage] * 1e-3
+    by, fl = a[f"{stage}_bytes"], a[f"{stage}_flops"]
+    bound = "hbm" if by / (HBM_PEAK_GBS * 1e9) >= fl / (MFMA_BF16_PEAK_TFLOPS * 1e12) else "mfma"
+    if bound == "hbm":
+        roof = dict(bound="hbm", achieved=round(by / t / 1e9, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(by / t / (HBM_PEAK_GBS * 1e9), 4))
+    else:
+        roof = dict(bound="mfma", achieved=round(fl / t / 1e12, 1), peak=MFMA_BF16_PEAK_TFLOPS,
+                    unit="TFLOP/s", frac=round(fl / t / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4))
+    roof.update(traffic=committed_traffic(workload, stage), kernel=stage,
+                kernel_ms=round(r["stage_ms"][stage], 4), alg_bytes=by, alg_flops=fl)
+    call_t = r["ms"] * 1e-3
+    layer = dict(hbm_frac=round(a["call_bytes"] / call_t / (HBM_PEAK_GBS * 1e9), 4),
+                 mfma_frac=round(a["call_flops"] / call_t / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
+                 alg_bytes=a["call_bytes"], alg_flops=a["call_flops"], unique_experts=r["U"])
+    return roof, layer
 
 
 def measure(cfg, dev_layer, steps, warmup):
@@ -152,6 +250,8 @@ def cpu_baseline(cfg, layer_np, seconds):
     import oracle
     import workloads as W
 
+    if cfg.backward:
+        return cpu_baseline_backward(cfg, layer_np, seconds)
     # a bounded sample: the first tokens of the batch (a token's output does
     # not depend on the others), about 1-2 s of oracle work per pass
     n = min(cfg.T, 32)
@@ -181,6 +281,36 @@ def cpu_baseline(cfg, layer_np, seconds):
                 sample=f"{what} of {cfg.name}, {reps} full passes in {el:.1f} s")
 
 
+def cpu_baseline_backward(cfg, layer_np, seconds):
+    """The oracle's backward pass on the first 8 tokens of the batch as a
+    batch of their own (routing, loss statistics and every gradient of that
+    batch; routed weight gradients of the experts those tokens chose)."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+
+    n = min(cfg.T, 8)
+    x = W.make_x(n, cfg.d, cfg.dtype, cfg.seed_x)
+    dout = W.dout_for(cfg)[:n]
+    L = layer_np
+    idx, w = oracle.route(x, L["w_router"], cfg.k)
+    experts = np.unique(idx)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.backward(x, L["w_router"], L["w_gate_up"], L["w_down"], idx, w, dout,
+                        L["w_sh_gate_up"], L["w_sh_down"], L["sh_gate"], aux_coef=cfg.aux_coef,
+                        experts=experts)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return dict(value=round(reps * n / el, 2), unit="tokens/s", cores=oracle.threads(),
+                kind="oracle",
+                sample=f"backward of the first {n} of {cfg.T} tokens of {cfg.name} as one batch, "
+                       f"{reps} full passes in {el:.1f} s")
+
+
 def device_layer(cfg, layer_np):
     """The layer's weights on the GPU: bf16 tensors, or (codes, scales) uint8
     pairs for MXFP4 expert weights."""
@@ -208,7 +338,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, help="workload of `value` (2 = decode T=32)")
-    ap.add_argument("--also", default="3", help="extra workloads reported in the line")
+    ap.add_argument("--also", default="3,9", help="extra workloads reported in the line")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -238,8 +368,11 @@ def main():
     cfg = W.CONFIGS[args.config]
     layer_np = W.layer_for(cfg)
     dev_layer = device_layer(cfg, layer_np)
-    r = measure(cfg, dev_layer, args.steps, args.warmup)
-    roof, layer = roofline_of(cfg, r, cfg.name)
+    run = lambda c, steps: (measure_backward if c.backward else measure)(c, dev_layer, steps,
+                                                                        args.warmup)
+    roof_of = lambda c, rr: (roofline_backward if c.backward else roofline_of)(c, rr, c.name)
+    r = run(cfg, args.steps)
+    roof, layer = roof_of(cfg, r)
     also = {}
     for c in [int(v) for v in args.also.split(",") if v]:
         c_cfg = W.CONFIGS[c]
@@ -247,8 +380,8 @@ def main():
             print(f"bench.py: --also {c} skipped ({c_cfg.name} uses another layer)",
                   file=sys.stderr)
             continue
-        rc = measure(c_cfg, dev_layer, max(3, args.steps // 2), args.warmup)
-        rroof, rlayer = roofline_of(c_cfg, rc, c_cfg.name)
+        rc = run(c_cfg, max(3, args.steps // 2))
+        rroof, rlayer = roof_of(c_cfg, rc)
         also[c_cfg.name] = dict(value=round(c_cfg.T / (rc["ms"] * 1e-3), 1), unit="tokens/s",
                                 ms_per_step=round(rc["ms"], 4), roofline=rroof, layer=rlayer,
                                 stage_ms={k: round(v, 4) for k, v in rc["stage_ms"].items()})
@@ -271,7 +404,8 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d, "experts": cfg.E,
                    "top_k": cfg.k, "d_expert": cfg.F, "d_shared": cfg.Fs, "router_bias": cfg.bias,
                    "expert_weights": "mxfp4" if cfg.dtype == "mxfp4" else "bf16",
-                   "pre_norm": "rmsnorm" if cfg.prenorm else None},
+                   "pre_norm": "rmsnorm" if cfg.prenorm else None,
+                   "pass": "backward" if cfg.backward else "forward"},
         "roofline": roof,
         "layer": layer,
         "stage_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},

@@ -321,9 +321,10 @@ def backward(x, w_router, w_gate_up, w_down, topk_idx, topk_w, dout, w_sh_gate_u
     routing (topk_idx, topk_w) given, in float64.  Returns a dict with dx
     [T,d], dw_router [E,d], dw_gate_up [E,2F,d], dw_down [E,d,F],
     dw_sh_gate_up [2Fs,d], dw_sh_down [d,Fs], dsh_gate [d] and aux_loss.
-    parts / tokens / experts restrict the work (dx of the listed tokens, the
-    routed weight gradients of the listed experts); what is not computed is
-    NaN."""
+    parts / tokens / experts restrict the work: dx of the listed tokens (the
+    other rows NaN), the routed weight gradients of the listed experts (then
+    dw_gate_up / dw_down hold only those, in the order listed).  Outputs of
+    parts not asked for are None."""
     T, d = x.shape
     E, twoF, _ = w_gate_up.shape
     F = twoF // 2
@@ -338,24 +339,30 @@ def backward(x, w_router, w_gate_up, w_down, topk_idx, topk_w, dout, w_sh_gate_u
     if g.shape != (T, d) or idx.shape != (T, k) or w.shape != (T, k):
         raise ValueError("dout must be [T, d], topk_idx / topk_w [T, k]")
     tok = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int32)
-    sel = None
+    slot, n_exp = None, E
     if experts is not None:
-        sel = np.zeros(E, np.uint8)
-        sel[np.asarray(experts, dtype=np.int64)] = 1
+        experts = np.asarray(experts, dtype=np.int64)
+        if len(np.unique(experts)) != len(experts) or (experts < 0).any() or (experts >= E).any():
+            raise ValueError("experts must be distinct indices in [0, E)")
+        slot = np.full(E, -1, np.int32)
+        slot[experts] = np.arange(len(experts), dtype=np.int32)
+        n_exp = len(experts)
 
-    def nan(*shape):
-        return np.full(shape, np.nan, np.float64)
-    r = dict(dx=nan(T, d), dw_router=nan(E, d), dw_gate_up=nan(E, 2 * F, d),
-             dw_down=nan(E, d, F), dw_sh_gate_up=nan(2 * Fs, d), dw_sh_down=nan(d, Fs),
-             dsh_gate=nan(d))
+    def nan(want, *shape):
+        return np.full(shape, np.nan, np.float64) if want else None
+    r = dict(dx=nan(parts & DX, T, d), dw_router=nan(parts & DW_ROUTER, E, d),
+             dw_gate_up=nan(parts & DW_ROUTED, n_exp, 2 * F, d),
+             dw_down=nan(parts & DW_ROUTED, n_exp, d, F),
+             dw_sh_gate_up=nan(parts & DW_SHARED, 2 * Fs, d),
+             dw_sh_down=nan(parts & DW_SHARED, d, Fs), dsh_gate=nan(parts & DW_SHARED, d))
     aux = ctypes.c_double(np.nan)
     rc = _load().oracle_backward(
         T, d, E, k, F, Fs, dt, _ptr(x), _ptr(w_router), _ptr(b), _ptr(w_gate_up),
         _ptr(w_down), _ptr(w_sh_gate_up), _ptr(w_sh_down), _ptr(sh_gate), _ptr(idx), _ptr(w),
         _ptr(g), ctypes.c_double(aux_coef), parts, _ptr(tok), 0 if tok is None else len(tok),
-        _ptr(sel), _ptr(r["dx"]), _ptr(r["dw_router"]), _ptr(r["dw_gate_up"]),
-        _ptr(r["dw_down"]), _ptr(r["dw_sh_gate_up"]), _ptr(r["dw_sh_down"]),
-        _ptr(r["dsh_gate"]), ctypes.byref(aux))
+        _ptr(slot), *[_ptr(r[n]) for n in ("dx", "dw_router", "dw_gate_up", "dw_down",
+                                           "dw_sh_gate_up", "dw_sh_down", "dsh_gate")],
+        ctypes.byref(aux))
     if rc:
         raise RuntimeError(f"oracle_backward failed ({rc})")
     r["aux_loss"] = aux.value

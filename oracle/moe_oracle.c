@@ -512,7 +512,8 @@ int oracle_forward_mx4(int64_t T, int d, int E, int k, int F, int Fs,
  *
  * parts selects what is computed (the rest of the outputs is left as is):
  *     1 dx of the tokens in tok_sel (all tokens when tok_sel is NULL)
- *     2 dW_gu, dW_dn of the experts e with exp_sel[e] != 0 (all when NULL)
+ *     2 dW_gu, dW_dn of the experts e with exp_slot[e] >= 0, written to
+ *       slot exp_slot[e] of dw_gu / dw_dn (exp_slot NULL: every expert, slot e)
  *     4 dW_sgu, dW_sdn and dsh_gate (shared expert and its gate)
  *     8 dW_router
  * aux_loss (nullable) receives L_aux.  Returns 0, 1 on bad arguments, 2 when
@@ -554,7 +555,7 @@ int oracle_backward(int64_t T, int d, int E, int k, int F, int Fs, int dtype,
                     const void *sh_gate, const int32_t *topk_idx,
                     const double *topk_w, const double *dout, double coef,
                     int parts, const int32_t *tok_sel, int64_t n_tok_sel,
-                    const uint8_t *exp_sel, double *dx, double *dw_router,
+                    const int32_t *exp_slot, double *dx, double *dw_router,
                     double *dw_gu, double *dw_dn, double *dw_sgu,
                     double *dw_sdn, double *dsh_gate, double *aux_loss)
 {
@@ -610,7 +611,7 @@ int oracle_backward(int64_t T, int d, int E, int k, int F, int Fs, int dtype,
     for (int64_t i = 0; i < P; i++) {
         int e = topk_idx[i];
         f[e] += 1.0; /* count first, divide once below */
-        if (tok_need[i / k] || ((parts & 2) && (!exp_sel || exp_sel[e])))
+        if (tok_need[i / k] || ((parts & 2) && (!exp_slot || exp_slot[e] >= 0)))
             pair_need[i] = 1;
     }
     for (int e = 0; e < E; e++)
@@ -706,10 +707,11 @@ int oracle_backward(int64_t T, int d, int E, int k, int F, int Fs, int dtype,
     if (parts & 2) {
 #pragma omp parallel for schedule(dynamic, 1)
         for (int e = 0; e < E; e++) {
-            if (exp_sel && !exp_sel[e])
+            if (exp_slot && exp_slot[e] < 0)
                 continue;
-            double *g = dw_gu + (int64_t)e * 2 * F * d;
-            double *dd = dw_dn + (int64_t)e * d * F;
+            int64_t slot = exp_slot ? exp_slot[e] : e;
+            double *g = dw_gu + slot * 2 * F * d;
+            double *dd = dw_dn + slot * d * F;
             memset(g, 0, sizeof(double) * (size_t)(2 * F * d));
             memset(dd, 0, sizeof(double) * (size_t)(d * F));
             for (int64_t i = 0; i < P; i++) {

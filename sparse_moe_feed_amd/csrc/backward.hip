@@ -74,6 +74,8 @@ struct Job {
     int64_t ldc;
     int c_alt;
     int mrows, ncols, K;
+    int N;       // output columns of the job (weight gradients)
+    bool c_f32;  // binary32 output whatever the kind's (split reductions' partials)
 };
 
 constexpr int QB = 128;           // tile rows and columns
@@ -142,6 +144,38 @@ __device__ __forceinline__ bool map_tile(const BwdArgs &a, int tile, MapTile &t)
     return t.nrows > 0;
 }
 
+// Block -> (bx, by) of the job grid, for a 1-D launch of nblocks(...) blocks.
+// Workgroups go to the 8 XCDs round robin (block b on XCD b % 8) and each
+// XCD has its own L2, so the blocks that share operands are kept on one XCD:
+//   weight gradients: every tile of one expert (its rows of X / dOut and of
+//     [da; du] / H, about 0.6-0.9 MB at the pages' shapes) on XCD g % 8, the
+//     column tiles of one row tile consecutive;
+//   the others: row tile m on XCD m % 8 with its column tiles consecutive
+//     (the tile's gathered rows are read once per XCD).
+template <int KIND>
+__device__ __forceinline__ bool block_tile(int nx, int ny, int groups, int &bx, int &by) {
+    const int b = blockIdx.x, x = b & 7, q = b >> 3;
+    if (KIND == K_DWGU || KIND == K_DWDN) {
+        const int mtiles = nx / groups;          // row tiles per group
+        const int per = mtiles * ny;             // tiles per group
+        const int g = 8 * (q / per) + x;
+        if (g >= groups) return false;
+        const int r = q - (q / per) * per;
+        bx = g * mtiles + r / ny;
+        by = r - (r / ny) * ny;
+        return true;
+    }
+    by = q % ny;
+    bx = 8 * (q / ny) + x;
+    return bx < nx;
+}
+
+__host__ __device__ inline unsigned bwd_blocks(int kind, int nx, int ny, int groups) {
+    if (kind == K_DWGU || kind == K_DWDN)
+        return 8u * (unsigned)((groups + 7) / 8) * (unsigned)(nx / groups) * (unsigned)ny;
+    return 8u * (unsigned)((nx + 7) / 8) * (unsigned)ny;
+}
+
 // The job of block (bx, by) for a contraction kind; false: nothing to do.
 // esize: bytes per element of the layer's dtype (2 bf16, 4 binary32).
 template <int KIND>
@@ -150,6 +184,7 @@ __device__ bool make_job(const BwdArgs &a, int bx, int by, int es, Job &j) {
     const int sh_rows = a.Fs > 0 ? 1 : 0;  // router row E (the shared gate) exists
     j.c_alt = INT_MAX;
     j.c_alt_p = nullptr;
+    j.c_f32 = false;
     if (KIND == K_LOGITS || KIND == K_DXR || KIND == K_DWR) {
         const int m0 = QB * bx, n0 = QB * by;
         if (KIND == K_LOGITS) {
@@ -234,12 +269,16 @@ __device__ bool make_job(const BwdArgs &a, int bx, int by, int es, Job &j) {
         }
         return true;
     }
-    // K_DWGU / K_DWDN: one group (expert, or E = shared) per run of M-tiles
+    // K_DWGU / K_DWDN: one group per run of M-tiles: the experts, then the
+    // shared expert (groups E .. E + sh_split - 1: its reduction over the
+    // tokens split into chunks of sh_chunk rows, each chunk's binary32
+    // partial written to part[chunk], when sh_split > 0)
     const int Fmax = a.F > a.Fs ? a.F : a.Fs;
     const int mtiles = KIND == K_DWGU ? (2 * Fmax + QB - 1) / QB : (d + QB - 1) / QB;
     const int g = bx / mtiles, mt = bx - g * mtiles;
-    if (g > E || (g == E && a.Fs == 0)) return false;
-    const bool shared = g == E;
+    if (g >= E + (a.sh_split > 0 ? a.sh_split : 1) || (g >= E && a.Fs == 0)) return false;
+    const bool shared = g >= E;
+    const int sp = g - E;
     const int Fg = shared ? a.Fs : a.F;
     const int M = KIND == K_DWGU ? 2 * Fg : d;
     const int N = KIND == K_DWGU ? d : Fg;
@@ -247,9 +286,19 @@ __device__ bool make_job(const BwdArgs &a, int bx, int by, int es, Job &j) {
     if (m0 >= M || n0 >= N) return false;
     j.mrows = min(QB, M - m0);
     j.ncols = min(QB, N - n0);
-    const int rb = shared ? 0 : a.offsets[g];
-    const int cnt = shared ? (int)a.T : a.counts[g];
+    int rb = 0, cnt = (int)a.T;
+    if (!shared) {
+        rb = a.offsets[g];
+        cnt = a.counts[g];
+    } else if (a.sh_split > 0) {
+        rb = sp * a.sh_chunk;
+        cnt = min(a.sh_chunk, (int)a.T - rb);
+        if (cnt <= 0) return false;
+    }
+    // groups up to dw_kmin rows are done by the short-reduction kernel
+    if ((!shared || a.sh_split == 0) && cnt <= a.dw_kmin) return false;
     j.K = cnt;
+    j.N = N;
     if (KIND == K_DWGU) {
         j.a = opnd(shared ? a.dgu_sh : a.dgu, 2 * Fg, rb, rb + cnt, es);
         j.b = opnd(a.x, d, rb, rb + cnt, es);
@@ -265,6 +314,11 @@ __device__ bool make_job(const BwdArgs &a, int bx, int by, int es, Job &j) {
                       : static_cast<char *>(a.dw_dn) + (int64_t)g * d * a.F * es) +
               ((int64_t)m0 * Fg + n0) * es;
         j.ldc = (int64_t)Fg * es;
+    }
+    if (shared && a.sh_split > 0) {
+        j.c = reinterpret_cast<char *>(a.part + (int64_t)sp * M * N + (int64_t)m0 * N + n0);
+        j.ldc = (int64_t)N * 4;
+        j.c_f32 = true;
     }
     j.a.cb = m0;
     j.a.ilim = j.mrows;
@@ -337,19 +391,26 @@ struct StageMC {
     float scl[2];   // scales of the looked-up step
     float sld[2];   // scales of the step whose data is in r / r2
     bool live[2];
+    bool okd[2][2]; // which of r / r2 hold data (else they are stored as zeros)
     uint4 r[2][2], r2[2][2];
     int kp, i0;
     __device__ void init(int tid) {
         kp = tid & 31;
         i0 = 8 * (tid >> 5);
     }
+    // Branch-free: every lane looks up and loads a valid address (a row past
+    // the end reads the last valid row, a column piece past the end reads
+    // piece 0) and selects zero afterwards.  A branch around a load makes the compiler wait for
+    // every memory operation in flight (stores included) at the next use.
     __device__ void lookup(const Opnd &o, int k0) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int s = o.base + k0 + 2 * kp + h;
             live[h] = s < o.lim;
-            rows[h] = live[h] ? op_row(o, s, scl[h]) : o.p;
-            if (!live[h]) scl[h] = 0.f;
+            const int sc_idx = max(min(s, o.lim - 1), 0);
+            float sc;
+            rows[h] = op_row(o, sc_idx, sc);
+            scl[h] = live[h] ? sc : 0.f;
         }
     }
     __device__ void load(const Opnd &o) {
@@ -360,27 +421,29 @@ struct StageMC {
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const int i = i0 + 64 * q;
-                const bool ok = live[h] && i < o.ilim;
-                const char *p = rows[h] + (int64_t)(o.cb + i) * (F32 ? 4 : 2);
+                okd[h][q] = live[h] && i < o.ilim;
+                const int ic = i < o.ilim ? i : 0;  // piece 0 of a row is always readable
+                const char *p = rows[h] + (int64_t)(o.cb + ic) * (F32 ? 4 : 2);
+                // the zero select waits until store(), so nothing waits for
+                // the data before the step that writes it to LDS
                 if (F32) {
-                    r[h][q] = ok ? __builtin_bit_cast(uint4, reinterpret_cast<const float4 *>(p)[0])
-                                 : uint4{0, 0, 0, 0};
-                    r2[h][q] = ok ? __builtin_bit_cast(uint4, reinterpret_cast<const float4 *>(p)[1])
-                                  : uint4{0, 0, 0, 0};
+                    r[h][q] = __builtin_bit_cast(uint4, reinterpret_cast<const float4 *>(p)[0]);
+                    r2[h][q] = __builtin_bit_cast(uint4, reinterpret_cast<const float4 *>(p)[1]);
                 } else {
-                    r[h][q] = ok ? *reinterpret_cast<const uint4 *>(p) : uint4{0, 0, 0, 0};
+                    r[h][q] = *reinterpret_cast<const uint4 *>(p);
                 }
             }
     }
-    __device__ void store(uint16_t *lds) {
+    __device__ void store(uint16_t *lds, int pitch = QLD, int koff = 0) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             uint32_t v[2][8];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
+                const uint4 z = uint4{0, 0, 0, 0};
                 if (F32) {
                     const float s = sld[h];
-                    const uint4 &a = r[h][q], &b = r2[h][q];
+                    const uint4 a = okd[h][q] ? r[h][q] : z, b = okd[h][q] ? r2[h][q] : z;
                     v[h][0] = f32_to_bf16_rne(s * __uint_as_float(a.x));
                     v[h][1] = f32_to_bf16_rne(s * __uint_as_float(a.y));
                     v[h][2] = f32_to_bf16_rne(s * __uint_as_float(a.z));
@@ -390,7 +453,7 @@ struct StageMC {
                     v[h][6] = f32_to_bf16_rne(s * __uint_as_float(b.z));
                     v[h][7] = f32_to_bf16_rne(s * __uint_as_float(b.w));
                 } else {
-                    const uint4 &a = r[h][q];
+                    const uint4 a = okd[h][q] ? r[h][q] : z;
                     v[h][0] = a.x & 0xFFFFu; v[h][1] = a.x >> 16;
                     v[h][2] = a.y & 0xFFFFu; v[h][3] = a.y >> 16;
                     v[h][4] = a.z & 0xFFFFu; v[h][5] = a.z >> 16;
@@ -400,7 +463,8 @@ struct StageMC {
             const int i = i0 + 64 * q;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                *reinterpret_cast<uint32_t *>(lds + (i + e) * QLD + 2 * kp) = v[0][e] | (v[1][e] << 16);
+                *reinterpret_cast<uint32_t *>(lds + (i + e) * pitch + koff + 2 * kp) =
+                    v[0][e] | (v[1][e] << 16);
         }
     }
 };
@@ -424,18 +488,70 @@ template <bool F32> struct Stager<false, F32> {
     __device__ void store(uint16_t *lds, int) { s.store(lds); }
 };
 
-// bfloat16 layers: 128 x 128 tiles, 4 waves in 2 x 2, each 64 x 64 from
-// v_mfma_f32_32x32x16_bf16; register-staged double buffer in LDS.
+// Store one accumulated tile (accumulator layout: lane holds column lane % 32
+// and rows 8 (v / 4) + 4 (lane / 32) + (v % 4)).
+template <bool C_F32>
+__device__ __forceinline__ void store_tile(const Job &j, f32x16 (&acc)[2][2], int wm, int wn,
+                                           int lane) {
+    const int fr = lane & 31;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int row = 64 * wm + 32 * mi + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            if (row >= j.mrows) continue;
+            char *crow = row >= j.c_alt ? j.c_alt_p + (int64_t)(row - j.c_alt) * j.ldc
+                                        : j.c + (int64_t)row * j.ldc;
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni) {
+                const int col = 64 * wn + 32 * ni + fr;
+                if (col >= j.ncols) continue;
+                if (C_F32 || j.c_f32)
+                    reinterpret_cast<float *>(crow)[col] = acc[mi][ni][v];
+                else
+                    reinterpret_cast<uint16_t *>(crow)[col] = f32_to_bf16_rne(acc[mi][ni][v]);
+            }
+        }
+}
+
+// One QK step of the 128 x 128 tile from LDS: 4 waves in 2 x 2, each 64 x 64
+// from v_mfma_f32_32x32x16_bf16.
+__device__ __forceinline__ void mfma_step(const uint16_t *As, const uint16_t *Bs,
+                                          f32x16 (&acc)[2][2], int wm, int wn, int lane) {
+    const int fr = lane & 31, fk = 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < QK / 16; ++ks) {
+        bf16x8 af[2], bfr[2];
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+            af[mi] = *reinterpret_cast<const bf16x8 *>(
+                &As[(64 * wm + 32 * mi + fr) * QLD + 16 * ks + fk]);
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+            bfr[ni] = *reinterpret_cast<const bf16x8 *>(
+                &Bs[(64 * wn + 32 * ni + fr) * QLD + 16 * ks + fk]);
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni],
+                                                                      acc[mi][ni], 0, 0, 0);
+    }
+}
+
+// bfloat16 layers, long reductions: 128 x 128 tiles, register-staged double
+// buffer in LDS (the next step's loads fly while this one computes); two
+// blocks per CU.
 template <int KIND>
-__global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(BwdArgs a, int nx, int ny, int groups) {
     using Tr = Traits<KIND>;
     __shared__ __align__(16) uint16_t As[2][QB * QLD];
     __shared__ __align__(16) uint16_t Bs[2][QB * QLD];
     Job j;
-    if (!make_job<KIND>(a, blockIdx.x, blockIdx.y, 2, j)) return;
+    int bx, by;
+    if (!block_tile<KIND>(nx, ny, groups, bx, by) || !make_job<KIND>(a, bx, by, 2, j)) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int wm = wave >> 1, wn = wave & 1;
-    const int fr = lane & 31, fk = 8 * (lane >> 5);
     Stager<Tr::A_KC, Tr::A_F32> sa;
     Stager<Tr::B_KC, Tr::B_F32> sb;
     sa.init(j.a, tid);
@@ -473,17 +589,93 @@ __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(BwdArgs a) {
                 sb.lookup(j.b, (kt + 2) * QK);
             }
         }
+        mfma_step(As[cur], Bs[cur], acc, wm, wn, lane);
+        if (kt + 1 < nk) {
+            sa.store(As[cur ^ 1], tid);
+            sb.store(Bs[cur ^ 1], tid);
+        }
+        __syncthreads();
+    }
+    store_tile<Tr::C_F32>(j, acc, wm, wn, lane);
+}
+
+// Weight gradients of experts with at most KS rows (the usual case: T k / E
+// rows per expert on average), bfloat16 layers.  Block (expert g, row tile
+// mt) stages its A tile -- 128 output rows x all K <= KS reduction rows --
+// in LDS once (with the row lookups through the permutation done once), then
+// walks every column tile of its rows: the next tile's B rows are loaded into
+// registers while the current one computes, and each finished tile goes out
+// through LDS as 16-byte row pieces, so a tile costs 8 stores per thread and
+// the next tile's loads do not wait behind a long tail of small stores.
+constexpr int KS = 128;
+constexpr int SLD = KS + 8;  // LDS row: 272 bytes (16 consecutive rows hit distinct banks)
+
+template <int KIND>
+__global__ __launch_bounds__(256, 2) void bwd_dw_small_kernel(BwdArgs a, int nx, int groups) {
+    using Tr = Traits<KIND>;
+    __shared__ __align__(16) uint16_t As[QB * SLD];
+    __shared__ __align__(16) uint16_t Bs[QB * SLD];  // also the output staging
+    Job j;
+    int bx, by;
+    if (!block_tile<KIND>(nx, 1, groups, bx, by)) return;
+    BwdArgs aa = a;
+    aa.dw_kmin = -1;  // every group with at most KS rows
+    if (!make_job<KIND>(aa, bx, 0, 2, j) || j.K > KS) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const int wm = wave >> 1, wn = wave & 1;
+    const int fr = lane & 31, fk = 8 * (lane >> 5);
+    const int ntiles = (j.N + QB - 1) / QB;
+
+    StageMC<Tr::A_F32> sa0, sa1;
+    StageMC<false> sb0, sb1;
+    sa0.init(tid);
+    sa1.init(tid);
+    sb0.init(tid);
+    sb1.init(tid);
+    sa0.lookup(j.a, 0);
+    sa1.lookup(j.a, QK);
+    sb0.lookup(j.b, 0);
+    sb1.lookup(j.b, QK);
+    sa0.load(j.a);
+    sa1.load(j.a);
+    sb0.load(j.b);
+    sb1.load(j.b);
+    sa0.store(As, SLD, 0);
+    sa1.store(As, SLD, QK);
+    sb0.store(Bs, SLD, 0);
+    sb1.store(Bs, SLD, QK);
+    __syncthreads();
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int n0 = QB * t, ncols = min(QB, j.N - n0);
+        // the next tile's B rows (the last iteration reloads its own tile: no
+        // branch, see StageMC)
+        const int tn = t + 1 < ntiles ? t + 1 : t;
+        j.b.cb = QB * tn;
+        j.b.ilim = min(QB, j.N - QB * tn);
+        sb0.load(j.b);
+        sb1.load(j.b);
+        // keep the loads ahead of the MFMAs and the next tile's packing after
+        // them (interleaving them only raises register pressure)
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 acc[2][2];
 #pragma unroll
-        for (int ks = 0; ks < QK / 16; ++ks) {
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS / 16; ++ks) {
             bf16x8 af[2], bfr[2];
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
                 af[mi] = *reinterpret_cast<const bf16x8 *>(
-                    &As[cur][(64 * wm + 32 * mi + fr) * QLD + 16 * ks + fk]);
+                    &As[(64 * wm + 32 * mi + fr) * SLD + 16 * ks + fk]);
 #pragma unroll
             for (int ni = 0; ni < 2; ++ni)
                 bfr[ni] = *reinterpret_cast<const bf16x8 *>(
-                    &Bs[cur][(64 * wn + 32 * ni + fr) * QLD + 16 * ks + fk]);
+                    &Bs[(64 * wn + 32 * ni + fr) * SLD + 16 * ks + fk]);
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
@@ -491,33 +683,35 @@ __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(BwdArgs a) {
                     acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni],
                                                                           acc[mi][ni], 0, 0, 0);
         }
-        if (kt + 1 < nk) {
-            sa.store(As[cur ^ 1], tid);
-            sb.store(Bs[cur ^ 1], tid);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();  // every wave is done reading Bs
+        // the tile as bf16 rows in Bs (accumulator layout: lane holds column
+        // lane % 32 and rows 8 (v / 4) + 4 (lane / 32) + (v % 4))
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int row = 64 * wm + 32 * mi + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    Bs[row * SLD + 64 * wn + 32 * ni + fr] = f32_to_bf16_rne(acc[mi][ni][v]);
+                }
+        __syncthreads();
+        char *c = j.c + (int64_t)n0 * 2;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            // pieces outside the tile rewrite a piece inside it with its own
+            // bytes (no branch around the store)
+            const int ch = tid + 256 * q;
+            const int row = min(ch >> 4, j.mrows - 1), c8 = min(8 * (ch & 15), ncols - 8);
+            *reinterpret_cast<uint4 *>(c + (int64_t)row * j.ldc + c8 * 2) =
+                *reinterpret_cast<const uint4 *>(&Bs[row * SLD + c8]);
         }
+        __syncthreads();  // the staged tile is read out
+        sb0.store(Bs, SLD, 0);
+        sb1.store(Bs, SLD, QK);
         __syncthreads();
     }
-
-    // accumulator layout: lane holds column lane % 32 and rows
-    // 8 (v / 4) + 4 (lane / 32) + (v % 4)
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int row = 64 * wm + 32 * mi + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            if (row >= j.mrows) continue;
-            char *crow = row >= j.c_alt ? j.c_alt_p + (int64_t)(row - j.c_alt) * j.ldc
-                                        : j.c + (int64_t)row * j.ldc;
-#pragma unroll
-            for (int ni = 0; ni < 2; ++ni) {
-                const int col = 64 * wn + 32 * ni + fr;
-                if (col >= j.ncols) continue;
-                if (Tr::C_F32)
-                    reinterpret_cast<float *>(crow)[col] = acc[mi][ni][v];
-                else
-                    reinterpret_cast<uint16_t *>(crow)[col] = f32_to_bf16_rne(acc[mi][ni][v]);
-            }
-        }
 }
 
 // binary32 layers: the same jobs, one output element per thread and step,
@@ -713,13 +907,38 @@ __global__ __launch_bounds__(256) void aux_loss_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 
+// nx row tiles (weight gradients: groups x row tiles per group) by ny column
+// tiles.
 template <int KIND>
-static void launch_gemm(const BwdArgs &a, dim3 grid, hipStream_t s) {
-    if (grid.x == 0 || grid.y == 0) return;
-    if (a.bf16)
-        hipLaunchKernelGGL(bwd_gemm_kernel<KIND>, grid, dim3(256), 0, s, a);
+static void launch_gemm(const BwdArgs &a, unsigned nx, unsigned ny, hipStream_t s,
+                        int groups = 1) {
+    if (nx == 0 || ny == 0) return;
+    const dim3 grid(bwd_blocks(KIND, (int)nx, (int)ny, groups));
+    if (!a.bf16)
+        hipLaunchKernelGGL(bwd_gemm_f32_kernel<KIND>, dim3(nx, ny), dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL(bwd_gemm_f32_kernel<KIND>, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(bwd_gemm_kernel<KIND>, grid, dim3(256), 0, s, a, (int)nx, (int)ny,
+                           groups);
+}
+
+// Shared expert's weight gradient from its split reduction: out = the sum of
+// the S binary32 partials in chunk order, rounded to bf16.
+__global__ __launch_bounds__(256) void sh_reduce_kernel(const float *__restrict__ part, int S,
+                                                        int64_t n, uint16_t *__restrict__ out) {
+    const int64_t i = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
+    if (i >= n) return;
+    float4 acc = *reinterpret_cast<const float4 *>(part + i);
+    for (int sp = 1; sp < S; ++sp) {
+        const float4 v = *reinterpret_cast<const float4 *>(part + (int64_t)sp * n + i);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+    }
+    uint2 q;
+    q.x = pack_bf16x2(acc.x, acc.y);
+    q.y = pack_bf16x2(acc.z, acc.w);
+    *reinterpret_cast<uint2 *>(out + i) = q;
 }
 
 static unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
@@ -730,10 +949,10 @@ hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
     if (err != hipSuccess) return err;
     const int Fmax = a.F > a.Fs ? a.F : a.Fs;
     const unsigned tiles = (unsigned)pp.max_tiles;
-    launch_gemm<K_LOGITS>(a, dim3(cdiv(a.T, QB), cdiv(a.E + 1, QB)), s);
+    launch_gemm<K_LOGITS>(a, cdiv(a.T, QB), cdiv(a.E + 1, QB), s);
     mark(1);
-    launch_gemm<K_AU>(a, dim3(tiles, cdiv(2 * Fmax, QB)), s);
-    launch_gemm<K_G>(a, dim3(tiles, cdiv(Fmax, QB)), s);
+    launch_gemm<K_AU>(a, tiles, cdiv(2 * Fmax, QB), s);
+    launch_gemm<K_G>(a, tiles, cdiv(Fmax, QB), s);
     mark(2);
     const int64_t rows = (int64_t)a.T * a.k + (a.Fs > 0 ? a.T : 0);
     const size_t lds = (size_t)a.ldd * sizeof(float);
@@ -745,14 +964,41 @@ hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
         hipLaunchKernelGGL(router_bwd_kernel<float>, dim3((unsigned)a.T), dim3(256), lds, s, a);
     }
     mark(3);
-    launch_gemm<K_DX>(a, dim3(tiles, cdiv(a.d, QB)), s);
+    launch_gemm<K_DX>(a, tiles, cdiv(a.d, QB), s);
     mark(4);
-    launch_gemm<K_DWGU>(a, dim3((unsigned)(a.E + 1) * cdiv(2 * Fmax, QB), cdiv(a.d, QB)), s);
+    // The weight gradients reduce over one expert's rows: experts (and a
+    // shared expert over T <= KS tokens) with at most KS rows in the
+    // short-reduction kernel, the rest in the tiled one; the shared expert
+    // over more tokens splits its reduction into sh_split chunks.
+    BwdArgs ab = a;
+    ab.dw_kmin = a.bf16 ? KS : -1;
+    const int g_small = a.E + (a.Fs > 0 && a.sh_split == 0 ? 1 : 0);
+    const int g_all = a.E + (a.Fs > 0 ? (a.sh_split > 0 ? a.sh_split : 1) : 0);
+    const unsigned gu_m = cdiv(2 * Fmax, QB), dn_m = cdiv(a.d, QB);
+    if (a.bf16)
+        hipLaunchKernelGGL(bwd_dw_small_kernel<K_DWGU>,
+                           dim3(bwd_blocks(K_DWGU, g_small * gu_m, 1, g_small)), dim3(256), 0, s,
+                           a, (int)(g_small * gu_m), g_small);
+    launch_gemm<K_DWGU>(ab, g_all * gu_m, cdiv(a.d, QB), s, g_all);
+    if (a.sh_split > 0) {
+        const int64_t n = (int64_t)2 * a.Fs * a.d;
+        hipLaunchKernelGGL(sh_reduce_kernel, dim3(cdiv(n / 4, 256)), dim3(256), 0, s, a.part,
+                           a.sh_split, n, static_cast<uint16_t *>(a.dw_sgu));
+    }
     mark(5);
-    launch_gemm<K_DWDN>(a, dim3((unsigned)(a.E + 1) * cdiv(a.d, QB), cdiv(Fmax, QB)), s);
+    if (a.bf16)
+        hipLaunchKernelGGL(bwd_dw_small_kernel<K_DWDN>,
+                           dim3(bwd_blocks(K_DWDN, g_small * dn_m, 1, g_small)), dim3(256), 0, s,
+                           a, (int)(g_small * dn_m), g_small);
+    launch_gemm<K_DWDN>(ab, g_all * dn_m, cdiv(Fmax, QB), s, g_all);
+    if (a.sh_split > 0) {
+        const int64_t n = (int64_t)a.d * a.Fs;
+        hipLaunchKernelGGL(sh_reduce_kernel, dim3(cdiv(n / 4, 256)), dim3(256), 0, s, a.part,
+                           a.sh_split, n, static_cast<uint16_t *>(a.dw_sdn));
+    }
     mark(6);
-    launch_gemm<K_DWR>(a, dim3(cdiv(a.E + 1, QB), cdiv(a.d, QB)), s);
-    launch_gemm<K_DXR>(a, dim3(cdiv(a.T, QB), cdiv(a.d, QB)), s);
+    launch_gemm<K_DWR>(a, cdiv(a.E + 1, QB), cdiv(a.d, QB), s);
+    launch_gemm<K_DXR>(a, cdiv(a.T, QB), cdiv(a.d, QB), s);
     const dim3 cgrid((unsigned)a.T, cdiv(a.d, 256));
     if (a.bf16)
         hipLaunchKernelGGL(dx_combine_kernel<uint16_t>, cgrid, dim3(256), 0, s, a);

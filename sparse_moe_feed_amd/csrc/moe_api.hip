@@ -133,8 +133,8 @@ moe::Problem make_problem(const moe_desc &d, int64_t T, const Plan &pl, void *ws
 // Workspace of moe_backward (regions as in moe::BwdArgs).
 struct BwdPlan {
     size_t counts, offsets, tile_start, tile_group, blk, rank, perm, logits, au, au_sh, g, g_sh, dgu,
-        dgu_sh, hh, hh_sh, dwp, gate, ds, q, dl, dxp, dxs, dxr, total;
-    int nblk, max_tiles, ldl, ldd;
+        dgu_sh, hh, hh_sh, dwp, gate, ds, q, dl, dxp, dxs, dxr, part, total;
+    int nblk, max_tiles, ldl, ldd, sh_split, sh_chunk;
 };
 
 BwdPlan make_bwd_plan(const moe_desc &d, int64_t T) {
@@ -176,6 +176,9 @@ BwdPlan make_bwd_plan(const moe_desc &d, int64_t T) {
     p.dxp = take((size_t)pairs * dm * es);
     p.dxs = take((size_t)T * dm * es);
     p.dxr = take((size_t)T * dm * 4);
+    p.sh_split = moe::bwd_sh_split(T, d.dtype == MOE_BF16, d.d_shared);
+    p.sh_chunk = moe::bwd_sh_chunk(T, p.sh_split);
+    p.part = take((size_t)p.sh_split * 2 * Fs * dm * 4);
     p.total = off;
     return p;
 }
@@ -622,6 +625,10 @@ moe_status moe_backward(const moe_desc *desc, int64_t T, const void *x, const vo
     a.dxp = base + pl.dxp;
     a.dxs = base + pl.dxs;
     a.dxr = reinterpret_cast<float *>(base + pl.dxr);
+    a.dw_kmin = -1;
+    a.sh_split = pl.sh_split;
+    a.sh_chunk = pl.sh_chunk;
+    a.part = reinterpret_cast<float *>(base + pl.part);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     mark_stage(0, s);

@@ -145,7 +145,21 @@ struct BwdArgs {
     int ldd;
     void *dxp, *dxs;    // [T*k, d], [T, d]  dx of each routed row, of the shared expert
     float *dxr;         // [T, d]            dx of the router
+    int dw_kmin;        // weight-gradient launches skip groups with at most this many rows
+    int sh_split;       // > 0: the shared expert's weight gradients reduce over the tokens
+    int sh_chunk;       //   in sh_split chunks of sh_chunk rows, partials in part
+    float *part;        // [sh_split, max(2 Fs d, d Fs)] binary32
 };
+// Chunks of the shared expert's weight-gradient reduction over T tokens
+// (bfloat16 layers; 0: not split).
+inline int bwd_sh_split(int64_t T, bool bf16, int Fs) {
+    if (!bf16 || Fs == 0 || T <= 128) return 0;
+    const int64_t s = (T + 511) / 512;
+    return (int)(s < 16 ? s : 16);
+}
+inline int bwd_sh_chunk(int64_t T, int split) {
+    return split ? (int)(((T + split - 1) / split + 63) / 64 * 64) : 0;
+}
 // p carries the routing and permutation buffers (tile map for kGemmBM rows).
 // mark(i) after stage i: 1 logits, 2 gate/up and G, 3 SwiGLU and router
 // backward, 4 dX, 5 dW_gu, 6 dW_dn, 7 router GEMMs, combine and loss.

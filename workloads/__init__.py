@@ -60,6 +60,8 @@ class MoEConfig:
     seed_b: int = 1000
     note: str = field(default="", compare=False)
     prenorm: bool = False           # the layer takes un-normalised rows h (pre-FFN RMSNorm)
+    backward: bool = False          # the training backward pass (gradients), not the forward
+    aux_coef: float = 0.0           # load-balancing loss coefficient of the backward pass
 
 
 CONFIGS = {
@@ -80,6 +82,10 @@ CONFIGS = {
     7: MoEConfig("decode_T32_prenorm", 32, 2560, 512, 10, 640, 640, "bf16", None, 1, 102, 1002,
                  "decode_T32 on RMSNorm(h): h = the decode tokens, gamma = 1 + N(0, 0.1^2)",
                  prenorm=True),
+    9: MoEConfig("backward_T4096", 4096, 2560, 512, 10, 640, 640, "bf16", None, 1, 103, 1003,
+                 "backward pass of prefill_T4096 for its own routing: dx and every weight "
+                 "gradient, load-balancing loss coefficient 0.001, dout ~ N(0,1)",
+                 backward=True, aux_coef=0.001),
 }
 
 
@@ -258,6 +264,12 @@ def make_dout(T: int, d: int, seed: int) -> np.ndarray:
     """Gradient arriving at the layer's output for the backward pass:
     dout ~ N(0,1), binary32 [T, d] (the layer's out is binary32)."""
     return _rng(seed, _DOUT).standard_normal((T, d), dtype=np.float32)
+
+
+def dout_for(cfg: MoEConfig) -> np.ndarray:
+    """dout of a backward configuration (stream seed_b: such configs have no
+    router bias)."""
+    return make_dout(cfg.T, cfg.d, cfg.seed_b)
 
 
 def zipf_bias(E: int, s: float, seed: int) -> np.ndarray:
