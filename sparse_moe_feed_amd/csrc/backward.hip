@@ -380,97 +380,118 @@ struct StageKC {
     }
 };
 
-// MC: thread owns reduction pair kp = tid % 32 (elements 2 kp, 2 kp + 1 of
-// the step) and column groups i8 = tid / 32 + 8 q (q < 2), eight columns each.
-// Each pair of 16-byte row pieces becomes eight 32-bit LDS writes of
-// (k, k+1) for one column.  The source rows of the next step are looked up
-// one step ahead (rows[], scl[]), so the data loads never wait on the map.
+// MC: the tile goes to LDS as it lies in memory, reduction row k by output
+// column m ([k][m], PM elements per row); the MFMA fragments are read back
+// transposed with ds_read_b64_tr_b16 (mc_frag).  Thread piece c = tid + 256 q
+// (q < 4) is row k = c / 16 of the step, columns 8 (c % 16) .. +7: sixteen
+// lanes cover one 256-byte row piece, so each load instruction reads four
+// whole row pieces.  The source rows of a step are looked up one step ahead
+// (rows[], scl[]), so the data loads never wait on the permutation.
+constexpr int PM = QB + 32;  // LDS row of an MC tile: 320 bytes (4 rows = 4 bank quarters)
+
 template <bool F32>
 struct StageMC {
-    const char *rows[2];
-    float scl[2];   // scales of the looked-up step
-    float sld[2];   // scales of the step whose data is in r / r2
-    bool live[2];
-    bool okd[2][2]; // which of r / r2 hold data (else they are stored as zeros)
-    uint4 r[2][2], r2[2][2];
-    int kp, i0;
+    const char *rows[4];
+    float scl[4];   // scales of the looked-up step
+    float sld[4];   // scales of the step whose data is in r / r2
+    bool live[4];
+    bool okd[4];    // which of r / r2 hold data (else they are stored as zeros)
+    uint4 r[4], r2[4];
+    int k_in, m8;
     __device__ void init(int tid) {
-        kp = tid & 31;
-        i0 = 8 * (tid >> 5);
+        k_in = tid >> 4;
+        m8 = 8 * (tid & 15);
     }
     // Branch-free: every lane looks up and loads a valid address (a row past
     // the end reads the last valid row, a column piece past the end reads
-    // piece 0) and selects zero afterwards.  A branch around a load makes the compiler wait for
-    // every memory operation in flight (stores included) at the next use.
+    // piece 0) and selects zero afterwards.  A branch around a load makes the
+    // compiler wait for every memory operation in flight (stores included) at
+    // the next use.
     __device__ void lookup(const Opnd &o, int k0) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int s = o.base + k0 + 2 * kp + h;
-            live[h] = s < o.lim;
+        for (int q = 0; q < 4; ++q) {
+            const int s = o.base + k0 + k_in + 16 * q;
+            live[q] = s < o.lim;
             const int sc_idx = max(min(s, o.lim - 1), 0);
             float sc;
-            rows[h] = op_row(o, sc_idx, sc);
-            scl[h] = live[h] ? sc : 0.f;
+            rows[q] = op_row(o, sc_idx, sc);
+            scl[q] = live[q] ? sc : 0.f;
         }
     }
     __device__ void load(const Opnd &o) {
-        sld[0] = scl[0];
-        sld[1] = scl[1];
+        const bool mok = m8 < o.ilim;
+        const int mc = mok ? m8 : 0;  // piece 0 of a row is always readable
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int i = i0 + 64 * q;
-                okd[h][q] = live[h] && i < o.ilim;
-                const int ic = i < o.ilim ? i : 0;  // piece 0 of a row is always readable
-                const char *p = rows[h] + (int64_t)(o.cb + ic) * (F32 ? 4 : 2);
-                // the zero select waits until store(), so nothing waits for
-                // the data before the step that writes it to LDS
-                if (F32) {
-                    r[h][q] = __builtin_bit_cast(uint4, reinterpret_cast<const float4 *>(p)[0]);
-                    r2[h][q] = __builtin_bit_cast(uint4, reinterpret_cast<const float4 *>(p)[1]);
-                } else {
-                    r[h][q] = *reinterpret_cast<const uint4 *>(p);
-                }
+        for (int q = 0; q < 4; ++q) {
+            sld[q] = scl[q];
+            okd[q] = live[q] && mok;
+            const char *p = rows[q] + (int64_t)(o.cb + mc) * (F32 ? 4 : 2);
+            // the zero select waits until store(), so nothing waits for the
+            // data before the step that writes it to LDS
+            if (F32) {
+                r[q] = __builtin_bit_cast(uint4, reinterpret_cast<const float4 *>(p)[0]);
+                r2[q] = __builtin_bit_cast(uint4, reinterpret_cast<const float4 *>(p)[1]);
+            } else {
+                r[q] = *reinterpret_cast<const uint4 *>(p);
             }
+        }
     }
-    __device__ void store(uint16_t *lds, int pitch = QLD, int koff = 0) {
+    // rows k0 .. k0 + 63 of the LDS tile (k0 = 0 for a one-step tile)
+    __device__ void store(uint16_t *lds, int k0 = 0) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            uint32_t v[2][8];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const uint4 z = uint4{0, 0, 0, 0};
-                if (F32) {
-                    const float s = sld[h];
-                    const uint4 a = okd[h][q] ? r[h][q] : z, b = okd[h][q] ? r2[h][q] : z;
-                    v[h][0] = f32_to_bf16_rne(s * __uint_as_float(a.x));
-                    v[h][1] = f32_to_bf16_rne(s * __uint_as_float(a.y));
-                    v[h][2] = f32_to_bf16_rne(s * __uint_as_float(a.z));
-                    v[h][3] = f32_to_bf16_rne(s * __uint_as_float(a.w));
-                    v[h][4] = f32_to_bf16_rne(s * __uint_as_float(b.x));
-                    v[h][5] = f32_to_bf16_rne(s * __uint_as_float(b.y));
-                    v[h][6] = f32_to_bf16_rne(s * __uint_as_float(b.z));
-                    v[h][7] = f32_to_bf16_rne(s * __uint_as_float(b.w));
-                } else {
-                    const uint4 a = okd[h][q] ? r[h][q] : z;
-                    v[h][0] = a.x & 0xFFFFu; v[h][1] = a.x >> 16;
-                    v[h][2] = a.y & 0xFFFFu; v[h][3] = a.y >> 16;
-                    v[h][4] = a.z & 0xFFFFu; v[h][5] = a.z >> 16;
-                    v[h][6] = a.w & 0xFFFFu; v[h][7] = a.w >> 16;
-                }
+        for (int q = 0; q < 4; ++q) {
+            const uint4 z = uint4{0, 0, 0, 0};
+            uint4 v;
+            if (F32) {
+                const float sc = sld[q];
+                const uint4 a = okd[q] ? r[q] : z, b = okd[q] ? r2[q] : z;
+                v.x = pack_bf16x2(sc * __uint_as_float(a.x), sc * __uint_as_float(a.y));
+                v.y = pack_bf16x2(sc * __uint_as_float(a.z), sc * __uint_as_float(a.w));
+                v.z = pack_bf16x2(sc * __uint_as_float(b.x), sc * __uint_as_float(b.y));
+                v.w = pack_bf16x2(sc * __uint_as_float(b.z), sc * __uint_as_float(b.w));
+            } else {
+                v = okd[q] ? r[q] : z;
             }
-            const int i = i0 + 64 * q;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                *reinterpret_cast<uint32_t *>(lds + (i + e) * pitch + koff + 2 * kp) =
-                    v[0][e] | (v[1][e] << 16);
+            *reinterpret_cast<uint4 *>(lds + (k0 + k_in + 16 * q) * PM + m8) = v;
         }
     }
 };
 
-// Only binary32 sources carry a scale (dOut scaled by the routing weight or
-// the shared gate); bfloat16 operands are staged as they are.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// MFMA fragment of an MC tile: eight consecutive reduction rows k0 + 8 (lane
+// / 32) .. + 7 of output column mb + lane % 32, as v_mfma_f32_32x32x16_bf16
+// takes them.  ds_read_b64_tr_b16 works on groups of 16 lanes: lane 4 a + b
+// of a group receives 16-bit element b of the 64-bit pieces addressed by
+// lanes a, a + 4, a + 8, a + 12 of the group.  So lane s of the group points
+// at row k + s / 4, columns 4 (s % 4) .. +3 of its 16-column block, and lane
+// s receives rows k .. k + 3 of column 4 (s / 4) + ... = the block's column
+// s; two reads (k and k + 4) give the eight rows.
+__device__ __forceinline__ bf16x8 mc_frag(const uint16_t *lds, int k0, int mb, int lane) {
+    const int g = lane >> 4, s = lane & 15;
+    const int k = k0 + 8 * (g >> 1) + (s >> 2);
+    const int m = mb + 16 * (g & 1) + 4 * (s & 3);
+    const uint16_t *p = lds + k * PM + m;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p + 4 * PM));
+    const short __attribute__((ext_vector_type(8))) v =
+        __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// Fragment of a KC tile (row m of the tile holds its reduction elements).
+__device__ __forceinline__ bf16x8 kc_frag(const uint16_t *lds, int k0, int mb, int lane) {
+    return *reinterpret_cast<const bf16x8 *>(&lds[(mb + (lane & 31)) * QLD + k0 + 8 * (lane >> 5)]);
+}
+
+template <bool KC>
+__device__ __forceinline__ bf16x8 frag(const uint16_t *lds, int k0, int mb, int lane) {
+    return KC ? kc_frag(lds, k0, mb, lane) : mc_frag(lds, k0, mb, lane);
+}
+
+// LDS elements of one QB x QK tile of either kind
+constexpr int TILE_E = QB * QLD > QK * PM ? QB * QLD : QK * PM;
 
 template <bool KC, bool F32> struct Stager;
 template <bool F32> struct Stager<true, F32> {
@@ -516,20 +537,16 @@ __device__ __forceinline__ void store_tile(const Job &j, f32x16 (&acc)[2][2], in
 
 // One QK step of the 128 x 128 tile from LDS: 4 waves in 2 x 2, each 64 x 64
 // from v_mfma_f32_32x32x16_bf16.
+template <bool A_KC, bool B_KC>
 __device__ __forceinline__ void mfma_step(const uint16_t *As, const uint16_t *Bs,
                                           f32x16 (&acc)[2][2], int wm, int wn, int lane) {
-    const int fr = lane & 31, fk = 8 * (lane >> 5);
 #pragma unroll
     for (int ks = 0; ks < QK / 16; ++ks) {
         bf16x8 af[2], bfr[2];
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-            af[mi] = *reinterpret_cast<const bf16x8 *>(
-                &As[(64 * wm + 32 * mi + fr) * QLD + 16 * ks + fk]);
+        for (int mi = 0; mi < 2; ++mi) af[mi] = frag<A_KC>(As, 16 * ks, 64 * wm + 32 * mi, lane);
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-            bfr[ni] = *reinterpret_cast<const bf16x8 *>(
-                &Bs[(64 * wn + 32 * ni + fr) * QLD + 16 * ks + fk]);
+        for (int ni = 0; ni < 2; ++ni) bfr[ni] = frag<B_KC>(Bs, 16 * ks, 64 * wn + 32 * ni, lane);
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
@@ -545,8 +562,8 @@ __device__ __forceinline__ void mfma_step(const uint16_t *As, const uint16_t *Bs
 template <int KIND>
 __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(BwdArgs a, int nx, int ny, int groups) {
     using Tr = Traits<KIND>;
-    __shared__ __align__(16) uint16_t As[2][QB * QLD];
-    __shared__ __align__(16) uint16_t Bs[2][QB * QLD];
+    __shared__ __align__(16) uint16_t As[2][TILE_E];
+    __shared__ __align__(16) uint16_t Bs[2][TILE_E];
     Job j;
     int bx, by;
     if (!block_tile<KIND>(nx, ny, groups, bx, by) || !make_job<KIND>(a, bx, by, 2, j)) return;
@@ -589,7 +606,7 @@ __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(BwdArgs a, int nx, int
                 sb.lookup(j.b, (kt + 2) * QK);
             }
         }
-        mfma_step(As[cur], Bs[cur], acc, wm, wn, lane);
+        mfma_step<Tr::A_KC, Tr::B_KC>(As[cur], Bs[cur], acc, wm, wn, lane);
         if (kt + 1 < nk) {
             sa.store(As[cur ^ 1], tid);
             sb.store(Bs[cur ^ 1], tid);
@@ -608,13 +625,13 @@ __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(BwdArgs a, int nx, int
 // through LDS as 16-byte row pieces, so a tile costs 8 stores per thread and
 // the next tile's loads do not wait behind a long tail of small stores.
 constexpr int KS = 128;
-constexpr int SLD = KS + 8;  // LDS row: 272 bytes (16 consecutive rows hit distinct banks)
+constexpr int SLD = QB + 8;  // output staging row: 272 bytes
 
 template <int KIND>
 __global__ __launch_bounds__(256, 2) void bwd_dw_small_kernel(BwdArgs a, int nx, int groups) {
     using Tr = Traits<KIND>;
-    __shared__ __align__(16) uint16_t As[QB * SLD];
-    __shared__ __align__(16) uint16_t Bs[QB * SLD];  // also the output staging
+    __shared__ __align__(16) uint16_t As[KS * PM];  // [k][m], as MC tiles
+    __shared__ __align__(16) uint16_t Bs[KS * PM];  // [k][n]; also the output staging
     Job j;
     int bx, by;
     if (!block_tile<KIND>(nx, 1, groups, bx, by)) return;
@@ -623,7 +640,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dw_small_kernel(BwdArgs a, int nx,
     if (!make_job<KIND>(aa, bx, 0, 2, j) || j.K > KS) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int wm = wave >> 1, wn = wave & 1;
-    const int fr = lane & 31, fk = 8 * (lane >> 5);
+    const int fr = lane & 31;
     const int ntiles = (j.N + QB - 1) / QB;
 
     StageMC<Tr::A_F32> sa0, sa1;
@@ -640,10 +657,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dw_small_kernel(BwdArgs a, int nx,
     sa1.load(j.a);
     sb0.load(j.b);
     sb1.load(j.b);
-    sa0.store(As, SLD, 0);
-    sa1.store(As, SLD, QK);
-    sb0.store(Bs, SLD, 0);
-    sb1.store(Bs, SLD, QK);
+    sa0.store(As, 0);
+    sa1.store(As, QK);
+    sb0.store(Bs, 0);
+    sb1.store(Bs, QK);
     __syncthreads();
 
     for (int t = 0; t < ntiles; ++t) {
@@ -669,13 +686,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dw_small_kernel(BwdArgs a, int nx,
         for (int ks = 0; ks < KS / 16; ++ks) {
             bf16x8 af[2], bfr[2];
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-                af[mi] = *reinterpret_cast<const bf16x8 *>(
-                    &As[(64 * wm + 32 * mi + fr) * SLD + 16 * ks + fk]);
+            for (int mi = 0; mi < 2; ++mi) af[mi] = mc_frag(As, 16 * ks, 64 * wm + 32 * mi, lane);
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
-                bfr[ni] = *reinterpret_cast<const bf16x8 *>(
-                    &Bs[(64 * wn + 32 * ni + fr) * SLD + 16 * ks + fk]);
+            for (int ni = 0; ni < 2; ++ni) bfr[ni] = mc_frag(Bs, 16 * ks, 64 * wn + 32 * ni, lane);
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
@@ -708,8 +721,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dw_small_kernel(BwdArgs a, int nx,
                 *reinterpret_cast<const uint4 *>(&Bs[row * SLD + c8]);
         }
         __syncthreads();  // the staged tile is read out
-        sb0.store(Bs, SLD, 0);
-        sb1.store(Bs, SLD, QK);
+        sb0.store(Bs, 0);
+        sb1.store(Bs, QK);
         __syncthreads();
     }
 }

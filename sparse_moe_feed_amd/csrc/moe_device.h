@@ -22,17 +22,15 @@ __device__ __forceinline__ float bf16_lo(uint32_t two) { return __uint_as_float(
 __device__ __forceinline__ float bf16_hi(uint32_t two) { return __uint_as_float(two & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// binary32 -> bfloat16, round to nearest, ties to even (NaN -> quiet NaN).
-// A select, not a branch: the streaming loops call it and must stay branch-free.
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    const uint32_t u = __float_as_uint(f);
-    const uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-    const uint32_t quiet = (u >> 16) | 0x40u;
-    return (uint16_t)((u & 0x7FFFFFFFu) > 0x7F800000u ? quiet : rounded);
-}
-
+// binary32 -> bfloat16, round to nearest, ties to even: gfx950's
+// v_cvt_pk_bf16_f32 (one instruction for two values; a NaN stays a NaN).
+typedef float moe_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 moe_bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(moe_f32x2{lo, hi}, moe_bf16x2));
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // Eight consecutive elements widened to binary32 (exact).
