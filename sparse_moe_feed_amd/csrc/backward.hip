@@ -153,8 +153,8 @@ __device__ __forceinline__ bool map_tile(const BwdArgs &a, int tile, MapTile &t)
 //   the others: row tile m on XCD m % 8 with its column tiles consecutive
 //     (the tile's gathered rows are read once per XCD).
 template <int KIND>
-__device__ __forceinline__ bool block_tile(int nx, int ny, int groups, int &bx, int &by) {
-    const int b = blockIdx.x, x = b & 7, q = b >> 3;
+__device__ __forceinline__ bool block_tile(int b, int nx, int ny, int groups, int &bx, int &by) {
+    const int x = b & 7, q = b >> 3;
     if (KIND == K_DWGU || KIND == K_DWDN) {
         const int mtiles = nx / groups;          // row tiles per group
         const int per = mtiles * ny;             // tiles per group
@@ -560,60 +560,67 @@ __device__ __forceinline__ void mfma_step(const uint16_t *As, const uint16_t *Bs
 // buffer in LDS (the next step's loads fly while this one computes); two
 // blocks per CU.
 template <int KIND>
-__global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(BwdArgs a, int nx, int ny, int groups) {
+__global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(BwdArgs a, int nx, int ny, int groups,
+                                                          int nvirt) {
     using Tr = Traits<KIND>;
     __shared__ __align__(16) uint16_t As[2][TILE_E];
     __shared__ __align__(16) uint16_t Bs[2][TILE_E];
-    Job j;
-    int bx, by;
-    if (!block_tile<KIND>(nx, ny, groups, bx, by) || !make_job<KIND>(a, bx, by, 2, j)) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int wm = wave >> 1, wn = wave & 1;
-    Stager<Tr::A_KC, Tr::A_F32> sa;
-    Stager<Tr::B_KC, Tr::B_F32> sb;
-    sa.init(j.a, tid);
-    sb.init(j.b, tid);
+    // grid-stride over the virtual blocks (the grid is a multiple of 8, so a
+    // block keeps its XCD's share of the tile map); tiles with nothing to do
+    // cost one look at the tile map instead of a block launch each
+    for (int b = blockIdx.x; b < nvirt; b += gridDim.x) {
+        Job j;
+        int bx, by;
+        if (!block_tile<KIND>(b, nx, ny, groups, bx, by) || !make_job<KIND>(a, bx, by, 2, j))
+            continue;
+        Stager<Tr::A_KC, Tr::A_F32> sa;
+        Stager<Tr::B_KC, Tr::B_F32> sb;
+        sa.init(j.a, tid);
+        sb.init(j.b, tid);
 
-    f32x16 acc[2][2];
+        f32x16 acc[2][2];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+        for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
+            for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
+                for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
 
-    const int nk = (j.K + QK - 1) / QK;
-    if (nk > 0) {
-        sa.lookup(j.a, 0);
-        sb.lookup(j.b, 0);
-        sa.load(j.a, 0);
-        sb.load(j.b, 0);
-        if (nk > 1) {
-            sa.lookup(j.a, QK);
-            sb.lookup(j.b, QK);
-        }
-        sa.store(As[0], tid);
-        sb.store(Bs[0], tid);
-        __syncthreads();
-    }
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) {
-            sa.load(j.a, (kt + 1) * QK);
-            sb.load(j.b, (kt + 1) * QK);
-            if (kt + 2 < nk) {
-                sa.lookup(j.a, (kt + 2) * QK);
-                sb.lookup(j.b, (kt + 2) * QK);
+        const int nk = (j.K + QK - 1) / QK;
+        if (nk > 0) {
+            sa.lookup(j.a, 0);
+            sb.lookup(j.b, 0);
+            sa.load(j.a, 0);
+            sb.load(j.b, 0);
+            if (nk > 1) {
+                sa.lookup(j.a, QK);
+                sb.lookup(j.b, QK);
             }
+            sa.store(As[0], tid);
+            sb.store(Bs[0], tid);
+            __syncthreads();
         }
-        mfma_step<Tr::A_KC, Tr::B_KC>(As[cur], Bs[cur], acc, wm, wn, lane);
-        if (kt + 1 < nk) {
-            sa.store(As[cur ^ 1], tid);
-            sb.store(Bs[cur ^ 1], tid);
+        for (int kt = 0; kt < nk; ++kt) {
+            const int cur = kt & 1;
+            if (kt + 1 < nk) {
+                sa.load(j.a, (kt + 1) * QK);
+                sb.load(j.b, (kt + 1) * QK);
+                if (kt + 2 < nk) {
+                    sa.lookup(j.a, (kt + 2) * QK);
+                    sb.lookup(j.b, (kt + 2) * QK);
+                }
+            }
+            mfma_step<Tr::A_KC, Tr::B_KC>(As[cur], Bs[cur], acc, wm, wn, lane);
+            if (kt + 1 < nk) {
+                sa.store(As[cur ^ 1], tid);
+                sb.store(Bs[cur ^ 1], tid);
+            }
+            __syncthreads();  // also: LDS free for the next tile of this block
         }
-        __syncthreads();
+        store_tile<Tr::C_F32>(j, acc, wm, wn, lane);
     }
-    store_tile<Tr::C_F32>(j, acc, wm, wn, lane);
 }
 
 // Weight gradients of experts with at most KS rows (the usual case: T k / E
@@ -634,7 +641,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dw_small_kernel(BwdArgs a, int nx,
     __shared__ __align__(16) uint16_t Bs[KS * PM];  // [k][n]; also the output staging
     Job j;
     int bx, by;
-    if (!block_tile<KIND>(nx, 1, groups, bx, by)) return;
+    if (!block_tile<KIND>(blockIdx.x, nx, 1, groups, bx, by)) return;
     BwdArgs aa = a;
     aa.dw_kmin = -1;  // every group with at most KS rows
     if (!make_job<KIND>(aa, bx, 0, 2, j) || j.K > KS) return;
@@ -909,6 +916,34 @@ __global__ __launch_bounds__(256) void dx_combine_kernel(BwdArgs a) {
     a.dx[t * a.d + c] = acc;
 }
 
+// The same for bfloat16 layers (d % 8 == 0), eight columns per thread: block
+// (t, c) handles token t and columns 512 c .. 512 c + 511.
+__global__ __launch_bounds__(64) void dx_combine_bf16_kernel(BwdArgs a) {
+    const int64_t t = blockIdx.x;
+    const int c = (blockIdx.y * 64 + threadIdx.x) * 8;
+    if (c >= a.d) return;
+    float acc[8], v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    const uint16_t *dxp = static_cast<const uint16_t *>(a.dxp);
+    for (int jj = 0; jj < a.k; ++jj) {
+        load8(dxp + (int64_t)a.rank[t * a.k + jj] * a.d + c, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    if (a.Fs > 0) {
+        load8(static_cast<const uint16_t *>(a.dxs) + t * a.d + c, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    load8(a.dxr + t * a.d + c, v);
+    float *o = a.dx + t * a.d + c;
+    reinterpret_cast<float4 *>(o)[0] = make_float4(acc[0] + v[0], acc[1] + v[1], acc[2] + v[2],
+                                                   acc[3] + v[3]);
+    reinterpret_cast<float4 *>(o)[1] = make_float4(acc[4] + v[4], acc[5] + v[5], acc[6] + v[6],
+                                                   acc[7] + v[7]);
+}
+
 // L_aux = coef (E / T) sum_t q_t (q_t = f . p_t), one block, fixed order.
 __global__ __launch_bounds__(256) void aux_loss_kernel(BwdArgs a) {
     __shared__ float red[4];
@@ -922,16 +957,18 @@ __global__ __launch_bounds__(256) void aux_loss_kernel(BwdArgs a) {
 
 // nx row tiles (weight gradients: groups x row tiles per group) by ny column
 // tiles.
+// max_blocks > 0 caps the grid (the blocks then stride over the tiles).
 template <int KIND>
 static void launch_gemm(const BwdArgs &a, unsigned nx, unsigned ny, hipStream_t s,
-                        int groups = 1) {
+                        int groups = 1, unsigned max_blocks = 0) {
     if (nx == 0 || ny == 0) return;
-    const dim3 grid(bwd_blocks(KIND, (int)nx, (int)ny, groups));
+    const unsigned nvirt = bwd_blocks(KIND, (int)nx, (int)ny, groups);
+    const unsigned grid = max_blocks && max_blocks < nvirt ? max_blocks : nvirt;
     if (!a.bf16)
         hipLaunchKernelGGL(bwd_gemm_f32_kernel<KIND>, dim3(nx, ny), dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL(bwd_gemm_kernel<KIND>, grid, dim3(256), 0, s, a, (int)nx, (int)ny,
-                           groups);
+        hipLaunchKernelGGL(bwd_gemm_kernel<KIND>, dim3(grid), dim3(256), 0, s, a, (int)nx,
+                           (int)ny, groups, (int)nvirt);
 }
 
 // Shared expert's weight gradient from its split reduction: out = the sum of
@@ -992,7 +1029,9 @@ hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
         hipLaunchKernelGGL(bwd_dw_small_kernel<K_DWGU>,
                            dim3(bwd_blocks(K_DWGU, g_small * gu_m, 1, g_small)), dim3(256), 0, s,
                            a, (int)(g_small * gu_m), g_small);
-    launch_gemm<K_DWGU>(ab, g_all * gu_m, cdiv(a.d, QB), s, g_all);
+    // most groups were done above: a capped grid strides over the tile map
+    const unsigned cap = 8 * 256 * 2;
+    launch_gemm<K_DWGU>(ab, g_all * gu_m, cdiv(a.d, QB), s, g_all, cap);
     if (a.sh_split > 0) {
         const int64_t n = (int64_t)2 * a.Fs * a.d;
         hipLaunchKernelGGL(sh_reduce_kernel, dim3(cdiv(n / 4, 256)), dim3(256), 0, s, a.part,
@@ -1003,7 +1042,7 @@ hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
         hipLaunchKernelGGL(bwd_dw_small_kernel<K_DWDN>,
                            dim3(bwd_blocks(K_DWDN, g_small * dn_m, 1, g_small)), dim3(256), 0, s,
                            a, (int)(g_small * dn_m), g_small);
-    launch_gemm<K_DWDN>(ab, g_all * dn_m, cdiv(Fmax, QB), s, g_all);
+    launch_gemm<K_DWDN>(ab, g_all * dn_m, cdiv(Fmax, QB), s, g_all, cap);
     if (a.sh_split > 0) {
         const int64_t n = (int64_t)a.d * a.Fs;
         hipLaunchKernelGGL(sh_reduce_kernel, dim3(cdiv(n / 4, 256)), dim3(256), 0, s, a.part,
@@ -1012,11 +1051,12 @@ hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
     mark(6);
     launch_gemm<K_DWR>(a, cdiv(a.E + 1, QB), cdiv(a.d, QB), s);
     launch_gemm<K_DXR>(a, cdiv(a.T, QB), cdiv(a.d, QB), s);
-    const dim3 cgrid((unsigned)a.T, cdiv(a.d, 256));
     if (a.bf16)
-        hipLaunchKernelGGL(dx_combine_kernel<uint16_t>, cgrid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(dx_combine_bf16_kernel, dim3((unsigned)a.T, cdiv(a.d / 8, 64)), dim3(64),
+                           0, s, a);
     else
-        hipLaunchKernelGGL(dx_combine_kernel<float>, cgrid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(dx_combine_kernel<float>, dim3((unsigned)a.T, cdiv(a.d, 256)),
+                           dim3(256), 0, s, a);
     if (a.aux_loss) hipLaunchKernelGGL(aux_loss_kernel, dim3(1), dim3(256), 0, s, a);
     mark(7);
     return hipGetLastError();
