@@ -14,7 +14,8 @@ loop.  `cpu_baseline` times the CPU oracle on the host cores.
 
 `--config 9` (reported by default under "also") times the training backward
 pass of the prefill-shaped layer: one moe_backward call (dx and every weight
-gradient, plus the load-balancing loss) for the routing of its batch.
+gradient, plus the load-balancing loss) for the routing of its batch, with the
+gate/up pre-activations its moe_forward_train saved.
 
 `--config 7` measures the decode layer with its pre-FFN RMSNorm (one call:
 moe_forward_prenorm); `--config 6` measures the same decode layer with MXFP4 expert weights
@@ -119,20 +120,21 @@ def measure_backward(cfg, dev_layer, steps, warmup):
     x = to(W.make_x(cfg.T, cfg.d, cfg.dtype, cfg.seed_x))
     dout = torch.from_numpy(W.dout_for(cfg)).cuda()
     L = dev_layer
-    # the routing of this batch (an input of the backward pass)
-    _, idx, w = moe.forward(x, L["w_router"], L["w_gate_up"], L["w_down"], cfg.k,
-                            L["w_sh_gate_up"], L["w_sh_down"], L["sh_gate"])
+    # the training forward of this batch: its routing and its saved gate/up
+    # pre-activations are the backward pass's inputs
+    _, idx, w, saved = moe.forward_train(x, L["w_router"], L["w_gate_up"], L["w_down"], cfg.k,
+                                         L["w_sh_gate_up"], L["w_sh_down"], L["sh_gate"])
     shape = moe.shape_of(x, L["w_gate_up"], cfg.k, L["w_sh_gate_up"])
     ws = torch.empty(moe.backward_workspace_size(shape, cfg.T), dtype=torch.uint8, device="cuda")
     grads = moe.backward(x, L["w_router"], L["w_gate_up"], L["w_down"], idx, w, dout,
                          L["w_sh_gate_up"], L["w_sh_down"], L["sh_gate"], aux_coef=cfg.aux_coef,
-                         ws=ws)
+                         ws=ws, saved=saved)
     aux = grads.pop("aux_loss")
 
     def step():
         moe.backward(x, L["w_router"], L["w_gate_up"], L["w_down"], idx, w, dout,
                      L["w_sh_gate_up"], L["w_sh_down"], L["sh_gate"], aux_coef=cfg.aux_coef,
-                     ws=ws, grads=grads, aux_loss=aux)
+                     ws=ws, grads=grads, aux_loss=aux, saved=saved)
     for _ in range(warmup):
         step()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -265,6 +265,26 @@ moe_status moe_forward_prenorm(const moe_desc *desc, int64_t T, const void *h,
                                float *topk_w, void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * Training forward: moe_forward plus the gate/up pre-activations that
+ * moe_backward would otherwise recompute (reading every touched expert's
+ * gate/up weights again).  `saved` (moe_saved_bytes bytes, desc->dtype,
+ * 16-byte aligned) receives [a | u] = [W_g x | W_u x] of every routed row in
+ * the permuted order the routing implies (the rows of expert e, ascending
+ * pair id t*k+j, after those of experts < e), each row 2F wide, then the
+ * shared expert's [a | u] per token (2Fs wide).  It stays valid while the
+ * routing and x are unchanged.  Everything else as moe_forward.
+ * --------------------------------------------------------------------------- */
+size_t moe_saved_bytes(const moe_desc *desc, int64_t T);
+
+moe_status moe_forward_train(const moe_desc *desc, int64_t T, const void *x,
+                             const void *w_router, const float *router_bias,
+                             const void *w_gate_up, const void *w_down,
+                             const void *w_sh_gate_up, const void *w_sh_down,
+                             const void *sh_gate, float *out, int32_t *topk_idx,
+                             float *topk_w, void *saved, size_t saved_bytes, void *ws,
+                             size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Backward pass (training).
  *
  * Gradients of  Lambda = sum_t dout[t] . out[t] + L_aux  for the layer of
@@ -281,7 +301,9 @@ moe_status moe_forward_prenorm(const moe_desc *desc, int64_t T, const void *h,
  * aux_coef = 0 gives the plain layer gradient.
  *
  * Inputs: the moe_forward operands, topk_idx / topk_w [T,k], dout [T,d]
- * (binary32, the gradient arriving at out).  The entries of one topk_idx row
+ * (binary32, the gradient arriving at out), and `saved`: NULL (the gate/up
+ * pre-activations are recomputed) or the buffer moe_forward_train filled for
+ * this x and routing.  The entries of one topk_idx row
  * must be distinct experts in [0,E) (else the result is undefined; every
  * access stays in bounds).
  * Outputs (all overwritten, none may alias an input):
@@ -304,9 +326,9 @@ moe_status moe_backward(const moe_desc *desc, int64_t T, const void *x,
                         const void *w_gate_up, const void *w_down,
                         const void *w_sh_gate_up, const void *w_sh_down,
                         const void *sh_gate, const int32_t *topk_idx,
-                        const float *topk_w, const float *dout, float aux_coef,
-                        float *dx, void *dw_router, void *dw_gate_up, void *dw_down,
-                        void *dw_sh_gate_up, void *dw_sh_down, void *dsh_gate,
+                        const float *topk_w, const float *dout, const void *saved,
+                        float aux_coef, float *dx, void *dw_router, void *dw_gate_up,
+                        void *dw_down, void *dw_sh_gate_up, void *dw_sh_down, void *dsh_gate,
                         float *aux_loss, void *ws, size_t ws_bytes, void *stream);
 
 /* Static, human-readable name of a status code. */

@@ -33,7 +33,8 @@ ROUTERS = {None: 0, "auto": 0, "exact": MOE_FLAG_ROUTER_EXACT,
 EXPORTED = ("moe_workspace_size", "moe_workspace_query", "moe_route", "moe_forward",
             "moe_experts", "moe_mx4_packed_bytes", "moe_mx4_pack", "moe_forward_mx4",
             "moe_experts_mx4", "moe_rmsnorm", "moe_forward_prenorm",
-            "moe_backward_workspace_size", "moe_backward", "moe_status_string",
+            "moe_saved_bytes", "moe_forward_train", "moe_backward_workspace_size",
+            "moe_backward", "moe_status_string",
             "moe_last_error", "moe_stage_events")
 MOE_WEIGHTS_DTYPE, MOE_WEIGHTS_MX4 = 0, 1
 
@@ -87,10 +88,13 @@ def lib():
         L.moe_forward.argtypes[3:]
     L.moe_backward_workspace_size.argtypes = [dp, i64]
     L.moe_backward_workspace_size.restype = sz
-    L.moe_backward.argtypes = [dp, i64] + [vp] * 11 + [ctypes.c_float] + [vp] * 8 + [vp, sz, vp]
+    L.moe_backward.argtypes = [dp, i64] + [vp] * 12 + [ctypes.c_float] + [vp] * 8 + [vp, sz, vp]
+    L.moe_saved_bytes.argtypes = [dp, i64]
+    L.moe_saved_bytes.restype = sz
+    L.moe_forward_train.argtypes = [dp, i64] + [vp] * 12 + [sz, vp, sz, vp]
     for f in (L.moe_workspace_query, L.moe_route, L.moe_forward, L.moe_experts,
               L.moe_forward_mx4, L.moe_experts_mx4, L.moe_mx4_pack, L.moe_rmsnorm,
-              L.moe_forward_prenorm, L.moe_backward):
+              L.moe_forward_prenorm, L.moe_backward, L.moe_forward_train):
         f.restype = ctypes.c_int
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
@@ -297,14 +301,51 @@ def backward_workspace_size(shape: Shape, T: int) -> int:
     return int(lib().moe_backward_workspace_size(ctypes.byref(shape.desc()), T))
 
 
+def saved_bytes(shape: Shape, T: int) -> int:
+    return int(lib().moe_saved_bytes(ctypes.byref(shape.desc()), T))
+
+
+def forward_train(x, w_router, w_gate_up, w_down, k, w_sh_gate_up=None, w_sh_down=None,
+                  sh_gate=None, bias=None, out=None, topk_idx=None, topk_w=None, saved=None,
+                  ws=None, router=None):
+    """The training forward: (out, topk_idx, topk_w, saved), saved being the
+    gate/up pre-activations moe_backward can take instead of recomputing them."""
+    T, d = x.shape
+    shape = shape_of(x, w_gate_up, k, w_sh_gate_up, router)
+    E, F, Fs = shape.n_experts, shape.d_expert, shape.d_shared
+    _dev(x, "x"), _dev(w_router, "w_router", x.dtype, (E, d))
+    _dev(w_gate_up, "w_gate_up", x.dtype), _dev(w_down, "w_down", x.dtype, (E, d, F))
+    if Fs:
+        _dev(w_sh_gate_up, "w_sh_gate_up", x.dtype, (2 * Fs, d))
+        _dev(w_sh_down, "w_sh_down", x.dtype, (d, Fs)), _dev(sh_gate, "sh_gate", x.dtype, (d,))
+    _dev(bias, "router_bias", torch.float32, (E,))
+    out = torch.empty((T, d), dtype=torch.float32, device=x.device) if out is None else out
+    topk_idx = torch.empty((T, k), dtype=torch.int32, device=x.device) if topk_idx is None else topk_idx
+    topk_w = torch.empty((T, k), dtype=torch.float32, device=x.device) if topk_w is None else topk_w
+    nbytes = saved_bytes(shape, T)
+    saved = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device) if saved is None else saved
+    _dev(out, "out", torch.float32, (T, d)), _dev(topk_idx, "topk_idx", torch.int32, (T, k))
+    _dev(topk_w, "topk_w", torch.float32, (T, k)), _dev(saved, "saved")
+    ws = alloc_workspace(shape, T, x.device) if ws is None else ws
+    st = lib().moe_forward_train(ctypes.byref(shape.desc()), T, _ptr(x), _ptr(w_router),
+                                 _ptr(bias), _ptr(w_gate_up), _ptr(w_down), _ptr(w_sh_gate_up),
+                                 _ptr(w_sh_down), _ptr(sh_gate), _ptr(out), _ptr(topk_idx),
+                                 _ptr(topk_w), _ptr(saved), saved.numel() * saved.element_size(),
+                                 _ptr(ws), ws.numel(), _stream())
+    _check(st, "moe_forward_train")
+    return out, topk_idx, topk_w, saved
+
+
 def backward(x, w_router, w_gate_up, w_down, topk_idx, topk_w, dout, w_sh_gate_up=None,
              w_sh_down=None, sh_gate=None, bias=None, aux_coef=0.0, ws=None, grads=None,
-             aux_loss=None):
+             aux_loss=None, saved=None):
     """Gradients of sum(dout * out) + aux_coef * E * sum_e f_e P_e with the
     routing given.  Returns a dict: dx (float32 [T,d]), dw_router,
     dw_gate_up, dw_down, dw_sh_gate_up, dw_sh_down, dsh_gate (x.dtype; the
     shared ones None without a shared expert) and aux_loss (float32 [1]).
-    grads may pass preallocated outputs under the same names."""
+    grads may pass preallocated outputs under the same names; saved is the
+    buffer forward_train returned for this x and routing (else the gate/up
+    pre-activations are recomputed)."""
     T, d = x.shape
     k = topk_idx.shape[1]
     shape = shape_of(x, w_gate_up, k, w_sh_gate_up)
@@ -336,7 +377,8 @@ def backward(x, w_router, w_gate_up, w_down, topk_idx, topk_w, dout, w_sh_gate_u
     st = lib().moe_backward(
         ctypes.byref(shape.desc()), T, _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w_gate_up),
         _ptr(w_down), _ptr(w_sh_gate_up), _ptr(w_sh_down), _ptr(sh_gate), _ptr(topk_idx),
-        _ptr(topk_w), _ptr(dout), ctypes.c_float(aux_coef), _ptr(g["dx"]), _ptr(g["dw_router"]),
+        _ptr(topk_w), _ptr(dout), _ptr(saved), ctypes.c_float(aux_coef), _ptr(g["dx"]),
+        _ptr(g["dw_router"]),
         _ptr(g["dw_gate_up"]), _ptr(g["dw_down"]), _ptr(g["dw_sh_gate_up"]),
         _ptr(g["dw_sh_down"]), _ptr(g["dsh_gate"]), _ptr(aux), _ptr(ws), ws.numel(), _stream())
     _check(st, "moe_backward")

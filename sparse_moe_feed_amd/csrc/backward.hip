@@ -1001,7 +1001,7 @@ hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
     const unsigned tiles = (unsigned)pp.max_tiles;
     launch_gemm<K_LOGITS>(a, cdiv(a.T, QB), cdiv(a.E + 1, QB), s);
     mark(1);
-    launch_gemm<K_AU>(a, tiles, cdiv(2 * Fmax, QB), s);
+    if (!a.au_given) launch_gemm<K_AU>(a, tiles, cdiv(2 * Fmax, QB), s);
     launch_gemm<K_G>(a, tiles, cdiv(Fmax, QB), s);
     mark(2);
     const int64_t rows = (int64_t)a.T * a.k + (a.Fs > 0 ? a.T : 0);

@@ -202,6 +202,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
                     const int col = n0 + 32 * wn + fr;
                     H[(int64_t)(row0 + row) * Fg + col] =
                         f32_to_bf16_rne(silu_mul(acc[mi][0][v], acc[mi][1][v]));
+                    if (a.au) {  // training forward: the pre-activations too
+                        uint16_t *arow = (shared ? a.au_sh : a.au) + (int64_t)(row0 + row) * 2 * Fg;
+                        arow[col] = f32_to_bf16_rne(acc[mi][0][v]);
+                        arow[Fg + col] = f32_to_bf16_rne(acc[mi][1][v]);
+                    }
                 }
             }
     } else if (MODE == 2) {
@@ -240,6 +245,8 @@ hipError_t launch_experts_bf16(const Problem &p, hipStream_t s,
     a.x = static_cast<const uint16_t *>(p.x);
     a.h = static_cast<uint16_t *>(p.h);
     a.h_sh = static_cast<uint16_t *>(p.h_shared);
+    a.au = static_cast<uint16_t *>(p.au);
+    a.au_sh = static_cast<uint16_t *>(p.au_sh);
     a.out = p.out;
     a.y = static_cast<uint16_t *>(p.y);
     a.perm = p.perm;

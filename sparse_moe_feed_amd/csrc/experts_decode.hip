@@ -29,6 +29,7 @@ struct DecodeArgs {
     const uint16_t *w_sh;  // gate/up: [2Fs, d]     down: [d, Fs]
     uint16_t *h;           // [T*k, F]
     uint16_t *h_sh;        // [T, Fs]
+    uint16_t *au, *au_sh;  // pre-activations [a | u] (training forward), or null
     float *out;
     uint16_t *y;           // [T*k, d] weighted routed rows (bf16)
     const int32_t *perm, *counts, *offsets, *tile_start, *tile_group;
@@ -200,9 +201,15 @@ __device__ void decode_gateup_body(const DecodeArgs &a, const TileInfo &ti) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * h + 4 * (lane >> 4) + i;
-            if (row < ti.nrows)
+            if (row < ti.nrows) {
                 H[(int64_t)(ti.row0 + row) * Fg + ncol + rl] =
                     f32_to_bf16_rne(silu_mul(acc[h][0][i], acc[h][1][i]));
+                if (a.au) {  // training forward: the pre-activations too
+                    uint16_t *arow = (ti.shared ? a.au_sh : a.au) + (int64_t)(ti.row0 + row) * 2 * Fg;
+                    arow[ncol + rl] = f32_to_bf16_rne(acc[h][0][i]);
+                    arow[Fg + ncol + rl] = f32_to_bf16_rne(acc[h][1][i]);
+                }
+            }
         }
 }
 
@@ -604,6 +611,8 @@ hipError_t launch_experts_decode(const Problem &p, hipStream_t s,
     a.x = static_cast<const uint16_t *>(p.x);
     a.h = static_cast<uint16_t *>(p.h);
     a.h_sh = static_cast<uint16_t *>(p.h_shared);
+    a.au = static_cast<uint16_t *>(p.au);
+    a.au_sh = static_cast<uint16_t *>(p.au_sh);
     a.out = p.out;
     a.y = static_cast<uint16_t *>(p.y);
     a.perm = p.perm;

@@ -404,6 +404,23 @@ __global__ __launch_bounds__(256, (NS * Geo<BM, BK>::STB <= 80 * 1024 ? 2 : 1)) 
                                       silu_mul(gt[4 * g + 3], up[4 * g + 3]));
                     *reinterpret_cast<uint2 *>(hrow + 32 * pr + 8 * g) = q;
                 }
+            if (a.au) {
+                // training forward: the pre-activations too, gate half then up half
+                uint16_t *arow = (shared ? a.au_sh : a.au) + (int64_t)(row0 + row) * 2 * Fg + n0 +
+                                 64 * wn + cq;
+#pragma unroll
+                for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+#pragma unroll
+                        for (int half = 0; half < 2; ++half) {
+                            const f32x16 &v = acc[mi][pr + 2 * half];
+                            uint2 q;
+                            q.x = pack_bf16x2(v[4 * g], v[4 * g + 1]);
+                            q.y = pack_bf16x2(v[4 * g + 2], v[4 * g + 3]);
+                            *reinterpret_cast<uint2 *>(arow + half * Fg + 32 * pr + 8 * g) = q;
+                        }
+            }
         }
     } else {
 #pragma unroll
@@ -452,6 +469,8 @@ hipError_t launch_experts_dma(const Problem &p, int bm, hipStream_t s,
     a.x = static_cast<const uint16_t *>(p.x);
     a.h = static_cast<uint16_t *>(p.h);
     a.h_sh = static_cast<uint16_t *>(p.h_shared);
+    a.au = static_cast<uint16_t *>(p.au);
+    a.au_sh = static_cast<uint16_t *>(p.au_sh);
     a.out = p.out;
     a.y = static_cast<uint16_t *>(p.y);
     a.perm = p.perm;

@@ -14,6 +14,7 @@ namespace moe {
 struct F32Args {
     const float *x, *w_gu, *w_dn, *w_sgu, *w_sdn;
     float *h, *h_sh, *out, *y;
+    float *au, *au_sh;  // pre-activations [a | u] (training forward), or null
     const int32_t *perm, *offsets;
     const float *topk_w, *gate;
     int64_t T;
@@ -74,6 +75,11 @@ __global__ __launch_bounds__(256) void f32_gateup_kernel(F32Args a) {
             u = fmaf(wu[kk], xr[kk], u);
         }
         hrow[n] = silu_mul(g, u);
+        if (a.au) {  // training forward: the pre-activations too
+            float *arow = grp < a.E ? a.au + (int64_t)blockIdx.x * 2 * a.F : a.au_sh + tok * 2 * a.Fs;
+            arow[n] = g;
+            arow[width + n] = u;
+        }
     }
 }
 
@@ -102,6 +108,8 @@ hipError_t launch_experts_f32(const Problem &p, hipStream_t s,
     a.w_sdn = static_cast<const float *>(p.w_sh_down);
     a.h = static_cast<float *>(p.h);
     a.h_sh = static_cast<float *>(p.h_shared);
+    a.au = static_cast<float *>(p.au);
+    a.au_sh = static_cast<float *>(p.au_sh);
     a.out = p.out;
     a.y = static_cast<float *>(p.y);
     a.perm = p.perm;

@@ -267,12 +267,17 @@ bool eps_ok(float eps) { return eps >= 0.0f && eps <= 3.4e38f; }
 // moe_forward / moe_forward_mx4 / moe_forward_prenorm: checks, then
 // [RMSNorm into the workspace,] router, permutation, experts, combine.
 // norm_weight != nullptr selects the pre-norm (x is then h).
+size_t saved_bytes_of(const moe_desc &d, int64_t T) {
+    const size_t es = d.dtype == MOE_BF16 ? 2 : 4;
+    return ((size_t)T * d.top_k * 2 * d.d_expert + (size_t)T * 2 * d.d_shared) * es;
+}
+
 moe_status forward_impl(const moe_desc *desc, int64_t T, const void *x, const void *norm_weight,
                         float eps, bool mx4, const void *w_router, const float *router_bias,
                         const void *w_gate_up, const void *w_down, const void *w_sh_gate_up,
                         const void *w_sh_down, const void *sh_gate, float *out,
                         int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
-                        void *stream) {
+                        void *stream, void *saved = nullptr, size_t saved_bytes = 0) {
     moe_status st = check_common(desc, T, {x, w_router, w_gate_up, w_down, out, topk_idx, topk_w},
                                  {router_bias, w_sh_gate_up, w_sh_down, sh_gate}, ws, ws_bytes);
     if (st != MOE_OK) return st;
@@ -284,6 +289,11 @@ moe_status forward_impl(const moe_desc *desc, int64_t T, const void *x, const vo
     if (desc->d_shared > 0 && (!w_sh_gate_up || !w_sh_down || !sh_gate)) return MOE_ERR_INVALID_ARG;
     const Plan pl = make_plan(*desc, T);
     moe::Problem p = make_problem(*desc, T, pl, ws);
+    if (saved) {
+        p.au = saved;
+        p.au_sh = static_cast<char *>(saved) + (size_t)T * desc->top_k * 2 * desc->d_expert *
+                                                   (desc->dtype == MOE_BF16 ? 2 : 4);
+    }
     p.x = norm_weight ? static_cast<const void *>(static_cast<char *>(ws) + pl.xnorm) : x;
     p.w_router = w_router;
     p.router_bias = router_bias;
@@ -367,6 +377,27 @@ moe_status moe_forward(const moe_desc *desc, int64_t T, const void *x, const voi
     return forward_impl(desc, T, x, nullptr, 0.0f, false, w_router, router_bias, w_gate_up, w_down,
                         w_sh_gate_up, w_sh_down, sh_gate, out, topk_idx, topk_w, ws, ws_bytes,
                         stream);
+}
+
+size_t moe_saved_bytes(const moe_desc *desc, int64_t T) {
+    if (check_desc(desc) != MOE_OK || check_T(desc, T) != MOE_OK) return 0;
+    return saved_bytes_of(*desc, T);
+}
+
+moe_status moe_forward_train(const moe_desc *desc, int64_t T, const void *x, const void *w_router,
+                             const float *router_bias, const void *w_gate_up, const void *w_down,
+                             const void *w_sh_gate_up, const void *w_sh_down, const void *sh_gate,
+                             float *out, int32_t *topk_idx, float *topk_w, void *saved,
+                             size_t saved_bytes, void *ws, size_t ws_bytes, void *stream) {
+    moe_status st = check_desc(desc);
+    if (st != MOE_OK) return st;
+    st = check_T(desc, T);
+    if (st != MOE_OK || T == 0) return st;
+    if (!saved || !aligned16(saved) || saved_bytes < saved_bytes_of(*desc, T))
+        return MOE_ERR_INVALID_ARG;
+    return forward_impl(desc, T, x, nullptr, 0.0f, false, w_router, router_bias, w_gate_up, w_down,
+                        w_sh_gate_up, w_sh_down, sh_gate, out, topk_idx, topk_w, ws, ws_bytes,
+                        stream, saved, saved_bytes);
 }
 
 moe_status moe_experts(const moe_desc *desc, int64_t T, const void *x, const void *w_gate_up,
@@ -525,7 +556,8 @@ moe_status moe_backward(const moe_desc *desc, int64_t T, const void *x, const vo
                         const float *router_bias, const void *w_gate_up, const void *w_down,
                         const void *w_sh_gate_up, const void *w_sh_down, const void *sh_gate,
                         const int32_t *topk_idx, const float *topk_w, const float *dout,
-                        float aux_coef, float *dx, void *dw_router, void *dw_gate_up,
+                        const void *saved, float aux_coef, float *dx, void *dw_router,
+                        void *dw_gate_up,
                         void *dw_down, void *dw_sh_gate_up, void *dw_sh_down, void *dsh_gate,
                         float *aux_loss, void *ws, size_t ws_bytes, void *stream) {
     moe_status st = check_desc(desc);
@@ -541,7 +573,7 @@ moe_status moe_backward(const moe_desc *desc, int64_t T, const void *x, const vo
                !dsh_gate))
         return MOE_ERR_INVALID_ARG;
     if (!all_aligned({x, w_router, router_bias, w_gate_up, w_down, w_sh_gate_up, w_sh_down,
-                      sh_gate, topk_idx, topk_w, dout, dx, dw_router, dw_gate_up, dw_down,
+                      sh_gate, topk_idx, topk_w, dout, saved, dx, dw_router, dw_gate_up, dw_down,
                       dw_sh_gate_up, dw_sh_down, dsh_gate}))
         return MOE_ERR_INVALID_ARG;
     if (aux_loss && (reinterpret_cast<uintptr_t>(aux_loss) & 3u)) return MOE_ERR_INVALID_ARG;
@@ -608,8 +640,16 @@ moe_status moe_backward(const moe_desc *desc, int64_t T, const void *x, const vo
     a.tile_group = p.tile_group;
     a.perm = p.perm;
     a.rank = p.rank;
-    a.au = base + pl.au;
-    a.au_sh = base + pl.au_sh;
+    if (saved) {  // the training forward's pre-activations: no recompute
+        a.au = const_cast<void *>(saved);
+        a.au_sh = static_cast<char *>(const_cast<void *>(saved)) +
+                  (size_t)T * p.k * 2 * p.F * (p.bf16 ? 2 : 4);
+        a.au_given = true;
+    } else {
+        a.au = base + pl.au;
+        a.au_sh = base + pl.au_sh;
+        a.au_given = false;
+    }
     a.g = reinterpret_cast<float *>(base + pl.g);
     a.g_sh = reinterpret_cast<float *>(base + pl.g_sh);
     a.dgu = base + pl.dgu;

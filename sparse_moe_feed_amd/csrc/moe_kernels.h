@@ -39,6 +39,10 @@ struct Problem {
                         // (bf16 for bfloat16 layers, binary32 otherwise)
     void *h;            // [T*k, F]
     void *h_shared;     // [T, Fs]
+    // training forward: the gate/up pre-activations [a | u] of every row
+    // (routed rows in the permuted order, then the shared expert's), or null
+    void *au;           // [T*k, 2F]
+    void *au_sh;        // [T, 2Fs]
     int nblk;           // ceil(T / kCountBlock)
     // MXFP4 expert weights: w_gate_up, w_down, w_sh_gate_up, w_sh_down are
     // then packed MXFP4 tensors (16 x 128 tiles of codes and scales)
@@ -65,6 +69,7 @@ struct GemmArgs {
     const uint16_t *w_sh;  // gate/up: [2Fs, d]     down: [d, Fs]
     uint16_t *h;           // [T*k, F]
     uint16_t *h_sh;        // [T, Fs]
+    uint16_t *au, *au_sh;  // [T*k, 2F], [T, 2Fs] pre-activations [a | u] (training), or null
     float *out;            // [T, d]   shared expert's term (plain stores)
     uint16_t *y;           // [T*k, d] routed rows, weighted, bf16 (plain stores)
     float *f;              // router logits [T, ldf] (MODE 2)
@@ -135,6 +140,7 @@ struct BwdArgs {
     int ldl;
     const int32_t *counts, *offsets, *tile_start, *tile_group, *perm, *rank;
     void *au, *au_sh;   // [T*k, 2F], [T, 2Fs]  gate | up pre-activations
+    bool au_given;      // au holds the training forward's values (no recompute)
     float *g, *g_sh;    // [T*k, F], [T, Fs]    W_dn^T dout of each row
     void *dgu, *dgu_sh; // [T*k, 2F], [T, 2Fs]  da | du
     void *hh, *hh_sh;   // [T*k, F], [T, Fs]    h = silu(a) u

@@ -252,17 +252,17 @@ def test_binding_refuses_cpu_tensors():
         moe.route(x, torch.zeros(8, 64, dtype=torch.bfloat16), 2)
 
 
-BWD_PTRS = ("x", "wr", "b", "gu", "dn", "sgu", "sdn", "g", "idx", "w", "dout", "dx", "dwr",
-            "dgu", "ddn", "dsgu", "dsdn", "dg", "aux")
+BWD_PTRS = ("x", "wr", "b", "gu", "dn", "sgu", "sdn", "g", "idx", "w", "dout", "saved", "dx",
+            "dwr", "dgu", "ddn", "dsgu", "dsdn", "dg", "aux")
 
 
 def call_backward(L, D, T, ptrs=None, coef=0.001, ws=FAKE, ws_bytes=1 << 40):
     p = {n: FAKE for n in BWD_PTRS}
-    p["b"] = p["aux"] = None
+    p["b"] = p["aux"] = p["saved"] = None
     p.update(ptrs or {})
     v = lambda a: None if a is None else ctypes.c_void_p(a)
     args = [v(p[n]) for n in BWD_PTRS]
-    return L.moe_backward(ctypes.byref(D), T, *args[:11], ctypes.c_float(coef), *args[11:],
+    return L.moe_backward(ctypes.byref(D), T, *args[:12], ctypes.c_float(coef), *args[12:],
                           v(ws), ws_bytes, None)
 
 
@@ -279,6 +279,7 @@ def test_backward_validation(L):
     assert call_backward(L, D, -1) == moe.MOE_ERR_INVALID_ARG
     assert call_backward(L, D, 8, {"dout": FAKE + 4}) == moe.MOE_ERR_INVALID_ARG
     assert call_backward(L, D, 8, {"aux": FAKE + 2}) == moe.MOE_ERR_INVALID_ARG
+    assert call_backward(L, D, 8, {"saved": FAKE + 8}) == moe.MOE_ERR_INVALID_ARG
     assert call_backward(L, D, 8, coef=float("nan")) == moe.MOE_ERR_INVALID_ARG
     assert call_backward(L, D, 8, ws=None) == moe.MOE_ERR_WORKSPACE
     need = L.moe_backward_workspace_size(ctypes.byref(D), 8)
@@ -297,3 +298,29 @@ def test_backward_workspace_grows_with_T(L):
     sizes = [L.moe_backward_workspace_size(ctypes.byref(D), T) for T in (1, 10, 1000)]
     assert 0 < sizes[0] < sizes[1] < sizes[2]
     assert L.moe_backward_workspace_size(ctypes.byref(desc(E=0)), 10) == 0
+
+
+def call_forward_train(L, D, T, saved=FAKE, saved_bytes=1 << 40, ws=FAKE, ws_bytes=1 << 40,
+                       ptrs=None):
+    p = dict(x=FAKE, wr=FAKE, b=None, gu=FAKE, dn=FAKE, sgu=FAKE, sdn=FAKE, g=FAKE, out=FAKE,
+             idx=FAKE, w=FAKE)
+    p.update(ptrs or {})
+    v = lambda a: None if a is None else ctypes.c_void_p(a)
+    return L.moe_forward_train(ctypes.byref(D), T, v(p["x"]), v(p["wr"]), v(p["b"]), v(p["gu"]),
+                               v(p["dn"]), v(p["sgu"]), v(p["sdn"]), v(p["g"]), v(p["out"]),
+                               v(p["idx"]), v(p["w"]), v(saved), saved_bytes, v(ws), ws_bytes,
+                               None)
+
+
+def test_forward_train_validation(L):
+    D = desc()
+    need = L.moe_saved_bytes(ctypes.byref(D), 8)
+    assert need == (8 * 4 * 2 * 128 + 8 * 2 * 64) * 2
+    assert L.moe_saved_bytes(ctypes.byref(desc(d=0)), 8) == 0
+    assert call_forward_train(L, D, 8, saved=None) == moe.MOE_ERR_INVALID_ARG
+    assert call_forward_train(L, D, 8, saved=FAKE + 4) == moe.MOE_ERR_INVALID_ARG
+    assert call_forward_train(L, D, 8, saved_bytes=need - 1) == moe.MOE_ERR_INVALID_ARG
+    # the rest as moe_forward: a missing x, a small workspace
+    assert call_forward_train(L, D, 8, saved_bytes=need, ptrs={"x": None}) == moe.MOE_ERR_INVALID_ARG
+    assert call_forward_train(L, D, 8, saved_bytes=need, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
+    assert call_forward_train(L, D, 0, saved=None, saved_bytes=0, ws=None, ws_bytes=0) == moe.MOE_OK

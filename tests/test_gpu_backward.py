@@ -211,3 +211,73 @@ def test_backward_prefill_sampled():
     assert float(got["aux_loss"].cpu()[0]) == pytest.approx(ref["aux_loss"], rel=1e-4)
     dwr = as_f64(got["dw_router"])
     assert np.abs(dwr.sum(axis=0)).max() <= 2.0 ** -8 * np.abs(dwr).sum(axis=0).max()
+
+
+def permuted_rows(idx, E):
+    """The pair id of every routed row in the layer's permuted order: the rows
+    of expert e (ascending pair id) after those of experts < e."""
+    flat = idx.ravel()
+    return np.concatenate([np.nonzero(flat == e)[0] for e in range(E)])
+
+
+@pytest.mark.parametrize("T,d,E,k,F,Fs,dtype", [
+    (24, 256, 16, 4, 128, 128, "bf16"),     # weight-streaming path
+    (300, 256, 16, 4, 128, 128, "bf16"),    # direct-to-LDS GEMM path
+    (300, 256, 16, 4, 192, 64, "bf16"),     # register-staged GEMM (F % 128 != 0)
+    (20, 96, 6, 2, 40, 24, "f32"),          # binary32 layer
+])
+def test_forward_train_saves_preactivations(T, d, E, k, F, Fs, dtype):
+    """moe_forward_train gives moe_forward's outputs bit for bit, and its
+    saved rows are the gate/up pre-activations x W^T of each (token, expert)
+    in the permuted order, within the bf16 rounding of the stored value plus
+    the binary32 accumulation."""
+    inp, _, _, _, _ = routed_case(T, d, E, k, F, Fs, dtype, 61, False)
+    ins = {n: to_dev(inp[n]) for n in WEIGHTS}
+    announce(f"forward_train {dtype} T={T} F={F}")
+    out, idx, w = moe.forward(ins["x"], ins["w_router"], ins["w_gate_up"], ins["w_down"], k,
+                              ins["w_sh_gate_up"], ins["w_sh_down"], ins["sh_gate"])
+    out2, idx2, w2, saved = moe.forward_train(ins["x"], ins["w_router"], ins["w_gate_up"],
+                                              ins["w_down"], k, ins["w_sh_gate_up"],
+                                              ins["w_sh_down"], ins["sh_gate"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(idx, idx2) and torch.equal(w, w2)
+    es = 2 if dtype == "bf16" else 4
+    raw = saved.cpu().numpy()
+    vals = (W.bf16_bits_to_f32(raw.view(np.uint16)) if es == 2 else raw.view(np.float32))
+    vals = vals.astype(np.float64)
+    routed = vals[:T * k * 2 * F].reshape(T * k, 2 * F)
+    shared = vals[T * k * 2 * F:].reshape(T, 2 * Fs)
+    f64 = lambda a: (W.bf16_bits_to_f32(a) if a.dtype == np.uint16 else a).astype(np.float64)
+    x, wgu = f64(inp["x"]), f64(inp["w_gate_up"])
+    pairs = permuted_rows(idx.cpu().numpy(), E)
+    kk = idx.cpu().numpy().ravel()
+    ref = np.stack([wgu[kk[p]] @ x[p // k] for p in pairs])
+    mag = np.stack([np.abs(wgu[kk[p]]) @ np.abs(x[p // k]) for p in pairs])
+    u = 2.0 ** -8 if es == 2 else 0.0
+    assert np.all(np.abs(routed - ref) <= u * np.abs(ref) + d * 2.0 ** -23 * mag + 1e-30)
+    ref_sh = x @ f64(inp["w_sh_gate_up"]).T
+    mag_sh = np.abs(x) @ np.abs(f64(inp["w_sh_gate_up"])).T
+    assert np.all(np.abs(shared - ref_sh) <= u * np.abs(ref_sh) + d * 2.0 ** -23 * mag_sh + 1e-30)
+
+
+@pytest.mark.parametrize("T,F,dtype", [(300, 128, "bf16"), (24, 128, "bf16"), (20, 40, "f32")])
+def test_backward_from_saved_preactivations(T, F, dtype):
+    """moe_backward given moe_forward_train's saved pre-activations (no
+    recompute) meets the same bars against the oracle."""
+    d, E, k, Fs = (256, 16, 4, 128) if dtype == "bf16" else (96, 6, 2, 24)
+    inp, idx, w, dout, b = routed_case(T, d, E, k, F, Fs, dtype, 71, True)
+    ins = {n: to_dev(inp[n]) for n in WEIGHTS}
+    announce(f"backward from saved {dtype} T={T}")
+    _, gidx, gw, saved = moe.forward_train(ins["x"], ins["w_router"], ins["w_gate_up"],
+                                           ins["w_down"], k, ins["w_sh_gate_up"],
+                                           ins["w_sh_down"], ins["sh_gate"], bias=to_dev(b))
+    assert np.array_equal(gidx.cpu().numpy(), idx)
+    got = moe.backward(ins["x"], ins["w_router"], ins["w_gate_up"], ins["w_down"], gidx, gw,
+                       to_dev(dout), ins["w_sh_gate_up"], ins["w_sh_down"], ins["sh_gate"],
+                       bias=to_dev(b), aux_coef=0.01, saved=saved)
+    torch.cuda.synchronize()
+    ref = oracle_backward(inp, idx, gw.cpu().numpy().astype(np.float64), dout, 0.01, b)
+    f32 = dtype == "f32"
+    check_grad("dx", got["dx"], ref["dx"], False, f32_layer=f32)
+    for n in GRADS:
+        check_grad(n, got[n], ref[n], not f32, f32_layer=f32)
