@@ -217,24 +217,25 @@ __global__ __launch_bounds__(256) void router_row_norm_kernel(const uint16_t *__
     if (lane == 0) wnorm[e] = sqrtf(s2);
 }
 
-// Exact canonical logit of expert e for the token whose 512-chunk slices
-// this wave holds (lane j: elements 512 c + 8 j .. + 8 of chunk c); the same
-// order as router_logits_kernel, so the bits agree.
+// Exact canonical logit for the token whose 512-chunk slices this wave holds
+// (lane j: elements 512 c + 8 j .. + 8 of chunk c), from the matching slices
+// wq of one router row; the same order as router_logits_kernel, so the bits
+// agree.
 template <int NC>
-__device__ __forceinline__ float canonical_logit(const uint4 (&xs)[NC], const uint16_t *wrow,
-                                                 int d, int lane, float b) {
+__device__ __forceinline__ float canonical_dot(const uint4 (&xs)[NC], const uint4 (&wq)[NC],
+                                               int d, int lane, float b) {
     float acc = 0.0f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         const int kk0 = 512 * c + 8 * lane;
         if (kk0 < d) {
-            float wv[8];
-            load8(wrow + kk0, wv);
-            const uint32_t q4[4] = {xs[c].x, xs[c].y, xs[c].z, xs[c].w};
+            const uint32_t x4[4] = {xs[c].x, xs[c].y, xs[c].z, xs[c].w};
+            const uint32_t w4[4] = {wq[c].x, wq[c].y, wq[c].z, wq[c].w};
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                const float xv = (q & 1) ? bf16_hi(q4[q >> 1]) : bf16_lo(q4[q >> 1]);
-                acc = __builtin_fmaf(xv, wv[q], acc);
+                const float xv = (q & 1) ? bf16_hi(x4[q >> 1]) : bf16_lo(x4[q >> 1]);
+                const float wv = (q & 1) ? bf16_hi(w4[q >> 1]) : bf16_lo(w4[q >> 1]);
+                acc = __builtin_fmaf(xv, wv, acc);
             }
         }
     }
@@ -244,6 +245,33 @@ __device__ __forceinline__ float canonical_logit(const uint4 (&xs)[NC], const ui
     }
     return __shfl(acc, 0, kWave) + b;
 }
+
+// This lane's slices of router row wrow; slices past d read slice 0 (a valid
+// address; canonical_dot never uses them).
+template <int NC>
+__device__ __forceinline__ void load_row_slices(const uint16_t *wrow, int d, int lane,
+                                                uint4 (&wq)[NC]) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int kk0 = 512 * c + 8 * lane;
+        wq[c] = *reinterpret_cast<const uint4 *>(wrow + (kk0 < d ? kk0 : 0));
+    }
+}
+
+template <int NC>
+__device__ __forceinline__ float canonical_logit(const uint4 (&xs)[NC], const uint16_t *wrow,
+                                                 int d, int lane, float b) {
+    uint4 wq[NC];
+    load_row_slices<NC>(wrow, d, lane, wq);
+    return canonical_dot<NC>(xs, wq, d, lane, b);
+}
+
+// Shortlist candidates whose exact logits are computed together: their row
+// loads are all in flight before the first dot product.  Two (one for rows
+// longer than 4096), with the kernel held to 128 VGPRs (4 waves per SIMD) for
+// d <= 2560, measured fastest at T = 4096, d = 2560: larger batches cost
+// occupancy, and this kernel is latency-bound.
+template <int NC> constexpr int cand_batch() { return NC <= 8 ? 2 : 1; }
 
 // Wave-wide argmax under (value desc, expert asc); every lane gets the result.
 __device__ __forceinline__ void wave_best(float &bv, int &be) {
@@ -259,12 +287,13 @@ __device__ __forceinline__ void wave_best(float &bv, int &be) {
 
 // One wave per token; NV = ceil(E / 64) logits per lane, NC >= ceil(d / 512).
 template <int NV, int NC>
-__global__ __launch_bounds__(256) void router_select_shortlist_kernel(
+__global__ __launch_bounds__(256, NC <= 5 ? 4 : 1) void router_select_shortlist_kernel(
     const float *__restrict__ f, const float *__restrict__ wnorm, const uint16_t *__restrict__ x,
     const uint16_t *__restrict__ w_router, const uint16_t *__restrict__ g,
     const float *__restrict__ bias, int64_t ntok, int d, int E, int k, float coef,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, float *__restrict__ gate,
     float *__restrict__ gate_user) {
+    __shared__ int s_cand[4][32];
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= ntok) return;
@@ -354,23 +383,40 @@ __global__ __launch_bounds__(256) void router_select_shortlist_kernel(
     float my_l = 0.f;
     int my_e = 0;
     if (count <= 32) {
-        // exact logits of the shortlist; candidate c lives in lane c
+        // the shortlist in ascending expert order, candidate c at cand[c]
+        int *cand = s_cand[threadIdx.x >> 6];
+        {
+            int base = 0;
+            const uint64_t below = (1ull << lane) - 1;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                if ((pass[i] >> lane) & 1ull) cand[base + __popcll(pass[i] & below)] = 64 * i + lane;
+                base += __popcll(pass[i]);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        // exact logits of the shortlist, CB rows in flight at a time;
+        // candidate c lives in lane c
         float lc = -INFINITY;
         int ec = 0x7FFFFFFF;
-        int c = 0;
+        constexpr int CB = cand_batch<NC>();
+        for (int c0 = 0; c0 < count; c0 += CB) {
+            int e[CB];
+            uint4 wq[CB][NC];
+            float b[CB];
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            uint64_t m = pass[i];
-            while (m) {
-                const int e = 64 * i + __builtin_ctzll(m);
-                m &= m - 1;
-                const float l = canonical_logit<NC>(xs, w_router + (int64_t)e * d, d, lane,
-                                                    bias ? bias[e] : 0.0f);
-                if (lane == c) {
+            for (int u = 0; u < CB; ++u) {
+                e[u] = cand[min(c0 + u, count - 1)];
+                load_row_slices<NC>(w_router + (int64_t)e[u] * d, d, lane, wq[u]);
+                b[u] = bias ? bias[e[u]] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < CB; ++u) {
+                const float l = canonical_dot<NC>(xs, wq[u], d, lane, b[u]);
+                if (lane == c0 + u) {
                     lc = (l == l) ? l : -INFINITY;
-                    ec = e;
+                    ec = e[u];
                 }
-                ++c;
             }
         }
         // top k of the shortlist: DPP maximum, lowest lane (= lowest expert,
