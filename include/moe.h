@@ -102,13 +102,21 @@ size_t moe_workspace_size(const moe_desc *desc, int64_t T);
  * after a call on the same stream has completed (y: moe_forward/moe_experts).
  *   logits   float [T, E+1]   router logits: exact router: canonical logits,
  *                             column E = g . x_t; shortlist router: the
- *                             MFMA logits f (no bias, column E unused)
+ *                             MFMA logits f (no bias, column E unused) as
+ *                             S partial sums [S, T, E+1] over consecutive
+ *                             K slices, f = p_0 + p_1 (S = 2) if
+ *                             d % 128 == 0, else S = 1
  *   gate     float [T]        s_t = sigmoid(g . x_t)
  *   counts   int32 [E+1]      tokens per expert; counts[E] = T (shared)
  *   offsets  int32 [E+1]      exclusive prefix of counts[0..E-1]
  *   perm     int32 [T*k]      row r of expert e (offsets[e] <= r < offsets[e+1])
  *                             holds the pair id t*k+j; rows of one expert are in
  *                             ascending pair id
+ *   Exception: moe_forward / moe_forward_mx4 / moe_forward_prenorm with
+ *   T <= 32 on the weight-streaming path and the exact router skip the
+ *   permutation: counts[e] = 1 for each selected expert (0 otherwise),
+ *   counts[E] = the number of selected experts, offsets and perm are not
+ *   written, and the rows of h and y are the pair ids t*k+j.
  *   h        [T*k, F]         gated activations of the routed rows (bf16 / f32)
  *   h_shared [T, Fs]          gated activations of the shared expert
  *   y        [T*k, d]         w[t,j] * expert output of each routed row (bf16 /

@@ -66,9 +66,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
         }
     }
     const int Fg = shared ? a.Fs : a.F;            // width of this group's expert
-    // output columns (gate half for MODE 0) and contraction length
+    // output columns (gate half for MODE 0) and contraction length; MODE 2
+    // blocks with blockIdx.y = s cover K slice s of ksplit
     const int N = MODE == 0 ? Fg : MODE == 1 ? a.d : a.E;
-    const int K = MODE == 1 ? Fg : a.d;
+    const int K = MODE == 1 ? Fg : MODE == 2 ? a.d / a.ksplit : a.d;
+    const int kbeg = MODE == 2 ? (int)blockIdx.y * K : 0;
     const int n0 = nt * (MODE == 0 ? 64 : BN);
     if (n0 >= N) return;
 
@@ -117,8 +119,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
             const int wrow = min(n0 + r, a.d - 1);
             bsrc[p] = wbase + (int64_t)wrow * Fg;
         }
-        asrc[p] += lchunk * 8;
-        bsrc[p] += lchunk * 8;
+        asrc[p] += kbeg + lchunk * 8;
+        bsrc[p] += kbeg + lchunk * 8;
     }
 
     uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
@@ -219,7 +221,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
                     const int row = 64 * wm + 32 * mi + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
                     const int col = n0 + (ni ? brow1 : brow0) + fr;
                     if (row < nrows && col < a.E)
-                        a.f[(int64_t)(row0 + row) * a.ldf + col] = acc[mi][ni][v];
+                        a.f[((int64_t)blockIdx.y * a.T + row0 + row) * a.ldf + col] =
+                            acc[mi][ni][v];
                 }
     } else {
 #pragma unroll
@@ -293,7 +296,9 @@ hipError_t launch_router_gemm(const Problem &p, hipStream_t s) {
     a.nm = (int)((p.T + BM - 1) / BM);
     a.nn = (p.E + BN - 1) / BN;
     a.gm = 8;
-    hipLaunchKernelGGL(grouped_gemm_kernel<2>, dim3((unsigned)(8 * ((a.nm * a.nn + 7) / 8))),
+    a.ksplit = p.router_split;
+    hipLaunchKernelGGL(grouped_gemm_kernel<2>,
+                       dim3((unsigned)(8 * ((a.nm * a.nn + 7) / 8)), (unsigned)a.ksplit),
                        dim3(256), 0, s, a);
     return hipGetLastError();
 }

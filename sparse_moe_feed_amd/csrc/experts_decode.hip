@@ -17,6 +17,8 @@
 #include "moe_device.h"
 #include "moe_kernels.h"
 
+#include <algorithm>
+
 namespace moe {
 
 constexpr int DBM = kDecodeBM;  // rows per decode tile
@@ -33,9 +35,11 @@ struct DecodeArgs {
     float *out;
     uint16_t *y;           // [T*k, d] weighted routed rows (bf16)
     const int32_t *perm, *counts, *offsets, *tile_start, *tile_group;
+    const int32_t *topk_idx;
     const float *topk_w, *gate;
     int64_t T;
     int d, E, k, F, Fs;
+    int direct;            // tiles without the permutation step (decode_tile)
 };
 
 struct Frag {
@@ -140,13 +144,77 @@ __device__ __forceinline__ void stream_k(const uint16_t *const (&bp)[NB],
     stream_k_from<NB, HALVES>(b0, a0, bp, ap, K, acc);
 }
 
+// A tile's rows: rows r < nrows of group g.  With the permutation step they
+// are the consecutive permuted rows row0 + r; without it (direct) routed rows
+// are the pairs rows[r] (h and y indexed by pair id); shared-expert rows are
+// the tokens row0 + r either way.
 struct TileInfo {
     int g, row0, nrows;
     bool shared;
+    const int *rows;  // direct routed tiles: this wave's LDS list of pair ids, else null
 };
 
+__device__ __forceinline__ int tile_row(const TileInfo &ti, int r) {
+    return ti.rows ? ti.rows[r] : ti.row0 + r;
+}
+
+// Pair (routed) or token (shared) of row r: what the gate/up A rows and the
+// down epilogue's weights are looked up by.
 template <class Args>
-__device__ __forceinline__ bool decode_tile(const Args &a, TileInfo &ti) {
+__device__ __forceinline__ int tile_src(const Args &a, const TileInfo &ti, int r) {
+    return ti.shared ? ti.row0 + r : ti.rows ? ti.rows[r] : a.perm[ti.row0 + r];
+}
+
+constexpr int kScanChunks = DBM * 32 / 64;  // 64-pair chunks of topk_idx at T <= DBM, k <= 32
+
+// Direct tiles (T <= DBM, so an expert has at most DBM pairs when the top-k
+// experts of a token are distinct): the router listed the n touched experts
+// (counts[E] = n, tile_group[0..n) = the experts); block x < n serves expert
+// tile_group[x], block n the shared expert (if any), later blocks end.  Each
+// wave scans topk_idx and lists the expert's pairs in ascending pair id in
+// its own LDS slots (no block barrier).
+template <class Args>
+__device__ __forceinline__ bool decode_tile_direct(const Args &a, TileInfo &ti, int *rows) {
+    const int nt = a.counts[a.E];
+    const int x = blockIdx.x;
+    if (x > nt || (x == nt && a.Fs == 0)) return false;
+    ti.shared = x == nt;
+    ti.g = ti.shared ? a.E : a.tile_group[x];
+    ti.row0 = 0;
+    ti.rows = nullptr;
+    if (ti.shared) {
+        ti.nrows = (int)a.T;
+        return true;
+    }
+    const int lane = threadIdx.x & 63;
+    const int np = (int)a.T * a.k;  // <= DBM * 32 = 64 kScanChunks
+    const uint64_t below = (1ull << lane) - 1;
+    // every chunk's load issued before the first compare: one round trip
+    // (addresses clamped into the array, so the loads need no branch)
+    int v[kScanChunks];
+#pragma unroll
+    for (int i = 0; i < kScanChunks; ++i) v[i] = a.topk_idx[min(64 * i + lane, np - 1)];
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < kScanChunks; ++i) {
+        const int p = 64 * i + lane;
+        const bool hit = v[i] == ti.g && p < np;
+        const uint64_t m = __ballot(hit);
+        const int at = n + __popcll(m & below);
+        if (hit && at < DBM) rows[at] = p;
+        n += __popcll(m);
+    }
+    if (n == 0) return false;
+    __builtin_amdgcn_wave_barrier();
+    ti.nrows = min(n, DBM);
+    ti.rows = rows;
+    return true;
+}
+
+template <class Args>
+__device__ __forceinline__ bool decode_tile(const Args &a, TileInfo &ti, int *rows) {
+    if (a.direct) return decode_tile_direct(a, ti, rows);
+    ti.rows = nullptr;
     const int tile = blockIdx.x;
     if (tile >= a.tile_start[a.E + 1]) return false;
     ti.g = a.tile_group[tile];
@@ -177,7 +245,7 @@ __device__ void decode_gateup_body(const DecodeArgs &a, const TileInfo &ti) {
 #pragma unroll
     for (int h = 0; h < HALVES; ++h) {
         const int r = min(16 * h + rl, ti.nrows - 1);  // padding rows repeat the last row
-        tok[h] = ti.shared ? ti.row0 + r : a.perm[ti.row0 + r];
+        tok[h] = tile_src(a, ti, r);
     }
     const uint16_t *bp[2] = {W + (int64_t)(ncol + rl) * a.d + kq,
                              W + (int64_t)(Fg + ncol + rl) * a.d + kq};
@@ -202,10 +270,10 @@ __device__ void decode_gateup_body(const DecodeArgs &a, const TileInfo &ti) {
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * h + 4 * (lane >> 4) + i;
             if (row < ti.nrows) {
-                H[(int64_t)(ti.row0 + row) * Fg + ncol + rl] =
-                    f32_to_bf16_rne(silu_mul(acc[h][0][i], acc[h][1][i]));
+                const int64_t hr = tile_row(ti, row);
+                H[hr * Fg + ncol + rl] = f32_to_bf16_rne(silu_mul(acc[h][0][i], acc[h][1][i]));
                 if (a.au) {  // training forward: the pre-activations too
-                    uint16_t *arow = (ti.shared ? a.au_sh : a.au) + (int64_t)(ti.row0 + row) * 2 * Fg;
+                    uint16_t *arow = (ti.shared ? a.au_sh : a.au) + hr * 2 * Fg;
                     arow[ncol + rl] = f32_to_bf16_rne(acc[h][0][i]);
                     arow[Fg + ncol + rl] = f32_to_bf16_rne(acc[h][1][i]);
                 }
@@ -214,8 +282,9 @@ __device__ void decode_gateup_body(const DecodeArgs &a, const TileInfo &ti) {
 }
 
 __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(DecodeArgs a) {
+    __shared__ int rows[DW][DBM];
     TileInfo ti;
-    if (!decode_tile(a, ti)) return;
+    if (!decode_tile(a, ti, rows[threadIdx.x >> 6])) return;
     const int Fg = ti.shared ? a.Fs : a.F;
     if (blockIdx.y * 16 * DW >= Fg) return;
     if (ti.nrows > 16) decode_gateup_body<2>(a, ti);
@@ -241,7 +310,7 @@ __device__ void decode_down_body(const DecodeArgs &a, const TileInfo &ti) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = min(16 * h + 4 * (lane >> 4) + i, ti.nrows - 1);
-            src[h][i] = ti.shared ? ti.row0 + r : a.perm[ti.row0 + r];
+            src[h][i] = tile_src(a, ti, r);
         }
     const uint16_t *W = ti.shared ? a.w_sh : a.w + (int64_t)ti.g * a.d * a.F;
     const uint16_t *bp[2] = {W + (int64_t)min(ncol + rl, a.d - 1) * Fg + kq,
@@ -251,7 +320,7 @@ __device__ void decode_down_body(const DecodeArgs &a, const TileInfo &ti) {
 #pragma unroll
     for (int h = 0; h < HALVES; ++h) {
         const int r = 16 * h + rl;
-        ap[h] = H + (int64_t)(ti.row0 + min(r, ti.nrows - 1)) * Fg + kq;
+        ap[h] = H + (int64_t)tile_row(ti, min(r, ti.nrows - 1)) * Fg + kq;
     }
     f32x4 acc[HALVES][2];
 #pragma unroll
@@ -275,14 +344,15 @@ __device__ void decode_down_body(const DecodeArgs &a, const TileInfo &ti) {
                 if (row < ti.nrows && col < a.d) {
                     const float v = wr[h][i] * acc[h][n][i];
                     if (ti.shared) a.out[(int64_t)(ti.row0 + row) * a.d + col] = v;
-                    else a.y[(int64_t)(ti.row0 + row) * a.d + col] = f32_to_bf16_rne(v);
+                    else a.y[(int64_t)tile_row(ti, row) * a.d + col] = f32_to_bf16_rne(v);
                 }
             }
 }
 
 __global__ __launch_bounds__(64 * DW) void decode_down_kernel(DecodeArgs a) {
+    __shared__ int rows[DW][DBM];
     TileInfo ti;
-    if (!decode_tile(a, ti)) return;
+    if (!decode_tile(a, ti, rows[threadIdx.x >> 6])) return;
     if (blockIdx.y * 32 * DW >= a.d) return;
     if (ti.nrows > 16) decode_down_body<2>(a, ti);
     else decode_down_body<1>(a, ti);
@@ -324,9 +394,11 @@ struct Mx4Args {
     float *out;
     uint16_t *y;
     const int32_t *perm, *counts, *offsets, *tile_start, *tile_group;
+    const int32_t *topk_idx;
     const float *topk_w, *gate;
     int64_t T;
     int d, E, k, F, Fs;
+    int direct;            // tiles without the permutation step (decode_tile)
 };
 
 struct Mx4Group {
@@ -420,7 +492,7 @@ __device__ void mx4_gateup_body(const Mx4Args &a, const TileInfo &ti) {
 #pragma unroll
     for (int h = 0; h < HALVES; ++h) {
         const int r = min(16 * h + rl, ti.nrows - 1);  // padding rows repeat the last row
-        tok[h] = ti.shared ? ti.row0 + r : a.perm[ti.row0 + r];
+        tok[h] = tile_src(a, ti, r);
     }
     const int64_t row_base = ti.shared ? 0 : (int64_t)ti.g * 2 * a.F;
     const uint8_t *P = ti.shared ? a.wp_sh : a.wp;
@@ -457,14 +529,15 @@ __device__ void mx4_gateup_body(const Mx4Args &a, const TileInfo &ti) {
             if (row < ti.nrows)
 #pragma unroll
                 for (int n = 0; n < 2; ++n)
-                    H[(int64_t)(ti.row0 + row) * Fg + c0 + 16 * n + rl] =
+                    H[(int64_t)tile_row(ti, row) * Fg + c0 + 16 * n + rl] =
                         f32_to_bf16_rne(silu_mul(acc[h][n][i], acc[h][n + 2][i]));
         }
 }
 
 __global__ __launch_bounds__(64 * DW) void decode_gateup_mx4_kernel(Mx4Args a) {
+    __shared__ int rows[DW][DBM];
     TileInfo ti;
-    if (!decode_tile(a, ti)) return;
+    if (!decode_tile(a, ti, rows[threadIdx.x >> 6])) return;
     const int Fg = ti.shared ? a.Fs : a.F;
     if (blockIdx.y * 32 * DW >= Fg) return;
     if (ti.nrows > 16) mx4_gateup_body<2>(a, ti);
@@ -486,7 +559,7 @@ __device__ void mx4_down_body(const Mx4Args &a, const TileInfo &ti) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = min(16 * h + 4 * q + i, ti.nrows - 1);
-            src[h][i] = ti.shared ? ti.row0 + r : a.perm[ti.row0 + r];
+            src[h][i] = tile_src(a, ti, r);
         }
     const int64_t row_base = ti.shared ? 0 : (int64_t)ti.g * a.d;
     const uint8_t *P = ti.shared ? a.wp_sh : a.wp;
@@ -506,7 +579,7 @@ __device__ void mx4_down_body(const Mx4Args &a, const TileInfo &ti) {
     const uint16_t *ap[HALVES];
 #pragma unroll
     for (int h = 0; h < HALVES; ++h)
-        ap[h] = H + (int64_t)(ti.row0 + min(16 * h + rl, ti.nrows - 1)) * Fg + 32 * q;
+        ap[h] = H + (int64_t)tile_row(ti, min(16 * h + rl, ti.nrows - 1)) * Fg + 32 * q;
     Frag a0[HALVES];
     mx4_load_a<HALVES>(a0, ap, 0);
     f32x4 acc[HALVES][NB4];
@@ -531,14 +604,15 @@ __device__ void mx4_down_body(const Mx4Args &a, const TileInfo &ti) {
                 if (row < ti.nrows && col < a.d) {
                     const float v = wr[h][i] * acc[h][n][i];
                     if (ti.shared) a.out[(int64_t)(ti.row0 + row) * a.d + col] = v;
-                    else a.y[(int64_t)(ti.row0 + row) * a.d + col] = f32_to_bf16_rne(v);
+                    else a.y[(int64_t)tile_row(ti, row) * a.d + col] = f32_to_bf16_rne(v);
                 }
             }
 }
 
 __global__ __launch_bounds__(64 * DW) void decode_down_mx4_kernel(Mx4Args a) {
+    __shared__ int rows[DW][DBM];
     TileInfo ti;
-    if (!decode_tile(a, ti)) return;
+    if (!decode_tile(a, ti, rows[threadIdx.x >> 6])) return;
     if (blockIdx.y * 64 * DW >= a.d) return;
     if (ti.nrows > 16) mx4_down_body<2>(a, ti);
     else mx4_down_body<1>(a, ti);
@@ -583,6 +657,8 @@ hipError_t launch_experts_decode_mx4(const Problem &p, hipStream_t s,
     a.offsets = p.offsets;
     a.tile_start = p.tile_start;
     a.tile_group = p.tile_group;
+    a.topk_idx = p.topk_idx;
+    a.direct = p.direct;
     a.topk_w = p.topk_w;
     a.gate = p.gate;
     a.T = p.T;
@@ -592,14 +668,16 @@ hipError_t launch_experts_decode_mx4(const Problem &p, hipStream_t s,
     a.F = p.F;
     a.Fs = p.Fs;
     const int fmax = p.F > p.Fs ? p.F : p.Fs;
+    // direct: at most min(E, T k) touched experts, then the shared expert
+    const unsigned gx = p.direct ? (unsigned)(std::min<int64_t>(p.E, p.T * p.k) + 1) : (unsigned)p.max_tiles;
     a.wp = static_cast<const uint8_t *>(p.w_gate_up);
     a.wp_sh = static_cast<const uint8_t *>(p.w_sh_gate_up);
-    hipLaunchKernelGGL(decode_gateup_mx4_kernel, dim3(p.max_tiles, (fmax + 32 * DW - 1) / (32 * DW)),
+    hipLaunchKernelGGL(decode_gateup_mx4_kernel, dim3(gx, (fmax + 32 * DW - 1) / (32 * DW)),
                        dim3(64 * DW), 0, s, a);
     mark(3);
     a.wp = static_cast<const uint8_t *>(p.w_down);
     a.wp_sh = static_cast<const uint8_t *>(p.w_sh_down);
-    hipLaunchKernelGGL(decode_down_mx4_kernel, dim3(p.max_tiles, (p.d + 64 * DW - 1) / (64 * DW)),
+    hipLaunchKernelGGL(decode_down_mx4_kernel, dim3(gx, (p.d + 64 * DW - 1) / (64 * DW)),
                        dim3(64 * DW), 0, s, a);
     mark(4);
     return hipGetLastError();
@@ -620,6 +698,8 @@ hipError_t launch_experts_decode(const Problem &p, hipStream_t s,
     a.offsets = p.offsets;
     a.tile_start = p.tile_start;
     a.tile_group = p.tile_group;
+    a.topk_idx = p.topk_idx;
+    a.direct = p.direct;
     a.topk_w = p.topk_w;
     a.gate = p.gate;
     a.T = p.T;
@@ -629,14 +709,16 @@ hipError_t launch_experts_decode(const Problem &p, hipStream_t s,
     a.F = p.F;
     a.Fs = p.Fs;
     const int fmax = p.F > p.Fs ? p.F : p.Fs;
+    // direct: at most min(E, T k) touched experts, then the shared expert
+    const unsigned gx = p.direct ? (unsigned)(std::min<int64_t>(p.E, p.T * p.k) + 1) : (unsigned)p.max_tiles;
     a.w = static_cast<const uint16_t *>(p.w_gate_up);
     a.w_sh = static_cast<const uint16_t *>(p.w_sh_gate_up);
-    hipLaunchKernelGGL(decode_gateup_kernel, dim3(p.max_tiles, (fmax + 16 * DW - 1) / (16 * DW)), dim3(64 * DW), 0, s,
+    hipLaunchKernelGGL(decode_gateup_kernel, dim3(gx, (fmax + 16 * DW - 1) / (16 * DW)), dim3(64 * DW), 0, s,
                        a);
     mark(3);
     a.w = static_cast<const uint16_t *>(p.w_down);
     a.w_sh = static_cast<const uint16_t *>(p.w_sh_down);
-    hipLaunchKernelGGL(decode_down_kernel, dim3(p.max_tiles, (p.d + 32 * DW - 1) / (32 * DW)), dim3(64 * DW), 0, s,
+    hipLaunchKernelGGL(decode_down_kernel, dim3(gx, (p.d + 32 * DW - 1) / (32 * DW)), dim3(64 * DW), 0, s,
                        a);
     mark(4);
     return hipGetLastError();

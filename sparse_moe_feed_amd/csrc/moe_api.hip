@@ -68,6 +68,12 @@ struct Plan {
     int max_tiles;
 };
 
+// The shortlist router serves bf16 layers of 128 tokens or more unless a
+// flag picks a router.
+bool uses_shortlist(const moe_desc &d, int64_t T) {
+    return d.flags == MOE_FLAG_ROUTER_SHORTLIST || (d.flags == 0 && d.dtype == MOE_BF16 && T >= 128);
+}
+
 Plan make_plan(const moe_desc &d, int64_t T) {
     Plan p;
     const size_t esize = d.dtype == MOE_BF16 ? 2 : 4;
@@ -81,7 +87,8 @@ Plan make_plan(const moe_desc &d, int64_t T) {
         off = align_up(off + bytes);
         return at;
     };
-    p.logits = take((size_t)T * (d.n_experts + 1) * sizeof(float));
+    p.logits = take((size_t)T * (d.n_experts + 1) * sizeof(float) *
+                    (uses_shortlist(d, T) ? moe::shortlist_split(d.d_model) : 1));
     p.wnorm = take((size_t)d.n_experts * sizeof(float));
     p.gate = take((size_t)T * sizeof(float));
     p.counts = take((size_t)(d.n_experts + 1) * sizeof(int32_t));
@@ -112,8 +119,8 @@ moe::Problem make_problem(const moe_desc &d, int64_t T, const Plan &pl, void *ws
     char *base = static_cast<char *>(ws);
     p.logits = reinterpret_cast<float *>(base + pl.logits);
     p.wnorm = reinterpret_cast<float *>(base + pl.wnorm);
-    p.router = d.flags == MOE_FLAG_ROUTER_SHORTLIST ||
-               (d.flags == 0 && d.dtype == MOE_BF16 && T >= 128);
+    p.router = uses_shortlist(d, T);
+    p.router_split = p.router ? moe::shortlist_split(d.d_model) : 1;
     p.gate = reinterpret_cast<float *>(base + pl.gate);
     p.counts = reinterpret_cast<int32_t *>(base + pl.counts);
     p.offsets = reinterpret_cast<int32_t *>(base + pl.offsets);
@@ -225,15 +232,27 @@ bool use_dma_path(const moe::Problem &p) {
     return pairs * widest < ((int64_t)1 << 32) && p.T * (int64_t)(p.E + 1) < ((int64_t)1 << 32);
 }
 
-// Stages 2..5 of a call: permutation, gate/up, down, combine.
+bool decode_regime(const moe::Problem &p) {
+    return p.mx4 ? p.T * p.k <= (int64_t)16 * p.E : use_decode_path(p);
+}
+
+// The weight-streaming path skips the permutation step when an expert fits
+// one tile (T <= kDecodeBM) and the exact router, run in the same call, lists
+// the touched experts (its top-k experts of a token are distinct); the
+// training forward keeps the permuted row order its saved tensors use.
+bool direct_decode(const moe::Problem &p) {
+    return decode_regime(p) && p.T <= moe::kDecodeBM && !p.au && p.router == 0;
+}
+
+// Stages 2..5 of a call: permutation (unless p.direct), gate/up, down, combine.
 moe_status run_experts(moe::Problem p, hipStream_t s) {
-    const bool decode = p.mx4 ? p.T * p.k <= (int64_t)16 * p.E : use_decode_path(p);
+    const bool decode = decode_regime(p);
     const bool dma = !decode && use_dma_path(p);
     // 256-row tiles once experts average 192+ rows
     const bool big = dma && !p.mx4 && p.T * p.k >= (int64_t)192 * p.E;  // MXFP4 GEMM: 128 rows
     const int bm = decode ? moe::kDecodeBM : big ? moe::kGemm256BM : moe::kGemmBM;
     p.max_tiles = (int)moe::max_gemm_tiles(p.T, p.k, p.E, bm, p.Fs > 0);
-    hipError_t err = moe::launch_permute(p, bm, s);
+    hipError_t err = p.direct ? hipSuccess : moe::launch_permute(p, bm, s);
     mark_stage(2, s);
     auto mark = [&](int i) { mark_stage(i, s); };
     if (err == hipSuccess)
@@ -312,6 +331,7 @@ moe_status forward_impl(const moe_desc *desc, int64_t T, const void *x, const vo
     if (norm_weight)
         err = moe::launch_rmsnorm(x, norm_weight, eps, static_cast<char *>(ws) + pl.xnorm, T, p.d,
                                   p.bf16, s);
+    p.direct = direct_decode(p);
     if (err == hipSuccess) err = moe::launch_router(p, nullptr, s);
     st = hip_status(err);
     mark_stage(1, s);

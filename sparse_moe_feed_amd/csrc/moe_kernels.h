@@ -23,9 +23,10 @@ struct Problem {
     int32_t *topk_idx;
     float *topk_w;
     // workspace regions
-    float *logits;      // [T, E+1]
+    float *logits;      // [T, E+1]; shortlist router: [router_split, T, E+1]
     float *wnorm;       // [E] Euclidean norms of the router rows
     int router;         // 0: exact canonical logits for all experts; 1: MFMA shortlist
+    int router_split;   // shortlist: K slices of the MFMA logits (partial sums)
     float *gate;        // [T]
     int32_t *counts;    // [E+1]
     int32_t *offsets;   // [E+1]
@@ -44,6 +45,13 @@ struct Problem {
     void *au;           // [T*k, 2F]
     void *au_sh;        // [T, 2Fs]
     int nblk;           // ceil(T / kCountBlock)
+    // weight-streaming path without the permutation step (T <= kDecodeBM,
+    // routing from this library's exact router): the router's select step
+    // lists the touched experts (counts[e] = 1 once e is selected, counts[E]
+    // = how many, tile_group[i] = the i-th in arrival order); block x serves
+    // expert tile_group[x] (x = counts[E]: the shared expert), finds its pairs
+    // in topk_idx, and h / y rows are indexed by pair id t*k+j
+    bool direct;
     // MXFP4 expert weights: w_gate_up, w_down, w_sh_gate_up, w_sh_down are
     // then packed MXFP4 tensors (16 x 128 tiles of codes and scales)
     bool mx4;
@@ -72,8 +80,8 @@ struct GemmArgs {
     uint16_t *au, *au_sh;  // [T*k, 2F], [T, 2Fs] pre-activations [a | u] (training), or null
     float *out;            // [T, d]   shared expert's term (plain stores)
     uint16_t *y;           // [T*k, d] routed rows, weighted, bf16 (plain stores)
-    float *f;              // router logits [T, ldf] (MODE 2)
-    int ldf;
+    float *f;              // router logits [ksplit, T, ldf] (MODE 2): one partial per K slice
+    int ldf, ksplit;
     const int32_t *perm, *counts, *offsets, *tile_start, *tile_group;
     const float *topk_w, *gate;
     int64_t T;
@@ -86,8 +94,14 @@ inline unsigned raster_blocks(int nm, int nn, int gm) {
     return gm < 0 ? (unsigned)(8 * ((nm + 7) / 8) * nn) : (unsigned)(8 * ((nm * nn + 7) / 8));
 }
 
-// Router logits f = x W_r^T on MFMA (binary32 accumulate, any order).
+// Router logits f = x W_r^T on MFMA (binary32 accumulate, any order), as
+// p.router_split partial sums over consecutive slices of K.
 hipError_t launch_router_gemm(const Problem &p, hipStream_t s);
+// K slices of the shortlist router's MFMA logits for d (d % 64 == 0): twice
+// the blocks for the short, wide GEMM; the select step adds them in order.
+// At T = 4096, d = 2560 the route stage took 80 / 67 / 69 / 86 us with
+// 1 / 2 / 4 / 8 slices.
+inline int shortlist_split(int d) { return d % 128 == 0 ? 2 : 1; }
 // Grouped GEMM expert stage with bm x 256 tiles (bm = 256 or 128) staged by
 // direct global -> LDS loads; needs F, Fs % 128 == 0 and 32-bit offsets.
 hipError_t launch_experts_dma(const Problem &p, int bm, hipStream_t s,

@@ -233,7 +233,8 @@ hipError_t launch_permute(const Problem &p, int bm, hipStream_t s) {
 // slot order j = 0..k-1, all in binary32.  Deterministic: no atomics.
 //
 // bfloat16 layers keep the routed rows in bf16: block (t, c) handles token t
-// and columns 512 c .. 512 c + 511, eight per thread.
+// and columns 512 c .. 512 c + 511, eight per thread.  row_of null: the rows
+// are indexed by pair id (the permutation step was skipped), row t*k+j.
 template <bool SHARED>
 __global__ __launch_bounds__(64) void combine_bf16_kernel(const uint16_t *__restrict__ y,
                                                           const int32_t *__restrict__ row_of,
@@ -252,10 +253,10 @@ __global__ __launch_bounds__(64) void combine_bf16_kernel(const uint16_t *__rest
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.f;
     }
-    const int32_t *rows = row_of + t * k;
     for (int j = 0; j < k; ++j) {
+        const int64_t r = row_of ? row_of[t * k + j] : t * k + j;
         float v[8];
-        load8(y + (int64_t)rows[j] * d + c, v);
+        load8(y + r * d + c, v);
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] += v[i];
     }
@@ -270,7 +271,7 @@ __global__ __launch_bounds__(128) void combine_f32_kernel(const float *__restric
                                                           float *__restrict__ out, int d, int k) {
     const int64_t t = blockIdx.x;
     __shared__ int32_t rows[32];
-    if (threadIdx.x < k) rows[threadIdx.x] = row_of[t * k + threadIdx.x];
+    if (threadIdx.x < k) rows[threadIdx.x] = row_of ? row_of[t * k + threadIdx.x] : (int32_t)(t * k + threadIdx.x);
     __syncthreads();
     float *o = out + t * d;
     for (int c = threadIdx.x; c < d; c += 128) {
@@ -281,23 +282,24 @@ __global__ __launch_bounds__(128) void combine_f32_kernel(const float *__restric
 }
 
 hipError_t launch_combine(const Problem &p, hipStream_t s) {
+    const int32_t *rows = p.direct ? nullptr : p.rank;
     if (p.bf16) {
         const dim3 grid((unsigned)p.T, (unsigned)((p.d / 8 + 63) / 64));
         const uint16_t *y = static_cast<const uint16_t *>(p.y);
         if (p.Fs > 0)
-            hipLaunchKernelGGL(combine_bf16_kernel<true>, grid, dim3(64), 0, s, y, p.rank, p.out,
+            hipLaunchKernelGGL(combine_bf16_kernel<true>, grid, dim3(64), 0, s, y, rows, p.out,
                                p.d, p.k);
         else
-            hipLaunchKernelGGL(combine_bf16_kernel<false>, grid, dim3(64), 0, s, y, p.rank, p.out,
+            hipLaunchKernelGGL(combine_bf16_kernel<false>, grid, dim3(64), 0, s, y, rows, p.out,
                                p.d, p.k);
     } else {
         const float *y = static_cast<const float *>(p.y);
         if (p.Fs > 0)
             hipLaunchKernelGGL(combine_f32_kernel<true>, dim3((unsigned)p.T), dim3(128), 0, s, y,
-                               p.rank, p.out, p.d, p.k);
+                               rows, p.out, p.d, p.k);
         else
             hipLaunchKernelGGL(combine_f32_kernel<false>, dim3((unsigned)p.T), dim3(128), 0, s, y,
-                               p.rank, p.out, p.d, p.k);
+                               rows, p.out, p.d, p.k);
     }
     return hipGetLastError();
 }

@@ -52,10 +52,16 @@ namespace moe {
 // any arithmetic, so a row costs one memory round trip.
 constexpr int kMaxChunks = 8;
 
+//
+// touch (null unless the select step lists the touched experts): block (0, 0)
+// clears its E + 1 counters for the select launch that follows.
 template <typename T, int TT, int RW>
 __global__ __launch_bounds__(256) void router_logits_kernel(
     const T *__restrict__ x, const T *__restrict__ w_router, const T *__restrict__ g,
-    const float *__restrict__ bias, float *__restrict__ logits, int64_t ntok, int d, int E) {
+    const float *__restrict__ bias, float *__restrict__ logits, int64_t ntok, int d, int E,
+    int32_t *__restrict__ touch) {
+    if (touch && blockIdx.x == 0 && blockIdx.y == 0)
+        for (int i = threadIdx.x; i <= E; i += 256) touch[i] = 0;
     extern __shared__ __align__(16) unsigned char smem_raw[];
     T *xs = reinterpret_cast<T *>(smem_raw);  // [TT][d]
     const int lane = threadIdx.x & 63;
@@ -185,18 +191,25 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 }
 
 // One wave per token: top-k by (logit desc, expert asc), weights, gate
-// (select_topk in router_select.h).
+// (select_topk in router_select.h).  With touch / tlist (cleared by the
+// logits launch): the first selection of expert e sets touch[e] and appends e
+// to tlist at slot touch[E]++ (device-scope atomics; the list order varies
+// from run to run, its contents do not).
 template <int NV>
 __global__ __launch_bounds__(256) void router_select_kernel(
     const float *__restrict__ logits, int64_t ntok, int E, int k, int has_gate,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, float *__restrict__ gate,
-    float *__restrict__ gate_user) {
+    float *__restrict__ gate_user, int32_t *__restrict__ touch, int32_t *__restrict__ tlist) {
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= ntok) return;
     select_topk<NV>(logits + t * (E + 1), E, k, lane, topk_idx + t * k, topk_w + t * k,
                     has_gate ? gate + t : nullptr, has_gate && gate_user ? gate_user + t : nullptr,
                     nullptr);
+    if (touch && lane < k) {
+        const int e = topk_idx[t * k + lane];  // written by this lane above
+        if (atomicOr(&touch[e], 1) == 0) tlist[atomicAdd(&touch[E], 1)] = e;
+    }
 }
 
 // Euclidean norm of each router row: one wave per row.
@@ -290,7 +303,7 @@ template <int NV, int NC>
 __global__ __launch_bounds__(256, NC <= 5 ? 4 : 1) void router_select_shortlist_kernel(
     const float *__restrict__ f, const float *__restrict__ wnorm, const uint16_t *__restrict__ x,
     const uint16_t *__restrict__ w_router, const uint16_t *__restrict__ g,
-    const float *__restrict__ bias, int64_t ntok, int d, int E, int k, float coef,
+    const float *__restrict__ bias, int64_t ntok, int d, int E, int k, int nsplit, float coef,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, float *__restrict__ gate,
     float *__restrict__ gate_user) {
     __shared__ int s_cand[4][32];
@@ -329,7 +342,10 @@ __global__ __launch_bounds__(256, NC <= 5 ? 4 : 1) void router_select_shortlist_
     for (int i = 0; i < NV; ++i) {
         const int e = lane + 64 * i;
         if (e < E) {
-            const float v = ft[e] + (bias ? bias[e] : 0.0f);
+            // f: the K slices' partial sums, added in slice order
+            float fe = ft[e];
+            for (int s = 1; s < nsplit; ++s) fe = fe + ft[(int64_t)s * ntok * (E + 1) + e];
+            const float v = fe + (bias ? bias[e] : 0.0f);
             fb[i] = (v == v) ? v : -INFINITY;
             dl[i] = coef * xnorm * wnorm[e] + 0x1p-22f * fabsf(fb[i]);
         } else {
@@ -608,7 +624,8 @@ static hipError_t launch_logits(const Problem &p, hipStream_t s) {
     do {                                                                                         \
         dim3 gr((unsigned)((p.T + TT - 1) / TT), (unsigned)((p.E + 1 + 4 * RW - 1) / (4 * RW))); \
         hipLaunchKernelGGL((router_logits_kernel<T, TT, RW>), gr, block, TT * row_bytes, s, x,   \
-                           wr, g, p.router_bias, p.logits, p.T, p.d, p.E);                       \
+                           wr, g, p.router_bias, p.logits, p.T, p.d, p.E,                        \
+                           p.direct ? p.counts : nullptr);                                       \
     } while (0)
     if (p.T <= 64) {
         // fewer tokens per block: more blocks in flight for a small batch
@@ -646,7 +663,8 @@ static hipError_t launch_shortlist(const Problem &p, float *sh_gate_user, hipStr
     const uint16_t *g = static_cast<const uint16_t *>(p.sh_gate);
 #define MOE_SL(NV, NC)                                                                          \
     hipLaunchKernelGGL((router_select_shortlist_kernel<NV, NC>), grid, block, 0, s, p.logits,   \
-                       p.wnorm, x, wr, g, p.router_bias, p.T, p.d, p.E, p.k, coef, p.topk_idx,  \
+                       p.wnorm, x, wr, g, p.router_bias, p.T, p.d, p.E, p.k, p.router_split,    \
+                       coef, p.topk_idx,                                                        \
                        p.topk_w, p.gate, sh_gate_user)
 #define MOE_SL_NV(NC)                                                                           \
     do {                                                                                        \
@@ -676,7 +694,8 @@ hipError_t launch_router(const Problem &p, float *sh_gate_user, hipStream_t s) {
     const int has_gate = p.sh_gate != nullptr;
 #define MOE_SELECT(NV)                                                                        \
     hipLaunchKernelGGL((router_select_kernel<NV>), grid, block, 0, s, p.logits, p.T, p.E, p.k, \
-                       has_gate, p.topk_idx, p.topk_w, p.gate, sh_gate_user)
+                       has_gate, p.topk_idx, p.topk_w, p.gate, sh_gate_user,                  \
+                       p.direct ? p.counts : nullptr, p.tile_group)
     if (nv <= 1) MOE_SELECT(1);
     else if (nv <= 2) MOE_SELECT(2);
     else if (nv <= 4) MOE_SELECT(4);

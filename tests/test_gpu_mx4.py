@@ -125,6 +125,21 @@ def test_mx4_experts_entry_with_given_routing():
     assert_out(out.cpu().numpy(), ref)
 
 
+def test_mx4_decode_without_permutation_matches_permuted_path():
+    """MXFP4 weight streaming at T = 24: the forward skips the permutation
+    step, the routing-given entry point keeps it; same routing, same bits
+    (no shared expert, whose gate each entry point computes in its own
+    order)."""
+    T, d, E, k, F = 24, 256, 32, 4, 128
+    inp = small_mx4(T, d, E, k, F, 0, seed=17)
+    announce("mxfp4 decode without permutation T=24")
+    out, idx, w = moe.forward_mx4(to_dev(inp["x"]), to_dev(inp["w_router"]), mx_dev(inp["gu"]),
+                                  mx_dev(inp["dn"]), k)
+    out2 = moe.experts_mx4(to_dev(inp["x"]), mx_dev(inp["gu"]), mx_dev(inp["dn"]), idx, w)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), out2.cpu().numpy())
+
+
 @pytest.mark.parametrize("T", [24, 300])
 def test_mx4_deterministic(T):
     """Both MXFP4 paths (weight streaming at T = 24, the GEMM at T = 300)

@@ -114,6 +114,42 @@ def test_experts_entry_with_given_routing():
     assert_out(out.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("T,bias_e", [(1, None), (32, None), (32, 5), (20, 5)])
+def test_decode_without_permutation_matches_permuted_path(T, bias_e):
+    """At T <= 32 the forward's weight-streaming path skips the permutation
+    step (block x serves expert x, h and y rows indexed by pair id); the
+    routing-given entry point keeps it.  Fed the forward's own routing, the
+    two give the same bits (no shared expert, whose gate each entry point
+    computes in its own order).  bias_e sends every token to one expert
+    first: at T = 32 its tile is full (32 rows)."""
+    d, E, k, F = 256, 64, 4, 128
+    inp = W.small_case(T, d, E, k, F, 0, "bf16", seed=70 + T)
+    if bias_e is not None:
+        inp["bias"] = np.zeros(E, np.float32)
+        inp["bias"][bias_e] = 100.0
+    announce(f"decode without permutation T={T} bias={bias_e}")
+    args = [to_dev(inp[n]) for n in ("x", "w_router", "w_gate_up", "w_down")]
+    out, idx, w = moe.forward(*args, k, bias=to_dev(inp.get("bias")))
+    out2 = moe.experts(args[0], args[2], args[3], idx, w)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), out2.cpu().numpy())
+    ref_out, ref_idx, _, _ = oracle_forward(inp, k)
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+    assert_out(out.cpu().numpy(), ref_out)
+
+
+@pytest.mark.parametrize("T,bias_e", [(1, None), (32, 5), (33, None)])
+def test_decode_shared_expert_near_permutation_boundary(T, bias_e):
+    """The shared expert's block on the path without the permutation (T <= 32)
+    and on the permuted path just past it (T = 33), against the oracle."""
+    d, E, k, F, Fs = 256, 64, 4, 128, 128
+    inp = W.small_case(T, d, E, k, F, Fs, "bf16", seed=90 + T)
+    if bias_e is not None:
+        inp["bias"] = np.zeros(E, np.float32)
+        inp["bias"][bias_e] = 100.0
+    check_case(inp, k, f"decode shared expert T={T} bias={bias_e}")
+
+
 def test_zero_router_ties_to_lower_index():
     T, d, E, k = 70, 128, 32, 6
     inp = W.small_case(T, d, E, k, 64, 64, "bf16", seed=1)
@@ -302,7 +338,12 @@ def test_shortlist_bound_is_far_from_tight():
     moe.route(to_dev(inp["x"]), to_dev(inp["w_router"]), k, ws=ws, router="shortlist")
     torch.cuda.synchronize()
     lay = moe.workspace_layout(shape, T)
-    f = ws.cpu().numpy()[lay.logits:lay.logits + 4 * T * (E + 1)].view(np.float32).reshape(T, E + 1)[:, :E]
+    S = 2 if d % 128 == 0 else 1  # K slices of the MFMA logits
+    parts = ws.cpu().numpy()[lay.logits:lay.logits + 4 * S * T * (E + 1)].view(np.float32)
+    parts = parts.reshape(S, T, E + 1)[:, :, :E]
+    f = parts[0]
+    for s in range(1, S):
+        f = f + parts[s]  # binary32, slice order, as the select step adds them
     l = oracle.router_logits(inp["x"], inp["w_router"]).astype(np.float64)
     xf = W.bf16_bits_to_f32(inp["x"]).astype(np.float64)
     wf = W.bf16_bits_to_f32(inp["w_router"]).astype(np.float64)
