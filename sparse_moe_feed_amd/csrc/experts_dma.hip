@@ -6,8 +6,9 @@
 // frontier-model-atlas, "Decoder microscope", Feed-forward panel).  A tile is
 // up to BM consecutive permuted rows of one group (group E = the shared
 // expert) against 256 output columns; gate/up tiles stack 128 gate rows on the
-// matching 128 up rows.  4 waves (2 x 2, one per SIMD) each own BM/2 x 128 of
-// the tile as (BM/64) x 4 v_mfma_f32_32x32x16_bf16 blocks.  BM = 256 serves
+// matching 128 up rows.  BM / 32 waves (BM / 64 x 2: 4 for 128-row tiles, 8
+// -- two per SIMD -- for 256-row tiles) each own 64 x 128 of the tile as 2 x 4
+// v_mfma_f32_32x32x16_bf16 blocks.  BM = 256 serves
 // many tokens per expert (each staged byte feeds 128 FLOP); BM = 128 serves
 // the middle ground, where streaming the expert weights sets the time.
 //
@@ -39,21 +40,26 @@ namespace {
 constexpr int BN = 256;
 constexpr int NB = 4;  // 32-column blocks per wave
 
-// Per tile height BM and K step BK (32 or 64): bytes per staged row, 16-byte
-// chunks per row, rows per 1 KB load, A and stage bytes (A then B), A and B
-// loads per wave per stage, k16 sub-steps per stage, 32-row sub-tiles per wave.
+// Per tile height BM and K step BK (32 or 64): waves per block (each owns
+// WR = 64 rows by 128 columns: BM / 32 waves, two per SIMD for 256-row
+// tiles), bytes per staged row, 16-byte chunks per row, rows per 1 KB load, A
+// and stage bytes (A then B), A and B loads per wave per stage, k16 sub-steps
+// per stage, 32-row sub-tiles per wave.
 template <int BM, int BK> struct Geo {
     static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
+    static constexpr int NW = BM / 32;
+    static constexpr int WR = 64;
     static constexpr int ROWB = BK * 2;
     static constexpr int CH = ROWB / 16;
     static constexpr int RPL = 64 / CH;
     static constexpr int OPA = BM * ROWB;
     static constexpr int STB = OPA + BN * ROWB;
-    static constexpr int AL = BM / RPL / 4;
-    static constexpr int BL = BN / RPL / 4;
+    static constexpr int AL = BM / RPL / NW;
+    static constexpr int BL = BN / RPL / NW;
     static constexpr int LOADS = AL + BL;
     static constexpr int Q = BK / 16;
-    static constexpr int MI = BM / 64;
+    static constexpr int MI = WR / 32;
+    static_assert(AL * RPL * NW == BM && BL * RPL * NW == BN, "loads cover the tile");
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -112,7 +118,7 @@ __device__ __forceinline__ void read_frags(const unsigned char *stage, int ks, i
 #pragma unroll
     for (int mi = 0; mi < MACT; ++mi)
         f.a[mi] = *reinterpret_cast<const bf16x8 *>(stage +
-                                                    tile_off<BK>(BM / 2 * wm + 32 * mi + fr, c));
+                                                    tile_off<BK>(Geo<BM, BK>::WR * wm + 32 * mi + fr, c));
 #pragma unroll
     for (int ni = 0; ni < NB; ++ni)
         f.b[ni] = *reinterpret_cast<const bf16x8 *>(stage + Geo<BM, BK>::OPA +
@@ -260,7 +266,7 @@ __device__ __forceinline__ void k_loop(const Stages<NS> &st, const uint16_t *aba
 // NS stage buffers; up to 80 KB of them leaves room for two blocks per CU, so
 // one block's start-up and epilogue overlap the other's streaming.
 template <int MODE, int BM, int BK, int NS>
-__global__ __launch_bounds__(256, (NS * Geo<BM, BK>::STB <= 80 * 1024 ? 2 : 1)) void gemm_dma_kernel(
+__global__ __launch_bounds__((64 * Geo<BM, BK>::NW), (NS * Geo<BM, BK>::STB <= 80 * 1024 ? 2 : 1)) void gemm_dma_kernel(
     GemmArgs a) {
     using G = Geo<BM, BK>;
     static_assert(NS >= 3 && NS <= 6, "three to six stage buffers");
@@ -346,7 +352,7 @@ __global__ __launch_bounds__(256, (NS * Geo<BM, BK>::STB <= 80 * 1024 ? 2 : 1)) 
     for (int ni = 0; ni < NB; ++ni)
         brow[ni] = MODE == 0 ? (ni >> 1) * (BN / 2) + 64 * wn + 32 * (ni & 1) : 128 * wn + 32 * ni;
     // active 32-row sub-tiles of this wave's BM/2 rows (wave-uniform)
-    const int mact = min(G::MI, max(0, (nrows - BM / 2 * wm + 31) / 32));
+    const int mact = min(G::MI, max(0, (nrows - G::WR * wm + 31) / 32));
 
     f32x16 acc[G::MI][NB];
 #pragma unroll
@@ -383,14 +389,14 @@ __global__ __launch_bounds__(256, (NS * Geo<BM, BK>::STB <= 80 * 1024 ? 2 : 1)) 
     }
 #undef MOE_LOOP
 
-    // Accumulator layout (B A^T): lane holds token row BM/2 wm + 32 mi + lane % 32
+    // Accumulator layout (B A^T): lane holds token row WR wm + 32 mi + lane % 32
     // and, in acc[mi][ni][4 g + q], output column brow[ni] + 8 g + 4 (lane / 32) + q.
     const int cq = 4 * (lane >> 5);
     if (MODE == 0) {
         uint16_t *H = shared ? a.h_sh : a.h;
 #pragma unroll
         for (int mi = 0; mi < G::MI; ++mi) {
-            const int row = BM / 2 * wm + 32 * mi + fr;
+            const int row = G::WR * wm + 32 * mi + fr;
             if (mi >= mact || row >= nrows) continue;
             uint16_t *hrow = H + (int64_t)(row0 + row) * Fg + n0 + 64 * wn + cq;
 #pragma unroll
@@ -425,7 +431,7 @@ __global__ __launch_bounds__(256, (NS * Geo<BM, BK>::STB <= 80 * 1024 ? 2 : 1)) 
     } else {
 #pragma unroll
         for (int mi = 0; mi < G::MI; ++mi) {
-            const int row = BM / 2 * wm + 32 * mi + fr;
+            const int row = G::WR * wm + 32 * mi + fr;
             if (mi >= mact || row >= nrows) continue;
             const float wgt = row_w[row];
             if (!shared) {
@@ -493,13 +499,13 @@ hipError_t launch_experts_dma(const Problem &p, int bm, hipStream_t s,
     a.nm = p.max_tiles;
     a.nn = (fmax + BN / 2 - 1) / (BN / 2);
     a.gm = -1;  // M-tile m on XCD m % 8: its N-tiles share A through one L2
-    if (bm == 256) hipLaunchKernelGGL((gemm_dma_kernel<0, 256, 32, 3>), grid(a), dim3(256), 0, s, a);
+    if (bm == 256) hipLaunchKernelGGL((gemm_dma_kernel<0, 256, 32, 3>), grid(a), dim3(512), 0, s, a);
     else hipLaunchKernelGGL((gemm_dma_kernel<0, 128, 64, 3>), grid(a), dim3(256), 0, s, a);
     mark(3);
     a.w = static_cast<const uint16_t *>(p.w_down);
     a.w_sh = static_cast<const uint16_t *>(p.w_sh_down);
     a.nn = (p.d + BN - 1) / BN;
-    if (bm == 256) hipLaunchKernelGGL((gemm_dma_kernel<1, 256, 32, 3>), grid(a), dim3(256), 0, s, a);
+    if (bm == 256) hipLaunchKernelGGL((gemm_dma_kernel<1, 256, 32, 3>), grid(a), dim3(512), 0, s, a);
     else hipLaunchKernelGGL((gemm_dma_kernel<1, 128, 32, 3>), grid(a), dim3(256), 0, s, a);
     mark(4);
     return hipGetLastError();
