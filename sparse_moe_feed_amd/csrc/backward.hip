@@ -514,29 +514,53 @@ template <bool F32> struct Stager<false, F32> {
 template <bool C_F32>
 __device__ __forceinline__ void store_tile(const Job &j, f32x16 (&acc)[2][2], int wm, int wn,
                                            int lane) {
+    // accumulator layout (B A^T, mfma_step): lane holds row 64 wm + 32 mi +
+    // lane % 32 and, in acc[mi][ni][4 g + q], column 64 wn + 32 ni + 8 g +
+    // 4 (lane / 32) + q: runs of four columns go out as one 16- (binary32) or
+    // 8-byte (bf16) store where the rows allow it
     const int fr = lane & 31;
+    const bool f32 = C_F32 || j.c_f32;
+    const int64_t vec_align = f32 ? 16 : 8;
+    const bool vec = j.ldc % vec_align == 0 &&
+                     reinterpret_cast<uintptr_t>(j.c) % vec_align == 0 &&
+                     (j.c_alt >= j.mrows || reinterpret_cast<uintptr_t>(j.c_alt_p) % vec_align == 0);
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < 2; ++mi) {
+        const int row = 64 * wm + 32 * mi + fr;
+        if (row >= j.mrows) continue;
+        char *crow = row >= j.c_alt ? j.c_alt_p + (int64_t)(row - j.c_alt) * j.ldc
+                                    : j.c + (int64_t)row * j.ldc;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int row = 64 * wm + 32 * mi + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            if (row >= j.mrows) continue;
-            char *crow = row >= j.c_alt ? j.c_alt_p + (int64_t)(row - j.c_alt) * j.ldc
-                                        : j.c + (int64_t)row * j.ldc;
+        for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni) {
-                const int col = 64 * wn + 32 * ni + fr;
-                if (col >= j.ncols) continue;
-                if (C_F32 || j.c_f32)
-                    reinterpret_cast<float *>(crow)[col] = acc[mi][ni][v];
-                else
-                    reinterpret_cast<uint16_t *>(crow)[col] = f32_to_bf16_rne(acc[mi][ni][v]);
+            for (int g = 0; g < 4; ++g) {
+                const int col = 64 * wn + 32 * ni + 8 * g + 4 * (lane >> 5);
+                const f32x16 &c4 = acc[mi][ni];
+                if (vec && col + 3 < j.ncols) {
+                    if (f32)
+                        *reinterpret_cast<float4 *>(crow + (int64_t)col * 4) =
+                            make_float4(c4[4 * g], c4[4 * g + 1], c4[4 * g + 2], c4[4 * g + 3]);
+                    else
+                        *reinterpret_cast<uint2 *>(crow + (int64_t)col * 2) =
+                            make_uint2(pack_bf16x2(c4[4 * g], c4[4 * g + 1]),
+                                       pack_bf16x2(c4[4 * g + 2], c4[4 * g + 3]));
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        if (col + q >= j.ncols) continue;
+                        if (f32)
+                            reinterpret_cast<float *>(crow)[col + q] = c4[4 * g + q];
+                        else
+                            reinterpret_cast<uint16_t *>(crow)[col + q] = f32_to_bf16_rne(c4[4 * g + q]);
+                    }
+                }
             }
-        }
+    }
 }
 
 // One QK step of the 128 x 128 tile from LDS: 4 waves in 2 x 2, each 64 x 64
-// from v_mfma_f32_32x32x16_bf16.
+// from v_mfma_f32_32x32x16_bf16, accumulated as B A^T (the layout store_tile
+// takes).
 template <bool A_KC, bool B_KC>
 __device__ __forceinline__ void mfma_step(const uint16_t *As, const uint16_t *Bs,
                                           f32x16 (&acc)[2][2], int wm, int wn, int lane) {
@@ -551,7 +575,7 @@ __device__ __forceinline__ void mfma_step(const uint16_t *As, const uint16_t *Bs
         for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
             for (int ni = 0; ni < 2; ++ni)
-                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni],
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi],
                                                                       acc[mi][ni], 0, 0, 0);
     }
 }
@@ -696,25 +720,32 @@ __global__ __launch_bounds__(256, 2) void bwd_dw_small_kernel(BwdArgs a, int nx,
             for (int mi = 0; mi < 2; ++mi) af[mi] = mc_frag(As, 16 * ks, 64 * wm + 32 * mi, lane);
 #pragma unroll
             for (int ni = 0; ni < 2; ++ni) bfr[ni] = mc_frag(Bs, 16 * ks, 64 * wn + 32 * ni, lane);
+            // B A^T: each lane ends with one output row and runs of four
+            // consecutive columns (8-byte LDS writes below)
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < 2; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni],
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi],
                                                                           acc[mi][ni], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();  // every wave is done reading Bs
-        // the tile as bf16 rows in Bs (accumulator layout: lane holds column
-        // lane % 32 and rows 8 (v / 4) + 4 (lane / 32) + (v % 4))
+        // the tile as bf16 rows in Bs (accumulator layout: lane holds row
+        // 64 wm + 32 mi + lane % 32 and, in acc[mi][ni][4 g + q], column
+        // 64 wn + 32 ni + 8 g + 4 (lane / 32) + q)
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
             for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int row = 64 * wm + 32 * mi + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                    Bs[row * SLD + 64 * wn + 32 * ni + fr] = f32_to_bf16_rne(acc[mi][ni][v]);
+                for (int g = 0; g < 4; ++g) {
+                    const int row = 64 * wm + 32 * mi + fr;
+                    const int col = 64 * wn + 32 * ni + 8 * g + 4 * (lane >> 5);
+                    const f32x16 &c4 = acc[mi][ni];
+                    *reinterpret_cast<uint2 *>(&Bs[row * SLD + col]) =
+                        make_uint2(pack_bf16x2(c4[4 * g], c4[4 * g + 1]),
+                                   pack_bf16x2(c4[4 * g + 2], c4[4 * g + 3]));
                 }
         __syncthreads();
         char *c = j.c + (int64_t)n0 * 2;

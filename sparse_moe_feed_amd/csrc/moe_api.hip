@@ -151,7 +151,7 @@ BwdPlan make_bwd_plan(const moe_desc &d, int64_t T) {
     const size_t F = (size_t)d.d_expert, Fs = (size_t)d.d_shared, dm = (size_t)d.d_model;
     p.nblk = (int)((T + moe::kCountBlock - 1) / moe::kCountBlock);
     p.max_tiles = (int)moe::max_gemm_tiles(T, d.top_k, d.n_experts, moe::kGemmBM, d.d_shared > 0);
-    p.ldl = d.n_experts + 1;
+    p.ldl = (d.n_experts + 1 + 3) / 4 * 4;  // 16-byte rows: the GEMM epilogue's vector stores
     p.ldd = (d.n_experts + 1 + 127) / 128 * 128;
     size_t off = 0;
     auto take = [&](size_t bytes) {

@@ -150,7 +150,7 @@ struct BwdArgs {
     void *dw_router, *dw_gu, *dw_dn, *dw_sgu, *dw_sdn, *dsh_gate;
     float *aux_loss;    // [1] or null
     // workspace
-    float *logits;      // [T, ldl]  x . [W_r; g] (no bias)
+    float *logits;      // [T, ldl]  x . [W_r; g] (no bias); ldl = E + 1 rounded up to 4
     int ldl;
     const int32_t *counts, *offsets, *tile_start, *tile_group, *perm, *rank;
     void *au, *au_sh;   // [T*k, 2F], [T, 2Fs]  gate | up pre-activations
