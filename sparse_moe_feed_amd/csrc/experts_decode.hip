@@ -172,22 +172,45 @@ constexpr int kScanChunks = DBM * 32 / 64;  // 64-pair chunks of topk_idx at T <
 // Direct tiles (T <= DBM, so an expert has at most DBM pairs when the top-k
 // experts of a token are distinct): the router listed the n touched experts
 // (counts[E] = n, tile_group[0..n) = the experts); block x < n serves expert
-// tile_group[x], block n the shared expert (if any), later blocks end.  Each
-// wave scans topk_idx and lists the expert's pairs in ascending pair id in
-// its own LDS slots (no block barrier).
+// tile_group[x], block n the shared expert (if any), later blocks end.
+// decode_tile finds the group (and, with the permutation, the rows); for a
+// direct routed tile the rows come from tile_rows, after the block has its
+// first weight loads in flight.
 template <class Args>
-__device__ __forceinline__ bool decode_tile_direct(const Args &a, TileInfo &ti, int *rows) {
-    const int nt = a.counts[a.E];
-    const int x = blockIdx.x;
-    if (x > nt || (x == nt && a.Fs == 0)) return false;
-    ti.shared = x == nt;
-    ti.g = ti.shared ? a.E : a.tile_group[x];
-    ti.row0 = 0;
+__device__ __forceinline__ bool decode_tile(const Args &a, TileInfo &ti) {
     ti.rows = nullptr;
-    if (ti.shared) {
-        ti.nrows = (int)a.T;
+    ti.row0 = 0;
+    if (a.direct) {
+        const int nt = a.counts[a.E];
+        const int x = blockIdx.x;
+        if (x > nt || (x == nt && a.Fs == 0)) return false;
+        ti.shared = x == nt;
+        ti.g = ti.shared ? a.E : a.tile_group[x];
+        ti.nrows = ti.shared ? (int)a.T : 0;  // routed: tile_rows
         return true;
     }
+    const int tile = blockIdx.x;
+    if (tile >= a.tile_start[a.E + 1]) return false;
+    ti.g = a.tile_group[tile];
+    ti.shared = ti.g == a.E;
+    const int m_local = (tile - a.tile_start[ti.g]) * DBM;
+    if (!ti.shared) {
+        ti.row0 = a.offsets[ti.g] + m_local;
+        ti.nrows = min(DBM, a.counts[ti.g] - m_local);
+    } else {
+        ti.row0 = m_local;
+        ti.nrows = (int)min<int64_t>(DBM, a.T - m_local);
+    }
+    return true;
+}
+
+// Rows of a direct routed tile: each wave scans topk_idx and lists the
+// expert's pairs in ascending pair id in its own LDS slots (no block
+// barrier).  Other tiles already have their rows.  False (no rows) cannot
+// happen for a listed expert; the caller then drains its loads and ends.
+template <class Args>
+__device__ __forceinline__ bool tile_rows(const Args &a, TileInfo &ti, int *rows) {
+    if (!a.direct || ti.shared) return true;
     const int lane = threadIdx.x & 63;
     const int np = (int)a.T * a.k;  // <= DBM * 32 = 64 kScanChunks
     const uint64_t below = (1ull << lane) - 1;
@@ -213,35 +236,19 @@ __device__ __forceinline__ bool decode_tile_direct(const Args &a, TileInfo &ti, 
     return true;
 }
 
-template <class Args>
-__device__ __forceinline__ bool decode_tile(const Args &a, TileInfo &ti, int *rows) {
-    if (a.direct) return decode_tile_direct(a, ti, rows);
-    ti.rows = nullptr;
-    const int tile = blockIdx.x;
-    if (tile >= a.tile_start[a.E + 1]) return false;
-    ti.g = a.tile_group[tile];
-    ti.shared = ti.g == a.E;
-    const int m_local = (tile - a.tile_start[ti.g]) * DBM;
-    if (!ti.shared) {
-        ti.row0 = a.offsets[ti.g] + m_local;
-        ti.nrows = min(DBM, a.counts[ti.g] - m_local);
-    } else {
-        ti.row0 = m_local;
-        ti.nrows = (int)min<int64_t>(DBM, a.T - m_local);
-    }
-    return true;
-}
+// A block whose tile has no rows ends here, after its loads in flight land.
+__device__ __forceinline__ void drain_and_end() { __builtin_amdgcn_s_waitcnt(0); }
 
 // gate/up: block = DW waves, wave w owns gate columns n0 + 16 w .. + 16 and
 // the matching up columns; grid.y walks 16 DW-column slabs of the expert width.
 // Each lane looks up the token of its own A rows; the first group's weight
 // loads are issued before those lookups are waited for.
 template <int HALVES>
-__device__ void decode_gateup_body(const DecodeArgs &a, const TileInfo &ti) {
+__device__ void decode_gateup_body(const DecodeArgs &a, const TileInfo &ti,
+                                   const uint16_t *const (&bp)[2], Frag (&b0)[2]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int Fg = ti.shared ? a.Fs : a.F;
     const int ncol = blockIdx.y * 16 * DW + wave * 16;  // first gate column of this wave
-    const uint16_t *W = ti.shared ? a.w_sh : a.w + (int64_t)ti.g * 2 * a.F * a.d;
     const int rl = lane & 15, kq = 8 * (lane >> 4);
     int tok[HALVES];
 #pragma unroll
@@ -249,10 +256,7 @@ __device__ void decode_gateup_body(const DecodeArgs &a, const TileInfo &ti) {
         const int r = min(16 * h + rl, ti.nrows - 1);  // padding rows repeat the last row
         tok[h] = tile_src(a, ti, r);
     }
-    const uint16_t *bp[2] = {W + (int64_t)(ncol + rl) * a.d + kq,
-                             W + (int64_t)(Fg + ncol + rl) * a.d + kq};
-    Frag b0[2], a0[HALVES];
-    load_b<2>(b0, bp, 0);
+    Frag a0[HALVES];
     const uint16_t *ap[HALVES];
 #pragma unroll
     for (int h = 0; h < HALVES; ++h)
@@ -286,11 +290,24 @@ __device__ void decode_gateup_body(const DecodeArgs &a, const TileInfo &ti) {
 __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(DecodeArgs a) {
     __shared__ int rows[DW][DBM];
     TileInfo ti;
-    if (!decode_tile(a, ti, rows[threadIdx.x >> 6])) return;
+    if (!decode_tile(a, ti)) return;
     const int Fg = ti.shared ? a.Fs : a.F;
     if (blockIdx.y * 16 * DW >= Fg) return;
-    if (ti.nrows > 16) decode_gateup_body<2>(a, ti);
-    else decode_gateup_body<1>(a, ti);
+    // the first weight group goes out before the rows are looked up
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int ncol = blockIdx.y * 16 * DW + wave * 16;
+    const int rl = lane & 15, kq = 8 * (lane >> 4);
+    const uint16_t *W = ti.shared ? a.w_sh : a.w + (int64_t)ti.g * 2 * a.F * a.d;
+    const uint16_t *bp[2] = {W + (int64_t)(ncol + rl) * a.d + kq,
+                             W + (int64_t)(Fg + ncol + rl) * a.d + kq};
+    Frag b0[2];
+    load_b<2>(b0, bp, 0);
+    if (!tile_rows(a, ti, rows[wave])) {
+        drain_and_end();
+        return;
+    }
+    if (ti.nrows > 16) decode_gateup_body<2>(a, ti, bp, b0);
+    else decode_gateup_body<1>(a, ti, bp, b0);
 }
 
 // down: block = DW waves, wave w owns output columns n0 + 16 DNB w .. + 16 DNB
@@ -299,7 +316,8 @@ __global__ __launch_bounds__(64 * DW) void decode_gateup_kernel(DecodeArgs a) {
 // lookups that the epilogue needs (pair ids, then weights) are issued first
 // and resolved after the stream.
 template <int HALVES>
-__device__ void decode_down_body(const DecodeArgs &a, const TileInfo &ti) {
+__device__ void decode_down_body(const DecodeArgs &a, const TileInfo &ti,
+                                 const uint16_t *const (&bp)[DNB], Frag (&b0)[DNB]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int Fg = ti.shared ? a.Fs : a.F;
     const int ncol = blockIdx.y * 16 * DNB * DW + wave * 16 * DNB;
@@ -314,10 +332,6 @@ __device__ void decode_down_body(const DecodeArgs &a, const TileInfo &ti) {
             const int r = min(16 * h + 4 * (lane >> 4) + i, ti.nrows - 1);
             src[h][i] = tile_src(a, ti, r);
         }
-    const uint16_t *W = ti.shared ? a.w_sh : a.w + (int64_t)ti.g * a.d * a.F;
-    const uint16_t *bp[DNB];
-#pragma unroll
-    for (int n = 0; n < DNB; ++n) bp[n] = W + (int64_t)min(ncol + 16 * n + rl, a.d - 1) * Fg + kq;
     const uint16_t *H = ti.shared ? a.h_sh : a.h;
     const uint16_t *ap[HALVES];
 #pragma unroll
@@ -325,12 +339,14 @@ __device__ void decode_down_body(const DecodeArgs &a, const TileInfo &ti) {
         const int r = 16 * h + rl;
         ap[h] = H + (int64_t)tile_row(ti, min(r, ti.nrows - 1)) * Fg + kq;
     }
+    Frag a0[HALVES];
+    load_a<HALVES>(a0, ap, 0);
     f32x4 acc[HALVES][DNB];
 #pragma unroll
     for (int h = 0; h < HALVES; ++h)
 #pragma unroll
         for (int n = 0; n < DNB; ++n) acc[h][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    stream_k<DNB, HALVES>(bp, ap, Fg, acc);
+    stream_k_from<DNB, HALVES>(b0, a0, bp, ap, Fg, acc);
     float wr[HALVES][4];
 #pragma unroll
     for (int h = 0; h < HALVES; ++h)
@@ -355,10 +371,25 @@ __device__ void decode_down_body(const DecodeArgs &a, const TileInfo &ti) {
 __global__ __launch_bounds__(64 * DW) void decode_down_kernel(DecodeArgs a) {
     __shared__ int rows[DW][DBM];
     TileInfo ti;
-    if (!decode_tile(a, ti, rows[threadIdx.x >> 6])) return;
+    if (!decode_tile(a, ti)) return;
     if (blockIdx.y * 16 * DNB * DW >= a.d) return;
-    if (ti.nrows > 16) decode_down_body<2>(a, ti);
-    else decode_down_body<1>(a, ti);
+    // the first weight group goes out before the rows are looked up
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int Fg = ti.shared ? a.Fs : a.F;
+    const int ncol = blockIdx.y * 16 * DNB * DW + wave * 16 * DNB;
+    const int rl = lane & 15, kq = 8 * (lane >> 4);
+    const uint16_t *W = ti.shared ? a.w_sh : a.w + (int64_t)ti.g * a.d * a.F;
+    const uint16_t *bp[DNB];
+#pragma unroll
+    for (int n = 0; n < DNB; ++n) bp[n] = W + (int64_t)min(ncol + 16 * n + rl, a.d - 1) * Fg + kq;
+    Frag b0[DNB];
+    load_b<DNB>(b0, bp, 0);
+    if (!tile_rows(a, ti, rows[wave])) {
+        drain_and_end();
+        return;
+    }
+    if (ti.nrows > 16) decode_down_body<2>(a, ti, bp, b0);
+    else decode_down_body<1>(a, ti, bp, b0);
 }
 
 // ---------------------------------------------------------------------------
@@ -540,7 +571,7 @@ __device__ void mx4_gateup_body(const Mx4Args &a, const TileInfo &ti) {
 __global__ __launch_bounds__(64 * DW) void decode_gateup_mx4_kernel(Mx4Args a) {
     __shared__ int rows[DW][DBM];
     TileInfo ti;
-    if (!decode_tile(a, ti, rows[threadIdx.x >> 6])) return;
+    if (!decode_tile(a, ti) || !tile_rows(a, ti, rows[threadIdx.x >> 6])) return;
     const int Fg = ti.shared ? a.Fs : a.F;
     if (blockIdx.y * 32 * DW >= Fg) return;
     if (ti.nrows > 16) mx4_gateup_body<2>(a, ti);
@@ -615,7 +646,7 @@ __device__ void mx4_down_body(const Mx4Args &a, const TileInfo &ti) {
 __global__ __launch_bounds__(64 * DW) void decode_down_mx4_kernel(Mx4Args a) {
     __shared__ int rows[DW][DBM];
     TileInfo ti;
-    if (!decode_tile(a, ti, rows[threadIdx.x >> 6])) return;
+    if (!decode_tile(a, ti) || !tile_rows(a, ti, rows[threadIdx.x >> 6])) return;
     if (blockIdx.y * 64 * DW >= a.d) return;
     if (ti.nrows > 16) mx4_down_body<2>(a, ti);
     else mx4_down_body<1>(a, ti);
