@@ -235,6 +235,8 @@ hipError_t launch_permute(const Problem &p, int bm, hipStream_t s) {
 // bfloat16 layers keep the routed rows in bf16: block (t, c) handles token t
 // and columns 512 c .. 512 c + 511, eight per thread.  row_of null: the rows
 // are indexed by pair id (the permutation step was skipped), row t*k+j.
+constexpr int kCombineGroup = 4;
+
 template <bool SHARED>
 __global__ __launch_bounds__(64) void combine_bf16_kernel(const uint16_t *__restrict__ y,
                                                           const int32_t *__restrict__ row_of,
@@ -253,12 +255,25 @@ __global__ __launch_bounds__(64) void combine_bf16_kernel(const uint16_t *__rest
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.f;
     }
-    for (int j = 0; j < k; ++j) {
-        const int64_t r = row_of ? row_of[t * k + j] : t * k + j;
-        float v[8];
-        load8(y + r * d + c, v);
+    // rows in groups of kCombineGroup, every load of a group issued before
+    // the first add; the adds stay in slot order (the tail group re-reads
+    // slot k - 1 for its missing slots and skips them)
+    for (int j0 = 0; j0 < k; j0 += kCombineGroup) {
+        uint4 q[kCombineGroup];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += v[i];
+        for (int u = 0; u < kCombineGroup; ++u) {
+            const int j = min(j0 + u, k - 1);
+            const int64_t r = row_of ? row_of[t * k + j] : t * k + j;
+            q[u] = *reinterpret_cast<const uint4 *>(y + r * d + c);
+        }
+#pragma unroll
+        for (int u = 0; u < kCombineGroup; ++u) {
+            if (j0 + u >= k) break;
+            const uint32_t w4[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                acc[i] += (i & 1) ? bf16_hi(w4[i >> 1]) : bf16_lo(w4[i >> 1]);
+        }
     }
     reinterpret_cast<float4 *>(o)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
     reinterpret_cast<float4 *>(o)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
