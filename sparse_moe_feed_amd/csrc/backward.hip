@@ -953,21 +953,36 @@ __global__ __launch_bounds__(64) void dx_combine_bf16_kernel(BwdArgs a) {
     const int64_t t = blockIdx.x;
     const int c = (blockIdx.y * 64 + threadIdx.x) * 8;
     if (c >= a.d) return;
-    float acc[8], v[8];
+    float acc[8], v[8], vs[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    // the shared expert's and the router's terms are loaded first; the pair
+    // rows in groups of four, every load of a group before its adds; the adds
+    // keep the order rows (slot order), shared, router
+    if (a.Fs > 0) load8(static_cast<const uint16_t *>(a.dxs) + t * a.d + c, vs);
+    load8(a.dxr + t * a.d + c, v);
     const uint16_t *dxp = static_cast<const uint16_t *>(a.dxp);
-    for (int jj = 0; jj < a.k; ++jj) {
-        load8(dxp + (int64_t)a.rank[t * a.k + jj] * a.d + c, v);
+    constexpr int G = 4;
+    for (int j0 = 0; j0 < a.k; j0 += G) {
+        uint4 q[G];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += v[i];
+        for (int u = 0; u < G; ++u) {
+            const int jj = min(j0 + u, a.k - 1);  // the tail re-reads the last row, unused
+            q[u] = *reinterpret_cast<const uint4 *>(dxp + (int64_t)a.rank[t * a.k + jj] * a.d + c);
+        }
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+            if (j0 + u >= a.k) break;
+            const uint32_t w4[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                acc[i] += (i & 1) ? bf16_hi(w4[i >> 1]) : bf16_lo(w4[i >> 1]);
+        }
     }
     if (a.Fs > 0) {
-        load8(static_cast<const uint16_t *>(a.dxs) + t * a.d + c, v);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += v[i];
+        for (int i = 0; i < 8; ++i) acc[i] += vs[i];
     }
-    load8(a.dxr + t * a.d + c, v);
     float *o = a.dx + t * a.d + c;
     reinterpret_cast<float4 *>(o)[0] = make_float4(acc[0] + v[0], acc[1] + v[1], acc[2] + v[2],
                                                    acc[3] + v[3]);
