@@ -43,6 +43,24 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
     __shared__ int32_t row_tok[BM];
     __shared__ float row_w[BM];
 
+    if (MODE == 2 && a.wnorm && (int)blockIdx.y == a.ksplit) {
+#pragma clang fp contract(off)
+        // router row norms ||W_r[e]|| for the shortlist bound, one wave per
+        // row, beside the GEMM blocks (which do not fill the chip)
+        const int lane = threadIdx.x & 63;
+        for (int e = blockIdx.x * 4 + (threadIdx.x >> 6); e < a.E; e += gridDim.x * 4) {
+            float s2 = 0.f;
+            for (int kk = 8 * lane; kk < a.d; kk += 512) {
+                float v[8];
+                load8(a.w + (int64_t)e * a.d + kk, v);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) s2 += v[q] * v[q];
+            }
+            s2 = wave_sum(s2);
+            if (lane == 0) a.wnorm[e] = sqrtf(s2);
+        }
+        return;
+    }
     int mt, nt;
     if (!raster_tile(a.nm, a.nn, a.gm, mt, nt)) return;
     int g = 0, row0, nrows;
@@ -297,8 +315,9 @@ hipError_t launch_router_gemm(const Problem &p, hipStream_t s) {
     a.nn = (p.E + BN - 1) / BN;
     a.gm = 8;
     a.ksplit = p.router_split;
+    a.wnorm = p.wnorm;  // one more slice of blocks computes the row norms
     hipLaunchKernelGGL(grouped_gemm_kernel<2>,
-                       dim3((unsigned)(8 * ((a.nm * a.nn + 7) / 8)), (unsigned)a.ksplit),
+                       dim3((unsigned)(8 * ((a.nm * a.nn + 7) / 8)), (unsigned)a.ksplit + 1),
                        dim3(256), 0, s, a);
     return hipGetLastError();
 }

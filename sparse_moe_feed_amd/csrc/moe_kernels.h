@@ -81,6 +81,7 @@ struct GemmArgs {
     float *out;            // [T, d]   shared expert's term (plain stores)
     uint16_t *y;           // [T*k, d] routed rows, weighted, bf16 (plain stores)
     float *f;              // router logits [ksplit, T, ldf] (MODE 2): one partial per K slice
+    float *wnorm;          // MODE 2: router row norms [E], from the blocks of slice ksplit (or null)
     int ldf, ksplit;
     const int32_t *perm, *counts, *offsets, *tile_start, *tile_group;
     const float *topk_w, *gate;

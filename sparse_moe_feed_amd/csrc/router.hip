@@ -212,24 +212,6 @@ __global__ __launch_bounds__(256) void router_select_kernel(
     }
 }
 
-// Euclidean norm of each router row: one wave per row.
-__global__ __launch_bounds__(256) void router_row_norm_kernel(const uint16_t *__restrict__ w,
-                                                              float *__restrict__ wnorm, int E,
-                                                              int d) {
-    const int lane = threadIdx.x & 63;
-    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (e >= E) return;
-    float s2 = 0.f;
-    for (int kk = 8 * lane; kk < d; kk += 512) {
-        float v[8];
-        load8(w + (int64_t)e * d + kk, v);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) s2 += v[q] * v[q];
-    }
-    s2 = wave_sum(s2);
-    if (lane == 0) wnorm[e] = sqrtf(s2);
-}
-
 // Exact canonical logit for the token whose 512-chunk slices this wave holds
 // (lane j: elements 512 c + 8 j .. + 8 of chunk c), from the matching slices
 // wq of one router row; the same order as router_logits_kernel, so the bits
@@ -648,10 +630,8 @@ static hipError_t launch_logits(const Problem &p, hipStream_t s) {
 }
 
 static hipError_t launch_shortlist(const Problem &p, float *sh_gate_user, hipStream_t s) {
-    hipError_t err = launch_router_gemm(p, s);
+    hipError_t err = launch_router_gemm(p, s);  // logits and row norms
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(router_row_norm_kernel, dim3((p.E + 3) / 4), dim3(256), 0, s,
-                       static_cast<const uint16_t *>(p.w_router), p.wnorm, p.E, p.d);
     const int nchunk = (p.d + 511) / 512;
     const int nc = (p.d + 511) / 512;
     const double u = 1.0 / 8388608.0;  // 2^-23
