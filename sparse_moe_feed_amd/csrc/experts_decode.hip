@@ -8,12 +8,13 @@
 // every touched expert's 3 x F x d weights once; the arithmetic is a few
 // MFMAs per 16-byte load.
 //
-// Tiles hold up to 32 permuted rows of one group (two 16-row halves of
-// v_mfma_f32_16x16x32_bf16).  Each wave owns NB blocks of 16 output columns
+// Tiles hold up to 32 rows of one group (two 16-row halves of
+// v_mfma_f32_16x16x32_bf16): consecutive permuted rows, or, at T <= 32 with
+// the exact router, the expert's pairs found in topk_idx.  Each wave owns NB blocks of 16 output columns
 // and walks K with weights loaded straight from HBM into registers: 4 MFMA
 // K-steps (128 elements, 256 contiguous bytes per weight row) per group, two
 // groups in flight (ping-pong).  A fragments (token rows) come from L2.  No
-// LDS staging: every weight byte is used by exactly one wave.
+// LDS staging of weights: every weight byte is used by exactly one wave.
 #include "moe_device.h"
 #include "moe_kernels.h"
 
@@ -26,7 +27,7 @@ constexpr int KG = 128;         // K elements per pipeline group (4 MFMA steps)
 constexpr int DW = 1;           // waves per block (finer blocks, a shorter tail: 4 / 2 / 1 waves
                                 // gave gate/up 286 / 279 / 277 us at T = 32, d = 2560, top-10 of 512)
 constexpr int DNB = 2;          // 16-column blocks per wave in the down projection (1 / 2 / 4:
-                                // 150 / 147 / 163 us at T = 32, d = 2560, 512 experts top-10)
+                                // 152 / 145 / 153 us at T = 32, d = 2560, 512 experts top-10)
 
 struct DecodeArgs {
     const uint16_t *x;
