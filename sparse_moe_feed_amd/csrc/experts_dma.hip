@@ -6,9 +6,11 @@
 // frontier-model-atlas, "Decoder microscope", Feed-forward panel).  A tile is
 // up to BM consecutive permuted rows of one group (group E = the shared
 // expert) against 256 output columns; gate/up tiles stack 128 gate rows on the
-// matching 128 up rows.  BM / 32 waves (BM / 64 x 2: 4 for 128-row tiles, 8
-// -- two per SIMD -- for 256-row tiles) each own 64 x 128 of the tile as 2 x 4
-// v_mfma_f32_32x32x16_bf16 blocks.  BM = 256 serves
+// matching 128 up rows.  Waves in a (NW / 2) x 2 grid, each owning WR x 128 of
+// the tile as (WR / 32) x 4 v_mfma_f32_32x32x16_bf16 blocks: 8 waves (two per
+// SIMD) for 256-row tiles (WR = 64) and for the one-block-per-CU 128-row
+// gate/up tiles (WR = 32), 4 waves for the 128-row down tiles (two blocks per
+// CU).  BM = 256 serves
 // many tokens per expert (each staged byte feeds 128 FLOP); BM = 128 serves
 // the middle ground, where streaming the expert weights sets the time.
 //
@@ -41,14 +43,14 @@ constexpr int BN = 256;
 constexpr int NB = 4;  // 32-column blocks per wave
 
 // Per tile height BM and K step BK (32 or 64): waves per block (each owns
-// WR = 64 rows by 128 columns: BM / 32 waves, two per SIMD for 256-row
-// tiles), bytes per staged row, 16-byte chunks per row, rows per 1 KB load, A
+// WR rows by 128 columns; 8 waves where one block fills a CU, measured faster
+// than 4 there), bytes per staged row, 16-byte chunks per row, rows per 1 KB load, A
 // and stage bytes (A then B), A and B loads per wave per stage, k16 sub-steps
 // per stage, 32-row sub-tiles per wave.
 template <int BM, int BK> struct Geo {
     static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
-    static constexpr int NW = BM / 32;
-    static constexpr int WR = 64;
+    static constexpr int NW = BK == 64 ? 8 : BM / 32;
+    static constexpr int WR = BM / (NW / 2);
     static constexpr int ROWB = BK * 2;
     static constexpr int CH = ROWB / 16;
     static constexpr int RPL = 64 / CH;
@@ -500,7 +502,7 @@ hipError_t launch_experts_dma(const Problem &p, int bm, hipStream_t s,
     a.nn = (fmax + BN / 2 - 1) / (BN / 2);
     a.gm = -1;  // M-tile m on XCD m % 8: its N-tiles share A through one L2
     if (bm == 256) hipLaunchKernelGGL((gemm_dma_kernel<0, 256, 32, 3>), grid(a), dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((gemm_dma_kernel<0, 128, 64, 3>), grid(a), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((gemm_dma_kernel<0, 128, 64, 3>), grid(a), dim3(64 * Geo<128, 64>::NW), 0, s, a);
     mark(3);
     a.w = static_cast<const uint16_t *>(p.w_down);
     a.w_sh = static_cast<const uint16_t *>(p.w_sh_down);
