@@ -516,10 +516,49 @@ __device__ __forceinline__ void mx4_stream(Mx4Group &b0, Frag (&a0)[HALVES],
     }
 }
 
+// This lane's first packed tile of each weight-row block of the wave (gate/up:
+// K = d, d / 128 tiles per 16-row block; the two gate blocks then the
+// matching up blocks), codes and scales.
+__device__ __forceinline__ void mx4_gateup_ptrs(const Mx4Args &a, const TileInfo &ti,
+                                                const uint8_t *(&cp)[NB4], const uint8_t *(&sp)[NB4]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int Fg = ti.shared ? a.Fs : a.F;
+    const int c0 = blockIdx.y * 32 * DW + wave * 32;
+    const int64_t row_base = ti.shared ? 0 : (int64_t)ti.g * 2 * a.F;
+    const uint8_t *P = ti.shared ? a.wp_sh : a.wp;
+#pragma unroll
+    for (int n = 0; n < NB4; ++n) {
+        const int64_t rb = (row_base + (n < 2 ? c0 + 16 * n : Fg + c0 + 16 * (n - 2))) / 16;
+        const uint8_t *tile = P + rb * (a.d / 128) * TILE4;
+        cp[n] = tile + 16 * lane;
+        sp[n] = tile + 1024 + lane;
+    }
+}
+
+// The same for the down projection (K = Fg: Fg / 128 tiles per block;
+// d % 128 == 0, so every block of the slab lies inside d).
+__device__ __forceinline__ void mx4_down_ptrs(const Mx4Args &a, const TileInfo &ti,
+                                              const uint8_t *(&cp)[NB4], const uint8_t *(&sp)[NB4]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int Fg = ti.shared ? a.Fs : a.F;
+    const int c0 = blockIdx.y * 64 * DW + wave * 64;
+    const int64_t row_base = ti.shared ? 0 : (int64_t)ti.g * a.d;
+    const uint8_t *P = ti.shared ? a.wp_sh : a.wp;
+#pragma unroll
+    for (int n = 0; n < NB4; ++n) {
+        const int64_t rb = (row_base + c0 + 16 * n) / 16;
+        const uint8_t *tile = P + rb * (Fg / 128) * TILE4;
+        cp[n] = tile + 16 * lane;
+        sp[n] = tile + 1024 + lane;
+    }
+}
+
 // gate/up: wave w owns gate columns c0 .. c0 + 31 (two 16-row blocks) and the
 // matching up columns; grid.y walks 32 DW-column slabs of the expert width.
 template <int HALVES>
-__device__ void mx4_gateup_body(const Mx4Args &a, const TileInfo &ti) {
+__device__ void mx4_gateup_body(const Mx4Args &a, const TileInfo &ti,
+                                const uint8_t *const (&cp)[NB4], const uint8_t *const (&sp)[NB4],
+                                Mx4Group &b0) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int Fg = ti.shared ? a.Fs : a.F;
     const int c0 = blockIdx.y * 32 * DW + wave * 32;
@@ -530,19 +569,6 @@ __device__ void mx4_gateup_body(const Mx4Args &a, const TileInfo &ti) {
         const int r = min(16 * h + rl, ti.nrows - 1);  // padding rows repeat the last row
         tok[h] = tile_src(a, ti, r);
     }
-    const int64_t row_base = ti.shared ? 0 : (int64_t)ti.g * 2 * a.F;
-    const uint8_t *P = ti.shared ? a.wp_sh : a.wp;
-    const uint8_t *cp[NB4], *sp[NB4];
-#pragma unroll
-    for (int n = 0; n < NB4; ++n) {
-        // first packed tile of this 16-row block (K = d: d / 128 tiles per block)
-        const int64_t rb = (row_base + (n < 2 ? c0 + 16 * n : Fg + c0 + 16 * (n - 2))) / 16;
-        const uint8_t *tile = P + rb * (a.d / 128) * TILE4;
-        cp[n] = tile + 16 * lane;
-        sp[n] = tile + 1024 + lane;
-    }
-    Mx4Group b0;
-    mx4_load_b(b0, cp, sp, 0);
     const uint16_t *ap[HALVES];
 #pragma unroll
     for (int h = 0; h < HALVES; ++h)
@@ -573,18 +599,29 @@ __device__ void mx4_gateup_body(const Mx4Args &a, const TileInfo &ti) {
 __global__ __launch_bounds__(64 * DW) void decode_gateup_mx4_kernel(Mx4Args a) {
     __shared__ int rows[DW][DBM];
     TileInfo ti;
-    if (!decode_tile(a, ti) || !tile_rows(a, ti, rows[threadIdx.x >> 6])) return;
+    if (!decode_tile(a, ti)) return;
     const int Fg = ti.shared ? a.Fs : a.F;
     if (blockIdx.y * 32 * DW >= Fg) return;
-    if (ti.nrows > 16) mx4_gateup_body<2>(a, ti);
-    else mx4_gateup_body<1>(a, ti);
+    // the first weight group goes out before the rows are looked up
+    const uint8_t *cp[NB4], *sp[NB4];
+    mx4_gateup_ptrs(a, ti, cp, sp);
+    Mx4Group b0;
+    mx4_load_b(b0, cp, sp, 0);
+    if (!tile_rows(a, ti, rows[threadIdx.x >> 6])) {
+        drain_and_end();
+        return;
+    }
+    if (ti.nrows > 16) mx4_gateup_body<2>(a, ti, cp, sp, b0);
+    else mx4_gateup_body<1>(a, ti, cp, sp, b0);
 }
 
 // down: wave w owns output columns c0 .. c0 + 63 (four 16-row blocks of
 // W_dn); grid.y walks 64 DW-column slabs of d.  The epilogue's lookups (pair
 // ids, then weights) are issued before the stream, as in decode_down_body.
 template <int HALVES>
-__device__ void mx4_down_body(const Mx4Args &a, const TileInfo &ti) {
+__device__ void mx4_down_body(const Mx4Args &a, const TileInfo &ti,
+                                const uint8_t *const (&cp)[NB4], const uint8_t *const (&sp)[NB4],
+                                Mx4Group &b0) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int Fg = ti.shared ? a.Fs : a.F;
     const int c0 = blockIdx.y * 64 * DW + wave * 64;
@@ -597,20 +634,6 @@ __device__ void mx4_down_body(const Mx4Args &a, const TileInfo &ti) {
             const int r = min(16 * h + 4 * q + i, ti.nrows - 1);
             src[h][i] = tile_src(a, ti, r);
         }
-    const int64_t row_base = ti.shared ? 0 : (int64_t)ti.g * a.d;
-    const uint8_t *P = ti.shared ? a.wp_sh : a.wp;
-    const uint8_t *cp[NB4], *sp[NB4];
-#pragma unroll
-    for (int n = 0; n < NB4; ++n) {
-        // first packed tile of this 16-row block (K = Fg: Fg / 128 tiles per
-        // block); d % 128 == 0, so every block of the slab lies inside d
-        const int64_t rb = (row_base + c0 + 16 * n) / 16;
-        const uint8_t *tile = P + rb * (Fg / 128) * TILE4;
-        cp[n] = tile + 16 * lane;
-        sp[n] = tile + 1024 + lane;
-    }
-    Mx4Group b0;
-    mx4_load_b(b0, cp, sp, 0);
     const uint16_t *H = ti.shared ? a.h_sh : a.h;
     const uint16_t *ap[HALVES];
 #pragma unroll
@@ -648,10 +671,19 @@ __device__ void mx4_down_body(const Mx4Args &a, const TileInfo &ti) {
 __global__ __launch_bounds__(64 * DW) void decode_down_mx4_kernel(Mx4Args a) {
     __shared__ int rows[DW][DBM];
     TileInfo ti;
-    if (!decode_tile(a, ti) || !tile_rows(a, ti, rows[threadIdx.x >> 6])) return;
+    if (!decode_tile(a, ti)) return;
     if (blockIdx.y * 64 * DW >= a.d) return;
-    if (ti.nrows > 16) mx4_down_body<2>(a, ti);
-    else mx4_down_body<1>(a, ti);
+    // the first weight group goes out before the rows are looked up
+    const uint8_t *cp[NB4], *sp[NB4];
+    mx4_down_ptrs(a, ti, cp, sp);
+    Mx4Group b0;
+    mx4_load_b(b0, cp, sp, 0);
+    if (!tile_rows(a, ti, rows[threadIdx.x >> 6])) {
+        drain_and_end();
+        return;
+    }
+    if (ti.nrows > 16) mx4_down_body<2>(a, ti, cp, sp, b0);
+    else mx4_down_body<1>(a, ti, cp, sp, b0);
 }
 
 // Row-major MX (codes [R, K/2], scales [R, K/32]) -> packed tiles.  Block of
