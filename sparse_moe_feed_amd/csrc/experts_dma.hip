@@ -9,8 +9,7 @@
 // matching 128 up rows.  Waves in a (NW / 2) x 2 grid, each owning WR x 128 of
 // the tile as (WR / 32) x 4 v_mfma_f32_32x32x16_bf16 blocks: 8 waves (two per
 // SIMD) for 256-row tiles (WR = 64) and for the one-block-per-CU 128-row
-// gate/up tiles (WR = 32), 4 waves for the 128-row down tiles (two blocks per
-// CU).  BM = 256 serves
+// tiles (WR = 32).  BM = 256 serves
 // many tokens per expert (each staged byte feeds 128 FLOP); BM = 128 serves
 // the middle ground, where streaming the expert weights sets the time.
 //
@@ -20,9 +19,8 @@
 // ahead through three stage buffers of BK = 32 or 64 (a buffer is refilled as
 // soon as every wave has read it).  BK = 64 reads 128 contiguous bytes of
 // each weight row per step, which HBM streams about 10% faster than 64-byte
-// pieces; its 48 KB stages leave room for one block per CU, so it serves the
-// long-K gate/up tiles of 128 rows, and BK = 32 (two blocks per CU) the
-// short-K down tiles and the 256-row tiles.  One load fills one KB of LDS:
+// pieces; its 48 KB stages leave room for one block per CU (of 8 waves), so
+// it serves the 128-row tiles of both GEMMs, and BK = 32 the 256-row tiles.  One load fills one KB of LDS:
 // 16 rows of 64 bytes (BK = 32) or 8 rows of 128 bytes (BK = 64).  A 16-byte
 // read by 64 lanes is served 16 lanes (256 bytes) per clock, so the 16 rows
 // read together at one chunk must cover all 64 banks: chunk c of row R sits
@@ -508,7 +506,7 @@ hipError_t launch_experts_dma(const Problem &p, int bm, hipStream_t s,
     a.w_sh = static_cast<const uint16_t *>(p.w_sh_down);
     a.nn = (p.d + BN - 1) / BN;
     if (bm == 256) hipLaunchKernelGGL((gemm_dma_kernel<1, 256, 32, 3>), grid(a), dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((gemm_dma_kernel<1, 128, 32, 3>), grid(a), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((gemm_dma_kernel<1, 128, 64, 3>), grid(a), dim3(64 * Geo<128, 64>::NW), 0, s, a);
     mark(4);
     return hipGetLastError();
 }
