@@ -73,6 +73,30 @@ def test_workspace_grows_with_T_and_layout_is_consistent(L):
     assert lay.perm + 1000 * 4 * 4 <= lay.h
 
 
+def test_shortlist_router_holds_two_logit_slices(L):
+    """The shortlist router keeps the MFMA logits as two partial sums over the
+    halves of K when d % 128 == 0 (one slice otherwise): its logits region is
+    [S, T, E+1] binary32, the exact router's [T, E+1] (both followed by the
+    row norms); nothing else differs."""
+    T, E = 300, 16
+
+    def region(d, flags):
+        D = desc(d=d, E=E, flags=flags)
+        lay = moe.moe_workspace_layout()
+        assert L.moe_workspace_query(ctypes.byref(D), T, ctypes.byref(lay)) == moe.MOE_OK
+        return lay.gate - lay.logits, lay.total - lay.gate
+
+    def aligned(n):  # regions start on 256-byte boundaries
+        return (n + 255) // 256 * 256
+
+    one = T * (E + 1) * 4
+    for d, S in ((256, 2), (192, 1)):
+        ex_logits, ex_rest = region(d, moe.MOE_FLAG_ROUTER_EXACT)
+        sl_logits, sl_rest = region(d, moe.MOE_FLAG_ROUTER_SHORTLIST)
+        assert sl_logits - ex_logits == aligned(S * one) - aligned(one)
+        assert ex_rest == sl_rest
+
+
 FAKE = 0x10000  # never dereferenced: every case fails validation first
 
 
