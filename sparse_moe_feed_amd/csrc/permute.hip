@@ -235,7 +235,7 @@ hipError_t launch_permute(const Problem &p, int bm, hipStream_t s) {
 // bfloat16 layers keep the routed rows in bf16: block (t, c) handles token t
 // and columns 512 c .. 512 c + 511, eight per thread.  row_of null: the rows
 // are indexed by pair id (the permutation step was skipped), row t*k+j.
-constexpr int kCombineGroup = 4;
+constexpr int kCombineGroup = 8;
 
 template <bool SHARED>
 __global__ __launch_bounds__(64) void combine_bf16_kernel(const uint16_t *__restrict__ y,
