@@ -76,10 +76,14 @@ def algorithmic(cfg, U: int):
     flops_gu = 2 * T * k * 2 * F * d + 2 * T * 2 * Fs * d
     flops_dn = 2 * T * k * F * d + 2 * T * Fs * d
     call_flops = 2 * T * d * (E + 1) + flops_gu + flops_dn
+    # the down stage's weighted per-pair rows y (T*k*d, bf16) are traffic of
+    # this design (the combine reads them back), not of the method: they are
+    # left out of its algorithmic bytes and reported as down_impl_bytes
     return dict(call_bytes=call_bytes, call_flops=call_flops,
                 gate_up_bytes=gu_w + T * d * b + (T * k * F + T * Fs) * b,
                 gate_up_flops=flops_gu,
-                down_bytes=dn_w + (T * k * F + T * Fs) * b + T * k * d * b + T * d * 4,
+                down_bytes=dn_w + (T * k * F + T * Fs) * b + T * d * 4,
+                down_impl_bytes=T * k * d * b,
                 down_flops=flops_dn)
 
 
@@ -248,6 +252,38 @@ def roofline_of(cfg, r, workload):
     return roof, layer
 
 
+def measure_ceiling(nbytes=1 << 30, reps=20):
+    """Practical HBM ceilings on this GPU, GB/s: a streaming read of nbytes
+    by the whole chip (moe_read_probe), a device-to-device copy (bytes read +
+    bytes written) and a fill (bytes written), each averaged over reps
+    launches timed with events on the current stream."""
+    import torch
+
+    import sparse_moe_feed_amd as moe
+
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    sink = torch.empty(moe.READ_PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
+
+    def rate(fn, moved):
+        fn()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(reps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return round(moved * reps / (t0.elapsed_time(t1) * 1e-3) / 1e9, 1)
+
+    r = dict(read_GBs=rate(lambda: moe.read_probe(src, sink), nbytes),
+             copy_GBs=rate(lambda: dst.copy_(src), 2 * nbytes),
+             write_GBs=rate(lambda: dst.zero_(), nbytes), bytes=nbytes)
+    del src, dst
+    torch.cuda.empty_cache()
+    return r
+
+
 def cpu_baseline(cfg, layer_np, seconds):
     import oracle
     import workloads as W
@@ -340,7 +376,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, help="workload of `value` (2 = decode T=32)")
-    ap.add_argument("--also", default="3,9", help="extra workloads reported in the line")
+    ap.add_argument("--also", default="3,4,5,9", help="extra workloads reported in the line")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="only measure the practical HBM read / copy / write ceilings (GB/s)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -355,6 +393,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n * 4}))
+        return
+    if args.ceiling:
+        print(json.dumps({"ceiling": measure_ceiling()}))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -389,6 +430,7 @@ def main():
                                 stage_ms={k: round(v, 4) for k, v in rc["stage_ms"].items()})
     del dev_layer
     torch.cuda.empty_cache()
+    ceiling = measure_ceiling()
     base = None if args.no_cpu_baseline else cpu_baseline(cfg, layer_np, args.cpu_seconds)
     line = {
         "metric": "MoE-layer tokens/s at T=32 decode and T=4096 prefill; % HBM / MFMA peak",
@@ -412,6 +454,7 @@ def main():
         "layer": layer,
         "stage_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},
         "also": also,
+        "ceiling": ceiling,
         "cpu_baseline": base,
     }
     print(json.dumps(line), flush=True)

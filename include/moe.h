@@ -339,6 +339,20 @@ moe_status moe_backward(const moe_desc *desc, int64_t T, const void *x,
                         void *dw_down, void *dw_sh_gate_up, void *dw_sh_down, void *dsh_gate,
                         float *aux_loss, void *ws, size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Measurement aid (not part of the layer): the practical HBM read ceiling.
+ * The expert-weight streams of the layer are HBM reads; this reads `bytes`
+ * bytes of device memory at `buf` once, with the whole chip, in coalesced
+ * 16-byte loads, so its rate is the read bandwidth those streams can reach.
+ * sink (device, MOE_READ_PROBE_SINK_WORDS uint32 words, 4-byte aligned) is
+ * overwritten with per-wave XOR folds: the XOR of all sink words equals the
+ * XOR of every 32-bit word of the buffer (a check that every byte was read).
+ * MOE_ERR_INVALID_ARG for NULL pointers, buf not 16-byte aligned or bytes not
+ * a multiple of 16; MOE_ERR_HIP if the launch fails.  Enqueued on `stream`.
+ * --------------------------------------------------------------------------- */
+#define MOE_READ_PROBE_SINK_WORDS 8192
+moe_status moe_read_probe(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *moe_status_string(moe_status status);
 

@@ -35,7 +35,7 @@ EXPORTED = ("moe_workspace_size", "moe_workspace_query", "moe_route", "moe_forwa
             "moe_experts_mx4", "moe_rmsnorm", "moe_forward_prenorm",
             "moe_saved_bytes", "moe_forward_train", "moe_backward_workspace_size",
             "moe_backward", "moe_status_string",
-            "moe_last_error", "moe_stage_events")
+            "moe_last_error", "moe_stage_events", "moe_read_probe")
 MOE_WEIGHTS_DTYPE, MOE_WEIGHTS_MX4 = 0, 1
 
 
@@ -102,6 +102,8 @@ def lib():
     L.moe_last_error.restype = ctypes.c_char_p
     L.moe_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
     L.moe_stage_events.restype = ctypes.c_int
+    L.moe_read_probe.argtypes = [vp, sz, vp, vp]
+    L.moe_read_probe.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -565,3 +567,22 @@ class MoELayer:
         return fwd(x, w["w_router"], w["w_gate_up"], w["w_down"], self.k, w["w_sh_gate_up"],
                    w["w_sh_down"], w["sh_gate"], w["bias"], out, topk_idx, topk_w, self.ws,
                    self.router)
+
+
+READ_PROBE_SINK_WORDS = 8192
+
+
+def read_probe(buf: torch.Tensor, sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One streaming read of ``buf`` (contiguous device tensor, a multiple of
+    16 bytes) by the whole chip (moe_read_probe): the practical HBM read
+    ceiling.  Returns the sink of per-wave XOR folds (int32 [8192]); the XOR of
+    its words is the XOR of the buffer's 32-bit words."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    if sink is None:
+        sink = torch.empty(READ_PROBE_SINK_WORDS, dtype=torch.int32, device=buf.device)
+    if sink.numel() < READ_PROBE_SINK_WORDS or sink.dtype != torch.int32 or not sink.is_cuda:
+        raise ValueError("sink must be a device int32 tensor of 8192 words")
+    _check(lib().moe_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                _stream()), "moe_read_probe")
+    return sink

@@ -380,7 +380,10 @@ __global__ __launch_bounds__(256, NC <= 5 ? 4 : 1) void router_select_shortlist_
 
     float my_l = 0.f;
     int my_e = 0;
-    if (count <= 32) {
+    // fewer than k candidates happens only when fewer than k approximate
+    // logits are finite (an infinite bias makes f + Delta NaN): the exact
+    // pass over every expert then decides, as it does for the oracle
+    if (count >= k && count <= 32) {
         // the shortlist in ascending expert order, candidate c at cand[c]
         int *cand = s_cand[threadIdx.x >> 6];
         {

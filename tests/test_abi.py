@@ -348,3 +348,15 @@ def test_forward_train_validation(L):
     assert call_forward_train(L, D, 8, saved_bytes=need, ptrs={"x": None}) == moe.MOE_ERR_INVALID_ARG
     assert call_forward_train(L, D, 8, saved_bytes=need, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
     assert call_forward_train(L, D, 0, saved=None, saved_bytes=0, ws=None, ws_bytes=0) == moe.MOE_OK
+
+
+def test_read_probe_rejects_bad_arguments(L):
+    """moe_read_probe checks its pointers and size before any launch (the
+    fake addresses below are never dereferenced)."""
+    buf, sink = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 21)
+    bad = moe.MOE_ERR_INVALID_ARG
+    assert L.moe_read_probe(None, 16, sink, None) == bad
+    assert L.moe_read_probe(buf, 16, None, None) == bad
+    assert L.moe_read_probe(ctypes.c_void_p((1 << 20) + 8), 16, sink, None) == bad
+    assert L.moe_read_probe(buf, 24, sink, None) == bad
+    assert L.moe_read_probe(buf, 16, ctypes.c_void_p((1 << 21) + 2), None) == bad

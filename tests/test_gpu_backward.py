@@ -185,11 +185,14 @@ def test_backward_full_shapes_small_batch():
     assert float(got["aux_loss"].cpu()[0]) == pytest.approx(ref["aux_loss"], rel=1e-4)
 
 
-def test_backward_prefill_sampled():
+@pytest.mark.slow
+def test_backward_prefill_full():
     """The timed training workload (backward_T4096: T = 4096 at the pages'
-    shapes): dx of sampled tokens and the routed gradients of sampled experts
-    against the oracle, the loss value, and the softmax invariance
-    sum_e dW_router[e] = 0 (within the bf16 rounding of the rows)."""
+    shapes) against the oracle: dx of every token, the router, shared-expert
+    and shared-gate gradients in full, the routed gradients of the four
+    busiest experts, three seeded ones and one no token chose, and the loss
+    value; plus the softmax invariance sum_e dW_router[e] = 0 (within the
+    bf16 rounding of the rows)."""
     cfg = W.CONFIGS[9]
     lay = W.layer_for(cfg)
     x = W.make_x(cfg.T, cfg.d, "bf16", cfg.seed_x)
@@ -199,15 +202,21 @@ def test_backward_prefill_sampled():
     dout = W.dout_for(cfg)
     announce(f"{cfg.name}: GPU")
     got = gpu_backward(inp, idx, w, dout, cfg.aux_coef)
-    toks = np.unique(np.concatenate([[0, cfg.T - 1],
-                                     np.random.default_rng(4).choice(cfg.T, 14, replace=False)]))
-    experts = [int(e) for e in np.random.default_rng(5).choice(cfg.E, 3, replace=False)]
-    announce(f"{cfg.name} backward: oracle on {len(toks)} tokens, experts {experts}")
-    ref = oracle_backward(inp, idx, w, dout, cfg.aux_coef, parts=oracle.DX | oracle.DW_ROUTED,
-                          tokens=toks, experts=experts)
-    check_grad("dx", got["dx"], ref["dx"], False, sel=toks)
+    counts = np.bincount(idx.ravel(), minlength=cfg.E)
+    experts = list(np.argsort(-counts, kind="stable")[:4])
+    experts += [e for e in np.random.default_rng(5).choice(cfg.E, 8, replace=False)
+                if e not in experts][:3]
+    experts += list(np.nonzero(counts == 0)[0][:1])
+    experts = [int(e) for e in experts]
+    announce(f"{cfg.name} backward: oracle on every token, experts {experts}")
+    ref = oracle_backward(inp, idx, w, dout, cfg.aux_coef, experts=experts)
+    worst = {"dx": check_grad("dx", got["dx"], ref["dx"], False)}
+    for n in ("dw_router", "dw_sh_gate_up", "dw_sh_down", "dsh_gate"):
+        worst[n] = check_grad(n, got[n], ref[n], True)
     for n in ("dw_gate_up", "dw_down"):
-        check_grad(n, got[n][np.array(experts)], ref[n], True)
+        worst[n] = check_grad(n, got[n][np.array(experts)], ref[n], True)
+    announce(f"{cfg.name} backward max|err|/RMS: "
+             + ", ".join(f"{n} {v:.3e}" for n, v in worst.items()))
     assert float(got["aux_loss"].cpu()[0]) == pytest.approx(ref["aux_loss"], rel=1e-4)
     dwr = as_f64(got["dw_router"])
     assert np.abs(dwr.sum(axis=0)).max() <= 2.0 ** -8 * np.abs(dwr).sum(axis=0).max()

@@ -180,25 +180,23 @@ def test_mx4_zero_tokens():
     assert out.shape == (0, 256) and idx.shape == (0, 2)
 
 
-def test_full_prefill_mx4_sampled():
-    """Pages' shapes with MXFP4 weights at T = 4096 (GEMM path): every
-    token's topk_idx bit-exact; out of 48 sampled tokens against the oracle."""
+@pytest.mark.slow
+def test_full_prefill_mx4():
+    """Pages' shapes with MXFP4 weights at T = 4096 (GEMM path), every token:
+    topk_idx bit-exact, topk_w within 1e-5 and every element of out against
+    the oracle."""
     cfg = W.CONFIGS[8]
     lay = W.layer_for(cfg)
     x = W.make_x(cfg.T, cfg.d, cfg.dtype, cfg.seed_x)
     announce(f"{cfg.name}: GPU forward")
     out, idx, w = gpu_forward_mx4(dict(lay, x=x, bias=None), cfg.k)
-    announce(f"{cfg.name}: oracle routing of all {cfg.T} tokens")
-    ref_idx, ref_w = oracle.route(x, lay["w_router"], cfg.k)
+    announce(f"{cfg.name}: oracle forward of all {cfg.T} tokens")
+    ref, ref_idx, ref_w, _ = oracle.forward_mx4(x, lay["w_router"], lay["gu"], lay["dn"], cfg.k,
+                                                lay["sgu"], lay["sdn"], lay["sh_gate"])
     assert np.array_equal(idx, ref_idx)
     assert np.abs(w - ref_w).max() <= W_TOL
-    toks = np.unique(np.concatenate([[0, cfg.T - 1],
-                                     np.random.default_rng(8).choice(cfg.T, 46, replace=False)]))
-    announce(f"{cfg.name}: oracle forward of {len(toks)} sampled tokens")
-    ref, _, _, _ = oracle.forward_mx4(np.ascontiguousarray(x[toks]), lay["w_router"], lay["gu"],
-                                      lay["dn"], cfg.k, lay["sgu"], lay["sdn"], lay["sh_gate"])
-    r = assert_out(out[toks], ref)
-    announce(f"{cfg.name}: max|err|/rms = {r:.3e}")
+    r = assert_out(out, ref)
+    announce(f"{cfg.name}: max|err|/rms = {r:.4e}")
 
 
 def test_full_config_mx4():

@@ -133,6 +133,24 @@ def test_bias_added_after_dot():
     assert (idx[:, 0] == 13).all()
 
 
+def test_minus_infinity_bias_masks_experts():
+    """A -inf bias masks an expert: the finite experts come first in logit
+    order, then the masked ones by ascending index (the full sort's order for
+    equal keys), with weight exactly 0; the finite weights are the softmax
+    over the finite selected logits."""
+    inp = W.small_case(30, 128, 16, 6, 8, 0, "bf16", seed=6)
+    b = np.full(16, -np.inf, np.float32)
+    keep = [2, 7, 11, 12]
+    b[keep] = 0.0
+    idx, w, logits = oracle.route(inp["x"], inp["w_router"], 6, bias=b, return_logits=True)
+    for t in range(30):
+        l = logits[t].astype(np.float64)
+        order = sorted(keep, key=lambda e: (-l[e], e))
+        assert list(idx[t]) == order + [0, 1]
+        assert (w[t, 4:] == 0.0).all()
+        assert np.allclose(w[t, :4], softmax(l[order]), rtol=1e-12, atol=1e-15)
+
+
 # ---------------------------------------------------------------- weights
 
 def test_weights_sum_to_one_and_equal_softmax_of_selected():
