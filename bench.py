@@ -76,14 +76,14 @@ def algorithmic(cfg, U: int):
     flops_gu = 2 * T * k * 2 * F * d + 2 * T * 2 * Fs * d
     flops_dn = 2 * T * k * F * d + 2 * T * Fs * d
     call_flops = 2 * T * d * (E + 1) + flops_gu + flops_dn
-    # the down stage's weighted per-pair rows y (T*k*d, bf16) are traffic of
-    # this design (the combine reads them back), not of the method: they are
-    # left out of its algorithmic bytes and reported as down_impl_bytes
+    # the down stage's weighted per-pair rows y (T*k*d, binary32) are traffic
+    # of this design (the combine reads them back), not of the method: they
+    # are left out of its algorithmic bytes and reported as down_impl_bytes
     return dict(call_bytes=call_bytes, call_flops=call_flops,
                 gate_up_bytes=gu_w + T * d * b + (T * k * F + T * Fs) * b,
                 gate_up_flops=flops_gu,
                 down_bytes=dn_w + (T * k * F + T * Fs) * b + T * d * 4,
-                down_impl_bytes=T * k * d * b,
+                down_impl_bytes=T * k * d * 4,
                 down_flops=flops_dn)
 
 

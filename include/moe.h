@@ -119,8 +119,8 @@ size_t moe_workspace_size(const moe_desc *desc, int64_t T);
  *   written, and the rows of h and y are the pair ids t*k+j.
  *   h        [T*k, F]         gated activations of the routed rows (bf16 / f32)
  *   h_shared [T, Fs]          gated activations of the shared expert
- *   y        [T*k, d]         w[t,j] * expert output of each routed row (bf16 /
- *                             f32, as h); the combine adds a token's k rows to
+ *   y        [T*k, d]         w[t,j] * expert output of each routed row
+ *                             (binary32); the combine adds a token's k rows to
  *                             the shared term in binary32
  *   xnorm    [T, d]           the normalised layer input of moe_forward_prenorm
  *                             (desc->dtype) */
@@ -263,14 +263,24 @@ enum { MOE_WEIGHTS_DTYPE = 0, MOE_WEIGHTS_MX4 = 1 };
  * (region xnorm) and the layer runs on it, with expert weights in
  * desc->dtype (weight_format MOE_WEIGHTS_DTYPE, as moe_forward) or packed
  * MXFP4 (MOE_WEIGHTS_MX4, as moe_forward_mx4, with its limits).  One call;
- * out, topk_idx and topk_w as for moe_forward. */
+ * out, topk_idx and topk_w as for moe_forward.
+ *
+ * resid (nullable, binary32 [T, d], 16-byte aligned, aliasing neither out
+ * nor h): the residual stream the layer's output joins.  The model feeds the
+ * output into its gated residual streams (frontier-model-atlas anatomy page,
+ * "Residual topology", Gated Residual); their gates are the caller's.  With
+ * resid given, the combine that finishes out also adds it to the stream in
+ * the same pass: resid[t,c] = resid[t,c] + out[t,c], one binary32 rounding
+ * (the gate-1 single-stream case; a caller with gates scales out itself).
+ * out is written as well. */
 moe_status moe_forward_prenorm(const moe_desc *desc, int64_t T, const void *h,
                                const void *norm_weight, float eps, int32_t weight_format,
                                const void *w_router, const float *router_bias,
                                const void *w_gate_up, const void *w_down,
                                const void *w_sh_gate_up, const void *w_sh_down,
                                const void *sh_gate, float *out, int32_t *topk_idx,
-                               float *topk_w, void *ws, size_t ws_bytes, void *stream);
+                               float *topk_w, float *resid, void *ws, size_t ws_bytes,
+                               void *stream);
 
 /* ---------------------------------------------------------------------------
  * Training forward: moe_forward plus the gate/up pre-activations that

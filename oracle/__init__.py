@@ -67,12 +67,15 @@ def build(force: bool = True) -> str:
 
 
 def _load():
+    """The oracle library: oracle/liboracle.so (built if missing), or the
+    build named by MOE_ORACLE_LIB (the sanitizer test's instrumented copy)."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
+    path = os.environ.get("MOE_ORACLE_LIB") or _LIB_PATH
+    if path == _LIB_PATH and not os.path.exists(_LIB_PATH):
         build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    lib = ctypes.CDLL(path)
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.oracle_router_logits.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp]
     lib.oracle_route.argtypes = [i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
@@ -84,12 +87,13 @@ def _load():
     lib.oracle_forward_mx4.argtypes = [i64, i32, i32, i32, i32, i32] + [vp] * 16
     lib.oracle_mx4_decode.argtypes = [i64, i64, vp, vp, vp]
     lib.oracle_rmsnorm.argtypes = [i64, i32, i32, vp, vp, ctypes.c_float, vp]
+    lib.oracle_residual.argtypes = [i64, i32, vp, vp, vp]
     lib.oracle_backward.argtypes = ([i64, i32, i32, i32, i32, i32, i32] + [vp] * 11
                                     + [ctypes.c_double, i32, vp, i64, vp] + [vp] * 8)
     for f in (lib.oracle_router_logits, lib.oracle_route, lib.oracle_experts,
               lib.oracle_forward, lib.oracle_threads, lib.oracle_experts_mx4,
               lib.oracle_forward_mx4, lib.oracle_mx4_decode, lib.oracle_rmsnorm,
-              lib.oracle_backward):
+              lib.oracle_backward, lib.oracle_residual):
         f.restype = ctypes.c_int
     lib.oracle_threads.argtypes = []
     _lib = lib
@@ -309,6 +313,20 @@ def rmsnorm(h, gamma, eps=1e-6):
     if rc:
         raise RuntimeError(f"oracle_rmsnorm failed ({rc})")
     return out
+
+
+def residual(resid, out):
+    """The residual stream after the layer (oracle_residual): resid [T, d]
+    float32 plus the layer's out [T, d] (float64), in float64."""
+    r = np.ascontiguousarray(resid, dtype=np.float32)
+    o = np.ascontiguousarray(out, dtype=np.float64)
+    if r.ndim != 2 or r.shape != o.shape:
+        raise ValueError("resid and out must both be [T, d]")
+    res = np.empty_like(o)
+    rc = _load().oracle_residual(r.shape[0], r.shape[1], _ptr(r), _ptr(o), _ptr(res))
+    if rc:
+        raise RuntimeError(f"oracle_residual failed ({rc})")
+    return res
 
 
 DX, DW_ROUTED, DW_SHARED, DW_ROUTER = 1, 2, 4, 8

@@ -196,6 +196,23 @@ int oracle_rmsnorm(int64_t T, int d, int dtype, const void *h, const void *gamma
     return 0;
 }
 
+/* Residual update after the layer.  The layer's output joins the residual
+ * stream, which the model carries as gated residual streams (anatomy page on
+ * frontier-model-atlas, "Residual topology", Gated Residual).  The stream
+ * gates are not defined on the pages and stay with the caller, so the update
+ * is the plain sum (the gate-1, single-stream case):
+ *   res[t, c] = resid[t, c] + out[t, c]      (binary64; resid is binary32)
+ * res may alias out. */
+int oracle_residual(int64_t T, int d, const float *resid, const double *out,
+                    double *res)
+{
+    if (T < 0 || d < 1 || !resid || !out || !res)
+        return 1;
+    for (int64_t i = 0; i < T * d; i++)
+        res[i] = (double)resid[i] + out[i];
+    return 0;
+}
+
 /* logits[t*E + e] for all tokens and experts. */
 int oracle_router_logits(int64_t T, int d, int E, int dtype, const void *x,
                          const void *w_router, const float *bias,

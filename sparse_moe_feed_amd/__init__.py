@@ -85,7 +85,7 @@ def lib():
     L.moe_mx4_pack.argtypes = [vp, vp, i64, i64, vp, vp]
     L.moe_rmsnorm.argtypes = [dp, i64, vp, vp, ctypes.c_float, vp, vp]
     L.moe_forward_prenorm.argtypes = [dp, i64, vp, vp, ctypes.c_float, ctypes.c_int32] + \
-        L.moe_forward.argtypes[3:]
+        L.moe_forward.argtypes[3:13] + [vp] + L.moe_forward.argtypes[13:]
     L.moe_backward_workspace_size.argtypes = [dp, i64]
     L.moe_backward_workspace_size.restype = sz
     L.moe_backward.argtypes = [dp, i64] + [vp] * 12 + [ctypes.c_float] + [vp] * 8 + [vp, sz, vp]
@@ -492,9 +492,11 @@ def rmsnorm(h, norm_weight, eps=1e-6, out=None):
 
 def forward_prenorm(h, norm_weight, w_router, w_gate_up, w_down, k, w_sh_gate_up=None,
                     w_sh_down=None, sh_gate=None, bias=None, eps=1e-6, out=None, topk_idx=None,
-                    topk_w=None, ws=None, router=None):
+                    topk_w=None, ws=None, router=None, resid=None):
     """The layer on RMSNorm(h), one call.  Expert weights are tensors in h's
-    dtype, or MX4Tensor (packed MXFP4).  Returns (out, topk_idx, topk_w)."""
+    dtype, or MX4Tensor (packed MXFP4).  resid (optional float32 [T, d]) is
+    updated in place to resid + out by the same call.  Returns (out,
+    topk_idx, topk_w)."""
     T, d = h.shape
     mx4 = isinstance(w_gate_up, MX4Tensor)
     if mx4:
@@ -517,12 +519,13 @@ def forward_prenorm(h, norm_weight, w_router, w_gate_up, w_down, k, w_sh_gate_up
     topk_idx = torch.empty((T, k), dtype=torch.int32, device=h.device) if topk_idx is None else topk_idx
     topk_w = torch.empty((T, k), dtype=torch.float32, device=h.device) if topk_w is None else topk_w
     _dev(out, "out", torch.float32, (T, d)), _dev(topk_idx, "topk_idx", torch.int32, (T, k))
-    _dev(topk_w, "topk_w", torch.float32, (T, k))
+    _dev(topk_w, "topk_w", torch.float32, (T, k)), _dev(resid, "resid", torch.float32, (T, d))
     ws = alloc_workspace(shape, T, h.device) if ws is None else ws
     st = lib().moe_forward_prenorm(ctypes.byref(shape.desc()), T, _ptr(h), _ptr(norm_weight),
                                    ctypes.c_float(eps), MOE_WEIGHTS_MX4 if mx4 else MOE_WEIGHTS_DTYPE,
                                    _ptr(w_router), _ptr(bias), *ptrs, _ptr(sh_gate), _ptr(out),
-                                   _ptr(topk_idx), _ptr(topk_w), _ptr(ws), ws.numel(), _stream())
+                                   _ptr(topk_idx), _ptr(topk_w), _ptr(resid), _ptr(ws), ws.numel(),
+                                   _stream())
     _check(st, "moe_forward_prenorm")
     return out, topk_idx, topk_w
 
@@ -555,14 +558,19 @@ class MoELayer:
         self.max_tokens = max_tokens
         self.ws = alloc_workspace(self.shape, max_tokens, w_router.device)
 
-    def __call__(self, x, out=None, topk_idx=None, topk_w=None):
+    def __call__(self, x, out=None, topk_idx=None, topk_w=None, resid=None):
+        """resid (pre-norm layers only): the binary32 residual stream, updated
+        in place to resid + out by the same call."""
         if x.shape[0] > self.max_tokens:
             raise ValueError("more tokens than the workspace was sized for")
         w = self.w
         if self.norm_weight is not None:
             return forward_prenorm(x, self.norm_weight, w["w_router"], w["w_gate_up"], w["w_down"],
                                    self.k, w["w_sh_gate_up"], w["w_sh_down"], w["sh_gate"],
-                                   w["bias"], self.eps, out, topk_idx, topk_w, self.ws, self.router)
+                                   w["bias"], self.eps, out, topk_idx, topk_w, self.ws, self.router,
+                                   resid)
+        if resid is not None:
+            raise ValueError("resid is taken by pre-norm layers (norm_weight given)")
         fwd = forward_mx4 if self.mx4 else forward
         return fwd(x, w["w_router"], w["w_gate_up"], w["w_down"], self.k, w["w_sh_gate_up"],
                    w["w_sh_down"], w["sh_gate"], w["bias"], out, topk_idx, topk_w, self.ws,

@@ -254,7 +254,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
                     if (row < nrows && col < a.d) {
                         const float val = row_w[row] * acc[mi][ni][v];
                         if (shared) a.out[(int64_t)row_tok[row] * a.d + col] = val;
-                        else a.y[(int64_t)(row0 + row) * a.d + col] = f32_to_bf16_rne(val);
+                        else a.y[(int64_t)(row0 + row) * a.d + col] = val;
                     }
                 }
     }
@@ -269,7 +269,7 @@ hipError_t launch_experts_bf16(const Problem &p, hipStream_t s,
     a.au = static_cast<uint16_t *>(p.au);
     a.au_sh = static_cast<uint16_t *>(p.au_sh);
     a.out = p.out;
-    a.y = static_cast<uint16_t *>(p.y);
+    a.y = p.y;
     a.perm = p.perm;
     a.counts = p.counts;
     a.offsets = p.offsets;

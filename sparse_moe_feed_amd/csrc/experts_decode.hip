@@ -37,7 +37,7 @@ struct DecodeArgs {
     uint16_t *h_sh;        // [T, Fs]
     uint16_t *au, *au_sh;  // pre-activations [a | u] (training forward), or null
     float *out;
-    uint16_t *y;           // [T*k, d] weighted routed rows (bf16)
+    float *y;              // [T*k, d] weighted routed rows (binary32)
     const int32_t *perm, *counts, *offsets, *tile_start, *tile_group;
     const int32_t *topk_idx;
     const float *topk_w, *gate;
@@ -366,7 +366,7 @@ __device__ void decode_down_body(const DecodeArgs &a, const TileInfo &ti,
                 if (row < ti.nrows && col < a.d) {
                     const float v = wr[h][i] * acc[h][n][i];
                     if (ti.shared) a.out[(int64_t)(ti.row0 + row) * a.d + col] = v;
-                    else a.y[(int64_t)tile_row(ti, row) * a.d + col] = f32_to_bf16_rne(v);
+                    else a.y[(int64_t)tile_row(ti, row) * a.d + col] = v;
                 }
             }
 }
@@ -429,7 +429,7 @@ struct Mx4Args {
     const uint16_t *x;
     uint16_t *h, *h_sh;
     float *out;
-    uint16_t *y;
+    float *y;
     const int32_t *perm, *counts, *offsets, *tile_start, *tile_group;
     const int32_t *topk_idx;
     const float *topk_w, *gate;
@@ -664,7 +664,7 @@ __device__ void mx4_down_body(const Mx4Args &a, const TileInfo &ti,
                 if (row < ti.nrows && col < a.d) {
                     const float v = wr[h][i] * acc[h][n][i];
                     if (ti.shared) a.out[(int64_t)(ti.row0 + row) * a.d + col] = v;
-                    else a.y[(int64_t)tile_row(ti, row) * a.d + col] = f32_to_bf16_rne(v);
+                    else a.y[(int64_t)tile_row(ti, row) * a.d + col] = v;
                 }
             }
 }
@@ -720,7 +720,7 @@ hipError_t launch_experts_decode_mx4(const Problem &p, hipStream_t s,
     a.h = static_cast<uint16_t *>(p.h);
     a.h_sh = static_cast<uint16_t *>(p.h_shared);
     a.out = p.out;
-    a.y = static_cast<uint16_t *>(p.y);
+    a.y = p.y;
     a.perm = p.perm;
     a.counts = p.counts;
     a.offsets = p.offsets;
@@ -761,7 +761,7 @@ hipError_t launch_experts_decode(const Problem &p, hipStream_t s,
     a.au = static_cast<uint16_t *>(p.au);
     a.au_sh = static_cast<uint16_t *>(p.au_sh);
     a.out = p.out;
-    a.y = static_cast<uint16_t *>(p.y);
+    a.y = p.y;
     a.perm = p.perm;
     a.counts = p.counts;
     a.offsets = p.offsets;

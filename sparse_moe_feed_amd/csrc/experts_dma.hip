@@ -435,8 +435,8 @@ __global__ __launch_bounds__((64 * Geo<BM, BK>::NW), (NS * Geo<BM, BK>::STB <= 8
             if (mi >= mact || row >= nrows) continue;
             const float wgt = row_w[row];
             if (!shared) {
-                // routed rows: weighted, bf16, into y
-                uint16_t *yrow = a.y + (int64_t)(row0 + row) * a.d + n0 + cq;
+                // routed rows: weighted, binary32, into y
+                float *yrow = a.y + (int64_t)(row0 + row) * a.d + n0 + cq;
 #pragma unroll
                 for (int ni = 0; ni < NB; ++ni)
 #pragma unroll
@@ -444,10 +444,9 @@ __global__ __launch_bounds__((64 * Geo<BM, BK>::NW), (NS * Geo<BM, BK>::STB <= 8
                         const int col = n0 + brow[ni] + 8 * g + cq;
                         if (col >= a.d) continue;
                         const f32x16 &c = acc[mi][ni];
-                        uint2 q;
-                        q.x = pack_bf16x2(wgt * c[4 * g], wgt * c[4 * g + 1]);
-                        q.y = pack_bf16x2(wgt * c[4 * g + 2], wgt * c[4 * g + 3]);
-                        *reinterpret_cast<uint2 *>(yrow + brow[ni] + 8 * g) = q;
+                        *reinterpret_cast<float4 *>(yrow + brow[ni] + 8 * g) =
+                            make_float4(wgt * c[4 * g], wgt * c[4 * g + 1], wgt * c[4 * g + 2],
+                                        wgt * c[4 * g + 3]);
                     }
             } else {
                 // shared expert: gated term, binary32, straight into out
@@ -478,7 +477,7 @@ hipError_t launch_experts_dma(const Problem &p, int bm, hipStream_t s,
     a.au = static_cast<uint16_t *>(p.au);
     a.au_sh = static_cast<uint16_t *>(p.au_sh);
     a.out = p.out;
-    a.y = static_cast<uint16_t *>(p.y);
+    a.y = p.y;
     a.perm = p.perm;
     a.counts = p.counts;
     a.offsets = p.offsets;

@@ -227,7 +227,7 @@ struct Mx4GemmArgs {
     const uint8_t *wp_sh;  // packed shared weights: gate/up [2Fs, d], down [d, Fs]
     uint16_t *h, *h_sh;
     float *out;
-    uint16_t *y;
+    float *y;
     const int32_t *perm, *counts, *offsets, *tile_start, *tile_group;
     const float *topk_w, *gate;
     int64_t T;
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(64 * XW, 1) void gemm_mx4_kernel(Mx4GemmArgs a) {
             if (mi >= mact || row >= nrows) continue;
             const float wgt = row_w[row];
             if (!shared) {
-                uint16_t *yrow = a.y + (int64_t)(row0 + row) * a.d + n0 + cq;
+                float *yrow = a.y + (int64_t)(row0 + row) * a.d + n0 + cq;
 #pragma unroll
                 for (int ni = 0; ni < XNB; ++ni)
 #pragma unroll
@@ -372,10 +372,9 @@ __global__ __launch_bounds__(64 * XW, 1) void gemm_mx4_kernel(Mx4GemmArgs a) {
                         const int col = n0 + brow[ni] + 8 * gg + cq;
                         if (col >= a.d) continue;
                         const f32x16 &c = acc[mi][ni];
-                        uint2 q;
-                        q.x = pack_bf16x2(wgt * c[4 * gg], wgt * c[4 * gg + 1]);
-                        q.y = pack_bf16x2(wgt * c[4 * gg + 2], wgt * c[4 * gg + 3]);
-                        *reinterpret_cast<uint2 *>(yrow + brow[ni] + 8 * gg) = q;
+                        *reinterpret_cast<float4 *>(yrow + brow[ni] + 8 * gg) =
+                            make_float4(wgt * c[4 * gg], wgt * c[4 * gg + 1], wgt * c[4 * gg + 2],
+                                        wgt * c[4 * gg + 3]);
                     }
             } else {
                 float *orow = a.out + (int64_t)row_tok[row] * a.d + n0 + cq;
@@ -403,7 +402,7 @@ hipError_t launch_experts_mx4_gemm(const Problem &p, hipStream_t s,
     a.h = static_cast<uint16_t *>(p.h);
     a.h_sh = static_cast<uint16_t *>(p.h_shared);
     a.out = p.out;
-    a.y = static_cast<uint16_t *>(p.y);
+    a.y = p.y;
     a.perm = p.perm;
     a.counts = p.counts;
     a.offsets = p.offsets;

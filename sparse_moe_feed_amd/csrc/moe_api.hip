@@ -15,6 +15,7 @@
 #include "moe_kernels.h"
 
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <string>
@@ -27,9 +28,50 @@ thread_local std::string g_last_error;
 thread_local hipEvent_t g_stage_events[8];
 thread_local int g_n_stage_events = 0;
 
+// MOE_DEBUG_SYNC (environment, read at every stage boundary; unset, empty or
+// "0" = off): the host waits for the stream after each stage, and the first
+// stage whose kernels failed is named in moe_last_error (the call then
+// returns MOE_ERR_HIP).  For finding a faulting kernel; not for streams under
+// graph capture, and slow.
+thread_local std::string g_debug_error;
+thread_local const char *const *g_stage_names = nullptr;
+
+const char *const kForwardStages[] = {
+    "start", "router (RMSNorm if any, router logits, top-k selection, gate)",
+    "permutation (histogram, scan, scatter, tile map)", "gate/up GEMM (h = silu(gate) * up)",
+    "down GEMM (weighted rows y, shared term into out)", "combine (out += rows y)"};
+const char *const kBackwardStages[] = {
+    "start", "permutation and router logits", "gate/up recompute and G = W_dn^T dout",
+    "SwiGLU and router backward", "dx of the routed rows", "dW_gate_up", "dW_down",
+    "router GEMMs, dx combine and load-balancing loss"};
+
+bool debug_sync_on() {
+    const char *v = getenv("MOE_DEBUG_SYNC");
+    return v && v[0] && strcmp(v, "0") != 0;
+}
+
+// Stage boundary i of the current call: its timing event, and under
+// MOE_DEBUG_SYNC a wait that attributes any failure to stage i (the kernels
+// enqueued since boundary i - 1).
 void mark_stage(int i, hipStream_t s) {
     if (i < g_n_stage_events && g_stage_events[i]) (void)hipEventRecord(g_stage_events[i], s);
+    if (i == 0) {
+        g_debug_error.clear();
+        return;
+    }
+    if (!g_debug_error.empty() || !debug_sync_on()) return;
+    hipError_t err = hipStreamSynchronize(s);
+    if (err == hipSuccess) err = hipPeekAtLastError();
+    if (err != hipSuccess) {
+        g_debug_error = std::string("MOE_DEBUG_SYNC: stage ") + std::to_string(i) + " failed";
+        if (g_stage_names) g_debug_error += std::string(" (") + g_stage_names[i] + ")";
+        g_debug_error += std::string(": ") + hipGetErrorString(err);
+    }
 }
+
+// End of a call: forgets the stage events; a failure seen by MOE_DEBUG_SYNC
+// outranks the launch status.
+moe_status end_call(hipError_t err);
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -100,7 +142,7 @@ Plan make_plan(const moe_desc &d, int64_t T) {
     p.perm = take((size_t)pairs * sizeof(int32_t));
     p.h = take((size_t)pairs * d.d_expert * esize);
     p.h_shared = take((size_t)T * d.d_shared * esize);
-    p.y = take((size_t)pairs * d.d_model * esize);
+    p.y = take((size_t)pairs * d.d_model * sizeof(float));
     p.xnorm = take((size_t)T * d.d_model * esize);
     p.total = off;
     return p;
@@ -131,7 +173,7 @@ moe::Problem make_problem(const moe_desc &d, int64_t T, const Plan &pl, void *ws
     p.perm = reinterpret_cast<int32_t *>(base + pl.perm);
     p.h = base + pl.h;
     p.h_shared = base + pl.h_shared;
-    p.y = base + pl.y;
+    p.y = reinterpret_cast<float *>(base + pl.y);
     p.nblk = pl.nblk;
     p.max_tiles = pl.max_tiles;
     return p;
@@ -196,15 +238,37 @@ moe_status hip_status(hipError_t err) {
     return MOE_ERR_HIP;
 }
 
+// A one-stage call (routing only, MXFP4 packing, RMSNorm alone): its launch
+// status and, under MOE_DEBUG_SYNC, the failure of its kernels by name.
+moe_status one_stage(hipError_t err, hipStream_t s, const char *name) {
+    static thread_local const char *names[2] = {"start", nullptr};
+    names[1] = name;
+    g_stage_names = names;
+    mark_stage(0, s);
+    if (err == hipSuccess) mark_stage(1, s);
+    return end_call(err);
+}
+
+moe_status end_call(hipError_t err) {
+    g_n_stage_events = 0;
+    if (!g_debug_error.empty()) {
+        g_last_error = g_debug_error;
+        g_debug_error.clear();
+        return MOE_ERR_HIP;
+    }
+    return hip_status(err);
+}
+
 bool all_aligned(std::initializer_list<const void *> ptrs) {
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return false;
     return true;
 }
 
-// Checks shared by the entry points.  Required pointers are listed in `req`.
-moe_status check_common(const moe_desc *desc, int64_t T, std::initializer_list<const void *> req,
-                        std::initializer_list<const void *> opt, void *ws, size_t ws_bytes) {
+// Checks shared by the entry points, workspace aside.  Required pointers are
+// listed in `req`.
+moe_status check_args(const moe_desc *desc, int64_t T, std::initializer_list<const void *> req,
+                      std::initializer_list<const void *> opt) {
     moe_status st = check_desc(desc);
     if (st != MOE_OK) return st;
     st = check_T(desc, T);
@@ -212,6 +276,13 @@ moe_status check_common(const moe_desc *desc, int64_t T, std::initializer_list<c
     for (const void *p : req)
         if (!p) return MOE_ERR_INVALID_ARG;
     if (!all_aligned(req) || !all_aligned(opt)) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+moe_status check_common(const moe_desc *desc, int64_t T, std::initializer_list<const void *> req,
+                        std::initializer_list<const void *> opt, void *ws, size_t ws_bytes) {
+    moe_status st = check_args(desc, T, req, opt);
+    if (st != MOE_OK || T == 0) return st;
     if (!ws || !aligned16(ws)) return MOE_ERR_WORKSPACE;
     if (ws_bytes < make_plan(*desc, T).total) return MOE_ERR_WORKSPACE;
     return MOE_OK;
@@ -264,8 +335,7 @@ moe_status run_experts(moe::Problem p, hipStream_t s) {
                        : moe::launch_experts_bf16(p, s, mark);
     if (err == hipSuccess) err = moe::launch_combine(p, s);
     mark_stage(5, s);
-    g_n_stage_events = 0;
-    return hip_status(err);
+    return end_call(err);
 }
 
 // MXFP4 expert weights: bf16 activations, 128-multiples (the packed tiles)
@@ -296,9 +366,11 @@ moe_status forward_impl(const moe_desc *desc, int64_t T, const void *x, const vo
                         const void *w_gate_up, const void *w_down, const void *w_sh_gate_up,
                         const void *w_sh_down, const void *sh_gate, float *out,
                         int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
-                        void *stream, void *saved = nullptr, size_t saved_bytes = 0) {
+                        void *stream, void *saved = nullptr, size_t saved_bytes = 0,
+                        float *resid = nullptr) {
     moe_status st = check_common(desc, T, {x, w_router, w_gate_up, w_down, out, topk_idx, topk_w},
-                                 {router_bias, w_sh_gate_up, w_sh_down, sh_gate}, ws, ws_bytes);
+                                 {router_bias, w_sh_gate_up, w_sh_down, sh_gate, resid}, ws,
+                                 ws_bytes);
     if (st != MOE_OK) return st;
     if (mx4) {
         st = check_mx4(desc, T);
@@ -323,9 +395,11 @@ moe_status forward_impl(const moe_desc *desc, int64_t T, const void *x, const vo
     p.w_sh_down = w_sh_down;
     p.sh_gate = desc->d_shared > 0 ? sh_gate : nullptr;
     p.out = out;
+    p.resid = resid;
     p.topk_idx = topk_idx;
     p.topk_w = topk_w;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    g_stage_names = kForwardStages;
     mark_stage(0, s);
     hipError_t err = hipSuccess;
     if (norm_weight)
@@ -333,12 +407,8 @@ moe_status forward_impl(const moe_desc *desc, int64_t T, const void *x, const vo
                                   p.bf16, s);
     p.direct = direct_decode(p);
     if (err == hipSuccess) err = moe::launch_router(p, nullptr, s);
-    st = hip_status(err);
     mark_stage(1, s);
-    if (st != MOE_OK) {
-        g_n_stage_events = 0;
-        return st;
-    }
+    if (err != hipSuccess) return end_call(err);
     return run_experts(p, s);
 }
 
@@ -386,7 +456,9 @@ moe_status moe_route(const moe_desc *desc, int64_t T, const void *x, const void 
     p.sh_gate = (sh_gate && sh_gate_out) ? sh_gate : nullptr;
     p.topk_idx = topk_idx;
     p.topk_w = topk_w;
-    return hip_status(moe::launch_router(p, sh_gate_out, static_cast<hipStream_t>(stream)));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return one_stage(moe::launch_router(p, sh_gate_out, s), s,
+                     "router (router logits, top-k selection, gate)");
 }
 
 moe_status moe_forward(const moe_desc *desc, int64_t T, const void *x, const void *w_router,
@@ -440,12 +512,13 @@ moe_status moe_experts(const moe_desc *desc, int64_t T, const void *x, const voi
     p.topk_idx = const_cast<int32_t *>(topk_idx);
     p.topk_w = const_cast<float *>(topk_w);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    g_stage_names = kForwardStages;
     mark_stage(0, s);
     if (p.Fs > 0) {
-        st = hip_status(moe::launch_shared_gate(p, s));
-        if (st != MOE_OK) {
-            g_n_stage_events = 0;
-            return st;
+        const hipError_t err = moe::launch_shared_gate(p, s);
+        if (err != hipSuccess) {
+            mark_stage(1, s);
+            return end_call(err);
         }
     }
     mark_stage(1, s);
@@ -462,8 +535,8 @@ moe_status moe_mx4_pack(const uint8_t *codes, const uint8_t *scales, int64_t row
     if (!codes || !scales || !packed || !aligned16(codes) || !aligned16(packed))
         return MOE_ERR_INVALID_ARG;
     if (moe_mx4_packed_bytes(rows, K) == 0) return MOE_ERR_INVALID_ARG;
-    return hip_status(
-        moe::launch_mx4_pack(codes, scales, rows, K, packed, static_cast<hipStream_t>(stream)));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return one_stage(moe::launch_mx4_pack(codes, scales, rows, K, packed, s), s, "MXFP4 packing");
 }
 
 moe_status moe_forward_mx4(const moe_desc *desc, int64_t T, const void *x, const void *w_router,
@@ -484,9 +557,10 @@ moe_status moe_rmsnorm(const moe_desc *desc, int64_t T, const void *h, const voi
     if (st != MOE_OK || T == 0) return st;
     if (!h || !norm_weight || !x_out || !all_aligned({h, norm_weight, x_out}) || !eps_ok(eps))
         return MOE_ERR_INVALID_ARG;
-    return hip_status(moe::launch_rmsnorm(h, norm_weight, eps, x_out, T, desc->d_model,
-                                          desc->dtype == MOE_BF16,
-                                          static_cast<hipStream_t>(stream)));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return one_stage(moe::launch_rmsnorm(h, norm_weight, eps, x_out, T, desc->d_model,
+                                         desc->dtype == MOE_BF16, s),
+                     s, "RMSNorm");
 }
 
 moe_status moe_forward_prenorm(const moe_desc *desc, int64_t T, const void *h,
@@ -494,10 +568,12 @@ moe_status moe_forward_prenorm(const moe_desc *desc, int64_t T, const void *h,
                                const void *w_router, const float *router_bias,
                                const void *w_gate_up, const void *w_down,
                                const void *w_sh_gate_up, const void *w_sh_down, const void *sh_gate,
-                               float *out, int32_t *topk_idx, float *topk_w, void *ws,
-                               size_t ws_bytes, void *stream) {
+                               float *out, int32_t *topk_idx, float *topk_w, float *resid,
+                               void *ws, size_t ws_bytes, void *stream) {
     if (weight_format != MOE_WEIGHTS_DTYPE && weight_format != MOE_WEIGHTS_MX4)
         return MOE_ERR_INVALID_ARG;
+    if (resid && (resid == out || static_cast<const void *>(resid) == h))
+        return check_desc(desc) != MOE_OK ? check_desc(desc) : MOE_ERR_INVALID_ARG;
     if (!norm_weight || !aligned16(norm_weight) || !eps_ok(eps)) {
         // a bad desc is reported first, as everywhere else
         moe_status st = check_desc(desc);
@@ -505,7 +581,7 @@ moe_status moe_forward_prenorm(const moe_desc *desc, int64_t T, const void *h,
     }
     return forward_impl(desc, T, h, norm_weight, eps, weight_format == MOE_WEIGHTS_MX4, w_router,
                         router_bias, w_gate_up, w_down, w_sh_gate_up, w_sh_down, sh_gate, out,
-                        topk_idx, topk_w, ws, ws_bytes, stream);
+                        topk_idx, topk_w, ws, ws_bytes, stream, nullptr, 0, resid);
 }
 
 moe_status moe_experts_mx4(const moe_desc *desc, int64_t T, const void *x, const void *w_gate_up,
@@ -531,12 +607,13 @@ moe_status moe_experts_mx4(const moe_desc *desc, int64_t T, const void *x, const
     p.topk_idx = const_cast<int32_t *>(topk_idx);
     p.topk_w = const_cast<float *>(topk_w);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    g_stage_names = kForwardStages;
     mark_stage(0, s);
     if (p.Fs > 0) {
-        st = hip_status(moe::launch_shared_gate(p, s));
-        if (st != MOE_OK) {
-            g_n_stage_events = 0;
-            return st;
+        const hipError_t err = moe::launch_shared_gate(p, s);
+        if (err != hipSuccess) {
+            mark_stage(1, s);
+            return end_call(err);
         }
     }
     mark_stage(1, s);
@@ -555,6 +632,13 @@ const char *moe_status_string(moe_status status) {
 }
 
 const char *moe_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"
+
+void moe::set_last_error(const char *msg) { g_last_error = msg ? msg : ""; }
+
+
+extern "C" {
 
 moe_status moe_stage_events(void *const *events, int n) {
     if (n < 0 || n > 8 || (n > 0 && !events)) return MOE_ERR_INVALID_ARG;
@@ -691,10 +775,10 @@ moe_status moe_backward(const moe_desc *desc, int64_t T, const void *x, const vo
     a.part = reinterpret_cast<float *>(base + pl.part);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    g_stage_names = kBackwardStages;
     mark_stage(0, s);
     const hipError_t err = moe::launch_backward(p, a, s, [&](int i) { mark_stage(i, s); });
-    g_n_stage_events = 0;
-    return hip_status(err);
+    return end_call(err);
 }
 
 }  // extern "C"

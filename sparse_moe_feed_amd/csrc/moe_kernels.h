@@ -7,6 +7,8 @@
 
 #include <functional>
 
+#include "moe.h"
+
 namespace moe {
 
 // Everything a launch needs to know about one call.  Pointers are device
@@ -36,7 +38,7 @@ struct Problem {
     int32_t *blk;       // [E, nblk]
     int32_t *rank;      // [T*k] rank inside the histogram block, then the pair's row
     int32_t *perm;      // [T*k]
-    void *y;            // [T*k, d] weighted down-projection of each routed row
+    float *y;           // [T*k, d] weighted down-projection of each routed row
                         // (bf16 for bfloat16 layers, binary32 otherwise)
     void *h;            // [T*k, F]
     void *h_shared;     // [T, Fs]
@@ -55,7 +57,13 @@ struct Problem {
     // MXFP4 expert weights: w_gate_up, w_down, w_sh_gate_up, w_sh_down are
     // then packed MXFP4 tensors (16 x 128 tiles of codes and scales)
     bool mx4;
+    // residual stream [T, d] binary32 or null: the combine's store also does
+    // resid[t] += out[t]
+    float *resid;
 };
+
+// Sets the text moe_last_error returns on this thread.
+void set_last_error(const char *msg);
 
 constexpr int kCountBlock = 256;     // tokens per histogram block
 constexpr int kGemmBM = 128;         // rows per grouped-GEMM tile (MFMA paths)
@@ -79,7 +87,7 @@ struct GemmArgs {
     uint16_t *h_sh;        // [T, Fs]
     uint16_t *au, *au_sh;  // [T*k, 2F], [T, 2Fs] pre-activations [a | u] (training), or null
     float *out;            // [T, d]   shared expert's term (plain stores)
-    uint16_t *y;           // [T*k, d] routed rows, weighted, bf16 (plain stores)
+    float *y;              // [T*k, d] routed rows, weighted, binary32 (plain stores)
     float *f;              // router logits [ksplit, T, ldf] (MODE 2): one partial per K slice
     float *wnorm;          // MODE 2: router row norms [E], from the blocks of slice ksplit (or null)
     int ldf, ksplit;

@@ -232,15 +232,26 @@ hipError_t launch_permute(const Problem &p, int bm, hipStream_t s) {
 // (written by the down-projection's shared tiles), then the routed rows in
 // slot order j = 0..k-1, all in binary32.  Deterministic: no atomics.
 //
-// bfloat16 layers keep the routed rows in bf16: block (t, c) handles token t
-// and columns 512 c .. 512 c + 511, eight per thread.  row_of null: the rows
-// are indexed by pair id (the permutation step was skipped), row t*k+j.
+// The routed rows y are binary32 (each is one expert's weighted output for
+// one token: rounding it too would add a second rounding of the size of the
+// output itself where one expert dominates a token).  Rows of a width that is
+// a multiple of 8: block (t, c) handles token t and columns 512 c .. 512 c +
+// 511, eight per thread.  row_of null: the rows are indexed by pair id (the
+// permutation step was skipped), row t*k+j.  resid (nullable): the caller's
+// binary32 residual stream, which gets the finished output added in the same
+// pass, resid[t] = resid[t] + out[t].
 constexpr int kCombineGroup = 8;
 
+__device__ __forceinline__ void add8(float (&acc)[8], const float4 &lo, const float4 &hi) {
+    acc[0] += lo.x; acc[1] += lo.y; acc[2] += lo.z; acc[3] += lo.w;
+    acc[4] += hi.x; acc[5] += hi.y; acc[6] += hi.z; acc[7] += hi.w;
+}
+
 template <bool SHARED>
-__global__ __launch_bounds__(64) void combine_bf16_kernel(const uint16_t *__restrict__ y,
+__global__ __launch_bounds__(64) void combine_rows_kernel(const float *__restrict__ y,
                                                           const int32_t *__restrict__ row_of,
-                                                          float *__restrict__ out, int d, int k) {
+                                                          float *__restrict__ out,
+                                                          float *__restrict__ resid, int d, int k) {
     const int64_t t = blockIdx.x;
     const int c = (blockIdx.y * 64 + threadIdx.x) * 8;
     if (c >= d) return;
@@ -259,31 +270,37 @@ __global__ __launch_bounds__(64) void combine_bf16_kernel(const uint16_t *__rest
     // the first add; the adds stay in slot order (the tail group re-reads
     // slot k - 1 for its missing slots and skips them)
     for (int j0 = 0; j0 < k; j0 += kCombineGroup) {
-        uint4 q[kCombineGroup];
+        float4 q[kCombineGroup][2];
 #pragma unroll
         for (int u = 0; u < kCombineGroup; ++u) {
             const int j = min(j0 + u, k - 1);
             const int64_t r = row_of ? row_of[t * k + j] : t * k + j;
-            q[u] = *reinterpret_cast<const uint4 *>(y + r * d + c);
+            const float4 *src = reinterpret_cast<const float4 *>(y + r * d + c);
+            q[u][0] = src[0];
+            q[u][1] = src[1];
         }
 #pragma unroll
         for (int u = 0; u < kCombineGroup; ++u) {
             if (j0 + u >= k) break;
-            const uint32_t w4[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                acc[i] += (i & 1) ? bf16_hi(w4[i >> 1]) : bf16_lo(w4[i >> 1]);
+            add8(acc, q[u][0], q[u][1]);
         }
     }
     reinterpret_cast<float4 *>(o)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
     reinterpret_cast<float4 *>(o)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    if (resid) {
+        float4 *r = reinterpret_cast<float4 *>(resid + t * d + c);
+        const float4 lo = r[0], hi = r[1];
+        r[0] = make_float4(lo.x + acc[0], lo.y + acc[1], lo.z + acc[2], lo.w + acc[3]);
+        r[1] = make_float4(hi.x + acc[4], hi.y + acc[5], hi.z + acc[6], hi.w + acc[7]);
+    }
 }
 
-// binary32 layers: one block per token.
+// Any width: one block per token.
 template <bool SHARED>
 __global__ __launch_bounds__(128) void combine_f32_kernel(const float *__restrict__ y,
                                                           const int32_t *__restrict__ row_of,
-                                                          float *__restrict__ out, int d, int k) {
+                                                          float *__restrict__ out,
+                                                          float *__restrict__ resid, int d, int k) {
     const int64_t t = blockIdx.x;
     __shared__ int32_t rows[32];
     if (threadIdx.x < k) rows[threadIdx.x] = row_of ? row_of[t * k + threadIdx.x] : (int32_t)(t * k + threadIdx.x);
@@ -293,28 +310,27 @@ __global__ __launch_bounds__(128) void combine_f32_kernel(const float *__restric
         float acc = SHARED ? o[c] : 0.f;
         for (int j = 0; j < k; ++j) acc += y[(int64_t)rows[j] * d + c];
         o[c] = acc;
+        if (resid) resid[t * d + c] += acc;
     }
 }
 
 hipError_t launch_combine(const Problem &p, hipStream_t s) {
     const int32_t *rows = p.direct ? nullptr : p.rank;
-    if (p.bf16) {
+    if (p.d % 8 == 0) {
         const dim3 grid((unsigned)p.T, (unsigned)((p.d / 8 + 63) / 64));
-        const uint16_t *y = static_cast<const uint16_t *>(p.y);
         if (p.Fs > 0)
-            hipLaunchKernelGGL(combine_bf16_kernel<true>, grid, dim3(64), 0, s, y, rows, p.out,
-                               p.d, p.k);
+            hipLaunchKernelGGL(combine_rows_kernel<true>, grid, dim3(64), 0, s, p.y, rows, p.out,
+                               p.resid, p.d, p.k);
         else
-            hipLaunchKernelGGL(combine_bf16_kernel<false>, grid, dim3(64), 0, s, y, rows, p.out,
-                               p.d, p.k);
+            hipLaunchKernelGGL(combine_rows_kernel<false>, grid, dim3(64), 0, s, p.y, rows, p.out,
+                               p.resid, p.d, p.k);
     } else {
-        const float *y = static_cast<const float *>(p.y);
         if (p.Fs > 0)
-            hipLaunchKernelGGL(combine_f32_kernel<true>, dim3((unsigned)p.T), dim3(128), 0, s, y,
-                               rows, p.out, p.d, p.k);
+            hipLaunchKernelGGL(combine_f32_kernel<true>, dim3((unsigned)p.T), dim3(128), 0, s, p.y,
+                               rows, p.out, p.resid, p.d, p.k);
         else
-            hipLaunchKernelGGL(combine_f32_kernel<false>, dim3((unsigned)p.T), dim3(128), 0, s, y,
-                               rows, p.out, p.d, p.k);
+            hipLaunchKernelGGL(combine_f32_kernel<false>, dim3((unsigned)p.T), dim3(128), 0, s, p.y,
+                               rows, p.out, p.resid, p.d, p.k);
     }
     return hipGetLastError();
 }

@@ -236,11 +236,11 @@ def test_rmsnorm_validation(L):
                          v(FAKE), None) == moe.MOE_ERR_INVALID_ARG
 
 
-def call_prenorm(L, D, T, fmt=0, eps=1e-6, g=FAKE, ws_bytes=1 << 40):
+def call_prenorm(L, D, T, fmt=0, eps=1e-6, g=FAKE, ws_bytes=1 << 40, resid=None, out=FAKE + 4096):
     v = lambda a: None if a is None else ctypes.c_void_p(a)
     return L.moe_forward_prenorm(ctypes.byref(D), T, v(FAKE), v(g), ctypes.c_float(eps), fmt,
                                  v(FAKE), None, v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE),
-                                 v(FAKE), v(FAKE), v(FAKE), v(FAKE), ws_bytes, None)
+                                 v(out), v(FAKE), v(FAKE), v(resid), v(FAKE), ws_bytes, None)
 
 
 def test_forward_prenorm_validation(L):
@@ -254,6 +254,11 @@ def test_forward_prenorm_validation(L):
     assert call_prenorm(L, mx4_desc(d=2560, E=512, k=10, F=640, Fs=640), 200000,
                         fmt=1) == moe.MOE_ERR_UNSUPPORTED
     assert call_prenorm(L, mx4_desc(dtype=moe.MOE_F32), 8, fmt=1) == moe.MOE_ERR_UNSUPPORTED
+    # the residual stream: 16-byte aligned, aliasing neither out nor h
+    assert call_prenorm(L, D, 8, resid=FAKE + 8) == moe.MOE_ERR_INVALID_ARG
+    assert call_prenorm(L, D, 8, resid=FAKE + 4096) == moe.MOE_ERR_INVALID_ARG
+    assert call_prenorm(L, D, 8, resid=FAKE) == moe.MOE_ERR_INVALID_ARG
+    assert call_prenorm(L, D, 8, resid=FAKE + 8192, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
 
 
 def test_workspace_has_xnorm_region(L):
@@ -360,3 +365,4 @@ def test_read_probe_rejects_bad_arguments(L):
     assert L.moe_read_probe(ctypes.c_void_p((1 << 20) + 8), 16, sink, None) == bad
     assert L.moe_read_probe(buf, 24, sink, None) == bad
     assert L.moe_read_probe(buf, 16, ctypes.c_void_p((1 << 21) + 2), None) == bad
+

@@ -14,7 +14,7 @@ import torch
 import oracle
 import sparse_moe_feed_amd as moe
 import workloads as W
-from gpu_util import W_TOL, announce, assert_out, to_dev
+from gpu_util import OUT_TOL, W_TOL, announce, assert_out, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -126,3 +126,38 @@ def test_prenorm_workspace_rows_bit_exact(T):
     got = ws.cpu().numpy()[lay.xnorm:lay.xnorm + 2 * T * d].view(np.uint16).reshape(T, d)
     ref = oracle.rmsnorm(h, g, 1e-6)
     assert int((got != ref).sum()) == 0
+
+
+@pytest.mark.parametrize("T,d,E,k,F,Fs,dtype", [
+    (24, 256, 32, 4, 128, 128, "bf16"),   # weight streaming, no permutation launch
+    (300, 256, 16, 4, 128, 64, "bf16"),   # shortlist router, LDS-tiled experts
+    (20, 96, 6, 2, 40, 24, "f32"),        # binary32 layer
+    (16, 256, 32, 4, 128, 0, "bf16"),     # no shared expert
+])
+def test_prenorm_residual_stream(T, d, E, k, F, Fs, dtype):
+    """moe_forward_prenorm with the residual stream: resid becomes resid + out
+    (the binary32 sum of the two, bit for bit, with the out the same call
+    returns), within the output tolerance of the oracle's resid + out."""
+    inp = W.small_case(T, d, E, k, F, Fs, dtype, seed=T + 3)
+    h = rows(T, d, dtype, T + 4)
+    g = W.make_norm_weight(d, dtype, 13)
+    resid0 = np.random.default_rng(T).standard_normal((T, d)).astype(np.float32)
+    resid = to_dev(resid0)
+    sh = [to_dev(inp[n]) for n in ("w_sh_gate_up", "w_sh_down", "sh_gate")]
+    announce(f"prenorm residual T={T} d={d} {dtype} Fs={Fs}")
+    out, idx, _ = moe.forward_prenorm(to_dev(h), to_dev(g), to_dev(inp["w_router"]),
+                                      to_dev(inp["w_gate_up"]), to_dev(inp["w_down"]), k, *sh,
+                                      resid=resid)
+    torch.cuda.synchronize()
+    out, got = out.cpu().numpy(), resid.cpu().numpy()
+    assert np.array_equal(got, resid0 + out)
+    x = oracle.rmsnorm(h, g, 1e-6)
+    ref_out, ref_idx, _, _ = oracle.forward(x, inp["w_router"], inp["w_gate_up"], inp["w_down"],
+                                            k, *[inp[n] for n in ("w_sh_gate_up", "w_sh_down",
+                                                                   "sh_gate")])
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+    ref = oracle.residual(resid0, ref_out)
+    rms = np.sqrt((ref_out ** 2).mean())
+    err = np.abs(got.astype(np.float64) - ref)
+    tol = (1e-4 if dtype == "f32" else OUT_TOL) * rms
+    assert np.all(err <= tol + 2.0 ** -23 * np.abs(ref)), f"max|err|/rms = {err.max() / rms:.3e}"

@@ -390,3 +390,24 @@ def test_shortlist_bound_is_far_from_tight():
     delta = coef * np.linalg.norm(xf, axis=1)[:, None] * np.linalg.norm(wf, axis=1)[None, :]
     ratio = np.abs(f.astype(np.float64) - l) / delta
     assert ratio.max() < 0.05, ratio.max()
+
+
+# ------------------------------------------------------------------ MOE_DEBUG_SYNC
+
+@pytest.mark.parametrize("T", [24, 300])
+def test_debug_sync_changes_no_result(monkeypatch, T):
+    """MOE_DEBUG_SYNC=1 (the host waits after every stage so that a failing
+    kernel is named) computes exactly what the asynchronous call computes,
+    for the forward (weight-streaming and grouped-GEMM paths) and for the
+    routing alone."""
+    inp = W.small_case(T, 256, 16, 4, 128, 64, "bf16", seed=T + 9)
+    ref = gpu_forward(inp, 4)
+    monkeypatch.setenv("MOE_DEBUG_SYNC", "1")
+    announce(f"MOE_DEBUG_SYNC forward T={T}")
+    got = gpu_forward(inp, 4)
+    for r, g in zip(ref, got):
+        assert np.array_equal(r, g)
+    i_dbg, w_dbg = gpu_route(inp, 4, None)
+    monkeypatch.delenv("MOE_DEBUG_SYNC")
+    i_ref, w_ref = gpu_route(inp, 4, None)
+    assert np.array_equal(i_dbg, i_ref) and np.array_equal(w_dbg, w_ref)

@@ -83,3 +83,31 @@ def test_rows_are_independent():
     g = W.make_x(1, 256, "bf16", 8)[0]
     full = oracle.rmsnorm(h, g)
     assert np.array_equal(oracle.rmsnorm(np.ascontiguousarray(h[5:9]), g), full[5:9])
+
+
+def test_prenorm_block_with_residual_equals_textbook():
+    """The whole pre-norm block with its residual update, k = 1 and no shared
+    expert: resid + SwiGLU_e(RMSNorm(h)) with the definition's binary64 norm
+    (no canonical order, no bf16 rounding of the normalised row beyond the
+    oracle's own) and a dense numpy gated MLP.  A residual taken from the
+    wrong operand, a dropped term or a doubled output fails."""
+    from scipy.special import expit
+
+    T, d, E, F = 9, 128, 6, 32
+    inp = W.small_case(T, d, E, 1, F, 0, "f32", seed=41)
+    h = (2.0 * inp["x"]).astype(np.float32)
+    g = W.make_norm_weight(d, "f32", 3)
+    resid = np.random.default_rng(4).standard_normal((T, d)).astype(np.float32)
+    x = oracle.rmsnorm(h, g, 1e-6)
+    out, idx, _, _ = oracle.forward(x, inp["w_router"], inp["w_gate_up"], inp["w_down"], 1)
+    res = oracle.residual(resid, out)
+    xd = definition(h, g, 1e-6)
+    gu, dn = inp["w_gate_up"].astype(np.float64), inp["w_down"].astype(np.float64)
+    for t in range(T):
+        e = idx[t, 0]
+        a, u = gu[e, :F] @ xd[t], gu[e, F:] @ xd[t]
+        ref = resid[t].astype(np.float64) + dn[e] @ (a * expit(a) * u)
+        # x is binary32 (one rounding per step of the fixed order): 1e-5 relative
+        assert np.allclose(res[t], ref, rtol=1e-5, atol=1e-5 * np.abs(ref).max())
+    assert np.array_equal(oracle.residual(resid, np.zeros_like(out)), resid.astype(np.float64))
+    assert np.array_equal(oracle.residual(np.zeros_like(resid), out), out)
