@@ -350,6 +350,28 @@ moe_status moe_backward(const moe_desc *desc, int64_t T, const void *x,
                         float *aux_loss, void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): moe_forward
+ * with the workspace taken from a static device array of the library,
+ * MOE_NOALLOC_SCRATCH_BYTES (64 MiB) on each GPU it runs on, held until the
+ * process ends.  At the pages' shape (d 2560, 512 experts top-10, width 640,
+ * shared 640, bf16) that serves up to 533 tokens per call.  Arguments,
+ * outputs and errors as moe_forward, without ws / ws_bytes; a call whose
+ * moe_workspace_size exceeds the array returns MOE_ERR_WORKSPACE (and says
+ * so in moe_last_error) before any GPU work.  The call allocates nothing: the
+ * first call on a GPU only looks up the array's device address there.  All
+ * calls on one GPU share its array, so calls that may overlap on one GPU
+ * (different streams, or different threads) race: serialise them.
+ * --------------------------------------------------------------------------- */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_forward_noalloc(const moe_desc *desc, int64_t T, const void *x,
+                               const void *w_router, const float *router_bias,
+                               const void *w_gate_up, const void *w_down,
+                               const void *w_sh_gate_up, const void *w_sh_down,
+                               const void *sh_gate, float *out, int32_t *topk_idx,
+                               float *topk_w, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Measurement aid (not part of the layer): the practical HBM read ceiling.
  * The expert-weight streams of the layer are HBM reads; this reads `bytes`
  * bytes of device memory at `buf` once, with the whole chip, in coalesced

@@ -35,7 +35,7 @@ EXPORTED = ("moe_workspace_size", "moe_workspace_query", "moe_route", "moe_forwa
             "moe_experts_mx4", "moe_rmsnorm", "moe_forward_prenorm",
             "moe_saved_bytes", "moe_forward_train", "moe_backward_workspace_size",
             "moe_backward", "moe_status_string",
-            "moe_last_error", "moe_stage_events", "moe_read_probe")
+            "moe_last_error", "moe_stage_events", "moe_read_probe", "moe_forward_noalloc")
 MOE_WEIGHTS_DTYPE, MOE_WEIGHTS_MX4 = 0, 1
 
 
@@ -104,6 +104,8 @@ def lib():
     L.moe_stage_events.restype = ctypes.c_int
     L.moe_read_probe.argtypes = [vp, sz, vp, vp]
     L.moe_read_probe.restype = ctypes.c_int
+    L.moe_forward_noalloc.argtypes = [dp, i64] + [vp] * 11 + [vp]
+    L.moe_forward_noalloc.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -270,6 +272,40 @@ def forward(x, w_router, w_gate_up, w_down, k, w_sh_gate_up=None, w_sh_down=None
                            _ptr(sh_gate), _ptr(out), _ptr(topk_idx), _ptr(topk_w), _ptr(ws),
                            ws.numel(), _stream())
     _check(st, "moe_forward")
+    return out, topk_idx, topk_w
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def forward_noalloc(x, w_router, w_gate_up, w_down, k, w_sh_gate_up=None, w_sh_down=None,
+                    sh_gate=None, bias=None, out=None, topk_idx=None, topk_w=None):
+    """The whole layer through moe_forward_noalloc: the workspace is the
+    library's static device array (64 MiB per GPU), so the call itself
+    allocates no device memory.  Calls that may overlap on one GPU race on
+    that array.  Returns (out, topk_idx, topk_w); the outputs are allocated
+    here when not given."""
+    T, d = x.shape
+    shape = shape_of(x, w_gate_up, k, w_sh_gate_up)
+    E, F, Fs = shape.n_experts, shape.d_expert, shape.d_shared
+    _dev(x, "x"), _dev(w_router, "w_router", x.dtype, (E, d))
+    _dev(w_gate_up, "w_gate_up", x.dtype), _dev(w_down, "w_down", x.dtype, (E, d, F))
+    if Fs:
+        _dev(w_sh_gate_up, "w_sh_gate_up", x.dtype, (2 * Fs, d))
+        _dev(w_sh_down, "w_sh_down", x.dtype, (d, Fs)), _dev(sh_gate, "sh_gate", x.dtype, (d,))
+    _dev(bias, "router_bias", torch.float32, (E,))
+    out = torch.empty((T, d), dtype=torch.float32, device=x.device) if out is None else out
+    topk_idx = torch.empty((T, k), dtype=torch.int32, device=x.device) if topk_idx is None else topk_idx
+    topk_w = torch.empty((T, k), dtype=torch.float32, device=x.device) if topk_w is None else topk_w
+    _dev(out, "out", torch.float32, (T, d)), _dev(topk_idx, "topk_idx", torch.int32, (T, k))
+    _dev(topk_w, "topk_w", torch.float32, (T, k))
+    st = lib().moe_forward_noalloc(ctypes.byref(shape.desc()), T, _ptr(x), _ptr(w_router),
+                                   _ptr(bias), _ptr(w_gate_up), _ptr(w_down), _ptr(w_sh_gate_up),
+                                   _ptr(w_sh_down), _ptr(sh_gate), _ptr(out), _ptr(topk_idx),
+                                   _ptr(topk_w), _stream())
+    if st == MOE_ERR_WORKSPACE:
+        raise MoEError(st, "moe_forward_noalloc", lib().moe_last_error().decode())
+    _check(st, "moe_forward_noalloc")
     return out, topk_idx, topk_w
 
 

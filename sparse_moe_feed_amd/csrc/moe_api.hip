@@ -637,6 +637,18 @@ const char *moe_last_error(void) { return g_last_error.c_str(); }
 
 void moe::set_last_error(const char *msg) { g_last_error = msg ? msg : ""; }
 
+moe_status moe::check_forward_args(const moe_desc *desc, int64_t T, const void *x,
+                                   const void *w_router, const float *router_bias,
+                                   const void *w_gate_up, const void *w_down,
+                                   const void *w_sh_gate_up, const void *w_sh_down,
+                                   const void *sh_gate, const float *out,
+                                   const int32_t *topk_idx, const float *topk_w) {
+    moe_status st = check_args(desc, T, {x, w_router, w_gate_up, w_down, out, topk_idx, topk_w},
+                               {router_bias, w_sh_gate_up, w_sh_down, sh_gate});
+    if (st != MOE_OK || T == 0) return st;
+    if (desc->d_shared > 0 && (!w_sh_gate_up || !w_sh_down || !sh_gate)) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
 
 extern "C" {
 

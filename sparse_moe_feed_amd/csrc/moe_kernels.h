@@ -65,6 +65,14 @@ struct Problem {
 // Sets the text moe_last_error returns on this thread.
 void set_last_error(const char *msg);
 
+// moe_forward's argument checks, the workspace aside (moe_status values).
+moe_status check_forward_args(const moe_desc *desc, int64_t T, const void *x,
+                              const void *w_router, const float *router_bias,
+                              const void *w_gate_up, const void *w_down,
+                              const void *w_sh_gate_up, const void *w_sh_down,
+                              const void *sh_gate, const float *out, const int32_t *topk_idx,
+                              const float *topk_w);
+
 constexpr int kCountBlock = 256;     // tokens per histogram block
 constexpr int kGemmBM = 128;         // rows per grouped-GEMM tile (MFMA paths)
 constexpr int kDecodeBM = 32;        // rows per tile of the weight-streaming (decode) path

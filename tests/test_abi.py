@@ -366,3 +366,24 @@ def test_read_probe_rejects_bad_arguments(L):
     assert L.moe_read_probe(buf, 24, sink, None) == bad
     assert L.moe_read_probe(buf, 16, ctypes.c_void_p((1 << 21) + 2), None) == bad
 
+
+def test_noalloc_checks_before_any_gpu_work(L):
+    """moe_forward_noalloc validates its arguments and the size of the call
+    against its static array before touching the GPU (none is needed here;
+    the fake addresses are never dereferenced)."""
+    D = desc(d=2560, E=512, k=10, F=640, Fs=640)
+    p = [ctypes.c_void_p(1 << 20)] * 10
+    # 533 tokens fit the 64 MiB array at the pages' shape, 534 do not
+    assert L.moe_workspace_size(ctypes.byref(D), 533) <= 64 << 20 < \
+        L.moe_workspace_size(ctypes.byref(D), 534)
+    assert L.moe_forward_noalloc(ctypes.byref(D), 534, *p[:3], *p[3:10], p[0], None) == \
+        moe.MOE_ERR_WORKSPACE
+    assert b"static scratch" in L.moe_last_error()
+    assert L.moe_forward_noalloc(ctypes.byref(D), 16, None, *p[1:3], *p[3:10], p[0], None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert L.moe_forward_noalloc(ctypes.byref(D), -1, *p[:3], *p[3:10], p[0], None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert L.moe_forward_noalloc(ctypes.byref(D), 0, *p[:3], *p[3:10], p[0], None) == moe.MOE_OK
+    bad = desc(d=2560, E=512, k=10, F=640, Fs=640, dtype=7)
+    assert L.moe_forward_noalloc(ctypes.byref(bad), 16, *p[:3], *p[3:10], p[0], None) == \
+        moe.MOE_ERR_INVALID_ARG
