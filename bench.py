@@ -76,14 +76,16 @@ def algorithmic(cfg, U: int):
     flops_gu = 2 * T * k * 2 * F * d + 2 * T * 2 * Fs * d
     flops_dn = 2 * T * k * F * d + 2 * T * Fs * d
     call_flops = 2 * T * d * (E + 1) + flops_gu + flops_dn
-    # the down stage's weighted per-pair rows y (T*k*d, binary32) are traffic
-    # of this design (the combine reads them back), not of the method: they
-    # are left out of its algorithmic bytes and reported as down_impl_bytes
+    # the down stage's weighted per-pair rows y (T*k rows: binary32 on the
+    # weight-streaming path, else 16-bit block floating point, 2d + d/8 bytes
+    # a row) are traffic of this design (the combine reads them back), not of
+    # the method: they are left out of its algorithmic bytes and reported as
+    # down_impl_bytes
     return dict(call_bytes=call_bytes, call_flops=call_flops,
                 gate_up_bytes=gu_w + T * d * b + (T * k * F + T * Fs) * b,
                 gate_up_flops=flops_gu,
                 down_bytes=dn_w + (T * k * F + T * Fs) * b + T * d * 4,
-                down_impl_bytes=T * k * d * 4,
+                down_impl_bytes=T * k * (4 * d if T * k <= 16 * E else 2 * d + d // 8),
                 down_flops=flops_dn)
 
 
@@ -379,6 +381,8 @@ def main():
     ap.add_argument("--also", default="3,4,5,9", help="extra workloads reported in the line")
     ap.add_argument("--ceiling", action="store_true",
                     help="only measure the practical HBM read / copy / write ceilings (GB/s)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="leave the ceiling measurement out of the line (profiler runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -430,7 +434,7 @@ def main():
                                 stage_ms={k: round(v, 4) for k, v in rc["stage_ms"].items()})
     del dev_layer
     torch.cuda.empty_cache()
-    ceiling = measure_ceiling()
+    ceiling = None if args.no_ceiling else measure_ceiling()
     base = None if args.no_cpu_baseline else cpu_baseline(cfg, layer_np, args.cpu_seconds)
     line = {
         "metric": "MoE-layer tokens/s at T=32 decode and T=4096 prefill; % HBM / MFMA peak",

@@ -353,9 +353,9 @@ moe_status moe_backward(const moe_desc *desc, int64_t T, const void *x,
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): moe_forward
  * with the workspace taken from a static device array of the library,
- * MOE_NOALLOC_SCRATCH_BYTES (64 MiB) on each GPU it runs on, held until the
+ * MOE_NOALLOC_SCRATCH_BYTES (100 MiB) on each GPU it runs on, held until the
  * process ends.  At the pages' shape (d 2560, 512 experts top-10, width 640,
- * shared 640, bf16) that serves up to 533 tokens per call.  Arguments,
+ * shared 640, bf16) that serves up to 1347 tokens per call.  Arguments,
  * outputs and errors as moe_forward, without ws / ws_bytes; a call whose
  * moe_workspace_size exceeds the array returns MOE_ERR_WORKSPACE (and says
  * so in moe_last_error) before any GPU work.  The call allocates nothing: the
@@ -363,7 +363,7 @@ moe_status moe_backward(const moe_desc *desc, int64_t T, const void *x,
  * calls on one GPU share its array, so calls that may overlap on one GPU
  * (different streams, or different threads) race: serialise them.
  * --------------------------------------------------------------------------- */
-#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)100 << 20)
 moe_status moe_forward_noalloc(const moe_desc *desc, int64_t T, const void *x,
                                const void *w_router, const float *router_bias,
                                const void *w_gate_up, const void *w_down,

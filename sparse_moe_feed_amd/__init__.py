@@ -275,13 +275,13 @@ def forward(x, w_router, w_gate_up, w_down, k, w_sh_gate_up=None, w_sh_down=None
     return out, topk_idx, topk_w
 
 
-NOALLOC_SCRATCH_BYTES = 64 << 20
+NOALLOC_SCRATCH_BYTES = 100 << 20
 
 
 def forward_noalloc(x, w_router, w_gate_up, w_down, k, w_sh_gate_up=None, w_sh_down=None,
                     sh_gate=None, bias=None, out=None, topk_idx=None, topk_w=None):
     """The whole layer through moe_forward_noalloc: the workspace is the
-    library's static device array (64 MiB per GPU), so the call itself
+    library's static device array (100 MiB per GPU), so the call itself
     allocates no device memory.  Calls that may overlap on one GPU race on
     that array.  Returns (out, topk_idx, topk_w); the outputs are allocated
     here when not given."""

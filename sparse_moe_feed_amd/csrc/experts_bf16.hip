@@ -251,10 +251,16 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
                 for (int v = 0; v < 16; ++v) {
                     const int row = 64 * wm + 32 * mi + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
                     const int col = n0 + (ni ? brow1 : brow0) + fr;
-                    if (row < nrows && col < a.d) {
-                        const float val = row_w[row] * acc[mi][ni][v];
-                        if (shared) a.out[(int64_t)row_tok[row] * a.d + col] = val;
-                        else a.y[(int64_t)(row0 + row) * a.d + col] = val;
+                    const float val = row_w[row] * acc[mi][ni][v];
+                    if (shared) {
+                        if (row < nrows && col < a.d)
+                            a.out[(int64_t)row_tok[row] * a.d + col] = val;
+                    } else {
+                        // eight consecutive lanes hold eight consecutive
+                        // columns of one row: one y16 group
+                        const uint32_t x = y16_octet_exponent(val);
+                        if (row < nrows && col < a.d)
+                            y16_store1(a.y + (int64_t)(row0 + row) * y16_pitch(a.d), a.d, col, val, x);
                     }
                 }
     }
@@ -269,7 +275,7 @@ hipError_t launch_experts_bf16(const Problem &p, hipStream_t s,
     a.au = static_cast<uint16_t *>(p.au);
     a.au_sh = static_cast<uint16_t *>(p.au_sh);
     a.out = p.out;
-    a.y = p.y;
+    a.y = static_cast<uint8_t *>(p.y);
     a.perm = p.perm;
     a.counts = p.counts;
     a.offsets = p.offsets;

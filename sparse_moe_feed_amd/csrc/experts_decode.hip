@@ -429,7 +429,7 @@ struct Mx4Args {
     const uint16_t *x;
     uint16_t *h, *h_sh;
     float *out;
-    float *y;
+    float *y;              // [T*k, d] weighted routed rows (binary32)
     const int32_t *perm, *counts, *offsets, *tile_start, *tile_group;
     const int32_t *topk_idx;
     const float *topk_w, *gate;
@@ -720,7 +720,7 @@ hipError_t launch_experts_decode_mx4(const Problem &p, hipStream_t s,
     a.h = static_cast<uint16_t *>(p.h);
     a.h_sh = static_cast<uint16_t *>(p.h_shared);
     a.out = p.out;
-    a.y = p.y;
+    a.y = static_cast<float *>(p.y);
     a.perm = p.perm;
     a.counts = p.counts;
     a.offsets = p.offsets;
@@ -761,7 +761,7 @@ hipError_t launch_experts_decode(const Problem &p, hipStream_t s,
     a.au = static_cast<uint16_t *>(p.au);
     a.au_sh = static_cast<uint16_t *>(p.au_sh);
     a.out = p.out;
-    a.y = p.y;
+    a.y = static_cast<float *>(p.y);
     a.perm = p.perm;
     a.counts = p.counts;
     a.offsets = p.offsets;

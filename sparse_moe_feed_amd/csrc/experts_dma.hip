@@ -435,19 +435,34 @@ __global__ __launch_bounds__((64 * Geo<BM, BK>::NW), (NS * Geo<BM, BK>::STB <= 8
             if (mi >= mact || row >= nrows) continue;
             const float wgt = row_w[row];
             if (!shared) {
-                // routed rows: weighted, binary32, into y
-                float *yrow = a.y + (int64_t)(row0 + row) * a.d + n0 + cq;
+                // routed rows: weighted, into y (16-bit block floating point)
+                uint8_t *yrow = a.y + (int64_t)(row0 + row) * y16_pitch(a.d);
+                // a lane holds four consecutive columns of each 8-column
+                // group, lane ^ 32 the other four (same row): the group's
+                // exponent is their joint maximum, and the lane below 32
+                // writes the four exponent bytes of a 32-column block at once
 #pragma unroll
-                for (int ni = 0; ni < NB; ++ni)
+                for (int ni = 0; ni < NB; ++ni) {
+                    const int cb = n0 + brow[ni];
+                    if (cb >= a.d) continue;
+                    const f32x16 &c = acc[mi][ni];
+                    uint32_t xw = 0;
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
-                        const int col = n0 + brow[ni] + 8 * g + cq;
-                        if (col >= a.d) continue;
-                        const f32x16 &c = acc[mi][ni];
-                        *reinterpret_cast<float4 *>(yrow + brow[ni] + 8 * g) =
-                            make_float4(wgt * c[4 * g], wgt * c[4 * g + 1], wgt * c[4 * g + 2],
-                                        wgt * c[4 * g + 3]);
+                        const float v0 = wgt * c[4 * g], v1 = wgt * c[4 * g + 1];
+                        const float v2 = wgt * c[4 * g + 2], v3 = wgt * c[4 * g + 3];
+                        float am = absmax4(v0, v1, v2, v3);
+                        am = fmaxf(am, __shfl_xor(am, 32, 64));
+                        const uint32_t x = y16_exponent(am);
+                        uint2 m;
+                        m.x = y16_pack2(v0, v1, x);
+                        m.y = y16_pack2(v2, v3, x);
+                        *reinterpret_cast<uint2 *>(yrow + 2 * (int64_t)(cb + 8 * g + cq)) = m;
+                        xw |= x << (8 * g);
                     }
+                    if (cq == 0)
+                        *reinterpret_cast<uint32_t *>(yrow + 2 * (int64_t)a.d + cb / 8) = xw;
+                }
             } else {
                 // shared expert: gated term, binary32, straight into out
                 float *orow = a.out + (int64_t)row_tok[row] * a.d + n0 + cq;
@@ -477,7 +492,7 @@ hipError_t launch_experts_dma(const Problem &p, int bm, hipStream_t s,
     a.au = static_cast<uint16_t *>(p.au);
     a.au_sh = static_cast<uint16_t *>(p.au_sh);
     a.out = p.out;
-    a.y = p.y;
+    a.y = static_cast<uint8_t *>(p.y);
     a.perm = p.perm;
     a.counts = p.counts;
     a.offsets = p.offsets;

@@ -111,7 +111,7 @@ hipError_t launch_experts_f32(const Problem &p, hipStream_t s,
     a.au = static_cast<float *>(p.au);
     a.au_sh = static_cast<float *>(p.au_sh);
     a.out = p.out;
-    a.y = p.y;
+    a.y = static_cast<float *>(p.y);
     a.perm = p.perm;
     a.offsets = p.offsets;
     a.topk_w = p.topk_w;

@@ -227,7 +227,7 @@ struct Mx4GemmArgs {
     const uint8_t *wp_sh;  // packed shared weights: gate/up [2Fs, d], down [d, Fs]
     uint16_t *h, *h_sh;
     float *out;
-    float *y;
+    uint8_t *y;            // routed rows, weighted, y16 rows
     const int32_t *perm, *counts, *offsets, *tile_start, *tile_group;
     const float *topk_w, *gate;
     int64_t T;
@@ -364,18 +364,33 @@ __global__ __launch_bounds__(64 * XW, 1) void gemm_mx4_kernel(Mx4GemmArgs a) {
             if (mi >= mact || row >= nrows) continue;
             const float wgt = row_w[row];
             if (!shared) {
-                float *yrow = a.y + (int64_t)(row0 + row) * a.d + n0 + cq;
+                uint8_t *yrow = a.y + (int64_t)(row0 + row) * y16_pitch(a.d);
+                // a lane holds four consecutive columns of each 8-column
+                // group, lane ^ 32 the other four (same row): the group's
+                // exponent is their joint maximum, and the lane below 32
+                // writes the four exponent bytes of a 32-column block at once
 #pragma unroll
-                for (int ni = 0; ni < XNB; ++ni)
+                for (int ni = 0; ni < XNB; ++ni) {
+                    const int cb = n0 + brow[ni];
+                    if (cb >= a.d) continue;
+                    const f32x16 &c = acc[mi][ni];
+                    uint32_t xw = 0;
 #pragma unroll
                     for (int gg = 0; gg < 4; ++gg) {
-                        const int col = n0 + brow[ni] + 8 * gg + cq;
-                        if (col >= a.d) continue;
-                        const f32x16 &c = acc[mi][ni];
-                        *reinterpret_cast<float4 *>(yrow + brow[ni] + 8 * gg) =
-                            make_float4(wgt * c[4 * gg], wgt * c[4 * gg + 1], wgt * c[4 * gg + 2],
-                                        wgt * c[4 * gg + 3]);
+                        const float v0 = wgt * c[4 * gg], v1 = wgt * c[4 * gg + 1];
+                        const float v2 = wgt * c[4 * gg + 2], v3 = wgt * c[4 * gg + 3];
+                        float am = absmax4(v0, v1, v2, v3);
+                        am = fmaxf(am, __shfl_xor(am, 32, 64));
+                        const uint32_t x = y16_exponent(am);
+                        uint2 m;
+                        m.x = y16_pack2(v0, v1, x);
+                        m.y = y16_pack2(v2, v3, x);
+                        *reinterpret_cast<uint2 *>(yrow + 2 * (int64_t)(cb + 8 * gg + cq)) = m;
+                        xw |= x << (8 * gg);
                     }
+                    if (cq == 0)
+                        *reinterpret_cast<uint32_t *>(yrow + 2 * (int64_t)a.d + cb / 8) = xw;
+                }
             } else {
                 float *orow = a.out + (int64_t)row_tok[row] * a.d + n0 + cq;
 #pragma unroll
@@ -402,7 +417,7 @@ hipError_t launch_experts_mx4_gemm(const Problem &p, hipStream_t s,
     a.h = static_cast<uint16_t *>(p.h);
     a.h_sh = static_cast<uint16_t *>(p.h_shared);
     a.out = p.out;
-    a.y = p.y;
+    a.y = static_cast<uint8_t *>(p.y);
     a.perm = p.perm;
     a.counts = p.counts;
     a.offsets = p.offsets;

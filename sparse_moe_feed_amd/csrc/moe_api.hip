@@ -12,6 +12,7 @@
 //   5. down grouped GEMM -> weighted rows y, shared term -> out
 //   6. combine: out[t] += sum_j y[row(t,j)]   (permute.hip)
 #include "moe.h"
+#include "moe_device.h"
 #include "moe_kernels.h"
 
 #include <stdio.h>
@@ -142,7 +143,12 @@ Plan make_plan(const moe_desc &d, int64_t T) {
     p.perm = take((size_t)pairs * sizeof(int32_t));
     p.h = take((size_t)pairs * d.d_expert * esize);
     p.h_shared = take((size_t)T * d.d_shared * esize);
-    p.y = take((size_t)pairs * d.d_model * sizeof(float));
+    // binary32 rows where the weight-streaming path may serve the call (few
+    // rows per expert) and for binary32 layers; 16-bit block floating point
+    // rows from the grouped GEMMs otherwise
+    const bool y_f32 = d.dtype != MOE_BF16 || pairs <= (int64_t)16 * d.n_experts;
+    p.y = take((size_t)pairs * (y_f32 ? (size_t)d.d_model * sizeof(float)
+                                      : (size_t)moe::y16_pitch(d.d_model)));
     p.xnorm = take((size_t)T * d.d_model * esize);
     p.total = off;
     return p;
@@ -173,7 +179,7 @@ moe::Problem make_problem(const moe_desc &d, int64_t T, const Plan &pl, void *ws
     p.perm = reinterpret_cast<int32_t *>(base + pl.perm);
     p.h = base + pl.h;
     p.h_shared = base + pl.h_shared;
-    p.y = reinterpret_cast<float *>(base + pl.y);
+    p.y = base + pl.y;
     p.nblk = pl.nblk;
     p.max_tiles = pl.max_tiles;
     return p;
@@ -322,6 +328,7 @@ moe_status run_experts(moe::Problem p, hipStream_t s) {
     // 256-row tiles once experts average 192+ rows
     const bool big = dma && !p.mx4 && p.T * p.k >= (int64_t)192 * p.E;  // MXFP4 GEMM: 128 rows
     const int bm = decode ? moe::kDecodeBM : big ? moe::kGemm256BM : moe::kGemmBM;
+    p.y_f32 = !p.bf16 || decode;
     p.max_tiles = (int)moe::max_gemm_tiles(p.T, p.k, p.E, bm, p.Fs > 0);
     hipError_t err = p.direct ? hipSuccess : moe::launch_permute(p, bm, s);
     mark_stage(2, s);

@@ -33,6 +33,56 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+// Weighted routed rows y of bfloat16 layers, in 16-bit block floating point.
+// A row of d values is stored as d signed 16-bit mantissas followed by d/8
+// exponent bytes, padded to a multiple of 16 bytes (y16_pitch(d)).  Group g,
+// elements 8g..8g+7, shares exponent byte X: element i is m_i * 2^(X - 141).
+// X is the biased binary32 exponent of the group's largest magnitude M (at
+// least 1; 0 when the group is all zeros), so M * 2^(141 - X) lies in
+// [2^14, 2^15) and every m_i = round-to-nearest-even(v_i * 2^(141 - X))
+// (+2^15 clamped to 2^15 - 1) is off by at most 2^-15 M.  Against bfloat16
+// (an error of up to 2^-9 of each element) this keeps the rows as good as
+// binary32 for the layer's output tolerance, at about 2.1 bytes per element
+// instead of 4.
+__host__ __device__ constexpr int64_t y16_pitch(int d) {
+    return (2 * (int64_t)d + d / 8 + 15) / 16 * 16;
+}
+
+__device__ __forceinline__ uint32_t y16_exponent(float amax) {
+    const uint32_t f = (__float_as_uint(amax) >> 23) & 0xFFu;
+    return amax == 0.0f ? 0u : (f > 1u ? f : 1u);
+}
+__device__ __forceinline__ int32_t y16_q(float v, uint32_t x) {
+    return (int32_t)fminf(__builtin_rintf(ldexpf(v, 141 - (int)x)), 32767.0f);
+}
+// Two elements as one packed pair of 16-bit mantissas (element a low).
+__device__ __forceinline__ uint32_t y16_pack2(float a, float b, uint32_t x) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pk_i16(y16_q(a, x), y16_q(b, x)));
+}
+__device__ __forceinline__ float y16_value(uint32_t m16, uint32_t x) {
+    return ldexpf((float)(int32_t)(int16_t)(uint16_t)m16, (int)x - 141);
+}
+__device__ __forceinline__ float absmax4(float a, float b, float c, float e) {
+    return fmaxf(fmaxf(fabsf(a), fabsf(b)), fmaxf(fabsf(c), fabsf(e)));
+}
+// One element per lane, a group's eight elements in eight consecutive lanes
+// (8q .. 8q+7, consecutive columns): the group's exponent byte.  Every lane
+// of the wave must execute it.
+__device__ __forceinline__ uint32_t y16_octet_exponent(float v) {
+    float a = fabsf(v);
+    a = fmaxf(a, __shfl_xor(a, 1, 64));
+    a = fmaxf(a, __shfl_xor(a, 2, 64));
+    a = fmaxf(a, __shfl_xor(a, 4, 64));
+    return y16_exponent(a);
+}
+// The element at col of row from its lane, with its octet's exponent x (the
+// lane holding the group's first column writes the exponent byte).
+__device__ __forceinline__ void y16_store1(uint8_t *row, int d, int col, float v, uint32_t x) {
+    *reinterpret_cast<uint16_t *>(row + 2 * (int64_t)col) =
+        (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pk_i16(y16_q(v, x), 0)) & 0xFFFFu);
+    if ((col & 7) == 0) row[2 * (int64_t)d + col / 8] = (uint8_t)x;
+}
+
 // Eight consecutive elements widened to binary32 (exact).
 __device__ __forceinline__ void load8(const uint16_t *p, float v[8]) {
     uint4 q = *reinterpret_cast<const uint4 *>(p);

@@ -38,7 +38,10 @@ struct Problem {
     int32_t *blk;       // [E, nblk]
     int32_t *rank;      // [T*k] rank inside the histogram block, then the pair's row
     int32_t *perm;      // [T*k]
-    float *y;           // [T*k, d] weighted down-projection of each routed row
+    void *y;            // [T*k] weighted down-projection of each routed row: rows of
+                        // y16_pitch(d) bytes in 16-bit block floating point from
+                        // the grouped GEMMs, binary32 [T*k, d] when y_f32
+    bool y_f32;         // y in binary32: binary32 layers and the weight-streaming path
                         // (bf16 for bfloat16 layers, binary32 otherwise)
     void *h;            // [T*k, F]
     void *h_shared;     // [T, Fs]
@@ -95,7 +98,7 @@ struct GemmArgs {
     uint16_t *h_sh;        // [T, Fs]
     uint16_t *au, *au_sh;  // [T*k, 2F], [T, 2Fs] pre-activations [a | u] (training), or null
     float *out;            // [T, d]   shared expert's term (plain stores)
-    float *y;              // [T*k, d] routed rows, weighted, binary32 (plain stores)
+    uint8_t *y;            // [T*k] routed rows, weighted, y16 rows (plain stores)
     float *f;              // router logits [ksplit, T, ldf] (MODE 2): one partial per K slice
     float *wnorm;          // MODE 2: router row norms [E], from the blocks of slice ksplit (or null)
     int ldf, ksplit;

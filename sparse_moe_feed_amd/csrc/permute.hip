@@ -232,11 +232,10 @@ hipError_t launch_permute(const Problem &p, int bm, hipStream_t s) {
 // (written by the down-projection's shared tiles), then the routed rows in
 // slot order j = 0..k-1, all in binary32.  Deterministic: no atomics.
 //
-// The routed rows y are binary32 (each is one expert's weighted output for
-// one token: rounding it too would add a second rounding of the size of the
-// output itself where one expert dominates a token).  Rows of a width that is
-// a multiple of 8: block (t, c) handles token t and columns 512 c .. 512 c +
-// 511, eight per thread.  row_of null: the rows are indexed by pair id (the
+// Binary32 layers and the weight-streaming path keep the routed rows y in
+// binary32.  Rows of a width that
+// is a multiple of 8: block (t, c) handles token t and columns 512 c .. 512 c
+// + 511, eight per thread.  row_of null: the rows are indexed by pair id (the
 // permutation step was skipped), row t*k+j.  resid (nullable): the caller's
 // binary32 residual stream, which gets the finished output added in the same
 // pass, resid[t] = resid[t] + out[t].
@@ -295,6 +294,64 @@ __global__ __launch_bounds__(64) void combine_rows_kernel(const float *__restric
     }
 }
 
+// bfloat16 layers: the same, with the routed rows in 16-bit block floating
+// point (y16_pitch bytes per row: mantissas, then one exponent byte per eight
+// columns); a thread's eight columns are one group.
+template <bool SHARED>
+__global__ __launch_bounds__(64) void combine_y16_kernel(const uint8_t *__restrict__ y,
+                                                         const int32_t *__restrict__ row_of,
+                                                         float *__restrict__ out,
+                                                         float *__restrict__ resid, int d, int k) {
+    const int64_t t = blockIdx.x;
+    const int c = (blockIdx.y * 64 + threadIdx.x) * 8;
+    if (c >= d) return;
+    const int64_t pitch = y16_pitch(d);
+    float acc[8];
+    float *o = out + t * d + c;
+    if (SHARED) {
+        const float4 lo = reinterpret_cast<const float4 *>(o)[0];
+        const float4 hi = reinterpret_cast<const float4 *>(o)[1];
+        acc[0] = lo.x; acc[1] = lo.y; acc[2] = lo.z; acc[3] = lo.w;
+        acc[4] = hi.x; acc[5] = hi.y; acc[6] = hi.z; acc[7] = hi.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    }
+    for (int j0 = 0; j0 < k; j0 += kCombineGroup) {
+        uint4 m[kCombineGroup];
+        uint32_t x[kCombineGroup];
+#pragma unroll
+        for (int u = 0; u < kCombineGroup; ++u) {
+            const int j = min(j0 + u, k - 1);
+            const int64_t r = row_of ? row_of[t * k + j] : t * k + j;
+            const uint8_t *row = y + r * pitch;
+            m[u] = *reinterpret_cast<const uint4 *>(row + 2 * (int64_t)c);
+            x[u] = row[2 * (int64_t)d + c / 8];
+        }
+#pragma unroll
+        for (int u = 0; u < kCombineGroup; ++u) {
+            if (j0 + u >= k) break;
+            const uint32_t xu = x[u];
+            acc[0] += y16_value(m[u].x & 0xFFFFu, xu);
+            acc[1] += y16_value(m[u].x >> 16, xu);
+            acc[2] += y16_value(m[u].y & 0xFFFFu, xu);
+            acc[3] += y16_value(m[u].y >> 16, xu);
+            acc[4] += y16_value(m[u].z & 0xFFFFu, xu);
+            acc[5] += y16_value(m[u].z >> 16, xu);
+            acc[6] += y16_value(m[u].w & 0xFFFFu, xu);
+            acc[7] += y16_value(m[u].w >> 16, xu);
+        }
+    }
+    reinterpret_cast<float4 *>(o)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    reinterpret_cast<float4 *>(o)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    if (resid) {
+        float4 *r = reinterpret_cast<float4 *>(resid + t * d + c);
+        const float4 lo = r[0], hi = r[1];
+        r[0] = make_float4(lo.x + acc[0], lo.y + acc[1], lo.z + acc[2], lo.w + acc[3]);
+        r[1] = make_float4(hi.x + acc[4], hi.y + acc[5], hi.z + acc[6], hi.w + acc[7]);
+    }
+}
+
 // Any width: one block per token.
 template <bool SHARED>
 __global__ __launch_bounds__(128) void combine_f32_kernel(const float *__restrict__ y,
@@ -316,20 +373,31 @@ __global__ __launch_bounds__(128) void combine_f32_kernel(const float *__restric
 
 hipError_t launch_combine(const Problem &p, hipStream_t s) {
     const int32_t *rows = p.direct ? nullptr : p.rank;
-    if (p.d % 8 == 0) {
-        const dim3 grid((unsigned)p.T, (unsigned)((p.d / 8 + 63) / 64));
+    const dim3 grid8((unsigned)p.T, (unsigned)((p.d / 8 + 63) / 64));
+    if (!p.y_f32) {
+        const uint8_t *y = static_cast<const uint8_t *>(p.y);
         if (p.Fs > 0)
-            hipLaunchKernelGGL(combine_rows_kernel<true>, grid, dim3(64), 0, s, p.y, rows, p.out,
+            hipLaunchKernelGGL(combine_y16_kernel<true>, grid8, dim3(64), 0, s, y, rows, p.out,
                                p.resid, p.d, p.k);
         else
-            hipLaunchKernelGGL(combine_rows_kernel<false>, grid, dim3(64), 0, s, p.y, rows, p.out,
+            hipLaunchKernelGGL(combine_y16_kernel<false>, grid8, dim3(64), 0, s, y, rows, p.out,
+                               p.resid, p.d, p.k);
+        return hipGetLastError();
+    }
+    const float *y = static_cast<const float *>(p.y);
+    if (p.d % 8 == 0) {
+        if (p.Fs > 0)
+            hipLaunchKernelGGL(combine_rows_kernel<true>, grid8, dim3(64), 0, s, y, rows, p.out,
+                               p.resid, p.d, p.k);
+        else
+            hipLaunchKernelGGL(combine_rows_kernel<false>, grid8, dim3(64), 0, s, y, rows, p.out,
                                p.resid, p.d, p.k);
     } else {
         if (p.Fs > 0)
-            hipLaunchKernelGGL(combine_f32_kernel<true>, dim3((unsigned)p.T), dim3(128), 0, s, p.y,
+            hipLaunchKernelGGL(combine_f32_kernel<true>, dim3((unsigned)p.T), dim3(128), 0, s, y,
                                rows, p.out, p.resid, p.d, p.k);
         else
-            hipLaunchKernelGGL(combine_f32_kernel<false>, dim3((unsigned)p.T), dim3(128), 0, s, p.y,
+            hipLaunchKernelGGL(combine_f32_kernel<false>, dim3((unsigned)p.T), dim3(128), 0, s, y,
                                rows, p.out, p.resid, p.d, p.k);
     }
     return hipGetLastError();

@@ -373,10 +373,10 @@ def test_noalloc_checks_before_any_gpu_work(L):
     the fake addresses are never dereferenced)."""
     D = desc(d=2560, E=512, k=10, F=640, Fs=640)
     p = [ctypes.c_void_p(1 << 20)] * 10
-    # 533 tokens fit the 64 MiB array at the pages' shape, 534 do not
-    assert L.moe_workspace_size(ctypes.byref(D), 533) <= 64 << 20 < \
-        L.moe_workspace_size(ctypes.byref(D), 534)
-    assert L.moe_forward_noalloc(ctypes.byref(D), 534, *p[:3], *p[3:10], p[0], None) == \
+    # every batch up to 1347 tokens fits the 100 MiB array at the pages' shape
+    assert all(L.moe_workspace_size(ctypes.byref(D), T) <= 100 << 20 for T in range(1, 1348))
+    assert L.moe_workspace_size(ctypes.byref(D), 1348) > 100 << 20
+    assert L.moe_forward_noalloc(ctypes.byref(D), 1348, *p[:3], *p[3:10], p[0], None) == \
         moe.MOE_ERR_WORKSPACE
     assert b"static scratch" in L.moe_last_error()
     assert L.moe_forward_noalloc(ctypes.byref(D), 16, None, *p[1:3], *p[3:10], p[0], None) == \
