@@ -233,6 +233,7 @@ def permuted_rows(idx, E):
     (24, 256, 16, 4, 128, 128, "bf16"),     # weight-streaming path
     (300, 256, 16, 4, 128, 128, "bf16"),    # direct-to-LDS GEMM path
     (300, 256, 16, 4, 192, 64, "bf16"),     # register-staged GEMM (F % 128 != 0)
+    (1000, 576, 192, 4, 640, 640, "bf16"),  # direct-to-LDS GEMM at the pages' widths
     (20, 96, 6, 2, 40, 24, "f32"),          # binary32 layer
 ])
 def test_forward_train_saves_preactivations(T, d, E, k, F, Fs, dtype):

@@ -65,6 +65,9 @@ def test_tiny_fp32_layer():
     (1200, 384, 8, 2, 256, 128),    # 256-row tiles, 2 per expert; d % 256 = 128
     (600, 256, 16, 4, 128, 128),    # 128-row LDS-DMA tiles, some experts > 128 rows
     (500, 320, 16, 3, 256, 128),    # 128-row LDS-DMA tiles; d % 256 = 64
+    (1000, 576, 192, 4, 640, 640),  # 128-row LDS-DMA tiles at the pages' widths (F == Fs),
+                                    # 9 K steps in gate/up, d % 256 = 64
+    (2000, 640, 96, 6, 640, 640),   # the same, experts of one and two tiles
 ])
 def test_small_bf16_layers(T, d, E, k, F, Fs):
     inp = W.small_case(T, d, E, k, F, Fs, "bf16", seed=T + E)
@@ -411,3 +414,28 @@ def test_debug_sync_changes_no_result(monkeypatch, T):
     monkeypatch.delenv("MOE_DEBUG_SYNC")
     i_ref, w_ref = gpu_route(inp, 4, None)
     assert np.array_equal(i_dbg, i_ref) and np.array_equal(w_dbg, w_ref)
+
+
+# ------------------------------------------------------------------ direct decode tiles
+
+@pytest.mark.parametrize("T,d,E,k,F,Fs,case", [
+    (32, 256, 16, 4, 128, 128, "one expert chosen by every token (two 16-row halves)"),
+    (24, 640, 64, 8, 256, 0, "no shared expert; ragged last column block"),
+    (32, 2560, 512, 10, 640, 640, "pages' shapes"),
+    (1, 384, 32, 6, 128, 256, "one token, Fs > F"),
+    (17, 1152, 128, 32, 128, 128, "k = 32, 17 tokens"),
+])
+def test_direct_decode_shapes(T, d, E, k, F, Fs, case):
+    """The weight-streaming path without the permutation step (T <= 32, exact
+    router) at odd shapes: routing bit-exact, out within tolerance of the
+    oracle, and deterministic run to run."""
+    inp = W.small_case(T, d, E, k, F, Fs, "bf16", seed=T * 7 + d)
+    if case.startswith("one expert"):
+        b = np.zeros(E, np.float32)
+        b[5] = 50.0
+        inp["bias"] = b
+    announce(f"direct decode: {case}")
+    r = check_case(inp, k, case)
+    out1, _, _ = gpu_forward(inp, k)
+    out2, _, _ = gpu_forward(inp, k)
+    assert np.array_equal(out1, out2), "not deterministic"
