@@ -439,3 +439,41 @@ def test_direct_decode_shapes(T, d, E, k, F, Fs, case):
     out1, _, _ = gpu_forward(inp, k)
     out2, _, _ = gpu_forward(inp, k)
     assert np.array_equal(out1, out2), "not deterministic"
+
+
+# ------------------------------------------------------------------ direct decode, many experts touched
+
+@pytest.mark.parametrize("T,d,E,k,F,bias_e,case", [
+    (32, 256, 1024, 8, 128, None, "227 experts touched, one or two rows each"),
+    (32, 256, 1024, 8, 128, 5, "one expert chosen by every token: 32 rows"),
+    (20, 384, 512, 16, 256, None, "20 tokens, k = 16"),
+    (32, 128, 256, 32, 2048, None, "widest expert held in LDS; d = 128: half the waves "
+                                   "have no down columns"),
+])
+def test_direct_decode_many_experts_matches_permuted_path(T, d, E, k, F, bias_e, case):
+    """The direct decode path with 200+ experts touched (the decode
+    workload's regime), up to 32 rows on one expert and experts up to 2048
+    wide: fed the forward's own routing, the routing-given entry point
+    (permuted rows) gives the same bits; both match the oracle."""
+    inp = W.small_case(T, d, E, k, F, 0, "bf16", seed=T * 3 + E)
+    if bias_e is not None:
+        inp["bias"] = np.zeros(E, np.float32)
+        inp["bias"][bias_e] = 100.0
+    announce(f"direct decode, many experts: {case}")
+    args = [to_dev(inp[n]) for n in ("x", "w_router", "w_gate_up", "w_down")]
+    out, idx, w = moe.forward(*args, k, bias=to_dev(inp.get("bias")))
+    out2 = moe.experts(args[0], args[2], args[3], idx, w)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), out2.cpu().numpy())
+    ref_out, ref_idx, _, _ = oracle_forward(inp, k)
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+    assert_out(out.cpu().numpy(), ref_out)
+
+
+@pytest.mark.parametrize("T,d,E,k,F,Fs,case", [
+    (32, 512, 1024, 8, 128, 256, "shared expert wider than the routed ones"),
+    (32, 256, 1024, 8, 256, 128, "shared expert narrower than the routed ones"),
+])
+def test_direct_decode_many_experts_with_shared_expert(T, d, E, k, F, Fs, case):
+    inp = W.small_case(T, d, E, k, F, Fs, "bf16", seed=T + E + F)
+    check_case(inp, k, f"direct decode, many experts: {case}")
