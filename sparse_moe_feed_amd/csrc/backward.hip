@@ -1060,7 +1060,12 @@ hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
         hipLaunchKernelGGL(router_bwd_kernel<float>, dim3((unsigned)a.T), dim3(256), lds, s, a);
     }
     mark(3);
-    launch_gemm<K_DX>(a, tiles, cdiv(a.d, QB), s);
+    if (bwd_dx_dma_ok(a)) {
+        err = launch_bwd_dx_dma(a, (int)tiles, s);
+        if (err != hipSuccess) return err;
+    } else {
+        launch_gemm<K_DX>(a, tiles, cdiv(a.d, QB), s);
+    }
     mark(4);
     // The weight gradients reduce over one expert's rows: experts (and a
     // shared expert over T <= KS tokens) with at most KS rows in the

@@ -482,6 +482,271 @@ __global__ __launch_bounds__((64 * Geo<BM, BK>::NW), (NS * Geo<BM, BK>::STB <= 8
     }
 }
 
+// ---------------------------------------------------------------------------
+// Backward: dx of each routed row and of the shared expert's rows,
+// dX = [da | du] W_gu (the transpose of the forward's gate/up product; the
+// backward's 128-row tile map), on the 128 x 256 tiles above (K = 2 F in
+// steps of 64, three direct-to-LDS stages, 8 waves).  A ([da | du] rows,
+// contiguous along K) is staged as the forward's A.  B = W_gu runs along the
+// output axis, so each K step's 64 rows of 256 columns (512 bytes) go to LDS
+// as loaded, two rows per 1 KB load, with the 16-byte chunks of row k
+// permuted by chunk ^ 2 (k & 3); the MFMA fragments are read with
+// ds_read_b64_tr_b16, and the four rows one 16-lane read phase touches then
+// sit on disjoint bank groups.
+namespace {
+constexpr int MC_ROWB = BN * 2;  // bytes per staged B row (one K index)
+__device__ __forceinline__ int mc_swz(int k) { return 2 * (k & 3); }
+
+// One stage: A as dma_stage; B rows k0 .. k0 + 63 (element offsets boff of
+// this lane's row and chunk, plus k0 rows of ldb elements).
+__device__ __forceinline__ void dma_stage_mc(unsigned char *stage, const uint16_t *abase,
+                                             const uint16_t *wbase,
+                                             const uint32_t (&aoff)[Geo<128, 64>::AL],
+                                             const uint32_t (&boff)[Geo<128, 64>::BL], int k0,
+                                             uint32_t ldb, int wave) {
+    using G = Geo<128, 64>;
+#pragma unroll
+    for (int j = 0; j < G::AL; ++j)
+        __builtin_amdgcn_global_load_lds((const global_void_t *)(abase + aoff[j] + k0),
+                                         (lds_void_t *)(stage + (G::AL * wave + j) * 1024), 16,
+                                         0, 0);
+    const uint16_t *wk = wbase + (size_t)k0 * ldb;
+#pragma unroll
+    for (int j = 0; j < G::BL; ++j)
+        __builtin_amdgcn_global_load_lds(
+            (const global_void_t *)(wk + boff[j]),
+            (lds_void_t *)(stage + G::OPA + (G::BL * wave + j) * 1024), 16, 0, 0);
+}
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// B fragment of output columns nb .. nb + 31 at k16 step ks: lane L gets
+// column nb + L % 32, K rows 16 ks + 8 (L / 32) .. + 7.  Lane s of a 16-lane
+// group addresses K row k + s / 4, columns 4 (s % 4) .. + 3 of its 16-column
+// half; the transposing read hands lane s column s of those four rows, and a
+// second read four rows down completes the eight.
+__device__ __forceinline__ bf16x8 mc_bfrag(const unsigned char *bst, int ks, int nb, int lane) {
+    const int g = lane >> 4, s = lane & 15;
+    const int k = 16 * ks + 8 * (g >> 1) + (s >> 2);
+    const int m = nb + 16 * (g & 1) + 4 * (s & 3);
+    const int off = (((m >> 3) ^ mc_swz(k)) << 4) + (m & 7) * 2;  // k and k + 4: same swizzle
+    const unsigned char *p = bst + k * MC_ROWB + off;
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)p);
+    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(p + 4 * MC_ROWB));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int MACT>
+__device__ __forceinline__ void read_frags_mc(const unsigned char *stage, int ks, int wm,
+                                              const int (&brow)[NB], int fr, int lane, Frags &f) {
+    if (MACT == 0) return;
+    const int c = 2 * ks + (lane >> 5);
+    f.a[0] = *reinterpret_cast<const bf16x8 *>(stage + tile_off<64>(32 * wm + fr, c));
+#pragma unroll
+    for (int ni = 0; ni < NB; ++ni) f.b[ni] = mc_bfrag(stage + Geo<128, 64>::OPA, ks, brow[ni], lane);
+}
+
+template <int MACT>
+__device__ __forceinline__ void sub_step_mc(const unsigned char *stage, int ks, int wm,
+                                            const int (&brow)[NB], int fr, int lane,
+                                            const Frags &cur, Frags &nxt, f32x16 (&acc)[1][NB]) {
+    if (MACT > 0) {
+        mfma_frags<MACT>(cur, acc);
+        read_frags_mc<MACT>(stage, ks, wm, brow, fr, lane, nxt);
+        interleave_reads<MACT>();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// One K step on constant buffer S (as k_step).
+template <int MACT, int S>
+__device__ __forceinline__ void k_step_mc(const Stages<3> &st, int kt, int last,
+                                          const uint16_t *abase, const uint16_t *wbase,
+                                          const uint32_t (&aoff)[Geo<128, 64>::AL],
+                                          const uint32_t (&boff)[Geo<128, 64>::BL], uint32_t ldb,
+                                          int wave, int wm, const int (&brow)[NB], int fr,
+                                          int lane, Frags &f0, Frags &f1, f32x16 (&acc)[1][NB]) {
+    using G = Geo<128, 64>;
+    sub_step_mc<MACT>(st.s[S], 1, wm, brow, fr, lane, f0, f1, acc);
+    sub_step_mc<MACT>(st.s[S], 2, wm, brow, fr, lane, f1, f0, acc);
+    sub_step_mc<MACT>(st.s[S], 3, wm, brow, fr, lane, f0, f1, acc);
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(G::LOADS));
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    dma_stage_mc(st.s[S], abase, wbase, aoff, boff, min((kt + 3) * 64, last), ldb, wave);
+    __builtin_amdgcn_sched_barrier(0);
+    sub_step_mc<MACT>(st.s[(S + 1) % 3], 0, wm, brow, fr, lane, f1, f0, acc);
+}
+
+template <int MACT, int S>
+__device__ __forceinline__ void k_steps_mc(const Stages<3> &st, int kt, int cnt, int last,
+                                           const uint16_t *abase, const uint16_t *wbase,
+                                           const uint32_t (&aoff)[Geo<128, 64>::AL],
+                                           const uint32_t (&boff)[Geo<128, 64>::BL],
+                                           uint32_t ldb, int wave, int wm, const int (&brow)[NB],
+                                           int fr, int lane, Frags &f0, Frags &f1,
+                                           f32x16 (&acc)[1][NB]) {
+    if constexpr (S < 3) {
+        if (S < cnt) {
+            k_step_mc<MACT, S>(st, kt + S, last, abase, wbase, aoff, boff, ldb, wave, wm, brow, fr,
+                               lane, f0, f1, acc);
+            k_steps_mc<MACT, S + 1>(st, kt, cnt, last, abase, wbase, aoff, boff, ldb, wave, wm,
+                                    brow, fr, lane, f0, f1, acc);
+        }
+    }
+}
+
+template <int MACT>
+__device__ __forceinline__ void k_loop_mc(const Stages<3> &st, const uint16_t *abase,
+                                          const uint16_t *wbase,
+                                          const uint32_t (&aoff)[Geo<128, 64>::AL],
+                                          const uint32_t (&boff)[Geo<128, 64>::BL], uint32_t ldb,
+                                          int nk, int wave, int wm, const int (&brow)[NB], int fr,
+                                          int lane, f32x16 (&acc)[1][NB]) {
+    const int last = (nk - 1) * 64;
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+        dma_stage_mc(st.s[i], abase, wbase, aoff, boff, min(i * 64, last), ldb, wave);
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * Geo<128, 64>::LOADS));
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    Frags f0, f1;
+    read_frags_mc<MACT>(st.s[0], 0, wm, brow, fr, lane, f0);
+    int kt = 0;
+    for (; kt + 3 <= nk; kt += 3)
+        k_steps_mc<MACT, 0>(st, kt, 3, last, abase, wbase, aoff, boff, ldb, wave, wm, brow, fr,
+                            lane, f0, f1, acc);
+    k_steps_mc<MACT, 0>(st, kt, nk - kt, last, abase, wbase, aoff, boff, ldb, wave, wm, brow, fr,
+                        lane, f0, f1, acc);
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land after the block ends
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+}
+}  // namespace
+
+struct DxArgs {
+    const uint16_t *dgu, *dgu_sh;  // [da | du] rows: [T k, 2F], [T, 2Fs]
+    const uint16_t *w, *w_sh;      // W_gu [E, 2F, d], [2Fs, d]
+    uint16_t *dxp, *dxs;           // [T k, d], [T, d]
+    const int32_t *counts, *offsets, *tile_start, *tile_group;
+    int64_t T;
+    int d, E, F, Fs;
+    int nm, nn, gm;
+};
+
+__global__ __launch_bounds__(512, 1) void bwd_dx_dma_kernel(DxArgs a) {
+    using G = Geo<128, 64>;
+    __shared__ __align__(1024) unsigned char st0[G::STB];
+    __shared__ __align__(1024) unsigned char st1[G::STB];
+    __shared__ __align__(1024) unsigned char st2[G::STB];
+    int mt, nt;
+    if (!raster_tile(a.nm, a.nn, a.gm, mt, nt)) return;
+    if (mt >= a.tile_start[a.E + 1]) return;
+    const int g = a.tile_group[mt];
+    const bool shared = g == a.E;
+    const int m_local = (mt - a.tile_start[g]) * 128;
+    int row0, nrows;
+    if (!shared) {
+        row0 = a.offsets[g] + m_local;
+        nrows = min(128, a.counts[g] - m_local);
+    } else {
+        row0 = m_local;
+        nrows = (int)min<int64_t>(128, a.T - m_local);
+    }
+    const int Fg = shared ? a.Fs : a.F;
+    const int K = 2 * Fg;
+    const int n0 = nt * BN;
+    if (n0 >= a.d) return;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const uint16_t *abase = shared ? a.dgu_sh : a.dgu;
+    const uint16_t *wbase = shared ? a.w_sh : a.w + (int64_t)g * 2 * a.F * a.d;
+    uint32_t aoff[G::AL], boff[G::BL];
+#pragma unroll
+    for (int j = 0; j < G::AL; ++j) {
+        const int R = (G::AL * wave + j) * G::RPL + lane / G::CH;
+        const int c = (lane % G::CH) ^ swz<64>(R);
+        aoff[j] = (uint32_t)(row0 + min(R, nrows - 1)) * (uint32_t)K + 8 * c;
+    }
+#pragma unroll
+    for (int j = 0; j < G::BL; ++j) {
+        // K row kr of the stage, physical chunk p: logical chunk p ^ swizzle;
+        // columns past d read the last full chunk (never stored)
+        const int kr = 2 * (G::BL * wave + j) + (lane >> 5);
+        const int col = min(n0 + 8 * ((lane & 31) ^ mc_swz(kr)), a.d - 8);
+        boff[j] = (uint32_t)kr * (uint32_t)a.d + (uint32_t)col;
+    }
+    const int wm = wave >> 1, wn = wave & 1, fr = lane & 31;
+    int brow[NB];
+#pragma unroll
+    for (int ni = 0; ni < NB; ++ni) brow[ni] = 128 * wn + 32 * ni;
+    const int mact = nrows > 32 * wm ? 1 : 0;  // this wave's 32 rows hold data
+    f32x16 acc[1][NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[0][j][v] = 0.f;
+    Stages<3> st;
+    st.s[0] = st0;
+    st.s[1] = st1;
+    st.s[2] = st2;
+    if (mact)
+        k_loop_mc<1>(st, abase, wbase, aoff, boff, (uint32_t)a.d, K / 64, wave, wm, brow, fr, lane, acc);
+    else
+        k_loop_mc<0>(st, abase, wbase, aoff, boff, (uint32_t)a.d, K / 64, wave, wm, brow, fr, lane, acc);
+    // lane holds row 32 wm + lane % 32 and, in acc[0][ni][4 q + i], column
+    // brow[ni] + 8 q + 4 (lane / 32) + i
+    const int row = 32 * wm + fr;
+    if (row >= nrows) return;
+    uint16_t *crow = (shared ? a.dxs : a.dxp) + (int64_t)(row0 + row) * a.d + n0 + 4 * (lane >> 5);
+#pragma unroll
+    for (int ni = 0; ni < NB; ++ni)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (n0 + brow[ni] + 8 * q >= a.d) continue;
+            const f32x16 &c4 = acc[0][ni];
+            uint2 v;
+            v.x = pack_bf16x2(c4[4 * q], c4[4 * q + 1]);
+            v.y = pack_bf16x2(c4[4 * q + 2], c4[4 * q + 3]);
+            *reinterpret_cast<uint2 *>(crow + brow[ni] + 8 * q) = v;
+        }
+}
+
+bool bwd_dx_dma_ok(const BwdArgs &a) {
+    if (!a.bf16 || a.F % 128 || a.Fs % 128 || a.d % 128) return false;
+    const int64_t rows = a.T * a.k;
+    const int64_t wide = 2 * (int64_t)(a.F > a.Fs ? a.F : a.Fs);
+    return rows * wide < ((int64_t)1 << 32) && wide * a.d < ((int64_t)1 << 32);
+}
+
+hipError_t launch_bwd_dx_dma(const BwdArgs &b, int max_tiles, hipStream_t s) {
+    DxArgs a;
+    a.dgu = static_cast<const uint16_t *>(b.dgu);
+    a.dgu_sh = static_cast<const uint16_t *>(b.dgu_sh);
+    a.w = static_cast<const uint16_t *>(b.w_gu);
+    a.w_sh = static_cast<const uint16_t *>(b.w_sgu);
+    a.dxp = static_cast<uint16_t *>(b.dxp);
+    a.dxs = static_cast<uint16_t *>(b.dxs);
+    a.counts = b.counts;
+    a.offsets = b.offsets;
+    a.tile_start = b.tile_start;
+    a.tile_group = b.tile_group;
+    a.T = b.T;
+    a.d = b.d;
+    a.E = b.E;
+    a.F = b.F;
+    a.Fs = b.Fs;
+    a.nm = max_tiles;
+    a.nn = (b.d + BN - 1) / BN;
+    a.gm = -1;  // M-tile m on XCD m % 8 (its N-tiles share A through one L2)
+    hipLaunchKernelGGL(bwd_dx_dma_kernel, dim3(raster_blocks(a.nm, a.nn, a.gm)), dim3(512), 0, s, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_experts_dma(const Problem &p, int bm, hipStream_t s,
                               const std::function<void(int)> &mark) {
     GemmArgs a;

@@ -203,13 +203,10 @@ __global__ __launch_bounds__(256) void router_select_kernel(
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= ntok) return;
-    select_topk<NV>(logits + t * (E + 1), E, k, lane, topk_idx + t * k, topk_w + t * k,
-                    has_gate ? gate + t : nullptr, has_gate && gate_user ? gate_user + t : nullptr,
-                    nullptr);
-    if (touch && lane < k) {
-        const int e = topk_idx[t * k + lane];  // written by this lane above
-        if (atomicOr(&touch[e], 1) == 0) tlist[atomicAdd(&touch[E], 1)] = e;
-    }
+    const int e = select_topk<NV>(logits + t * (E + 1), E, k, lane, topk_idx + t * k,
+                                  topk_w + t * k, has_gate ? gate + t : nullptr,
+                                  has_gate && gate_user ? gate_user + t : nullptr, nullptr);
+    if (touch && lane < k && atomicOr(&touch[e], 1) == 0) tlist[atomicAdd(&touch[E], 1)] = e;
 }
 
 // Exact canonical logit for the token whose 512-chunk slices this wave holds

@@ -37,15 +37,17 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
 // holds the logits of experts L, L+64, ..., so a lane's candidates are
 // already in ascending expert order.  Writes idx[0..k) (descending logit),
 // w[0..k), and *gate_t / *gate_user_t (when non-null) = sigmoid(l[E]);
-// idx_copy (non-null) receives idx too.
+// idx_copy (non-null) receives idx too.  Returns, in lane j < k, the j-th
+// selected expert.
 template <int NV>
-__device__ __forceinline__ void select_topk(const float *__restrict__ l, int E, int k, int lane,
-                                            int32_t *idx, float *w, float *gate_t,
-                                            float *gate_user_t, int32_t *idx_copy) {
+__device__ __forceinline__ int select_topk(const float *__restrict__ l, int E, int k, int lane,
+                                           int32_t *idx, float *w, float *gate_t,
+                                           float *gate_user_t, int32_t *idx_copy) {
 #pragma clang fp contract(off)
     // Candidates still in play hold their logit; taken ones (and padding
     // past E) hold NaN, which fmaxf skips and == never matches.  NaN logits
-    // are read as -inf first, so NaN marks only "not a candidate".
+    // are read as -inf first, so NaN marks only "not a candidate".  The gate
+    // logit goes out with the others.
     float v[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -53,6 +55,7 @@ __device__ __forceinline__ void select_topk(const float *__restrict__ l, int E, 
         const float val = e < E ? l[e] : __builtin_nanf("");
         v[i] = e < E && val != val ? -INFINITY : val;
     }
+    const float lg = gate_t ? l[E] : 0.0f;
 
     float my_l = 0.0f;
     int my_e = 0;
@@ -90,10 +93,11 @@ __device__ __forceinline__ void select_topk(const float *__restrict__ l, int E, 
         if (idx_copy) idx_copy[lane] = my_e;
     }
     if (gate_t && lane == 0) {
-        const float s = 1.0f / (1.0f + expf(-l[E]));
+        const float s = 1.0f / (1.0f + expf(-lg));
         *gate_t = s;
         if (gate_user_t) *gate_user_t = s;
     }
+    return my_e;
 }
 
 }  // namespace moe
