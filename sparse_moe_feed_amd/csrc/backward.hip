@@ -1048,7 +1048,15 @@ hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
     launch_gemm<K_LOGITS>(a, cdiv(a.T, QB), cdiv(a.E + 1, QB), s);
     mark(1);
     if (!a.au_given) launch_gemm<K_AU>(a, tiles, cdiv(2 * Fmax, QB), s);
-    launch_gemm<K_G>(a, tiles, cdiv(Fmax, QB), s);
+    // the dX rows of the shared expert (dxs, [T, d] bf16) are written only
+    // after G, so G's bf16 copy of dOut lives there until then
+    const bool dma = bwd_dma_ok(a);
+    if (dma) {
+        err = launch_bwd_g_dma(a, (int)tiles, a.dxs, s);
+        if (err != hipSuccess) return err;
+    } else {
+        launch_gemm<K_G>(a, tiles, cdiv(Fmax, QB), s);
+    }
     mark(2);
     const int64_t rows = (int64_t)a.T * a.k + (a.Fs > 0 ? a.T : 0);
     const size_t lds = (size_t)a.ldd * sizeof(float);
@@ -1060,7 +1068,7 @@ hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
         hipLaunchKernelGGL(router_bwd_kernel<float>, dim3((unsigned)a.T), dim3(256), lds, s, a);
     }
     mark(3);
-    if (bwd_dx_dma_ok(a)) {
+    if (dma) {
         err = launch_bwd_dx_dma(a, (int)tiles, s);
         if (err != hipSuccess) return err;
     } else {

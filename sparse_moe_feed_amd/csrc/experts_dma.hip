@@ -483,16 +483,15 @@ __global__ __launch_bounds__((64 * Geo<BM, BK>::NW), (NS * Geo<BM, BK>::STB <= 8
 }
 
 // ---------------------------------------------------------------------------
-// Backward: dx of each routed row and of the shared expert's rows,
-// dX = [da | du] W_gu (the transpose of the forward's gate/up product; the
-// backward's 128-row tile map), on the 128 x 256 tiles above (K = 2 F in
-// steps of 64, three direct-to-LDS stages, 8 waves).  A ([da | du] rows,
-// contiguous along K) is staged as the forward's A.  B = W_gu runs along the
-// output axis, so each K step's 64 rows of 256 columns (512 bytes) go to LDS
-// as loaded, two rows per 1 KB load, with the 16-byte chunks of row k
-// permuted by chunk ^ 2 (k & 3); the MFMA fragments are read with
-// ds_read_b64_tr_b16, and the four rows one 16-lane read phase touches then
-// sit on disjoint bank groups.
+// Backward products whose weight operand runs along the output axis (dX of
+// the rows, [da | du] W_gu, and G = dOut W_dn; the backward's 128-row tile
+// map), on the 128 x 256 tiles above (K in steps of 64, three direct-to-LDS
+// stages, 8 waves).  A (rows contiguous along K) is staged as the forward's
+// A.  Each K step's 64 weight rows of 256 columns (512 bytes) go to LDS as
+// loaded, two rows per 1 KB load, with the 16-byte chunks of row k permuted
+// by chunk ^ 2 (k & 3); the MFMA fragments are read with ds_read_b64_tr_b16,
+// and the four rows one 16-lane read phase touches then sit on disjoint bank
+// groups.
 namespace {
 constexpr int MC_ROWB = BN * 2;  // bytes per staged B row (one K index)
 __device__ __forceinline__ int mc_swz(int k) { return 2 * (k & 3); }
@@ -628,17 +627,24 @@ __device__ __forceinline__ void k_loop_mc(const Stages<3> &st, const uint16_t *a
 }
 }  // namespace
 
-struct DxArgs {
-    const uint16_t *dgu, *dgu_sh;  // [da | du] rows: [T k, 2F], [T, 2Fs]
-    const uint16_t *w, *w_sh;      // W_gu [E, 2F, d], [2Fs, d]
-    uint16_t *dxp, *dxs;           // [T k, d], [T, d]
-    const int32_t *counts, *offsets, *tile_start, *tile_group;
+// The two backward products on these tiles (B runs along the output axis):
+//   BWD_DX: dX rows = [da | du] W_gu   (A: [da | du] rows, K = 2 Fg; bf16 out, N = d)
+//   BWD_G:  G rows  = dOut W_dn        (A: the rows' tokens of dOut, rounded to
+//           bf16 beforehand, K = d; binary32 out, N = Fg)
+enum { BWD_DX = 0, BWD_G = 1 };
+
+struct BwdTileArgs {
+    const uint16_t *a, *a_sh;      // DX: [da | du] [T k, 2F], [T, 2Fs]; G: dOut bf16 [T, d]
+    const uint16_t *w, *w_sh;      // DX: W_gu [E, 2F, d], [2Fs, d]; G: W_dn [E, d, F], [d, Fs]
+    void *c, *c_sh;                // DX: dX rows bf16 [T k, d], [T, d]; G: binary32 [T k, F], [T, Fs]
+    const int32_t *perm, *counts, *offsets, *tile_start, *tile_group;
     int64_t T;
-    int d, E, F, Fs;
+    int d, E, k, F, Fs;
     int nm, nn, gm;
 };
 
-__global__ __launch_bounds__(512, 1) void bwd_dx_dma_kernel(DxArgs a) {
+template <int KIND>
+__global__ __launch_bounds__(512, 1) void bwd_mc_dma_kernel(BwdTileArgs a) {
     using G = Geo<128, 64>;
     __shared__ __align__(1024) unsigned char st0[G::STB];
     __shared__ __align__(1024) unsigned char st1[G::STB];
@@ -658,27 +664,31 @@ __global__ __launch_bounds__(512, 1) void bwd_dx_dma_kernel(DxArgs a) {
         nrows = (int)min<int64_t>(128, a.T - m_local);
     }
     const int Fg = shared ? a.Fs : a.F;
-    const int K = 2 * Fg;
+    const int K = KIND == BWD_DX ? 2 * Fg : a.d;
+    const int N = KIND == BWD_DX ? a.d : Fg;
     const int n0 = nt * BN;
-    if (n0 >= a.d) return;
+    if (n0 >= N) return;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-    const uint16_t *abase = shared ? a.dgu_sh : a.dgu;
-    const uint16_t *wbase = shared ? a.w_sh : a.w + (int64_t)g * 2 * a.F * a.d;
+    const uint16_t *abase = shared ? a.a_sh : a.a;
+    const uint16_t *wbase = shared ? a.w_sh : a.w + (int64_t)g * (KIND == BWD_DX ? 2 * a.F : a.F) * a.d;
     uint32_t aoff[G::AL], boff[G::BL];
 #pragma unroll
     for (int j = 0; j < G::AL; ++j) {
         const int R = (G::AL * wave + j) * G::RPL + lane / G::CH;
         const int c = (lane % G::CH) ^ swz<64>(R);
-        aoff[j] = (uint32_t)(row0 + min(R, nrows - 1)) * (uint32_t)K + 8 * c;
+        const int r = row0 + min(R, nrows - 1);  // padding rows repeat the last row
+        // G: the row's token (routed rows through the permutation)
+        const int src = KIND == BWD_DX || shared ? r : a.perm[r] / a.k;
+        aoff[j] = (uint32_t)src * (uint32_t)K + 8 * c;
     }
 #pragma unroll
     for (int j = 0; j < G::BL; ++j) {
         // K row kr of the stage, physical chunk p: logical chunk p ^ swizzle;
-        // columns past d read the last full chunk (never stored)
+        // columns past N read the last full chunk (never stored)
         const int kr = 2 * (G::BL * wave + j) + (lane >> 5);
-        const int col = min(n0 + 8 * ((lane & 31) ^ mc_swz(kr)), a.d - 8);
-        boff[j] = (uint32_t)kr * (uint32_t)a.d + (uint32_t)col;
+        const int col = min(n0 + 8 * ((lane & 31) ^ mc_swz(kr)), N - 8);
+        boff[j] = (uint32_t)kr * (uint32_t)N + (uint32_t)col;
     }
     const int wm = wave >> 1, wn = wave & 1, fr = lane & 31;
     int brow[NB];
@@ -695,42 +705,61 @@ __global__ __launch_bounds__(512, 1) void bwd_dx_dma_kernel(DxArgs a) {
     st.s[1] = st1;
     st.s[2] = st2;
     if (mact)
-        k_loop_mc<1>(st, abase, wbase, aoff, boff, (uint32_t)a.d, K / 64, wave, wm, brow, fr, lane, acc);
+        k_loop_mc<1>(st, abase, wbase, aoff, boff, (uint32_t)N, K / 64, wave, wm, brow, fr, lane, acc);
     else
-        k_loop_mc<0>(st, abase, wbase, aoff, boff, (uint32_t)a.d, K / 64, wave, wm, brow, fr, lane, acc);
+        k_loop_mc<0>(st, abase, wbase, aoff, boff, (uint32_t)N, K / 64, wave, wm, brow, fr, lane, acc);
     // lane holds row 32 wm + lane % 32 and, in acc[0][ni][4 q + i], column
     // brow[ni] + 8 q + 4 (lane / 32) + i
     const int row = 32 * wm + fr;
     if (row >= nrows) return;
-    uint16_t *crow = (shared ? a.dxs : a.dxp) + (int64_t)(row0 + row) * a.d + n0 + 4 * (lane >> 5);
+    const int64_t cbase = (int64_t)(row0 + row) * N + n0 + 4 * (lane >> 5);
 #pragma unroll
     for (int ni = 0; ni < NB; ++ni)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            if (n0 + brow[ni] + 8 * q >= a.d) continue;
+            if (n0 + brow[ni] + 8 * q >= N) continue;
             const f32x16 &c4 = acc[0][ni];
-            uint2 v;
-            v.x = pack_bf16x2(c4[4 * q], c4[4 * q + 1]);
-            v.y = pack_bf16x2(c4[4 * q + 2], c4[4 * q + 3]);
-            *reinterpret_cast<uint2 *>(crow + brow[ni] + 8 * q) = v;
+            if (KIND == BWD_DX) {
+                uint2 v;
+                v.x = pack_bf16x2(c4[4 * q], c4[4 * q + 1]);
+                v.y = pack_bf16x2(c4[4 * q + 2], c4[4 * q + 3]);
+                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(shared ? a.c_sh : a.c) + cbase +
+                                           brow[ni] + 8 * q) = v;
+            } else {
+                *reinterpret_cast<float4 *>(static_cast<float *>(shared ? a.c_sh : a.c) + cbase +
+                                            brow[ni] + 8 * q) =
+                    make_float4(c4[4 * q], c4[4 * q + 1], c4[4 * q + 2], c4[4 * q + 3]);
+            }
         }
 }
 
-bool bwd_dx_dma_ok(const BwdArgs &a) {
+// dOut rounded to bf16 (nearest even, as the generic kernel rounds it when
+// staging), n a multiple of 8.
+__global__ __launch_bounds__(256) void round_bf16_kernel(const float *__restrict__ src,
+                                                         uint16_t *__restrict__ dst, int64_t n) {
+    const int64_t i = 8 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
+    if (i >= n) return;
+    const float4 lo = *reinterpret_cast<const float4 *>(src + i);
+    const float4 hi = *reinterpret_cast<const float4 *>(src + i + 4);
+    uint4 v;
+    v.x = pack_bf16x2(lo.x, lo.y);
+    v.y = pack_bf16x2(lo.z, lo.w);
+    v.z = pack_bf16x2(hi.x, hi.y);
+    v.w = pack_bf16x2(hi.z, hi.w);
+    *reinterpret_cast<uint4 *>(dst + i) = v;
+}
+
+bool bwd_dma_ok(const BwdArgs &a) {
     if (!a.bf16 || a.F % 128 || a.Fs % 128 || a.d % 128) return false;
     const int64_t rows = a.T * a.k;
     const int64_t wide = 2 * (int64_t)(a.F > a.Fs ? a.F : a.Fs);
-    return rows * wide < ((int64_t)1 << 32) && wide * a.d < ((int64_t)1 << 32);
+    return rows * wide < ((int64_t)1 << 32) && wide * a.d < ((int64_t)1 << 32) &&
+           a.T * a.d < ((int64_t)1 << 32);
 }
 
-hipError_t launch_bwd_dx_dma(const BwdArgs &b, int max_tiles, hipStream_t s) {
-    DxArgs a;
-    a.dgu = static_cast<const uint16_t *>(b.dgu);
-    a.dgu_sh = static_cast<const uint16_t *>(b.dgu_sh);
-    a.w = static_cast<const uint16_t *>(b.w_gu);
-    a.w_sh = static_cast<const uint16_t *>(b.w_sgu);
-    a.dxp = static_cast<uint16_t *>(b.dxp);
-    a.dxs = static_cast<uint16_t *>(b.dxs);
+static BwdTileArgs bwd_tile_args(const BwdArgs &b, int max_tiles) {
+    BwdTileArgs a;
+    a.perm = b.perm;
     a.counts = b.counts;
     a.offsets = b.offsets;
     a.tile_start = b.tile_start;
@@ -738,12 +767,43 @@ hipError_t launch_bwd_dx_dma(const BwdArgs &b, int max_tiles, hipStream_t s) {
     a.T = b.T;
     a.d = b.d;
     a.E = b.E;
+    a.k = b.k;
     a.F = b.F;
     a.Fs = b.Fs;
     a.nm = max_tiles;
-    a.nn = (b.d + BN - 1) / BN;
     a.gm = -1;  // M-tile m on XCD m % 8 (its N-tiles share A through one L2)
-    hipLaunchKernelGGL(bwd_dx_dma_kernel, dim3(raster_blocks(a.nm, a.nn, a.gm)), dim3(512), 0, s, a);
+    return a;
+}
+
+hipError_t launch_bwd_dx_dma(const BwdArgs &b, int max_tiles, hipStream_t s) {
+    BwdTileArgs a = bwd_tile_args(b, max_tiles);
+    a.a = static_cast<const uint16_t *>(b.dgu);
+    a.a_sh = static_cast<const uint16_t *>(b.dgu_sh);
+    a.w = static_cast<const uint16_t *>(b.w_gu);
+    a.w_sh = static_cast<const uint16_t *>(b.w_sgu);
+    a.c = b.dxp;
+    a.c_sh = b.dxs;
+    a.nn = (b.d + BN - 1) / BN;
+    hipLaunchKernelGGL(bwd_mc_dma_kernel<BWD_DX>, dim3(raster_blocks(a.nm, a.nn, a.gm)), dim3(512), 0,
+                       s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_g_dma(const BwdArgs &b, int max_tiles, void *dout_bf16, hipStream_t s) {
+    const int64_t n = b.T * b.d;  // d % 128 == 0
+    hipLaunchKernelGGL(round_bf16_kernel, dim3((unsigned)((n / 8 + 255) / 256)), dim3(256), 0, s,
+                       b.dout, static_cast<uint16_t *>(dout_bf16), n);
+    BwdTileArgs a = bwd_tile_args(b, max_tiles);
+    a.a = static_cast<const uint16_t *>(dout_bf16);
+    a.a_sh = a.a;
+    a.w = static_cast<const uint16_t *>(b.w_dn);
+    a.w_sh = static_cast<const uint16_t *>(b.w_sdn);
+    a.c = b.g;
+    a.c_sh = b.g_sh;
+    const int fmax = b.F > b.Fs ? b.F : b.Fs;
+    a.nn = (fmax + BN - 1) / BN;
+    hipLaunchKernelGGL(bwd_mc_dma_kernel<BWD_G>, dim3(raster_blocks(a.nm, a.nn, a.gm)), dim3(512), 0,
+                       s, a);
     return hipGetLastError();
 }
 

@@ -205,10 +205,12 @@ inline int bwd_sh_chunk(int64_t T, int split) {
 // backward, 4 dX, 5 dW_gu, 6 dW_dn, 7 router GEMMs, combine and loss.
 hipError_t launch_backward(const Problem &p, const BwdArgs &a, hipStream_t s,
                            const std::function<void(int)> &mark);
-// dX of the routed and shared rows ([da | du] W_gu) on direct-to-LDS tiles:
-// bf16 layers with F, Fs and d multiples of 128 and 32-bit element offsets.
-bool bwd_dx_dma_ok(const BwdArgs &a);
+// dX of the routed and shared rows ([da | du] W_gu) and G (dOut W_dn) on
+// direct-to-LDS tiles: bf16 layers with F, Fs and d multiples of 128 and
+// 32-bit element offsets.  G first rounds dOut to bf16 into dout_bf16 [T, d].
+bool bwd_dma_ok(const BwdArgs &a);
 hipError_t launch_bwd_dx_dma(const BwdArgs &a, int max_tiles, hipStream_t s);
+hipError_t launch_bwd_g_dma(const BwdArgs &a, int max_tiles, void *dout_bf16, hipStream_t s);
 // Row-major MXFP4 [rows, K] (codes, scales) -> packed tiles (rows % 16 == 0,
 // K % 128 == 0).
 hipError_t launch_mx4_pack(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t K,
