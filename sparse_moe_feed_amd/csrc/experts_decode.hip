@@ -173,8 +173,9 @@ constexpr int kScanChunks = DBM * 32 / 64;  // 64-pair chunks of topk_idx at T <
 
 // Direct tiles (T <= DBM, so an expert has at most DBM pairs when the top-k
 // experts of a token are distinct): the router listed the n touched experts
-// (counts[E] = n, tile_group[0..n) = the experts); block x < n serves expert
-// tile_group[x], block n the shared expert (if any), later blocks end.
+// (counts[E] = n, tile_group[0..n) = the experts); block 0 serves the shared
+// expert (if any; its tile has all T rows, so it starts first), the next n
+// blocks expert tile_group[x], later blocks end.
 // decode_tile finds the group (and, with the permutation, the rows); for a
 // direct routed tile the rows come from tile_rows, after the block has its
 // first weight loads in flight.
@@ -185,9 +186,10 @@ __device__ __forceinline__ bool decode_tile(const Args &a, TileInfo &ti, int til
     if (a.direct) {
         const int nt = a.counts[a.E];
         const int x = tile;
-        if (x > nt || (x == nt && a.Fs == 0)) return false;
-        ti.shared = x == nt;
-        ti.g = ti.shared ? a.E : a.tile_group[x];
+        const int sh = a.Fs > 0 ? 1 : 0;
+        if (x >= nt + sh) return false;
+        ti.shared = sh && x == 0;
+        ti.g = ti.shared ? a.E : a.tile_group[x - sh];
         ti.nrows = ti.shared ? (int)a.T : 0;  // routed: tile_rows
         return true;
     }

@@ -53,9 +53,9 @@ struct Problem {
     // weight-streaming path without the permutation step (T <= kDecodeBM,
     // routing from this library's exact router): the router's select step
     // lists the touched experts (counts[e] = 1 once e is selected, counts[E]
-    // = how many, tile_group[i] = the i-th in arrival order); block x serves
-    // expert tile_group[x] (x = counts[E]: the shared expert), finds its pairs
-    // in topk_idx, and h / y rows are indexed by pair id t*k+j
+    // = how many, tile_group[i] = the i-th in arrival order); block 0 serves
+    // the shared expert (if any), the next blocks expert tile_group[x], each
+    // finding its pairs in topk_idx, and h / y rows are indexed by pair id t*k+j
     bool direct;
     // MXFP4 expert weights: w_gate_up, w_down, w_sh_gate_up, w_sh_down are
     // then packed MXFP4 tensors (16 x 128 tiles of codes and scales)
