@@ -591,10 +591,24 @@ __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(BwdArgs a, int nx, int
     __shared__ __align__(16) uint16_t Bs[2][TILE_E];
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int wm = wave >> 1, wn = wave & 1;
+    // Weight gradients after the short-reduction kernel: when no routed
+    // expert has more than dw_kmin rows, only the shared expert's groups
+    // (E .. , after the routed ones in the virtual order) have work, so the
+    // walk starts at their first virtual block instead of looking at every
+    // routed tile.
+    int b0 = blockIdx.x;
+    if ((KIND == K_DWGU || KIND == K_DWDN) && a.dw_kmin >= 0) {
+        bool big = false;
+        for (int g = tid; g < a.E; g += 256) big |= a.counts[g] > a.dw_kmin;
+        if (!__syncthreads_or(big)) {
+            const int per = (nx / groups) * ny;  // virtual blocks per group
+            b0 += 8 * per * (a.E / 8);
+        }
+    }
     // grid-stride over the virtual blocks (the grid is a multiple of 8, so a
     // block keeps its XCD's share of the tile map); tiles with nothing to do
     // cost one look at the tile map instead of a block launch each
-    for (int b = blockIdx.x; b < nvirt; b += gridDim.x) {
+    for (int b = b0; b < nvirt; b += gridDim.x) {
         Job j;
         int bx, by;
         if (!block_tile<KIND>(b, nx, ny, groups, bx, by) || !make_job<KIND>(a, bx, by, 2, j))
