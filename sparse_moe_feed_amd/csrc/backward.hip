@@ -44,6 +44,8 @@
 
 #include <limits.h>
 
+#include <algorithm>
+
 namespace moe {
 
 enum BwdKind { K_LOGITS, K_AU, K_G, K_DX, K_DWGU, K_DWDN, K_DWR, K_DXR };
@@ -186,16 +188,25 @@ __device__ bool make_job(const BwdArgs &a, int bx, int by, int es, Job &j) {
     j.c_alt_p = nullptr;
     j.c_f32 = false;
     if (KIND == K_LOGITS || KIND == K_DXR || KIND == K_DWR) {
-        const int m0 = QB * bx, n0 = QB * by;
+        int m0 = QB * bx, n0 = QB * by;
         if (KIND == K_LOGITS) {
+            // column tiles of K slice sl follow those of slice sl - 1
+            const int ntn = (E + sh_rows + QB - 1) / QB;
+            const int sl = by / ntn;
+            if (sl >= a.logit_split) return false;
+            n0 = QB * (by - sl * ntn);
+            const int ks = d / a.logit_split;
             j.mrows = (int)min<int64_t>(QB, a.T - m0);
             j.ncols = min(QB, E + sh_rows - n0);
-            j.K = d;
+            j.K = ks;
             j.a = opnd(a.x, d, m0, (int)a.T, es);
             j.b = opnd(a.w_router, d, n0, E + sh_rows, es);
             j.b.alt = E;
             j.b.p_alt = static_cast<const char *>(a.sh_gate ? a.sh_gate : a.w_router);
-            j.c = reinterpret_cast<char *>(a.logits + (int64_t)m0 * a.ldl + n0);
+            j.a.p += (int64_t)sl * ks * es;  // rows start at the slice's first element
+            j.b.p += (int64_t)sl * ks * es;
+            j.b.p_alt += (int64_t)sl * ks * es;
+            j.c = reinterpret_cast<char *>(a.logits + (int64_t)sl * a.T * a.ldl + (int64_t)m0 * a.ldl + n0);
             j.ldc = (int64_t)a.ldl * 4;
         } else if (KIND == K_DXR) {
             j.mrows = (int)min<int64_t>(QB, a.T - m0);
@@ -210,20 +221,35 @@ __device__ bool make_job(const BwdArgs &a, int bx, int by, int es, Job &j) {
             j.c = reinterpret_cast<char *>(a.dxr + (int64_t)m0 * d + n0);
             j.ldc = (int64_t)d * 4;
         } else {  // K_DWR
+            // with dwr_split > 1, column tiles of token chunk sl follow those
+            // of chunk sl - 1, and each chunk writes a binary32 partial
+            const int ntn = (d + QB - 1) / QB;
+            const int sl = by / ntn;
+            if (sl >= a.dwr_split) return false;
+            n0 = QB * (by - sl * ntn);
+            const int chunk = (int)((a.T + a.dwr_split - 1) / a.dwr_split);
+            const int rb = sl * chunk, re = (int)min<int64_t>(a.T, (int64_t)rb + chunk);
+            if (re <= rb) return false;
             j.mrows = min(QB, E + sh_rows - m0);
             j.ncols = min(QB, d - n0);
-            j.K = (int)a.T;
-            j.a = opnd(a.dl, a.ldd, 0, (int)a.T, es);
+            j.K = re - rb;
+            j.a = opnd(a.dl, a.ldd, rb, re, es);
             j.a.cb = m0;
             j.a.ilim = min(QB, E + 1 - m0);
-            j.b = opnd(a.x, d, 0, (int)a.T, es);
+            j.b = opnd(a.x, d, rb, re, es);
             j.b.cb = n0;
             j.b.ilim = j.ncols;
-            j.c = static_cast<char *>(a.dw_router) + ((int64_t)m0 * d + n0) * es;
-            j.ldc = (int64_t)d * es;
-            if (a.dsh_gate) {
-                j.c_alt = E - m0;
-                j.c_alt_p = static_cast<char *>(a.dsh_gate) + (int64_t)n0 * es;
+            if (a.dwr_split > 1) {
+                j.c = reinterpret_cast<char *>(a.part + ((int64_t)sl * (E + sh_rows) + m0) * d + n0);
+                j.ldc = (int64_t)d * 4;
+                j.c_f32 = true;
+            } else {
+                j.c = static_cast<char *>(a.dw_router) + ((int64_t)m0 * d + n0) * es;
+                j.ldc = (int64_t)d * es;
+                if (a.dsh_gate) {
+                    j.c_alt = E - m0;
+                    j.c_alt_p = static_cast<char *>(a.dsh_gate) + (int64_t)n0 * es;
+                }
             }
         }
         return j.mrows > 0 && j.ncols > 0;
@@ -838,7 +864,8 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(BwdArgs a) {
     } else {
         if (a.Fs == 0 || r - routed >= a.T) return;
         row = r - routed;
-        const float z = a.logits[row * a.ldl + a.E];
+        float z = a.logits[row * a.ldl + a.E];
+        for (int sl = 1; sl < a.logit_split; ++sl) z += a.logits[(sl * a.T + row) * a.ldl + a.E];
         w = 1.0f / (1.0f + __expf(-z));
         Fg = a.Fs;
         if (lane == 0) a.gate[row] = w;
@@ -898,10 +925,17 @@ __device__ __forceinline__ float block_max(float v, float *red) {
 // to ldd columns (layer dtype).
 template <typename Tv>
 __global__ __launch_bounds__(256) void router_bwd_kernel(BwdArgs a) {
-    extern __shared__ float dls[];  // [ldd]
+    extern __shared__ float dls[];  // [ldd], then the token's logits [E + 1]
     __shared__ float red[4];
     const int64_t t = blockIdx.x;
-    const float *l = a.logits + t * a.ldl;
+    // the token's logits: the sum of the K slices' partials
+    float *l = dls + a.ldd;
+    for (int e = threadIdx.x; e <= a.E; e += 256) {
+        float v = a.logits[t * a.ldl + e];
+        for (int sl = 1; sl < a.logit_split; ++sl) v += a.logits[(sl * a.T + t) * a.ldl + e];
+        l[e] = v;
+    }
+    __syncthreads();
     const float inv_pairs = 1.0f / (float)((int64_t)a.T * a.k);
     float m = -INFINITY;
     for (int e = threadIdx.x; e < a.E; e += 256)
@@ -1031,6 +1065,32 @@ static void launch_gemm(const BwdArgs &a, unsigned nx, unsigned ny, hipStream_t 
                            (int)ny, groups, (int)nvirt);
 }
 
+// dW_router (rows 0 .. E-1) and the shared gate's gradient (row E, when a
+// shared expert exists and its output is given) from the token chunks'
+// binary32 partials [S, rows, d]: summed in chunk order, rounded to bf16.
+__global__ __launch_bounds__(256) void dwr_reduce_kernel(const float *__restrict__ part, int S,
+                                                         int E, int d, int rows,
+                                                         uint16_t *__restrict__ dw_router,
+                                                         uint16_t *__restrict__ dsh_gate) {
+    const int64_t n = (int64_t)rows * d;
+    const int64_t i = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
+    if (i >= n) return;
+    float4 acc = *reinterpret_cast<const float4 *>(part + i);
+    for (int sp = 1; sp < S; ++sp) {
+        const float4 v = *reinterpret_cast<const float4 *>(part + (int64_t)sp * n + i);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+    }
+    uint2 q;
+    q.x = pack_bf16x2(acc.x, acc.y);
+    q.y = pack_bf16x2(acc.z, acc.w);
+    // d % 4 == 0: the four values share a row
+    if (i < (int64_t)E * d) *reinterpret_cast<uint2 *>(dw_router + i) = q;
+    else if (dsh_gate) *reinterpret_cast<uint2 *>(dsh_gate + (i - (int64_t)E * d)) = q;
+}
+
 // Shared expert's weight gradient from its split reduction: out = the sum of
 // the S binary32 partials in chunk order, rounded to bf16.
 __global__ __launch_bounds__(256) void sh_reduce_kernel(const float *__restrict__ part, int S,
@@ -1059,7 +1119,7 @@ hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
     if (err != hipSuccess) return err;
     const int Fmax = a.F > a.Fs ? a.F : a.Fs;
     const unsigned tiles = (unsigned)pp.max_tiles;
-    launch_gemm<K_LOGITS>(a, cdiv(a.T, QB), cdiv(a.E + 1, QB), s);
+    launch_gemm<K_LOGITS>(a, cdiv(a.T, QB), cdiv(a.E + 1, QB) * a.logit_split, s);
     mark(1);
     if (!a.au_given) launch_gemm<K_AU>(a, tiles, cdiv(2 * Fmax, QB), s);
     // the dX rows of the shared expert (dxs, [T, d] bf16) are written only
@@ -1073,7 +1133,7 @@ hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
     }
     mark(2);
     const int64_t rows = (int64_t)a.T * a.k + (a.Fs > 0 ? a.T : 0);
-    const size_t lds = (size_t)a.ldd * sizeof(float);
+    const size_t lds = (size_t)(a.ldd + a.E + 1) * sizeof(float);
     if (a.bf16) {
         hipLaunchKernelGGL(swiglu_bwd_kernel<uint16_t>, dim3(cdiv(rows, 4)), dim3(256), 0, s, a);
         hipLaunchKernelGGL(router_bwd_kernel<uint16_t>, dim3((unsigned)a.T), dim3(256), lds, s, a);
@@ -1122,7 +1182,23 @@ hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
                            a.sh_split, n, static_cast<uint16_t *>(a.dw_sdn));
     }
     mark(6);
-    launch_gemm<K_DWR>(a, cdiv(a.E + 1, QB), cdiv(a.d, QB), s);
+    // dW_router reduces over all T tokens on few tiles: at larger T in token
+    // chunks, their binary32 partials in part (free again: its last reader ran)
+    BwdArgs ar = a;
+    ar.dwr_split = 1;
+    const int rrows = a.E + (a.Fs > 0 ? 1 : 0);  // router rows (row E: the shared gate)
+    if (a.bf16 && a.T >= 1024 && a.d % 4 == 0 && a.sh_split > 0) {
+        const int64_t cap = (int64_t)a.sh_split * 2 * a.Fs;  // rows of d binary32 in part
+        ar.dwr_split = (int)std::min<int64_t>(4, cap / (a.E + 1));
+        if (ar.dwr_split < 2) ar.dwr_split = 1;
+    }
+    launch_gemm<K_DWR>(ar, cdiv(a.E + 1, QB), cdiv(a.d, QB) * ar.dwr_split, s);
+    if (ar.dwr_split > 1) {
+        const int64_t n = (int64_t)rrows * a.d;
+        hipLaunchKernelGGL(dwr_reduce_kernel, dim3(cdiv(n / 4, 256)), dim3(256), 0, s, a.part,
+                           ar.dwr_split, a.E, a.d, rrows, static_cast<uint16_t *>(a.dw_router),
+                           static_cast<uint16_t *>(a.dsh_gate));
+    }
     launch_gemm<K_DXR>(a, cdiv(a.T, QB), cdiv(a.d, QB), s);
     if (a.bf16)
         hipLaunchKernelGGL(dx_combine_bf16_kernel, dim3((unsigned)a.T, cdiv(a.d / 8, 64)), dim3(64),

@@ -489,12 +489,12 @@ __global__ __launch_bounds__((64 * Geo<BM, BK>::NW), (NS * Geo<BM, BK>::STB <= 8
 // stages, 8 waves).  A (rows contiguous along K) is staged as the forward's
 // A.  Each K step's 64 weight rows of 256 columns (512 bytes) go to LDS as
 // loaded, two rows per 1 KB load, with the 16-byte chunks of row k permuted
-// by chunk ^ 2 (k & 3); the MFMA fragments are read with ds_read_b64_tr_b16,
-// and the four rows one 16-lane read phase touches then sit on disjoint bank
-// groups.
+// by chunk ^ 4 (k & 3); the MFMA fragments are read with ds_read_b64_tr_b16,
+// and the 64 bytes that one read touches in each of four consecutive rows
+// then sit in four different quarters of the 256-byte bank space.
 namespace {
 constexpr int MC_ROWB = BN * 2;  // bytes per staged B row (one K index)
-__device__ __forceinline__ int mc_swz(int k) { return 2 * (k & 3); }
+__device__ __forceinline__ int mc_swz(int k) { return 4 * (k & 3); }
 
 // One stage: A as dma_stage; B rows k0 .. k0 + 63 (element offsets boff of
 // this lane's row and chunk, plus k0 rows of ldb elements).

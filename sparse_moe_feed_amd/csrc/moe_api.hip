@@ -189,7 +189,7 @@ moe::Problem make_problem(const moe_desc &d, int64_t T, const Plan &pl, void *ws
 struct BwdPlan {
     size_t counts, offsets, tile_start, tile_group, blk, rank, perm, logits, au, au_sh, g, g_sh, dgu,
         dgu_sh, hh, hh_sh, dwp, gate, ds, q, dl, dxp, dxs, dxr, part, total;
-    int nblk, max_tiles, ldl, ldd, sh_split, sh_chunk;
+    int nblk, max_tiles, ldl, ldd, sh_split, sh_chunk, logit_split;
 };
 
 BwdPlan make_bwd_plan(const moe_desc &d, int64_t T) {
@@ -214,7 +214,10 @@ BwdPlan make_bwd_plan(const moe_desc &d, int64_t T) {
     p.blk = take((size_t)d.n_experts * p.nblk * 4);
     p.rank = take((size_t)pairs * 4);
     p.perm = take((size_t)pairs * 4);
-    p.logits = take((size_t)T * p.ldl * 4);
+    // the router logits in two K slices at larger T (twice the blocks; the
+    // consumers add the slices)
+    p.logit_split = d.dtype == MOE_BF16 && T >= 1024 && d.d_model % 128 == 0 ? 2 : 1;
+    p.logits = take((size_t)p.logit_split * T * p.ldl * 4);
     p.au = take((size_t)pairs * 2 * F * es);
     p.au_sh = take((size_t)T * 2 * Fs * es);
     p.g = take((size_t)pairs * F * 4);
@@ -757,6 +760,8 @@ moe_status moe_backward(const moe_desc *desc, int64_t T, const void *x, const vo
     a.aux_loss = aux_loss;
     a.logits = reinterpret_cast<float *>(base + pl.logits);
     a.ldl = pl.ldl;
+    a.logit_split = pl.logit_split;
+    a.dwr_split = 1;
     a.counts = p.counts;
     a.offsets = p.offsets;
     a.tile_start = p.tile_start;

@@ -170,8 +170,11 @@ struct BwdArgs {
     void *dw_router, *dw_gu, *dw_dn, *dw_sgu, *dw_sdn, *dsh_gate;
     float *aux_loss;    // [1] or null
     // workspace
-    float *logits;      // [T, ldl]  x . [W_r; g] (no bias); ldl = E + 1 rounded up to 4
+    float *logits;      // [logit_split, T, ldl]  x . [W_r; g] (no bias) in logit_split K
+                        // slices (partial sums; the logit is their sum); ldl = E + 1 rounded up to 4
     int ldl;
+    int logit_split;
+    int dwr_split;      // dW_router's reduction over the tokens in this many chunks (partials in part)
     const int32_t *counts, *offsets, *tile_start, *tile_group, *perm, *rank;
     void *au, *au_sh;   // [T*k, 2F], [T, 2Fs]  gate | up pre-activations
     bool au_given;      // au holds the training forward's values (no recompute)

@@ -120,6 +120,8 @@ def routed_case(T, d, E, k, F, Fs, dtype, seed, bias):
     (777, 320, 8, 2, 192, 64, 0.5, True),       # ragged tiles, d and F not multiples of 128
     (20, 256, 64, 2, 128, 128, 0.001, False),   # most experts get no token: zero gradients
     (1, 256, 16, 4, 128, 128, 0.001, False),    # one token
+    (1200, 256, 32, 4, 128, 128, 0.01, True),   # T >= 1024: router logits in two K slices,
+                                                # dW_router over four token chunks
 ])
 def test_backward_bf16_layers(T, d, E, k, F, Fs, coef, bias):
     inp, idx, w, dout, b = routed_case(T, d, E, k, F, Fs, "bf16", T + E, bias)
