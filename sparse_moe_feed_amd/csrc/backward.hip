@@ -1163,8 +1163,16 @@ hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
                            dim3(bwd_blocks(K_DWGU, g_small * gu_m, 1, g_small)), dim3(256), 0, s,
                            a, (int)(g_small * gu_m), g_small);
     // most groups were done above: a capped grid strides over the tile map
+    // (the routed groups only when the shared expert's token chunks run on
+    // the direct-to-LDS tiles)
     const unsigned cap = 8 * 256 * 2;
-    launch_gemm<K_DWGU>(ab, g_all * gu_m, cdiv(a.d, QB), s, g_all, cap);
+    const bool wsh = bwd_wsh_dma_ok(a);
+    const int g_tiled = wsh ? a.E : g_all;
+    launch_gemm<K_DWGU>(ab, g_tiled * gu_m, cdiv(a.d, QB), s, g_tiled, cap);
+    if (wsh) {
+        err = launch_bwd_wsh_dma(a, false, s);
+        if (err != hipSuccess) return err;
+    }
     if (a.sh_split > 0) {
         const int64_t n = (int64_t)2 * a.Fs * a.d;
         hipLaunchKernelGGL(sh_reduce_kernel, dim3(cdiv(n / 4, 256)), dim3(256), 0, s, a.part,
@@ -1175,7 +1183,11 @@ hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
         hipLaunchKernelGGL(bwd_dw_small_kernel<K_DWDN>,
                            dim3(bwd_blocks(K_DWDN, g_small * dn_m, 1, g_small)), dim3(256), 0, s,
                            a, (int)(g_small * dn_m), g_small);
-    launch_gemm<K_DWDN>(ab, g_all * dn_m, cdiv(Fmax, QB), s, g_all, cap);
+    launch_gemm<K_DWDN>(ab, g_tiled * dn_m, cdiv(Fmax, QB), s, g_tiled, cap);
+    if (wsh) {
+        err = launch_bwd_wsh_dma(a, true, s);
+        if (err != hipSuccess) return err;
+    }
     if (a.sh_split > 0) {
         const int64_t n = (int64_t)a.d * a.Fs;
         hipLaunchKernelGGL(sh_reduce_kernel, dim3(cdiv(n / 4, 256)), dim3(256), 0, s, a.part,

@@ -494,19 +494,24 @@ __global__ __launch_bounds__((64 * Geo<BM, BK>::NW), (NS * Geo<BM, BK>::STB <= 8
 // then sit in four different quarters of the 256-byte bank space.
 namespace {
 constexpr int MC_ROWB = BN * 2;  // bytes per staged B row (one K index)
+constexpr int MC_AROWB = 128 * 2; // bytes per staged A row when A runs along the output axis too
 __device__ __forceinline__ int mc_swz(int k) { return 4 * (k & 3); }
 
-// One stage: A as dma_stage; B rows k0 .. k0 + 63 (element offsets boff of
-// this lane's row and chunk, plus k0 rows of ldb elements).
+// One stage: A as dma_stage (AMC: like B, K rows k0 .. k0 + 63 of lda
+// elements, aoff of this lane's row and chunk); B rows k0 .. k0 + 63
+// (element offsets boff of this lane's row and chunk, plus k0 rows of ldb
+// elements).
+template <bool AMC>
 __device__ __forceinline__ void dma_stage_mc(unsigned char *stage, const uint16_t *abase,
                                              const uint16_t *wbase,
                                              const uint32_t (&aoff)[Geo<128, 64>::AL],
                                              const uint32_t (&boff)[Geo<128, 64>::BL], int k0,
-                                             uint32_t ldb, int wave) {
+                                             uint32_t lda, uint32_t ldb, int wave) {
     using G = Geo<128, 64>;
+    const uint16_t *ak = AMC ? abase + (size_t)k0 * lda : abase + k0;
 #pragma unroll
     for (int j = 0; j < G::AL; ++j)
-        __builtin_amdgcn_global_load_lds((const global_void_t *)(abase + aoff[j] + k0),
+        __builtin_amdgcn_global_load_lds((const global_void_t *)(ak + aoff[j]),
                                          (lds_void_t *)(stage + (G::AL * wave + j) * 1024), 16,
                                          0, 0);
     const uint16_t *wk = wbase + (size_t)k0 * ldb;
@@ -520,106 +525,109 @@ __device__ __forceinline__ void dma_stage_mc(unsigned char *stage, const uint16_
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
-// B fragment of output columns nb .. nb + 31 at k16 step ks: lane L gets
-// column nb + L % 32, K rows 16 ks + 8 (L / 32) .. + 7.  Lane s of a 16-lane
-// group addresses K row k + s / 4, columns 4 (s % 4) .. + 3 of its 16-column
-// half; the transposing read hands lane s column s of those four rows, and a
-// second read four rows down completes the eight.
-__device__ __forceinline__ bf16x8 mc_bfrag(const unsigned char *bst, int ks, int nb, int lane) {
+// Fragment of output columns nb .. nb + 31 at k16 step ks from a tile whose
+// K rows are ROWB bytes: lane L gets column nb + L % 32, K rows 16 ks + 8 (L
+// / 32) .. + 7.  Lane s of a 16-lane group addresses K row k + s / 4,
+// columns 4 (s % 4) .. + 3 of its 16-column half; the transposing read hands
+// lane s column s of those four rows, and a second read four rows down
+// completes the eight.
+template <int ROWB>
+__device__ __forceinline__ bf16x8 mc_tfrag(const unsigned char *bst, int ks, int nb, int lane) {
     const int g = lane >> 4, s = lane & 15;
     const int k = 16 * ks + 8 * (g >> 1) + (s >> 2);
     const int m = nb + 16 * (g & 1) + 4 * (s & 3);
     const int off = (((m >> 3) ^ mc_swz(k)) << 4) + (m & 7) * 2;  // k and k + 4: same swizzle
-    const unsigned char *p = bst + k * MC_ROWB + off;
+    const unsigned char *p = bst + k * ROWB + off;
     const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)p);
-    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(p + 4 * MC_ROWB));
+    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(p + 4 * ROWB));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-template <int MACT>
+template <int MACT, bool AMC>
 __device__ __forceinline__ void read_frags_mc(const unsigned char *stage, int ks, int wm,
                                               const int (&brow)[NB], int fr, int lane, Frags &f) {
     if (MACT == 0) return;
-    const int c = 2 * ks + (lane >> 5);
-    f.a[0] = *reinterpret_cast<const bf16x8 *>(stage + tile_off<64>(32 * wm + fr, c));
+    if (AMC) {
+        f.a[0] = mc_tfrag<MC_AROWB>(stage, ks, 32 * wm, lane);
+    } else {
+        const int c = 2 * ks + (lane >> 5);
+        f.a[0] = *reinterpret_cast<const bf16x8 *>(stage + tile_off<64>(32 * wm + fr, c));
+    }
 #pragma unroll
-    for (int ni = 0; ni < NB; ++ni) f.b[ni] = mc_bfrag(stage + Geo<128, 64>::OPA, ks, brow[ni], lane);
+    for (int ni = 0; ni < NB; ++ni) f.b[ni] = mc_tfrag<MC_ROWB>(stage + Geo<128, 64>::OPA, ks, brow[ni], lane);
 }
 
-template <int MACT>
+template <int MACT, bool AMC>
 __device__ __forceinline__ void sub_step_mc(const unsigned char *stage, int ks, int wm,
                                             const int (&brow)[NB], int fr, int lane,
                                             const Frags &cur, Frags &nxt, f32x16 (&acc)[1][NB]) {
     if (MACT > 0) {
         mfma_frags<MACT>(cur, acc);
-        read_frags_mc<MACT>(stage, ks, wm, brow, fr, lane, nxt);
+        read_frags_mc<MACT, AMC>(stage, ks, wm, brow, fr, lane, nxt);
         interleave_reads<MACT>();
     }
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// Operands of one tile's K loop.
+struct McOps {
+    const uint16_t *abase, *wbase;
+    uint32_t aoff[Geo<128, 64>::AL], boff[Geo<128, 64>::BL];
+    uint32_t lda, ldb;
+};
+
 // One K step on constant buffer S (as k_step).
-template <int MACT, int S>
-__device__ __forceinline__ void k_step_mc(const Stages<3> &st, int kt, int last,
-                                          const uint16_t *abase, const uint16_t *wbase,
-                                          const uint32_t (&aoff)[Geo<128, 64>::AL],
-                                          const uint32_t (&boff)[Geo<128, 64>::BL], uint32_t ldb,
+template <int MACT, bool AMC, int S>
+__device__ __forceinline__ void k_step_mc(const Stages<3> &st, int kt, int last, const McOps &o,
                                           int wave, int wm, const int (&brow)[NB], int fr,
                                           int lane, Frags &f0, Frags &f1, f32x16 (&acc)[1][NB]) {
     using G = Geo<128, 64>;
-    sub_step_mc<MACT>(st.s[S], 1, wm, brow, fr, lane, f0, f1, acc);
-    sub_step_mc<MACT>(st.s[S], 2, wm, brow, fr, lane, f1, f0, acc);
-    sub_step_mc<MACT>(st.s[S], 3, wm, brow, fr, lane, f0, f1, acc);
+    sub_step_mc<MACT, AMC>(st.s[S], 1, wm, brow, fr, lane, f0, f1, acc);
+    sub_step_mc<MACT, AMC>(st.s[S], 2, wm, brow, fr, lane, f1, f0, acc);
+    sub_step_mc<MACT, AMC>(st.s[S], 3, wm, brow, fr, lane, f0, f1, acc);
     compiler_fence();
     __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(G::LOADS));
     __builtin_amdgcn_s_barrier();
     compiler_fence();
-    dma_stage_mc(st.s[S], abase, wbase, aoff, boff, min((kt + 3) * 64, last), ldb, wave);
+    dma_stage_mc<AMC>(st.s[S], o.abase, o.wbase, o.aoff, o.boff, min((kt + 3) * 64, last), o.lda,
+                      o.ldb, wave);
     __builtin_amdgcn_sched_barrier(0);
-    sub_step_mc<MACT>(st.s[(S + 1) % 3], 0, wm, brow, fr, lane, f1, f0, acc);
+    sub_step_mc<MACT, AMC>(st.s[(S + 1) % 3], 0, wm, brow, fr, lane, f1, f0, acc);
 }
 
-template <int MACT, int S>
+template <int MACT, bool AMC, int S>
 __device__ __forceinline__ void k_steps_mc(const Stages<3> &st, int kt, int cnt, int last,
-                                           const uint16_t *abase, const uint16_t *wbase,
-                                           const uint32_t (&aoff)[Geo<128, 64>::AL],
-                                           const uint32_t (&boff)[Geo<128, 64>::BL],
-                                           uint32_t ldb, int wave, int wm, const int (&brow)[NB],
-                                           int fr, int lane, Frags &f0, Frags &f1,
-                                           f32x16 (&acc)[1][NB]) {
+                                           const McOps &o, int wave, int wm,
+                                           const int (&brow)[NB], int fr, int lane, Frags &f0,
+                                           Frags &f1, f32x16 (&acc)[1][NB]) {
     if constexpr (S < 3) {
         if (S < cnt) {
-            k_step_mc<MACT, S>(st, kt + S, last, abase, wbase, aoff, boff, ldb, wave, wm, brow, fr,
-                               lane, f0, f1, acc);
-            k_steps_mc<MACT, S + 1>(st, kt, cnt, last, abase, wbase, aoff, boff, ldb, wave, wm,
-                                    brow, fr, lane, f0, f1, acc);
+            k_step_mc<MACT, AMC, S>(st, kt + S, last, o, wave, wm, brow, fr, lane, f0, f1, acc);
+            k_steps_mc<MACT, AMC, S + 1>(st, kt, cnt, last, o, wave, wm, brow, fr, lane, f0, f1,
+                                         acc);
         }
     }
 }
 
-template <int MACT>
-__device__ __forceinline__ void k_loop_mc(const Stages<3> &st, const uint16_t *abase,
-                                          const uint16_t *wbase,
-                                          const uint32_t (&aoff)[Geo<128, 64>::AL],
-                                          const uint32_t (&boff)[Geo<128, 64>::BL], uint32_t ldb,
-                                          int nk, int wave, int wm, const int (&brow)[NB], int fr,
-                                          int lane, f32x16 (&acc)[1][NB]) {
+template <int MACT, bool AMC>
+__device__ __forceinline__ void k_loop_mc(const Stages<3> &st, const McOps &o, int nk, int wave,
+                                          int wm, const int (&brow)[NB], int fr, int lane,
+                                          f32x16 (&acc)[1][NB]) {
     const int last = (nk - 1) * 64;
 #pragma unroll
     for (int i = 0; i < 3; ++i)
-        dma_stage_mc(st.s[i], abase, wbase, aoff, boff, min(i * 64, last), ldb, wave);
+        dma_stage_mc<AMC>(st.s[i], o.abase, o.wbase, o.aoff, o.boff, min(i * 64, last), o.lda,
+                          o.ldb, wave);
     compiler_fence();
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * Geo<128, 64>::LOADS));
     __builtin_amdgcn_s_barrier();
     compiler_fence();
     Frags f0, f1;
-    read_frags_mc<MACT>(st.s[0], 0, wm, brow, fr, lane, f0);
+    read_frags_mc<MACT, AMC>(st.s[0], 0, wm, brow, fr, lane, f0);
     int kt = 0;
     for (; kt + 3 <= nk; kt += 3)
-        k_steps_mc<MACT, 0>(st, kt, 3, last, abase, wbase, aoff, boff, ldb, wave, wm, brow, fr,
-                            lane, f0, f1, acc);
-    k_steps_mc<MACT, 0>(st, kt, nk - kt, last, abase, wbase, aoff, boff, ldb, wave, wm, brow, fr,
-                        lane, f0, f1, acc);
+        k_steps_mc<MACT, AMC, 0>(st, kt, 3, last, o, wave, wm, brow, fr, lane, f0, f1, acc);
+    k_steps_mc<MACT, AMC, 0>(st, kt, nk - kt, last, o, wave, wm, brow, fr, lane, f0, f1, acc);
     compiler_fence();
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land after the block ends
     __builtin_amdgcn_s_barrier();
@@ -670,9 +678,13 @@ __global__ __launch_bounds__(512, 1) void bwd_mc_dma_kernel(BwdTileArgs a) {
     if (n0 >= N) return;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-    const uint16_t *abase = shared ? a.a_sh : a.a;
-    const uint16_t *wbase = shared ? a.w_sh : a.w + (int64_t)g * (KIND == BWD_DX ? 2 * a.F : a.F) * a.d;
-    uint32_t aoff[G::AL], boff[G::BL];
+    McOps o;
+    o.abase = shared ? a.a_sh : a.a;
+    o.wbase = shared ? a.w_sh : a.w + (int64_t)g * (KIND == BWD_DX ? 2 * a.F : a.F) * a.d;
+    o.lda = (uint32_t)K;
+    o.ldb = (uint32_t)N;
+    uint32_t (&aoff)[G::AL] = o.aoff;
+    uint32_t (&boff)[G::BL] = o.boff;
 #pragma unroll
     for (int j = 0; j < G::AL; ++j) {
         const int R = (G::AL * wave + j) * G::RPL + lane / G::CH;
@@ -705,9 +717,9 @@ __global__ __launch_bounds__(512, 1) void bwd_mc_dma_kernel(BwdTileArgs a) {
     st.s[1] = st1;
     st.s[2] = st2;
     if (mact)
-        k_loop_mc<1>(st, abase, wbase, aoff, boff, (uint32_t)N, K / 64, wave, wm, brow, fr, lane, acc);
+        k_loop_mc<1, false>(st, o, K / 64, wave, wm, brow, fr, lane, acc);
     else
-        k_loop_mc<0>(st, abase, wbase, aoff, boff, (uint32_t)N, K / 64, wave, wm, brow, fr, lane, acc);
+        k_loop_mc<0, false>(st, o, K / 64, wave, wm, brow, fr, lane, acc);
     // lane holds row 32 wm + lane % 32 and, in acc[0][ni][4 q + i], column
     // brow[ni] + 8 q + 4 (lane / 32) + i
     const int row = 32 * wm + fr;
@@ -747,6 +759,136 @@ __global__ __launch_bounds__(256) void round_bf16_kernel(const float *__restrict
     v.z = pack_bf16x2(hi.x, hi.y);
     v.w = pack_bf16x2(hi.z, hi.w);
     *reinterpret_cast<uint4 *>(dst + i) = v;
+}
+
+// Weight gradients of the shared expert, whose reduction runs over all T
+// tokens: token chunk sp on 128 x 256 tiles of the output, both operands
+// running along the output axis (A [K, M] and B [K, N], K = the chunk's
+// token rows), binary32 partials part[sp] for the chunk-order sum that
+// follows (the same products, in the same order, as the generic tiled
+// kernel's):
+//   gate/up: dW_sgu [2Fs, d] <- [da | du]_sh^T X
+//   down:    dW_sdn [d, Fs]  <- (s dOut)^T H_sh, s dOut rounded to bf16 first
+struct WshArgs {
+    const uint16_t *a, *b;  // [T, M], [T, N]
+    float *part;            // [S, M, N]
+    int64_t T;
+    int M, N, chunk, S;
+};
+
+__global__ __launch_bounds__(512, 1) void bwd_wsh_dma_kernel(WshArgs a) {
+    using G = Geo<128, 64>;
+    __shared__ __align__(1024) unsigned char st0[G::STB];
+    __shared__ __align__(1024) unsigned char st1[G::STB];
+    __shared__ __align__(1024) unsigned char st2[G::STB];
+    const int mtn = a.M / 128, ntn = (a.N + BN - 1) / BN;
+    int b = blockIdx.x;
+    const int nt = b % ntn;
+    b /= ntn;
+    const int mt = b % mtn, sp = b / mtn;
+    if (sp >= a.S) return;
+    const int64_t rb = (int64_t)sp * a.chunk;
+    const int64_t re = min<int64_t>(rb + a.chunk, a.T);
+    if (re <= rb) return;
+    const int K = (int)(re - rb);  // a multiple of 64
+    const int m0 = 128 * mt, n0 = BN * nt;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    McOps o;
+    o.abase = a.a + rb * a.M;
+    o.wbase = a.b + rb * a.N;
+    o.lda = (uint32_t)a.M;
+    o.ldb = (uint32_t)a.N;
+#pragma unroll
+    for (int j = 0; j < G::AL; ++j) {
+        // K row kr of the stage (16 lanes per 256-byte row), physical chunk p:
+        // logical chunk p ^ swizzle
+        const int kr = 4 * (G::AL * wave + j) + (lane >> 4);
+        o.aoff[j] = (uint32_t)kr * (uint32_t)a.M + (uint32_t)(m0 + 8 * ((lane & 15) ^ mc_swz(kr)));
+    }
+#pragma unroll
+    for (int j = 0; j < G::BL; ++j) {
+        const int kr = 2 * (G::BL * wave + j) + (lane >> 5);
+        const int col = min(n0 + 8 * ((lane & 31) ^ mc_swz(kr)), a.N - 8);
+        o.boff[j] = (uint32_t)kr * (uint32_t)a.N + (uint32_t)col;
+    }
+    const int wm = wave >> 1, wn = wave & 1, fr = lane & 31;
+    int brow[NB];
+#pragma unroll
+    for (int ni = 0; ni < NB; ++ni) brow[ni] = 128 * wn + 32 * ni;
+    f32x16 acc[1][NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[0][j][v] = 0.f;
+    Stages<3> st;
+    st.s[0] = st0;
+    st.s[1] = st1;
+    st.s[2] = st2;
+    k_loop_mc<1, true>(st, o, K / 64, wave, wm, brow, fr, lane, acc);
+    // lane holds output row m0 + 32 wm + lane % 32 and, in acc[0][ni][4 q + i],
+    // column n0 + brow[ni] + 8 q + 4 (lane / 32) + i
+    float *crow = a.part + ((int64_t)sp * a.M + m0 + 32 * wm + fr) * a.N + n0 + 4 * (lane >> 5);
+#pragma unroll
+    for (int ni = 0; ni < NB; ++ni)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (n0 + brow[ni] + 8 * q >= a.N) continue;
+            const f32x16 &c4 = acc[0][ni];
+            *reinterpret_cast<float4 *>(crow + brow[ni] + 8 * q) =
+                make_float4(c4[4 * q], c4[4 * q + 1], c4[4 * q + 2], c4[4 * q + 3]);
+        }
+}
+
+// s_t dOut[t] rounded to bf16 (nearest even), d a multiple of 8.
+__global__ __launch_bounds__(256) void scale_round_bf16_kernel(const float *__restrict__ src,
+                                                               const float *__restrict__ scale,
+                                                               uint16_t *__restrict__ dst,
+                                                               int64_t T, int d) {
+    const int64_t i = 8 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
+    if (i >= T * d) return;
+    const float sc = scale[i / d];
+    const float4 lo = *reinterpret_cast<const float4 *>(src + i);
+    const float4 hi = *reinterpret_cast<const float4 *>(src + i + 4);
+    uint4 v;
+    v.x = pack_bf16x2(sc * lo.x, sc * lo.y);
+    v.y = pack_bf16x2(sc * lo.z, sc * lo.w);
+    v.z = pack_bf16x2(sc * hi.x, sc * hi.y);
+    v.w = pack_bf16x2(sc * hi.z, sc * hi.w);
+    *reinterpret_cast<uint4 *>(dst + i) = v;
+}
+
+bool bwd_wsh_dma_ok(const BwdArgs &a) {
+    // chunks of whole 64-row K steps; the rounded s dOut [T, d] bf16 fits the
+    // G region ([T k, F] binary32, free by then)
+    return bwd_dma_ok(a) && a.sh_split > 0 && a.Fs > 0 && a.T % 64 == 0 && a.sh_chunk % 64 == 0 &&
+           (int64_t)2 * a.k * a.F >= a.d;
+}
+
+hipError_t launch_bwd_wsh_dma(const BwdArgs &b, bool down, hipStream_t s) {
+    WshArgs a;
+    a.part = b.part;
+    a.T = b.T;
+    a.chunk = b.sh_chunk;
+    a.S = b.sh_split;
+    if (!down) {
+        a.a = static_cast<const uint16_t *>(b.dgu_sh);
+        a.b = static_cast<const uint16_t *>(b.x);
+        a.M = 2 * b.Fs;
+        a.N = b.d;
+    } else {
+        uint16_t *sdout = reinterpret_cast<uint16_t *>(b.g);
+        const int64_t n = b.T * b.d;
+        hipLaunchKernelGGL(scale_round_bf16_kernel, dim3((unsigned)((n / 8 + 255) / 256)), dim3(256),
+                           0, s, b.dout, b.gate, sdout, b.T, b.d);
+        a.a = sdout;
+        a.b = static_cast<const uint16_t *>(b.hh_sh);
+        a.M = b.d;
+        a.N = b.Fs;
+    }
+    const unsigned blocks = (unsigned)(a.S * (a.M / 128) * ((a.N + BN - 1) / BN));
+    hipLaunchKernelGGL(bwd_wsh_dma_kernel, dim3(blocks), dim3(512), 0, s, a);
+    return hipGetLastError();
 }
 
 bool bwd_dma_ok(const BwdArgs &a) {

@@ -214,6 +214,11 @@ hipError_t launch_backward(const Problem &p, const BwdArgs &a, hipStream_t s,
 bool bwd_dma_ok(const BwdArgs &a);
 hipError_t launch_bwd_dx_dma(const BwdArgs &a, int max_tiles, hipStream_t s);
 hipError_t launch_bwd_g_dma(const BwdArgs &a, int max_tiles, void *dout_bf16, hipStream_t s);
+// The shared expert's weight gradients (token chunks, binary32 partials into
+// part) on the same tiles with both operands along the output axis; down
+// first rounds s dOut to bf16 into the G region.
+bool bwd_wsh_dma_ok(const BwdArgs &a);
+hipError_t launch_bwd_wsh_dma(const BwdArgs &a, bool down, hipStream_t s);
 // Row-major MXFP4 [rows, K] (codes, scales) -> packed tiles (rows % 16 == 0,
 // K % 128 == 0).
 hipError_t launch_mx4_pack(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t K,

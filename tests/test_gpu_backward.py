@@ -122,6 +122,9 @@ def routed_case(T, d, E, k, F, Fs, dtype, seed, bias):
     (1, 256, 16, 4, 128, 128, 0.001, False),    # one token
     (1200, 256, 32, 4, 128, 128, 0.01, True),   # T >= 1024: router logits in two K slices,
                                                 # dW_router over four token chunks
+    (1280, 256, 32, 4, 128, 256, 0.01, False),  # T % 64 == 0: the shared expert's weight
+                                                # gradients on direct-to-LDS tiles, 3 token chunks
+    (512, 384, 16, 4, 128, 128, 0.001, True),   # the same with one chunk
 ])
 def test_backward_bf16_layers(T, d, E, k, F, Fs, coef, bias):
     inp, idx, w, dout, b = routed_case(T, d, E, k, F, Fs, "bf16", T + E, bias)
