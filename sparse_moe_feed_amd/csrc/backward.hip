@@ -696,6 +696,7 @@ __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(BwdArgs a, int nx, int
 // through LDS as 16-byte row pieces, so a tile costs 8 stores per thread and
 // the next tile's loads do not wait behind a long tail of small stores.
 constexpr int KS = 128;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int SLD = QB + 8;  // output staging row: 272 bytes
 
 template <int KIND>
@@ -795,8 +796,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dw_small_kernel(BwdArgs a, int nx,
             // bytes (no branch around the store)
             const int ch = tid + 256 * q;
             const int row = min(ch >> 4, j.mrows - 1), c8 = min(8 * (ch & 15), ncols - 8);
-            *reinterpret_cast<uint4 *>(c + (int64_t)row * j.ldc + c8 * 2) =
-                *reinterpret_cast<const uint4 *>(&Bs[row * SLD + c8]);
+            // the gradient is read by no later kernel of the call: streamed
+            // past the caches (nontemporal) so it does not evict the rows
+            // the next tiles read
+            __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(&Bs[row * SLD + c8]),
+                                        reinterpret_cast<u32x4 *>(c + (int64_t)row * j.ldc + c8 * 2));
         }
         __syncthreads();  // the staged tile is read out
         sb0.store(Bs, 0);
