@@ -1183,10 +1183,14 @@ hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
                            a.sh_split, n, static_cast<uint16_t *>(a.dw_sgu));
     }
     mark(5);
-    if (a.bf16)
+    if (bwd_dwdn_stream_ok(a)) {
+        err = launch_bwd_dwdn_stream(a, s);
+        if (err != hipSuccess) return err;
+    } else if (a.bf16) {
         hipLaunchKernelGGL(bwd_dw_small_kernel<K_DWDN>,
                            dim3(bwd_blocks(K_DWDN, g_small * dn_m, 1, g_small)), dim3(256), 0, s,
                            a, (int)(g_small * dn_m), g_small);
+    }
     launch_gemm<K_DWDN>(ab, g_tiled * dn_m, cdiv(Fmax, QB), s, g_tiled, cap);
     if (wsh) {
         err = launch_bwd_wsh_dma(a, true, s);

@@ -891,6 +891,316 @@ hipError_t launch_bwd_wsh_dma(const BwdArgs &b, bool down, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Down-projection weight gradients of the routed experts with at most 128
+// rows (the usual case: T k / E rows on average), as a stream of output
+// tiles: over the expert's K <= 128 rows,
+//   dW_dn[e] [d, F] = Q^T P,  P = w H_e,  Q = dOut_e
+// (dOut_e: the rows' tokens through the permutation, dOut rounded to bf16
+// once beforehand; w: the rows' combine weights, folded into H -- the weight
+// scales the product of the row's two factors, so it may sit on either).
+// Output rows run along Q's columns (d), output columns along P's (F).
+// Block (expert g, 128-column slice of P) loads that slice of P for the K
+// rows once, keeps its MFMA fragments in registers, and walks 64-column
+// tiles of Q through three direct-to-LDS buffers (two tiles in flight while
+// one computes).  Only the k16 steps that hold rows are loaded and computed
+// (rows past K inside the last step repeat row K - 1 and meet zeros in P).
+// A finished 128 x 64 tile goes out through an LDS staging buffer as 64
+// whole 256-byte row pieces, nontemporal (no later kernel of the call reads
+// the gradient).  Two barriers per tile: one when the tile's buffer has
+// landed (which also frees the staging buffer), one when the staging is
+// complete (which also frees the tile's buffer for the load three tiles
+// ahead).  4 waves in 2 x 2, each 64 columns of P by 32 of Q; 80 KB of LDS,
+// so two blocks share a CU and one's loads, barriers and stores overlap the
+// other's MFMAs.
+struct DwArgs {
+    const uint16_t *p;      // H [T k, F]: row k of the expert is permuted row offsets[g] + k
+    const uint16_t *q;      // dOut bf16 [T, d]: row k of the expert is its token's row
+    uint16_t *out;          // dW_dn [E, d, F]
+    const int32_t *perm, *counts, *offsets;
+    const float *w;         // combine weights (pair order), folded into P
+    int64_t estride;
+    int E, k, ldp, ldq, ldo;
+    int RT, CT;             // 128-column slices of P, 64-column tiles of Q
+};
+
+namespace {
+constexpr int DW_QROWB = 128;             // one staged Q row: 64 bf16
+constexpr int DW_QBUF = 128 * DW_QROWB;   // 128 K rows: 16 KB
+constexpr int DW_STG = 128 * 256;         // P's K rows of 128 bf16, then 64 output rows
+
+// Q rows of 128 bytes, 16-byte chunk c of row k at c ^ 4 ((k >> 1) & 1): a
+// transposing read touches two chunks of each of four consecutive rows, and
+// the two 16-lane groups that share a pass then cover all 64 banks.
+__device__ __forceinline__ int q_swz(int k) { return 4 * ((k >> 1) & 1); }
+
+// Fragment of Q columns nb .. nb + 31 at k16 step ks (as mc_tfrag, for
+// 128-byte rows; k and k + 4 share the swizzle).
+__device__ __forceinline__ bf16x8 q_frag(const unsigned char *qb, int ks, int nb, int lane) {
+    const int g = lane >> 4, s = lane & 15;
+    const int k = 16 * ks + 8 * (g >> 1) + (s >> 2);
+    const int m = nb + 16 * (g & 1) + 4 * (s & 3);
+    const int off = (((m >> 3) ^ q_swz(k)) << 4) + (m & 7) * 2;
+    const unsigned char *p = qb + k * DW_QROWB + off;
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)p);
+    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(p + 4 * DW_QROWB));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Staging of a finished tile: output row R (of 64), 16-byte chunk c at
+// chunk c ^ (R & 15), so the 32 rows one accumulator write touches fall on
+// distinct banks (two passes of 256 bytes) and a row read by 16 lanes too.
+__device__ __forceinline__ int stg_off(int R, int c) { return R * 256 + ((c ^ (R & 15)) << 4); }
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Output piece c (16 bytes) of staged row R of tile t: row 64 t + R,
+// columns r0 + 8 c ..
+__device__ __forceinline__ u32x4_t *dw_dst(const DwArgs &a, uint16_t *out, int t, int r0, int R,
+                                           int c) {
+    return reinterpret_cast<u32x4_t *>(out + (int64_t)(64 * t + R) * a.ldo + r0 + 8 * c);
+}
+
+// MFMAs of one tile over N k16 steps: this wave's Q fragments, then 2 N
+// products with the P fragments held in registers (the accumulator's runs
+// of four go along P's columns, i.e. along the output rows).
+template <int N>
+__device__ __forceinline__ void dw_tile_mfma(const unsigned char *qb, const bf16x8 (&pf)[8][2],
+                                             int wc, int lane, f32x16 (&acc)[2]) {
+    bf16x8 qf[N];
+#pragma unroll
+    for (int ks = 0; ks < N; ++ks) qf[ks] = q_frag(qb, ks, 32 * wc, lane);
+#pragma unroll
+    for (int ks = 0; ks < N; ++ks)
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+            acc[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[ks][mi], qf[ks], acc[mi], 0, 0, 0);
+}
+
+__device__ __forceinline__ void dw_mfma(int nks, const unsigned char *qb, const bf16x8 (&pf)[8][2],
+                                        int wc, int lane, f32x16 (&acc)[2]) {
+    switch (nks) {
+    case 1: dw_tile_mfma<1>(qb, pf, wc, lane, acc); break;
+    case 2: dw_tile_mfma<2>(qb, pf, wc, lane, acc); break;
+    case 3: dw_tile_mfma<3>(qb, pf, wc, lane, acc); break;
+    case 4: dw_tile_mfma<4>(qb, pf, wc, lane, acc); break;
+    case 5: dw_tile_mfma<5>(qb, pf, wc, lane, acc); break;
+    case 6: dw_tile_mfma<6>(qb, pf, wc, lane, acc); break;
+    case 7: dw_tile_mfma<7>(qb, pf, wc, lane, acc); break;
+    case 8: dw_tile_mfma<8>(qb, pf, wc, lane, acc); break;
+    default: break;
+    }
+}
+
+// Q tile t (columns 64 t ..) into buffer qb: this wave's 32 K rows, four
+// loads of eight 128-byte rows (qrow: this lane's row and swizzled chunk).
+__device__ __forceinline__ void dw_load_q(unsigned char *qb, const uint16_t *const (&qrow)[4], int t,
+                                          int wave) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        __builtin_amdgcn_global_load_lds((const global_void_t *)(qrow[j] + 64 * t),
+                                         (lds_void_t *)(qb + (4 * wave + j) * 1024), 16, 0, 0);
+}
+
+// One tile on constant buffer qb: wait until this wave's loads of it have
+// landed (16 vector-memory operations follow them: two tiles' stores and
+// loads) and the other waves' too (barrier), compute, stage, store, and load
+// tile t + 3 into the same buffer (past the last tile the loads re-read
+// tile CT - 1 into a buffer that is never computed).
+__device__ __forceinline__ void dw_tile(const DwArgs &a, unsigned char *qb, unsigned char *stg,
+                                        const uint16_t *const (&qrow)[4], bool dma,
+                                        const bf16x8 (&pf)[8][2], int nks, int t, uint16_t *out,
+                                        int r0, int wave, int wr, int wc, int lane, int tid) {
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(16));
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    f32x16 acc[2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[mi][v] = 0.f;
+    dw_mfma(nks, qb, pf, wc, lane, acc);
+    // accumulator layout: lane holds Q column 32 wc + lane % 32 (the output
+    // row) and, in acc[mi][4 gq + i], P columns 64 wr + 32 mi + 8 gq +
+    // 4 (lane / 32) + i (runs of four along the output row)
+    const int fr = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            const int R = 32 * wc + fr;
+            const int C = 64 * wr + 32 * mi + 8 * gq + 4 * h;
+            const f32x16 &c = acc[mi];
+            // an offset the compiler cannot relate to the others: paired
+            // LDS writes merged into one ds_write2 lose the buffer's alias
+            // scope, and the compiler then waits for every load in flight
+            int off = stg_off(R, C >> 3) + (C & 7) * 2;
+            asm volatile("" : "+v"(off));
+            *reinterpret_cast<uint2 *>(stg + off) =
+                make_uint2(pack_bf16x2(c[4 * gq], c[4 * gq + 1]), pack_bf16x2(c[4 * gq + 2], c[4 * gq + 3]));
+        }
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+        const int pc = tid + 256 * qq, R = pc >> 4, c = pc & 15;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(stg + stg_off(R, c));
+        __builtin_nontemporal_store(v, dw_dst(a, out, t, r0, R, c));
+    }
+    if (dma) dw_load_q(qb, qrow, min(t + 3, a.CT - 1), wave);
+    __builtin_amdgcn_sched_barrier(0);
+}
+}  // namespace
+
+__global__ __launch_bounds__(256, 2) void bwd_dwdn_stream_kernel(DwArgs a) {
+    __shared__ __align__(1024) unsigned char qb0[DW_QBUF];
+    __shared__ __align__(1024) unsigned char qb1[DW_QBUF];
+    __shared__ __align__(1024) unsigned char qb2[DW_QBUF];
+    __shared__ __align__(1024) unsigned char stg[DW_STG];
+    // expert g on XCD g % 8 with its RT blocks consecutive (they share the
+    // expert's Q rows through that XCD's L2)
+    const int b = blockIdx.x, q8 = b >> 3;
+    const int g = 8 * (q8 / a.RT) + (b & 7), rt = q8 % a.RT;
+    if (g >= a.E) return;
+    const int K = a.counts[g];
+    if (K > 128) return;  // the tiled kernel's
+    const int rb = a.offsets[g], nks = (K + 15) >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const int wr = wave >> 1, wc = wave & 1;
+    const int r0 = 128 * rt;
+    uint16_t *out = a.out + (int64_t)g * a.estride;
+    if (K == 0) {  // no rows: the gradient is zero
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+        for (int t = 0; t < a.CT; ++t)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int pc = tid + 256 * qq;
+                __builtin_nontemporal_store(z, dw_dst(a, out, t, r0, pc >> 4, pc & 15));
+            }
+        return;
+    }
+    // this wave loads K rows 32 wave .. + 31: P in eight loads of four
+    // 256-byte rows, Q in four loads of eight 128-byte rows per tile (lane:
+    // its row, physical chunk <- logical chunk ^ swizzle); rows past K
+    // repeat row K - 1
+    const bool dma = 2 * wave < nks;
+    // the permutation lookups (Q's tokens, the weights' pair indices)
+    int qt[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qt[j] = a.perm[rb + max(min(32 * wave + 8 * j + (lane >> 3), K - 1), 0)];
+    const int wt0 = a.perm[rb + min(lane, K - 1)], wt1 = a.perm[rb + min(64 + lane, K - 1)];
+    // used here, so the compiler issues all six lookups before the first
+    // wait (it would otherwise wait for them one at a time)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" ::"v"(qt[j]));
+    asm volatile("" ::"v"(wt0), "v"(wt1));
+    const uint16_t *qrow[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int kr = 32 * wave + 8 * j + (lane >> 3);
+        const int src = qt[j] / a.k;
+        qrow[j] = a.q + (int64_t)src * a.ldq + 8 * ((lane & 7) ^ q_swz(kr));
+    }
+    const uint16_t *prow[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int kr = 32 * wave + 4 * j + (lane >> 4);
+        const int row = rb + max(min(kr, K - 1), 0);
+        prow[j] = a.p + (int64_t)row * a.ldp + r0 + 8 * ((lane & 15) ^ mc_swz(kr));
+    }
+    // every lookup has landed before the first load goes out (a wait for a
+    // lookup issued after a load would wait for the load too)
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    compiler_fence();
+    // the row weights of K rows lane and 64 + lane
+    const float wv0 = a.w[wt0], wv1 = a.w[wt1];
+    // P into the staging buffer (free until the P fragments are in
+    // registers) and the first three tiles; these loads go out on every wave
+    // (rows past the expert's included) so that the compiler sees them on
+    // every path
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        __builtin_amdgcn_global_load_lds((const global_void_t *)prow[j],
+                                         (lds_void_t *)(stg + (8 * wave + j) * 1024), 16, 0, 0);
+    dw_load_q(qb0, qrow, 0, wave);
+    dw_load_q(qb1, qrow, min(1, a.CT - 1), wave);
+    dw_load_q(qb2, qrow, min(2, a.CT - 1), wave);
+    // P, the weights and the first three tiles are in LDS.  A full drain:
+    // with loads in flight at the tile loop's entry the compiler can no
+    // longer tell the buffers apart and waits for every load before each LDS
+    // read in the loop.
+    __syncthreads();
+    // P fragments (P column 64 wr + 32 mi + lane % 32, K rows 16 ks + 8 (lane
+    // / 32) .. + 7), zero past K, times the row weights
+    bf16x8 pf[8][2];
+    const int h = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) {
+            bf16x8 v = {};
+            if (ks < nks) {
+                v = mc_tfrag<256>(stg, ks, 64 * wr + 32 * mi, lane);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int kidx = 16 * ks + 8 * h + e;
+                    float f = kidx < K ? (float)v[e] : 0.f;
+                    f *= __shfl(ks < 4 ? wv0 : wv1, kidx & 63);
+                    v[e] = (__bf16)f;
+                }
+            }
+            pf[ks][mi] = v;
+        }
+    // every wave's P reads are done before the first tile's staging writes
+    // (the first tile's barrier follows this wait)
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    compiler_fence();
+    for (int t = 0; t < a.CT; t += 3) {
+        dw_tile(a, qb0, stg, qrow, dma, pf, nks, t, out, r0, wave, wr, wc, lane, tid);
+        if (t + 1 < a.CT) dw_tile(a, qb1, stg, qrow, dma, pf, nks, t + 1, out, r0, wave, wr, wc, lane, tid);
+        if (t + 2 < a.CT) dw_tile(a, qb2, stg, qrow, dma, pf, nks, t + 2, out, r0, wave, wr, wc, lane, tid);
+    }
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land after the block ends
+}
+
+bool bwd_dwdn_stream_ok(const BwdArgs &a) {
+    // the shared expert is left to the tiled kernels (split over token
+    // chunks); dOut rounded to bf16 goes behind s dOut in the G region
+    // ([T k, F] binary32, free by then): 2 T d bf16 <= T k F binary32
+    return bwd_dma_ok(a) && (a.Fs == 0 || a.sh_split > 0) && a.d <= (int64_t)a.k * a.F;
+}
+
+hipError_t launch_bwd_dwdn_stream(const BwdArgs &b, hipStream_t s) {
+    uint16_t *dob = reinterpret_cast<uint16_t *>(b.g) + b.T * b.d;
+    const int64_t n = b.T * b.d;
+    hipLaunchKernelGGL(round_bf16_kernel, dim3((unsigned)((n / 8 + 255) / 256)), dim3(256), 0, s,
+                       b.dout, dob, n);
+    DwArgs a;
+    a.p = static_cast<const uint16_t *>(b.hh);
+    a.q = dob;
+    a.out = static_cast<uint16_t *>(b.dw_dn);
+    a.perm = b.perm;
+    a.counts = b.counts;
+    a.offsets = b.offsets;
+    a.w = b.topk_w;
+    a.estride = (int64_t)b.d * b.F;
+    a.E = b.E;
+    a.k = b.k;
+    a.ldp = b.F;
+    a.ldq = b.d;
+    a.ldo = b.F;
+    a.RT = b.F / 128;
+    a.CT = b.d / 64;
+    const unsigned blocks = 8u * (unsigned)((b.E + 7) / 8) * (unsigned)a.RT;
+    hipLaunchKernelGGL(bwd_dwdn_stream_kernel, dim3(blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
 bool bwd_dma_ok(const BwdArgs &a) {
     if (!a.bf16 || a.F % 128 || a.Fs % 128 || a.d % 128) return false;
     const int64_t rows = a.T * a.k;

@@ -212,6 +212,12 @@ hipError_t launch_backward(const Problem &p, const BwdArgs &a, hipStream_t s,
 // direct-to-LDS tiles: bf16 layers with F, Fs and d multiples of 128 and
 // 32-bit element offsets.  G first rounds dOut to bf16 into dout_bf16 [T, d].
 bool bwd_dma_ok(const BwdArgs &a);
+// Down-projection weight gradients of the routed experts with at most 128
+// rows on streamed direct-to-LDS tiles (the shared expert's go to the tiled
+// kernels): bf16 layers as bwd_dma_ok, the shared expert split (or absent),
+// d <= k F.  First rounds dOut to bf16 into the G region (behind s dOut).
+bool bwd_dwdn_stream_ok(const BwdArgs &a);
+hipError_t launch_bwd_dwdn_stream(const BwdArgs &a, hipStream_t s);
 hipError_t launch_bwd_dx_dma(const BwdArgs &a, int max_tiles, hipStream_t s);
 hipError_t launch_bwd_g_dma(const BwdArgs &a, int max_tiles, void *dout_bf16, hipStream_t s);
 // The shared expert's weight gradients (token chunks, binary32 partials into

@@ -125,6 +125,9 @@ def routed_case(T, d, E, k, F, Fs, dtype, seed, bias):
     (1280, 256, 32, 4, 128, 256, 0.01, False),  # T % 64 == 0: the shared expert's weight
                                                 # gradients on direct-to-LDS tiles, 3 token chunks
     (512, 384, 16, 4, 128, 128, 0.001, True),   # the same with one chunk
+    (160, 256, 256, 2, 128, 128, 0.001, False), # streamed weight-gradient tiles with many
+                                                # experts that get no row (zero gradients)
+    (600, 256, 64, 4, 256, 128, 0.01, True),    # F = 256: two 128-column slices of H per expert
 ])
 def test_backward_bf16_layers(T, d, E, k, F, Fs, coef, bias):
     inp, idx, w, dout, b = routed_case(T, d, E, k, F, Fs, "bf16", T + E, bias)
