@@ -1173,14 +1173,15 @@ hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
     const bool wsh = bwd_wsh_dma_ok(a);
     const int g_tiled = wsh ? a.E : g_all;
     launch_gemm<K_DWGU>(ab, g_tiled * gu_m, cdiv(a.d, QB), s, g_tiled, cap);
+    int parts = a.sh_split;  // binary32 partials of the shared expert's gradient
     if (wsh) {
-        err = launch_bwd_wsh_dma(a, false, s);
+        err = launch_bwd_wsh_dma(a, false, s, &parts);
         if (err != hipSuccess) return err;
     }
     if (a.sh_split > 0) {
         const int64_t n = (int64_t)2 * a.Fs * a.d;
         hipLaunchKernelGGL(sh_reduce_kernel, dim3(cdiv(n / 4, 256)), dim3(256), 0, s, a.part,
-                           a.sh_split, n, static_cast<uint16_t *>(a.dw_sgu));
+                           parts, n, static_cast<uint16_t *>(a.dw_sgu));
     }
     mark(5);
     if (bwd_dwdn_stream_ok(a)) {
@@ -1192,14 +1193,15 @@ hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
                            a, (int)(g_small * dn_m), g_small);
     }
     launch_gemm<K_DWDN>(ab, g_tiled * dn_m, cdiv(Fmax, QB), s, g_tiled, cap);
+    parts = a.sh_split;
     if (wsh) {
-        err = launch_bwd_wsh_dma(a, true, s);
+        err = launch_bwd_wsh_dma(a, true, s, &parts);
         if (err != hipSuccess) return err;
     }
     if (a.sh_split > 0) {
         const int64_t n = (int64_t)a.d * a.Fs;
         hipLaunchKernelGGL(sh_reduce_kernel, dim3(cdiv(n / 4, 256)), dim3(256), 0, s, a.part,
-                           a.sh_split, n, static_cast<uint16_t *>(a.dw_sdn));
+                           parts, n, static_cast<uint16_t *>(a.dw_sdn));
     }
     mark(6);
     // dW_router reduces over all T tokens on few tiles: at larger T in token

@@ -765,8 +765,8 @@ __global__ __launch_bounds__(256) void round_bf16_kernel(const float *__restrict
 // tokens: token chunk sp on 128 x 256 tiles of the output, both operands
 // running along the output axis (A [K, M] and B [K, N], K = the chunk's
 // token rows), binary32 partials part[sp] for the chunk-order sum that
-// follows (the same products, in the same order, as the generic tiled
-// kernel's):
+// follows (the number of chunks is chosen per gradient shape, so that the
+// tiles fill the CUs in few rounds):
 //   gate/up: dW_sgu [2Fs, d] <- [da | du]_sh^T X
 //   down:    dW_sdn [d, Fs]  <- (s dOut)^T H_sh, s dOut rounded to bf16 first
 struct WshArgs {
@@ -865,12 +865,33 @@ bool bwd_wsh_dma_ok(const BwdArgs &a) {
            (int64_t)2 * a.k * a.F >= a.d;
 }
 
-hipError_t launch_bwd_wsh_dma(const BwdArgs &b, bool down, hipStream_t s) {
+// Token chunks for an M x N gradient on 128 x 256 tiles: of the splits into
+// at most smax chunks of whole 64-row k-steps, the one with the fewest k-step
+// rounds per CU (rounds of ncu tiles times steps per chunk), fewer chunks on
+// ties (less binary32 partial traffic).
+static int wsh_split(int64_t T, int M, int N, int smax, int ncu, int &chunk) {
+    const int64_t base = (int64_t)(M / 128) * ((N + BN - 1) / BN);
+    int best = 1;
+    int64_t best_cost = INT64_MAX;
+    chunk = (int)T;
+    for (int sp = 1; sp <= smax; ++sp) {
+        const int64_t c = (T + sp - 1) / sp;
+        const int64_t ch = (c + 63) / 64 * 64;
+        const int eff = (int)((T + ch - 1) / ch);  // every chunk holds rows
+        const int64_t cost = (eff * base + ncu - 1) / ncu * (ch / 64);
+        if (cost < best_cost || (cost == best_cost && eff < best)) {
+            best_cost = cost;
+            best = eff;
+            chunk = (int)ch;
+        }
+    }
+    return best;
+}
+
+hipError_t launch_bwd_wsh_dma(const BwdArgs &b, bool down, hipStream_t s, int *split) {
     WshArgs a;
     a.part = b.part;
     a.T = b.T;
-    a.chunk = b.sh_chunk;
-    a.S = b.sh_split;
     if (!down) {
         a.a = static_cast<const uint16_t *>(b.dgu_sh);
         a.b = static_cast<const uint16_t *>(b.x);
@@ -886,6 +907,12 @@ hipError_t launch_bwd_wsh_dma(const BwdArgs &b, bool down, hipStream_t s) {
         a.M = b.d;
         a.N = b.Fs;
     }
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+        ncu = 256;
+    a.S = wsh_split(b.T, a.M, a.N, b.sh_split, ncu, a.chunk);
+    *split = a.S;
     const unsigned blocks = (unsigned)(a.S * (a.M / 128) * ((a.N + BN - 1) / BN));
     hipLaunchKernelGGL(bwd_wsh_dma_kernel, dim3(blocks), dim3(512), 0, s, a);
     return hipGetLastError();

@@ -222,9 +222,11 @@ hipError_t launch_bwd_dx_dma(const BwdArgs &a, int max_tiles, hipStream_t s);
 hipError_t launch_bwd_g_dma(const BwdArgs &a, int max_tiles, void *dout_bf16, hipStream_t s);
 // The shared expert's weight gradients (token chunks, binary32 partials into
 // part) on the same tiles with both operands along the output axis; down
-// first rounds s dOut to bf16 into the G region.
+// first rounds s dOut to bf16 into the G region.  The launch picks its own
+// number of chunks (at most sh_split) for its gradient's shape and returns
+// it in *split (the partials to sum).
 bool bwd_wsh_dma_ok(const BwdArgs &a);
-hipError_t launch_bwd_wsh_dma(const BwdArgs &a, bool down, hipStream_t s);
+hipError_t launch_bwd_wsh_dma(const BwdArgs &a, bool down, hipStream_t s, int *split);
 // Row-major MXFP4 [rows, K] (codes, scales) -> packed tiles (rows % 16 == 0,
 // K % 128 == 0).
 hipError_t launch_mx4_pack(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t K,
