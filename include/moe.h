@@ -285,11 +285,17 @@ moe_status moe_forward_prenorm(const moe_desc *desc, int64_t T, const void *h,
 /* ---------------------------------------------------------------------------
  * Training forward: moe_forward plus the gate/up pre-activations that
  * moe_backward would otherwise recompute (reading every touched expert's
- * gate/up weights again).  `saved` (moe_saved_bytes bytes, desc->dtype,
- * 16-byte aligned) receives [a | u] = [W_g x | W_u x] of every routed row in
+ * gate/up weights again).  `saved` (moe_saved_bytes bytes, 16-byte aligned)
+ * receives [a | u] = [W_g x | W_u x] (desc->dtype) of every routed row in
  * the permuted order the routing implies (the rows of expert e, ascending
  * pair id t*k+j, after those of experts < e), each row 2F wide, then the
- * shared expert's [a | u] per token (2Fs wide).  It stays valid while the
+ * shared expert's [a | u] per token (2Fs wide).  When the layer routes with
+ * the shortlist router (bf16 layers of 128 tokens or more, unless a flag
+ * picks the exact router), the router logits follow, at the next multiple
+ * of 256 bytes: binary32 [S][T][E + 1], S = 2 K-slice partial sums (1 when
+ * d % 128 != 0) of x W_r^T (no bias), the shared gate's logit x . g in
+ * column E of slice 0 and zeros in the other slices' column E; moe_backward
+ * then reads them instead of recomputing them.  It stays valid while the
  * routing and x are unchanged.  Everything else as moe_forward.
  * --------------------------------------------------------------------------- */
 size_t moe_saved_bytes(const moe_desc *desc, int64_t T);
@@ -320,8 +326,8 @@ moe_status moe_forward_train(const moe_desc *desc, int64_t T, const void *x,
  *
  * Inputs: the moe_forward operands, topk_idx / topk_w [T,k], dout [T,d]
  * (binary32, the gradient arriving at out), and `saved`: NULL (the gate/up
- * pre-activations are recomputed) or the buffer moe_forward_train filled for
- * this x and routing.  The entries of one topk_idx row
+ * pre-activations and the router logits are recomputed) or the buffer
+ * moe_forward_train filled for this x and routing (with the same desc).  The entries of one topk_idx row
  * must be distinct experts in [0,E) (else the result is undefined; every
  * access stays in bounds).
  * Outputs (all overwritten, none may alias an input):

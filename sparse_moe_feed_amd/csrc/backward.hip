@@ -1123,7 +1123,8 @@ hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
     if (err != hipSuccess) return err;
     const int Fmax = a.F > a.Fs ? a.F : a.Fs;
     const unsigned tiles = (unsigned)pp.max_tiles;
-    launch_gemm<K_LOGITS>(a, cdiv(a.T, QB), cdiv(a.E + 1, QB) * a.logit_split, s);
+    if (!a.logits_given)
+        launch_gemm<K_LOGITS>(a, cdiv(a.T, QB), cdiv(a.E + 1, QB) * a.logit_split, s);
     mark(1);
     if (!a.au_given) launch_gemm<K_AU>(a, tiles, cdiv(2 * Fmax, QB), s);
     // the dX rows of the shared expert (dxs, [T, d] bf16) are written only

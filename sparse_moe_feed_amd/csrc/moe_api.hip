@@ -366,9 +366,20 @@ bool eps_ok(float eps) { return eps >= 0.0f && eps <= 3.4e38f; }
 // moe_forward / moe_forward_mx4 / moe_forward_prenorm: checks, then
 // [RMSNorm into the workspace,] router, permutation, experts, combine.
 // norm_weight != nullptr selects the pre-norm (x is then h).
-size_t saved_bytes_of(const moe_desc &d, int64_t T) {
+// The training forward's saved buffer: the gate/up pre-activations, then
+// (with the shortlist router) its logits, which the backward then reads
+// instead of recomputing them: K-slice partials [split][T][E + 1] of
+// x W_r^T, the shared gate's logit x . g in column E of slice 0 (zeros in
+// the other slices' column E).
+size_t saved_au_bytes(const moe_desc &d, int64_t T) {
     const size_t es = d.dtype == MOE_BF16 ? 2 : 4;
     return ((size_t)T * d.top_k * 2 * d.d_expert + (size_t)T * 2 * d.d_shared) * es;
+}
+size_t saved_logits_off(const moe_desc &d, int64_t T) { return align_up(saved_au_bytes(d, T)); }
+size_t saved_bytes_of(const moe_desc &d, int64_t T) {
+    if (!uses_shortlist(d, T)) return saved_au_bytes(d, T);
+    return saved_logits_off(d, T) +
+           (size_t)moe::shortlist_split(d.d_model) * T * (d.n_experts + 1) * sizeof(float);
 }
 
 moe_status forward_impl(const moe_desc *desc, int64_t T, const void *x, const void *norm_weight,
@@ -394,6 +405,9 @@ moe_status forward_impl(const moe_desc *desc, int64_t T, const void *x, const vo
         p.au = saved;
         p.au_sh = static_cast<char *>(saved) + (size_t)T * desc->top_k * 2 * desc->d_expert *
                                                    (desc->dtype == MOE_BF16 ? 2 : 4);
+        if (p.router == 1)  // the shortlist router's logits go straight into saved
+            p.logits = reinterpret_cast<float *>(static_cast<char *>(saved) +
+                                                 saved_logits_off(*desc, T));
     }
     p.x = norm_weight ? static_cast<const void *>(static_cast<char *>(ws) + pl.xnorm) : x;
     p.w_router = w_router;
@@ -768,11 +782,19 @@ moe_status moe_backward(const moe_desc *desc, int64_t T, const void *x, const vo
     a.tile_group = p.tile_group;
     a.perm = p.perm;
     a.rank = p.rank;
+    a.logits_given = false;
     if (saved) {  // the training forward's pre-activations: no recompute
         a.au = const_cast<void *>(saved);
         a.au_sh = static_cast<char *>(const_cast<void *>(saved)) +
                   (size_t)T * p.k * 2 * p.F * (p.bf16 ? 2 : 4);
         a.au_given = true;
+        if (uses_shortlist(*desc, T)) {  // and its router logits
+            a.logits = reinterpret_cast<float *>(static_cast<char *>(const_cast<void *>(saved)) +
+                                                 saved_logits_off(*desc, T));
+            a.ldl = p.E + 1;
+            a.logit_split = moe::shortlist_split(p.d);
+            a.logits_given = true;
+        }
     } else {
         a.au = base + pl.au;
         a.au_sh = base + pl.au_sh;

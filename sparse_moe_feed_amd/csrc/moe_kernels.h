@@ -174,6 +174,7 @@ struct BwdArgs {
                         // slices (partial sums; the logit is their sum); ldl = E + 1 rounded up to 4
     int ldl;
     int logit_split;
+    bool logits_given;  // logits hold the training forward's router logits: not recomputed
     int dwr_split;      // dW_router's reduction over the tokens in this many chunks (partials in part)
     const int32_t *counts, *offsets, *tile_start, *tile_group, *perm, *rank;
     void *au, *au_sh;   // [T*k, 2F], [T, 2Fs]  gate | up pre-activations

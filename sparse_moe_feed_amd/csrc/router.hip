@@ -280,7 +280,7 @@ __device__ __forceinline__ void wave_best(float &bv, int &be) {
 // One wave per token; NV = ceil(E / 64) logits per lane, NC >= ceil(d / 512).
 template <int NV, int NC>
 __global__ __launch_bounds__(256, NC <= 5 ? 4 : 1) void router_select_shortlist_kernel(
-    const float *__restrict__ f, const float *__restrict__ wnorm, const uint16_t *__restrict__ x,
+    float *__restrict__ f, const float *__restrict__ wnorm, const uint16_t *__restrict__ x,
     const uint16_t *__restrict__ w_router, const uint16_t *__restrict__ g,
     const float *__restrict__ bias, int64_t ntok, int d, int E, int k, int nsplit, float coef,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, float *__restrict__ gate,
@@ -315,6 +315,10 @@ __global__ __launch_bounds__(256, NC <= 5 ? 4 : 1) void router_select_shortlist_
     if (g) zg = wave_sum(zg);
 
     const float *ft = f + t * (E + 1);
+    // column E (not written by the GEMM): the shared gate's logit in slice
+    // 0, zeros in the others, so that the logits buffer carries x [W_r; g]^T
+    // as K-slice partials (the training forward keeps it for the backward)
+    if (lane < nsplit) f[((int64_t)lane * ntok + t) * (E + 1) + E] = lane == 0 ? zg : 0.0f;
     float fb[NV], dl[NV];
     uint32_t removed = 0;
 #pragma unroll

@@ -196,11 +196,13 @@ def test_backward_full_shapes_small_batch():
 @pytest.mark.slow
 def test_backward_prefill_full():
     """The timed training workload (backward_T4096: T = 4096 at the pages'
-    shapes) against the oracle: dx of every token, the router, shared-expert
-    and shared-gate gradients in full, the routed gradients of the four
-    busiest experts, three seeded ones and one no token chose, and the loss
-    value; plus the softmax invariance sum_e dW_router[e] = 0 (within the
-    bf16 rounding of the rows)."""
+    shapes) against the oracle, both from the training forward's saved
+    pre-activations and router logits (the timed launch) and recomputing
+    them: dx of every token, the router, shared-expert and shared-gate
+    gradients in full, the routed gradients of the four busiest experts,
+    three seeded ones and one no token chose, and the loss value; plus the
+    softmax invariance sum_e dW_router[e] = 0 (within the bf16 rounding of
+    the rows)."""
     cfg = W.CONFIGS[9]
     lay = W.layer_for(cfg)
     x = W.make_x(cfg.T, cfg.d, "bf16", cfg.seed_x)
@@ -208,7 +210,17 @@ def test_backward_prefill_full():
     announce(f"{cfg.name}: oracle routing")
     idx, w = oracle.route(x, lay["w_router"], cfg.k)
     dout = W.dout_for(cfg)
-    announce(f"{cfg.name}: GPU")
+    announce(f"{cfg.name}: GPU, training forward then backward from its saved buffer")
+    ins = {n: to_dev(inp[n]) for n in WEIGHTS}
+    _, gidx, gw, saved = moe.forward_train(ins["x"], ins["w_router"], ins["w_gate_up"],
+                                           ins["w_down"], cfg.k, ins["w_sh_gate_up"],
+                                           ins["w_sh_down"], ins["sh_gate"])
+    assert np.array_equal(gidx.cpu().numpy(), idx)
+    got_saved = moe.backward(ins["x"], ins["w_router"], ins["w_gate_up"], ins["w_down"], gidx, gw,
+                             to_dev(dout), ins["w_sh_gate_up"], ins["w_sh_down"], ins["sh_gate"],
+                             aux_coef=cfg.aux_coef, saved=saved)
+    torch.cuda.synchronize()
+    announce(f"{cfg.name}: GPU, recomputing")
     got = gpu_backward(inp, idx, w, dout, cfg.aux_coef)
     counts = np.bincount(idx.ravel(), minlength=cfg.E)
     experts = list(np.argsort(-counts, kind="stable")[:4])
@@ -218,16 +230,17 @@ def test_backward_prefill_full():
     experts = [int(e) for e in experts]
     announce(f"{cfg.name} backward: oracle on every token, experts {experts}")
     ref = oracle_backward(inp, idx, w, dout, cfg.aux_coef, experts=experts)
-    worst = {"dx": check_grad("dx", got["dx"], ref["dx"], False)}
-    for n in ("dw_router", "dw_sh_gate_up", "dw_sh_down", "dsh_gate"):
-        worst[n] = check_grad(n, got[n], ref[n], True)
-    for n in ("dw_gate_up", "dw_down"):
-        worst[n] = check_grad(n, got[n][np.array(experts)], ref[n], True)
-    announce(f"{cfg.name} backward max|err|/RMS: "
-             + ", ".join(f"{n} {v:.3e}" for n, v in worst.items()))
-    assert float(got["aux_loss"].cpu()[0]) == pytest.approx(ref["aux_loss"], rel=1e-4)
-    dwr = as_f64(got["dw_router"])
-    assert np.abs(dwr.sum(axis=0)).max() <= 2.0 ** -8 * np.abs(dwr).sum(axis=0).max()
+    for how, g in (("saved", got_saved), ("recomputed", got)):
+        worst = {"dx": check_grad("dx", g["dx"], ref["dx"], False)}
+        for n in ("dw_router", "dw_sh_gate_up", "dw_sh_down", "dsh_gate"):
+            worst[n] = check_grad(n, g[n], ref[n], True)
+        for n in ("dw_gate_up", "dw_down"):
+            worst[n] = check_grad(n, g[n][np.array(experts)], ref[n], True)
+        announce(f"{cfg.name} backward ({how}) max|err|/RMS: "
+                 + ", ".join(f"{n} {v:.3e}" for n, v in worst.items()))
+        assert float(g["aux_loss"].cpu()[0]) == pytest.approx(ref["aux_loss"], rel=1e-4)
+        dwr = as_f64(g["dw_router"])
+        assert np.abs(dwr.sum(axis=0)).max() <= 2.0 ** -8 * np.abs(dwr).sum(axis=0).max()
 
 
 def permuted_rows(idx, E):
@@ -261,10 +274,12 @@ def test_forward_train_saves_preactivations(T, d, E, k, F, Fs, dtype):
     assert torch.equal(out, out2) and torch.equal(idx, idx2) and torch.equal(w, w2)
     es = 2 if dtype == "bf16" else 4
     raw = saved.cpu().numpy()
-    vals = (W.bf16_bits_to_f32(raw.view(np.uint16)) if es == 2 else raw.view(np.float32))
+    au_bytes = (T * k * 2 * F + T * 2 * Fs) * es
+    au = raw[:au_bytes]
+    vals = (W.bf16_bits_to_f32(au.view(np.uint16)) if es == 2 else au.view(np.float32))
     vals = vals.astype(np.float64)
     routed = vals[:T * k * 2 * F].reshape(T * k, 2 * F)
-    shared = vals[T * k * 2 * F:].reshape(T, 2 * Fs)
+    shared = vals[T * k * 2 * F:T * k * 2 * F + T * 2 * Fs].reshape(T, 2 * Fs)
     f64 = lambda a: (W.bf16_bits_to_f32(a) if a.dtype == np.uint16 else a).astype(np.float64)
     x, wgu = f64(inp["x"]), f64(inp["w_gate_up"])
     pairs = permuted_rows(idx.cpu().numpy(), E)
@@ -276,6 +291,19 @@ def test_forward_train_saves_preactivations(T, d, E, k, F, Fs, dtype):
     ref_sh = x @ f64(inp["w_sh_gate_up"]).T
     mag_sh = np.abs(x) @ np.abs(f64(inp["w_sh_gate_up"])).T
     assert np.all(np.abs(shared - ref_sh) <= u * np.abs(ref_sh) + d * 2.0 ** -23 * mag_sh + 1e-30)
+    # with the shortlist router (bf16, T >= 128) the router logits follow:
+    # K-slice partials of x [W_r; g]^T, binary32, at the next 256 bytes
+    if dtype == "bf16" and T >= 128:
+        off = (au_bytes + 255) // 256 * 256
+        S = 2 if d % 128 == 0 else 1
+        assert raw.size == off + S * T * (E + 1) * 4
+        lg = raw[off:].view(np.float32).reshape(S, T, E + 1).astype(np.float64).sum(axis=0)
+        wr = np.concatenate([f64(inp["w_router"]), f64(inp["sh_gate"]).reshape(1, d)])
+        ref_l = x @ wr.T
+        mag_l = np.abs(x) @ np.abs(wr).T
+        assert np.all(np.abs(lg - ref_l) <= d * 2.0 ** -23 * mag_l + 1e-30)
+    else:
+        assert raw.size == au_bytes
 
 
 @pytest.mark.parametrize("T,F,dtype", [(300, 128, "bf16"), (24, 128, "bf16"), (20, 40, "f32")])
