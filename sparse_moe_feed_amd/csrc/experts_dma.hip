@@ -722,6 +722,90 @@ __global__ __launch_bounds__(512, 1) void bwd_mc_dma_kernel(BwdTileArgs a) {
         k_loop_mc<0, false>(st, o, K / 64, wave, wm, brow, fr, lane, acc);
     // lane holds row 32 wm + lane % 32 and, in acc[0][ni][4 q + i], column
     // brow[ni] + 8 q + 4 (lane / 32) + i
+    if (KIND == BWD_DX) {
+        // the tile goes out through the idle stage buffers (rows 0 .. 63 in
+        // buffer 0, 64 .. 127 in buffer 1; 512-byte rows, chunk c of row r
+        // at chunk c ^ (r & 31)) as whole 512-byte row pieces, nontemporal:
+        // 8-byte pieces straight from the accumulators took 0.81 against
+        // 0.73 ms for the 210 MB at T = 4096 (the dx combine, which reads
+        // them next, is no slower for it)
+        typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+        unsigned char *sbuf = wm < 2 ? st0 : st1;
+        const int rl = 32 * (wm & 1) + fr;
+#pragma unroll
+        for (int ni = 0; ni < NB; ++ni)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x16 &c4 = acc[0][ni];
+                const int col = brow[ni] + 8 * q + 4 * (lane >> 5);
+                int off = rl * 512 + (((col >> 3) ^ (rl & 31)) << 4) + (col & 7) * 2;
+                asm volatile("" : "+v"(off));
+                *reinterpret_cast<uint2 *>(sbuf + off) =
+                    make_uint2(pack_bf16x2(c4[4 * q], c4[4 * q + 1]), pack_bf16x2(c4[4 * q + 2], c4[4 * q + 3]));
+            }
+        compiler_fence();
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
+        uint16_t *cb = static_cast<uint16_t *>(shared ? a.c_sh : a.c) + (int64_t)row0 * N + n0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int pc = tid + 512 * i, r = pc >> 5, c = pc & 31, r2 = r & 63;
+            const unsigned char *src = (i < 4 ? st0 : st1) + r2 * 512 + ((c ^ (r2 & 31)) << 4);
+            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(src);
+            if (r < nrows && n0 + 8 * c < N) {
+                uint16_t *dst = cb + (int64_t)r * N + 8 * c;
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(dst));
+            }
+        }
+        return;
+    }
+    if (KIND == BWD_G) {
+        // binary32 rows in two passes of 128 columns (512-byte staged rows
+        // as above): pass h stages the columns of the waves with wn == h;
+        // nontemporal too (T = 4096: G 0.403 -> 0.390 ms, the SwiGLU
+        // backward that reads it next no slower)
+        typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+        unsigned char *sbuf = wm < 2 ? st0 : st1;
+        const int rl = 32 * (wm & 1) + fr;
+        float *cb = static_cast<float *>(shared ? a.c_sh : a.c) + (int64_t)row0 * N + n0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if (wn == h) {
+#pragma unroll
+                for (int ni = 0; ni < NB; ++ni)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x16 &c4 = acc[0][ni];
+                        const int col = 32 * ni + 8 * q + 4 * (lane >> 5);  // of the 128
+                        int off = rl * 512 + (((col >> 2) ^ (rl & 31)) << 4);
+                        asm volatile("" : "+v"(off));
+                        *reinterpret_cast<float4 *>(sbuf + off) =
+                            make_float4(c4[4 * q], c4[4 * q + 1], c4[4 * q + 2], c4[4 * q + 3]);
+                    }
+            }
+            compiler_fence();
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_s_barrier();
+            compiler_fence();
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int pc = tid + 512 * i, r = pc >> 5, c = pc & 31, r2 = r & 63;
+                const unsigned char *src = (i < 4 ? st0 : st1) + r2 * 512 + ((c ^ (r2 & 31)) << 4);
+                const u32x4_t v = *reinterpret_cast<const u32x4_t *>(src);
+                const int colg = 128 * h + 4 * c;
+                if (r < nrows && n0 + colg < N) {
+                    float *dst = cb + (int64_t)r * N + colg;
+                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(dst));
+                }
+            }
+            compiler_fence();
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_s_barrier();
+            compiler_fence();
+        }
+        return;
+    }
     const int row = 32 * wm + fr;
     if (row >= nrows) return;
     const int64_t cbase = (int64_t)(row0 + row) * N + n0 + 4 * (lane >> 5);
