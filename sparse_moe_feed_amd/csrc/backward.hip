@@ -12,7 +12,7 @@
 // field", ffns.moe.gated):
 //   a, u = W_g x, W_u x;  h = silu(a) u;  G = W_dn^T dout_t;  dw = G . h
 //   dh = w G;  da = dh u silu'(a);  du = dh silu(a)
-//   dx_t += W_gu^T [da; du];  dW_gu += [da; du] x_t^T;  dW_dn += (w dout_t) h^T
+//   dx_t += W_gu^T [da; du];  dW_gu += [da; du] x_t^T;  dW_dn += dout_t (w h)^T
 // The shared expert is the same with w = s_t = sigmoid(g . x_t); its gate
 // logit gets ds s (1 - s), ds = G_sh . h_sh.  The router logits get
 //   dl_te = [e = idx_tj] w_j (dw_j - sum_j' w_j' dw_j') + coef (E/T) p_te (f_e - f . p_t)
@@ -25,10 +25,10 @@
 //   2. logits   [T, E+1]  = X [W_r; g]^T                       (binary32)
 //   3. AU       [rows, 2F] = X_gathered W_gu^T  (pre-activations a | u)
 //   4. G        [rows, F]  = dOut_gathered W_dn                 (binary32)
-//   5. SwiGLU backward per row: dGU = [da | du], H = h, dw (pair) or ds (token)
+//   5. SwiGLU backward per row: dGU = [da | du], H = w h, dw (pair) or ds (token)
 //   6. router backward per token: dL [T, E+1], q_t = f . p_t
 //   7. dXp      [rows, d]  = dGU W_gu
-//   8. dW_gu,e  = dGU_e^T X_e;   dW_dn,e = (w dOut)_e^T H_e     (K = rows of e)
+//   8. dW_gu,e  = dGU_e^T X_e;   dW_dn,e = dOut_e^T H_e         (K = rows of e)
 //   9. dW_r     = dL^T X;        dXr = dL [W_r; g]
 //  10. dx[t] = sum_j dXp[row(t,j)] + dXs[t] + dXr[t];  L_aux = coef E/T sum_t q_t
 //
@@ -333,8 +333,7 @@ __device__ bool make_job(const BwdArgs &a, int bx, int by, int es, Job &j) {
               ((int64_t)m0 * d + n0) * es;
         j.ldc = (int64_t)d * es;
     } else {
-        j.a = opnd(a.dout, d, rb, rb + cnt, 4);
-        j.a.scale = shared ? a.gate : a.topk_w;
+        j.a = opnd(a.dout, d, rb, rb + cnt, 4);  // the weights are in H
         j.b = opnd(shared ? a.hh_sh : a.hh, Fg, rb, rb + cnt, es);
         j.c = (shared ? static_cast<char *>(a.dw_sdn)
                       : static_cast<char *>(a.dw_dn) + (int64_t)g * d * a.F * es) +
@@ -888,14 +887,16 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(BwdArgs a) {
         const float dh = w * gv;
         const float da = dh * uv * (sg * (1.0f + av * (1.0f - sg)));
         const float du = dh * silu;
+        // H carries the row's weight (w, or s_t for the shared expert): the
+        // down-projection weight gradient is then dOut^T H alone
         if constexpr (sizeof(Tv) == 2) {
             dgu[f] = f32_to_bf16_rne(da);
             dgu[Fg + f] = f32_to_bf16_rne(du);
-            hh[f] = f32_to_bf16_rne(h);
+            hh[f] = f32_to_bf16_rne(w * h);
         } else {
             dgu[f] = da;
             dgu[Fg + f] = du;
-            hh[f] = h;
+            hh[f] = w * h;
         }
     }
     acc = wave_sum(acc);
@@ -1127,11 +1128,11 @@ hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
         launch_gemm<K_LOGITS>(a, cdiv(a.T, QB), cdiv(a.E + 1, QB) * a.logit_split, s);
     mark(1);
     if (!a.au_given) launch_gemm<K_AU>(a, tiles, cdiv(2 * Fmax, QB), s);
-    // the dX rows of the shared expert (dxs, [T, d] bf16) are written only
-    // after G, so G's bf16 copy of dOut lives there until then
+    // G rounds dOut to bf16 once (dob), for itself and for the
+    // down-projection weight gradients
     const bool dma = bwd_dma_ok(a);
     if (dma) {
-        err = launch_bwd_g_dma(a, (int)tiles, a.dxs, s);
+        err = launch_bwd_g_dma(a, (int)tiles, a.dob, s);
         if (err != hipSuccess) return err;
     } else {
         launch_gemm<K_G>(a, tiles, cdiv(Fmax, QB), s);

@@ -852,7 +852,7 @@ __global__ __launch_bounds__(256) void round_bf16_kernel(const float *__restrict
 // follows (the number of chunks is chosen per gradient shape, so that the
 // tiles fill the CUs in few rounds):
 //   gate/up: dW_sgu [2Fs, d] <- [da | du]_sh^T X
-//   down:    dW_sdn [d, Fs]  <- (s dOut)^T H_sh, s dOut rounded to bf16 first
+//   down:    dW_sdn [d, Fs]  <- dOut^T (s H)_sh, dOut rounded to bf16 first
 struct WshArgs {
     const uint16_t *a, *b;  // [T, M], [T, N]
     float *part;            // [S, M, N]
@@ -924,29 +924,9 @@ __global__ __launch_bounds__(512, 1) void bwd_wsh_dma_kernel(WshArgs a) {
         }
 }
 
-// s_t dOut[t] rounded to bf16 (nearest even), d a multiple of 8.
-__global__ __launch_bounds__(256) void scale_round_bf16_kernel(const float *__restrict__ src,
-                                                               const float *__restrict__ scale,
-                                                               uint16_t *__restrict__ dst,
-                                                               int64_t T, int d) {
-    const int64_t i = 8 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
-    if (i >= T * d) return;
-    const float sc = scale[i / d];
-    const float4 lo = *reinterpret_cast<const float4 *>(src + i);
-    const float4 hi = *reinterpret_cast<const float4 *>(src + i + 4);
-    uint4 v;
-    v.x = pack_bf16x2(sc * lo.x, sc * lo.y);
-    v.y = pack_bf16x2(sc * lo.z, sc * lo.w);
-    v.z = pack_bf16x2(sc * hi.x, sc * hi.y);
-    v.w = pack_bf16x2(sc * hi.z, sc * hi.w);
-    *reinterpret_cast<uint4 *>(dst + i) = v;
-}
-
 bool bwd_wsh_dma_ok(const BwdArgs &a) {
-    // chunks of whole 64-row K steps; the rounded s dOut [T, d] bf16 fits the
-    // G region ([T k, F] binary32, free by then)
-    return bwd_dma_ok(a) && a.sh_split > 0 && a.Fs > 0 && a.T % 64 == 0 && a.sh_chunk % 64 == 0 &&
-           (int64_t)2 * a.k * a.F >= a.d;
+    // chunks of whole 64-row K steps; dOut in bf16 is G's copy
+    return bwd_dma_ok(a) && a.sh_split > 0 && a.Fs > 0 && a.T % 64 == 0 && a.sh_chunk % 64 == 0;
 }
 
 // Token chunks for an M x N gradient on 128 x 256 tiles: of the splits into
@@ -982,11 +962,7 @@ hipError_t launch_bwd_wsh_dma(const BwdArgs &b, bool down, hipStream_t s, int *s
         a.M = 2 * b.Fs;
         a.N = b.d;
     } else {
-        uint16_t *sdout = reinterpret_cast<uint16_t *>(b.g);
-        const int64_t n = b.T * b.d;
-        hipLaunchKernelGGL(scale_round_bf16_kernel, dim3((unsigned)((n / 8 + 255) / 256)), dim3(256),
-                           0, s, b.dout, b.gate, sdout, b.T, b.d);
-        a.a = sdout;
+        a.a = static_cast<const uint16_t *>(b.dob);
         a.b = static_cast<const uint16_t *>(b.hh_sh);
         a.M = b.d;
         a.N = b.Fs;
@@ -1005,11 +981,11 @@ hipError_t launch_bwd_wsh_dma(const BwdArgs &b, bool down, hipStream_t s, int *s
 // Down-projection weight gradients of the routed experts with at most 128
 // rows (the usual case: T k / E rows on average), as a stream of output
 // tiles: over the expert's K <= 128 rows,
-//   dW_dn[e] [d, F] = Q^T P,  P = w H_e,  Q = dOut_e
-// (dOut_e: the rows' tokens through the permutation, dOut rounded to bf16
-// once beforehand; w: the rows' combine weights, folded into H -- the weight
-// scales the product of the row's two factors, so it may sit on either).
-// Output rows run along Q's columns (d), output columns along P's (F).
+//   dW_dn[e] [d, F] = Q^T P,  P = H_e,  Q = dOut_e
+// (H_e: the rows' w h, the combine weight folded in by the SwiGLU backward;
+// dOut_e: the rows' tokens through the permutation, dOut rounded to bf16
+// once beforehand).  Output rows run along Q's columns (d), output columns
+// along P's (F).
 // Block (expert g, 128-column slice of P) loads that slice of P for the K
 // rows once, keeps its MFMA fragments in registers, and walks 64-column
 // tiles of Q through three direct-to-LDS buffers (two tiles in flight while
@@ -1024,11 +1000,10 @@ hipError_t launch_bwd_wsh_dma(const BwdArgs &b, bool down, hipStream_t s, int *s
 // so two blocks share a CU and one's loads, barriers and stores overlap the
 // other's MFMAs.
 struct DwArgs {
-    const uint16_t *p;      // H [T k, F]: row k of the expert is permuted row offsets[g] + k
+    const uint16_t *p;      // w H [T k, F]: row k of the expert is permuted row offsets[g] + k
     const uint16_t *q;      // dOut bf16 [T, d]: row k of the expert is its token's row
     uint16_t *out;          // dW_dn [E, d, F]
     const int32_t *perm, *counts, *offsets;
-    const float *w;         // combine weights (pair order), folded into P
     int64_t estride;
     int E, k, ldp, ldq, ldo;
     int RT, CT;             // 128-column slices of P, 64-column tiles of Q
@@ -1197,16 +1172,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dwdn_stream_kernel(DwArgs a) {
     // its row, physical chunk <- logical chunk ^ swizzle); rows past K
     // repeat row K - 1
     const bool dma = 2 * wave < nks;
-    // the permutation lookups (Q's tokens, the weights' pair indices)
+    // the permutation lookups of Q's tokens
     int qt[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) qt[j] = a.perm[rb + max(min(32 * wave + 8 * j + (lane >> 3), K - 1), 0)];
-    const int wt0 = a.perm[rb + min(lane, K - 1)], wt1 = a.perm[rb + min(64 + lane, K - 1)];
-    // used here, so the compiler issues all six lookups before the first
+    // used here, so the compiler issues all four lookups before the first
     // wait (it would otherwise wait for them one at a time)
 #pragma unroll
     for (int j = 0; j < 4; ++j) asm volatile("" ::"v"(qt[j]));
-    asm volatile("" ::"v"(wt0), "v"(wt1));
     const uint16_t *qrow[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -1226,8 +1199,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dwdn_stream_kernel(DwArgs a) {
     compiler_fence();
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     compiler_fence();
-    // the row weights of K rows lane and 64 + lane
-    const float wv0 = a.w[wt0], wv1 = a.w[wt1];
     // P into the staging buffer (free until the P fragments are in
     // registers) and the first three tiles; these loads go out on every wave
     // (rows past the expert's included) so that the compiler sees them on
@@ -1239,13 +1210,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dwdn_stream_kernel(DwArgs a) {
     dw_load_q(qb0, qrow, 0, wave);
     dw_load_q(qb1, qrow, min(1, a.CT - 1), wave);
     dw_load_q(qb2, qrow, min(2, a.CT - 1), wave);
-    // P, the weights and the first three tiles are in LDS.  A full drain:
+    // P and the first three tiles are in LDS.  A full drain:
     // with loads in flight at the tile loop's entry the compiler can no
     // longer tell the buffers apart and waits for every load before each LDS
     // read in the loop.
     __syncthreads();
     // P fragments (P column 64 wr + 32 mi + lane % 32, K rows 16 ks + 8 (lane
-    // / 32) .. + 7), zero past K, times the row weights
+    // / 32) .. + 7), zero past K
     bf16x8 pf[8][2];
     const int h = lane >> 5;
 #pragma unroll
@@ -1256,12 +1227,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dwdn_stream_kernel(DwArgs a) {
             if (ks < nks) {
                 v = mc_tfrag<256>(stg, ks, 64 * wr + 32 * mi, lane);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int kidx = 16 * ks + 8 * h + e;
-                    float f = kidx < K ? (float)v[e] : 0.f;
-                    f *= __shfl(ks < 4 ? wv0 : wv1, kidx & 63);
-                    v[e] = (__bf16)f;
-                }
+                for (int e = 0; e < 8; ++e)
+                    if (16 * ks + 8 * h + e >= K) v[e] = (__bf16)0.f;
             }
             pf[ks][mi] = v;
         }
@@ -1281,24 +1248,25 @@ __global__ __launch_bounds__(256, 2) void bwd_dwdn_stream_kernel(DwArgs a) {
 
 bool bwd_dwdn_stream_ok(const BwdArgs &a) {
     // the shared expert is left to the tiled kernels (split over token
-    // chunks); dOut rounded to bf16 goes behind s dOut in the G region
-    // ([T k, F] binary32, free by then): 2 T d bf16 <= T k F binary32
-    return bwd_dma_ok(a) && (a.Fs == 0 || a.sh_split > 0) && a.d <= (int64_t)a.k * a.F;
+    // chunks); dOut in bf16 is G's copy (the same condition)
+    return bwd_dma_ok(a) && (a.Fs == 0 || a.sh_split > 0);
 }
 
 hipError_t launch_bwd_dwdn_stream(const BwdArgs &b, hipStream_t s) {
-    uint16_t *dob = reinterpret_cast<uint16_t *>(b.g) + b.T * b.d;
+    // dOut rounded to bf16 again (the same bits G's copy holds): written
+    // just before, the rows that the tiles gather stay in the caches
+    // (T = 4096: reading G's copy from 1.5 ms earlier made the stage 30 us
+    // slower than rounding again)
     const int64_t n = b.T * b.d;
     hipLaunchKernelGGL(round_bf16_kernel, dim3((unsigned)((n / 8 + 255) / 256)), dim3(256), 0, s,
-                       b.dout, dob, n);
+                       b.dout, static_cast<uint16_t *>(b.dob), n);
     DwArgs a;
     a.p = static_cast<const uint16_t *>(b.hh);
-    a.q = dob;
+    a.q = static_cast<const uint16_t *>(b.dob);
     a.out = static_cast<uint16_t *>(b.dw_dn);
     a.perm = b.perm;
     a.counts = b.counts;
     a.offsets = b.offsets;
-    a.w = b.topk_w;
     a.estride = (int64_t)b.d * b.F;
     a.E = b.E;
     a.k = b.k;

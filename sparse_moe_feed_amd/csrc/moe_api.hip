@@ -188,7 +188,7 @@ moe::Problem make_problem(const moe_desc &d, int64_t T, const Plan &pl, void *ws
 // Workspace of moe_backward (regions as in moe::BwdArgs).
 struct BwdPlan {
     size_t counts, offsets, tile_start, tile_group, blk, rank, perm, logits, au, au_sh, g, g_sh, dgu,
-        dgu_sh, hh, hh_sh, dwp, gate, ds, q, dl, dxp, dxs, dxr, part, total;
+        dgu_sh, hh, hh_sh, dwp, gate, ds, q, dl, dxp, dxs, dxr, dob, part, total;
     int nblk, max_tiles, ldl, ldd, sh_split, sh_chunk, logit_split;
 };
 
@@ -234,6 +234,7 @@ BwdPlan make_bwd_plan(const moe_desc &d, int64_t T) {
     p.dxp = take((size_t)pairs * dm * es);
     p.dxs = take((size_t)T * dm * es);
     p.dxr = take((size_t)T * dm * 4);
+    p.dob = take(d.dtype == MOE_BF16 ? (size_t)T * dm * 2 : 0);  // dout rounded to bf16 once
     p.sh_split = moe::bwd_sh_split(T, d.dtype == MOE_BF16, d.d_shared);
     p.sh_chunk = moe::bwd_sh_chunk(T, p.sh_split);
     p.part = take((size_t)p.sh_split * 2 * Fs * dm * 4);
@@ -815,6 +816,7 @@ moe_status moe_backward(const moe_desc *desc, int64_t T, const void *x, const vo
     a.dxp = base + pl.dxp;
     a.dxs = base + pl.dxs;
     a.dxr = reinterpret_cast<float *>(base + pl.dxr);
+    a.dob = base + pl.dob;
     a.dw_kmin = -1;
     a.sh_split = pl.sh_split;
     a.sh_chunk = pl.sh_chunk;

@@ -181,7 +181,7 @@ struct BwdArgs {
     bool au_given;      // au holds the training forward's values (no recompute)
     float *g, *g_sh;    // [T*k, F], [T, Fs]    W_dn^T dout of each row
     void *dgu, *dgu_sh; // [T*k, 2F], [T, 2Fs]  da | du
-    void *hh, *hh_sh;   // [T*k, F], [T, Fs]    h = silu(a) u
+    void *hh, *hh_sh;   // [T*k, F], [T, Fs]    w h (h = silu(a) u; w the row's combine weight, s_t shared)
     float *dwp;         // [T*k] d/dw of each pair (pair order)
     float *gate, *ds;   // [T] s_t and d/ds_t
     float *q;           // [T] f . p_t
@@ -189,6 +189,7 @@ struct BwdArgs {
     int ldd;
     void *dxp, *dxs;    // [T*k, d], [T, d]  dx of each routed row, of the shared expert
     float *dxr;         // [T, d]            dx of the router
+    void *dob;          // [T, d] bf16       dout rounded once (bf16 layers on the direct-to-LDS tiles)
     int dw_kmin;        // weight-gradient launches skip groups with at most this many rows
     int sh_split;       // > 0: the shared expert's weight gradients reduce over the tokens
     int sh_chunk;       //   in sh_split chunks of sh_chunk rows, partials in part
@@ -211,19 +212,21 @@ hipError_t launch_backward(const Problem &p, const BwdArgs &a, hipStream_t s,
                            const std::function<void(int)> &mark);
 // dX of the routed and shared rows ([da | du] W_gu) and G (dOut W_dn) on
 // direct-to-LDS tiles: bf16 layers with F, Fs and d multiples of 128 and
-// 32-bit element offsets.  G first rounds dOut to bf16 into dout_bf16 [T, d].
+// 32-bit element offsets.  G first rounds dOut to bf16 into dout_bf16 [T, d]
+// (dob, which the down-projection weight gradients read later too).
 bool bwd_dma_ok(const BwdArgs &a);
 // Down-projection weight gradients of the routed experts with at most 128
 // rows on streamed direct-to-LDS tiles (the shared expert's go to the tiled
-// kernels): bf16 layers as bwd_dma_ok, the shared expert split (or absent),
-// d <= k F.  First rounds dOut to bf16 into the G region (behind s dOut).
+// kernels): bf16 layers as bwd_dma_ok, the shared expert split (or absent);
+// rounds dOut to bf16 into dob again first (fresh in the caches for its
+// gathered reads and for the shared expert's gradient that follows).
 bool bwd_dwdn_stream_ok(const BwdArgs &a);
 hipError_t launch_bwd_dwdn_stream(const BwdArgs &a, hipStream_t s);
 hipError_t launch_bwd_dx_dma(const BwdArgs &a, int max_tiles, hipStream_t s);
 hipError_t launch_bwd_g_dma(const BwdArgs &a, int max_tiles, void *dout_bf16, hipStream_t s);
 // The shared expert's weight gradients (token chunks, binary32 partials into
 // part) on the same tiles with both operands along the output axis; down
-// first rounds s dOut to bf16 into the G region.  The launch picks its own
+// reads dOut rounded to bf16 (dob) and s h (hh_sh).  The launch picks its own
 // number of chunks (at most sh_split) for its gradient's shape and returns
 // it in *split (the partials to sum).
 bool bwd_wsh_dma_ok(const BwdArgs &a);
