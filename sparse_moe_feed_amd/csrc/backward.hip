@@ -1072,9 +1072,10 @@ static void launch_gemm(const BwdArgs &a, unsigned nx, unsigned ny, hipStream_t 
 
 // dW_router (rows 0 .. E-1) and the shared gate's gradient (row E, when a
 // shared expert exists and its output is given) from the token chunks'
-// binary32 partials [S, rows, d]: summed in chunk order, rounded to bf16.
+// binary32 partials (partial sp at part + sp pstride, rows of d): summed in
+// chunk order, rounded to bf16.
 __global__ __launch_bounds__(256) void dwr_reduce_kernel(const float *__restrict__ part, int S,
-                                                         int E, int d, int rows,
+                                                         int64_t pstride, int E, int d, int rows,
                                                          uint16_t *__restrict__ dw_router,
                                                          uint16_t *__restrict__ dsh_gate) {
     const int64_t n = (int64_t)rows * d;
@@ -1082,7 +1083,7 @@ __global__ __launch_bounds__(256) void dwr_reduce_kernel(const float *__restrict
     if (i >= n) return;
     float4 acc = *reinterpret_cast<const float4 *>(part + i);
     for (int sp = 1; sp < S; ++sp) {
-        const float4 v = *reinterpret_cast<const float4 *>(part + (int64_t)sp * n + i);
+        const float4 v = *reinterpret_cast<const float4 *>(part + (int64_t)sp * pstride + i);
         acc.x += v.x;
         acc.y += v.y;
         acc.z += v.z;
@@ -1224,12 +1225,24 @@ hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
         ar.dwr_split = (int)std::min<int64_t>(4, cap / (a.E + 1));
         if (ar.dwr_split < 2) ar.dwr_split = 1;
     }
-    launch_gemm<K_DWR>(ar, cdiv(a.E + 1, QB), cdiv(a.d, QB) * ar.dwr_split, s);
-    if (ar.dwr_split > 1) {
+    if (bwd_dwr_dma_ok(a)) {
+        // on the direct-to-LDS split-K tiles (both operands token-major)
+        int parts = 1;
+        err = launch_bwd_dwr_dma(a, s, &parts);
+        if (err != hipSuccess) return err;
         const int64_t n = (int64_t)rrows * a.d;
         hipLaunchKernelGGL(dwr_reduce_kernel, dim3(cdiv(n / 4, 256)), dim3(256), 0, s, a.part,
-                           ar.dwr_split, a.E, a.d, rrows, static_cast<uint16_t *>(a.dw_router),
-                           static_cast<uint16_t *>(a.dsh_gate));
+                           parts, (int64_t)a.ldd * a.d, a.E, a.d, rrows,
+                           static_cast<uint16_t *>(a.dw_router), static_cast<uint16_t *>(a.dsh_gate));
+    } else {
+        launch_gemm<K_DWR>(ar, cdiv(a.E + 1, QB), cdiv(a.d, QB) * ar.dwr_split, s);
+        if (ar.dwr_split > 1) {
+            const int64_t n = (int64_t)rrows * a.d;
+            hipLaunchKernelGGL(dwr_reduce_kernel, dim3(cdiv(n / 4, 256)), dim3(256), 0, s, a.part,
+                               ar.dwr_split, n, a.E, a.d, rrows,
+                               static_cast<uint16_t *>(a.dw_router),
+                               static_cast<uint16_t *>(a.dsh_gate));
+        }
     }
     launch_gemm<K_DXR>(a, cdiv(a.T, QB), cdiv(a.d, QB), s);
     if (a.bf16)

@@ -34,6 +34,8 @@
 
 #include <string.h>
 
+#include <algorithm>
+
 namespace moe {
 
 namespace {
@@ -1277,6 +1279,35 @@ hipError_t launch_bwd_dwdn_stream(const BwdArgs &b, hipStream_t s) {
     a.CT = b.d / 64;
     const unsigned blocks = 8u * (unsigned)((b.E + 7) / 8) * (unsigned)a.RT;
     hipLaunchKernelGGL(bwd_dwdn_stream_kernel, dim3(blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+// dW_router (and the shared gate's gradient) on the same tiles: dL^T X with
+// dL [T, ldd] (the router-logit gradient, zero padded to ldd, a multiple of
+// 128) and X [T, d], token chunks with binary32 partials [S, ldd, d] in part
+// (free by then: its last reader ran), summed in chunk order afterwards.
+bool bwd_dwr_dma_ok(const BwdArgs &a) {
+    return bwd_dma_ok(a) && a.T % 64 == 0 && a.ldd % 128 == 0 && a.sh_split > 0 && a.Fs > 0 &&
+           (int64_t)a.sh_split * 2 * a.Fs >= 2 * (int64_t)a.ldd;
+}
+
+hipError_t launch_bwd_dwr_dma(const BwdArgs &b, hipStream_t s, int *split) {
+    WshArgs a;
+    a.a = static_cast<const uint16_t *>(b.dl);
+    a.b = static_cast<const uint16_t *>(b.x);
+    a.part = b.part;
+    a.T = b.T;
+    a.M = b.ldd;
+    a.N = b.d;
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+        ncu = 256;
+    const int smax = (int)std::min<int64_t>(16, (int64_t)b.sh_split * 2 * b.Fs / b.ldd);
+    a.S = wsh_split(b.T, a.M, a.N, smax, ncu, a.chunk);
+    *split = a.S;
+    const unsigned blocks = (unsigned)(a.S * (a.M / 128) * ((a.N + BN - 1) / BN));
+    hipLaunchKernelGGL(bwd_wsh_dma_kernel, dim3(blocks), dim3(512), 0, s, a);
     return hipGetLastError();
 }
 

@@ -231,6 +231,10 @@ hipError_t launch_bwd_g_dma(const BwdArgs &a, int max_tiles, void *dout_bf16, hi
 // it in *split (the partials to sum).
 bool bwd_wsh_dma_ok(const BwdArgs &a);
 hipError_t launch_bwd_wsh_dma(const BwdArgs &a, bool down, hipStream_t s, int *split);
+// dW_router and the shared gate's gradient (dL^T X) on the same tiles, split
+// over token chunks into binary32 partials [*split, ldd, d] in part.
+bool bwd_dwr_dma_ok(const BwdArgs &a);
+hipError_t launch_bwd_dwr_dma(const BwdArgs &a, hipStream_t s, int *split);
 // Row-major MXFP4 [rows, K] (codes, scales) -> packed tiles (rows % 16 == 0,
 // K % 128 == 0).
 hipError_t launch_mx4_pack(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t K,
