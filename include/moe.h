@@ -295,8 +295,12 @@ moe_status moe_forward_prenorm(const moe_desc *desc, int64_t T, const void *h,
  * of 256 bytes: binary32 [S][T][E + 1], S = 2 K-slice partial sums (1 when
  * d % 128 != 0) of x W_r^T (no bias), the shared gate's logit x . g in
  * column E of slice 0 and zeros in the other slices' column E; moe_backward
- * then reads them instead of recomputing them.  It stays valid while the
- * routing and x are unchanged.  Everything else as moe_forward.
+ * then reads them instead of recomputing them.  With T > 256 the layer's
+ * permutation follows, int32, each part at the next multiple of 256 bytes:
+ * rank [T k] (the permuted row of pair t*k+j), perm [T k] (the pair of each
+ * permuted row) and the rows per expert [E + 1] (the last = T); moe_backward
+ * then builds only its tile map.  It stays valid while the routing and x
+ * are unchanged.  Everything else as moe_forward.
  * --------------------------------------------------------------------------- */
 size_t moe_saved_bytes(const moe_desc *desc, int64_t T);
 
@@ -326,8 +330,9 @@ moe_status moe_forward_train(const moe_desc *desc, int64_t T, const void *x,
  *
  * Inputs: the moe_forward operands, topk_idx / topk_w [T,k], dout [T,d]
  * (binary32, the gradient arriving at out), and `saved`: NULL (the gate/up
- * pre-activations and the router logits are recomputed) or the buffer
- * moe_forward_train filled for this x and routing (with the same desc).  The entries of one topk_idx row
+ * pre-activations, the router logits and the permutation are recomputed) or
+ * the buffer moe_forward_train filled for this x and routing (with the same
+ * desc).  The entries of one topk_idx row
  * must be distinct experts in [0,E) (else the result is undefined; every
  * access stays in bounds).
  * Outputs (all overwritten, none may alias an input):

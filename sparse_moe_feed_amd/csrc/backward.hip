@@ -1121,7 +1121,8 @@ static unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b);
 
 hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
                            const std::function<void(int)> &mark) {
-    hipError_t err = launch_permute(pp, QB, s);
+    hipError_t err = a.counts_given ? launch_permute_tiles(pp, a.counts_given, QB, s)
+                                    : launch_permute(pp, QB, s);
     if (err != hipSuccess) return err;
     const int Fmax = a.F > a.Fs ? a.F : a.Fs;
     const unsigned tiles = (unsigned)pp.max_tiles;

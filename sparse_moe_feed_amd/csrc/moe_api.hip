@@ -377,10 +377,26 @@ size_t saved_au_bytes(const moe_desc &d, int64_t T) {
     return ((size_t)T * d.top_k * 2 * d.d_expert + (size_t)T * 2 * d.d_shared) * es;
 }
 size_t saved_logits_off(const moe_desc &d, int64_t T) { return align_up(saved_au_bytes(d, T)); }
+size_t saved_logits_bytes(const moe_desc &d, int64_t T) {
+    return (size_t)moe::shortlist_split(d.d_model) * T * (d.n_experts + 1) * sizeof(float);
+}
+// ... then (with more than one histogram block) the permutation: rank and
+// perm [T k] and the counts [E + 1], int32.
+int saved_nblk(int64_t T) { return (int)((T + moe::kCountBlock - 1) / moe::kCountBlock); }
+bool saved_routing(const moe_desc &d, int64_t T) { return uses_shortlist(d, T) && saved_nblk(T) > 1; }
+size_t saved_rank_off(const moe_desc &d, int64_t T) {
+    return align_up(saved_logits_off(d, T) + saved_logits_bytes(d, T));
+}
+size_t saved_perm_off(const moe_desc &d, int64_t T) {
+    return align_up(saved_rank_off(d, T) + (size_t)T * d.top_k * 4);
+}
+size_t saved_counts_off(const moe_desc &d, int64_t T) {
+    return align_up(saved_perm_off(d, T) + (size_t)T * d.top_k * 4);
+}
 size_t saved_bytes_of(const moe_desc &d, int64_t T) {
     if (!uses_shortlist(d, T)) return saved_au_bytes(d, T);
-    return saved_logits_off(d, T) +
-           (size_t)moe::shortlist_split(d.d_model) * T * (d.n_experts + 1) * sizeof(float);
+    if (!saved_routing(d, T)) return saved_logits_off(d, T) + saved_logits_bytes(d, T);
+    return saved_counts_off(d, T) + (size_t)(d.n_experts + 1) * 4;
 }
 
 moe_status forward_impl(const moe_desc *desc, int64_t T, const void *x, const void *norm_weight,
@@ -409,6 +425,12 @@ moe_status forward_impl(const moe_desc *desc, int64_t T, const void *x, const vo
         if (p.router == 1)  // the shortlist router's logits go straight into saved
             p.logits = reinterpret_cast<float *>(static_cast<char *>(saved) +
                                                  saved_logits_off(*desc, T));
+        if (saved_routing(*desc, T)) {  // and the permutation
+            char *sb = static_cast<char *>(saved);
+            p.rank = reinterpret_cast<int32_t *>(sb + saved_rank_off(*desc, T));
+            p.perm = reinterpret_cast<int32_t *>(sb + saved_perm_off(*desc, T));
+            p.counts = reinterpret_cast<int32_t *>(sb + saved_counts_off(*desc, T));
+        }
     }
     p.x = norm_weight ? static_cast<const void *>(static_cast<char *>(ws) + pl.xnorm) : x;
     p.w_router = w_router;
@@ -743,9 +765,18 @@ moe_status moe_backward(const moe_desc *desc, int64_t T, const void *x, const vo
     p.perm = reinterpret_cast<int32_t *>(base + pl.perm);
     p.nblk = pl.nblk;
     p.max_tiles = pl.max_tiles;
+    // with the training forward's permutation only the tile map is built
+    const int32_t *counts_given = nullptr;
+    if (saved && saved_routing(*desc, T)) {
+        char *sb = static_cast<char *>(const_cast<void *>(saved));
+        p.rank = reinterpret_cast<int32_t *>(sb + saved_rank_off(*desc, T));
+        p.perm = reinterpret_cast<int32_t *>(sb + saved_perm_off(*desc, T));
+        counts_given = reinterpret_cast<const int32_t *>(sb + saved_counts_off(*desc, T));
+    }
 
     moe::BwdArgs a;
     memset(&a, 0, sizeof a);
+    a.counts_given = counts_given;
     a.T = T;
     a.d = p.d;
     a.E = p.E;

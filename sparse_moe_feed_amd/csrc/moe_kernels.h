@@ -135,6 +135,9 @@ hipError_t launch_rmsnorm(const void *h, const void *gamma, float eps, void *x, 
 hipError_t launch_shared_gate(const Problem &p, hipStream_t s);
 // Histogram, scan, stable permutation and GEMM tile map for tile height bm.
 hipError_t launch_permute(const Problem &p, int bm, hipStream_t s);
+// Counts (copied), offsets and the tile map of tile height bm from given
+// per-expert counts, for a permutation whose rank and perm are there (E <= 1024).
+hipError_t launch_permute_tiles(const Problem &p, const int32_t *counts_in, int bm, hipStream_t s);
 // out[t] (= shared term, if any) += sum_j y[row(t, j)]
 hipError_t launch_combine(const Problem &p, hipStream_t s);
 // Expert stage for bfloat16 (MFMA) and binary32 (plain FMA) layers:
@@ -175,6 +178,8 @@ struct BwdArgs {
     int ldl;
     int logit_split;
     bool logits_given;  // logits hold the training forward's router logits: not recomputed
+    const int32_t *counts_given;  // non-null: rank / perm hold the training forward's
+                                  // permutation, these its counts (only the tile map is built)
     int dwr_split;      // dW_router's reduction over the tokens in this many chunks (partials in part)
     const int32_t *counts, *offsets, *tile_start, *tile_group, *perm, *rank;
     void *au, *au_sh;   // [T*k, 2F], [T, 2Fs]  gate | up pre-activations

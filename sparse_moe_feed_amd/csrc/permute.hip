@@ -210,6 +210,45 @@ __global__ __launch_bounds__(1024) void route_permute_small_kernel(
                   tile_group, row_of, perm);
 }
 
+// Offsets and the tile map of tile height bm from given per-expert counts
+// (a permutation whose rank and perm are already there), as the scan step
+// derives them.
+__global__ __launch_bounds__(1024) void route_tiles_kernel(const int32_t *__restrict__ cnt, int E,
+                                                           int64_t ntok, int bm, int has_shared,
+                                                           int32_t *__restrict__ counts,
+                                                           int32_t *__restrict__ offsets,
+                                                           int32_t *__restrict__ tile_start,
+                                                           int32_t *__restrict__ tile_group) {
+    const int e = threadIdx.x;
+    const int total = e < E ? cnt[e] : 0;
+    if (e < E) counts[e] = total;
+    const int tiles = e < E ? (total + bm - 1) / bm : 0;
+    int all_rows, all_tiles;
+    const int off = block_exclusive_scan(e < E ? total : 0, &all_rows);
+    const int ts = block_exclusive_scan(tiles, &all_tiles);
+    if (e < E) {
+        offsets[e] = off;
+        tile_start[e] = ts;
+        for (int i = 0; i < tiles; ++i) tile_group[ts + i] = e;
+    }
+    if (e == 0) {
+        offsets[E] = all_rows;
+        counts[E] = (int)ntok;
+        tile_start[E] = all_tiles;
+        tile_start[E + 1] = all_tiles + (has_shared ? (int)((ntok + bm - 1) / bm) : 0);
+    }
+    if (has_shared) {
+        const int shared_tiles = (int)((ntok + bm - 1) / bm);
+        for (int i = threadIdx.x; i < shared_tiles; i += 1024) tile_group[all_tiles + i] = E;
+    }
+}
+
+hipError_t launch_permute_tiles(const Problem &p, const int32_t *counts_in, int bm, hipStream_t s) {
+    hipLaunchKernelGGL(route_tiles_kernel, dim3(1), dim3(1024), 0, s, counts_in, p.E, p.T, bm,
+                       p.Fs > 0 ? 1 : 0, p.counts, p.offsets, p.tile_start, p.tile_group);
+    return hipGetLastError();
+}
+
 hipError_t launch_permute(const Problem &p, int bm, hipStream_t s) {
     if (p.nblk == 1) {
         const size_t lds = (size_t)p.E * (kWords + 1) * sizeof(uint32_t);

@@ -296,12 +296,29 @@ def test_forward_train_saves_preactivations(T, d, E, k, F, Fs, dtype):
     if dtype == "bf16" and T >= 128:
         off = (au_bytes + 255) // 256 * 256
         S = 2 if d % 128 == 0 else 1
-        assert raw.size == off + S * T * (E + 1) * 4
-        lg = raw[off:].view(np.float32).reshape(S, T, E + 1).astype(np.float64).sum(axis=0)
+        end = off + S * T * (E + 1) * 4
+        lg = raw[off:end].view(np.float32).reshape(S, T, E + 1).astype(np.float64).sum(axis=0)
         wr = np.concatenate([f64(inp["w_router"]), f64(inp["sh_gate"]).reshape(1, d)])
         ref_l = x @ wr.T
         mag_l = np.abs(x) @ np.abs(wr).T
         assert np.all(np.abs(lg - ref_l) <= d * 2.0 ** -23 * mag_l + 1e-30)
+        # with more than one 256-token histogram block the permutation
+        # follows: rank and perm [T k] and the counts [E + 1]
+        nblk = (T + 255) // 256
+        if nblk > 1:
+            a256 = lambda v: (v + 255) // 256 * 256
+            r_off = a256(end)
+            p_off = a256(r_off + T * k * 4)
+            c_off = a256(p_off + T * k * 4)
+            assert raw.size == c_off + (E + 1) * 4
+            rank = raw[r_off:r_off + T * k * 4].view(np.int32)
+            perm = raw[p_off:p_off + T * k * 4].view(np.int32)
+            counts = raw[c_off:].view(np.int32)
+            assert np.array_equal(perm, pairs)
+            assert np.array_equal(rank[perm], np.arange(T * k))
+            assert np.array_equal(counts[:E], np.bincount(kk, minlength=E)) and counts[E] == T
+        else:
+            assert raw.size == end
     else:
         assert raw.size == au_bytes
 
