@@ -1173,7 +1173,7 @@ hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
     // most groups were done above: a capped grid strides over the tile map
     // (the routed groups only when the shared expert's token chunks run on
     // the direct-to-LDS tiles)
-    // two rounds of the two blocks per CU that fit: enough to fill the chip
+    // one round of the two blocks per CU that fit: enough to fill the chip
     // for the grid-stride walk, and few when there is nothing to do (the
     // usual case when the shared expert runs on the direct-to-LDS tiles)
     int dev = 0, ncu = 256;
@@ -1181,7 +1181,7 @@ hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         ncu <= 0)
         ncu = 256;
-    const unsigned cap = 8u * (unsigned)((ncu + 1) / 2);  // a multiple of 8 (XCD order)
+    const unsigned cap = 8u * (unsigned)((ncu + 3) / 4);  // 2 ncu, a multiple of 8 (XCD order)
     const bool wsh = bwd_wsh_dma_ok(a);
     const int g_tiled = wsh ? a.E : g_all;
     launch_gemm<K_DWGU>(ab, g_tiled * gu_m, cdiv(a.d, QB), s, g_tiled, cap);
