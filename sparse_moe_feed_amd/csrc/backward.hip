@@ -1005,6 +1005,15 @@ __global__ __launch_bounds__(256) void dx_combine_kernel(BwdArgs a) {
 __global__ __launch_bounds__(64) void dx_combine_bf16_kernel(BwdArgs a) {
     const int64_t t = blockIdx.x;
     const int c = (blockIdx.y * 64 + threadIdx.x) * 8;
+    if (a.aux_loss && blockIdx.x == 0 && blockIdx.y == 0) {
+        // the load-balancing loss, coef E / T sum_t q_t, summed in a fixed
+        // order by this one block (a launch of its own cost more than the
+        // sum; the other blocks of the grid run meanwhile)
+        float sq = 0.f;
+        for (int64_t u = threadIdx.x; u < a.T; u += 64) sq += a.q[u];
+        sq = wave_sum(sq);
+        if (threadIdx.x == 0) a.aux_loss[0] = a.coef * (float)a.E / (float)a.T * sq;
+    }
     if (c >= a.d) return;
     float acc[8], v[8], vs[8];
 #pragma unroll
@@ -1252,7 +1261,8 @@ hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
     else
         hipLaunchKernelGGL(dx_combine_kernel<float>, dim3((unsigned)a.T, cdiv(a.d, 256)),
                            dim3(256), 0, s, a);
-    if (a.aux_loss) hipLaunchKernelGGL(aux_loss_kernel, dim3(1), dim3(256), 0, s, a);
+    // (bf16 layers: the loss comes from the dx combine's first block)
+    if (a.aux_loss && !a.bf16) hipLaunchKernelGGL(aux_loss_kernel, dim3(1), dim3(256), 0, s, a);
     mark(7);
     return hipGetLastError();
 }
