@@ -932,7 +932,32 @@ template <typename Tv>
 __global__ __launch_bounds__(256) void router_bwd_kernel(BwdArgs a) {
     extern __shared__ float dls[];  // [ldd], then the token's logits [E + 1]
     __shared__ float red[4];
+    __shared__ float pterm[kWave];  // the selected experts' terms (k <= 32)
+    __shared__ int pexp[kWave];
     const int64_t t = blockIdx.x;
+    // G . h of each pair (lane jj < k of wave 0) and of the shared row
+    // (thread 64): one value, or partial sums over 128 columns of G each,
+    // added in column order; loaded first, used after the softmax
+    const int st = a.gtile > 0 ? a.gtile : 1;
+    const int nr = a.gtile > 0 ? (a.F + 127) / 128 : 1;
+    const int ns = a.gtile > 0 ? (a.Fs + 127) / 128 : 1;
+    float wj = 0.f, dwj = 0.f, dsv = 0.f, sg = 0.f;
+    int ej = 0;
+    if ((int)threadIdx.x < a.k) {
+        const int64_t pj = t * a.k + threadIdx.x;
+        wj = a.topk_w[pj];
+        ej = a.topk_idx[pj];
+        ej = ej < 0 ? 0 : (ej >= a.E ? a.E - 1 : ej);
+        const float *pp = a.dwp + pj * st;
+        dwj = pp[0];
+        for (int i = 1; i < nr; ++i) dwj += pp[i];
+    }
+    if (threadIdx.x == 64 && a.Fs > 0) {
+        sg = a.gate[t];
+        const float *pp = a.ds + t * st;
+        dsv = pp[0];
+        for (int i = 1; i < ns; ++i) dsv += pp[i];
+    }
     // the token's logits: the sum of the K slices' partials
     float *l = dls + a.ldd;
     for (int e = threadIdx.x; e <= a.E; e += 256) {
@@ -960,23 +985,21 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(BwdArgs a) {
     const float c = a.coef * (float)a.E / (float)a.T;
     for (int e = threadIdx.x; e < a.ldd; e += 256)
         dls[e] = e < a.E ? c * dls[e] * ((float)a.counts[e] * inv_pairs - fp) : 0.f;
+    if (threadIdx.x < kWave) {
+        // sum_j w_j dw_j over the k pairs (a fixed tree over the wave; lanes
+        // past k add zeros), then each pair's softmax-weight term
+        float wdw = wj * dwj;
+        for (int o = kWave / 2; o >= 1; o >>= 1) wdw += __shfl_xor(wdw, o, kWave);
+        pterm[threadIdx.x] = wj * (dwj - wdw);
+        pexp[threadIdx.x] = ej;
+    }
     __syncthreads();
     if (threadIdx.x == 0) {
         a.q[t] = fp;
-        const float *w = a.topk_w + t * a.k;
-        const float *dw = a.dwp + t * a.k;
-        float wdw = 0.f;
-        for (int jj = 0; jj < a.k; ++jj) wdw = fmaf(w[jj], dw[jj], wdw);
-        for (int jj = 0; jj < a.k; ++jj) {
-            int e = a.topk_idx[t * a.k + jj];
-            e = e < 0 ? 0 : (e >= a.E ? a.E - 1 : e);
-            dls[e] += w[jj] * (dw[jj] - wdw);
-        }
-        if (a.Fs > 0) {
-            const float s = a.gate[t];
-            dls[a.E] = a.ds[t] * s * (1.0f - s);
-        }
+        // in slot order (a repeated expert adds its terms in that order)
+        for (int jj = 0; jj < a.k; ++jj) dls[pexp[jj]] += pterm[jj];
     }
+    if (threadIdx.x == 64 && a.Fs > 0) dls[a.E] = dsv * sg * (1.0f - sg);
     __syncthreads();
     Tv *out = static_cast<Tv *>(a.dl) + t * a.ldd;
     for (int e = threadIdx.x; e < a.ldd; e += 256) {
@@ -1140,10 +1163,14 @@ hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
     mark(1);
     if (!a.au_given) launch_gemm<K_AU>(a, tiles, cdiv(2 * Fmax, QB), s);
     // G rounds dOut to bf16 once (dob), for itself and for the
-    // down-projection weight gradients
+    // down-projection weight gradients; on the direct-to-LDS tiles the
+    // SwiGLU backward runs in its epilogue (G . h as partial sums per 128
+    // columns), elsewhere in a kernel of its own that reads G
     const bool dma = bwd_dma_ok(a);
+    BwdArgs ag = a;
+    ag.gtile = dma ? (int)cdiv(Fmax, 128) : 0;
     if (dma) {
-        err = launch_bwd_g_dma(a, (int)tiles, a.dob, s);
+        err = launch_bwd_g_dma(ag, (int)tiles, a.dob, s);
         if (err != hipSuccess) return err;
     } else {
         launch_gemm<K_G>(a, tiles, cdiv(Fmax, QB), s);
@@ -1152,11 +1179,13 @@ hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
     const int64_t rows = (int64_t)a.T * a.k + (a.Fs > 0 ? a.T : 0);
     const size_t lds = (size_t)(a.ldd + a.E + 1) * sizeof(float);
     if (a.bf16) {
-        hipLaunchKernelGGL(swiglu_bwd_kernel<uint16_t>, dim3(cdiv(rows, 4)), dim3(256), 0, s, a);
-        hipLaunchKernelGGL(router_bwd_kernel<uint16_t>, dim3((unsigned)a.T), dim3(256), lds, s, a);
+        if (!dma)
+            hipLaunchKernelGGL(swiglu_bwd_kernel<uint16_t>, dim3(cdiv(rows, 4)), dim3(256), 0, s,
+                               ag);
+        hipLaunchKernelGGL(router_bwd_kernel<uint16_t>, dim3((unsigned)a.T), dim3(256), lds, s, ag);
     } else {
-        hipLaunchKernelGGL(swiglu_bwd_kernel<float>, dim3(cdiv(rows, 4)), dim3(256), 0, s, a);
-        hipLaunchKernelGGL(router_bwd_kernel<float>, dim3((unsigned)a.T), dim3(256), lds, s, a);
+        hipLaunchKernelGGL(swiglu_bwd_kernel<float>, dim3(cdiv(rows, 4)), dim3(256), 0, s, ag);
+        hipLaunchKernelGGL(router_bwd_kernel<float>, dim3((unsigned)a.T), dim3(256), lds, s, ag);
     }
     mark(3);
     if (dma) {

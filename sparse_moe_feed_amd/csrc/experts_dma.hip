@@ -640,17 +640,27 @@ __device__ __forceinline__ void k_loop_mc(const Stages<3> &st, const McOps &o, i
 // The two backward products on these tiles (B runs along the output axis):
 //   BWD_DX: dX rows = [da | du] W_gu   (A: [da | du] rows, K = 2 Fg; bf16 out, N = d)
 //   BWD_G:  G rows  = dOut W_dn        (A: the rows' tokens of dOut, rounded to
-//           bf16 beforehand, K = d; binary32 out, N = Fg)
+//           bf16 beforehand, K = d; N = Fg), consumed in the epilogue by the
+//           SwiGLU backward: G never leaves the registers
 enum { BWD_DX = 0, BWD_G = 1 };
 
 struct BwdTileArgs {
     const uint16_t *a, *a_sh;      // DX: [da | du] [T k, 2F], [T, 2Fs]; G: dOut bf16 [T, d]
     const uint16_t *w, *w_sh;      // DX: W_gu [E, 2F, d], [2Fs, d]; G: W_dn [E, d, F], [d, Fs]
-    void *c, *c_sh;                // DX: dX rows bf16 [T k, d], [T, d]; G: binary32 [T k, F], [T, Fs]
+    void *c, *c_sh;                // DX: dX rows bf16 [T k, d], [T, d]
     const int32_t *perm, *counts, *offsets, *tile_start, *tile_group;
     int64_t T;
     int d, E, k, F, Fs;
     int nm, nn, gm;
+    // BWD_G's SwiGLU backward (rows in the tile map's order, as G's)
+    const uint16_t *au, *au_sh;    // [T k, 2F], [T, 2Fs]  gate | up pre-activations
+    uint16_t *dgu, *dgu_sh;        // [T k, 2F], [T, 2Fs]  da | du
+    uint16_t *hh, *hh_sh;          // [T k, F], [T, Fs]    w h
+    const float *topk_w;           // [T k] routed rows' combine weights (pair order)
+    const float *logits;           // [logit_split, T, ldl] router logit partials (column E: shared gate)
+    float *gate;                   // [T] s_t = sigmoid of the shared gate's logit
+    float *dwp, *ds;               // G . h per row and 128 columns: [T k, np] (pair order), [T, np]
+    int ldl, logit_split, np;
 };
 
 template <int KIND>
@@ -687,6 +697,17 @@ __global__ __launch_bounds__(512, 1) void bwd_mc_dma_kernel(BwdTileArgs a) {
     o.ldb = (uint32_t)N;
     uint32_t (&aoff)[G::AL] = o.aoff;
     uint32_t (&boff)[G::BL] = o.boff;
+    // BWD_G: the SwiGLU backward in the epilogue gives thread tid the rows
+    // 32 it + tid / 16 (it < 4) of the tile and, in each 128-column half, the
+    // 8 columns 8 (tid % 16); their pairs are looked up with the A rows' (a
+    // shared row reads some pair id, clamped to the valid range, unused)
+    const int er = tid >> 4, ec = 8 * (tid & 15);
+    int epair[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+        epair[it] = KIND == BWD_G ? (int)min<int64_t>(max(a.perm[row0 + min(32 * it + er, nrows - 1)], 0),
+                                                      a.T * a.k - 1)
+                                  : 0;
 #pragma unroll
     for (int j = 0; j < G::AL; ++j) {
         const int R = (G::AL * wave + j) * G::RPL + lane / G::CH;
@@ -709,6 +730,30 @@ __global__ __launch_bounds__(512, 1) void bwd_mc_dma_kernel(BwdTileArgs a) {
 #pragma unroll
     for (int ni = 0; ni < NB; ++ni) brow[ni] = 128 * wn + 32 * ni;
     const int mact = nrows > 32 * wm ? 1 : 0;  // this wave's 32 rows hold data
+    // BWD_G: the epilogue's operands, issued before the K loop so that they
+    // land with its first stages, all unconditionally (clamped to valid
+    // addresses; a branch here makes the compiler wait for every load at its
+    // join): the routed rows' weights, the shared rows' gate logits (at most
+    // two K slices), and 8 gate and 8 up pre-activations per row and half
+    uint4 pa[2][4], pu[2][4];
+    float wpair[4], z0[4], z1[4];
+    if (KIND == BWD_G) {
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int64_t rc = row0 + min(32 * it + er, nrows - 1);
+            wpair[it] = a.topk_w[epair[it]];
+            const int64_t tok = shared ? rc : 0;
+            z0[it] = a.logits[tok * a.ldl + a.E];
+            z1[it] = a.logits[((a.logit_split > 1 ? a.T : 0) + tok) * a.ldl + a.E];
+            const uint16_t *aur = (shared ? a.au_sh : a.au) + rc * 2 * Fg + ec;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int c0 = min(n0 + 128 * h, N - 128);
+                pa[h][it] = *reinterpret_cast<const uint4 *>(aur + c0);
+                pu[h][it] = *reinterpret_cast<const uint4 *>(aur + Fg + c0);
+            }
+        }
+    }
     f32x16 acc[1][NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j)
@@ -722,6 +767,20 @@ __global__ __launch_bounds__(512, 1) void bwd_mc_dma_kernel(BwdTileArgs a) {
         k_loop_mc<1, false>(st, o, K / 64, wave, wm, brow, fr, lane, acc);
     else
         k_loop_mc<0, false>(st, o, K / 64, wave, wm, brow, fr, lane, acc);
+    if (KIND == BWD_G) {
+        // the K loop ended with every load complete; uses here let the
+        // compiler know (else it waits for them again in the epilogue,
+        // counting the epilogue's own stores)
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            asm volatile("" ::"v"(wpair[it]), "v"(z0[it]), "v"(z1[it]), "v"(epair[it]));
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                asm volatile("" ::"v"(pa[h][it].x), "v"(pa[h][it].y), "v"(pa[h][it].z),
+                             "v"(pa[h][it].w), "v"(pu[h][it].x), "v"(pu[h][it].y),
+                             "v"(pu[h][it].z), "v"(pu[h][it].w));
+        }
+    }
     // lane holds row 32 wm + lane % 32 and, in acc[0][ni][4 q + i], column
     // brow[ni] + 8 q + 4 (lane / 32) + i
     if (KIND == BWD_DX) {
@@ -763,16 +822,34 @@ __global__ __launch_bounds__(512, 1) void bwd_mc_dma_kernel(BwdTileArgs a) {
         return;
     }
     if (KIND == BWD_G) {
-        // binary32 rows in two passes of 128 columns (512-byte staged rows
-        // as above): pass h stages the columns of the waves with wn == h;
-        // nontemporal too (T = 4096: G 0.403 -> 0.390 ms, the SwiGLU
-        // backward that reads it next no slower)
+        // SwiGLU backward on the tile, in two passes of 128 columns: pass h
+        // stages G of the waves with wn == h in LDS (binary32, 512-byte rows,
+        // rows 0 .. 63 in buffer 0 and 64 .. 127 in buffer 1, chunk c of row
+        // r at chunk c ^ (r & 31)); then every thread takes its rows' 8
+        // columns (only rows that hold data: the work is spread evenly over
+        // the block whatever the tile's fill).  With s = sigmoid(a) (through
+        // the hardware reciprocal, about 1 ulp), h = a s u, dh = w G:
+        // da = dh u s (1 + a (1 - s)), du = dh a s, the stored H = w h; and
+        // G . h of the row's 128 columns (16 lanes' sums in a fixed tree) as
+        // one partial, 128 columns apart in dwp / ds.
         typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+        float ew[4];
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+            ew[it] = shared ? 1.0f / (1.0f + __expf(-(z0[it] + (a.logit_split > 1 ? z1[it] : 0.f))))
+                            : wpair[it];
+        if (shared && nt == 0 && (tid & 15) == 0) {
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+                if (32 * it + er < nrows) a.gate[row0 + 32 * it + er] = ew[it];
+        }
+        uint16_t *dgu = shared ? a.dgu_sh : a.dgu;
+        uint16_t *hhp = shared ? a.hh_sh : a.hh;
         unsigned char *sbuf = wm < 2 ? st0 : st1;
         const int rl = 32 * (wm & 1) + fr;
-        float *cb = static_cast<float *>(shared ? a.c_sh : a.c) + (int64_t)row0 * N + n0;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
+            if (n0 + 128 * h >= N) break;  // block-uniform
             if (wn == h) {
 #pragma unroll
                 for (int ni = 0; ni < NB; ++ni)
@@ -790,15 +867,59 @@ __global__ __launch_bounds__(512, 1) void bwd_mc_dma_kernel(BwdTileArgs a) {
             __builtin_amdgcn_s_waitcnt(0xC07F);
             __builtin_amdgcn_s_barrier();
             compiler_fence();
+            const int cb = (n0 >> 7) + h;  // the partial's 128-column block
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int pc = tid + 512 * i, r = pc >> 5, c = pc & 31, r2 = r & 63;
-                const unsigned char *src = (i < 4 ? st0 : st1) + r2 * 512 + ((c ^ (r2 & 31)) << 4);
-                const u32x4_t v = *reinterpret_cast<const u32x4_t *>(src);
-                const int colg = 128 * h + 4 * c;
-                if (r < nrows && n0 + colg < N) {
-                    float *dst = cb + (int64_t)r * N + colg;
-                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(dst));
+            for (int it = 0; it < 4; ++it) {
+                if (32 * it >= nrows) break;  // block-uniform
+                const int row = 32 * it + er, r2 = row & 63;
+                const unsigned char *gb = (row < 64 ? st0 : st1) + r2 * 512;
+                const int ch = ec >> 2;
+                const float4 g0 = *reinterpret_cast<const float4 *>(gb + ((ch ^ (r2 & 31)) << 4));
+                const float4 g1 =
+                    *reinterpret_cast<const float4 *>(gb + (((ch + 1) ^ (r2 & 31)) << 4));
+                const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+                const uint32_t av2[4] = {pa[h][it].x, pa[h][it].y, pa[h][it].z, pa[h][it].w};
+                const uint32_t uv2[4] = {pu[h][it].x, pu[h][it].y, pu[h][it].z, pu[h][it].w};
+                const float w = ew[it];
+                uint32_t da2[4], du2[4], hw2[4];
+                float dot = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float da[2], du[2], hw[2];
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        const float av = i ? bf16_hi(av2[e]) : bf16_lo(av2[e]);
+                        const float uv = i ? bf16_hi(uv2[e]) : bf16_lo(uv2[e]);
+                        const float g = gv[2 * e + i];
+                        const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-av));
+                        const float silu = av * sg;
+                        const float hv = silu * uv;
+                        dot = fmaf(g, hv, dot);
+                        const float dh = w * g;
+                        da[i] = dh * uv * (sg * fmaf(av, 1.0f - sg, 1.0f));
+                        du[i] = dh * silu;
+                        hw[i] = w * hv;
+                    }
+                    da2[e] = pack_bf16x2(da[0], da[1]);
+                    du2[e] = pack_bf16x2(du[0], du[1]);
+                    hw2[e] = pack_bf16x2(hw[0], hw[1]);
+                }
+#pragma unroll
+                for (int o = 8; o >= 1; o >>= 1) dot += __shfl_xor(dot, o, kWave);
+                if (row < nrows) {
+                    const int64_t gr = row0 + row;
+                    const int col = n0 + 128 * h + ec;
+                    uint16_t *d0 = dgu + gr * 2 * Fg + col;
+                    __builtin_nontemporal_store(u32x4_t{da2[0], da2[1], da2[2], da2[3]},
+                                                reinterpret_cast<u32x4_t *>(d0));
+                    __builtin_nontemporal_store(u32x4_t{du2[0], du2[1], du2[2], du2[3]},
+                                                reinterpret_cast<u32x4_t *>(d0 + Fg));
+                    __builtin_nontemporal_store(u32x4_t{hw2[0], hw2[1], hw2[2], hw2[3]},
+                                                reinterpret_cast<u32x4_t *>(hhp + gr * Fg + col));
+                    if ((tid & 15) == 0) {
+                        if (!shared) a.dwp[(int64_t)epair[it] * a.np + cb] = dot;
+                        else a.ds[gr * a.np + cb] = dot;
+                    }
                 }
             }
             compiler_fence();
@@ -808,27 +929,6 @@ __global__ __launch_bounds__(512, 1) void bwd_mc_dma_kernel(BwdTileArgs a) {
         }
         return;
     }
-    const int row = 32 * wm + fr;
-    if (row >= nrows) return;
-    const int64_t cbase = (int64_t)(row0 + row) * N + n0 + 4 * (lane >> 5);
-#pragma unroll
-    for (int ni = 0; ni < NB; ++ni)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if (n0 + brow[ni] + 8 * q >= N) continue;
-            const f32x16 &c4 = acc[0][ni];
-            if (KIND == BWD_DX) {
-                uint2 v;
-                v.x = pack_bf16x2(c4[4 * q], c4[4 * q + 1]);
-                v.y = pack_bf16x2(c4[4 * q + 2], c4[4 * q + 3]);
-                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(shared ? a.c_sh : a.c) + cbase +
-                                           brow[ni] + 8 * q) = v;
-            } else {
-                *reinterpret_cast<float4 *>(static_cast<float *>(shared ? a.c_sh : a.c) + cbase +
-                                            brow[ni] + 8 * q) =
-                    make_float4(c4[4 * q], c4[4 * q + 1], c4[4 * q + 2], c4[4 * q + 3]);
-            }
-        }
 }
 
 // dOut rounded to bf16 (nearest even, as the generic kernel rounds it when
@@ -1312,7 +1412,7 @@ hipError_t launch_bwd_dwr_dma(const BwdArgs &b, hipStream_t s, int *split) {
 }
 
 bool bwd_dma_ok(const BwdArgs &a) {
-    if (!a.bf16 || a.F % 128 || a.Fs % 128 || a.d % 128) return false;
+    if (!a.bf16 || a.F % 128 || a.Fs % 128 || a.d % 128 || a.logit_split > 2) return false;
     const int64_t rows = a.T * a.k;
     const int64_t wide = 2 * (int64_t)(a.F > a.Fs ? a.F : a.Fs);
     return rows * wide < ((int64_t)1 << 32) && wide * a.d < ((int64_t)1 << 32) &&
@@ -1360,8 +1460,22 @@ hipError_t launch_bwd_g_dma(const BwdArgs &b, int max_tiles, void *dout_bf16, hi
     a.a_sh = a.a;
     a.w = static_cast<const uint16_t *>(b.w_dn);
     a.w_sh = static_cast<const uint16_t *>(b.w_sdn);
-    a.c = b.g;
-    a.c_sh = b.g_sh;
+    a.c = nullptr;
+    a.c_sh = nullptr;
+    a.au = static_cast<const uint16_t *>(b.au);
+    a.au_sh = static_cast<const uint16_t *>(b.au_sh);
+    a.dgu = static_cast<uint16_t *>(b.dgu);
+    a.dgu_sh = static_cast<uint16_t *>(b.dgu_sh);
+    a.hh = static_cast<uint16_t *>(b.hh);
+    a.hh_sh = static_cast<uint16_t *>(b.hh_sh);
+    a.topk_w = b.topk_w;
+    a.logits = b.logits;
+    a.gate = b.gate;
+    a.dwp = b.dwp;
+    a.ds = b.ds;
+    a.ldl = b.ldl;
+    a.logit_split = b.logit_split;
+    a.np = b.gtile;  // cdiv(max(F, Fs), 128)
     const int fmax = b.F > b.Fs ? b.F : b.Fs;
     a.nn = (fmax + BN - 1) / BN;
     hipLaunchKernelGGL(bwd_mc_dma_kernel<BWD_G>, dim3(raster_blocks(a.nm, a.nn, a.gm)), dim3(512), 0,

@@ -15,6 +15,7 @@
 #include "moe_device.h"
 #include "moe_kernels.h"
 
+#include <algorithm>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -226,9 +227,12 @@ BwdPlan make_bwd_plan(const moe_desc &d, int64_t T) {
     p.dgu_sh = take((size_t)T * 2 * Fs * es);
     p.hh = take((size_t)pairs * F * es);
     p.hh_sh = take((size_t)T * Fs * es);
-    p.dwp = take((size_t)pairs * 4);
+    // G . h per row: one value, or one partial per 128 columns of G when the
+    // SwiGLU backward runs in G's epilogue
+    const size_t gparts = std::max<size_t>(1, (std::max(F, Fs) + 127) / 128);
+    p.dwp = take((size_t)pairs * gparts * 4);
     p.gate = take((size_t)T * 4);
-    p.ds = take((size_t)T * 4);
+    p.ds = take((size_t)T * gparts * 4);
     p.q = take((size_t)T * 4);
     p.dl = take((size_t)T * p.ldd * es);
     p.dxp = take((size_t)pairs * dm * es);
@@ -841,6 +845,7 @@ moe_status moe_backward(const moe_desc *desc, int64_t T, const void *x, const vo
     a.dwp = reinterpret_cast<float *>(base + pl.dwp);
     a.gate = reinterpret_cast<float *>(base + pl.gate);
     a.ds = reinterpret_cast<float *>(base + pl.ds);
+    a.gtile = 0;
     a.q = reinterpret_cast<float *>(base + pl.q);
     a.dl = base + pl.dl;
     a.ldd = pl.ldd;

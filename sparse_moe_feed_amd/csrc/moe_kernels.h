@@ -187,8 +187,10 @@ struct BwdArgs {
     float *g, *g_sh;    // [T*k, F], [T, Fs]    W_dn^T dout of each row
     void *dgu, *dgu_sh; // [T*k, 2F], [T, 2Fs]  da | du
     void *hh, *hh_sh;   // [T*k, F], [T, Fs]    w h (h = silu(a) u; w the row's combine weight, s_t shared)
-    float *dwp;         // [T*k] d/dw of each pair (pair order)
-    float *gate, *ds;   // [T] s_t and d/ds_t
+    float *dwp;         // [T*k, max(gtile, 1)] d/dw of each pair (pair order)
+    float *gate, *ds;   // [T] s_t and [T, max(gtile, 1)] d/ds_t
+    int gtile;          // 0: dwp / ds hold one value per row; > 0: per row, one partial
+                        //   sum per 128 columns of G (G's direct-to-LDS tiles), gtile apart
     float *q;           // [T] f . p_t
     void *dl;           // [T, ldd] router-logit gradient, zero padded
     int ldd;
@@ -211,14 +213,18 @@ inline int bwd_sh_chunk(int64_t T, int split) {
     return split ? (int)(((T + split - 1) / split + 63) / 64 * 64) : 0;
 }
 // p carries the routing and permutation buffers (tile map for kGemmBM rows).
-// mark(i) after stage i: 1 logits, 2 gate/up and G, 3 SwiGLU and router
-// backward, 4 dX, 5 dW_gu, 6 dW_dn, 7 router GEMMs, combine and loss.
+// mark(i) after stage i: 1 logits, 2 gate/up and G (with the SwiGLU backward
+// on the direct-to-LDS tiles), 3 SwiGLU (other paths) and router backward,
+// 4 dX, 5 dW_gu, 6 dW_dn, 7 router GEMMs, combine and loss.
 hipError_t launch_backward(const Problem &p, const BwdArgs &a, hipStream_t s,
                            const std::function<void(int)> &mark);
 // dX of the routed and shared rows ([da | du] W_gu) and G (dOut W_dn) on
 // direct-to-LDS tiles: bf16 layers with F, Fs and d multiples of 128 and
-// 32-bit element offsets.  G first rounds dOut to bf16 into dout_bf16 [T, d]
-// (dob, which the down-projection weight gradients read later too).
+// 32-bit element offsets, router logits in at most two K slices.  G first
+// rounds dOut to bf16 into dout_bf16 [T, d] (dob, which the down-projection
+// weight gradients read later too); its epilogue runs the SwiGLU backward
+// (dgu, hh, gate and the G . h partials in dwp / ds, a.gtile apart), so G is
+// never stored.
 bool bwd_dma_ok(const BwdArgs &a);
 // Down-projection weight gradients of the routed experts with at most 128
 // rows on streamed direct-to-LDS tiles (the shared expert's go to the tiled

@@ -128,6 +128,9 @@ def routed_case(T, d, E, k, F, Fs, dtype, seed, bias):
     (160, 256, 256, 2, 128, 128, 0.001, False), # streamed weight-gradient tiles with many
                                                 # experts that get no row (zero gradients)
     (600, 256, 64, 4, 256, 128, 0.01, True),    # F = 256: two 128-column slices of H per expert
+    (400, 256, 16, 4, 384, 128, 0.01, True),    # G . h in two column tiles for routed rows,
+                                                # one for the shared ones
+    (264, 256, 16, 4, 128, 384, 0.01, False),   # ... and the other way round
 ])
 def test_backward_bf16_layers(T, d, E, k, F, Fs, coef, bias):
     inp, idx, w, dout, b = routed_case(T, d, E, k, F, Fs, "bf16", T + E, bias)
