@@ -906,7 +906,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(BwdArgs a) {
     }
 }
 
-// Block-wide fixed-order reductions over 256 threads (4 waves).
+// Block-wide fixed-order sum over 256 threads (4 waves).
 __device__ __forceinline__ float block_sum(float v, float *red) {
     v = wave_sum(v);
     const int w = threadIdx.x >> 6;
@@ -915,96 +915,112 @@ __device__ __forceinline__ float block_sum(float v, float *red) {
     __syncthreads();
     return (red[0] + red[1]) + (red[2] + red[3]);
 }
-__device__ __forceinline__ float block_max(float v, float *red) {
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-    const int w = threadIdx.x >> 6;
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[w] = v;
-    __syncthreads();
-    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-}
 
-// Router backward, one block of 256 threads per token: softmax p over the E
-// logits (+ bias), f . p, the load-balancing term, the selected experts'
-// term and the shared-gate logit's gradient, written as a dL row zero padded
-// to ldd columns (layer dtype).
-template <typename Tv>
+// Router backward, one wave per token (four per block), expert e in lane
+// e % 64, slot e / 64 (NS slots, E <= 64 NS): softmax p over the E logits
+// (+ bias), f . p, the load-balancing term, the selected experts' term and
+// the shared-gate logit's gradient, written as a dL row zero padded to ldd
+// columns (layer dtype).  Sums run over each lane's slots in order, then a
+// fixed tree over the wave.
+template <typename Tv, int NS>
 __global__ __launch_bounds__(256) void router_bwd_kernel(BwdArgs a) {
-    extern __shared__ float dls[];  // [ldd], then the token's logits [E + 1]
-    __shared__ float red[4];
-    __shared__ float pterm[kWave];  // the selected experts' terms (k <= 32)
-    __shared__ int pexp[kWave];
-    const int64_t t = blockIdx.x;
-    // G . h of each pair (lane jj < k of wave 0) and of the shared row
-    // (thread 64): one value, or partial sums over 128 columns of G each,
-    // added in column order; loaded first, used after the softmax
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= a.T) return;
+    // G . h of each pair (lane jj < k) and of the shared row (every lane):
+    // one value, or partial sums over 128 columns of G each, added in column
+    // order; loaded first, used after the softmax
+    // (every load is issued here, none waits for another: the kernel's time
+    // is one memory latency, not a chain of them)
     const int st = a.gtile > 0 ? a.gtile : 1;
     const int nr = a.gtile > 0 ? (a.F + 127) / 128 : 1;
     const int ns = a.gtile > 0 ? (a.Fs + 127) / 128 : 1;
-    float wj = 0.f, dwj = 0.f, dsv = 0.f, sg = 0.f;
-    int ej = 0;
-    if ((int)threadIdx.x < a.k) {
-        const int64_t pj = t * a.k + threadIdx.x;
-        wj = a.topk_w[pj];
-        ej = a.topk_idx[pj];
-        ej = ej < 0 ? 0 : (ej >= a.E ? a.E - 1 : ej);
-        const float *pp = a.dwp + pj * st;
-        dwj = pp[0];
-        for (int i = 1; i < nr; ++i) dwj += pp[i];
+    // (unconditional loads from clamped addresses: a load under a branch
+    // makes the compiler wait for every load at the join)
+    const bool pl = lane < a.k;
+    const int64_t pj = t * a.k + (pl ? lane : 0);
+    float wj = a.topk_w[pj];
+    int ej = a.topk_idx[pj];
+    constexpr int U = 8;  // partial sums loaded up front; more come one by one
+    float dpart[U], spart[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+        dpart[i] = a.dwp[pj * st + min(i, nr - 1)];
+        spart[i] = a.ds[t * st + min(i, max(ns, 1) - 1)];
     }
-    if (threadIdx.x == 64 && a.Fs > 0) {
-        sg = a.gate[t];
-        const float *pp = a.ds + t * st;
-        dsv = pp[0];
-        for (int i = 1; i < ns; ++i) dsv += pp[i];
-    }
-    // the token's logits: the sum of the K slices' partials
-    float *l = dls + a.ldd;
-    for (int e = threadIdx.x; e <= a.E; e += 256) {
-        float v = a.logits[t * a.ldl + e];
-        for (int sl = 1; sl < a.logit_split; ++sl) v += a.logits[(sl * a.T + t) * a.ldl + e];
-        l[e] = v;
-    }
-    __syncthreads();
+    float sg = a.gate[t];
+    // the token's logits (the sum of the K slices' partials) plus the bias,
+    // and f_e = counts_e / (T k)
+    float v[NS], fe[NS];
     const float inv_pairs = 1.0f / (float)((int64_t)a.T * a.k);
-    float m = -INFINITY;
-    for (int e = threadIdx.x; e < a.E; e += 256)
-        m = fmaxf(m, l[e] + (a.bias ? a.bias[e] : 0.f));
-    m = block_max(m, red);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        const int e = min(lane + 64 * j, a.E - 1);
+        const float x0 = a.logits[t * a.ldl + e];
+        const float x1 = a.logits[((a.logit_split > 1 ? a.T : 0) + t) * a.ldl + e];
+        const float b = a.bias ? a.bias[e] : 0.f;
+        fe[j] = (float)a.counts[e] * inv_pairs;
+        v[j] = lane + 64 * j < a.E ? (a.logit_split > 1 ? x0 + x1 : x0) + b : -INFINITY;
+    }
+    ej = ej < 0 ? 0 : (ej >= a.E ? a.E - 1 : ej);
+    float dwj = dpart[0], dsv = spart[0];
+#pragma unroll
+    for (int i = 1; i < U; ++i) {
+        if (i < nr) dwj += dpart[i];
+        if (i < ns) dsv += spart[i];
+    }
+    for (int i = U; i < nr; ++i) dwj += a.dwp[pj * st + i];
+    for (int i = U; i < ns; ++i) dsv += a.ds[t * st + i];
+    if (!pl) wj = dwj = 0.f;
+    if (a.Fs == 0) dsv = sg = 0.f;
+    float m = v[0];
+#pragma unroll
+    for (int j = 1; j < NS; ++j) m = fmaxf(m, v[j]);
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
     float z = 0.f;
-    for (int e = threadIdx.x; e < a.E; e += 256) z += __expf(l[e] + (a.bias ? a.bias[e] : 0.f) - m);
-    z = block_sum(z, red);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        v[j] = lane + 64 * j < a.E ? __expf(v[j] - m) : 0.f;
+        z += v[j];
+    }
+    z = wave_sum(z);
     const float rz = 1.0f / z;
     float fp = 0.f;
-    for (int e = threadIdx.x; e < a.E; e += 256) {
-        const float p = __expf(l[e] + (a.bias ? a.bias[e] : 0.f) - m) * rz;
-        dls[e] = p;
-        fp = fmaf((float)a.counts[e] * inv_pairs, p, fp);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        v[j] *= rz;  // 0 past E
+        fp = fmaf(fe[j], v[j], fp);
     }
-    fp = block_sum(fp, red);
+    fp = wave_sum(fp);
     const float c = a.coef * (float)a.E / (float)a.T;
-    for (int e = threadIdx.x; e < a.ldd; e += 256)
-        dls[e] = e < a.E ? c * dls[e] * ((float)a.counts[e] * inv_pairs - fp) : 0.f;
-    if (threadIdx.x < kWave) {
-        // sum_j w_j dw_j over the k pairs (a fixed tree over the wave; lanes
-        // past k add zeros), then each pair's softmax-weight term
-        float wdw = wj * dwj;
-        for (int o = kWave / 2; o >= 1; o >>= 1) wdw += __shfl_xor(wdw, o, kWave);
-        pterm[threadIdx.x] = wj * (dwj - wdw);
-        pexp[threadIdx.x] = ej;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) v[j] = c * v[j] * (fe[j] - fp);
+    // the selected experts' terms w_j (dw_j - sum_i w_i dw_i), added in slot
+    // order (a repeated expert takes its terms in that order)
+    float wdw = wj * dwj;
+    for (int o = 32; o >= 1; o >>= 1) wdw += __shfl_xor(wdw, o, kWave);
+    const float term = wj * (dwj - wdw);
+    for (int jj = 0; jj < a.k; ++jj) {
+        const int e = __shfl(ej, jj, kWave);
+        const float tv = __shfl(term, jj, kWave);
+        if ((e & 63) == lane) {
+#pragma unroll
+            for (int j = 0; j < NS; ++j)
+                if (j == (e >> 6)) v[j] += tv;
+        }
     }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        a.q[t] = fp;
-        // in slot order (a repeated expert adds its terms in that order)
-        for (int jj = 0; jj < a.k; ++jj) dls[pexp[jj]] += pterm[jj];
-    }
-    if (threadIdx.x == 64 && a.Fs > 0) dls[a.E] = dsv * sg * (1.0f - sg);
-    __syncthreads();
+    if (lane == 0) a.q[t] = fp;
+    const float dgate = a.Fs > 0 ? dsv * sg * (1.0f - sg) : 0.f;
     Tv *out = static_cast<Tv *>(a.dl) + t * a.ldd;
-    for (int e = threadIdx.x; e < a.ldd; e += 256) {
-        if constexpr (sizeof(Tv) == 2) out[e] = f32_to_bf16_rne(dls[e]);
-        else out[e] = dls[e];
+    for (int e = lane; e < a.ldd; e += 64) {
+        const int j = e >> 6;
+        float x = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < NS; ++jj)
+            if (jj == j) x = v[jj];
+        if (e >= a.E) x = e == a.E ? dgate : 0.f;
+        if constexpr (sizeof(Tv) == 2) out[e] = f32_to_bf16_rne(x);
+        else out[e] = x;
     }
 }
 
@@ -1151,6 +1167,19 @@ __global__ __launch_bounds__(256) void sh_reduce_kernel(const float *__restrict_
 
 static unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
 
+// The router backward for E <= 64 NS (E <= 1024).
+template <typename Tv> static hipError_t launch_router_bwd(const BwdArgs &a, hipStream_t s) {
+    const dim3 grid(cdiv(a.T, 4)), block(256);
+    const int slots = (a.E + 63) / 64;
+    if (slots <= 1) hipLaunchKernelGGL((router_bwd_kernel<Tv, 1>), grid, block, 0, s, a);
+    else if (slots <= 2) hipLaunchKernelGGL((router_bwd_kernel<Tv, 2>), grid, block, 0, s, a);
+    else if (slots <= 4) hipLaunchKernelGGL((router_bwd_kernel<Tv, 4>), grid, block, 0, s, a);
+    else if (slots <= 8) hipLaunchKernelGGL((router_bwd_kernel<Tv, 8>), grid, block, 0, s, a);
+    else if (slots <= 16) hipLaunchKernelGGL((router_bwd_kernel<Tv, 16>), grid, block, 0, s, a);
+    else return hipErrorInvalidValue;
+    return hipSuccess;
+}
+
 hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
                            const std::function<void(int)> &mark) {
     hipError_t err = a.counts_given ? launch_permute_tiles(pp, a.counts_given, QB, s)
@@ -1177,16 +1206,16 @@ hipError_t launch_backward(const Problem &pp, const BwdArgs &a, hipStream_t s,
     }
     mark(2);
     const int64_t rows = (int64_t)a.T * a.k + (a.Fs > 0 ? a.T : 0);
-    const size_t lds = (size_t)(a.ldd + a.E + 1) * sizeof(float);
     if (a.bf16) {
         if (!dma)
             hipLaunchKernelGGL(swiglu_bwd_kernel<uint16_t>, dim3(cdiv(rows, 4)), dim3(256), 0, s,
                                ag);
-        hipLaunchKernelGGL(router_bwd_kernel<uint16_t>, dim3((unsigned)a.T), dim3(256), lds, s, ag);
+        err = launch_router_bwd<uint16_t>(ag, s);
     } else {
         hipLaunchKernelGGL(swiglu_bwd_kernel<float>, dim3(cdiv(rows, 4)), dim3(256), 0, s, ag);
-        hipLaunchKernelGGL(router_bwd_kernel<float>, dim3((unsigned)a.T), dim3(256), lds, s, ag);
+        err = launch_router_bwd<float>(ag, s);
     }
+    if (err != hipSuccess) return err;
     mark(3);
     if (dma) {
         err = launch_bwd_dx_dma(a, (int)tiles, s);
