@@ -172,24 +172,55 @@ __device__ __forceinline__ int tile_src(const Args &a, const TileInfo &ti, int r
 constexpr int kScanChunks = DBM * 32 / 64;  // 64-pair chunks of topk_idx at T <= DBM, k <= 32
 
 // Direct tiles (T <= DBM, so an expert has at most DBM pairs when the top-k
-// experts of a token are distinct): the router listed the n touched experts
-// (counts[E] = n, tile_group[0..n) = the experts); block 0 serves the shared
-// expert (if any; its tile has all T rows, so it starts first), the next n
-// blocks expert tile_group[x], later blocks end.
+// experts of a token are distinct): the router set bit e % 32 of word e / 32
+// of a 32-word map in counts for every touched expert e (the map cleared
+// before it); block 0 serves the shared expert (if any; its tile has all T
+// rows, so it starts first), block sh + x the x-th touched expert in
+// ascending order, later blocks end.  The map is uniform over the block and
+// read by scalar loads, which do not queue behind the weight streams of the
+// CU's other blocks the way a vector load does.
 // decode_tile finds the group (and, with the permutation, the rows); for a
 // direct routed tile the rows come from tile_rows, after the block has its
 // first weight loads in flight.
+constexpr int kTouchWords = 32;  // 32-expert words of the touched map, E <= 1024
+
+// Position of the x-th (from 0) set bit of w; w has more than x set bits.
+__device__ __forceinline__ int nth_set_bit(uint32_t w, int x) {
+    int pos = 0;
+#pragma unroll
+    for (int s = 16; s >= 1; s >>= 1) {
+        const int c = __popc(w & ((1u << s) - 1));
+        if (x >= c) {
+            x -= c;
+            w >>= s;
+            pos += s;
+        }
+    }
+    return pos;
+}
+
+__device__ __forceinline__ int touched_expert(const int *__restrict__ map, int x) {
+    uint32_t w[kTouchWords];
+#pragma unroll
+    for (int j = 0; j < kTouchWords; ++j) w[j] = (uint32_t)map[j];
+#pragma unroll
+    for (int j = 0; j < kTouchWords; ++j) {
+        const int c = __popc(w[j]);
+        if (x < c) return 32 * j + nth_set_bit(w[j], x);
+        x -= c;
+    }
+    return -1;  // fewer than x + 1 experts touched
+}
+
 template <class Args>
 __device__ __forceinline__ bool decode_tile(const Args &a, TileInfo &ti, int tile) {
     ti.rows = nullptr;
     ti.row0 = 0;
     if (a.direct) {
-        const int nt = a.counts[a.E];
-        const int x = tile;
         const int sh = a.Fs > 0 ? 1 : 0;
-        if (x >= nt + sh) return false;
-        ti.shared = sh && x == 0;
-        ti.g = ti.shared ? a.E : a.tile_group[x - sh];
+        ti.shared = sh && tile == 0;
+        ti.g = ti.shared ? a.E : touched_expert(a.counts, tile - sh);
+        if (ti.g < 0) return false;
         ti.nrows = ti.shared ? (int)a.T : 0;  // routed: tile_rows
         return true;
     }

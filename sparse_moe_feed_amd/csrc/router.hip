@@ -45,28 +45,32 @@
 namespace moe {
 
 // Rows 0..E-1 of the extended router matrix are W_r, row E is the shared gate
-// vector g (absent when g == nullptr).  Block (x, y) owns tokens
-// [TT x, TT x + TT) and rows [4 RW y, 4 RW y + 4 RW); each wave owns RW rows.
+// vector g (absent when g == nullptr).  Block (tx, ry) owns tokens
+// [TT tx, TT tx + TT) and rows [4 RW ry, 4 RW ry + 4 RW); each wave owns RW rows.
+// The grid is one-dimensional over ntg token groups and nry_pad (a multiple
+// of 8) row groups.  Workgroups go to the 8 XCDs round robin (block b on XCD
+// b % 8), so block b takes row group 8 ((b / 8) / ntg) + b % 8 and token
+// group (b / 8) mod ntg: every row group stays on one XCD, whose L2 serves its
+// W_r rows to all token groups (one HBM read of W_r instead of one per XCD).
+// Row groups at or past nry have nothing to do.  A grid capped below the
+// number of blocks (a multiple of 8, so b and blockIdx.x share an XCD) walks
+// the blocks with a stride of gridDim.x.
 // The block's token rows are staged in LDS.  For bf16 rows of at most
 // kMaxChunks 512-element chunks, all of a row's chunk loads are issued before
 // any arithmetic, so a row costs one memory round trip.
 constexpr int kMaxChunks = 8;
 
 //
-// touch (null unless the select step lists the touched experts): block (0, 0)
-// clears its E + 1 counters for the select launch that follows.
+// touch (null unless the select step marks the touched experts): block (0, 0)
+// clears its 32-word map for the select launch that follows.
 template <typename T, int TT, int RW>
-__global__ __launch_bounds__(256) void router_logits_kernel(
+__device__ __forceinline__ void router_logits_block(
     const T *__restrict__ x, const T *__restrict__ w_router, const T *__restrict__ g,
     const float *__restrict__ bias, float *__restrict__ logits, int64_t ntok, int d, int E,
-    int32_t *__restrict__ touch) {
-    if (touch && blockIdx.x == 0 && blockIdx.y == 0)
-        for (int i = threadIdx.x; i <= E; i += 256) touch[i] = 0;
-    extern __shared__ __align__(16) unsigned char smem_raw[];
-    T *xs = reinterpret_cast<T *>(smem_raw);  // [TT][d]
+    int64_t tx, int ry, T *xs) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t t0 = (int64_t)blockIdx.x * TT;
+    const int64_t t0 = tx * TT;
     const int ntt = (int)min<int64_t>(TT, ntok - t0);
 
     const bool vec = (d % 8) == 0;
@@ -75,7 +79,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
     // before the token rows are staged.
     uint4 wq[kMaxChunks];
     if (preload) {
-        const int row = blockIdx.y * 4 * RW + wave * RW;
+        const int row = ry * 4 * RW + wave * RW;
         const T *wrow = row < E ? w_router + (int64_t)row * d : (row == E ? g : nullptr);
 #pragma unroll
         for (int c = 0; c < kMaxChunks; ++c) {
@@ -113,7 +117,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
     __syncthreads();
 
     for (int rr = 0; rr < RW; ++rr) {
-        const int row = blockIdx.y * 4 * RW + wave * RW + rr;
+        const int row = ry * 4 * RW + wave * RW + rr;
         if (row > E || (row == E && g == nullptr)) break;
         const T *wrow = row < E ? w_router + (int64_t)row * d : g;
         float acc[TT];
@@ -190,23 +194,53 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
     }
 }
 
+template <typename T, int TT, int RW>
+__global__ __launch_bounds__(256) void router_logits_kernel(
+    const T *__restrict__ x, const T *__restrict__ w_router, const T *__restrict__ g,
+    const float *__restrict__ bias, float *__restrict__ logits, int64_t ntok, int d, int E,
+    int64_t ntg, int nry, int64_t nblk, int32_t *__restrict__ touch) {
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    T *xs = reinterpret_cast<T *>(smem_raw);  // [TT][d]
+    for (int64_t b = blockIdx.x; b < nblk; b += gridDim.x) {
+        const int64_t bj = b >> 3;
+        const int64_t tx = bj % ntg;
+        const int ry = (int)(8 * (bj / ntg) + (b & 7));
+        if (ry >= nry) continue;  // uniform over the block
+        if (touch && tx == 0 && ry == 0 && threadIdx.x < 32) touch[threadIdx.x] = 0;
+        if (b != blockIdx.x) __syncthreads();  // the last block's reads of xs are done
+        router_logits_block<T, TT, RW>(x, w_router, g, bias, logits, ntok, d, E, tx, ry, xs);
+    }
+}
+
 // One wave per token: top-k by (logit desc, expert asc), weights, gate
-// (select_topk in router_select.h).  With touch / tlist (cleared by the
-// logits launch): the first selection of expert e sets touch[e] and appends e
-// to tlist at slot touch[E]++ (device-scope atomics; the list order varies
-// from run to run, its contents do not).
+// (select_topk in router_select.h).  With touch (its 32 words cleared by the
+// logits launch, E <= 1024): every selected expert e sets bit e % 32 of word
+// e / 32, the map of touched experts that the weight-streaming kernels read.
+// The block's four tokens are merged in LDS first, so each block sends at
+// most one atomic OR per word.
 template <int NV>
 __global__ __launch_bounds__(256) void router_select_kernel(
     const float *__restrict__ logits, int64_t ntok, int E, int k, int has_gate,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, float *__restrict__ gate,
-    float *__restrict__ gate_user, int32_t *__restrict__ touch, int32_t *__restrict__ tlist) {
+    float *__restrict__ gate_user, int32_t *__restrict__ touch) {
+    __shared__ uint32_t map[32];
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= ntok) return;
-    const int e = select_topk<NV>(logits + t * (E + 1), E, k, lane, topk_idx + t * k,
-                                  topk_w + t * k, has_gate ? gate + t : nullptr,
-                                  has_gate && gate_user ? gate_user + t : nullptr, nullptr);
-    if (touch && lane < k && atomicOr(&touch[e], 1) == 0) tlist[atomicAdd(&touch[E], 1)] = e;
+    if (touch) {
+        if (threadIdx.x < 32) map[threadIdx.x] = 0;
+        __syncthreads();
+    }
+    if (t < ntok) {
+        const int e = select_topk<NV>(logits + t * (E + 1), E, k, lane, topk_idx + t * k,
+                                      topk_w + t * k, has_gate ? gate + t : nullptr,
+                                      has_gate && gate_user ? gate_user + t : nullptr, nullptr);
+        if (touch && lane < k) atomicOr(&map[e >> 5], 1u << (e & 31));
+    }
+    if (touch) {
+        __syncthreads();
+        if (threadIdx.x < 32 && map[threadIdx.x])
+            atomicOr(reinterpret_cast<unsigned int *>(touch) + threadIdx.x, map[threadIdx.x]);
+    }
 }
 
 // Exact canonical logit for the token whose 512-chunk slices this wave holds
@@ -608,9 +642,12 @@ static hipError_t launch_logits(const Problem &p, hipStream_t s) {
     const T *g = static_cast<const T *>(p.sh_gate);
 #define MOE_LOGITS(TT, RW)                                                                       \
     do {                                                                                         \
-        dim3 gr((unsigned)((p.T + TT - 1) / TT), (unsigned)((p.E + 1 + 4 * RW - 1) / (4 * RW))); \
+        const int64_t ntg = (p.T + TT - 1) / TT;                                                 \
+        const int nry = (p.E + 1 + 4 * RW - 1) / (4 * RW);                                        \
+        const int64_t nblk = ntg * ((nry + 7) / 8 * 8);                                           \
+        const dim3 gr((unsigned)(nblk < ((int64_t)1 << 22) ? nblk : ((int64_t)1 << 22)));         \
         hipLaunchKernelGGL((router_logits_kernel<T, TT, RW>), gr, block, TT * row_bytes, s, x,   \
-                           wr, g, p.router_bias, p.logits, p.T, p.d, p.E,                        \
+                           wr, g, p.router_bias, p.logits, p.T, p.d, p.E, ntg, nry, nblk,        \
                            p.direct ? p.counts : nullptr);                                       \
     } while (0)
     if (p.T <= 64) {
@@ -679,7 +716,7 @@ hipError_t launch_router(const Problem &p, float *sh_gate_user, hipStream_t s) {
 #define MOE_SELECT(NV)                                                                        \
     hipLaunchKernelGGL((router_select_kernel<NV>), grid, block, 0, s, p.logits, p.T, p.E, p.k, \
                        has_gate, p.topk_idx, p.topk_w, p.gate, sh_gate_user,                  \
-                       p.direct ? p.counts : nullptr, p.tile_group)
+                       p.direct ? p.counts : nullptr)
     if (nv <= 1) MOE_SELECT(1);
     else if (nv <= 2) MOE_SELECT(2);
     else if (nv <= 4) MOE_SELECT(4);
