@@ -484,6 +484,388 @@ __global__ __launch_bounds__((64 * Geo<BM, BK>::NW), (NS * Geo<BM, BK>::STB <= 8
     }
 }
 
+// One tile of a launch: M-tile m of the permutation's tile map and N-tile n.
+struct DmaTile {
+    int g, row0, nrows, n0, Fg;
+    bool shared;
+};
+
+// Tile of virtual block v (raster_tile's XCD-aware order: M-tile m on XCD
+// m % 8, its N-tiles 8 ids apart); false when v has no work.  ntiles is the
+// tile map's length.
+template <int MODE, int BM>
+__device__ __forceinline__ bool dma_tile(const GemmArgs &a, int v, int ntiles, DmaTile &t) {
+    const int x = v & 7, q = v >> 3;
+    const int n = q % a.nn, m = 8 * (q / a.nn) + x;
+    if (m >= a.nm || m >= ntiles) return false;
+    t.g = a.tile_group[m];
+    t.shared = t.g == a.E;
+    const int m_local = (m - a.tile_start[t.g]) * BM;
+    if (!t.shared) {
+        t.row0 = a.offsets[t.g] + m_local;
+        t.nrows = min(BM, a.counts[t.g] - m_local);
+    } else {
+        t.row0 = m_local;
+        t.nrows = (int)min<int64_t>(BM, a.T - m_local);
+    }
+    t.Fg = t.shared ? a.Fs : a.F;
+    t.n0 = n * (MODE == 0 ? BN / 2 : BN);
+    return t.n0 < (MODE == 0 ? t.Fg : a.d);
+}
+
+// Token (the gathered A row) and combine weight of tile row r (padding rows
+// repeat the last row and are never stored).
+template <int MODE>
+__device__ __forceinline__ void dma_row(const GemmArgs &a, const DmaTile &t, int r, int &tok,
+                                        float &wgt) {
+    r = min(r, t.nrows - 1);
+    wgt = 0.f;
+    if (!t.shared) {
+        const int pair = a.perm[t.row0 + r];
+        tok = pair / a.k;
+        if (MODE == 1) wgt = a.topk_w[pair];
+    } else {
+        tok = t.row0 + r;
+        if (MODE == 1) wgt = a.gate[tok];
+    }
+}
+
+template <int MODE>
+__device__ __forceinline__ const uint16_t *dma_wbase(const GemmArgs &a, const DmaTile &t) {
+    return t.shared ? a.w_sh
+                    : a.w + (int64_t)t.g * (MODE == 0 ? (int64_t)2 * a.F * a.d : (int64_t)a.d * a.F);
+}
+template <int MODE>
+__device__ __forceinline__ const uint16_t *dma_abase(const GemmArgs &a, const DmaTile &t) {
+    return MODE == 1 ? (t.shared ? a.h_sh : a.h) : a.x;
+}
+
+// The tile's outputs from the accumulators: gate/up writes h = silu(g) u
+// (and, training, the pre-activations), down writes the weighted routed rows
+// y or the gated shared-expert term into out.
+template <int MODE, int BM, int BK>
+__device__ __forceinline__ void dma_epilogue(const GemmArgs &a, const DmaTile &t,
+                                             const int32_t *row_tok, const float *row_w,
+                                             const f32x16 (&acc)[Geo<BM, BK>::MI][NB], int mact,
+                                             int wm, int wn, const int (&brow)[NB], int fr,
+                                             int lane) {
+    using G = Geo<BM, BK>;
+    const bool shared = t.shared;
+    const int row0 = t.row0, nrows = t.nrows, n0 = t.n0, Fg = t.Fg;
+    // Accumulator layout (B A^T): lane holds token row WR wm + 32 mi + lane % 32
+    // and, in acc[mi][ni][4 g + q], output column brow[ni] + 8 g + 4 (lane / 32) + q.
+    const int cq = 4 * (lane >> 5);
+    if (MODE == 0) {
+        uint16_t *H = shared ? a.h_sh : a.h;
+#pragma unroll
+        for (int mi = 0; mi < G::MI; ++mi) {
+            const int row = G::WR * wm + 32 * mi + fr;
+            if (mi >= mact || row >= nrows) continue;
+            uint16_t *hrow = H + (int64_t)(row0 + row) * Fg + n0 + 64 * wn + cq;
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x16 &gt = acc[mi][pr], &up = acc[mi][pr + 2];
+                    uint2 q;
+                    q.x = pack_bf16x2(silu_mul(gt[4 * g], up[4 * g]), silu_mul(gt[4 * g + 1], up[4 * g + 1]));
+                    q.y = pack_bf16x2(silu_mul(gt[4 * g + 2], up[4 * g + 2]),
+                                      silu_mul(gt[4 * g + 3], up[4 * g + 3]));
+                    *reinterpret_cast<uint2 *>(hrow + 32 * pr + 8 * g) = q;
+                }
+            if (a.au) {
+                // training forward: the pre-activations too, gate half then up half
+                uint16_t *arow = (shared ? a.au_sh : a.au) + (int64_t)(row0 + row) * 2 * Fg + n0 +
+                                 64 * wn + cq;
+#pragma unroll
+                for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+#pragma unroll
+                        for (int half = 0; half < 2; ++half) {
+                            const f32x16 &v = acc[mi][pr + 2 * half];
+                            uint2 q;
+                            q.x = pack_bf16x2(v[4 * g], v[4 * g + 1]);
+                            q.y = pack_bf16x2(v[4 * g + 2], v[4 * g + 3]);
+                            *reinterpret_cast<uint2 *>(arow + half * Fg + 32 * pr + 8 * g) = q;
+                        }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int mi = 0; mi < G::MI; ++mi) {
+            const int row = G::WR * wm + 32 * mi + fr;
+            if (mi >= mact || row >= nrows) continue;
+            const float wgt = row_w[row];
+            if (!shared) {
+                // routed rows: weighted, into y (16-bit block floating point)
+                uint8_t *yrow = a.y + (int64_t)(row0 + row) * y16_pitch(a.d);
+                // a lane holds four consecutive columns of each 8-column
+                // group, lane ^ 32 the other four (same row): the group's
+                // exponent is their joint maximum, and the lane below 32
+                // writes the four exponent bytes of a 32-column block at once
+#pragma unroll
+                for (int ni = 0; ni < NB; ++ni) {
+                    const int cb = n0 + brow[ni];
+                    if (cb >= a.d) continue;
+                    const f32x16 &c = acc[mi][ni];
+                    uint32_t xw = 0;
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const float v0 = wgt * c[4 * g], v1 = wgt * c[4 * g + 1];
+                        const float v2 = wgt * c[4 * g + 2], v3 = wgt * c[4 * g + 3];
+                        float am = absmax4(v0, v1, v2, v3);
+                        am = fmaxf(am, __shfl_xor(am, 32, 64));
+                        const uint32_t x = y16_exponent(am);
+                        uint2 m;
+                        m.x = y16_pack2(v0, v1, x);
+                        m.y = y16_pack2(v2, v3, x);
+                        *reinterpret_cast<uint2 *>(yrow + 2 * (int64_t)(cb + 8 * g + cq)) = m;
+                        xw |= x << (8 * g);
+                    }
+                    if (cq == 0)
+                        *reinterpret_cast<uint32_t *>(yrow + 2 * (int64_t)a.d + cb / 8) = xw;
+                }
+            } else {
+                // shared expert: gated term, binary32, straight into out
+                float *orow = a.out + (int64_t)row_tok[row] * a.d + n0 + cq;
+#pragma unroll
+                for (int ni = 0; ni < NB; ++ni)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int col = n0 + brow[ni] + 8 * g + cq;
+                        if (col >= a.d) continue;
+                        const f32x16 &c = acc[mi][ni];
+                        *reinterpret_cast<float4 *>(orow + brow[ni] + 8 * g) =
+                            make_float4(wgt * c[4 * g], wgt * c[4 * g + 1], wgt * c[4 * g + 2],
+                                        wgt * c[4 * g + 3]);
+                    }
+            }
+        }
+    }
+}
+
+// Where a K step's refill comes from: the operands of one tile.
+template <int BM, int BK> struct DmaSrc {
+    const uint16_t *a, *w;
+    uint32_t ao[Geo<BM, BK>::AL], bo[Geo<BM, BK>::BL];
+};
+
+// The tile's load sources: B rows of its weight slice, A rows of its tokens
+// (gate/up: the gathered x rows, each lane looking up the tokens of its own
+// loads) or of h (down).  Element offsets are 32-bit (the host checks that
+// every offset fits).
+template <int MODE, int BM, int BK>
+__device__ __forceinline__ void dma_src(const GemmArgs &a, const DmaTile &t, int wave, int lane,
+                                        DmaSrc<BM, BK> &src) {
+    using G = Geo<BM, BK>;
+    src.a = dma_abase<MODE>(a, t);
+    src.w = dma_wbase<MODE>(a, t);
+#pragma unroll
+    for (int j = 0; j < G::AL; ++j) {
+        const int R = (G::AL * wave + j) * G::RPL + lane / G::CH;
+        const int c = (lane % G::CH) ^ swz<BK>(R);
+        const int r = t.row0 + min(R, t.nrows - 1);
+        if (MODE == 1) {
+            src.ao[j] = (uint32_t)r * (uint32_t)t.Fg + 8 * c;
+        } else {
+            const int tok = t.shared ? r : a.perm[r] / a.k;
+            src.ao[j] = (uint32_t)tok * (uint32_t)a.d + 8 * c;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < G::BL; ++j) {
+        const int R = (G::BL * wave + j) * G::RPL + lane / G::CH;
+        const int c = (lane % G::CH) ^ swz<BK>(R);
+        src.bo[j] = (MODE == 1 ? (uint32_t)min(t.n0 + R, a.d - 1) * (uint32_t)t.Fg
+                               : (uint32_t)(R < BN / 2 ? t.n0 + R : t.Fg + t.n0 + (R - BN / 2)) *
+                                     (uint32_t)a.d) + 8 * c;
+    }
+}
+
+// k_step with the refill taken across tiles: stage kt + NS of this tile, or,
+// past its last step, stage kt + NS - nk of the next tile (nk % NS == 0, so
+// that stage lands in the buffer the next tile's K loop reads it from), or,
+// with no next tile, this tile's last stage again (never computed).  The
+// source is selected, the loads are issued either way, so every step keeps
+// NS - 1 stages in flight and the waits are those of k_step.
+template <int BM, int BK, int NS, int MACT, int S>
+__device__ __forceinline__ void k_step_xt(const Stages<NS> &st, int kt, int nk, bool has,
+                                          const DmaSrc<BM, BK> &cur, const DmaSrc<BM, BK> &nxt,
+                                          int wave, int wm, const int (&brow)[NB], int fr,
+                                          int lane, Frags &f0, Frags &f1,
+                                          f32x16 (&acc)[Geo<BM, BK>::MI][NB]) {
+    using G = Geo<BM, BK>;
+    sub_step<BM, BK, MACT>(st.s[S], 1, wm, brow, fr, lane, f0, f1, acc);
+    if constexpr (G::Q == 4) {
+        sub_step<BM, BK, MACT>(st.s[S], 2, wm, brow, fr, lane, f1, f0, acc);
+        sub_step<BM, BK, MACT>(st.s[S], 3, wm, brow, fr, lane, f0, f1, acc);
+    }
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm((NS - 2) * G::LOADS));
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    const int sk = kt + NS;
+    const bool in = sk < nk, to_next = !in && has;
+    const int k0 = (in ? sk : (has ? sk - nk : nk - 1)) * BK;
+    uint32_t ao[G::AL], bo[G::BL];
+#pragma unroll
+    for (int j = 0; j < G::AL; ++j) ao[j] = to_next ? nxt.ao[j] : cur.ao[j];
+#pragma unroll
+    for (int j = 0; j < G::BL; ++j) bo[j] = to_next ? nxt.bo[j] : cur.bo[j];
+    dma_stage<BM, BK>(st.s[S], to_next ? nxt.a : cur.a, to_next ? nxt.w : cur.w, ao, bo, k0, wave);
+    __builtin_amdgcn_sched_barrier(0);
+    sub_step<BM, BK, MACT>(st.s[(S + 1) % NS], 0, wm, brow, fr, lane, f1, f0, acc);
+}
+
+template <int BM, int BK, int NS, int MACT, int S>
+__device__ __forceinline__ void k_steps_xt(const Stages<NS> &st, int kt, int nk, bool has,
+                                           const DmaSrc<BM, BK> &cur, const DmaSrc<BM, BK> &nxt,
+                                           int wave, int wm, const int (&brow)[NB], int fr,
+                                           int lane, Frags &f0, Frags &f1,
+                                           f32x16 (&acc)[Geo<BM, BK>::MI][NB]) {
+    if constexpr (S < NS) {
+        k_step_xt<BM, BK, NS, MACT, S>(st, kt + S, nk, has, cur, nxt, wave, wm, brow, fr, lane, f0,
+                                       f1, acc);
+        k_steps_xt<BM, BK, NS, MACT, S + 1>(st, kt, nk, has, cur, nxt, wave, wm, brow, fr, lane,
+                                            f0, f1, acc);
+    }
+}
+
+// One tile's K loop (nk a multiple of NS): wait for its stage 0 (issued by
+// the prologue or by the previous tile's last steps), then every step.  No
+// drain at the end: the next tile's first stages stay in flight.
+template <int BM, int BK, int NS, int MACT>
+__device__ __forceinline__ void k_loop_xt(const Stages<NS> &st, int nk, bool has,
+                                          const DmaSrc<BM, BK> &cur, const DmaSrc<BM, BK> &nxt,
+                                          int wave, int wm, const int (&brow)[NB], int fr,
+                                          int lane, f32x16 (&acc)[Geo<BM, BK>::MI][NB]) {
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 1) * Geo<BM, BK>::LOADS));
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    Frags f0, f1;
+    read_frags<BM, BK, MACT>(st.s[0], 0, wm, brow, fr, lane, f0);
+    for (int kt = 0; kt < nk; kt += NS)
+        k_steps_xt<BM, BK, NS, MACT, 0>(st, kt, nk, has, cur, nxt, wave, wm, brow, fr, lane, f0,
+                                        f1, acc);
+}
+
+// The grouped GEMM with its K pipeline running across tiles: persistent
+// blocks (one per CU, a multiple of 8) walk the tiles v = blockIdx.x,
+// + gridDim.x, ... in raster_tile's XCD-aware order; the last NS steps of a
+// tile load the first NS stages of the block's next tile, so the next tile
+// starts on landed data while this one's epilogue runs.  Every tile has the
+// same number of K steps, a multiple of NS (the host checks).  The next
+// tile's token and weight lookups go out at the start of this tile's K loop;
+// its rows' tokens and weights reach row_tok / row_w (the half this tile's
+// epilogue does not read) before this tile's epilogue.
+template <int MODE, int BM, int BK, int NS>
+__global__ __launch_bounds__((64 * Geo<BM, BK>::NW), 1) void gemm_dma_xt_kernel(GemmArgs a) {
+    using G = Geo<BM, BK>;
+    static_assert(NS >= 3 && NS <= 4, "three or four stage buffers");
+    __shared__ __align__(1024) unsigned char st0[G::STB];
+    __shared__ __align__(1024) unsigned char st1[G::STB];
+    __shared__ __align__(1024) unsigned char st2[G::STB];
+    __shared__ __align__(1024) unsigned char st3[NS > 3 ? G::STB : 16];
+    __shared__ int32_t row_tok[2][BM];
+    __shared__ float row_w[2][BM];
+
+    const int ntiles = a.tile_start[a.E + 1];
+    const int nv = 8 * ((a.nm + 7) / 8) * a.nn;  // raster_blocks(nm, nn, -1)
+    const int stride = (int)gridDim.x;
+    const int nk = (MODE == 1 ? a.F : a.d) / BK;  // the same for every tile
+    int v = blockIdx.x;
+    DmaTile cur;
+    while (v < nv && !dma_tile<MODE, BM>(a, v, ntiles, cur)) v += stride;
+    if (v >= nv) return;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = wave_id();
+    const int wm = wave >> 1, wn = wave & 1;
+    const int fr = lane & 31;
+    int brow[NB];
+#pragma unroll
+    for (int ni = 0; ni < NB; ++ni)
+        brow[ni] = MODE == 0 ? (ni >> 1) * (BN / 2) + 64 * wn + 32 * (ni & 1) : 128 * wn + 32 * ni;
+    Stages<NS> st;
+    {
+        unsigned char *all[4] = {st0, st1, st2, st3};
+#pragma unroll
+        for (int i = 0; i < NS; ++i) st.s[i] = all[i];
+    }
+
+    int buf = 0;
+    if (tid < BM) {
+        int tok;
+        float wgt;
+        dma_row<MODE>(a, cur, tid, tok, wgt);
+        row_tok[0][tid] = tok;
+        row_w[0][tid] = wgt;
+    }
+    DmaSrc<BM, BK> cs, ns;
+    dma_src<MODE, BM, BK>(a, cur, wave, lane, cs);
+    prologue<BM, BK, NS, 0>(st, (nk - 1) * BK, cs.a, cs.w, cs.ao, cs.bo, wave);
+    for (;;) {
+        int vn = v + stride;
+        DmaTile nxt;
+        bool has = false;
+        for (; vn < nv; vn += stride)
+            if (dma_tile<MODE, BM>(a, vn, ntiles, nxt)) {
+                has = true;
+                break;
+            }
+        int ntok = 0;
+        float nwgt = 0.f;
+        if (has) {
+            dma_src<MODE, BM, BK>(a, nxt, wave, lane, ns);
+            if (tid < BM) dma_row<MODE>(a, nxt, tid, ntok, nwgt);
+        } else {
+            ns = cs;
+        }
+
+        f32x16 acc[G::MI][NB];
+#pragma unroll
+        for (int i = 0; i < G::MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+        const int mact = min(G::MI, max(0, (cur.nrows - G::WR * wm + 31) / 32));
+#define MOE_LOOP(M) k_loop_xt<BM, BK, NS, M>(st, nk, has, cs, ns, wave, wm, brow, fr, lane, acc)
+        if constexpr (G::MI == 2) {
+            switch (mact) {
+            case 2: MOE_LOOP(2); break;
+            case 1: MOE_LOOP(1); break;
+            default: MOE_LOOP(0); break;
+            }
+        } else {
+            switch (mact) {
+            case 1: MOE_LOOP(1); break;
+            default: MOE_LOOP(0); break;
+            }
+        }
+#undef MOE_LOOP
+        // row_tok / row_w [buf ^ 1] were last read by the previous tile's
+        // epilogue, before this tile's K-loop barriers; the next tile's
+        // epilogue reads them after its own K-loop barriers
+        if (has && tid < BM) {
+            row_tok[buf ^ 1][tid] = ntok;
+            row_w[buf ^ 1][tid] = nwgt;
+        }
+        dma_epilogue<MODE, BM, BK>(a, cur, row_tok[buf], row_w[buf], acc, mact, wm, wn, brow, fr,
+                                   lane);
+        if (!has) break;
+        cur = nxt;
+        cs = ns;
+        v = vn;
+        buf ^= 1;
+    }
+    // the last tile's refills re-read its own last stage: no load may land
+    // after the block ends
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+}
+
 // ---------------------------------------------------------------------------
 // Backward products whose weight operand runs along the output axis (dX of
 // the rows, [da | du] W_gu, and G = dOut W_dn; the backward's 128-row tile
@@ -1514,13 +1896,28 @@ hipError_t launch_experts_dma(const Problem &p, int bm, hipStream_t s,
     a.nm = p.max_tiles;
     a.nn = (fmax + BN / 2 - 1) / (BN / 2);
     a.gm = -1;  // M-tile m on XCD m % 8: its N-tiles share A through one L2
+    // Down projection on 256-row tiles with every tile on the same number of
+    // K steps, a multiple of four (F == Fs, or no shared expert): the K
+    // pipeline runs across tiles on persistent blocks (its 20-step tiles at
+    // F = 640 lose a larger share to each tile's start and end than gate/up's
+    // 80-step tiles, which stay on the dispatcher's dynamic order)
+    const bool xt_dn = bm == 256 && (p.Fs == 0 || p.Fs == p.F) && (p.F / 32) % 4 == 0;
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 8)
+        ncu = 256;
+    auto xgrid = [ncu](const GemmArgs &g) {
+        const unsigned n = raster_blocks(g.nm, g.nn, g.gm), cap = 8u * (unsigned)(ncu / 8);
+        return dim3(n < cap ? n : cap);
+    };
     if (bm == 256) hipLaunchKernelGGL((gemm_dma_kernel<0, 256, 32, 3>), grid(a), dim3(512), 0, s, a);
     else hipLaunchKernelGGL((gemm_dma_kernel<0, 128, 64, 3>), grid(a), dim3(64 * Geo<128, 64>::NW), 0, s, a);
     mark(3);
     a.w = static_cast<const uint16_t *>(p.w_down);
     a.w_sh = static_cast<const uint16_t *>(p.w_sh_down);
     a.nn = (p.d + BN - 1) / BN;
-    if (bm == 256) hipLaunchKernelGGL((gemm_dma_kernel<1, 256, 32, 3>), grid(a), dim3(512), 0, s, a);
+    if (xt_dn) hipLaunchKernelGGL((gemm_dma_xt_kernel<1, 256, 32, 4>), xgrid(a), dim3(512), 0, s, a);
+    else if (bm == 256) hipLaunchKernelGGL((gemm_dma_kernel<1, 256, 32, 3>), grid(a), dim3(512), 0, s, a);
     else hipLaunchKernelGGL((gemm_dma_kernel<1, 128, 64, 3>), grid(a), dim3(64 * Geo<128, 64>::NW), 0, s, a);
     mark(4);
     return hipGetLastError();

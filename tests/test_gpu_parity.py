@@ -68,6 +68,10 @@ def test_tiny_fp32_layer():
     (1000, 576, 192, 4, 640, 640),  # 128-row LDS-DMA tiles at the pages' widths (F == Fs),
                                     # 9 K steps in gate/up, d % 256 = 64
     (2000, 640, 96, 6, 640, 640),   # the same, experts of one and two tiles
+    (8192, 1024, 8, 4, 128, 0),     # 256-row tiles, down pipelined across tiles: about two
+                                    # tiles per persistent block, no shared expert
+    (3000, 384, 32, 4, 640, 640),   # the same with the pages' expert widths (20 K steps per
+                                    # tile), ragged last column tile (d % 256 = 128)
 ])
 def test_small_bf16_layers(T, d, E, k, F, Fs):
     inp = W.small_case(T, d, E, k, F, Fs, "bf16", seed=T + E)
@@ -168,6 +172,18 @@ def test_duplicate_router_rows():
     inp["w_router"] = inp["w_router"].copy()
     inp["w_router"][9] = inp["w_router"][3]
     check_case(inp, 5, "duplicate router rows 3 and 9")
+
+
+def test_cross_tile_pipeline_with_empty_experts():
+    """256-row tiles whose down projection runs its K pipeline across tiles,
+    with a third of the experts chosen by no token (their tiles absent) and
+    one expert taking every token first (many tiles in a row)."""
+    T, d, E, k, F = 6144, 512, 12, 3, 256
+    inp = W.small_case(T, d, E, k, F, F, "bf16", seed=11)
+    inp["bias"] = np.zeros(E, np.float32)
+    inp["bias"][[1, 4, 7, 10]] = -100.0
+    inp["bias"][2] = 100.0
+    check_case(inp, k, "256-row tiles, four empty experts, expert 2 first for every token")
 
 
 @pytest.mark.parametrize("T,d,E,k,F", [(600, 128, 16, 2, 64), (100, 256, 32, 2, 128)])
