@@ -683,9 +683,9 @@ __device__ __forceinline__ void dma_src(const GemmArgs &a, const DmaTile &t, int
     }
 }
 
-// k_step with the refill taken across tiles: stage kt + NS of this tile, or,
-// past its last step, stage kt + NS - nk of the next tile (nk % NS == 0, so
-// that stage lands in the buffer the next tile's K loop reads it from), or,
+// k_step (on buffer S) with the refill taken across tiles: stage kt + NS of
+// this tile, or, past its last step, stage kt + NS - nk of the next tile
+// (which lands in the buffer the next tile's K loop reads it from), or,
 // with no next tile, this tile's last stage again (never computed).  The
 // source is selected, the loads are issued either way, so every step keeps
 // NS - 1 stages in flight and the waits are those of k_step.
@@ -718,24 +718,30 @@ __device__ __forceinline__ void k_step_xt(const Stages<NS> &st, int kt, int nk, 
     sub_step<BM, BK, MACT>(st.s[(S + 1) % NS], 0, wm, brow, fr, lane, f1, f0, acc);
 }
 
-template <int BM, int BK, int NS, int MACT, int S>
-__device__ __forceinline__ void k_steps_xt(const Stages<NS> &st, int kt, int nk, bool has,
+// Local steps kt + I .. kt + cnt - 1 (cnt <= NS) of a tile whose stage 0
+// sits in buffer P: local step j reads buffer (P + j) % NS, a constant here.
+template <int BM, int BK, int NS, int MACT, int P, int I>
+__device__ __forceinline__ void k_steps_xt(const Stages<NS> &st, int kt, int cnt, int nk, bool has,
                                            const DmaSrc<BM, BK> &cur, const DmaSrc<BM, BK> &nxt,
                                            int wave, int wm, const int (&brow)[NB], int fr,
                                            int lane, Frags &f0, Frags &f1,
                                            f32x16 (&acc)[Geo<BM, BK>::MI][NB]) {
-    if constexpr (S < NS) {
-        k_step_xt<BM, BK, NS, MACT, S>(st, kt + S, nk, has, cur, nxt, wave, wm, brow, fr, lane, f0,
-                                       f1, acc);
-        k_steps_xt<BM, BK, NS, MACT, S + 1>(st, kt, nk, has, cur, nxt, wave, wm, brow, fr, lane,
-                                            f0, f1, acc);
+    if constexpr (I < NS) {
+        if (I < cnt) {
+            k_step_xt<BM, BK, NS, MACT, (P + I) % NS>(st, kt + I, nk, has, cur, nxt, wave, wm,
+                                                      brow, fr, lane, f0, f1, acc);
+            k_steps_xt<BM, BK, NS, MACT, P, I + 1>(st, kt, cnt, nk, has, cur, nxt, wave, wm, brow,
+                                                   fr, lane, f0, f1, acc);
+        }
     }
 }
 
-// One tile's K loop (nk a multiple of NS): wait for its stage 0 (issued by
-// the prologue or by the previous tile's last steps), then every step.  No
-// drain at the end: the next tile's first stages stay in flight.
-template <int BM, int BK, int NS, int MACT>
+// One tile's K loop, its stage 0 in buffer P: wait for that stage (issued by
+// the prologue or by the previous tile's last steps), then every step.  A
+// refill past the last step lands where the next tile reads it: the next
+// tile's stage 0 in buffer (P + nk) % NS.  No drain at the end: the next
+// tile's first stages stay in flight.
+template <int BM, int BK, int NS, int MACT, int P>
 __device__ __forceinline__ void k_loop_xt(const Stages<NS> &st, int nk, bool has,
                                           const DmaSrc<BM, BK> &cur, const DmaSrc<BM, BK> &nxt,
                                           int wave, int wm, const int (&brow)[NB], int fr,
@@ -745,10 +751,30 @@ __device__ __forceinline__ void k_loop_xt(const Stages<NS> &st, int nk, bool has
     __builtin_amdgcn_s_barrier();
     compiler_fence();
     Frags f0, f1;
-    read_frags<BM, BK, MACT>(st.s[0], 0, wm, brow, fr, lane, f0);
-    for (int kt = 0; kt < nk; kt += NS)
-        k_steps_xt<BM, BK, NS, MACT, 0>(st, kt, nk, has, cur, nxt, wave, wm, brow, fr, lane, f0,
-                                        f1, acc);
+    read_frags<BM, BK, MACT>(st.s[P], 0, wm, brow, fr, lane, f0);
+    int kt = 0;
+    for (; kt + NS <= nk; kt += NS)
+        k_steps_xt<BM, BK, NS, MACT, P, 0>(st, kt, NS, nk, has, cur, nxt, wave, wm, brow, fr, lane,
+                                           f0, f1, acc);
+    k_steps_xt<BM, BK, NS, MACT, P, 0>(st, kt, nk - kt, nk, has, cur, nxt, wave, wm, brow, fr,
+                                       lane, f0, f1, acc);
+}
+
+template <int BM, int BK, int NS, int MACT>
+__device__ __forceinline__ void k_loop_xt_at(int ph, const Stages<NS> &st, int nk, bool has,
+                                             const DmaSrc<BM, BK> &cur, const DmaSrc<BM, BK> &nxt,
+                                             int wave, int wm, const int (&brow)[NB], int fr,
+                                             int lane, f32x16 (&acc)[Geo<BM, BK>::MI][NB]) {
+#define MOE_XT(P) k_loop_xt<BM, BK, NS, MACT, P>(st, nk, has, cur, nxt, wave, wm, brow, fr, lane, acc)
+    switch (ph) {
+    case 0: MOE_XT(0); break;
+    case 1: MOE_XT(1); break;
+    case 2: MOE_XT(2); break;
+    default:
+        if constexpr (NS > 3) MOE_XT(3);
+        break;
+    }
+#undef MOE_XT
 }
 
 // The grouped GEMM with its K pipeline running across tiles: persistent
@@ -756,7 +782,9 @@ __device__ __forceinline__ void k_loop_xt(const Stages<NS> &st, int nk, bool has
 // + gridDim.x, ... in raster_tile's XCD-aware order; the last NS steps of a
 // tile load the first NS stages of the block's next tile, so the next tile
 // starts on landed data while this one's epilogue runs.  Every tile has the
-// same number of K steps, a multiple of NS (the host checks).  The next
+// same number of K steps nk >= NS (the host checks); the next tile's stage 0
+// then sits in buffer (ph + nk) % NS, and its K loop is the instantiation
+// for that buffer.  The next
 // tile's token and weight lookups go out at the start of this tile's K loop;
 // its rows' tokens and weights reach row_tok / row_w (the half this tile's
 // epilogue does not read) before this tile's epilogue.
@@ -795,7 +823,7 @@ __global__ __launch_bounds__((64 * Geo<BM, BK>::NW), 1) void gemm_dma_xt_kernel(
         for (int i = 0; i < NS; ++i) st.s[i] = all[i];
     }
 
-    int buf = 0;
+    int buf = 0, ph = 0;  // ph: the buffer holding the current tile's stage 0
     if (tid < BM) {
         int tok;
         float wgt;
@@ -832,7 +860,7 @@ __global__ __launch_bounds__((64 * Geo<BM, BK>::NW), 1) void gemm_dma_xt_kernel(
 #pragma unroll
                 for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
         const int mact = min(G::MI, max(0, (cur.nrows - G::WR * wm + 31) / 32));
-#define MOE_LOOP(M) k_loop_xt<BM, BK, NS, M>(st, nk, has, cs, ns, wave, wm, brow, fr, lane, acc)
+#define MOE_LOOP(M) k_loop_xt_at<BM, BK, NS, M>(ph, st, nk, has, cs, ns, wave, wm, brow, fr, lane, acc)
         if constexpr (G::MI == 2) {
             switch (mact) {
             case 2: MOE_LOOP(2); break;
@@ -860,6 +888,7 @@ __global__ __launch_bounds__((64 * Geo<BM, BK>::NW), 1) void gemm_dma_xt_kernel(
         cs = ns;
         v = vn;
         buf ^= 1;
+        ph = (ph + nk) % NS;
     }
     // the last tile's refills re-read its own last stage: no load may land
     // after the block ends
@@ -1896,12 +1925,16 @@ hipError_t launch_experts_dma(const Problem &p, int bm, hipStream_t s,
     a.nm = p.max_tiles;
     a.nn = (fmax + BN / 2 - 1) / (BN / 2);
     a.gm = -1;  // M-tile m on XCD m % 8: its N-tiles share A through one L2
-    // Down projection on 256-row tiles with every tile on the same number of
-    // K steps, a multiple of four (F == Fs, or no shared expert): the K
-    // pipeline runs across tiles on persistent blocks (its 20-step tiles at
-    // F = 640 lose a larger share to each tile's start and end than gate/up's
-    // 80-step tiles, which stay on the dispatcher's dynamic order)
-    const bool xt_dn = bm == 256 && (p.Fs == 0 || p.Fs == p.F) && (p.F / 32) % 4 == 0;
+    // The K pipeline runs across tiles on persistent blocks wherever every
+    // tile has the same number of K steps, at least the stage count: both
+    // GEMMs on 128-row tiles (T = 4096: gate/up 0.683 -> 0.674 ms, down
+    // 0.456 -> 0.442 ms), and the down projection on 256-row tiles with a
+    // multiple of four steps (its 20-step tiles at F = 640 lose a larger
+    // share to each tile's start and end than gate/up's 80-step tiles, which
+    // measured faster on the dispatcher's dynamic order)
+    const int d_steps128 = p.d / 64;
+    const bool xt_dn128 = (p.Fs == 0 || p.Fs == p.F) && p.F / 64 >= 3;
+    const bool xt_dn = bm == 256 && (p.Fs == 0 || p.Fs == p.F) && (p.F / 32) % 4 == 0 && p.F / 32 >= 4;
     int dev = 0, ncu = 256;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 8)
@@ -1911,6 +1944,7 @@ hipError_t launch_experts_dma(const Problem &p, int bm, hipStream_t s,
         return dim3(n < cap ? n : cap);
     };
     if (bm == 256) hipLaunchKernelGGL((gemm_dma_kernel<0, 256, 32, 3>), grid(a), dim3(512), 0, s, a);
+    else if (d_steps128 >= 3) hipLaunchKernelGGL((gemm_dma_xt_kernel<0, 128, 64, 3>), xgrid(a), dim3(512), 0, s, a);
     else hipLaunchKernelGGL((gemm_dma_kernel<0, 128, 64, 3>), grid(a), dim3(64 * Geo<128, 64>::NW), 0, s, a);
     mark(3);
     a.w = static_cast<const uint16_t *>(p.w_down);
@@ -1918,6 +1952,7 @@ hipError_t launch_experts_dma(const Problem &p, int bm, hipStream_t s,
     a.nn = (p.d + BN - 1) / BN;
     if (xt_dn) hipLaunchKernelGGL((gemm_dma_xt_kernel<1, 256, 32, 4>), xgrid(a), dim3(512), 0, s, a);
     else if (bm == 256) hipLaunchKernelGGL((gemm_dma_kernel<1, 256, 32, 3>), grid(a), dim3(512), 0, s, a);
+    else if (xt_dn128) hipLaunchKernelGGL((gemm_dma_xt_kernel<1, 128, 64, 3>), xgrid(a), dim3(512), 0, s, a);
     else hipLaunchKernelGGL((gemm_dma_kernel<1, 128, 64, 3>), grid(a), dim3(64 * Geo<128, 64>::NW), 0, s, a);
     mark(4);
     return hipGetLastError();
